@@ -1,0 +1,284 @@
+"""ctypes binding of the CPU oracle (fs_oracle.c) and its synchronous loop.
+
+TEST INFRASTRUCTURE ONLY: imported by ``tests/``, ``__graft_entry__.smoke()``
+and the CPU-baseline leg of ``bench.py``. The product path never imports it.
+
+``SyncRun`` is the plain synchronous training loop that the prioritized
+schedule must reproduce exactly (FreeScale paper, section 3.2: keeping a strict
+write-then-read order on the collision rows gives numerical parity with the
+synchronized baseline): per iteration, balance, permute, dedup, look up every
+row from the current table, reduce the gradients and update every row.
+"""
+
+from __future__ import annotations
+
+import ctypes as C
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "fs_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+
+def build(force: bool = False) -> str:
+    """Compile the oracle with gcc (single-threaded, no FP contraction)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-ffp-contract=off", "-fPIC", "-shared",
+                               "-Wall", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+class _Store(C.Structure):
+    _fields_ = [("row_ids", C.c_void_p), ("n_rows", C.c_int64), ("vals", C.c_void_p),
+                ("state", C.c_void_p), ("dim", C.c_int32), ("bf16", C.c_int32)]
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        L = C.CDLL(build())
+        P = C.c_void_p
+        i32, i64 = C.c_int32, C.c_int64
+        L.or_fbs_rank_of_position.argtypes = [i64, i32]
+        L.or_fbs_rank_of_position.restype = i32
+        L.or_balance_fbs.argtypes = [P, i32, i32, P, P]
+        L.or_balance_fbs.restype = C.c_int
+        L.or_vbs_weight.argtypes = [i64, i32, i32]
+        L.or_vbs_weight.restype = i64
+        L.or_balance_vbs.argtypes = [P, i32, i32, i32, i32, P, P, P]
+        L.or_balance_vbs.restype = C.c_int
+        L.or_bucketize.argtypes = [P, i64, P, i32, i32, P, P, P, P, i32, P, P, P, P, P, P]
+        L.or_bucketize.restype = i64
+        L.or_unique.argtypes = [P, P, i64, i32, P, P, i32, P, P, P, P, P]
+        L.or_unique.restype = i64
+        L.or_collision.argtypes = [P, i64, P, i64, P, P, P]
+        L.or_collision.restype = None
+        L.or_lookup.argtypes = [C.POINTER(_Store), i64, i64, i64, P, P, P, P, i32, P]
+        L.or_lookup.restype = i64
+        L.or_reduce.argtypes = [i32, i64, i64, P, P, P, P]
+        L.or_reduce.restype = None
+        L.or_update.argtypes = [C.POINTER(_Store), i64, i64, i64, P, P, i32, P, i32, C.c_float,
+                                C.c_float]
+        L.or_update.restype = i64
+        L.or_bf16_to_f32.argtypes = [C.c_uint16]
+        L.or_bf16_to_f32.restype = C.c_float
+        L.or_f32_to_bf16.argtypes = [C.c_float]
+        L.or_f32_to_bf16.restype = C.c_uint16
+        _lib = L
+    return _lib
+
+
+def _p(a: np.ndarray):
+    assert a.flags.c_contiguous
+    return a.ctypes.data
+
+
+def _c(a, dt):
+    return np.ascontiguousarray(a, dtype=dt)
+
+
+# ----------------------------------------------------------------------------
+# stage wrappers
+
+
+def balance_fbs(uih_len, W):
+    L = _c(uih_len, np.int32)
+    perm = np.empty(len(L), np.int32)
+    ro = np.empty(W + 1, np.int32)
+    assert lib().or_balance_fbs(_p(L), len(L), W, _p(perm), _p(ro)) == 0
+    return perm, ro
+
+
+def balance_vbs(uih_len, W, alpha=(3, 2)):
+    L = _c(uih_len, np.int32)
+    perm = np.empty(len(L), np.int32)
+    ro = np.empty(W + 1, np.int32)
+    rw = np.empty(W, np.int64)
+    rc = lib().or_balance_vbs(_p(L), len(L), W, int(alpha[0]), int(alpha[1]), _p(perm), _p(ro),
+                              _p(rw))
+    if rc != 0:
+        raise ValueError(f"or_balance_vbs failed ({rc})")
+    return perm, ro, rw
+
+
+def vbs_weight(L, alpha):
+    return int(lib().or_vbs_weight(int(L), int(alpha[0]), int(alpha[1])))
+
+
+def fbs_rank_of_position(p, W):
+    return int(lib().or_fbs_rank_of_position(int(p), int(W)))
+
+
+def bucketize(ids, sample_offsets, rows, perm, rank_offsets, W):
+    ids = _c(np.atleast_2d(ids), np.int64)
+    T, n_tok = ids.shape
+    so = _c(sample_offsets, np.int64)
+    N = len(so) - 1
+    rows_a = _c(rows, np.int64)
+    rb = np.zeros(T, np.int64)
+    rb[1:] = np.cumsum(rows_a)[:-1]
+    perm = _c(perm, np.int32)
+    ro = _c(rank_offsets, np.int32)
+    n = T * n_tok
+    bal = np.empty(N + 1, np.int64)
+    keys = np.empty(max(n, 1), np.int64)
+    bm = np.empty(max(n, 1), np.int32)
+    splits = np.empty(W * W, np.int64)
+    sho = np.empty(W + 1, np.int64)
+    err = np.zeros(1, np.int32)
+    nv = lib().or_bucketize(_p(ids), n_tok, _p(so), N, T, _p(rows_a), _p(rb), _p(perm), _p(ro), W,
+                            _p(bal), _p(keys), _p(bm), _p(splits), _p(sho), _p(err))
+    return dict(bal_offsets=bal, shard_keys=keys[:nv], shard_bm=bm[:nv],
+                splits=splits.reshape(W, W), shard_offsets=sho, err=int(err[0]), row_base=rb)
+
+
+def unique(shard_keys, shard_bm, rows, W):
+    keys = _c(shard_keys, np.int64)
+    bm = _c(shard_bm, np.int32)
+    n = len(keys)
+    rows_a = _c(rows, np.int64)
+    T = len(rows_a)
+    rb = np.zeros(T, np.int64)
+    rb[1:] = np.cumsum(rows_a)[:-1]
+    uq = np.empty(max(n, 1), np.int64)
+    uo = np.empty(T * W + 1, np.int64)
+    seg = np.empty(n + 1, np.int32)
+    occ_bm = np.empty(max(n, 1), np.int32)
+    occ_uid = np.empty(max(n, 1), np.int32)
+    U = lib().or_unique(_p(keys), _p(bm), n, T, _p(rows_a), _p(rb), W, _p(uq), _p(uo), _p(seg),
+                        _p(occ_bm), _p(occ_uid))
+    return dict(unique=uq[:U].copy(), unique_offsets=uo, seg_offsets=seg[:U + 1].copy(),
+                occ_bm=occ_bm[:n].copy(), occ_uid=occ_uid[:n].copy())
+
+
+def collision(unique_new, unique_prev):
+    a = _c(unique_new, np.int64)
+    b = _c(unique_prev if unique_prev is not None else np.zeros(0, np.int64), np.int64)
+    cls = np.empty(max(len(a), 1), np.uint8)
+    pcls = np.empty(max(len(b), 1), np.uint8)
+    counts = np.empty(4, np.int64)
+    lib().or_collision(_p(a), len(a), _p(b), len(b), _p(cls), _p(pcls), _p(counts))
+    return cls[:len(a)].copy(), pcls[:len(b)].copy(), counts
+
+
+def bf16_to_f32(h):
+    return float(lib().or_bf16_to_f32(int(h)))
+
+
+def f32_to_bf16(f):
+    return int(lib().or_f32_to_bf16(float(f)))
+
+
+class RowStore:
+    """Touched rows of one table: ascending row ids, values, Adagrad state."""
+
+    def __init__(self, row_ids, vals, state=None, bf16=False):
+        self.row_ids = _c(row_ids, np.int64)
+        self.bf16 = bool(bf16)
+        self.vals = _c(vals, np.uint16 if bf16 else np.float32)
+        assert self.vals.shape[0] == len(self.row_ids)
+        self.dim = self.vals.shape[1]
+        self.state = _c(state if state is not None else np.zeros(len(self.row_ids)), np.float32)
+
+    def _s(self):
+        return _Store(_p(self.row_ids), len(self.row_ids), _p(self.vals), _p(self.state),
+                      self.dim, int(self.bf16))
+
+    def rows_of(self, row_ids):
+        idx = np.searchsorted(self.row_ids, row_ids)
+        assert np.all(self.row_ids[idx] == row_ids)
+        return self.vals[idx], self.state[idx]
+
+
+def lookup(store, row_base, u_lo, u_hi, uq, n_tok, which=-1, out=None):
+    if out is None:
+        out = np.zeros((n_tok, store.dim), store.vals.dtype)
+    s = store._s()
+    miss = lib().or_lookup(C.byref(s), row_base, u_lo, u_hi, _p(uq["unique"]),
+                           _p(uq["seg_offsets"]), _p(uq["occ_bm"]),
+                           _p(uq.get("cls", np.zeros(max(len(uq["unique"]), 1), np.uint8))),
+                           which, _p(out))
+    assert miss == 0, f"{miss} rows missing from the store"
+    return out
+
+
+def reduce(dim, u_lo, u_hi, uq, grad):
+    grad = _c(grad, np.float32)
+    g = np.empty((max(u_hi - u_lo, 1), dim), np.float32)
+    lib().or_reduce(dim, u_lo, u_hi, _p(uq["seg_offsets"]), _p(uq["occ_bm"]), _p(grad), _p(g))
+    return g[:u_hi - u_lo]
+
+
+def update(store, row_base, u_lo, u_hi, unique_keys, g, optim, lr, eps, cls=None, which=-1):
+    s = store._s()
+    g = _c(g, np.float32)
+    cls_a = _c(cls if cls is not None else np.zeros(max(len(unique_keys), 1)), np.uint8)
+    miss = lib().or_update(C.byref(s), row_base, u_lo, u_hi, _p(_c(unique_keys, np.int64)),
+                           _p(cls_a), which, _p(g), 1 if optim == "rw_adagrad" else 0,
+                           np.float32(lr), np.float32(eps))
+    assert miss == 0, f"{miss} rows missing from the store"
+
+
+# ----------------------------------------------------------------------------
+# the synchronous loop
+
+
+class SyncRun:
+    """Plain synchronous sparse steps over a sequence of batches.
+
+    ``stores[t]`` holds at least every row of table t that the run touches.
+    ``step(batch, grad_fn)`` runs one iteration and returns every stage output;
+    ``grad_fn(t, n_tok, bal) -> fp32 [n_tok, dim]`` supplies the batch-major
+    gradient of the balanced batch.
+    """
+
+    def __init__(self, workload, stores):
+        self.w = workload
+        self.stores = stores
+        self.rows = np.array([t.rows for t in workload.tables], np.int64)
+        self.row_base = np.zeros(len(self.rows), np.int64)
+        self.row_base[1:] = np.cumsum(self.rows)[:-1]
+        self.prev_unique = None
+
+    def index_stages(self, batch):
+        w = self.w
+        if w.balancer == "fbs":
+            perm, ro = balance_fbs(batch["uih_len"], w.world)
+            rw = None
+        else:
+            perm, ro, rw = balance_vbs(batch["uih_len"], w.world, w.alpha)
+        bk = bucketize(batch["ids"], batch["sample_offsets"], self.rows, perm, ro, w.world)
+        uq = unique(bk["shard_keys"], bk["shard_bm"], self.rows, w.world)
+        cls, pcls, counts = collision(uq["unique"], self.prev_unique)
+        uq["cls"] = cls
+        return dict(perm=perm, rank_offsets=ro, rank_weight=rw, bucket=bk, uniq=uq,
+                    prev_cls=pcls, counts=counts)
+
+    def step(self, batch, grad_fn, optimize=True):
+        out = self.index_stages(batch)
+        uq = out["uniq"]
+        n_tok = batch["n_tok"]
+        W = self.w.world
+        emb, red = [], []
+        for t, st in enumerate(self.stores):
+            lo = int(uq["unique_offsets"][t * W])
+            hi = int(uq["unique_offsets"][(t + 1) * W])
+            emb.append(lookup(st, int(self.row_base[t]), lo, hi, uq, n_tok))
+            if optimize:
+                G = grad_fn(t, n_tok, out["bucket"]["bal_offsets"])
+                g = reduce(st.dim, lo, hi, uq, G)
+                update(st, int(self.row_base[t]), lo, hi, uq["unique"], g, self.w.optim,
+                       self.w.lr, self.w.eps)
+                red.append(g)
+        self.prev_unique = uq["unique"]
+        out["emb"] = emb
+        out["reduced"] = red
+        return out

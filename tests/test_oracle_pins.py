@@ -1,0 +1,451 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Every check here is independent of the oracle's own code: hand-derived deals
+from the FreeScale paper (section 4.1), closed forms, invariants, brute force
+on tiny inputs in pure Python, and library routines (numpy.unique, math.fsum,
+torch.optim, torch's bfloat16 cast) on cases where the method reduces to them.
+"""
+
+import math
+import os
+from decimal import Decimal, getcontext
+
+import numpy as np
+import pytest
+
+from oracle import oracle as O
+
+
+def _read_golden(path):
+    with open(path) as f:
+        return [ln.strip() for ln in f if ln.strip() and not ln.startswith("#")]
+
+
+# ----------------------------------------------------------------------------
+# FBS
+
+
+def _ranks_positions(perm, ro, order):
+    """Sorted positions held by each rank, from (perm, rank_offsets)."""
+    pos_of = {s: p for p, s in enumerate(order)}
+    return [sorted(pos_of[s] for s in perm[ro[r]:ro[r + 1]]) for r in range(len(ro) - 1)]
+
+
+def _py_order(L):
+    return [s for _, s in sorted((int(l), s) for s, l in enumerate(L))]
+
+
+def test_fbs_hand_deals(golden_dir):
+    rng = np.random.default_rng(0)
+    for ln in _read_golden(os.path.join(golden_dir, "fbs_deals.txt")):
+        head, pos = ln.split(":")
+        N, W, r = map(int, head.split())
+        L = rng.permutation(N).astype(np.int32) + 1  # distinct lengths
+        perm, ro = O.balance_fbs(L, W)
+        got = _ranks_positions(perm, ro, _py_order(L))[r]
+        assert got == [int(x) for x in pos.split()], ln
+
+
+def test_fbs_printed_pattern_is_not_a_partition():
+    # The literal "i, 2n-i, 2n+i, 4n-i" assigns some position twice and skips
+    # another (0-based and 1-based alike); the snake reading is a partition.
+    n, rounds = 4, 4
+    for base in (0, 1):
+        taken = []
+        for i in range(base, n + base):
+            for k in range(rounds // 2):
+                taken += [2 * k * n + i, 2 * (k + 1) * n - i]
+        assert len(set(taken)) < len(taken)
+    snake = [O.fbs_rank_of_position(p, n) for p in range(n * rounds)]
+    assert all(snake.count(r) == rounds for r in range(n))
+
+
+@pytest.mark.parametrize("N,W", [(64, 4), (512, 16), (1024, 64), (4096, 512), (10, 4), (7, 8),
+                                 (1, 1), (0, 3)])
+def test_fbs_counts_and_order(N, W):
+    rng = np.random.default_rng(N * 7 + W)
+    L = rng.integers(1, 50, size=N).astype(np.int32)  # many ties
+    perm, ro = O.balance_fbs(L, W)
+    counts = np.diff(ro)
+    assert counts.sum() == N and counts.max() - counts.min() <= 1
+    if N % W == 0:
+        assert np.all(counts == N // W)
+    assert sorted(perm.tolist()) == list(range(N))
+    # each rank's samples are in dealing order: ascending (length, index)
+    for r in range(W):
+        seg = perm[ro[r]:ro[r + 1]]
+        keys = [(int(L[s]), int(s)) for s in seg]
+        assert keys == sorted(keys)
+
+
+@pytest.mark.parametrize("N,W", [(16, 4), (48, 6), (4096, 512)])
+def test_fbs_position_sums_equal_when_2W_divides_N(N, W):
+    # each pair of rounds hands every rank positions summing to 4kW + 2W - 1
+    L = np.arange(N, dtype=np.int32)[::-1].copy()
+    perm, ro = O.balance_fbs(L, W)
+    pos = _ranks_positions(perm, ro, _py_order(L))
+    sums = {sum(p) for p in pos}
+    assert len(sums) == 1
+    assert sums.pop() == sum(4 * k * W + 2 * W - 1 for k in range(N // (2 * W)))
+
+
+# ----------------------------------------------------------------------------
+# VBS
+
+
+def _decimal_round_pow(L, num, den):
+    getcontext().prec = 60
+    if num == 0:
+        return 1  # L**0 = 1, also for L = 0
+    x = Decimal(L) ** (Decimal(num) / Decimal(den))
+    return int((x + Decimal("0.5")).to_integral_value(rounding="ROUND_FLOOR"))
+
+
+def test_vbs_weights_exact():
+    for L in list(range(0, 300)) + [1024, 4095, 8191, 16384, 32767, 32768, 65535]:
+        for a in [(3, 2), (2, 1), (1, 1), (0, 1), (1, 2), (4, 2)]:
+            assert O.vbs_weight(L, a) == _decimal_round_pow(L, *a), (L, a)
+    assert O.vbs_weight(3, (1, 3)) == -1  # unsupported exponent
+
+
+def test_vbs_hand_example(golden_dir):
+    g = dict(ln.split(":", 1) for ln in _read_golden(os.path.join(golden_dir,
+                                                                  "vbs_example.txt")))
+    L = np.array(g["lengths"].split(), np.int32)
+    a = tuple(map(int, g["alpha"].split()))
+    perm, ro, rw = O.balance_vbs(L, int(g["ranks"]), a)
+    assert perm.tolist() == [int(x) for x in g["perm"].split()]
+    assert ro.tolist() == [int(x) for x in g["rank_offsets"].split()]
+    assert rw.tolist() == [int(x) for x in g["rank_weight"].split()]
+
+
+@pytest.mark.parametrize("N,W,alpha", [(64, 4, (3, 2)), (1024, 64, (3, 2)), (2048, 256, (2, 1)),
+                                       (4096, 512, (3, 2)), (9, 4, (1, 1)), (5, 8, (2, 1))])
+def test_vbs_cut_property(N, W, alpha):
+    rng = np.random.default_rng(N + W)
+    L = np.minimum(np.ceil(rng.lognormal(5, 1.3, size=N)), 32768).astype(np.int32)
+    perm, ro, rw = O.balance_vbs(L, W, alpha)
+    order = _py_order(L)
+    assert perm.tolist() == order
+    w = [_decimal_round_pow(int(L[s]), *alpha) for s in order]
+    T = sum(w)
+    assert ro[0] == 0 and ro[-1] == N and np.all(np.diff(ro) >= 0)
+    assert rw.sum() == T
+    for r in range(W):
+        seg = sum(w[ro[r]:ro[r + 1]])
+        assert seg == rw[r]
+        # within one boundary sample's weight of T/W
+        bnd = [w[c - 1] for c in (ro[r], ro[r + 1]) if 0 < c <= N]
+        assert abs(seg * W - T) < W * max(bnd + [0]) or seg * W == T
+    # brute force: no cut can move one sample and get closer to its ideal
+    S = np.concatenate([[0], np.cumsum(w)])
+    for r in range(1, W):
+        c = ro[r]
+        assert S[c] * W >= r * T
+        assert c == 0 or S[c - 1] * W < r * T
+
+
+def test_vbs_equal_lengths_equal_blocks():
+    L = np.full(64, 37, np.int32)
+    perm, ro, rw = O.balance_vbs(L, 8, (3, 2))
+    assert ro.tolist() == list(range(0, 65, 8))
+    assert len(set(rw.tolist())) == 1
+
+
+def test_vbs_alpha_zero_is_equal_counts():
+    L = np.random.default_rng(3).integers(1, 9000, size=100).astype(np.int32)
+    perm, ro, _ = O.balance_vbs(L, 7, (0, 1))
+    c = np.diff(ro)
+    assert set(c.tolist()) <= {100 // 7, 100 // 7 + 1}
+
+
+# ----------------------------------------------------------------------------
+# bucketize (indexed permute + ranged dispatch)
+
+
+def _tiny_batch(rng, N, T, R, maxlen=6):
+    n_s = rng.integers(1, maxlen + 1, size=N)
+    so = np.concatenate([[0], np.cumsum(n_s)]).astype(np.int64)
+    ids = np.stack([rng.integers(0, R[t], size=int(so[-1])) for t in range(T)])
+    return n_s, so, ids
+
+
+def _brute_shard_major(ids, so, rows, perm, ro, W):
+    """Shard-major items by explicit sort of (d, r, t, q, j) tuples."""
+    T = len(rows)
+    rb = np.concatenate([[0], np.cumsum(rows)[:-1]])
+    bal = [0]
+    for s in perm:
+        bal.append(bal[-1] + int(so[s + 1] - so[s]))
+    rank_of_q = {}
+    for r in range(W):
+        for q in range(ro[r], ro[r + 1]):
+            rank_of_q[q] = r
+    items = []
+    for q, s in enumerate(perm):
+        for j in range(int(so[s + 1] - so[s])):
+            for t in range(T):
+                idv = int(ids[t][so[s] + j])
+                block = -(-int(rows[t]) // W)
+                d = idv // block
+                items.append(((d, rank_of_q[q], t, q, j), int(rb[t]) + idv, bal[q] + j))
+    items.sort()
+    return items, bal
+
+
+@pytest.mark.parametrize("W,T", [(1, 1), (3, 1), (4, 2), (5, 3)])
+def test_bucketize_brute_force(W, T):
+    rng = np.random.default_rng(W * 10 + T)
+    R = [int(x) for x in rng.integers(5, 40, size=T)]
+    N = 9
+    _, so, ids = _tiny_batch(rng, N, T, R)
+    L = rng.integers(1, 5, size=N).astype(np.int32)
+    perm, ro = O.balance_fbs(L, W)
+    bk = O.bucketize(ids, so, R, perm, ro, W)
+    items, bal = _brute_shard_major(ids, so, R, perm, ro, W)
+    assert bk["bal_offsets"].tolist() == bal
+    assert bk["shard_keys"].tolist() == [k for _, k, _ in items]
+    assert bk["shard_bm"].tolist() == [b for _, _, b in items]
+    d_of = [t[0] for t, _, _ in items]
+    assert bk["shard_offsets"].tolist() == [sum(1 for d in d_of if d < x) for x in range(W + 1)]
+    sp = bk["splits"]
+    for d in range(W):
+        for r in range(W):
+            assert sp[d, r] == sum(1 for t, _, _ in items if t[0] == d and t[1] == r)
+    assert bk["err"] == 0
+
+
+def test_bucketize_single_shard_is_identity():
+    rng = np.random.default_rng(5)
+    _, so, ids = _tiny_batch(rng, 20, 1, [1000])
+    L = rng.integers(1, 9, size=20).astype(np.int32)
+    perm, ro = O.balance_fbs(L, 1)
+    bk = O.bucketize(ids, so, [1000], perm, ro, 1)
+    n = ids.shape[1]
+    assert bk["splits"].tolist() == [[n]]
+    assert bk["shard_bm"].tolist() == list(range(n))  # shard-major = batch-major
+    src = np.concatenate([ids[0][so[s]:so[s + 1]] for s in perm])
+    assert np.array_equal(bk["shard_keys"], src)
+
+
+def test_bucketize_drops_out_of_range_ids():
+    so = np.array([0, 3, 5], np.int64)
+    ids = np.array([[1, 50, 2, -1, 3]], np.int64)
+    perm, ro = O.balance_fbs(np.array([3, 2], np.int32), 2)
+    bk = O.bucketize(ids, so, [10], perm, ro, 2)
+    assert bk["err"] & 1
+    assert sorted(bk["shard_keys"].tolist()) == [1, 2, 3]
+    assert bk["shard_offsets"][-1] == 3
+
+
+# ----------------------------------------------------------------------------
+# dedup / CSR and collision
+
+
+def test_unique_against_numpy():
+    rng = np.random.default_rng(11)
+    rows = [300, 50]
+    W = 4
+    _, so, ids = _tiny_batch(rng, 40, 2, rows, maxlen=30)
+    L = rng.integers(1, 9, size=40).astype(np.int32)
+    perm, ro = O.balance_fbs(L, W)
+    bk = O.bucketize(ids, so, rows, perm, ro, W)
+    uq = O.unique(bk["shard_keys"], bk["shard_bm"], rows, W)
+    keys, bm = bk["shard_keys"], bk["shard_bm"]
+    u_np, inv, cnt = np.unique(keys, return_inverse=True, return_counts=True)
+    assert np.array_equal(uq["unique"], u_np)
+    assert np.array_equal(np.diff(uq["seg_offsets"]), cnt)
+    for u in range(len(u_np)):
+        occ = uq["occ_bm"][uq["seg_offsets"][u]:uq["seg_offsets"][u + 1]]
+        assert occ.tolist() == sorted(bm[inv == u].tolist())
+        assert np.all(uq["occ_uid"][uq["seg_offsets"][u]:uq["seg_offsets"][u + 1]] == u)
+    # every item exactly once
+    assert sorted(uq["occ_bm"].tolist() + []) == sorted(bm.tolist())
+    # (table, shard) groups
+    rb = [0, 300]
+    for t in range(2):
+        block = -(-rows[t] // W)
+        for d in range(W):
+            lo, hi = uq["unique_offsets"][t * W + d], uq["unique_offsets"][t * W + d + 1]
+            for k in uq["unique"][lo:hi]:
+                assert (k - rb[t]) // block == d and rb[t] <= k < rb[t] + rows[t]
+
+
+def test_collision_brute_force():
+    rng = np.random.default_rng(2)
+    for _ in range(20):
+        a = np.unique(rng.integers(0, 40, size=rng.integers(0, 30)))
+        b = np.unique(rng.integers(0, 40, size=rng.integers(0, 30)))
+        cls, pcls, counts = O.collision(a, b)
+        sa, sb = set(a.tolist()), set(b.tolist())
+        assert cls.tolist() == [int(x in sb) for x in a.tolist()]
+        assert pcls.tolist() == [int(x in sa) for x in b.tolist()]
+        C = len(sa & sb)
+        assert counts.tolist() == [len(a), C, len(a) - C, len(b) - C]
+    a = np.arange(10)
+    assert O.collision(a, a)[2][1] == 10
+    assert O.collision(a, a + 100)[2][1] == 0
+    assert O.collision(a, None)[2].tolist() == [10, 0, 10, 0]
+
+
+# ----------------------------------------------------------------------------
+# lookup, reduce, update
+
+
+def _csr_from(keys, bm):
+    return O.unique(np.asarray(keys, np.int64), np.asarray(bm, np.int32), [10_000], 1)
+
+
+def test_lookup_decodes_row_and_column():
+    # table value = row*1024 + col is exact in fp32: the output names its row
+    R, D = 4000, 16
+    vals = (np.arange(R)[:, None] * 1024 + np.arange(D)[None, :]).astype(np.float32)
+    st = O.RowStore(np.arange(R), vals)
+    rng = np.random.default_rng(4)
+    n = 500
+    keys = rng.integers(0, R, size=n)
+    uq = _csr_from(keys, np.arange(n))
+    out = O.lookup(st, 0, 0, len(uq["unique"]), uq, n)
+    assert np.array_equal(out[:, 0] // 1024, keys.astype(np.float32))
+    assert np.array_equal(out - out[:, :1], np.broadcast_to(np.arange(D, dtype=np.float32), out.shape))
+
+
+def test_lookup_class_filter_and_bf16():
+    R, D = 50, 8
+    vals = np.arange(R * D, dtype=np.uint16).reshape(R, D)
+    st = O.RowStore(np.arange(R), vals, bf16=True)
+    keys = [3, 3, 7, 9, 7, 3]
+    uq = _csr_from(keys, range(6))
+    uq["cls"] = np.array([1, 0, 1], np.uint8)  # rows 3 and 9 collide
+    out = np.full((6, D), 0xFFFF, np.uint16)
+    O.lookup(st, 0, 0, 3, uq, 6, which=1, out=out)
+    for i, k in enumerate(keys):
+        exp = vals[k] if k in (3, 9) else np.full(D, 0xFFFF, np.uint16)
+        assert np.array_equal(out[i], exp)
+
+
+def test_reduce_counts_and_one_hot():
+    rng = np.random.default_rng(8)
+    n, D = 3000, 8
+    keys = rng.zipf(1.3, size=n) % 200
+    uq = _csr_from(keys, np.arange(n))
+    U = len(uq["unique"])
+    ones = np.ones((n, D), np.float32)
+    g = O.reduce(D, 0, U, uq, ones)
+    assert np.array_equal(g[:, 0], np.diff(uq["seg_offsets"]).astype(np.float32))
+    # one-hot in the column = bm % D, value = bm: each row's sum lists its bms
+    oh = np.zeros((n, D), np.float32)
+    oh[np.arange(n), np.arange(n) % D] = np.arange(n)
+    g = O.reduce(D, 0, U, uq, oh)
+    for u in range(U):
+        bms = np.nonzero(keys == uq["unique"][u])[0]
+        exp = np.zeros(D)
+        np.add.at(exp, bms % D, bms)
+        assert np.array_equal(g[u], exp.astype(np.float32))
+
+
+def test_reduce_is_exactly_rounded_sum():
+    rng = np.random.default_rng(9)
+    n, D = 4000, 4
+    keys = rng.integers(0, 3, size=n)
+    grad = (rng.standard_normal((n, D)) * np.exp(rng.uniform(-20, 20, (n, D)))).astype(np.float32)
+    uq = _csr_from(keys, np.arange(n))
+    g = O.reduce(D, 0, 3, uq, grad)
+    for u in range(3):
+        for d in range(D):
+            exact = math.fsum(float(x) for x in grad[keys == uq["unique"][u], d])
+            # fp64 accumulation of 1300 terms: within 1e-13 of the exact sum's scale
+            assert abs(float(g[u, d]) - exact) <= abs(exact) * 2 ** -23 + 1e-12 * np.abs(
+                grad[keys == uq["unique"][u], d]).astype(np.float64).sum()
+
+
+def test_sgd_matches_torch():
+    import torch
+    rng = np.random.default_rng(1)
+    R, D = 30, 16
+    w0 = rng.standard_normal((R, D)).astype(np.float32) * 0.01
+    keys = rng.integers(0, R, size=200)
+    grad = rng.standard_normal((200, D)).astype(np.float32)
+    uq = _csr_from(keys, np.arange(200))
+    U = len(uq["unique"])
+    g = O.reduce(D, 0, U, uq, grad)
+    st = O.RowStore(np.arange(R), w0.copy())
+    O.update(st, 0, 0, U, uq["unique"], g, "sgd", 0.01, 0.0)
+    p = torch.nn.Parameter(torch.from_numpy(w0.copy()))
+    opt = torch.optim.SGD([p], lr=0.01)
+    gt = torch.zeros(R, D)
+    gt[torch.from_numpy(uq["unique"])] = torch.from_numpy(g)
+    p.grad = gt
+    opt.step()
+    # torch may fuse the multiply-add (one rounding); ours rounds lr*g first
+    # (two roundings of the operands' scale apart at most, even under cancellation)
+    ref = p.detach().numpy()
+    scale = np.maximum(np.abs(w0), np.abs(ref - w0)).astype(np.float32)
+    assert np.all(np.abs(st.vals - ref) <= 2 * np.spacing(scale))
+
+
+def test_rowwise_adagrad_dim1_matches_torch_adagrad():
+    # with one column, row-wise Adagrad is torch's element-wise Adagrad
+    import torch
+    rng = np.random.default_rng(2)
+    R = 64
+    w0 = rng.standard_normal((R, 1)).astype(np.float32)
+    st = O.RowStore(np.arange(R), w0.copy())
+    p = torch.nn.Parameter(torch.from_numpy(w0.copy()))
+    opt = torch.optim.Adagrad([p], lr=0.05, eps=1e-8, initial_accumulator_value=0.0)
+    for it in range(3):
+        g = rng.standard_normal((R, 1)).astype(np.float32)
+        O.update(st, 0, 0, R, np.arange(R), g, "rw_adagrad", 0.05, 1e-8)
+        p.grad = torch.from_numpy(g.copy())
+        opt.step()
+        # torch divides g by the root first; ours scales lr first: ulp-level apart
+        np.testing.assert_allclose(st.vals, p.detach().numpy(), rtol=4e-7, atol=1e-9)
+    np.testing.assert_allclose(st.state, opt.state[p]["sum"].numpy().ravel(), rtol=2.5e-7)
+
+
+def test_rowwise_adagrad_closed_form():
+    # |g_d| = c on every column: state = c^2 after one step, step = lr*g/(c+eps)
+    R, D, c = 5, 64, 0.375  # exact binary fraction
+    w0 = np.zeros((R, D), np.float32)
+    st = O.RowStore(np.arange(R), w0.copy())
+    signs = np.where(np.random.default_rng(0).random((R, D)) < 0.5, -1.0, 1.0)
+    g = (signs * c).astype(np.float32)
+    O.update(st, 0, 0, R, np.arange(R), g, "rw_adagrad", 0.05, 1e-8)
+    assert np.all(st.state == np.float32(c * c))
+    np.testing.assert_allclose(st.vals, -0.05 * g / (c + 1e-8), rtol=1e-6)
+    # a single non-zero column: the accumulator is the MEAN over columns
+    st2 = O.RowStore(np.arange(1), np.zeros((1, D), np.float32))
+    g1 = np.zeros((1, D), np.float32)
+    g1[0, 3] = 2.0
+    O.update(st2, 0, 0, 1, np.arange(1), g1, "rw_adagrad", 1.0, 0.0)
+    assert st2.state[0] == np.float32(4.0 / D)
+    assert st2.vals[0, 3] == np.float32(-2.0 / math.sqrt(4.0 / D))
+
+
+def test_bf16_rounding_matches_torch():
+    import torch
+    rng = np.random.default_rng(3)
+    x = np.concatenate([rng.standard_normal(5000).astype(np.float32) * 0.01,
+                        np.array([1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, 1.0 + 2 ** -9, -1.0 - 2 ** -8,
+                                  3.4e38, -3.4e38, np.inf, -np.inf, 0.0, -0.0, 1e-40],
+                                 np.float32)])
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().astype(np.uint16)
+    got = np.array([O.f32_to_bf16(float(v)) for v in x], np.uint16)
+    assert np.array_equal(got, ref)
+    nan = O.f32_to_bf16(float("nan"))
+    assert (nan & 0x7F80) == 0x7F80 and (nan & 0x7F)
+    for h in [0x3F80, 0xBF81, 0x0001, 0x7F7F]:
+        ref = torch.from_numpy(np.array([h], np.uint16).view(np.int16)).view(torch.bfloat16)
+        assert np.float32(O.bf16_to_f32(h)) == ref.float().item()
+
+
+def test_bf16_update_rounds_once():
+    # bf16 rows widen exactly, update in fp32, round-to-nearest-even on store
+    import torch
+    D = 32
+    w0 = torch.randn(1, D).mul(0.01).to(torch.bfloat16)
+    g = np.random.default_rng(0).standard_normal((1, D)).astype(np.float32)
+    st = O.RowStore([0], w0.view(torch.int16).numpy().astype(np.uint16), bf16=True)
+    O.update(st, 0, 0, 1, np.arange(1), g, "sgd", 0.01, 0.0)
+    ref = (w0.float() - torch.from_numpy(g) * np.float32(0.01)).to(torch.bfloat16)
+    assert np.array_equal(st.vals, ref.view(torch.int16).numpy().astype(np.uint16))
