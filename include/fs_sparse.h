@@ -1,0 +1,251 @@
+/*
+ * fs_sparse.h -- C ABI of the MI355X (gfx950) jagged sparse step.
+ *
+ * The library runs, on one GPU, the per-step sparse path of row-wise sharded
+ * sequence-recommender training as one rank of a virtual W-rank job would:
+ * balance the global batch, permute and bucketize its IDs into per-shard
+ * (shard-major) buffers, dedup each shard, split the unique rows into the
+ * ones that collide with the previous iteration and the exclusive rest, gather
+ * embeddings, segment-reduce gradients per unique row and apply a row-wise
+ * SGD / Adagrad update. The method is the one of "FreeScale: distributed
+ * training for sequence recommendation models" (arXiv 2604.24073), cited
+ * below as [FS] with its section, algorithm or equation.
+ *
+ * Conventions for every call:
+ *  - Array arguments are DEVICE pointers unless marked "host". The caller owns
+ *    all memory; no call allocates or frees, and none keeps state between
+ *    calls. Scratch memory comes from a caller workspace (ws, ws_bytes) whose
+ *    size a host-only fs_*_workspace_size() query returns; it depends only on
+ *    capacities, never on data.
+ *  - Every call is asynchronous on `stream`, makes no host synchronisation and
+ *    may be captured. Data-dependent counts (unique rows, collisions, valid
+ *    items) are written to device memory only; grids are sized by capacity.
+ *    The caller orders streams (events), e.g. so that a lookup of iteration
+ *    i+1 runs after the collision-row update of iteration i.
+ *  - Return value: FS_OK or a negative FS_ERR_* code for what the host can
+ *    check before launching (null pointers, sizes, unsupported shapes, a
+ *    workspace that is too small, a failed launch). On error nothing is
+ *    launched, except FS_ERR_HIP where earlier launches of the call may run.
+ *  - Data faults found on the device are OR-ed into a caller-owned sticky
+ *    int32 flag word `err` (FS_EF_* bits); the offending element is handled
+ *    as documented per call and the rest of the output stays defined.
+ *  - Integer types: IDs, keys and offsets into token arrays are int64;
+ *    positions inside one call's arrays are int32, so one call handles fewer
+ *    than 2^31 items.
+ *  - Tables: `fs_table` describes table t of T. Keys are global row numbers:
+ *    key = row_base_t + id with row_base_t = rows_0 + ... + rows_{t-1}; the
+ *    sum of all rows must be below 2^32. Table t is row-wise sharded into W
+ *    contiguous blocks of ceil(rows_t / W) rows: shard(t, id) = id / that.
+ */
+#ifndef FS_SPARSE_H
+#define FS_SPARSE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* return codes */
+#define FS_OK 0
+#define FS_ERR_INVALID_ARG (-1)
+#define FS_ERR_WORKSPACE (-2)
+#define FS_ERR_HIP (-3)
+#define FS_ERR_UNSUPPORTED (-4)
+
+/* sticky device error bits */
+#define FS_EF_ID_RANGE 1  /* an ID outside [0, rows_t) was dropped */
+#define FS_EF_SHAPE 2     /* sample_offsets[n] != n_tok, or offsets decrease */
+#define FS_EF_LEN_RANGE 4 /* a UIH length outside [0, FS_MAX_UIH] was clamped */
+
+/* limits */
+#define FS_MAX_SAMPLES 16384 /* samples per balance / bucketize call */
+#define FS_MAX_RANKS 1024    /* virtual ranks = shards, W */
+#define FS_MAX_TABLES 8
+#define FS_MAX_UIH 65535
+
+/* enums */
+#define FS_F32 0
+#define FS_BF16 1
+#define FS_SGD 0
+#define FS_RW_ADAGRAD 1
+#define FS_ALL (-1)
+#define FS_EXCLUSIVE 0
+#define FS_COLLISION 1
+
+typedef struct fs_table {
+  void* weights;  /* device [rows][dim], dtype FS_F32 or FS_BF16, row-major */
+  float* state;   /* device [rows] fp32 row-wise Adagrad accumulator, or NULL */
+  int64_t rows;   /* R_t */
+  int32_t dim;    /* D_t */
+  int32_t dtype;  /* FS_F32 or FS_BF16 */
+} fs_table;
+
+/* ------------------------------------------------------------------------ */
+/* Load balancing -- [FS] section 4.1 (partitioning algorithms), run inside  */
+/* the protocol of section 3.1 / Algorithm 1 (the partition function P      */
+/* maps the gathered global batch to ranks). Every rank computes the same   */
+/* result from the gathered lengths.                                        */
+/*                                                                          */
+/* Both sort the n samples of the global batch by UIH length, ascending,    */
+/* ties by global sample index (stable).                                    */
+/*  uih_len      [n] int32, UIH length of global sample s (s = the rank-major */
+/*               gather order). Values outside [0, FS_MAX_UIH] are clamped   */
+/*               and flag FS_EF_LEN_RANGE.                                   */
+/*  perm         [n] int32 out: the balanced batch, rank-major: rank r's      */
+/*               samples are perm[rank_offsets[r] .. rank_offsets[r+1]).      */
+/*  rank_offsets [W+1] int32 out.                                            */
+/*  err          sticky flags (may be NULL: faults then go unreported).      */
+/* n in [0, FS_MAX_SAMPLES], W in [1, FS_MAX_RANKS].                         */
+
+/* FBS: zig-zag (snake) deal of the sorted samples. [FS] 4.1 prints rank i's */
+/* positions as i, 2n-i, 2n+i, 4n-i, ... which is not a partition as printed; */
+/* the build reads it as the snake draft i, 2W-1-i, 2W+i, 4W-1-i, ... (0-based). */
+/* Each rank keeps its samples in dealing order. Counts differ by at most 1. */
+int fs_balance_fbs(const int32_t* uih_len, int32_t n, int32_t W, int32_t* perm,
+                   int32_t* rank_offsets, int32_t* err, void* ws, size_t ws_bytes,
+                   hipStream_t stream);
+
+/* VBS: weights w = round(L^alpha), alpha = alpha_num / alpha_den, exact in   */
+/* integers (alpha in {0, 1/2, 1, 3/2, 2}; else FS_ERR_UNSUPPORTED). The     */
+/* sorted samples are cut into W contiguous segments of about equal weight: */
+/* rank r starts at the first prefix position whose weight sum reaches       */
+/* r/W of the total, so each segment is within one boundary sample's weight */
+/* of total/W; empty segments are legal. perm is the sorted order.           */
+/*  rank_weight  [W] int64 out, weight of each segment (may be NULL).        */
+int fs_balance_vbs(const int32_t* uih_len, int32_t n, int32_t W, int32_t alpha_num,
+                   int32_t alpha_den, int32_t* perm, int32_t* rank_offsets,
+                   int64_t* rank_weight, int32_t* err, void* ws, size_t ws_bytes,
+                   hipStream_t stream);
+
+size_t fs_balance_workspace_size(int32_t n, int32_t W);
+
+/* ------------------------------------------------------------------------ */
+/* Indexed permute + ranged dispatch -- [FS] 4.2 (the indexed-permute kernel */
+/* applies the partition to the gathered IDs; the ranged-dispatch kernel    */
+/* prepares the ID AllToAll's per-destination ranges) and 3.2 (batch-major  */
+/* vs shard-major forms).                                                   */
+/*                                                                          */
+/*  ids            [T][n_tok] int64, table-major: ids[t*n_tok + k] is table t's */
+/*                 ID of token k of the unbalanced batch.                   */
+/*  sample_offsets [n+1] int64: sample s owns tokens [so[s], so[s+1]) (UIH   */
+/*                 tokens, then candidate tokens). so[n] must equal n_tok.   */
+/*  tables         host [T]: rows and dim are read (weights may be NULL).    */
+/*  perm, rank_offsets: a balance call's output for the same n and W.        */
+/* Outputs:                                                                  */
+/*  bal_offsets    [n+1] int64: the q-th balanced sample s = perm[q] owns     */
+/*                 batch-major tokens [bal[q], bal[q+1]); token j of it has   */
+/*                 batch-major index bm = bal[q] + j.                          */
+/*  shard_keys     [T*n_tok] int64, shard_bm [T*n_tok] int32: every valid    */
+/*                 (table, token) item as key = row_base_t + id and its bm,  */
+/*                 in shard-major order: destination shard d, then source    */
+/*                 rank r, then table t, then balanced sample, then token    */
+/*                 (what a W-way AllToAll of per-destination, table-major     */
+/*                 send buffers delivers). Entries past shard_offsets[W] are  */
+/*                 unspecified.                                               */
+/*  splits         [W*W] int64: splits[d*W + r] = items rank r sends to d.    */
+/*  shard_offsets  [W+1] int64: shard d's items are [so_d, so_{d+1}).        */
+/*  err            IDs outside [0, rows_t) are dropped (FS_EF_ID_RANGE); a   */
+/*                 bad so[n] flags FS_EF_SHAPE and the output is undefined.  */
+int fs_bucketize_permute(const int64_t* ids, int64_t n_tok, const int64_t* sample_offsets,
+                         int32_t n, const fs_table* tables, int32_t T, const int32_t* perm,
+                         const int32_t* rank_offsets, int32_t W, int64_t* bal_offsets,
+                         int64_t* shard_keys, int32_t* shard_bm, int64_t* splits,
+                         int64_t* shard_offsets, int32_t* err, void* ws, size_t ws_bytes,
+                         hipStream_t stream);
+
+size_t fs_bucketize_workspace_size(int64_t n_tok, int32_t n, int32_t T, int32_t W);
+
+/* ------------------------------------------------------------------------ */
+/* Dedup + collision split -- [FS] 3.2 and Algorithm 2 (compute_collision on */
+/* the shard-major indices of iterations i and i+1): a row of iteration i+1 */
+/* collides when iteration i updates it; only those rows need the write-    */
+/* then-read order, every other (exclusive) row can be fetched ahead.       */
+/*                                                                          */
+/*  shard_keys, shard_bm, shard_offsets: a bucketize call's output.          */
+/*  n_cap          host: capacity of the shard arrays (T*n_tok).             */
+/*  prev_unique, prev_counts: the previous call's unique and counts (device), */
+/*                 or both NULL for the first iteration (all rows exclusive). */
+/*  prev_cap       host: capacity of prev_unique / prev_cls (0 when NULL).   */
+/* Outputs (capacities n_cap unless noted):                                  */
+/*  unique         int64 unique keys, ascending (= by table, then row). The   */
+/*                 rows of (table t, shard d) are the contiguous range        */
+/*                 unique_offsets[t*W+d] .. unique_offsets[t*W+d+1].          */
+/*  unique_offsets [T*W+1] int64; the last entry is U.                        */
+/*  seg_offsets    [n_cap+1] int32 CSR: unique row u's occurrences are        */
+/*                 occ_bm[seg_offsets[u] .. seg_offsets[u+1]).                */
+/*  occ_bm         int32 batch-major index of each occurrence, ascending      */
+/*                 within each row.                                           */
+/*  occ_uid        int32 unique index of each occurrence (CSR order).          */
+/*  cls            uint8 [U]: FS_COLLISION if the row is in prev_unique.      */
+/*  prev_cls       uint8 [prev U] (NULL when prev_unique is NULL):            */
+/*                 FS_COLLISION if the previous row is in unique.             */
+/*  counts         [4] int64: U, collisions C, U - C, prev U - C.             */
+int fs_unique_collision_split(const int64_t* shard_keys, const int32_t* shard_bm,
+                              const int64_t* shard_offsets, int64_t n_cap,
+                              const fs_table* tables, int32_t T, int32_t W,
+                              const int64_t* prev_unique, const int64_t* prev_counts,
+                              int64_t prev_cap, int64_t* unique, int64_t* unique_offsets,
+                              int32_t* seg_offsets, int32_t* occ_bm, int32_t* occ_uid,
+                              uint8_t* cls, uint8_t* prev_cls, int64_t* counts, void* ws,
+                              size_t ws_bytes, hipStream_t stream);
+
+size_t fs_unique_workspace_size(int64_t n_cap, int32_t T, int32_t W);
+
+/* ------------------------------------------------------------------------ */
+/* Jagged lookup -- Algorithm 2's Lookup, the batch-major transform that     */
+/* follows it, and merge: every occurrence of a unique row of class `which`  */
+/* (FS_ALL, FS_EXCLUSIVE or FS_COLLISION) gets a bit copy of the row, at its */
+/* batch-major slot: out[t][bm] = weights_t[unique - row_base_t]. Other rows */
+/* of out are not written.                                                   */
+/*  tables   host [T] (weights, rows, dim, dtype are read).                  */
+/*  unique .. occ_uid, cls: the split call's outputs for this iteration      */
+/*           (cls may be NULL when which == FS_ALL).                          */
+/*  out      host [T] of device [n_tok][dim_t] pointers, table dtype.         */
+/* Row sizes dim_t * sizeof(dtype) must be 64, 128, 256, 512, 1024 or 2048    */
+/* bytes (else FS_ERR_UNSUPPORTED).                                           */
+int fs_jagged_lookup(const fs_table* tables, int32_t T, int32_t W, const int64_t* unique,
+                     const int64_t* unique_offsets, const int32_t* seg_offsets,
+                     const int32_t* occ_bm, const int32_t* occ_uid, const uint8_t* cls,
+                     int32_t which, void* const* out, int64_t n_tok, hipStream_t stream);
+
+/* ------------------------------------------------------------------------ */
+/* Gradient segment-reduce + row update -- Algorithm 2's backward (split the */
+/* batch-major gradients into collision and exclusive parts, send them to    */
+/* the shards, update_embedding) and its forward (the previous iteration's   */
+/* exclusive rows are updated before the next exchange). For every unique    */
+/* row u of class `which`: g_u = sum over its occurrences of grad[t][bm]     */
+/* (fp64 accumulation in CSR order, rounded once to fp32), then              */
+/*   FS_SGD:        w -= lr * g                                              */
+/*   FS_RW_ADAGRAD: s += mean_d(g_d^2); w -= lr / (sqrt(s) + eps) * g        */
+/* in fp32 with one rounding per operation; bf16 rows are widened exactly and */
+/* stored round-to-nearest-even. Collision rows must be updated before the   */
+/* next iteration's lookup of the same rows ([FS] 3.2).                      */
+/*  grad         host [T] of device fp32 [n_tok][dim_t], batch-major.         */
+/*  cls          the class of THIS iteration's rows against the next one: the */
+/*               next split call's prev_cls (NULL with which == FS_ALL).      */
+/*  reduced_out  host [T] of device fp32 [U_t][dim_t] (or NULL array / NULL   */
+/*               entries): row u of table t is written at u - unique_offsets[t*W]. */
+/* dim_t must be a multiple of 64 in [64, 1024] (else FS_ERR_UNSUPPORTED);    */
+/* FS_RW_ADAGRAD needs every table's state.                                   */
+int fs_grad_reduce_update(const fs_table* tables, int32_t T, int32_t W,
+                          const float* const* grad, int64_t n_tok, const int64_t* unique,
+                          const int64_t* unique_offsets, const int32_t* seg_offsets,
+                          const int32_t* occ_bm, const int32_t* occ_uid, const uint8_t* cls,
+                          int32_t which, int32_t optim, float lr, float eps,
+                          float* const* reduced_out, void* ws, size_t ws_bytes,
+                          hipStream_t stream);
+
+size_t fs_grad_reduce_update_workspace_size(int64_t n_tok, int32_t max_dim);
+
+/* ------------------------------------------------------------------------ */
+const char* fs_strerror(int code);
+int fs_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FS_SPARSE_H */

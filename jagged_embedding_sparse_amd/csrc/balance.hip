@@ -1,0 +1,193 @@
+// Sequence load balancing: FBS and VBS partition functions.
+//
+// "FreeScale: distributed training for sequence recommendation models",
+// section 4.1 (Partitioning Algorithms): both sort the global batch by UIH
+// length; FBS deals the sorted samples to ranks zig-zag, VBS cuts them into W
+// contiguous segments of about equal weight L^alpha. Inside the load-balancing
+// protocol of section 3.1 (Algorithm 1) every rank computes the same P from
+// the gathered lengths, so one GPU computing it is exactly what each rank does.
+//
+// Sort: the batch is small (n <= 16384) and every key (length, index) is
+// distinct, so the sorted position of sample s is the number of keys below
+// its own. One lane per sample counts over a slice of the batch, a workgroup
+// sums the 16 slices: O(n^2 / 64) wave instructions spread over n/64
+// workgroups, no passes, no atomics, stable by construction.
+#include "common.hpp"
+
+namespace fs {
+namespace {
+
+constexpr int kRankThreads = 1024;  // 16 waves, one comparand slice each
+
+__device__ __forceinline__ uint32_t clamp_len(int32_t L) {
+  return (uint32_t)(L < 0 ? 0 : (L > FS_MAX_UIH ? FS_MAX_UIH : L));
+}
+
+__device__ __forceinline__ uint64_t sort_key(int32_t L, int32_t s) {
+  return ((uint64_t)clamp_len(L) << 32) | (uint32_t)s;
+}
+
+__device__ __forceinline__ int64_t isqrt64(int64_t x) {
+  if (x <= 0) return 0;
+  int64_t r = (int64_t)sqrt((double)x);
+  while (r * r > x) --r;
+  while ((r + 1) * (r + 1) <= x) ++r;
+  return r;
+}
+
+// round(L^(num/den)) for den in {1, 2}, exact (half-integer powers are
+// integers or irrational, so there is no tie to break).
+__device__ __forceinline__ int64_t vbs_weight(int64_t L, int num, int den) {
+  if (den == 2 && (num & 1) == 0) {
+    num >>= 1;
+    den = 1;
+  }
+  int64_t p = 1;
+  for (int k = 0; k < num; ++k) p *= L;
+  if (den == 1) return p;
+  return (isqrt64(4 * p) + 1) / 2;
+}
+
+// FBS deal. Sorted position p goes to rank (round even ? p%W : W-1-p%W)
+// with round = p/W, as that rank's round-th sample; rank r's first slot is
+// r*F plus the ranks before it that got a sample in the final partial round.
+__device__ __forceinline__ int32_t fbs_rank_start(int32_t r, int32_t n, int32_t W) {
+  int32_t F = n / W, Rm = n % W;
+  int32_t extra = (F % 2 == 0) ? min(r, Rm) : max(0, r - (W - Rm));
+  return r * F + extra;
+}
+
+template <bool kFbs>
+__global__ void __launch_bounds__(kRankThreads)
+k_sort_place(const int32_t* __restrict__ len, int32_t n, int32_t W, int32_t* __restrict__ perm,
+             int32_t* __restrict__ rank_offsets, int64_t* __restrict__ wsorted, int anum,
+             int aden, int32_t* __restrict__ err) {
+  __shared__ int32_t part[kRankThreads / kWave][kWave];
+  const int w = threadIdx.x / kWave, l = lane();
+  const int nw = kRankThreads / kWave;
+  const int32_t s = blockIdx.x * kWave + l;
+  const bool valid = s < n;
+  const int32_t Ls = valid ? len[s] : 0;
+  if (w == 0) flag_err(err, valid && (Ls < 0 || Ls > FS_MAX_UIH), FS_EF_LEN_RANGE);
+  const uint64_t mine = sort_key(Ls, s);
+
+  const int32_t chunk = (n + nw - 1) / nw;
+  const int32_t c0 = w * chunk, c1 = min(n, c0 + chunk);
+  int32_t below = 0;
+  for (int32_t c = c0; c < c1; ++c) below += sort_key(len[c], c) < mine;
+  part[w][l] = below;
+  __syncthreads();
+
+  if (w == 0 && valid) {
+    int32_t p = 0;
+    for (int k = 0; k < nw; ++k) p += part[k][l];
+    if (kFbs) {
+      int32_t round = p / W, off = p % W;
+      int32_t r = (round % 2 == 0) ? off : (W - 1 - off);
+      perm[fbs_rank_start(r, n, W) + round] = s;
+    } else {
+      perm[p] = s;
+      wsorted[p] = vbs_weight(clamp_len(Ls), anum, aden);
+    }
+  }
+  if (kFbs && blockIdx.x == 0)
+    for (int32_t r = threadIdx.x; r <= W; r += kRankThreads)
+      rank_offsets[r] = r == W ? n : fbs_rank_start(r, n, W);
+}
+
+// VBS cuts: prefix sums S of the sorted weights, then for each rank r the
+// first k with W*S_k >= r*T (binary search; S is non-decreasing).
+constexpr int kCutThreads = 1024;
+
+__global__ void __launch_bounds__(kCutThreads)
+k_vbs_cut(const int64_t* __restrict__ wsorted, int32_t n, int32_t W, int64_t* __restrict__ S,
+          int32_t* __restrict__ rank_offsets, int64_t* __restrict__ rank_weight) {
+  __shared__ int64_t tmp[17];
+  __shared__ int32_t cut[FS_MAX_RANKS + 1];
+  const int32_t per = (n + kCutThreads - 1) / kCutThreads;
+  const int32_t k0 = min(n, (int32_t)threadIdx.x * per), k1 = min(n, k0 + per);
+  int64_t local = 0;
+  for (int32_t k = k0; k < k1; ++k) local += wsorted[k];
+  int64_t total;
+  int64_t run = block_excl_scan<int64_t>(local, tmp, &total);
+  for (int32_t k = k0; k < k1; ++k) {
+    S[k] = run;
+    run += wsorted[k];
+  }
+  if (threadIdx.x == 0) S[n] = total;
+  __syncthreads();
+  const int64_t T = total;
+  for (int32_t r = threadIdx.x; r <= W; r += kCutThreads) {
+    int32_t lo = 0, hi = n;  // answer in [0, n]
+    const int64_t goal = (int64_t)r * T;
+    while (lo < hi) {
+      int32_t mid = (lo + hi) >> 1;
+      if ((int64_t)W * S[mid] >= goal) hi = mid; else lo = mid + 1;
+    }
+    cut[r] = (r == W) ? n : lo;
+    rank_offsets[r] = cut[r];
+  }
+  __syncthreads();
+  if (rank_weight)
+    for (int32_t r = threadIdx.x; r < W; r += kCutThreads) rank_weight[r] = S[cut[r + 1]] - S[cut[r]];
+}
+
+int check_common(const int32_t* uih_len, int32_t n, int32_t W, const int32_t* perm,
+                 const int32_t* rank_offsets) {
+  if (n < 0 || n > FS_MAX_SAMPLES || W < 1 || W > FS_MAX_RANKS) return FS_ERR_INVALID_ARG;
+  if (!rank_offsets || (n > 0 && (!uih_len || !perm))) return FS_ERR_INVALID_ARG;
+  return FS_OK;
+}
+
+}  // namespace
+}  // namespace fs
+
+using namespace fs;
+
+extern "C" size_t fs_balance_workspace_size(int32_t n, int32_t W) {
+  (void)W;
+  Carve c(nullptr);
+  c.take<int64_t>((size_t)(n > 0 ? n : 1));      // sorted weights
+  c.take<int64_t>((size_t)(n > 0 ? n : 1) + 1);  // prefix sums
+  return c.used + 256;
+}
+
+extern "C" int fs_balance_fbs(const int32_t* uih_len, int32_t n, int32_t W, int32_t* perm,
+                              int32_t* rank_offsets, int32_t* err, void* ws, size_t ws_bytes,
+                              hipStream_t stream) {
+  (void)ws;
+  (void)ws_bytes;
+  int rc = check_common(uih_len, n, W, perm, rank_offsets);
+  if (rc) return rc;
+  int blocks = (int)cdiv(n, kWave);
+  if (blocks == 0) blocks = 1;  // still writes rank_offsets
+  hipLaunchKernelGGL(k_sort_place<true>, dim3(blocks), dim3(kRankThreads), 0, stream, uih_len, n,
+                     W, perm, rank_offsets, (int64_t*)nullptr, 0, 1, err);
+  FS_LAUNCH_CHECK();
+  return FS_OK;
+}
+
+extern "C" int fs_balance_vbs(const int32_t* uih_len, int32_t n, int32_t W, int32_t alpha_num,
+                              int32_t alpha_den, int32_t* perm, int32_t* rank_offsets,
+                              int64_t* rank_weight, int32_t* err, void* ws, size_t ws_bytes,
+                              hipStream_t stream) {
+  int rc = check_common(uih_len, n, W, perm, rank_offsets);
+  if (rc) return rc;
+  bool ok = (alpha_den == 1 && alpha_num >= 0 && alpha_num <= 2) ||
+            (alpha_den == 2 && alpha_num >= 0 && alpha_num <= 4);
+  if (!ok) return FS_ERR_UNSUPPORTED;
+  if (ws_bytes < fs_balance_workspace_size(n, W) || !ws) return FS_ERR_WORKSPACE;
+  Carve c(ws);
+  int64_t* wsorted = c.take<int64_t>((size_t)(n > 0 ? n : 1));
+  int64_t* S = c.take<int64_t>((size_t)(n > 0 ? n : 1) + 1);
+  if (n > 0) {
+    hipLaunchKernelGGL(k_sort_place<false>, dim3((int)cdiv(n, kWave)), dim3(kRankThreads), 0,
+                       stream, uih_len, n, W, perm, rank_offsets, wsorted, alpha_num, alpha_den,
+                       err);
+    FS_LAUNCH_CHECK();
+  }
+  hipLaunchKernelGGL(k_vbs_cut, dim3(1), dim3(kCutThreads), 0, stream, wsorted, n, W, S,
+                     rank_offsets, rank_weight);
+  FS_LAUNCH_CHECK();
+  return FS_OK;
+}

@@ -1,0 +1,123 @@
+// Device and host helpers shared by the gfx950 kernels of libfs_sparse.
+//
+// Wavefronts are 64 lanes wide (CDNA). Scans and match-by-value use ballots
+// and cross-lane shuffles; workgroup scans go through LDS.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fs_sparse.h"
+
+namespace fs {
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------- lanes
+__device__ __forceinline__ int lane() { return (int)__lane_id(); }
+
+// bits of the lanes below this one
+__device__ __forceinline__ uint64_t lanemask_lt() {
+  int l = lane();
+  return l == 0 ? 0ull : (~0ull >> (64 - l));
+}
+
+__device__ __forceinline__ int popc(uint64_t x) { return __popcll(x); }
+
+// lanes of the wave holding the same `bits`-bit value v (all lanes active)
+__device__ __forceinline__ uint64_t match_bits(uint32_t v, int bits) {
+  uint64_t m = ~0ull;
+  for (int b = 0; b < bits; ++b) {
+    uint64_t on = __ballot((v >> b) & 1u);
+    m &= ((v >> b) & 1u) ? on : ~on;
+  }
+  return m;
+}
+
+template <typename T>
+__device__ __forceinline__ T wave_incl_scan(T v) {
+  int l = lane();
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    T t = __shfl_up(v, d, kWave);
+    if (l >= d) v += t;
+  }
+  return v;
+}
+
+template <typename T>
+__device__ __forceinline__ T wave_sum(T v) {
+#pragma unroll
+  for (int d = kWave / 2; d > 0; d >>= 1) v += __shfl_xor(v, d, kWave);
+  return v;
+}
+
+// Exclusive scan over the workgroup (blockDim.x a multiple of 64, <= 1024).
+// `tmp` is LDS scratch of at least 17 elements. Returns the exclusive prefix;
+// *total receives the workgroup sum. Contains barriers: call uniformly.
+template <typename T>
+__device__ T block_excl_scan(T v, T* tmp, T* total) {
+  int w = threadIdx.x / kWave, nw = blockDim.x / kWave;
+  T inc = wave_incl_scan(v);
+  if (lane() == kWave - 1) tmp[w] = inc;
+  __syncthreads();
+  if (w == 0) {
+    T x = lane() < nw ? tmp[lane()] : T(0);
+    T xi = wave_incl_scan(x);
+    if (lane() < nw) tmp[lane()] = xi - x;
+    if (lane() == nw - 1) tmp[16] = xi;
+  }
+  __syncthreads();
+  T r = tmp[w] + inc - v;
+  *total = tmp[16];
+  __syncthreads();
+  return r;
+}
+
+// ---------------------------------------------------------------- errors
+__device__ __forceinline__ void flag_err(int32_t* err, bool bad, int bit) {
+  if (__ballot(bad) && err != nullptr) {
+    if (lane() == __ffsll((unsigned long long)__ballot(bad)) - 1) atomicOr(err, bit);
+  }
+}
+
+// ---------------------------------------------------------------- bf16
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) {
+  return __uint_as_float(h << 16);
+}
+
+// round-to-nearest-even of the top 16 bits; NaN stays a (quiet) NaN
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) return (u >> 16) | 0x40u;
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// ---------------------------------------------------------------- misc
+__host__ __device__ __forceinline__ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+__host__ __device__ __forceinline__ size_t align_up(size_t x, size_t a) {
+  return (x + a - 1) / a * a;
+}
+
+// bump allocator over a caller workspace
+struct Carve {
+  char* base;
+  size_t used = 0;
+  explicit Carve(void* b) : base((char*)b) {}
+  template <typename T>
+  T* take(size_t count) {
+    used = align_up(used, 256);
+    T* p = (T*)(base ? base + used : nullptr);
+    used += sizeof(T) * count;
+    return p;
+  }
+};
+
+}  // namespace fs
+
+#define FS_LAUNCH_CHECK()                         \
+  do {                                            \
+    if (hipGetLastError() != hipSuccess) return FS_ERR_HIP; \
+  } while (0)

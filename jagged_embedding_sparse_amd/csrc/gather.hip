@@ -1,0 +1,148 @@
+// Jagged embedding lookup: unique rows -> batch-major output slots.
+//
+// "FreeScale: distributed training for sequence recommendation models",
+// Algorithm 2: Lookup of the (exclusive or collision) rows, the AllToAll back
+// to batch-major form and the merge of both classes into one batch. On one
+// GPU the three fuse: each occurrence's batch-major slot receives a bit copy
+// of its row.
+//
+// Work is spread over occurrences in CSR order, not over unique rows: hot
+// rows (tens of thousands of occurrences under Zipf IDs) split evenly, and
+// consecutive occurrences of one row re-read it from L1/L2, so HBM sees
+// each unique row about once. A lane group of row_bytes/16 lanes (at most
+// 64) copies one row with 16-byte loads and streaming stores.
+#include "common.hpp"
+
+namespace fs {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;
+constexpr int kSteps = 8;  // rows in flight per lane group
+
+struct LookupArgs {
+  const char* weights;
+  char* out;
+  int64_t row_base;
+  int64_t n_cap;  // occurrences this table can have (n_tok)
+  const int64_t* unique;
+  const int64_t* unique_offsets;
+  const int32_t* seg_offsets;
+  const int32_t* occ_bm;
+  const int32_t* occ_uid;
+  const uint8_t* cls;
+  int32_t g_lo, g_hi;  // group range of the table: [t*W, (t+1)*W]
+  int32_t which;
+};
+
+template <int VPR>  // 16-byte vectors per row
+__global__ void __launch_bounds__(kThreads) k_lookup(LookupArgs a) {
+  constexpr int LPR = VPR < kWave ? VPR : kWave;  // lanes per row
+  constexpr int RPW = kWave / LPR;                // rows per wave step
+  constexpr int VPL = VPR / LPR;                  // vectors per lane
+  constexpr int OPW = RPW * kSteps;               // occurrences per wave
+  const int64_t o_lo = a.seg_offsets[a.unique_offsets[a.g_lo]];
+  const int64_t o_hi = a.seg_offsets[a.unique_offsets[a.g_hi]];
+  const int w = threadIdx.x / kWave;
+  const int grp = lane() / LPR, sub = lane() % LPR;
+  const int64_t ob = o_lo + ((int64_t)blockIdx.x * (kThreads / kWave) + w) * OPW;
+  if (ob >= o_hi) return;
+
+  u32x4 v[kSteps][VPL];
+  int64_t dst[kSteps];
+#pragma unroll
+  for (int s = 0; s < kSteps; ++s) {
+    const int64_t o = ob + s * RPW + grp;
+    dst[s] = -1;
+    if (o < o_hi) {
+      const int32_t u = a.occ_uid[o];
+      if (a.which < 0 || a.cls[u] == (uint8_t)a.which) {
+        const int64_t row = a.unique[u] - a.row_base;
+        const u32x4* src = (const u32x4*)(a.weights + row * (VPR * 16));
+#pragma unroll
+        for (int k = 0; k < VPL; ++k) v[s][k] = src[sub + k * LPR];
+        dst[s] = a.occ_bm[o];
+      }
+    }
+  }
+#pragma unroll
+  for (int s = 0; s < kSteps; ++s) {
+    if (dst[s] < 0) continue;
+    u32x4* d = (u32x4*)(a.out + dst[s] * (VPR * 16));
+#pragma unroll
+    for (int k = 0; k < VPL; ++k) __builtin_nontemporal_store(v[s][k], d + sub + k * LPR);
+  }
+}
+
+template <int VPR>
+int launch(const LookupArgs& a, hipStream_t stream) {
+  constexpr int LPR = VPR < kWave ? VPR : kWave;
+  constexpr int OPB = (kWave / LPR) * kSteps * (kThreads / kWave);
+  const int64_t blocks = cdiv(a.n_cap, OPB);
+  if (blocks == 0) return FS_OK;
+  hipLaunchKernelGGL(k_lookup<VPR>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
+  FS_LAUNCH_CHECK();
+  return FS_OK;
+}
+
+}  // namespace
+}  // namespace fs
+
+using namespace fs;
+
+extern "C" int fs_jagged_lookup(const fs_table* tables, int32_t T, int32_t W,
+                                const int64_t* unique, const int64_t* unique_offsets,
+                                const int32_t* seg_offsets, const int32_t* occ_bm,
+                                const int32_t* occ_uid, const uint8_t* cls, int32_t which,
+                                void* const* out, int64_t n_tok, hipStream_t stream) {
+  if (!tables || T < 1 || T > FS_MAX_TABLES || W < 1 || W > FS_MAX_RANKS || n_tok < 0 ||
+      (int64_t)T * n_tok >= (int64_t)INT32_MAX || !out || !unique_offsets || !seg_offsets)
+    return FS_ERR_INVALID_ARG;
+  if (which != FS_ALL && which != FS_EXCLUSIVE && which != FS_COLLISION) return FS_ERR_INVALID_ARG;
+  if (which != FS_ALL && !cls) return FS_ERR_INVALID_ARG;
+  if (n_tok > 0 && (!unique || !occ_bm || !occ_uid)) return FS_ERR_INVALID_ARG;
+  int64_t base = 0;
+  for (int t = 0; t < T; ++t) {
+    const fs_table& tb = tables[t];
+    if (tb.rows < 1 || tb.dim < 1 || (tb.dtype != FS_F32 && tb.dtype != FS_BF16))
+      return FS_ERR_INVALID_ARG;
+    if (n_tok > 0 && (!tb.weights || !out[t])) return FS_ERR_INVALID_ARG;
+    const int64_t rb = (int64_t)tb.dim * (tb.dtype == FS_F32 ? 4 : 2);
+    if (rb != 64 && rb != 128 && rb != 256 && rb != 512 && rb != 1024 && rb != 2048)
+      return FS_ERR_UNSUPPORTED;
+    base += tb.rows;
+  }
+  if (base > (int64_t)UINT32_MAX + 1) return FS_ERR_UNSUPPORTED;
+  base = 0;
+  for (int t = 0; t < T; ++t) {
+    const fs_table& tb = tables[t];
+    LookupArgs a;
+    a.weights = (const char*)tb.weights;
+    a.out = (char*)out[t];
+    a.row_base = base;
+    a.n_cap = n_tok;
+    a.unique = unique;
+    a.unique_offsets = unique_offsets;
+    a.seg_offsets = seg_offsets;
+    a.occ_bm = occ_bm;
+    a.occ_uid = occ_uid;
+    a.cls = cls;
+    a.g_lo = t * W;
+    a.g_hi = (t + 1) * W;
+    a.which = which;
+    base += tb.rows;
+    const int64_t rb = (int64_t)tb.dim * (tb.dtype == FS_F32 ? 4 : 2);
+    int rc;
+    switch (rb) {
+      case 64: rc = launch<4>(a, stream); break;
+      case 128: rc = launch<8>(a, stream); break;
+      case 256: rc = launch<16>(a, stream); break;
+      case 512: rc = launch<32>(a, stream); break;
+      case 1024: rc = launch<64>(a, stream); break;
+      default: rc = launch<128>(a, stream); break;
+    }
+    if (rc) return rc;
+  }
+  return FS_OK;
+}

@@ -1,0 +1,464 @@
+// Gradient segment-reduce per unique row, fused with the row-wise update.
+//
+// "FreeScale: distributed training for sequence recommendation models",
+// Algorithm 2: backward splits the batch-major gradients into collision and
+// exclusive parts and sends them to the row shards, where update_embedding
+// applies them; collision rows first, so the next iteration reads them
+// updated (section 3.2), exclusive rows at leisure. The optimizer is not
+// named on the pages; SGD and row-wise Adagrad are supported.
+//
+// g_u = sum of grad[bm] over u's occurrences, accumulated in fp64 and rounded
+// once to fp32, so the result does not depend on how the sum is split.
+// Zipf IDs make segment lengths span 1 .. ~10^5, so two paths:
+//   short rows (<= kLong occurrences): one lane group per row, grid-stride
+//     over the table's unique rows; the group sums and updates the row.
+//   long rows: the table's occurrence range is cut into chunks of kChunk;
+//     a wave streams each long row's piece of its chunk (all lane groups of
+//     the wave interleaved), updates rows that lie inside the chunk and
+//     leaves fp64 partials for the rest; a fix-up sums each row's partials
+//     in chunk order and updates it.
+// Lanes: a group of LPG = min(64, D/4) lanes covers a row, 4*CPL/4 columns
+// per lane (16-byte gradient loads); weights use the same column mapping.
+#include "common.hpp"
+
+namespace fs {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kLong = 64;     // longer segments take the chunked path
+constexpr int kChunk = 512;   // occurrences per long-path chunk (one wave)
+constexpr int kShortBlocks = 2048;
+
+struct RUArgs {
+  void* weights;
+  float* state;
+  const float* grad;
+  float* reduced;  // may be null
+  const int64_t* unique;
+  const int64_t* unique_offsets;
+  const int32_t* seg_offsets;
+  const int32_t* occ_bm;
+  const int32_t* occ_uid;
+  const uint8_t* cls;
+  double* partials;  // [chunks][2][D]
+  int64_t row_base;
+  int64_t n_cap;  // occurrences this table can have
+  int32_t g_lo, g_hi;
+  int32_t which, optim;
+  float lr, eps;
+};
+
+template <int D>
+struct Map {
+  static constexpr int LPG = (D / 4) < kWave ? (D / 4) : kWave;  // lanes per row
+  static constexpr int CPL = D / LPG;                            // columns per lane
+  static constexpr int NV = CPL / 4;                             // float4 per lane
+  static constexpr int GPW = kWave / LPG;                        // groups per wave
+  __device__ static int col(int sub, int v) { return 4 * (sub + v * LPG); }
+};
+
+__device__ __forceinline__ bool class_ok(const RUArgs& a, int64_t u) {
+  return a.which < 0 || a.cls[u] == (uint8_t)a.which;
+}
+
+template <int D>
+__device__ __forceinline__ void add_row(double (&acc)[Map<D>::CPL], const float* grad, int64_t bm,
+                                        int sub) {
+  using M = Map<D>;
+  const float4* p = (const float4*)(grad + bm * D);
+#pragma unroll
+  for (int v = 0; v < M::NV; ++v) {
+    const float4 g = p[sub + v * M::LPG];
+    acc[4 * v + 0] += (double)g.x;
+    acc[4 * v + 1] += (double)g.y;
+    acc[4 * v + 2] += (double)g.z;
+    acc[4 * v + 3] += (double)g.w;
+  }
+}
+
+// Weight columns of one lane, widened to fp32.
+template <int D, typename WT>
+struct RowW {
+  float w[Map<D>::CPL];
+};
+
+template <int D, typename WT>
+__device__ __forceinline__ void load_w(const RUArgs& a, int64_t row, int sub, RowW<D, WT>& r) {
+  using M = Map<D>;
+  if constexpr (sizeof(WT) == 4) {
+    const float4* w = (const float4*)((const float*)a.weights + row * D);
+#pragma unroll
+    for (int v = 0; v < M::NV; ++v) {
+      const float4 x = w[sub + v * M::LPG];
+      r.w[4 * v] = x.x;
+      r.w[4 * v + 1] = x.y;
+      r.w[4 * v + 2] = x.z;
+      r.w[4 * v + 3] = x.w;
+    }
+  } else {
+    const uint2* w = (const uint2*)((const uint16_t*)a.weights + row * D);
+#pragma unroll
+    for (int v = 0; v < M::NV; ++v) {
+      const uint2 x = w[sub + v * M::LPG];
+      r.w[4 * v] = bf16_bits_to_f32(x.x & 0xFFFFu);
+      r.w[4 * v + 1] = bf16_bits_to_f32(x.x >> 16);
+      r.w[4 * v + 2] = bf16_bits_to_f32(x.y & 0xFFFFu);
+      r.w[4 * v + 3] = bf16_bits_to_f32(x.y >> 16);
+    }
+  }
+}
+
+// Applies the optimizer to row u (weights already loaded into r) with the
+// group's fp64 sums. Every lane of the group calls it: the Adagrad sum of
+// squares is a reduction over the group's lanes (all of which hold the same
+// u and `active`).
+template <int D, typename WT>
+__device__ __forceinline__ void apply_row(const RUArgs& a, int64_t u, int64_t row, float st,
+                                          int sub, const double (&acc)[Map<D>::CPL],
+                                          RowW<D, WT>& r, bool active) {
+  using M = Map<D>;
+  float g[M::CPL];
+#pragma unroll
+  for (int c = 0; c < M::CPL; ++c) g[c] = (float)acc[c];
+  float m = a.lr;
+  if (a.optim == FS_RW_ADAGRAD) {
+    double ss = 0.0;
+#pragma unroll
+    for (int c = 0; c < M::CPL; ++c) ss += (double)g[c] * (double)g[c];
+#pragma unroll
+    for (int off = M::LPG / 2; off > 0; off >>= 1) ss += __shfl_xor(ss, off, kWave);
+    if (active) {
+      const float mean_sq = (float)(ss / (double)D);
+      const float s = st + mean_sq;
+      if (sub == 0) a.state[row] = s;
+      const float denom = sqrtf(s) + a.eps;
+      m = a.lr / denom;
+    }
+  }
+  if (!active) return;
+  if (a.reduced) {
+    const int64_t lu = u - a.unique_offsets[a.g_lo];
+    float4* rp = (float4*)(a.reduced + lu * D);
+#pragma unroll
+    for (int v = 0; v < M::NV; ++v)
+      rp[sub + v * M::LPG] = make_float4(g[4 * v], g[4 * v + 1], g[4 * v + 2], g[4 * v + 3]);
+  }
+#pragma unroll
+  for (int c = 0; c < M::CPL; ++c) {
+    const float step = m * g[c];
+    r.w[c] = r.w[c] - step;
+  }
+  if constexpr (sizeof(WT) == 4) {
+    float4* w = (float4*)((float*)a.weights + row * D);
+#pragma unroll
+    for (int v = 0; v < M::NV; ++v)
+      w[sub + v * M::LPG] = make_float4(r.w[4 * v], r.w[4 * v + 1], r.w[4 * v + 2], r.w[4 * v + 3]);
+  } else {
+    uint2* w = (uint2*)((uint16_t*)a.weights + row * D);
+#pragma unroll
+    for (int v = 0; v < M::NV; ++v) {
+      uint2 x;
+      x.x = f32_to_bf16_bits(r.w[4 * v]) | (f32_to_bf16_bits(r.w[4 * v + 1]) << 16);
+      x.y = f32_to_bf16_bits(r.w[4 * v + 2]) | (f32_to_bf16_bits(r.w[4 * v + 3]) << 16);
+      w[sub + v * M::LPG] = x;
+    }
+  }
+}
+
+template <int D, typename WT>
+__device__ __forceinline__ void update_row(const RUArgs& a, int64_t u, int sub,
+                                           const double (&acc)[Map<D>::CPL], bool active) {
+  RowW<D, WT> r;
+  int64_t row = 0;
+  float st = 0.f;
+  if (active) {
+    row = a.unique[u] - a.row_base;
+    load_w<D, WT>(a, row, sub, r);
+    if (a.optim == FS_RW_ADAGRAD) st = a.state[row];
+  }
+  apply_row<D, WT>(a, u, row, st, sub, acc, r, active);
+}
+
+// ---------------------------------------------------------------- short rows
+// Grid-stride over the table's unique rows; each lane group takes R
+// consecutive rows per step and keeps all of their loads in flight:
+// offsets and keys, then first-occurrence index, weights and state, then
+// the gradient rows.
+template <int D, typename WT>
+__global__ void __launch_bounds__(kThreads) k_short(RUArgs a) {
+  using M = Map<D>;
+  constexpr int R = M::CPL <= 4 ? 4 : 2;
+  const int64_t u_lo = a.unique_offsets[a.g_lo], u_hi = a.unique_offsets[a.g_hi];
+  const int sub = lane() % M::LPG;
+  constexpr int64_t GPB = (kThreads / kWave) * M::GPW;  // groups per block
+  const int64_t local = threadIdx.x / M::LPG;
+  const int64_t NG = (int64_t)gridDim.x * GPB;
+  for (int64_t it = 0;; ++it) {
+    const int64_t g0 = (it * NG + (int64_t)blockIdx.x * GPB) * R;  // block's first row
+    if (u_lo + g0 >= u_hi) break;
+    const int64_t ub = u_lo + g0 + local * R;
+    int32_t lo[R], hi[R];
+    int64_t row[R];
+    bool act[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int64_t u = ub + r;
+      act[r] = u < u_hi;
+      lo[r] = act[r] ? a.seg_offsets[u] : 0;
+      hi[r] = act[r] ? a.seg_offsets[u + 1] : 0;
+      row[r] = act[r] ? a.unique[u] - a.row_base : 0;
+      if (act[r]) act[r] = (hi[r] - lo[r]) <= kLong && class_ok(a, u);
+    }
+    int32_t bm0[R];
+    RowW<D, WT> wr[R];
+    float st[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      bm0[r] = act[r] ? a.occ_bm[lo[r]] : 0;
+      st[r] = 0.f;
+      if (act[r]) {
+        load_w<D, WT>(a, row[r], sub, wr[r]);
+        if (a.optim == FS_RW_ADAGRAD) st[r] = a.state[row[r]];
+      }
+    }
+    double acc[R][M::CPL];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+#pragma unroll
+      for (int c = 0; c < M::CPL; ++c) acc[r][c] = 0.0;
+      if (act[r]) add_row<D>(acc[r], a.grad, bm0[r], sub);
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      if (act[r]) {
+        int32_t k = lo[r] + 1;
+        for (; k + 2 <= hi[r]; k += 2) {
+          const int32_t b0 = a.occ_bm[k], b1 = a.occ_bm[k + 1];
+          add_row<D>(acc[r], a.grad, b0, sub);
+          add_row<D>(acc[r], a.grad, b1, sub);
+        }
+        if (k < hi[r]) add_row<D>(acc[r], a.grad, a.occ_bm[k], sub);
+      }
+      apply_row<D, WT>(a, ub + r, row[r], st[r], sub, acc[r], wr[r], act[r]);
+    }
+  }
+}
+
+// ---------------------------------------------------------------- long rows
+template <int D, typename WT>
+__global__ void __launch_bounds__(kThreads) k_long(RUArgs a) {
+  using M = Map<D>;
+  const int64_t o_lo = a.seg_offsets[a.unique_offsets[a.g_lo]];
+  const int64_t o_hi = a.seg_offsets[a.unique_offsets[a.g_hi]];
+  const int64_t c = (int64_t)blockIdx.x * (kThreads / kWave) + threadIdx.x / kWave;
+  const int64_t cb = o_lo + c * kChunk;
+  if (cb >= o_hi) return;
+  const int64_t ce = min(cb + (int64_t)kChunk, o_hi);
+  const int grp = lane() / M::LPG, sub = lane() % M::LPG;
+  const int32_t u_first = a.occ_uid[cb], u_last = a.occ_uid[ce - 1];
+  for (int32_t ub = u_first; ub <= u_last; ub += kWave) {
+    const int32_t uu = ub + lane();
+    const bool in = uu <= u_last;
+    const int32_t lo = in ? a.seg_offsets[uu] : 0, hi = in ? a.seg_offsets[uu + 1] : 0;
+    uint64_t todo = __ballot(in && hi - lo > kLong && class_ok(a, uu));
+    while (todo) {
+      const int j = __ffsll((unsigned long long)todo) - 1;
+      todo &= todo - 1;
+      const int64_t s_lo = __shfl(lo, j, kWave), s_hi = __shfl(hi, j, kWave);
+      const int64_t u = ub + j;
+      const int64_t p0 = max(s_lo, cb), p1 = min(s_hi, ce);
+      double acc[M::CPL];
+#pragma unroll
+      for (int x = 0; x < M::CPL; ++x) acc[x] = 0.0;
+      int64_t o = p0 + grp;
+      for (; o + 3 * M::GPW < p1; o += 4 * M::GPW) {
+        const int32_t b0 = a.occ_bm[o], b1 = a.occ_bm[o + M::GPW];
+        const int32_t b2 = a.occ_bm[o + 2 * M::GPW], b3 = a.occ_bm[o + 3 * M::GPW];
+        add_row<D>(acc, a.grad, b0, sub);
+        add_row<D>(acc, a.grad, b1, sub);
+        add_row<D>(acc, a.grad, b2, sub);
+        add_row<D>(acc, a.grad, b3, sub);
+      }
+      for (; o < p1; o += M::GPW) add_row<D>(acc, a.grad, a.occ_bm[o], sub);
+      // combine the interleaved groups (fixed order)
+#pragma unroll
+      for (int off = M::LPG; off < kWave; off <<= 1)
+#pragma unroll
+        for (int x = 0; x < M::CPL; ++x) acc[x] += __shfl_xor(acc[x], off, kWave);
+      const bool complete = s_lo >= cb && s_hi <= ce;
+      if (complete) {
+        update_row<D, WT>(a, u, sub, acc, grp == 0);
+      } else if (grp == 0) {
+        const int slot = s_lo >= cb ? 1 : 0;
+        double* p = a.partials + ((c - 0) * 2 + slot) * D;
+#pragma unroll
+        for (int v = 0; v < M::NV; ++v)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) p[M::col(sub, v) + e] = acc[4 * v + e];
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- fix-up
+// Chunk c owns the long row that starts in it and runs past its end: sum the
+// row's partials (slot 1 of c, slot 0 of each later chunk it covers), four
+// waves in contiguous slices, combined in wave order.
+template <int D, typename WT>
+__global__ void __launch_bounds__(kThreads) k_fix(RUArgs a) {
+  using M = Map<D>;
+  __shared__ double part[kThreads / kWave][D];
+  const int64_t o_lo = a.seg_offsets[a.unique_offsets[a.g_lo]];
+  const int64_t o_hi = a.seg_offsets[a.unique_offsets[a.g_hi]];
+  const int64_t c = blockIdx.x;
+  const int64_t cb = o_lo + c * kChunk;
+  if (cb >= o_hi) return;
+  const int64_t ce = min(cb + (int64_t)kChunk, o_hi);
+  const int64_t u = a.occ_uid[ce - 1];
+  const int64_t s_lo = a.seg_offsets[u], s_hi = a.seg_offsets[u + 1];
+  if (!(s_hi - s_lo > kLong && s_lo >= cb && s_hi > ce && class_ok(a, u))) return;
+  const int64_t c_last = (s_hi - 1 - o_lo) / kChunk;  // slot 0 of chunks c+1..c_last
+  const int64_t n_parts = 1 + (c_last - c);
+  const int w = threadIdx.x / kWave;
+  const int grp = lane() / M::LPG, sub = lane() % M::LPG;
+  // part k of the row: k == 0 -> chunk c slot 1; k >= 1 -> chunk c+k slot 0
+  const int64_t per = cdiv(n_parts, kThreads / kWave);
+  const int64_t k0 = min(n_parts, w * per), k1 = min(n_parts, k0 + per);
+  double acc[M::CPL];
+#pragma unroll
+  for (int x = 0; x < M::CPL; ++x) acc[x] = 0.0;
+  for (int64_t k = k0 + grp; k < k1; k += M::GPW) {
+    const double* p = a.partials + ((c + k) * 2 + (k == 0 ? 1 : 0)) * D;
+#pragma unroll
+    for (int v = 0; v < M::NV; ++v)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[4 * v + e] += p[M::col(sub, v) + e];
+  }
+#pragma unroll
+  for (int off = M::LPG; off < kWave; off <<= 1)
+#pragma unroll
+    for (int x = 0; x < M::CPL; ++x) acc[x] += __shfl_xor(acc[x], off, kWave);
+  if (grp == 0) {
+#pragma unroll
+    for (int v = 0; v < M::NV; ++v)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) part[w][M::col(sub, v) + e] = acc[4 * v + e];
+  }
+  __syncthreads();
+  if (w == 0) {
+#pragma unroll
+    for (int x = 0; x < M::CPL; ++x) acc[x] = 0.0;
+    for (int ww = 0; ww < kThreads / kWave; ++ww)
+#pragma unroll
+      for (int v = 0; v < M::NV; ++v)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[4 * v + e] += part[ww][M::col(sub, v) + e];
+    update_row<D, WT>(a, u, sub, acc, grp == 0);
+  }
+}
+
+template <int D, typename WT>
+int launch_all(const RUArgs& a, hipStream_t stream) {
+  using M = Map<D>;
+  const int64_t groups_per_block = (kThreads / kWave) * M::GPW;
+  int64_t sb = cdiv(a.n_cap, groups_per_block);
+  if (sb > kShortBlocks) sb = kShortBlocks;
+  if (sb < 1) sb = 1;
+  hipLaunchKernelGGL((k_short<D, WT>), dim3((unsigned)sb), dim3(kThreads), 0, stream, a);
+  FS_LAUNCH_CHECK();
+  const int64_t chunks = cdiv(a.n_cap, kChunk);
+  if (chunks > 0) {
+    hipLaunchKernelGGL((k_long<D, WT>), dim3((unsigned)cdiv(chunks, kThreads / kWave)),
+                       dim3(kThreads), 0, stream, a);
+    FS_LAUNCH_CHECK();
+    hipLaunchKernelGGL((k_fix<D, WT>), dim3((unsigned)chunks), dim3(kThreads), 0, stream, a);
+    FS_LAUNCH_CHECK();
+  }
+  return FS_OK;
+}
+
+template <typename WT>
+int dispatch_dim(int dim, const RUArgs& a, hipStream_t stream) {
+  switch (dim) {
+    case 64: return launch_all<64, WT>(a, stream);
+    case 128: return launch_all<128, WT>(a, stream);
+    case 256: return launch_all<256, WT>(a, stream);
+    case 512: return launch_all<512, WT>(a, stream);
+    case 1024: return launch_all<1024, WT>(a, stream);
+  }
+  return FS_ERR_UNSUPPORTED;
+}
+
+bool dim_ok(int d) { return d == 64 || d == 128 || d == 256 || d == 512 || d == 1024; }
+
+}  // namespace
+}  // namespace fs
+
+using namespace fs;
+
+extern "C" size_t fs_grad_reduce_update_workspace_size(int64_t n_tok, int32_t max_dim) {
+  Carve c(nullptr);
+  c.take<double>((size_t)(cdiv(n_tok > 0 ? n_tok : 1, kChunk) * 2) * (size_t)max_dim);
+  return c.used + 256;
+}
+
+extern "C" int fs_grad_reduce_update(const fs_table* tables, int32_t T, int32_t W,
+                                     const float* const* grad, int64_t n_tok,
+                                     const int64_t* unique, const int64_t* unique_offsets,
+                                     const int32_t* seg_offsets, const int32_t* occ_bm,
+                                     const int32_t* occ_uid, const uint8_t* cls, int32_t which,
+                                     int32_t optim, float lr, float eps,
+                                     float* const* reduced_out, void* ws, size_t ws_bytes,
+                                     hipStream_t stream) {
+  if (!tables || T < 1 || T > FS_MAX_TABLES || W < 1 || W > FS_MAX_RANKS || n_tok < 0 ||
+      (int64_t)T * n_tok >= (int64_t)INT32_MAX || !grad || !unique_offsets || !seg_offsets)
+    return FS_ERR_INVALID_ARG;
+  if (which != FS_ALL && which != FS_EXCLUSIVE && which != FS_COLLISION) return FS_ERR_INVALID_ARG;
+  if (which != FS_ALL && !cls) return FS_ERR_INVALID_ARG;
+  if (optim != FS_SGD && optim != FS_RW_ADAGRAD) return FS_ERR_INVALID_ARG;
+  if (n_tok > 0 && (!unique || !occ_bm || !occ_uid)) return FS_ERR_INVALID_ARG;
+  int max_dim = 0;
+  int64_t base = 0;
+  for (int t = 0; t < T; ++t) {
+    const fs_table& tb = tables[t];
+    if (tb.rows < 1 || (tb.dtype != FS_F32 && tb.dtype != FS_BF16)) return FS_ERR_INVALID_ARG;
+    if (!dim_ok(tb.dim)) return FS_ERR_UNSUPPORTED;
+    if (n_tok > 0 && (!tb.weights || !grad[t])) return FS_ERR_INVALID_ARG;
+    if (optim == FS_RW_ADAGRAD && n_tok > 0 && !tb.state) return FS_ERR_INVALID_ARG;
+    max_dim = tb.dim > max_dim ? tb.dim : max_dim;
+    base += tb.rows;
+  }
+  if (base > (int64_t)UINT32_MAX + 1) return FS_ERR_UNSUPPORTED;
+  if (!ws || ws_bytes < fs_grad_reduce_update_workspace_size(n_tok, max_dim))
+    return FS_ERR_WORKSPACE;
+  base = 0;
+  for (int t = 0; t < T; ++t) {
+    const fs_table& tb = tables[t];
+    RUArgs a;
+    a.weights = tb.weights;
+    a.state = tb.state;
+    a.grad = grad[t];
+    a.reduced = reduced_out ? reduced_out[t] : nullptr;
+    a.unique = unique;
+    a.unique_offsets = unique_offsets;
+    a.seg_offsets = seg_offsets;
+    a.occ_bm = occ_bm;
+    a.occ_uid = occ_uid;
+    a.cls = cls;
+    a.partials = (double*)ws;
+    a.row_base = base;
+    a.n_cap = n_tok;
+    a.g_lo = t * W;
+    a.g_hi = (t + 1) * W;
+    a.which = which;
+    a.optim = optim;
+    a.lr = lr;
+    a.eps = eps;
+    base += tb.rows;
+    if (n_tok == 0) continue;
+    const int rc = tb.dtype == FS_F32 ? dispatch_dim<float>(tb.dim, a, stream)
+                                      : dispatch_dim<uint16_t>(tb.dim, a, stream);
+    if (rc) return rc;
+  }
+  return FS_OK;
+}

@@ -1,0 +1,480 @@
+// Per-shard dedup into CSR + collision/exclusive split.
+//
+// "FreeScale: distributed training for sequence recommendation models",
+// section 3.2 and Algorithm 2: the collision and exclusive index sets of
+// iterations i and i+1 are computed on the shard-major (post-AllToAll) IDs.
+//
+//  1. LSD radix sort of (key, bm) over the shard-major items, 8-bit digits,
+//     only as many passes as the key space needs. Every pass is a stable
+//     counting sort (per-tile histograms, per-digit column scans, per-tile
+//     ranked scatter), so equal keys keep their shard-major order, which for
+//     one key is ascending bm: the CSR's occurrence order falls out.
+//  2. Head flags (key differs from its left neighbour), one scan over tiles,
+//     compaction: unique keys, CSR segment starts, occurrence -> unique index,
+//     and the (table, shard) group offsets, written where the group changes.
+//  3. Set intersection of the new and previous unique lists by merge path:
+//     one search per 2048-element tile of the merged order, then exact
+//     membership tests inside LDS.
+#include "common.hpp"
+
+namespace fs {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kRounds = 16;
+constexpr int kWaveItems = kWave * kRounds;
+constexpr int kTile = kThreads * kRounds;  // 4096
+constexpr int kRadixBits = 8;
+constexpr int kRadix = 1 << kRadixBits;
+constexpr int kMaxPasses = 4;  // keys < 2^32
+
+struct Groups {
+  int64_t row_base[FS_MAX_TABLES + 1];
+  int64_t block[FS_MAX_TABLES];
+  int32_t T, W;
+};
+
+__device__ __forceinline__ int32_t group_of(uint32_t key, const Groups& g) {
+  int t = 0;
+  while (t + 1 < g.T && (int64_t)key >= g.row_base[t + 1]) ++t;
+  return t * g.W + (int32_t)(((int64_t)key - g.row_base[t]) / g.block[t]);
+}
+
+// Valid item count of the call: shard_offsets[W] clamped to the capacity the
+// host sized every buffer for (k_init stores it; later kernels read it).
+__device__ __forceinline__ int64_t n_valid_of(const int64_t* n_valid, int32_t W) {
+  (void)W;
+  return *n_valid;
+}
+
+// ---------------------------------------------------------------- init
+__global__ void k_init(uint32_t* __restrict__ tot, int n_tot, uint32_t* __restrict__ ticket,
+                       const int64_t* __restrict__ shard_offsets, int32_t W, int64_t n_cap,
+                       int64_t* __restrict__ n_valid) {
+  for (int i = threadIdx.x; i < n_tot; i += blockDim.x) tot[i] = 0;
+  if (threadIdx.x == 0) {
+    *ticket = 0;
+    const int64_t v = shard_offsets[W];
+    *n_valid = v < 0 ? 0 : (v > n_cap ? n_cap : v);
+  }
+}
+
+// ---------------------------------------------------------------- radix pass
+template <typename KIn>
+__global__ void __launch_bounds__(kThreads)
+k_rs_hist(const KIn* __restrict__ keys, const int64_t* __restrict__ nvp, int32_t W,
+          int shift, uint32_t mask, int64_t tiles_cap, uint32_t* __restrict__ hist,
+          uint32_t* __restrict__ tot) {
+  __shared__ uint32_t h[kRadix];
+  const int64_t n = n_valid_of(nvp, W);
+  const int64_t t0 = (int64_t)blockIdx.x * kTile;
+  if (t0 >= n) return;
+  h[threadIdx.x] = 0;  // kThreads == kRadix
+  __syncthreads();
+#pragma unroll 4
+  for (int i = 0; i < kRounds; ++i) {
+    const int64_t x = t0 + i * kThreads + threadIdx.x;
+    if (x < n) atomicAdd(&h[((uint32_t)keys[x] >> shift) & mask], 1u);
+  }
+  __syncthreads();
+  const uint32_t c = h[threadIdx.x];
+  hist[(int64_t)threadIdx.x * tiles_cap + blockIdx.x] = c;
+  if (c) atomicAdd(&tot[threadIdx.x], c);
+}
+
+__global__ void __launch_bounds__(kThreads)
+k_rs_scan(const int64_t* __restrict__ nvp, int32_t W, int64_t tiles_cap,
+          uint32_t* __restrict__ hist, const uint32_t* __restrict__ tot) {
+  __shared__ int64_t tmp[17];
+  const int32_t b = blockIdx.x;
+  const int64_t lower = threadIdx.x < b ? (int64_t)tot[threadIdx.x] : 0;
+  int64_t base;
+  (void)block_excl_scan<int64_t>(lower, tmp, &base);
+  const int64_t n_tiles = cdiv(n_valid_of(nvp, W), kTile);
+  uint32_t* col = hist + (int64_t)b * tiles_cap;
+  int64_t carry = base;
+  for (int64_t c0 = 0; c0 < n_tiles; c0 += kThreads) {
+    const int64_t c = c0 + threadIdx.x;
+    const int64_t v = c < n_tiles ? col[c] : 0;
+    int64_t sum;
+    const int64_t ex = block_excl_scan<int64_t>(v, tmp, &sum);
+    if (c < n_tiles) col[c] = (uint32_t)(carry + ex);
+    carry += sum;
+  }
+}
+
+template <typename KIn>
+__global__ void __launch_bounds__(kThreads)
+k_rs_scatter(const KIn* __restrict__ keys_in, const int32_t* __restrict__ vals_in,
+             const int64_t* __restrict__ nvp, int32_t W, int shift, uint32_t mask,
+             int nbits, int64_t tiles_cap, const uint32_t* __restrict__ hist,
+             uint32_t* __restrict__ keys_out, int32_t* __restrict__ vals_out) {
+  __shared__ uint32_t cnt[kThreads / kWave][kRadix];
+  const int64_t n = n_valid_of(nvp, W);
+  const int64_t t0 = (int64_t)blockIdx.x * kTile;
+  if (t0 >= n) return;
+  const int w = threadIdx.x / kWave;
+  for (int b = lane(); b < kRadix; b += kWave) cnt[w][b] = 0;
+  const uint64_t lt = lanemask_lt();
+  uint32_t key[kRounds], dig[kRounds], rk[kRounds];
+  int32_t val[kRounds];
+  const uint32_t none = mask + 1;  // lanes without an item (fits nbits + 1 bits)
+#pragma unroll
+  for (int i = 0; i < kRounds; ++i) {
+    const int64_t x = t0 + (int64_t)w * kWaveItems + i * kWave + lane();
+    const bool valid = x < n;
+    key[i] = valid ? (uint32_t)keys_in[x] : 0u;
+    val[i] = valid ? vals_in[x] : 0;
+    const uint32_t d = valid ? ((key[i] >> shift) & mask) : none;
+    dig[i] = d;
+    const uint64_t peers = match_bits(d, nbits + 1);
+    const uint32_t before = cnt[w][valid ? d : 0];
+    rk[i] = before + (uint32_t)popc(peers & lt);
+    if (valid && (peers & lt) == 0) cnt[w][d] = before + (uint32_t)popc(peers);
+  }
+  __syncthreads();
+  {
+    const int b = threadIdx.x;  // kThreads == kRadix
+    uint32_t run = 0;
+#pragma unroll
+    for (int x = 0; x < kThreads / kWave; ++x) {
+      const uint32_t c = cnt[x][b];
+      cnt[x][b] = run;
+      run += c;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kRounds; ++i) {
+    if (dig[i] == none) continue;
+    const int64_t pos = (int64_t)hist[(int64_t)dig[i] * tiles_cap + blockIdx.x] + cnt[w][dig[i]] + rk[i];
+    keys_out[pos] = key[i];
+    vals_out[pos] = val[i];
+  }
+}
+
+// ---------------------------------------------------------------- unique
+__global__ void __launch_bounds__(kThreads)
+k_heads(const uint32_t* __restrict__ sk, const int64_t* __restrict__ nvp, int32_t W,
+        uint32_t* __restrict__ tile_heads) {
+  __shared__ uint32_t tmp[kThreads / kWave];
+  const int64_t n = n_valid_of(nvp, W);
+  const int64_t t0 = (int64_t)blockIdx.x * kTile;
+  if (t0 >= n) return;
+  uint32_t c = 0;
+  for (int i = 0; i < kRounds; ++i) {
+    const int64_t x = t0 + i * kThreads + threadIdx.x;
+    if (x < n) c += (x == 0 || sk[x] != sk[x - 1]);
+  }
+  c = wave_sum(c);
+  if (lane() == 0) tmp[threadIdx.x / kWave] = c;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t s = 0;
+    for (int k = 0; k < kThreads / kWave; ++k) s += tmp[k];
+    tile_heads[blockIdx.x] = s;
+  }
+}
+
+__global__ void __launch_bounds__(1024)
+k_heads_scan(const int64_t* __restrict__ nvp, int32_t W, int32_t n_groups,
+             uint32_t* __restrict__ tile_heads, int64_t* __restrict__ counts,
+             int32_t* __restrict__ seg_offsets, int64_t* __restrict__ unique_offsets) {
+  __shared__ int64_t tmp[17];
+  const int64_t n = n_valid_of(nvp, W);
+  const int64_t n_tiles = cdiv(n, kTile);
+  int64_t carry = 0;
+  for (int64_t c0 = 0; c0 < n_tiles; c0 += blockDim.x) {
+    const int64_t c = c0 + threadIdx.x;
+    const int64_t v = c < n_tiles ? tile_heads[c] : 0;
+    int64_t sum;
+    const int64_t ex = block_excl_scan<int64_t>(v, tmp, &sum);
+    if (c < n_tiles) tile_heads[c] = (uint32_t)(carry + ex);
+    carry += sum;
+  }
+  if (threadIdx.x == 0) {
+    counts[0] = carry;  // U
+    counts[1] = 0;
+    counts[2] = 0;
+    counts[3] = 0;
+    seg_offsets[carry] = (int32_t)n;
+  }
+  if (carry == 0)
+    for (int32_t g = threadIdx.x; g <= n_groups; g += blockDim.x) unique_offsets[g] = 0;
+}
+
+// Blocked layout: thread x owns items [x*16, x*16+16) of the tile.
+__global__ void __launch_bounds__(kThreads)
+k_compact(const uint32_t* __restrict__ sk, const int64_t* __restrict__ nvp, Groups g,
+          const uint32_t* __restrict__ tile_base, const int64_t* __restrict__ counts,
+          int64_t* __restrict__ unique, int32_t* __restrict__ seg_offsets,
+          int32_t* __restrict__ occ_uid, int64_t* __restrict__ unique_offsets) {
+  __shared__ uint32_t tmp[17];
+  const int64_t n = n_valid_of(nvp, g.W);
+  const int64_t t0 = (int64_t)blockIdx.x * kTile;
+  if (t0 >= n) return;
+  const int64_t x0 = t0 + (int64_t)threadIdx.x * kRounds;
+  uint32_t k[kRounds];
+  uint32_t heads = 0;
+  uint32_t prev = x0 > 0 && x0 <= n ? sk[x0 - 1] : 0u;
+#pragma unroll
+  for (int i = 0; i < kRounds; ++i) {
+    const int64_t x = x0 + i;
+    k[i] = x < n ? sk[x] : 0u;
+    const bool h = x < n && (x == 0 || k[i] != prev);
+    heads |= (uint32_t)h << i;
+    prev = k[i];
+  }
+  uint32_t tile_total;
+  const uint32_t before = block_excl_scan<uint32_t>((uint32_t)__popc(heads), tmp, &tile_total);
+  const int64_t U = counts[0];
+  const int32_t n_groups = g.T * g.W;
+  int64_t uid = (int64_t)tile_base[blockIdx.x] + before - 1;
+#pragma unroll
+  for (int i = 0; i < kRounds; ++i) {
+    const int64_t x = x0 + i;
+    if (x >= n) break;
+    if ((heads >> i) & 1u) {
+      ++uid;
+      unique[uid] = (int64_t)k[i];
+      seg_offsets[uid] = (int32_t)x;
+      // group offsets: every group in (group(prev unique), group(this)] starts here
+      const int32_t gi = group_of(k[i], g);
+      const int32_t gp = uid == 0 ? -1 : group_of(x == 0 ? 0u : sk[x - 1], g);
+      for (int32_t q = gp + 1; q <= gi; ++q) unique_offsets[q] = uid;
+      if (uid == U - 1)
+        for (int32_t q = gi + 1; q <= n_groups; ++q) unique_offsets[q] = U;
+    }
+    occ_uid[x] = (int32_t)uid;
+  }
+}
+
+// ---------------------------------------------------------------- collision
+constexpr int kMergeThreads = 256;
+constexpr int kMergeTile = 2048;
+
+// Merged order of a (new) and b (prev) with ties taken from b first.
+// Returns how many a-elements are among the first d merged elements.
+__device__ __forceinline__ int64_t merge_split(const int64_t* a, int64_t na, const int64_t* b,
+                                               int64_t nb, int64_t d) {
+  int64_t lo = d > nb ? d - nb : 0, hi = d < na ? d : na;
+  while (lo < hi) {
+    const int64_t mid = (lo + hi) >> 1;
+    if (a[mid] < b[d - mid - 1]) lo = mid + 1; else hi = mid;
+  }
+  return lo;
+}
+
+__device__ __forceinline__ int lds_upper(const int64_t* s, int n, int64_t v) {  // # s <= v
+  int lo = 0, hi = n;
+  while (lo < hi) {
+    int mid = (lo + hi) >> 1;
+    if (s[mid] <= v) lo = mid + 1; else hi = mid;
+  }
+  return lo;
+}
+
+__device__ __forceinline__ int lds_lower(const int64_t* s, int n, int64_t v) {  // # s < v
+  int lo = 0, hi = n;
+  while (lo < hi) {
+    int mid = (lo + hi) >> 1;
+    if (s[mid] < v) lo = mid + 1; else hi = mid;
+  }
+  return lo;
+}
+
+__global__ void __launch_bounds__(kMergeThreads)
+k_collide(const int64_t* __restrict__ a, const int64_t* __restrict__ counts_a, int64_t cap_a,
+          const int64_t* __restrict__ b, const int64_t* __restrict__ counts_b, int64_t cap_b,
+          uint8_t* __restrict__ cls, uint8_t* __restrict__ prev_cls, int64_t* __restrict__ counts,
+          uint32_t* __restrict__ ticket) {
+  __shared__ int64_t sa[kMergeTile + 1], sb[kMergeTile + 1];
+  __shared__ int64_t span[4];
+  __shared__ uint32_t hits[kMergeThreads / kWave];
+  const int64_t na = min(counts_a[0], cap_a);
+  const int64_t nb = counts_b ? max((int64_t)0, min(counts_b[0], cap_b)) : 0;
+  const int64_t M = na + nb;
+  const int64_t d0 = (int64_t)blockIdx.x * kMergeTile;
+  uint32_t mine = 0;
+  if (d0 < M) {
+    if (threadIdx.x == 0) {
+      const int64_t d1 = min(M, d0 + kMergeTile);
+      const int64_t i0 = merge_split(a, na, b, nb, d0);
+      const int64_t i1 = merge_split(a, na, b, nb, d1);
+      span[0] = i0;
+      span[1] = i1;
+      span[2] = d0 - i0;
+      span[3] = d1 - i1;
+    }
+    __syncthreads();
+    const int64_t i0 = span[0], i1 = span[1], j0 = span[2], j1 = span[3];
+    const int ca = (int)(i1 - i0), cb = (int)(j1 - j0);
+    // sa[0] = a[i1] sentinel area is after the slice; sb holds b[j0-1] first
+    for (int x = threadIdx.x; x < ca; x += kMergeThreads) sa[x] = a[i0 + x];
+    for (int x = threadIdx.x; x < cb; x += kMergeThreads) sb[x + 1] = b[j0 + x];
+    if (threadIdx.x == 0) {
+      sb[0] = j0 > 0 ? b[j0 - 1] : INT64_MIN;  // b element before the slice
+      sa[ca] = i1 < na ? a[i1] : INT64_MAX;    // a element after the slice
+    }
+    __syncthreads();
+    // a side: a[i] collides iff the last b <= a[i] equals it
+    for (int x = threadIdx.x; x < ca; x += kMergeThreads) {
+      const int64_t v = sa[x];
+      const int jj = lds_upper(sb + 1, cb, v);  // b elements of the slice <= v
+      const int64_t last = sb[jj];              // sb[0] when none in the slice
+      const bool hit = (j0 + jj > 0) && last == v;
+      cls[i0 + x] = hit ? FS_COLLISION : FS_EXCLUSIVE;
+      mine += hit;
+    }
+    // b side: b[j] collides iff the first a >= b[j] equals it
+    for (int x = threadIdx.x; x < cb; x += kMergeThreads) {
+      const int64_t v = sb[x + 1];
+      const int ii = lds_lower(sa, ca, v);  // a elements of the slice < v
+      const bool hit = (i0 + ii < na) && sa[ii] == v;
+      prev_cls[j0 + x] = hit ? FS_COLLISION : FS_EXCLUSIVE;
+    }
+  }
+  mine = wave_sum(mine);
+  if (lane() == 0) hits[threadIdx.x / kWave] = mine;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t s = 0;
+    for (int k = 0; k < kMergeThreads / kWave; ++k) s += hits[k];
+    if (s) atomicAdd((unsigned long long*)&counts[1], (unsigned long long)s);
+    __threadfence();
+    const uint32_t arrived = atomicAdd(ticket, 1u);
+    if (arrived == gridDim.x - 1) {  // last block: every count is in
+      const int64_t C = (int64_t)atomicAdd((unsigned long long*)&counts[1], 0ull);
+      counts[2] = na - C;
+      counts[3] = nb - C;
+    }
+  }
+}
+
+}  // namespace
+}  // namespace fs
+
+using namespace fs;
+
+static int key_bits(int64_t key_space) {
+  int b = 1;
+  while (b < 32 && ((int64_t)1 << b) < key_space) ++b;
+  return b;
+}
+
+extern "C" size_t fs_unique_workspace_size(int64_t n_cap, int32_t T, int32_t W) {
+  (void)T;
+  (void)W;
+  const int64_t cap = n_cap > 0 ? n_cap : 1;
+  const int64_t tiles = cdiv(cap, kTile);
+  Carve c(nullptr);
+  c.take<uint32_t>((size_t)cap);                // keys A
+  c.take<uint32_t>((size_t)cap);                // keys B
+  c.take<int32_t>((size_t)cap);                 // vals A
+  c.take<int32_t>((size_t)cap);                 // vals B
+  c.take<uint32_t>((size_t)kRadix * tiles);     // histograms
+  c.take<uint32_t>((size_t)kRadix * kMaxPasses);  // digit totals
+  c.take<uint32_t>((size_t)tiles);              // heads per tile
+  c.take<uint32_t>(1);                          // ticket
+  c.take<int64_t>(1);                           // valid item count
+  return c.used + 256;
+}
+
+extern "C" int fs_unique_collision_split(const int64_t* shard_keys, const int32_t* shard_bm,
+                                         const int64_t* shard_offsets, int64_t n_cap,
+                                         const fs_table* tables, int32_t T, int32_t W,
+                                         const int64_t* prev_unique, const int64_t* prev_counts,
+                                         int64_t prev_cap, int64_t* unique,
+                                         int64_t* unique_offsets, int32_t* seg_offsets,
+                                         int32_t* occ_bm, int32_t* occ_uid, uint8_t* cls,
+                                         uint8_t* prev_cls, int64_t* counts, void* ws,
+                                         size_t ws_bytes, hipStream_t stream) {
+  if (n_cap < 0 || n_cap >= (int64_t)INT32_MAX || T < 1 || T > FS_MAX_TABLES || W < 1 ||
+      W > FS_MAX_RANKS || !tables || !shard_offsets || !unique_offsets || !seg_offsets ||
+      !counts)
+    return FS_ERR_INVALID_ARG;
+  if (n_cap > 0 && (!shard_keys || !shard_bm || !unique || !occ_bm || !occ_uid || !cls))
+    return FS_ERR_INVALID_ARG;
+  if ((prev_unique == nullptr) != (prev_counts == nullptr)) return FS_ERR_INVALID_ARG;
+  if (prev_unique && (prev_cap < 0 || !prev_cls)) return FS_ERR_INVALID_ARG;
+  if (!prev_unique) prev_cap = 0;
+  Groups g;
+  g.T = T;
+  g.W = W;
+  int64_t base = 0;
+  for (int t = 0; t < T; ++t) {
+    if (tables[t].rows < 1) return FS_ERR_INVALID_ARG;
+    g.row_base[t] = base;
+    g.block[t] = cdiv(tables[t].rows, W);
+    base += tables[t].rows;
+  }
+  g.row_base[T] = base;
+  if (base > (int64_t)UINT32_MAX + 1) return FS_ERR_UNSUPPORTED;
+  if (!ws || ws_bytes < fs_unique_workspace_size(n_cap, T, W)) return FS_ERR_WORKSPACE;
+
+  const int64_t cap = n_cap > 0 ? n_cap : 1;
+  const int64_t tiles = cdiv(cap, kTile);
+  Carve c(ws);
+  uint32_t* ka = c.take<uint32_t>((size_t)cap);
+  uint32_t* kb = c.take<uint32_t>((size_t)cap);
+  int32_t* va = c.take<int32_t>((size_t)cap);
+  int32_t* vb = c.take<int32_t>((size_t)cap);
+  uint32_t* hist = c.take<uint32_t>((size_t)kRadix * tiles);
+  uint32_t* tot = c.take<uint32_t>((size_t)kRadix * kMaxPasses);
+  uint32_t* tile_heads = c.take<uint32_t>((size_t)tiles);
+  uint32_t* ticket = c.take<uint32_t>(1);
+  int64_t* n_valid = c.take<int64_t>(1);
+
+  const int kbits = key_bits(base);
+  const int passes = (kbits + kRadixBits - 1) / kRadixBits;
+  hipLaunchKernelGGL(k_init, dim3(1), dim3(256), 0, stream, tot, kRadix * kMaxPasses, ticket,
+                     shard_offsets, W, n_cap, n_valid);
+  FS_LAUNCH_CHECK();
+  uint32_t* kbuf[2] = {ka, kb};
+  int32_t* vbuf[2] = {va, vb};
+  const unsigned grid = (unsigned)tiles;
+  for (int p = 0; p < passes; ++p) {
+    const int shift = p * kRadixBits;
+    const int bits = (kbits - shift) < kRadixBits ? (kbits - shift) : kRadixBits;
+    const uint32_t mask = (1u << bits) - 1u;
+    uint32_t* tp = tot + kRadix * p;
+    uint32_t* kout = kbuf[p & 1];
+    int32_t* vout = (p == passes - 1) ? occ_bm : vbuf[p & 1];
+    if (p == 0) {
+      hipLaunchKernelGGL(k_rs_hist<int64_t>, dim3(grid), dim3(kThreads), 0, stream, shard_keys,
+                         n_valid, W, shift, mask, tiles, hist, tp);
+    } else {
+      hipLaunchKernelGGL(k_rs_hist<uint32_t>, dim3(grid), dim3(kThreads), 0, stream,
+                         kbuf[(p - 1) & 1], n_valid, W, shift, mask, tiles, hist, tp);
+    }
+    FS_LAUNCH_CHECK();
+    hipLaunchKernelGGL(k_rs_scan, dim3(kRadix), dim3(kThreads), 0, stream, n_valid, W,
+                       tiles, hist, tp);
+    FS_LAUNCH_CHECK();
+    if (p == 0) {
+      hipLaunchKernelGGL(k_rs_scatter<int64_t>, dim3(grid), dim3(kThreads), 0, stream, shard_keys,
+                         shard_bm, n_valid, W, shift, mask, bits, tiles, hist, kout, vout);
+    } else {
+      hipLaunchKernelGGL(k_rs_scatter<uint32_t>, dim3(grid), dim3(kThreads), 0, stream,
+                         kbuf[(p - 1) & 1], vbuf[(p - 1) & 1], n_valid, W, shift, mask,
+                         bits, tiles, hist, kout, vout);
+    }
+    FS_LAUNCH_CHECK();
+  }
+  const uint32_t* sk = kbuf[(passes - 1) & 1];
+  hipLaunchKernelGGL(k_heads, dim3(grid), dim3(kThreads), 0, stream, sk, n_valid, W,
+                     tile_heads);
+  FS_LAUNCH_CHECK();
+  hipLaunchKernelGGL(k_heads_scan, dim3(1), dim3(1024), 0, stream, n_valid, W, T * W,
+                     tile_heads, counts, seg_offsets, unique_offsets);
+  FS_LAUNCH_CHECK();
+  hipLaunchKernelGGL(k_compact, dim3(grid), dim3(kThreads), 0, stream, sk, n_valid, g,
+                     tile_heads, counts, unique, seg_offsets, occ_uid, unique_offsets);
+  FS_LAUNCH_CHECK();
+  const int64_t merge_blocks = cdiv(cap + prev_cap, kMergeTile);
+  hipLaunchKernelGGL(k_collide, dim3((unsigned)merge_blocks), dim3(kMergeThreads), 0, stream,
+                     unique, counts, n_cap, prev_unique, prev_counts, prev_cap, cls, prev_cls, counts,
+                     ticket);
+  FS_LAUNCH_CHECK();
+  return FS_OK;
+}

@@ -1,0 +1,276 @@
+"""ctypes binding of libfs_sparse.so (the C ABI in include/fs_sparse.h).
+
+Argument marshalling only: every function takes torch tensors on the GPU,
+allocates any output the caller did not pass, hands raw pointers and the
+current HIP stream to the C call and raises on a non-zero return code. All
+computation happens in the library's HIP kernels; there is no fallback: if
+the library is missing, importing this module raises.
+"""
+
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.environ.get("FS_SPARSE_LIB", os.path.join(_HERE, "libfs_sparse.so"))
+
+FS_OK, FS_ERR_INVALID_ARG, FS_ERR_WORKSPACE, FS_ERR_HIP, FS_ERR_UNSUPPORTED = 0, -1, -2, -3, -4
+FS_EF_ID_RANGE, FS_EF_SHAPE, FS_EF_LEN_RANGE = 1, 2, 4
+FS_F32, FS_BF16 = 0, 1
+FS_SGD, FS_RW_ADAGRAD = 0, 1
+FS_ALL, FS_EXCLUSIVE, FS_COLLISION = -1, 0, 1
+FS_MAX_SAMPLES, FS_MAX_RANKS, FS_MAX_TABLES, FS_MAX_UIH = 16384, 1024, 8, 65535
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built: run `python __graft_entry__.py build` "
+                      "(or jagged_embedding_sparse_amd/build.py) first")
+
+
+class FsTable(C.Structure):
+    _fields_ = [("weights", C.c_void_p), ("state", C.c_void_p), ("rows", C.c_int64),
+                ("dim", C.c_int32), ("dtype", C.c_int32)]
+
+
+_L = C.CDLL(LIB_PATH)
+_P, _i32, _i64, _sz, _f = C.c_void_p, C.c_int32, C.c_int64, C.c_size_t, C.c_float
+_TP = C.POINTER(FsTable)
+
+
+def _sig(name, res, *args):
+    fn = getattr(_L, name)
+    fn.restype = res
+    fn.argtypes = list(args)
+    return fn
+
+
+_c_balance_fbs = _sig("fs_balance_fbs", C.c_int, _P, _i32, _i32, _P, _P, _P, _P, _sz, _P)
+_c_balance_vbs = _sig("fs_balance_vbs", C.c_int, _P, _i32, _i32, _i32, _i32, _P, _P, _P, _P, _P,
+                      _sz, _P)
+_c_balance_ws = _sig("fs_balance_workspace_size", _sz, _i32, _i32)
+_c_bucketize = _sig("fs_bucketize_permute", C.c_int, _P, _i64, _P, _i32, _TP, _i32, _P, _P, _i32,
+                    _P, _P, _P, _P, _P, _P, _P, _sz, _P)
+_c_bucketize_ws = _sig("fs_bucketize_workspace_size", _sz, _i64, _i32, _i32, _i32)
+_c_unique = _sig("fs_unique_collision_split", C.c_int, _P, _P, _P, _i64, _TP, _i32, _i32, _P, _P,
+                 _i64, _P, _P, _P, _P, _P, _P, _P, _P, _P, _sz, _P)
+_c_unique_ws = _sig("fs_unique_workspace_size", _sz, _i64, _i32, _i32)
+_c_lookup = _sig("fs_jagged_lookup", C.c_int, _TP, _i32, _i32, _P, _P, _P, _P, _P, _P, _i32,
+                 C.POINTER(_P), _i64, _P)
+_c_reduce = _sig("fs_grad_reduce_update", C.c_int, _TP, _i32, _i32, C.POINTER(_P), _i64, _P, _P,
+                 _P, _P, _P, _P, _i32, _i32, _f, _f, C.POINTER(_P), _P, _sz, _P)
+_c_reduce_ws = _sig("fs_grad_reduce_update_workspace_size", _sz, _i64, _i32)
+_c_strerror = _sig("fs_strerror", C.c_char_p, C.c_int)
+_c_version = _sig("fs_version", C.c_int)
+
+EXPORTED = ["fs_balance_fbs", "fs_balance_vbs", "fs_balance_workspace_size",
+            "fs_bucketize_permute", "fs_bucketize_workspace_size", "fs_unique_collision_split",
+            "fs_unique_workspace_size", "fs_jagged_lookup", "fs_grad_reduce_update",
+            "fs_grad_reduce_update_workspace_size", "fs_strerror", "fs_version"]
+
+
+class FsError(RuntimeError):
+    def __init__(self, fn, code):
+        super().__init__(f"{fn}: {strerror(code)} ({code})")
+        self.code = code
+
+
+def strerror(code: int) -> str:
+    return _c_strerror(int(code)).decode()
+
+
+def version() -> int:
+    return int(_c_version())
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    assert t.is_cuda and t.is_contiguous(), "device tensors must be contiguous CUDA tensors"
+    return t.data_ptr()
+
+
+def _stream(stream):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _check(fn, rc):
+    if rc != FS_OK:
+        raise FsError(fn, rc)
+
+
+def _dev():
+    return torch.device("cuda", torch.cuda.current_device())
+
+
+def _get(o, key, make):
+    """o[key] if present, else a fresh tensor from make() (evaluated lazily)."""
+    return o[key] if key in o and o[key] is not None else make()
+
+
+def _ws(nbytes, ws):
+    if ws is not None:
+        assert ws.numel() * ws.element_size() >= nbytes
+        return ws
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=_dev())
+
+
+def make_tables(weights, states=None):
+    """Host array of fs_table for a list of [rows, dim] weight tensors."""
+    T = len(weights)
+    arr = (FsTable * T)()
+    for t, w in enumerate(weights):
+        st = states[t] if states is not None else None
+        assert w.dtype in (torch.float32, torch.bfloat16) and w.dim() == 2
+        arr[t].weights = _ptr(w)
+        arr[t].state = _ptr(st) if st is not None else None
+        arr[t].rows = w.shape[0]
+        arr[t].dim = w.shape[1]
+        arr[t].dtype = FS_F32 if w.dtype == torch.float32 else FS_BF16
+    return arr
+
+
+def make_row_tables(rows, dims=None):
+    """Host fs_table array that only carries row counts (bucketize, unique)."""
+    T = len(rows)
+    arr = (FsTable * T)()
+    for t, r in enumerate(rows):
+        arr[t].rows = int(r)
+        arr[t].dim = int(dims[t]) if dims is not None else 0
+    return arr
+
+
+# ---------------------------------------------------------------------------- calls
+
+
+def balance_workspace_size(n, W):
+    return int(_c_balance_ws(n, W))
+
+
+def fs_balance_fbs(uih_len, W, perm=None, rank_offsets=None, err=None, ws=None, stream=None):
+    n = uih_len.numel()
+    perm = perm if perm is not None else torch.empty(n, dtype=torch.int32, device=_dev())
+    ro = rank_offsets if rank_offsets is not None else torch.empty(W + 1, dtype=torch.int32,
+                                                                   device=_dev())
+    _check("fs_balance_fbs", _c_balance_fbs(_ptr(uih_len), n, W, _ptr(perm), _ptr(ro), _ptr(err),
+                                            None, 0, _stream(stream)))
+    return perm, ro
+
+
+def fs_balance_vbs(uih_len, W, alpha=(3, 2), perm=None, rank_offsets=None, rank_weight=None,
+                   err=None, ws=None, stream=None):
+    n = uih_len.numel()
+    perm = perm if perm is not None else torch.empty(n, dtype=torch.int32, device=_dev())
+    ro = rank_offsets if rank_offsets is not None else torch.empty(W + 1, dtype=torch.int32,
+                                                                   device=_dev())
+    rw = rank_weight if rank_weight is not None else torch.empty(W, dtype=torch.int64,
+                                                                 device=_dev())
+    nb = balance_workspace_size(n, W)
+    ws = _ws(nb, ws)
+    _check("fs_balance_vbs", _c_balance_vbs(_ptr(uih_len), n, W, int(alpha[0]), int(alpha[1]),
+                                            _ptr(perm), _ptr(ro), _ptr(rw), _ptr(err), _ptr(ws),
+                                            ws.numel(), _stream(stream)))
+    return perm, ro, rw
+
+
+def bucketize_workspace_size(n_tok, n, T, W):
+    return int(_c_bucketize_ws(n_tok, n, T, W))
+
+
+def fs_bucketize_permute(ids, sample_offsets, rows, perm, rank_offsets, W, out=None, err=None,
+                         ws=None, stream=None):
+    """ids: int64 [T, n_tok]. Returns dict of bal_offsets, shard_keys, shard_bm, splits,
+    shard_offsets."""
+    T, n_tok = ids.shape
+    n = sample_offsets.numel() - 1
+    d = _dev()
+    o = out or {}
+    bal = _get(o, "bal_offsets", lambda: torch.empty(n + 1, dtype=torch.int64, device=d))
+    keys = _get(o, "shard_keys", lambda: torch.empty(max(T * n_tok, 1), dtype=torch.int64, device=d))
+    bm = _get(o, "shard_bm", lambda: torch.empty(max(T * n_tok, 1), dtype=torch.int32, device=d))
+    splits = _get(o, "splits", lambda: torch.empty(W * W, dtype=torch.int64, device=d))
+    sho = _get(o, "shard_offsets", lambda: torch.empty(W + 1, dtype=torch.int64, device=d))
+    tabs = make_row_tables(rows)
+    ws = _ws(bucketize_workspace_size(n_tok, n, T, W), ws)
+    _check("fs_bucketize_permute",
+           _c_bucketize(_ptr(ids), n_tok, _ptr(sample_offsets), n, tabs, T, _ptr(perm),
+                        _ptr(rank_offsets), W, _ptr(bal), _ptr(keys), _ptr(bm), _ptr(splits),
+                        _ptr(sho), _ptr(err), _ptr(ws), ws.numel(), _stream(stream)))
+    return dict(bal_offsets=bal, shard_keys=keys, shard_bm=bm, splits=splits, shard_offsets=sho)
+
+
+def unique_workspace_size(n_cap, T, W):
+    return int(_c_unique_ws(n_cap, T, W))
+
+
+def fs_unique_collision_split(shard_keys, shard_bm, shard_offsets, n_cap, rows, W,
+                              prev_unique=None, prev_counts=None, prev_cap=0, out=None, ws=None,
+                              stream=None):
+    d = _dev()
+    T = len(rows)
+    cap = max(int(n_cap), 1)
+    o = out or {}
+    uq = _get(o, "unique", lambda: torch.empty(cap, dtype=torch.int64, device=d))
+    uo = _get(o, "unique_offsets", lambda: torch.empty(T * W + 1, dtype=torch.int64, device=d))
+    seg = _get(o, "seg_offsets", lambda: torch.empty(cap + 1, dtype=torch.int32, device=d))
+    occ_bm = _get(o, "occ_bm", lambda: torch.empty(cap, dtype=torch.int32, device=d))
+    occ_uid = _get(o, "occ_uid", lambda: torch.empty(cap, dtype=torch.int32, device=d))
+    cls = _get(o, "cls", lambda: torch.empty(cap, dtype=torch.uint8, device=d))
+    pcls = o.get("prev_cls", None)
+    if prev_unique is not None and pcls is None:
+        pcls = torch.empty(max(int(prev_cap), 1), dtype=torch.uint8, device=d)
+    counts = _get(o, "counts", lambda: torch.empty(4, dtype=torch.int64, device=d))
+    tabs = make_row_tables(rows)
+    ws = _ws(unique_workspace_size(n_cap, T, W), ws)
+    _check("fs_unique_collision_split",
+           _c_unique(_ptr(shard_keys), _ptr(shard_bm), _ptr(shard_offsets), int(n_cap), tabs, T,
+                     W, _ptr(prev_unique), _ptr(prev_counts), int(prev_cap) if prev_unique
+                     is not None else 0, _ptr(uq), _ptr(uo), _ptr(seg), _ptr(occ_bm),
+                     _ptr(occ_uid), _ptr(cls), _ptr(pcls) if prev_unique is not None else None,
+                     _ptr(counts), _ptr(ws), ws.numel(), _stream(stream)))
+    return dict(unique=uq, unique_offsets=uo, seg_offsets=seg, occ_bm=occ_bm, occ_uid=occ_uid,
+                cls=cls, prev_cls=pcls, counts=counts)
+
+
+def _ptr_array(ts):
+    arr = (C.c_void_p * len(ts))()
+    for i, t in enumerate(ts):
+        arr[i] = _ptr(t) if t is not None else None
+    return arr
+
+
+def fs_jagged_lookup(weights, W, uq, n_tok, which=FS_ALL, cls=None, out=None, stream=None):
+    """weights: list of [rows, dim] tensors; uq: the split call's outputs."""
+    d = _dev()
+    T = len(weights)
+    if out is None:
+        out = [torch.zeros((n_tok, w.shape[1]), dtype=w.dtype, device=d) for w in weights]
+    tabs = make_tables(weights)
+    cls_t = cls if cls is not None else uq.get("cls")
+    _check("fs_jagged_lookup",
+           _c_lookup(tabs, T, W, _ptr(uq["unique"]), _ptr(uq["unique_offsets"]),
+                     _ptr(uq["seg_offsets"]), _ptr(uq["occ_bm"]), _ptr(uq["occ_uid"]),
+                     _ptr(cls_t) if which != FS_ALL else None, which, _ptr_array(out), n_tok,
+                     _stream(stream)))
+    return out
+
+
+def reduce_workspace_size(n_tok, max_dim):
+    return int(_c_reduce_ws(n_tok, max_dim))
+
+
+def fs_grad_reduce_update(weights, states, W, grads, n_tok, uq, optim, lr, eps=0.0,
+                          which=FS_ALL, cls=None, reduced_out=None, ws=None, stream=None):
+    T = len(weights)
+    tabs = make_tables(weights, states)
+    max_dim = max(w.shape[1] for w in weights)
+    ws = _ws(reduce_workspace_size(n_tok, max_dim), ws)
+    red = _ptr_array(reduced_out) if reduced_out is not None else None
+    _check("fs_grad_reduce_update",
+           _c_reduce(tabs, T, W, _ptr_array(grads), n_tok, _ptr(uq["unique"]),
+                     _ptr(uq["unique_offsets"]), _ptr(uq["seg_offsets"]), _ptr(uq["occ_bm"]),
+                     _ptr(uq["occ_uid"]), _ptr(cls) if which != FS_ALL else None, which,
+                     FS_RW_ADAGRAD if optim in ("rw_adagrad", FS_RW_ADAGRAD) else FS_SGD,
+                     float(lr), float(eps), red, _ptr(ws), ws.numel(), _stream(stream)))

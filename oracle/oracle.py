@@ -262,23 +262,36 @@ class SyncRun:
         return dict(perm=perm, rank_offsets=ro, rank_weight=rw, bucket=bk, uniq=uq,
                     prev_cls=pcls, counts=counts)
 
-    def step(self, batch, grad_fn, optimize=True):
-        out = self.index_stages(batch)
+    def lookup_all(self, out, n_tok):
+        """Lookup of every unique row from the current rows (before the update)."""
         uq = out["uniq"]
-        n_tok = batch["n_tok"]
         W = self.w.world
-        emb, red = [], []
+        emb = []
         for t, st in enumerate(self.stores):
             lo = int(uq["unique_offsets"][t * W])
             hi = int(uq["unique_offsets"][(t + 1) * W])
             emb.append(lookup(st, int(self.row_base[t]), lo, hi, uq, n_tok))
-            if optimize:
-                G = grad_fn(t, n_tok, out["bucket"]["bal_offsets"])
-                g = reduce(st.dim, lo, hi, uq, G)
-                update(st, int(self.row_base[t]), lo, hi, uq["unique"], g, self.w.optim,
-                       self.w.lr, self.w.eps)
-                red.append(g)
-        self.prev_unique = uq["unique"]
-        out["emb"] = emb
-        out["reduced"] = red
+        return emb
+
+    def reduce_update(self, out, grads):
+        """Reduce the balanced batch-major gradients per unique row and update."""
+        uq = out["uniq"]
+        W = self.w.world
+        red = []
+        for t, st in enumerate(self.stores):
+            lo = int(uq["unique_offsets"][t * W])
+            hi = int(uq["unique_offsets"][(t + 1) * W])
+            g = reduce(st.dim, lo, hi, uq, grads[t])
+            update(st, int(self.row_base[t]), lo, hi, uq["unique"], g, self.w.optim, self.w.lr,
+                   self.w.eps)
+            red.append(g)
+        return red
+
+    def step(self, batch, grads_fn):
+        """One synchronous iteration. grads_fn(index_outputs) -> list of T
+        balanced batch-major fp32 gradients."""
+        out = self.index_stages(batch)
+        out["emb"] = self.lookup_all(out, batch["n_tok"])
+        out["reduced"] = self.reduce_update(out, grads_fn(out))
+        self.prev_unique = out["uniq"]["unique"]
         return out

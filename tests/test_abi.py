@@ -1,0 +1,131 @@
+"""The C ABI without a GPU: the library loads, exports every call the header
+declares, answers host-only queries and rejects bad arguments on the host
+(before any launch) with the documented return codes."""
+
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fs_sparse.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(fs_\w+)\s*\(", src,
+                                 flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    from jagged_embedding_sparse_amd import lib
+    return lib
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = _declared()
+    assert len(names) >= 12
+    raw = C.CDLL(L.LIB_PATH)
+    for n in names:
+        assert hasattr(raw, n), n
+    assert sorted(L.EXPORTED) == names
+
+
+def test_strerror_and_version(L):
+    assert L.strerror(0) == "ok"
+    for code in (-1, -2, -3, -4):
+        assert L.strerror(code) and L.strerror(code) != "unknown error"
+    assert L.strerror(-99) == "unknown error"
+    assert L.version() >= 1
+
+
+def test_workspace_queries_are_host_only_and_monotone(L):
+    assert L.balance_workspace_size(4096, 512) >= 4096 * 16
+    a = L.bucketize_workspace_size(1 << 20, 4096, 1, 512)
+    b = L.bucketize_workspace_size(1 << 22, 4096, 1, 512)
+    assert 0 < a < b
+    assert L.unique_workspace_size(1 << 22, 1, 512) >= 16 * (1 << 22)
+    assert L.reduce_workspace_size(1 << 20, 256) > L.reduce_workspace_size(1 << 20, 64)
+
+
+FAKE = 0x1000  # never dereferenced: every case below fails host-side validation
+
+
+def test_balance_rejects(L):
+    f = L._c_balance_fbs
+    assert f(None, 10, 4, None, None, None, None, 0, None) == L.FS_ERR_INVALID_ARG
+    assert f(FAKE, 10, 0, FAKE, FAKE, None, None, 0, None) == L.FS_ERR_INVALID_ARG
+    assert f(FAKE, 10, L.FS_MAX_RANKS + 1, FAKE, FAKE, None, None, 0, None) == L.FS_ERR_INVALID_ARG
+    assert f(FAKE, L.FS_MAX_SAMPLES + 1, 4, FAKE, FAKE, None, None, 0, None) == \
+        L.FS_ERR_INVALID_ARG
+    v = L._c_balance_vbs
+    assert v(FAKE, 10, 4, 1, 3, FAKE, FAKE, None, None, FAKE, 1 << 20, None) == \
+        L.FS_ERR_UNSUPPORTED
+    assert v(FAKE, 10, 4, 5, 2, FAKE, FAKE, None, None, FAKE, 1 << 20, None) == \
+        L.FS_ERR_UNSUPPORTED
+    assert v(FAKE, 10, 4, 3, 2, FAKE, FAKE, None, None, FAKE, 8, None) == L.FS_ERR_WORKSPACE
+
+
+def _tables(L, specs):
+    arr = (L.FsTable * len(specs))()
+    for i, (rows, dim, dt, st) in enumerate(specs):
+        arr[i].weights = FAKE
+        arr[i].state = FAKE if st else None
+        arr[i].rows = rows
+        arr[i].dim = dim
+        arr[i].dtype = dt
+    return arr
+
+
+def test_bucketize_rejects(L):
+    f = L._c_bucketize
+    tab = _tables(L, [(1000, 64, L.FS_F32, False)])
+    args = lambda T, ws_bytes, tabs=tab: f(FAKE, 100, FAKE, 8, tabs, T, FAKE, FAKE, 4, FAKE, FAKE,
+                                           FAKE, FAKE, FAKE, None, FAKE, ws_bytes, None)
+    assert args(0, 1 << 20) == L.FS_ERR_INVALID_ARG
+    assert args(L.FS_MAX_TABLES + 1, 1 << 20) == L.FS_ERR_INVALID_ARG
+    assert args(1, 16) == L.FS_ERR_WORKSPACE
+    big = _tables(L, [(1 << 31, 64, L.FS_F32, False), (1 << 31, 64, L.FS_F32, False),
+                      (8, 64, L.FS_F32, False)])
+    assert args(3, 1 << 30, big) == L.FS_ERR_UNSUPPORTED  # key space beyond 2^32
+    zero = _tables(L, [(0, 64, L.FS_F32, False)])
+    assert args(1, 1 << 20, zero) == L.FS_ERR_INVALID_ARG
+
+
+def test_unique_rejects(L):
+    f = L._c_unique
+    tab = _tables(L, [(1000, 64, L.FS_F32, False)])
+    call = lambda prev_u, prev_c, ws: f(FAKE, FAKE, FAKE, 100, tab, 1, 4, prev_u, prev_c, 100,
+                                        FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws,
+                                        None)
+    assert call(FAKE, None, 1 << 20) == L.FS_ERR_INVALID_ARG  # prev arrays come in pairs
+    assert call(None, None, 64) == L.FS_ERR_WORKSPACE
+
+
+def test_lookup_and_update_reject_unsupported_rows(L):
+    lk = L._c_lookup
+    outs = (C.c_void_p * 1)(FAKE)
+    for dim, dt in [(48, L.FS_F32), (100, L.FS_BF16), (8, L.FS_F32)]:
+        tab = _tables(L, [(1000, dim, dt, False)])
+        assert lk(tab, 1, 4, FAKE, FAKE, FAKE, FAKE, FAKE, None, L.FS_ALL, outs, 10, None) == \
+            L.FS_ERR_UNSUPPORTED
+    tab = _tables(L, [(1000, 64, L.FS_F32, False)])
+    assert lk(tab, 1, 4, FAKE, FAKE, FAKE, FAKE, FAKE, None, L.FS_COLLISION, outs, 10, None) == \
+        L.FS_ERR_INVALID_ARG  # class filter without classes
+    assert lk(tab, 1, 4, FAKE, FAKE, FAKE, FAKE, FAKE, None, 7, outs, 10, None) == \
+        L.FS_ERR_INVALID_ARG
+    ru = L._c_reduce
+    grads = (C.c_void_p * 1)(FAKE)
+    for dim in (96, 32, 2048):
+        tab = _tables(L, [(1000, dim, L.FS_F32, True)])
+        assert ru(tab, 1, 4, grads, 10, FAKE, FAKE, FAKE, FAKE, FAKE, None, L.FS_ALL, L.FS_SGD,
+                  0.1, 0.0, None, FAKE, 1 << 30, None) == L.FS_ERR_UNSUPPORTED
+    tab = _tables(L, [(1000, 128, L.FS_F32, False)])  # Adagrad needs state
+    assert ru(tab, 1, 4, grads, 10, FAKE, FAKE, FAKE, FAKE, FAKE, None, L.FS_ALL,
+              L.FS_RW_ADAGRAD, 0.1, 0.0, None, FAKE, 1 << 30, None) == L.FS_ERR_INVALID_ARG
+    tab = _tables(L, [(1000, 128, L.FS_F32, True)])
+    assert ru(tab, 1, 4, grads, 10, FAKE, FAKE, FAKE, FAKE, FAKE, None, L.FS_ALL,
+              L.FS_RW_ADAGRAD, 0.1, 0.0, None, FAKE, 8, None) == L.FS_ERR_WORKSPACE

@@ -1,0 +1,379 @@
+"""Per-call parity of the HIP path against the CPU oracle on seeded inputs.
+
+Index outputs are compared bit for bit; reduced gradients and updated rows
+to the tolerance the fp32 / bf16 arithmetic leaves (1e-5 fp32, 1e-2 bf16,
+relative to the size of the combined values). Sizes span several tiles and
+a ragged tail; edge cases cover empty and tiny batches, W > N, zero-token
+samples, dropped IDs, and hot rows long enough to cross many chunks.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from harness import host, snapshot_stores, store_vals_f32, rel_err_rows
+from jagged_embedding_sparse_amd import lib, synth
+from oracle import oracle as O
+
+pytestmark = pytest.mark.gpu
+
+
+def cu(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+
+
+# ----------------------------------------------------------------------------- balance
+
+BAL_CASES = [(64, 4), (512, 16), (1024, 64), (2048, 256), (4096, 512), (0, 3), (1, 1), (7, 8),
+             (10, 4), (6, 4), (100, 1024), (16384, 1024), (4097, 512)]
+
+
+def _lengths(N, seed, kind):
+    rng = np.random.default_rng(seed)
+    if kind == "ties":
+        return rng.integers(1, 40, size=N).astype(np.int32)
+    if kind == "zero":
+        return rng.integers(0, 3, size=N).astype(np.int32)
+    return np.minimum(np.ceil(rng.lognormal(6.5, 1.3, size=N)), 32768).astype(np.int32)
+
+
+@pytest.mark.parametrize("kind", ["ties", "skew", "zero"])
+@pytest.mark.parametrize("N,W", BAL_CASES)
+def test_fbs_parity(N, W, kind):
+    say("fbs", N, W, kind)
+    L = _lengths(N, N + W, kind)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    perm, ro = lib.fs_balance_fbs(cu(L), W, err=err)
+    operm, oro = O.balance_fbs(L, W)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(ro), oro)
+    assert np.array_equal(host(perm), operm)
+    assert int(err.item()) == 0
+
+
+@pytest.mark.parametrize("alpha", [(3, 2), (2, 1), (1, 1), (0, 1), (1, 2)])
+@pytest.mark.parametrize("N,W", BAL_CASES)
+def test_vbs_parity(N, W, alpha):
+    say("vbs", N, W, alpha)
+    L = _lengths(N, 3 * N + W, "skew")
+    perm, ro, rw = lib.fs_balance_vbs(cu(L), W, alpha)
+    operm, oro, orw = O.balance_vbs(L, W, alpha)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(perm), operm)
+    assert np.array_equal(host(ro), oro)
+    assert np.array_equal(host(rw), orw)
+
+
+def test_balance_length_range_is_clamped_and_flagged():
+    say("len-range")
+    L = np.array([5, -3, 70000, 12, 0, 65535], np.int32)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    perm, ro, rw = lib.fs_balance_vbs(cu(L), 2, (2, 1), err=err)
+    operm, oro, orw = O.balance_vbs(np.clip(L, 0, 65535), 2, (2, 1))
+    torch.cuda.synchronize()
+    assert int(err.item()) & lib.FS_EF_LEN_RANGE
+    assert np.array_equal(host(perm), operm) and np.array_equal(host(rw), orw)
+
+
+@pytest.mark.parametrize("k", [1, 2, 3, 4, 5])
+def test_balance_workload_lengths(k):
+    w = synth.WORKLOADS[k]
+    for it in range(3):
+        say("bal-workload", k, it)
+        L = synth.draw_lengths(w, k, it)
+        perm, ro = lib.fs_balance_fbs(cu(L), w.world)
+        operm, oro = O.balance_fbs(L, w.world)
+        vperm, vro, vrw = lib.fs_balance_vbs(cu(L), w.world, w.alpha)
+        ovp, ovro, ovrw = O.balance_vbs(L, w.world, w.alpha)
+        torch.cuda.synchronize()
+        assert np.array_equal(host(perm), operm) and np.array_equal(host(ro), oro)
+        assert np.array_equal(host(vperm), ovp) and np.array_equal(host(vro), ovro)
+        assert np.array_equal(host(vrw), ovrw)
+
+
+# ----------------------------------------------------------------------------- bucketize
+
+
+def _tiny_batch(seed, N, rows, maxlen=40, bad=0, zero_tok=0):
+    rng = np.random.default_rng(seed)
+    n_s = rng.integers(1, maxlen + 1, size=N)
+    if zero_tok:
+        n_s[rng.choice(N, size=min(zero_tok, N), replace=False)] = 0
+    so = np.concatenate([[0], np.cumsum(n_s)]).astype(np.int64)
+    n = int(so[-1])
+    ids = np.stack([rng.zipf(1.2, size=n) % r for r in rows]).astype(np.int64)
+    if bad and n:
+        pos = rng.choice(n, size=min(bad, n), replace=False)
+        ids[0, pos[::2]] = -1
+        ids[-1, pos[1::2]] = rows[-1] + 7
+    L = np.maximum(n_s - rng.integers(0, 2, size=N), 0).astype(np.int32)
+    return dict(uih_len=L, sample_offsets=so, ids=ids, n_tok=n)
+
+
+def _gpu_bucketize(b, rows, W, balancer="fbs", alpha=(3, 2)):
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    if balancer == "fbs":
+        perm, ro = lib.fs_balance_fbs(cu(b["uih_len"]), W, err=err)
+    else:
+        perm, ro, _ = lib.fs_balance_vbs(cu(b["uih_len"]), W, alpha, err=err)
+    bk = lib.fs_bucketize_permute(cu(b["ids"]), cu(b["sample_offsets"]), rows, perm, ro, W,
+                                  err=err)
+    return perm, ro, bk, err
+
+
+def _oracle_bucketize(b, rows, W, balancer="fbs", alpha=(3, 2)):
+    if balancer == "fbs":
+        perm, ro = O.balance_fbs(b["uih_len"], W)
+    else:
+        perm, ro, _ = O.balance_vbs(b["uih_len"], W, alpha)
+    return perm, ro, O.bucketize(b["ids"], b["sample_offsets"], rows, perm, ro, W)
+
+
+def _cmp_bucket(bk, obk):
+    nv = int(obk["shard_offsets"][-1])
+    assert np.array_equal(host(bk["bal_offsets"]), obk["bal_offsets"])
+    assert np.array_equal(host(bk["shard_offsets"]), obk["shard_offsets"])
+    assert np.array_equal(host(bk["splits"]).reshape(obk["splits"].shape), obk["splits"])
+    assert np.array_equal(host(bk["shard_keys"])[:nv], obk["shard_keys"])
+    assert np.array_equal(host(bk["shard_bm"])[:nv], obk["shard_bm"])
+
+
+BKT_CASES = [
+    # (seed, N, rows, W, maxlen, bad, zero_tok, balancer)
+    (1, 64, [100_000], 4, 60, 0, 0, "fbs"),
+    (2, 512, [10_000_000], 16, 200, 0, 0, "fbs"),
+    (3, 300, [5000, 70, 900_000], 7, 90, 0, 0, "vbs"),
+    (4, 50, [1000], 64, 30, 9, 3, "fbs"),          # W > N, dropped IDs, empty samples
+    (5, 2048, [20_000_000, 20_000_000, 20_000_000, 5_000_000], 256, 50, 0, 0, "vbs"),
+    (6, 1, [10], 3, 9000, 0, 0, "fbs"),            # one long sample, many tiles
+    (7, 40, [3], 8, 20, 0, 0, "fbs"),              # table smaller than W
+    (8, 4096, [200_000_000], 512, 120, 4, 0, "fbs"),
+    (9, 9, [1 << 20], 1024, 800, 0, 2, "vbs"),
+]
+
+
+@pytest.mark.parametrize("case", BKT_CASES, ids=lambda c: f"s{c[0]}")
+def test_bucketize_parity(case):
+    seed, N, rows, W, maxlen, bad, zt, bal = case
+    say("bucketize", case)
+    b = _tiny_batch(seed, N, rows, maxlen, bad, zt)
+    perm, ro, bk, err = _gpu_bucketize(b, rows, W, bal)
+    operm, oro, obk = _oracle_bucketize(b, rows, W, bal)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(perm), operm)
+    _cmp_bucket(bk, obk)
+    assert (int(err.item()) & lib.FS_EF_ID_RANGE) == (obk["err"] & 1)
+
+
+@pytest.mark.parametrize("k", [1, 2, 3, 4])
+def test_bucketize_workload_batch(k):
+    w = synth.WORKLOADS[k]
+    bt = synth.Batches(w, k)
+    rows = [t.rows for t in w.tables]
+    for it in range(2):
+        b = bt.batch(it)
+        for bal in ("fbs", "vbs"):
+            say("bucketize-workload", k, it, bal)
+            _, _, bk, err = _gpu_bucketize(b, rows, w.world, bal, w.alpha)
+            _, _, obk = _oracle_bucketize(b, rows, w.world, bal, w.alpha)
+            torch.cuda.synchronize()
+            _cmp_bucket(bk, obk)
+            assert int(err.item()) == 0
+
+
+def test_bucketize_bad_offsets_flag_shape():
+    say("bucketize-shape")
+    b = _tiny_batch(3, 20, [100], 10)
+    so = b["sample_offsets"].copy()
+    so[-1] += 5  # disagrees with n_tok
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    perm, ro = lib.fs_balance_fbs(cu(b["uih_len"]), 4)
+    bk = lib.fs_bucketize_permute(cu(b["ids"]), cu(so), [100], perm, ro, 4, err=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) & lib.FS_EF_SHAPE
+    assert np.all(host(bk["shard_offsets"]) == 0) and np.all(host(bk["splits"]) == 0)
+
+
+# ----------------------------------------------------------------------------- unique
+
+
+def _gpu_unique(bk, rows, W, n_cap, prev=None, prev_cap=0):
+    return lib.fs_unique_collision_split(
+        bk["shard_keys"], bk["shard_bm"], bk["shard_offsets"], n_cap, rows, W,
+        prev_unique=prev["unique"] if prev else None, prev_counts=prev["counts"] if prev else None,
+        prev_cap=prev_cap)
+
+
+def _cmp_unique(uq, ouq, cls, pcls, counts):
+    U = len(ouq["unique"])
+    assert int(host(uq["counts"])[0]) == U
+    assert np.array_equal(host(uq["counts"]), counts)
+    assert np.array_equal(host(uq["unique"])[:U], ouq["unique"])
+    assert np.array_equal(host(uq["unique_offsets"]), ouq["unique_offsets"])
+    assert np.array_equal(host(uq["seg_offsets"])[:U + 1], ouq["seg_offsets"])
+    n = len(ouq["occ_bm"])
+    assert np.array_equal(host(uq["occ_bm"])[:n], ouq["occ_bm"])
+    assert np.array_equal(host(uq["occ_uid"])[:n], ouq["occ_uid"])
+    assert np.array_equal(host(uq["cls"])[:U], cls)
+    if pcls is not None and len(pcls):
+        assert np.array_equal(host(uq["prev_cls"])[:len(pcls)], pcls)
+
+
+UQ_CASES = [(11, 64, [100_000], 4, 60), (12, 512, [300, 5000], 16, 200),
+            (13, 2048, [20_000, 20_000, 9000, 500], 256, 40), (14, 37, [50], 8, 30),
+            (15, 4096, [200_000_000], 512, 60), (16, 3, [7], 2, 3)]
+
+
+@pytest.mark.parametrize("case", UQ_CASES, ids=lambda c: f"s{c[0]}")
+def test_unique_collision_parity(case):
+    seed, N, rows, W, maxlen = case
+    T = len(rows)
+    prev, oprev, prev_cap = None, None, 0
+    for it in range(3):
+        say("unique", case, it)
+        b = _tiny_batch(seed * 10 + it, N, rows, maxlen, bad=2 if it == 1 else 0)
+        if it == 2:  # identical to the previous batch: every row collides
+            b = _tiny_batch(seed * 10 + 1, N, rows, maxlen, bad=2)
+        _, _, bk, _ = _gpu_bucketize(b, rows, W)
+        _, _, obk = _oracle_bucketize(b, rows, W)
+        n_cap = T * b["n_tok"]
+        uq = _gpu_unique(bk, rows, W, n_cap, prev, prev_cap)
+        ouq = O.unique(obk["shard_keys"], obk["shard_bm"], rows, W)
+        cls, pcls, counts = O.collision(ouq["unique"], oprev["unique"] if oprev else None)
+        torch.cuda.synchronize()
+        _cmp_unique(uq, ouq, cls, pcls if prev else None, counts)
+        if it == 2:
+            assert counts[1] == counts[0]
+        prev, oprev, prev_cap = uq, ouq, n_cap
+
+
+def test_unique_empty_batch():
+    say("unique-empty")
+    rows = [100]
+    b = dict(uih_len=np.zeros(4, np.int32), sample_offsets=np.zeros(5, np.int64),
+             ids=np.zeros((1, 0), np.int64), n_tok=0)
+    _, _, bk, _ = _gpu_bucketize(b, rows, 4)
+    uq = _gpu_unique(bk, rows, 4, 0)
+    torch.cuda.synchronize()
+    assert host(uq["counts"]).tolist() == [0, 0, 0, 0]
+    assert np.all(host(uq["unique_offsets"]) == 0)
+
+
+# ----------------------------------------------------------------------------- lookup + update
+
+
+def _csr_to_dev(ouq):
+    return {k: cu(v) for k, v in ouq.items()}
+
+
+def _table(rows, dim, dtype, seed):
+    return synth.init_table(rows, dim, dtype, seed, "cuda")
+
+
+LK_CASES = [([100_000], [64], ["f32"], 4), ([5000, 300], [128, 256], ["bf16", "f32"], 16),
+            ([4000, 4000, 9000, 20], [64, 128, 256, 64], ["f32"] * 4, 8),
+            ([777], [512], ["f32"], 2), ([3000], [1024], ["bf16"], 3), ([100], [32], ["f32"], 4),
+            ([200], [16], ["f32"], 4), ([1000], [512], ["bf16"], 5)]
+
+
+@pytest.mark.parametrize("case", LK_CASES, ids=lambda c: f"D{c[1]}")
+def test_lookup_parity(case):
+    rows, dims, dts, W = case
+    say("lookup", case)
+    b0 = _tiny_batch(21, 300, rows, 50)
+    b1 = _tiny_batch(22, 300, rows, 50)
+    ws = [_table(r, d, dt, 5 + t) for t, (r, d, dt) in enumerate(zip(rows, dims, dts))]
+    stores = snapshot_stores(ws, [None] * len(ws), [np.arange(r) for r in rows])
+    outs = {}
+    oq = []
+    for b in (b0, b1):
+        _, _, obk = _oracle_bucketize(b, rows, W)
+        oq.append(O.unique(obk["shard_keys"], obk["shard_bm"], rows, W))
+    cls1, _, _ = O.collision(oq[1]["unique"], oq[0]["unique"])
+    oq[1]["cls"] = cls1
+    n = b1["n_tok"]
+    for which in (lib.FS_ALL, lib.FS_COLLISION, lib.FS_EXCLUSIVE):
+        dq = _csr_to_dev(oq[1])
+        fill = [torch.full((n, d), 7, dtype=w.dtype, device="cuda") for d, w in zip(dims, ws)]
+        outs[which] = lib.fs_jagged_lookup(ws, W, dq, n, which=which, cls=dq["cls"], out=fill)
+    torch.cuda.synchronize()
+    rb = np.concatenate([[0], np.cumsum(rows)[:-1]])
+    for t, st in enumerate(stores):
+        lo, hi = int(oq[1]["unique_offsets"][t * W]), int(oq[1]["unique_offsets"][(t + 1) * W])
+        for which in (lib.FS_ALL, lib.FS_COLLISION, lib.FS_EXCLUSIVE):
+            sentinel = torch.full((1, dims[t]), 7, dtype=ws[t].dtype)
+            sentinel = (sentinel.view(torch.int16).numpy().view(np.uint16) if st.bf16
+                        else sentinel.numpy())
+            exp = np.broadcast_to(sentinel, (n, dims[t])).copy()
+            O.lookup(st, int(rb[t]), lo, hi, oq[1], n, which=which, out=exp)
+            got = outs[which][t]
+            got = host(got.view(torch.int16)).view(np.uint16) if st.bf16 else host(got)
+            assert np.array_equal(got, exp), (t, which)
+
+
+def _hot_batch(seed, rows, n_tok, hot):
+    """One sample per token; `hot` = [(row, count)] forced occurrences."""
+    rng = np.random.default_rng(seed)
+    ids = rng.integers(0, rows, size=n_tok).astype(np.int64)
+    pos = rng.permutation(n_tok)
+    k = 0
+    for r, c in hot:
+        ids[pos[k:k + c]] = r
+        k += c
+    so = np.arange(n_tok + 1, dtype=np.int64)
+    return dict(uih_len=np.ones(n_tok, np.int32), sample_offsets=so, ids=ids[None, :],
+                n_tok=n_tok)
+
+
+RU_CASES = [
+    # (dim, dtype, optim, hot, n_tok, W, rows)
+    (128, "f32", "sgd", [(3, 5000), (9, 700), (11, 65), (12, 64), (13, 513)], 16384, 8, 2000),
+    (128, "bf16", "rw_adagrad", [(3, 5000), (9, 700), (11, 65), (12, 64)], 16384, 8, 2000),
+    (64, "f32", "rw_adagrad", [(1, 3000), (2, 1025)], 12000, 4, 50_000),
+    (256, "f32", "sgd", [(5, 2000), (6, 600)], 9000, 16, 30_000),
+    (512, "bf16", "rw_adagrad", [(5, 1500)], 6000, 2, 3000),
+    (1024, "f32", "rw_adagrad", [(7, 900)], 4000, 3, 5000),
+    (128, "f32", "rw_adagrad", [], 10000, 4, 10_000_000),  # all rows short
+    (128, "f32", "sgd", [(0, 30000)], 30000, 4, 100),       # one row owns every token
+]
+
+
+@pytest.mark.parametrize("case", RU_CASES, ids=lambda c: f"D{c[0]}-{c[1]}-{c[2]}-{c[4]}")
+def test_reduce_update_parity(case):
+    dim, dt, optim, hot, n_tok, W, rows = case
+    say("reduce-update", case)
+    b = _hot_batch(dim + n_tok, rows, n_tok, hot)
+    _, _, obk = _oracle_bucketize(b, [rows], W)
+    ouq = O.unique(obk["shard_keys"], obk["shard_bm"], [rows], W)
+    U = len(ouq["unique"])
+    cls = (np.random.default_rng(1).random(U) < 0.5).astype(np.uint8)
+    grad = synth.gradient_rows(7, 0, 0, np.arange(n_tok), dim)
+    wt = _table(rows, dim, dt, 9)
+    st = torch.zeros(rows, dtype=torch.float32, device="cuda") if optim == "rw_adagrad" else None
+    stores = snapshot_stores([wt], [st], [np.unique(b["ids"][0])])
+    dq = _csr_to_dev(ouq)
+    dcls = cu(cls)
+    red = torch.full((U, dim), np.nan, dtype=torch.float32, device="cuda")
+    # collision rows first, then exclusive rows (two calls, as the schedule does)
+    for which in (lib.FS_COLLISION, lib.FS_EXCLUSIVE):
+        lib.fs_grad_reduce_update([wt], [st], W, [cu(grad)], n_tok, dq, optim, 0.05, 1e-8,
+                                  which=which, cls=dcls, reduced_out=[red])
+    g = O.reduce(dim, 0, U, ouq, grad)
+    prev = store_vals_f32(stores[0]).copy()
+    O.update(stores[0], 0, 0, U, ouq["unique"], g, optim, 0.05, 1e-8)
+    torch.cuda.synchronize()
+    gr = host(red)
+    assert np.array_equal(gr, g), float(np.nanmax(np.abs(gr - g)))  # exact fp64 sums
+    rid = stores[0].row_ids
+    got = host(wt.index_select(0, cu(rid)).float())
+    ref = store_vals_f32(stores[0])
+    tol = 1e-2 if dt == "bf16" else 1e-5
+    assert rel_err_rows(got, ref, prev) <= tol
+    if dt == "f32" and optim == "sgd":
+        assert np.array_equal(got, ref)
+    if optim == "rw_adagrad":
+        np.testing.assert_allclose(host(st.index_select(0, cu(rid))), stores[0].state, rtol=1e-6)

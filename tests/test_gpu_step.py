@@ -1,0 +1,208 @@
+"""End-to-end parity of the prioritized two-stream step against the oracle's
+synchronous loop, on the five seeded workloads at their full sizes.
+
+Per iteration: balance, bucketize, dedup, collision classes and counts are
+bit-exact; every lookup is a bit copy of the GPU's own current row and
+equals the oracle's lookup (bit-exact for fp32 SGD, within the update
+tolerance otherwise); after the last update every touched row matches the
+oracle within 1e-5 (fp32) / 1e-2 (bf16). The schedule test checks that the
+two-stream step is bit-identical to the one-stream synchronous step.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from harness import (balanced_grads, gpu_tables, host, rel_err_rows, rows_now, snapshot_stores,
+                     store_vals_f32, to_dev, touched_rows)
+from jagged_embedding_sparse_amd import synth
+from jagged_embedding_sparse_amd.step import SparseStep
+from oracle import oracle as O
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+
+
+def _bits(t):
+    return host(t.view(torch.int16)).view(np.uint16) if t.dtype == torch.bfloat16 else host(t)
+
+
+def _cmp_index(st, o, prev_o, prev_st, W, T, n_tok):
+    assert np.array_equal(host(st.perm), o["perm"])
+    assert np.array_equal(host(st.rank_offsets), o["rank_offsets"])
+    if o["rank_weight"] is not None:
+        assert np.array_equal(host(st.rank_weight), o["rank_weight"])
+    bk, obk = st.bucket, o["bucket"]
+    nv = int(obk["shard_offsets"][-1])
+    assert np.array_equal(host(bk["bal_offsets"]), obk["bal_offsets"])
+    assert np.array_equal(host(bk["shard_offsets"]), obk["shard_offsets"])
+    assert np.array_equal(host(bk["splits"]).reshape(W, W), obk["splits"])
+    assert np.array_equal(host(bk["shard_keys"])[:nv], obk["shard_keys"])
+    assert np.array_equal(host(bk["shard_bm"])[:nv], obk["shard_bm"])
+    uq, ouq = st.uq, o["uniq"]
+    U = len(ouq["unique"])
+    assert np.array_equal(host(uq["counts"]), o["counts"])
+    assert np.array_equal(host(uq["unique"])[:U], ouq["unique"])
+    assert np.array_equal(host(uq["unique_offsets"]), ouq["unique_offsets"])
+    assert np.array_equal(host(uq["seg_offsets"])[:U + 1], ouq["seg_offsets"])
+    assert np.array_equal(host(uq["occ_bm"])[:nv], ouq["occ_bm"])
+    assert np.array_equal(host(uq["occ_uid"])[:nv], ouq["occ_uid"])
+    assert np.array_equal(host(uq["cls"])[:U], ouq["cls"])
+    if prev_o is not None:
+        Up = len(prev_o["uniq"]["unique"])
+        assert np.array_equal(host(prev_st.cls_next)[:Up], o["prev_cls"])
+
+
+def _cmp_lookup(step, st, o, w, exact):
+    """GPU lookup == GPU current rows (bit copy) and == oracle lookup."""
+    worst = 0.0
+    for t in range(len(w.tables)):
+        got = st.out[t][:st.n_tok]
+        keys = st.uq["unique"][:int(o["counts"][0])]
+        # bit copy of the GPU's own rows: out[bm] == weights[key - row_base]
+        uq = o["uniq"]
+        lo, hi = int(uq["unique_offsets"][t * w.world]), int(uq["unique_offsets"][(t + 1) * w.world])
+        if hi > lo:
+            rb = int(step_rowbase(w)[t])
+            occ = slice(int(uq["seg_offsets"][lo]), int(uq["seg_offsets"][hi]))
+            bm = torch.from_numpy(uq["occ_bm"][occ].astype(np.int64)).cuda()
+            key = torch.from_numpy(uq["unique"][uq["occ_uid"][occ]] - rb).cuda()
+            a = got.index_select(0, bm)
+            b = step.weights[t].index_select(0, key)
+            assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a,
+                               b.view(torch.int16) if b.dtype == torch.bfloat16 else b)
+        del keys
+        g, ref = _bits(got), o["emb"][t]
+        if exact:
+            assert np.array_equal(g, ref), t
+        else:
+            gf = g.astype(np.uint32) << 16 if g.dtype == np.uint16 else None
+            gv = gf.view(np.float32) if gf is not None else g
+            rv = (ref.astype(np.uint32) << 16).view(np.float32) if ref.dtype == np.uint16 else ref
+            worst = max(worst, float(np.max(np.abs(gv - rv))) if gv.size else 0.0)
+    return worst
+
+
+def step_rowbase(w):
+    rows = np.array([t.rows for t in w.tables], np.int64)
+    return np.concatenate([[0], np.cumsum(rows)[:-1]])
+
+
+def run_parity(k, balancer=None, iters=None, seed=None):
+    w = synth.workload(k, balancer)
+    seed = k if seed is None else seed
+    K = iters or w.iterations
+    say("workload", k, w.name, w.balancer, "iterations", K)
+    bt = synth.Batches(w, seed)
+    batches = [bt.batch(i) for i in range(K)]
+    weights, states = gpu_tables(w, seed)
+    rows_t = touched_rows(batches, w)
+    stores = snapshot_stores(weights, states, rows_t)
+    init_vals = [store_vals_f32(s).copy() for s in stores]
+    # oracle: synchronous loop
+    orun = O.SyncRun(w, stores)
+    outs, grads = [], []
+    for i, b in enumerate(batches):
+        def gfn(o, i=i, b=b):
+            g = balanced_grads(w, seed, i, b, o["perm"], o["bucket"]["bal_offsets"])
+            grads.append(g)
+            return g
+        outs.append(orun.step(b, gfn))
+    say("oracle done")
+    # GPU: prioritized schedule
+    cap = max(b["n_tok"] for b in batches)
+    step = SparseStep(w, weights, states, cap)
+    exact = w.optim == "sgd" and all(t.dtype == "f32" for t in w.tables)
+    worst = 0.0
+    st = step.prologue(to_dev(batches[0]))
+    step.join()
+    torch.cuda.synchronize()
+    _cmp_index(st, outs[0], None, None, w.world, len(w.tables), batches[0]["n_tok"])
+    worst = max(worst, _cmp_lookup(step, st, outs[0], w, True))  # iteration 0: initial rows
+    for i in range(K - 1):
+        say("step", i)
+        prev = st
+        gdev = [torch.from_numpy(g).cuda() for g in grads[i]]
+        st = step.step(to_dev(batches[i + 1]), gdev)
+        step.join()
+        torch.cuda.synchronize()
+        _cmp_index(st, outs[i + 1], outs[i], prev, w.world, len(w.tables), batches[i + 1]["n_tok"])
+        worst = max(worst, _cmp_lookup(step, st, outs[i + 1], w, exact))
+    step.epilogue([torch.from_numpy(g).cuda() for g in grads[K - 1]])
+    step.join()
+    torch.cuda.synchronize()
+    tol = 1e-2 if any(t.dtype == "bf16" for t in w.tables) else 1e-5
+    for t, s in enumerate(stores):
+        got, gst = rows_now(weights, states, t, s.row_ids)
+        ref = store_vals_f32(s)
+        e = rel_err_rows(got, ref, init_vals[t])
+        say("table", t, "rows", len(s.row_ids), "max rel err", e, "lookup max abs diff", worst)
+        assert e <= tol
+        if exact:
+            assert np.array_equal(got, ref)
+        if gst is not None:
+            np.testing.assert_allclose(gst, s.state, rtol=1e-5, atol=0)
+    return outs
+
+
+def test_workload1_all_iterations():
+    run_parity(1)
+
+
+def test_workload2_all_iterations():
+    run_parity(2)
+
+
+@pytest.mark.timeout(600)
+def test_workload3_vbs():
+    run_parity(3, iters=4)
+
+
+@pytest.mark.timeout(600)
+def test_workload4_vbs_four_tables():
+    run_parity(4, iters=3)
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("bal", ["fbs", "vbs"])
+def test_workload5_full_size(bal):
+    run_parity(5, balancer=bal, iters=2)
+
+
+@pytest.mark.parametrize("k", [2, 3])
+def test_prioritized_equals_synchronous(k):
+    """Two-stream prioritized schedule == one-stream synchronous, bit for bit."""
+    w = synth.workload(k)
+    K = 4
+    bt = synth.Batches(w, 50 + k)
+    batches = [bt.batch(i) for i in range(K)]
+    cap = max(b["n_tok"] for b in batches)
+    runs = []
+    for mode in ("prio", "sync"):
+        say("schedule", k, mode)
+        weights, states = gpu_tables(w, 50 + k)
+        step = SparseStep(w, weights, states, cap)
+        st = step.prologue(to_dev(batches[0]))
+        looks = [[_bits(o[:st.n_tok]).copy() for o in st.out]]
+        for i in range(K - 1):
+            g = [torch.from_numpy(x).cuda() for x in balanced_grads(
+                w, 50 + k, i, batches[i], host(st.perm), host(st.bucket["bal_offsets"]))]
+            step.join()
+            torch.cuda.synchronize()
+            st = (step.step if mode == "prio" else step.step_sync)(to_dev(batches[i + 1]), g)
+            step.join()
+            torch.cuda.synchronize()
+            looks.append([_bits(o[:st.n_tok]).copy() for o in st.out])
+        rows_t = touched_rows(batches, w)
+        final = [_bits(weights[t].index_select(0, torch.from_numpy(r).cuda()))
+                 for t, r in enumerate(rows_t)]
+        runs.append((looks, final))
+    (la, fa), (lb, fb) = runs
+    for x, y in zip(la, lb):
+        for a, b in zip(x, y):
+            assert np.array_equal(a, b)
+    for a, b in zip(fa, fb):
+        assert np.array_equal(a, b)
