@@ -193,7 +193,7 @@ int fs_unique_collision_split(const int64_t* shard_keys, const int32_t* shard_bm
                               uint8_t* cls, uint8_t* prev_cls, int64_t* counts, void* ws,
                               size_t ws_bytes, hipStream_t stream);
 
-size_t fs_unique_workspace_size(int64_t n_cap, int32_t T, int32_t W);
+size_t fs_unique_workspace_size(int64_t n_cap, int64_t prev_cap, int32_t T, int32_t W);
 
 /* ------------------------------------------------------------------------ */
 /* Jagged lookup -- Algorithm 2's Lookup, the batch-major transform that     */

@@ -71,10 +71,21 @@ k_sort_place(const int32_t* __restrict__ len, int32_t n, int32_t W, int32_t* __r
   if (w == 0) flag_err(err, valid && (Ls < 0 || Ls > FS_MAX_UIH), FS_EF_LEN_RANGE);
   const uint64_t mine = sort_key(Ls, s);
 
-  const int32_t chunk = (n + nw - 1) / nw;
+  // this wave's slice of comparands, 64 per coalesced load, broadcast lane
+  // by lane with readlane (uniform operands for the 64-bit compares)
+  const int32_t chunk = ((n + nw - 1) / nw + kWave - 1) / kWave * kWave;
   const int32_t c0 = w * chunk, c1 = min(n, c0 + chunk);
   int32_t below = 0;
-  for (int32_t c = c0; c < c1; ++c) below += sort_key(len[c], c) < mine;
+  for (int32_t cb = c0; cb < c1; cb += kWave) {
+    const int32_t c = cb + l;
+    const int32_t Lc = c < c1 ? len[c] : 0;
+    const int32_t m = min(kWave, c1 - cb);
+#pragma unroll 16
+    for (int j = 0; j < kWave; ++j) {
+      const int32_t Lj = __builtin_amdgcn_readlane(Lc, j);
+      below += (j < m) && sort_key(Lj, cb + j) < mine;
+    }
+  }
   part[w][l] = below;
   __syncthreads();
 

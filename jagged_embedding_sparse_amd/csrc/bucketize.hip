@@ -13,7 +13,8 @@
 //   * every tile knows its rank and table without a search per item,
 //   * splits[d][r] is a difference of the per-shard tile-count prefix sums.
 // Four launches: prep (balanced offsets + tile table), per-tile histograms,
-// per-shard column scans (+ splits, shard offsets), stable per-tile scatter.
+// per-shard column scans (+ splits, shard totals), stable per-tile scatter
+// staged through LDS (+ shard offsets). No device-scope atomics.
 #include "common.hpp"
 
 namespace fs {
@@ -31,11 +32,11 @@ struct TableRows {
 };
 
 // ---------------------------------------------------------------- prep
-// bal_offsets, input validation, tile table, zeroed shard totals.
+// bal_offsets, input validation, tile table.
 __global__ void __launch_bounds__(1024)
 k_prep(const int64_t* __restrict__ so, int32_t n, int64_t n_tok, const int32_t* __restrict__ perm,
        const int32_t* __restrict__ ro, int32_t W, int32_t T, int64_t* __restrict__ bal,
-       int32_t* __restrict__ tile_pref, uint32_t* __restrict__ tot, int32_t* __restrict__ err) {
+       int32_t* __restrict__ tile_pref, int32_t* __restrict__ err) {
   __shared__ int64_t tmp64[17];
   __shared__ int32_t tmp32[17];
   __shared__ int bad_s;
@@ -91,7 +92,6 @@ k_prep(const int64_t* __restrict__ so, int32_t n, int64_t n_tok, const int32_t* 
   int32_t pref = block_excl_scan<int32_t>(my_tiles, tmp32, &ttot);
   if (r < W) tile_pref[r] = pref;
   if (threadIdx.x == 0) tile_pref[W] = ttot;
-  for (int32_t b = threadIdx.x; b <= W; b += blockDim.x) tot[b] = 0;
 }
 
 // ---------------------------------------------------------------- tiles
@@ -124,72 +124,92 @@ __device__ __forceinline__ bool tile_info(int32_t tile, const int32_t* tile_pref
   return true;
 }
 
-// first balanced sample q in [q_lo, q_hi) whose tokens reach past bm
-__device__ __forceinline__ int32_t sample_of(const int64_t* bal, int32_t q_lo, int32_t q_hi,
-                                             int64_t bm) {
-  int32_t lo = q_lo, hi = q_hi - 1;  // answer in [q_lo, q_hi-1]
-  while (lo < hi) {
-    int32_t mid = (lo + hi + 1) >> 1;
-    if (bal[mid] <= bm) lo = mid; else hi = mid - 1;
-  }
-  return lo;
-}
-
-// Walks one wave's 1024 consecutive tokens of a tile, round by round, and
-// yields (valid, key, bin, bm) per lane. The balanced sample of a lane's
-// token is found by walking forward from the sample of the round's first
-// token (tokens are contiguous, so a round spans few samples).
-struct ItemWalker {
-  const int64_t* ids;
-  const int64_t* so;
-  const int32_t* perm;
-  const int64_t* bal;
-  int64_t n_tok;
-  int64_t rows, row_base, block;
-  int32_t t, q_hi, nbin;
-  int32_t q_cur;
-
-  __device__ __forceinline__ void next(int64_t bm, int64_t bm_hi, bool& valid, int64_t& key,
-                                       int32_t& bin) {
-    valid = bm < bm_hi;
-    int32_t q = q_cur;
-    if (valid)
-      while (q + 1 < q_hi && bal[q + 1] <= bm) ++q;
-    // the next round starts at or after the last valid lane's sample
-    q_cur = __shfl(q, kWave - 1, kWave);
-    key = 0;
-    bin = nbin;  // sentinel: not counted
-    if (valid) {
-      const int32_t s = perm[q];
-      const int64_t tok = so[s] + (bm - bal[q]);
-      const int64_t id = ids[(int64_t)t * n_tok + tok];
-      const bool in = id >= 0 && id < rows;
-      key = row_base + id;
-      bin = in ? (int32_t)(id / block) : -1;  // -1 marks a dropped ID
-    }
-  }
+// Loads one wave's 16 rounds of 64 consecutive tokens of a tile (table t,
+// batch-major positions bm) and returns, per round and lane, the item's key
+// and bin (shard, -1 for a dropped ID, `sentinel` past the tile's end).
+//
+// The wave finds the balanced sample of its first token with one cooperative
+// search, then loads a window of 64 samples: their end offsets and the shift
+// from batch-major to original token index (so[perm[q]] - bal[q]). A lane
+// finds its token's sample in the window by binary lifting over the window
+// with shuffles; the window restarts at each round's first sample, and a lane
+// whose token lies past the window (only possible with runs of empty
+// samples) walks forward on its own. All 16 ID loads are independent.
+struct Window {
+  int32_t qa;    // first sample of the window
+  int64_t bnd;   // this lane: end offset of sample qa + lane (INT64_MAX past q_hi)
+  int64_t shift; // this lane: so[perm[q]] - bal[q] for q = qa + lane
 };
 
-__device__ __forceinline__ ItemWalker make_walker(const TileInfo& ti, int32_t w,
-                                                  const int64_t* ids, const int64_t* so,
-                                                  const int32_t* perm, const int64_t* bal,
-                                                  int64_t n_tok, const TableRows& tr,
-                                                  int32_t nbin) {
-  ItemWalker it;
-  it.ids = ids;
-  it.so = so;
-  it.perm = perm;
-  it.bal = bal;
-  it.n_tok = n_tok;
-  it.t = ti.t;
-  it.rows = tr.rows[ti.t];
-  it.row_base = tr.row_base[ti.t];
-  it.block = tr.block[ti.t];
-  it.q_hi = ti.q_hi;
-  it.nbin = nbin;
+__device__ __forceinline__ Window load_window(int32_t qa, int32_t q_hi, const int64_t* bal,
+                                              const int32_t* perm, const int64_t* so) {
+  Window win;
+  win.qa = qa;
+  const int32_t q = qa + lane();
+  win.bnd = INT64_MAX;
+  win.shift = 0;
+  if (q < q_hi) {
+    win.bnd = bal[q + 1];
+    win.shift = so[perm[q]] - bal[q];
+  }
+  return win;
+}
+
+__device__ __forceinline__ void wave_items(const TileInfo& ti, int32_t w, const int64_t* ids,
+                                           const int64_t* so, const int32_t* perm,
+                                           const int64_t* bal, int64_t n_tok,
+                                           const TableRows& tr, int32_t sentinel,
+                                           int64_t (&key)[kRounds], int32_t (&bin)[kRounds]) {
   const int64_t first = ti.bm_lo + (int64_t)w * kWaveItems;
-  it.q_cur = sample_of(bal, ti.q_lo, ti.q_hi, min(first, ti.bm_hi - 1));
-  return it;
+#pragma unroll
+  for (int i = 0; i < kRounds; ++i) {
+    key[i] = 0;
+    bin[i] = sentinel;
+  }
+  if (first >= ti.bm_hi) return;
+  // sample of the first token: one past the last q in (q_lo, q_hi) with bal[q] <= first
+  const int32_t qa = (int32_t)wave_partition_point(
+      ti.q_lo + 1, ti.q_hi, [&](int64_t q) { return bal[q] <= first; }) - 1;
+  Window win = load_window(qa, ti.q_hi, bal, perm, so);
+  const int t = ti.t;
+  const int64_t rows = tr.rows[t], rbase = tr.row_base[t], block = tr.block[t];
+  int64_t tok[kRounds];
+  bool valid[kRounds];
+#pragma unroll
+  for (int i = 0; i < kRounds; ++i) {
+    const int64_t rb = first + i * kWave;  // the round's first token
+    if (rb < ti.bm_hi) {
+      // restart the window at the round's first sample (a round of 64
+      // tokens then spans at most the window, unless samples are empty)
+      const int kf = popc(__ballot(win.bnd <= rb));
+      if (kf > 0) win = load_window(win.qa + kf, ti.q_hi, bal, perm, so);
+    }
+    const int64_t bm = rb + lane();
+    valid[i] = bm < ti.bm_hi;
+    int pos = 0;  // window samples ending at or before bm (binary lifting)
+#pragma unroll
+    for (int step = kWave / 2; step >= 1; step >>= 1) {
+      const int64_t v = __shfl(win.bnd, pos + step - 1, kWave);
+      if (v <= bm) pos += step;
+    }
+    const int64_t last = __shfl(win.bnd, kWave - 1, kWave);
+    if (pos == kWave - 1 && last <= bm) pos = kWave;
+    int64_t sh = __shfl(win.shift, pos < kWave ? pos : 0, kWave);
+    if (valid[i] && pos >= kWave) {  // past the window: walk (rare)
+      int32_t q = win.qa + kWave - 1;
+      while (q + 1 < ti.q_hi && bal[q + 1] <= bm) ++q;
+      sh = so[perm[q]] - bal[q];
+    }
+    tok[i] = bm + sh;
+  }
+#pragma unroll
+  for (int i = 0; i < kRounds; ++i) {
+    if (!valid[i]) continue;
+    const int64_t id = ids[(int64_t)t * n_tok + tok[i]];
+    const bool in = id >= 0 && id < rows;
+    key[i] = rbase + id;
+    bin[i] = in ? (int32_t)(id / block) : -1;
+  }
 }
 
 // ---------------------------------------------------------------- histogram
@@ -198,7 +218,7 @@ k_hist(const int64_t* __restrict__ ids, int64_t n_tok, const int64_t* __restrict
        const int32_t* __restrict__ perm, const int32_t* __restrict__ ro,
        const int64_t* __restrict__ bal, const int32_t* __restrict__ tile_pref, TableRows tr,
        int32_t W, int32_t T, int64_t tiles_cap, uint32_t* __restrict__ hist,
-       uint32_t* __restrict__ tot, int32_t* __restrict__ err) {
+       int32_t* __restrict__ err) {
   __shared__ uint32_t h[FS_MAX_RANKS + 1];
   TileInfo ti;
   const int32_t tile = blockIdx.x;
@@ -206,48 +226,42 @@ k_hist(const int64_t* __restrict__ ids, int64_t n_tok, const int64_t* __restrict
   for (int b = threadIdx.x; b <= W; b += kThreads) h[b] = 0;
   __syncthreads();
   const int32_t w = threadIdx.x / kWave;
-  ItemWalker it = make_walker(ti, w, ids, so, perm, bal, n_tok, tr, W + 1);
+  int64_t key[kRounds];
+  int32_t bin[kRounds];
+  wave_items(ti, w, ids, so, perm, bal, n_tok, tr, W + 1, key, bin);
   bool dropped_any = false;
+  int nbits = 1;
+  while ((1 << nbits) - 1 <= W + 1) ++nbits;
+  const uint64_t lt = lanemask_lt();
+#pragma unroll
   for (int i = 0; i < kRounds; ++i) {
-    const int64_t bm = ti.bm_lo + (int64_t)w * kWaveItems + i * kWave + lane();
-    bool valid;
-    int64_t key;
-    int32_t bin;
-    it.next(bm, ti.bm_hi, valid, key, bin);
-    if (valid) {
-      if (bin < 0) {
-        bin = W;
-        dropped_any = true;
-      }
-      atomicAdd(&h[bin], 1u);
+    int32_t b = bin[i];
+    if (b < 0) {
+      b = W;
+      dropped_any = true;
     }
+    // one LDS add per distinct shard of the round (hot rows share a shard)
+    const uint64_t peers = match_bits((uint32_t)b, nbits);
+    if (b != W + 1 && (peers & lt) == 0) atomicAdd(&h[b], (uint32_t)popc(peers));
   }
   flag_err(err, dropped_any, FS_EF_ID_RANGE);
   __syncthreads();
-  for (int b = threadIdx.x; b <= W; b += kThreads) {
-    uint32_t c = h[b];
-    hist[(int64_t)b * tiles_cap + tile] = c;
-    if (c) atomicAdd(&tot[b], c);
-  }
+  for (int b = threadIdx.x; b <= W; b += kThreads) hist[(int64_t)b * tiles_cap + tile] = h[b];
 }
 
 // ---------------------------------------------------------------- column scan
 // One workgroup per bin b (shard d = b, or b == W for dropped items): the
-// bin's base is the sum of the lower bins' totals; its tiles' counts become
-// exclusive output offsets in place; splits[b][r] sums rank r's tiles.
+// bin's tile counts become exclusive offsets within the bin, in place; the
+// bin total goes to tot[b]; splits[b][r] sums rank r's tiles (the tiles of a
+// rank are contiguous). The bins' global bases are formed by the scatter.
 __global__ void __launch_bounds__(kThreads)
 k_scan(const int32_t* __restrict__ tile_pref, int32_t W, int64_t tiles_cap,
-       uint32_t* __restrict__ hist, const uint32_t* __restrict__ tot,
-       int64_t* __restrict__ splits, int64_t* __restrict__ shard_offsets) {
+       uint32_t* __restrict__ hist, uint32_t* __restrict__ tot, int64_t* __restrict__ splits) {
   __shared__ int64_t tmp[17];
   const int32_t b = blockIdx.x;
-  int64_t lower = 0;
-  for (int32_t x = threadIdx.x; x < b; x += kThreads) lower += tot[x];
-  int64_t base;
-  (void)block_excl_scan<int64_t>(lower, tmp, &base);
   const int32_t n_tiles = tile_pref[W];
   uint32_t* col = hist + (int64_t)b * tiles_cap;
-  int64_t carry = base;
+  int64_t carry = 0;
   for (int32_t c0 = 0; c0 < n_tiles; c0 += kThreads) {
     const int32_t c = c0 + threadIdx.x;
     const int64_t v = c < n_tiles ? col[c] : 0;
@@ -257,71 +271,131 @@ k_scan(const int32_t* __restrict__ tile_pref, int32_t W, int64_t tiles_cap,
     carry += sum;
   }
   __syncthreads();
-  if (threadIdx.x == 0) shard_offsets[b] = base;
+  if (threadIdx.x == 0) tot[b] = (uint32_t)carry;
   if (b < W) {
-    const int64_t end = carry;  // base + column total
     for (int32_t r = threadIdx.x; r < W; r += kThreads) {
       const int32_t a = tile_pref[r], z = tile_pref[r + 1];
-      const int64_t pa = a < n_tiles ? (int64_t)col[a] : end;
-      const int64_t pz = z < n_tiles ? (int64_t)col[z] : end;
+      const int64_t pa = a < n_tiles ? (int64_t)col[a] : carry;
+      const int64_t pz = z < n_tiles ? (int64_t)col[z] : carry;
       splits[(int64_t)b * W + r] = pz - pa;
     }
   }
 }
 
 // ---------------------------------------------------------------- scatter
+// Each tile ranks its items stably per bin (ballot match inside a wave, wave
+// order across waves), derives every bin's global base from the bin totals,
+// sorts the tile by bin in LDS and writes each bin's run contiguously.
+// Workgroup 0 also publishes the shard offsets.
 __global__ void __launch_bounds__(kThreads)
 k_scatter(const int64_t* __restrict__ ids, int64_t n_tok, const int64_t* __restrict__ so,
           const int32_t* __restrict__ perm, const int32_t* __restrict__ ro,
           const int64_t* __restrict__ bal, const int32_t* __restrict__ tile_pref, TableRows tr,
           int32_t W, int32_t T, int32_t nbits, int64_t tiles_cap,
-          const uint32_t* __restrict__ hist, int64_t* __restrict__ shard_keys,
-          int32_t* __restrict__ shard_bm) {
+          const uint32_t* __restrict__ hist, const uint32_t* __restrict__ tot,
+          int64_t* __restrict__ shard_keys, int32_t* __restrict__ shard_bm,
+          int64_t* __restrict__ shard_offsets) {
   __shared__ uint32_t cnt[kThreads / kWave][FS_MAX_RANKS + 1];
+  __shared__ uint32_t gbase[FS_MAX_RANKS + 1];  // global start of each bin
+  __shared__ uint32_t tbin[FS_MAX_RANKS + 1];   // start of each bin in the sorted tile
+  __shared__ uint32_t skey[kTile];
+  __shared__ int32_t sbm[kTile];
+  __shared__ uint16_t sbin[kTile];
+  __shared__ int64_t tmp[17];
   TileInfo ti;
   const int32_t tile = blockIdx.x;
-  if (!tile_info(tile, tile_pref, W, T, bal, ro, ti)) return;
+  const bool has_tile = tile_info(tile, tile_pref, W, T, bal, ro, ti);
+  if (!has_tile && tile != 0) return;
   const int32_t w = threadIdx.x / kWave;
+  const int32_t nb = W + 1;
+  // global bin bases: exclusive scan of the bin totals (4+ bins per thread)
+  {
+    constexpr int kPer = (FS_MAX_RANKS + 1 + kThreads - 1) / kThreads;
+    uint32_t v[kPer];
+    int64_t local = 0;
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int b = threadIdx.x * kPer + k;
+      v[k] = b < nb ? tot[b] : 0u;
+      local += v[k];
+    }
+    int64_t all;
+    int64_t run = block_excl_scan<int64_t>(local, tmp, &all);
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int b = threadIdx.x * kPer + k;
+      if (b < nb) {
+        gbase[b] = (uint32_t)run;
+        if (tile == 0) shard_offsets[b] = run;
+      }
+      run += v[k];
+    }
+  }
+  if (!has_tile) return;
   const int32_t sentinel = (1 << nbits) - 1;  // > W: lanes without an item
   for (int b = lane(); b <= W; b += kWave) cnt[w][b] = 0;
-  // (each wave only touches its own row until the barrier below)
-  ItemWalker it = make_walker(ti, w, ids, so, perm, bal, n_tok, tr, sentinel);
   int64_t key[kRounds];
-  int32_t bm32[kRounds], bin[kRounds], rk[kRounds];
+  int32_t bin[kRounds], rk[kRounds];
+  wave_items(ti, w, ids, so, perm, bal, n_tok, tr, sentinel, key, bin);
   const uint64_t lt = lanemask_lt();
 #pragma unroll
   for (int i = 0; i < kRounds; ++i) {
-    const int64_t bm = ti.bm_lo + (int64_t)w * kWaveItems + i * kWave + lane();
-    bool valid;
-    int32_t b;
-    it.next(bm, ti.bm_hi, valid, key[i], b);
-    if (valid && b < 0) b = W;
+    int32_t b = bin[i];
+    if (b < 0) b = W;
     bin[i] = b;
-    bm32[i] = (int32_t)bm;
     const uint64_t peers = match_bits((uint32_t)b, nbits);
     const uint32_t before = cnt[w][b == sentinel ? 0 : b];
     rk[i] = (int32_t)before + popc(peers & lt);
     if (b != sentinel && (peers & lt) == 0) cnt[w][b] = before + (uint32_t)popc(peers);
   }
   __syncthreads();
-  // exclusive prefix over the waves of each bin
-  for (int b = threadIdx.x; b <= W; b += kThreads) {
-    uint32_t run = 0;
+  // per bin: exclusive prefix over the waves, then the bins' starts in the tile
+  {
+    constexpr int kPer = (FS_MAX_RANKS + 1 + kThreads - 1) / kThreads;
+    uint32_t tot_b[kPer];
+    int64_t local = 0;
 #pragma unroll
-    for (int x = 0; x < kThreads / kWave; ++x) {
-      uint32_t c = cnt[x][b];
-      cnt[x][b] = run;
-      run += c;
+    for (int k = 0; k < kPer; ++k) {
+      const int b = threadIdx.x * kPer + k;
+      uint32_t run = 0;
+      if (b < nb) {
+#pragma unroll
+        for (int x = 0; x < kThreads / kWave; ++x) {
+          const uint32_t c = cnt[x][b];
+          cnt[x][b] = run;
+          run += c;
+        }
+      }
+      tot_b[k] = run;
+      local += run;
+    }
+    int64_t all;
+    int64_t run = block_excl_scan<int64_t>(local, tmp, &all);
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int b = threadIdx.x * kPer + k;
+      if (b < nb) tbin[b] = (uint32_t)run;
+      run += tot_b[k];
     }
   }
   __syncthreads();
+  const int32_t bm_base = (int32_t)(ti.bm_lo + (int64_t)w * kWaveItems);
 #pragma unroll
   for (int i = 0; i < kRounds; ++i) {
     const int32_t b = bin[i];
     if (b == sentinel) continue;
-    const int64_t pos = (int64_t)hist[(int64_t)b * tiles_cap + tile] + cnt[w][b] + rk[i];
-    shard_keys[pos] = key[i];
-    shard_bm[pos] = bm32[i];
+    const uint32_t p = tbin[b] + cnt[w][b] + (uint32_t)rk[i];
+    skey[p] = (uint32_t)key[i];
+    sbm[p] = bm_base + i * kWave + lane();
+    sbin[p] = (uint16_t)b;
+  }
+  __syncthreads();
+  const int m = (int)(ti.bm_hi - ti.bm_lo);
+  for (int p = threadIdx.x; p < m; p += kThreads) {
+    const int b = sbin[p];
+    const int64_t pos = (int64_t)gbase[b] + hist[(int64_t)b * tiles_cap + tile] + (p - (int)tbin[b]);
+    shard_keys[pos] = (int64_t)skey[p];
+    shard_bm[pos] = sbm[p];
   }
 }
 
@@ -366,7 +440,7 @@ extern "C" int fs_bucketize_permute(const int64_t* ids, int64_t n_tok,
     tr.block[t] = cdiv(tables[t].rows, W);
     base += tables[t].rows;
   }
-  if (base > (int64_t)UINT32_MAX + 1) return FS_ERR_UNSUPPORTED;
+  if (base > (int64_t)UINT32_MAX) return FS_ERR_UNSUPPORTED;
   if (!ws || ws_bytes < fs_bucketize_workspace_size(n_tok, n, T, W)) return FS_ERR_WORKSPACE;
   const int64_t tiles_cap = tiles_capacity(n_tok, T, W);
   if (tiles_cap >= INT32_MAX) return FS_ERR_UNSUPPORTED;
@@ -378,22 +452,22 @@ extern "C" int fs_bucketize_permute(const int64_t* ids, int64_t n_tok,
   while ((1 << nbits) - 1 <= W) ++nbits;  // sentinel (2^nbits - 1) > W
 
   hipLaunchKernelGGL(k_prep, dim3(1), dim3(1024), 0, stream, sample_offsets, n, n_tok, perm,
-                     rank_offsets, W, T, bal_offsets, tile_pref, tot, err);
+                     rank_offsets, W, T, bal_offsets, tile_pref, err);
   FS_LAUNCH_CHECK();
   if (tiles_cap > 0) {
     hipLaunchKernelGGL(k_hist, dim3((unsigned)tiles_cap), dim3(kThreads), 0, stream, ids, n_tok,
                        sample_offsets, perm, rank_offsets, bal_offsets, tile_pref, tr, W, T,
-                       tiles_cap, hist, tot, err);
+                       tiles_cap, hist, err);
     FS_LAUNCH_CHECK();
   }
   hipLaunchKernelGGL(k_scan, dim3(W + 1), dim3(kThreads), 0, stream, tile_pref, W, tiles_cap, hist,
-                     tot, splits, shard_offsets);
+                     tot, splits);
   FS_LAUNCH_CHECK();
-  if (tiles_cap > 0) {
-    hipLaunchKernelGGL(k_scatter, dim3((unsigned)tiles_cap), dim3(kThreads), 0, stream, ids,
-                       n_tok, sample_offsets, perm, rank_offsets, bal_offsets, tile_pref, tr, W, T,
-                       nbits, tiles_cap, hist, shard_keys, shard_bm);
-    FS_LAUNCH_CHECK();
-  }
+  // at least one workgroup runs: workgroup 0 writes the shard offsets
+  hipLaunchKernelGGL(k_scatter, dim3((unsigned)(tiles_cap > 0 ? tiles_cap : 1)), dim3(kThreads),
+                     0, stream, ids, n_tok, sample_offsets, perm, rank_offsets, bal_offsets,
+                     tile_pref, tr, W, T, nbits, tiles_cap, hist, tot, shard_keys, shard_bm,
+                     shard_offsets);
+  FS_LAUNCH_CHECK();
   return FS_OK;
 }

@@ -74,6 +74,27 @@ __device__ T block_excl_scan(T v, T* tmp, T* total) {
   return r;
 }
 
+// Smallest i in [lo, hi] with pred(i) false, for a predicate that is true
+// then false over [lo, hi). All lanes of the wave call it with the same
+// arguments; each round probes 64 positions in parallel and keeps the gap
+// between the last true and the first false probe, so a range of 2^k takes
+// about k/6 dependent rounds instead of k.
+template <typename P>
+__device__ __forceinline__ int64_t wave_partition_point(int64_t lo, int64_t hi, P pred) {
+  while (hi - lo > kWave) {
+    const int64_t span = hi - lo;
+    const int64_t p = lo + (span * (lane() + 1)) / (kWave + 1);
+    const int k = popc(__ballot(pred(p)));
+    const int64_t nlo = k > 0 ? __shfl(p, k - 1, kWave) + 1 : lo;
+    const int64_t nhi = k < kWave ? __shfl(p, k < kWave ? k : 0, kWave) : hi;
+    lo = nlo;
+    hi = nhi;
+  }
+  const int64_t p = lo + lane();
+  const bool t = p < hi && pred(p);
+  return lo + popc(__ballot(t));
+}
+
 // ---------------------------------------------------------------- errors
 __device__ __forceinline__ void flag_err(int32_t* err, bool bad, int bit) {
   if (__ballot(bad) && err != nullptr) {

@@ -19,7 +19,6 @@ namespace {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
-constexpr int kSteps = 8;  // rows in flight per lane group
 
 struct LookupArgs {
   const char* weights;
@@ -36,49 +35,69 @@ struct LookupArgs {
   int32_t which;
 };
 
+// One wave per 64 consecutive occurrences (CSR order). Index data is read
+// coalesced once per wave -- occurrence -> (unique, slot), then the <= 64
+// unique rows those occurrences span -> (key, class) -- and handed to the
+// copying lanes with cross-lane shuffles, so rows start loading after two
+// dependent index loads and up to 16 rows per lane group are in flight.
 template <int VPR>  // 16-byte vectors per row
 __global__ void __launch_bounds__(kThreads) k_lookup(LookupArgs a) {
   constexpr int LPR = VPR < kWave ? VPR : kWave;  // lanes per row
-  constexpr int RPW = kWave / LPR;                // rows per wave step
+  constexpr int RPW = kWave / LPR;                // rows per wave instruction
   constexpr int VPL = VPR / LPR;                  // vectors per lane
-  constexpr int OPW = RPW * kSteps;               // occurrences per wave
+  constexpr int STEPS = kWave / RPW;              // row steps for 64 occurrences
+  constexpr int BATCH = STEPS < 16 / VPL ? STEPS : 16 / VPL;
   const int64_t o_lo = a.seg_offsets[a.unique_offsets[a.g_lo]];
   const int64_t o_hi = a.seg_offsets[a.unique_offsets[a.g_hi]];
-  const int w = threadIdx.x / kWave;
-  const int grp = lane() / LPR, sub = lane() % LPR;
-  const int64_t ob = o_lo + ((int64_t)blockIdx.x * (kThreads / kWave) + w) * OPW;
-  if (ob >= o_hi) return;
-
-  u32x4 v[kSteps][VPL];
-  int64_t dst[kSteps];
+  const int w = threadIdx.x / kWave, l = lane();
+  const int64_t o0 = o_lo + ((int64_t)blockIdx.x * (kThreads / kWave) + w) * kWave;
+  if (o0 >= o_hi) return;
+  const int nvalid = (int)min((int64_t)kWave, o_hi - o0);
+  const bool valid = l < nvalid;
+  const int32_t u = valid ? a.occ_uid[o0 + l] : 0;
+  const int32_t bm = valid ? a.occ_bm[o0 + l] : -1;
+  const int32_t u0 = __shfl(u, 0, kWave);
+  const int32_t span = __shfl(u, nvalid - 1, kWave) - u0 + 1;  // <= 64
+  uint32_t key = 0;
+  int c = 0;
+  if (l < span) {
+    key = (uint32_t)(a.unique[u0 + l] - a.row_base);
+    if (a.which >= 0) c = a.cls[u0 + l];
+  }
+  const int src = valid ? u - u0 : 0;
+  const uint32_t row = (uint32_t)__shfl((int)key, src, kWave);
+  const int cc = __shfl(c, src, kWave);
+  const int32_t dst = (valid && (a.which < 0 || cc == a.which)) ? bm : -1;
+  if (!__ballot(dst >= 0)) return;
+  const int grp = l / LPR, sub = l % LPR;
 #pragma unroll
-  for (int s = 0; s < kSteps; ++s) {
-    const int64_t o = ob + s * RPW + grp;
-    dst[s] = -1;
-    if (o < o_hi) {
-      const int32_t u = a.occ_uid[o];
-      if (a.which < 0 || a.cls[u] == (uint8_t)a.which) {
-        const int64_t row = a.unique[u] - a.row_base;
-        const u32x4* src = (const u32x4*)(a.weights + row * (VPR * 16));
+  for (int s0 = 0; s0 < STEPS; s0 += BATCH) {
+    u32x4 v[BATCH][VPL];
+    int32_t d[BATCH];
 #pragma unroll
-        for (int k = 0; k < VPL; ++k) v[s][k] = src[sub + k * LPR];
-        dst[s] = a.occ_bm[o];
+    for (int b = 0; b < BATCH; ++b) {
+      const int j = (s0 + b) * RPW + grp;
+      const uint32_t r = (uint32_t)__shfl((int)row, j, kWave);
+      d[b] = __shfl(dst, j, kWave);
+      if (d[b] >= 0) {
+        const u32x4* sp = (const u32x4*)(a.weights + (int64_t)r * (VPR * 16));
+#pragma unroll
+        for (int k = 0; k < VPL; ++k) v[b][k] = sp[sub + k * LPR];
       }
     }
-  }
 #pragma unroll
-  for (int s = 0; s < kSteps; ++s) {
-    if (dst[s] < 0) continue;
-    u32x4* d = (u32x4*)(a.out + dst[s] * (VPR * 16));
+    for (int b = 0; b < BATCH; ++b) {
+      if (d[b] < 0) continue;
+      u32x4* dp = (u32x4*)(a.out + (int64_t)d[b] * (VPR * 16));
 #pragma unroll
-    for (int k = 0; k < VPL; ++k) __builtin_nontemporal_store(v[s][k], d + sub + k * LPR);
+      for (int k = 0; k < VPL; ++k) __builtin_nontemporal_store(v[b][k], dp + sub + k * LPR);
+    }
   }
 }
 
 template <int VPR>
 int launch(const LookupArgs& a, hipStream_t stream) {
-  constexpr int LPR = VPR < kWave ? VPR : kWave;
-  constexpr int OPB = (kWave / LPR) * kSteps * (kThreads / kWave);
+  constexpr int OPB = kWave * (kThreads / kWave);  // occurrences per block
   const int64_t blocks = cdiv(a.n_cap, OPB);
   if (blocks == 0) return FS_OK;
   hipLaunchKernelGGL(k_lookup<VPR>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
@@ -113,7 +132,7 @@ extern "C" int fs_jagged_lookup(const fs_table* tables, int32_t T, int32_t W,
       return FS_ERR_UNSUPPORTED;
     base += tb.rows;
   }
-  if (base > (int64_t)UINT32_MAX + 1) return FS_ERR_UNSUPPORTED;
+  if (base > (int64_t)UINT32_MAX) return FS_ERR_UNSUPPORTED;
   base = 0;
   for (int t = 0; t < T; ++t) {
     const fs_table& tb = tables[t];

@@ -10,8 +10,9 @@
 // g_u = sum of grad[bm] over u's occurrences, accumulated in fp64 and rounded
 // once to fp32, so the result does not depend on how the sum is split.
 // Zipf IDs make segment lengths span 1 .. ~10^5, so two paths:
-//   short rows (<= kLong occurrences): one lane group per row, grid-stride
-//     over the table's unique rows; the group sums and updates the row.
+//   short rows (<= kLong = 4 occurrences, most rows): one lane group per row,
+//     grid-stride over the table's unique rows; all of a row's loads are in
+//     flight at once, then the group sums and updates the row.
 //   long rows: the table's occurrence range is cut into chunks of kChunk;
 //     a wave streams each long row's piece of its chunk (all lane groups of
 //     the wave interleaved), updates rows that lie inside the chunk and
@@ -25,9 +26,9 @@ namespace fs {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kLong = 64;     // longer segments take the chunked path
+constexpr int kLong = 4;      // longer segments take the chunked path
 constexpr int kChunk = 512;   // occurrences per long-path chunk (one wave)
-constexpr int kShortBlocks = 2048;
+constexpr int kShortBlocks = 4096;
 
 struct RUArgs {
   void* weights;
@@ -180,66 +181,90 @@ __device__ __forceinline__ void update_row(const RUArgs& a, int64_t u, int sub,
 }
 
 // ---------------------------------------------------------------- short rows
-// Grid-stride over the table's unique rows; each lane group takes R
-// consecutive rows per step and keeps all of their loads in flight:
-// offsets and keys, then first-occurrence index, weights and state, then
-// the gradient rows.
+// Grid-stride over the table's unique rows, 64 per wave. The wave loads the
+// rows' CSR bounds, keys, classes, first occurrence and Adagrad state with one
+// coalesced or gathered load each; lane groups then take the rows in turn, R
+// at a time, fetch their metadata by shuffle and keep R weight rows and R
+// gradient rows in flight.
 template <int D, typename WT>
 __global__ void __launch_bounds__(kThreads) k_short(RUArgs a) {
   using M = Map<D>;
-  constexpr int R = M::CPL <= 4 ? 4 : 2;
+  constexpr int R = M::CPL <= 4 ? 4 : (M::CPL <= 8 ? 2 : 1);
+  constexpr int PER = M::GPW * R;  // rows per batch of the wave
   const int64_t u_lo = a.unique_offsets[a.g_lo], u_hi = a.unique_offsets[a.g_hi];
-  const int sub = lane() % M::LPG;
-  constexpr int64_t GPB = (kThreads / kWave) * M::GPW;  // groups per block
-  const int64_t local = threadIdx.x / M::LPG;
-  const int64_t NG = (int64_t)gridDim.x * GPB;
-  for (int64_t it = 0;; ++it) {
-    const int64_t g0 = (it * NG + (int64_t)blockIdx.x * GPB) * R;  // block's first row
-    if (u_lo + g0 >= u_hi) break;
-    const int64_t ub = u_lo + g0 + local * R;
-    int32_t lo[R], hi[R];
-    int64_t row[R];
-    bool act[R];
+  const int l = lane(), grp = l / M::LPG, sub = l % M::LPG;
+  const bool ada = a.optim == FS_RW_ADAGRAD;
+  const int64_t wid = (int64_t)blockIdx.x * (kThreads / kWave) + threadIdx.x / kWave;
+  const int64_t nwaves = (int64_t)gridDim.x * (kThreads / kWave);
+  for (int64_t ub = u_lo + wid * kWave; ub < u_hi; ub += nwaves * kWave) {
+    const int64_t uu = ub + l;
+    const bool in = uu < u_hi;
+    const int32_t lo = in ? a.seg_offsets[uu] : 0;
+    const int32_t hi = in ? a.seg_offsets[uu + 1] : 0;
+    const bool act = in && (hi - lo) <= kLong && class_ok(a, uu);
+    const uint64_t actm = __ballot(act);
+    if (!actm) continue;
+    const uint32_t row = act ? (uint32_t)(a.unique[uu] - a.row_base) : 0u;
+    const float st = (act && ada) ? a.state[row] : 0.f;
+#pragma unroll 1
+    for (int j0 = 0; j0 < kWave; j0 += PER) {
+      const uint64_t win = (PER >= kWave) ? ~0ull : (((1ull << PER) - 1ull) << j0);
+      if (!(actm & win)) continue;
+      int32_t jlo[R], jhi[R];
+      uint32_t jrow[R];
+      float jst[R];
+      bool ja[R];
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const int64_t u = ub + r;
-      act[r] = u < u_hi;
-      lo[r] = act[r] ? a.seg_offsets[u] : 0;
-      hi[r] = act[r] ? a.seg_offsets[u + 1] : 0;
-      row[r] = act[r] ? a.unique[u] - a.row_base : 0;
-      if (act[r]) act[r] = (hi[r] - lo[r]) <= kLong && class_ok(a, u);
-    }
-    int32_t bm0[R];
-    RowW<D, WT> wr[R];
-    float st[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      bm0[r] = act[r] ? a.occ_bm[lo[r]] : 0;
-      st[r] = 0.f;
-      if (act[r]) {
-        load_w<D, WT>(a, row[r], sub, wr[r]);
-        if (a.optim == FS_RW_ADAGRAD) st[r] = a.state[row[r]];
+      for (int r = 0; r < R; ++r) {
+        const int j = j0 + r * M::GPW + grp;
+        ja[r] = (actm >> j) & 1ull;
+        jlo[r] = __shfl(lo, j, kWave);
+        jhi[r] = __shfl(hi, j, kWave);
+        jrow[r] = (uint32_t)__shfl((int)row, j, kWave);
+        jst[r] = __shfl(st, j, kWave);
       }
-    }
-    double acc[R][M::CPL];
+      // a short row has at most kLong occurrences: lanes sub < kLong of the
+      // group load their indices, then all of its gradient rows load at once
+      RowW<D, WT> wr[R];
+      double acc[R][M::CPL];
+      int32_t bmv[R];
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
+      for (int r = 0; r < R; ++r) {
+        bmv[r] = (ja[r] && sub < jhi[r] - jlo[r]) ? a.occ_bm[jlo[r] + sub] : 0;
+        if (ja[r]) load_w<D, WT>(a, jrow[r], sub, wr[r]);
+      }
 #pragma unroll
-      for (int c = 0; c < M::CPL; ++c) acc[r][c] = 0.0;
-      if (act[r]) add_row<D>(acc[r], a.grad, bm0[r], sub);
-    }
+      for (int r = 0; r < R; ++r) {
+        const int len = ja[r] ? jhi[r] - jlo[r] : 0;
+        float4 gv[kLong][M::NV];
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      if (act[r]) {
-        int32_t k = lo[r] + 1;
-        for (; k + 2 <= hi[r]; k += 2) {
-          const int32_t b0 = a.occ_bm[k], b1 = a.occ_bm[k + 1];
-          add_row<D>(acc[r], a.grad, b0, sub);
-          add_row<D>(acc[r], a.grad, b1, sub);
+        for (int m = 0; m < kLong; ++m) {
+          const int32_t bm = __shfl(bmv[r], grp * M::LPG + m, kWave);
+          if (m < len) {
+            const float4* gp = (const float4*)(a.grad + (int64_t)bm * D);
+#pragma unroll
+            for (int v = 0; v < M::NV; ++v) gv[m][v] = gp[sub + v * M::LPG];
+          }
         }
-        if (k < hi[r]) add_row<D>(acc[r], a.grad, a.occ_bm[k], sub);
+#pragma unroll
+        for (int c = 0; c < M::CPL; ++c) acc[r][c] = 0.0;
+#pragma unroll
+        for (int m = 0; m < kLong; ++m) {
+          if (m < len) {
+#pragma unroll
+            for (int v = 0; v < M::NV; ++v) {
+              acc[r][4 * v + 0] += (double)gv[m][v].x;
+              acc[r][4 * v + 1] += (double)gv[m][v].y;
+              acc[r][4 * v + 2] += (double)gv[m][v].z;
+              acc[r][4 * v + 3] += (double)gv[m][v].w;
+            }
+          }
+        }
       }
-      apply_row<D, WT>(a, ub + r, row[r], st[r], sub, acc[r], wr[r], act[r]);
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+        apply_row<D, WT>(a, ub + j0 + r * M::GPW + grp, jrow[r], jst[r], sub, acc[r], wr[r],
+                         ja[r]);
     }
   }
 }
@@ -267,27 +292,57 @@ __global__ void __launch_bounds__(kThreads) k_long(RUArgs a) {
       const int64_t s_lo = __shfl(lo, j, kWave), s_hi = __shfl(hi, j, kWave);
       const int64_t u = ub + j;
       const int64_t p0 = max(s_lo, cb), p1 = min(s_hi, ce);
+      const bool complete = s_lo >= cb && s_hi <= ce;
+      // a row that lies inside the chunk is updated here: fetch its weights
+      // and state now, while its gradients stream in
+      RowW<D, WT> wr;
+      int64_t row = 0;
+      float st = 0.f;
+      if (complete) {
+        row = a.unique[u] - a.row_base;
+        if (grp == 0) load_w<D, WT>(a, row, sub, wr);
+        if (a.optim == FS_RW_ADAGRAD) st = a.state[row];
+      }
       double acc[M::CPL];
 #pragma unroll
       for (int x = 0; x < M::CPL; ++x) acc[x] = 0.0;
-      int64_t o = p0 + grp;
-      for (; o + 3 * M::GPW < p1; o += 4 * M::GPW) {
-        const int32_t b0 = a.occ_bm[o], b1 = a.occ_bm[o + M::GPW];
-        const int32_t b2 = a.occ_bm[o + 2 * M::GPW], b3 = a.occ_bm[o + 3 * M::GPW];
-        add_row<D>(acc, a.grad, b0, sub);
-        add_row<D>(acc, a.grad, b1, sub);
-        add_row<D>(acc, a.grad, b2, sub);
-        add_row<D>(acc, a.grad, b3, sub);
+      for (int64_t ob = p0; ob < p1; ob += kWave) {
+        const int nblk = (int)min((int64_t)kWave, p1 - ob);
+        const int32_t bmv = lane() < nblk ? a.occ_bm[ob + lane()] : 0;
+        // group g takes rows g, g + GPW, ... of this block of 64
+        for (int m0 = 0; m0 < nblk; m0 += 8 * M::GPW) {
+          float4 gv[8][M::NV];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int m = m0 + e * M::GPW + grp;
+            const int32_t bm = __shfl(bmv, m < kWave ? m : 0, kWave);
+            if (m < nblk) {
+              const float4* gp = (const float4*)(a.grad + (int64_t)bm * D);
+#pragma unroll
+              for (int v = 0; v < M::NV; ++v) gv[e][v] = gp[sub + v * M::LPG];
+            }
+          }
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            if (m0 + e * M::GPW + grp < nblk) {
+#pragma unroll
+              for (int v = 0; v < M::NV; ++v) {
+                acc[4 * v + 0] += (double)gv[e][v].x;
+                acc[4 * v + 1] += (double)gv[e][v].y;
+                acc[4 * v + 2] += (double)gv[e][v].z;
+                acc[4 * v + 3] += (double)gv[e][v].w;
+              }
+            }
+          }
+        }
       }
-      for (; o < p1; o += M::GPW) add_row<D>(acc, a.grad, a.occ_bm[o], sub);
       // combine the interleaved groups (fixed order)
 #pragma unroll
       for (int off = M::LPG; off < kWave; off <<= 1)
 #pragma unroll
         for (int x = 0; x < M::CPL; ++x) acc[x] += __shfl_xor(acc[x], off, kWave);
-      const bool complete = s_lo >= cb && s_hi <= ce;
       if (complete) {
-        update_row<D, WT>(a, u, sub, acc, grp == 0);
+        apply_row<D, WT>(a, u, row, st, sub, acc, wr, grp == 0);
       } else if (grp == 0) {
         const int slot = s_lo >= cb ? 1 : 0;
         double* p = a.partials + ((c - 0) * 2 + slot) * D;
@@ -359,9 +414,7 @@ __global__ void __launch_bounds__(kThreads) k_fix(RUArgs a) {
 
 template <int D, typename WT>
 int launch_all(const RUArgs& a, hipStream_t stream) {
-  using M = Map<D>;
-  const int64_t groups_per_block = (kThreads / kWave) * M::GPW;
-  int64_t sb = cdiv(a.n_cap, groups_per_block);
+  int64_t sb = cdiv(a.n_cap, kThreads);  // 64 rows per wave, 4 waves per block
   if (sb > kShortBlocks) sb = kShortBlocks;
   if (sb < 1) sb = 1;
   hipLaunchKernelGGL((k_short<D, WT>), dim3((unsigned)sb), dim3(kThreads), 0, stream, a);
@@ -428,7 +481,7 @@ extern "C" int fs_grad_reduce_update(const fs_table* tables, int32_t T, int32_t 
     max_dim = tb.dim > max_dim ? tb.dim : max_dim;
     base += tb.rows;
   }
-  if (base > (int64_t)UINT32_MAX + 1) return FS_ERR_UNSUPPORTED;
+  if (base > (int64_t)UINT32_MAX) return FS_ERR_UNSUPPORTED;
   if (!ws || ws_bytes < fs_grad_reduce_update_workspace_size(n_tok, max_dim))
     return FS_ERR_WORKSPACE;
   base = 0;

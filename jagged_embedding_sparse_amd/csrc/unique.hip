@@ -37,7 +37,8 @@ struct Groups {
 __device__ __forceinline__ int32_t group_of(uint32_t key, const Groups& g) {
   int t = 0;
   while (t + 1 < g.T && (int64_t)key >= g.row_base[t + 1]) ++t;
-  return t * g.W + (int32_t)(((int64_t)key - g.row_base[t]) / g.block[t]);
+  // row within the table and the shard block both fit 32 bits
+  return t * g.W + (int32_t)((uint32_t)((int64_t)key - g.row_base[t]) / (uint32_t)g.block[t]);
 }
 
 // Valid item count of the call: shard_offsets[W] clamped to the capacity the
@@ -48,51 +49,55 @@ __device__ __forceinline__ int64_t n_valid_of(const int64_t* n_valid, int32_t W)
 }
 
 // ---------------------------------------------------------------- init
-__global__ void k_init(uint32_t* __restrict__ tot, int n_tot, uint32_t* __restrict__ ticket,
-                       const int64_t* __restrict__ shard_offsets, int32_t W, int64_t n_cap,
+__global__ void k_init(const int64_t* __restrict__ shard_offsets, int32_t W, int64_t n_cap,
                        int64_t* __restrict__ n_valid) {
-  for (int i = threadIdx.x; i < n_tot; i += blockDim.x) tot[i] = 0;
   if (threadIdx.x == 0) {
-    *ticket = 0;
     const int64_t v = shard_offsets[W];
     *n_valid = v < 0 ? 0 : (v > n_cap ? n_cap : v);
   }
 }
 
 // ---------------------------------------------------------------- radix pass
+// Per pass: k_rs_hist writes each tile's digit histogram (LDS atomics only);
+// k_rs_scan turns each digit's column of tile counts into exclusive offsets
+// and the digit's total; k_rs_scatter derives the digit bases from the
+// totals, ranks its tile stably, sorts it by digit in LDS and writes every
+// digit's run contiguously. No device-scope atomics anywhere.
 template <typename KIn>
 __global__ void __launch_bounds__(kThreads)
-k_rs_hist(const KIn* __restrict__ keys, const int64_t* __restrict__ nvp, int32_t W,
-          int shift, uint32_t mask, int64_t tiles_cap, uint32_t* __restrict__ hist,
-          uint32_t* __restrict__ tot) {
+k_rs_hist(const KIn* __restrict__ keys, const int64_t* __restrict__ nvp, int32_t W, int shift,
+          uint32_t mask, int64_t tiles_cap, uint32_t* __restrict__ hist) {
   __shared__ uint32_t h[kRadix];
   const int64_t n = n_valid_of(nvp, W);
   const int64_t t0 = (int64_t)blockIdx.x * kTile;
   if (t0 >= n) return;
   h[threadIdx.x] = 0;  // kThreads == kRadix
   __syncthreads();
+  // one LDS add per distinct digit of each wave round: hot keys (many equal
+  // digits) would otherwise serialise on one counter
+  const uint32_t none = mask + 1;
+  int nbits = 0;
+  while ((1u << nbits) <= mask) ++nbits;
+  const uint64_t lt = lanemask_lt();
 #pragma unroll 4
   for (int i = 0; i < kRounds; ++i) {
     const int64_t x = t0 + i * kThreads + threadIdx.x;
-    if (x < n) atomicAdd(&h[((uint32_t)keys[x] >> shift) & mask], 1u);
+    const uint32_t d = x < n ? (((uint32_t)keys[x] >> shift) & mask) : none;
+    const uint64_t peers = match_bits(d, nbits + 1);
+    if (d != none && (peers & lt) == 0) atomicAdd(&h[d], (uint32_t)popc(peers));
   }
   __syncthreads();
-  const uint32_t c = h[threadIdx.x];
-  hist[(int64_t)threadIdx.x * tiles_cap + blockIdx.x] = c;
-  if (c) atomicAdd(&tot[threadIdx.x], c);
+  hist[(int64_t)threadIdx.x * tiles_cap + blockIdx.x] = h[threadIdx.x];
 }
 
 __global__ void __launch_bounds__(kThreads)
 k_rs_scan(const int64_t* __restrict__ nvp, int32_t W, int64_t tiles_cap,
-          uint32_t* __restrict__ hist, const uint32_t* __restrict__ tot) {
+          uint32_t* __restrict__ hist, uint32_t* __restrict__ tot) {
   __shared__ int64_t tmp[17];
   const int32_t b = blockIdx.x;
-  const int64_t lower = threadIdx.x < b ? (int64_t)tot[threadIdx.x] : 0;
-  int64_t base;
-  (void)block_excl_scan<int64_t>(lower, tmp, &base);
   const int64_t n_tiles = cdiv(n_valid_of(nvp, W), kTile);
   uint32_t* col = hist + (int64_t)b * tiles_cap;
-  int64_t carry = base;
+  int64_t carry = 0;
   for (int64_t c0 = 0; c0 < n_tiles; c0 += kThreads) {
     const int64_t c = c0 + threadIdx.x;
     const int64_t v = c < n_tiles ? col[c] : 0;
@@ -101,15 +106,22 @@ k_rs_scan(const int64_t* __restrict__ nvp, int32_t W, int64_t tiles_cap,
     if (c < n_tiles) col[c] = (uint32_t)(carry + ex);
     carry += sum;
   }
+  if (threadIdx.x == 0) tot[b] = (uint32_t)carry;
 }
 
 template <typename KIn>
 __global__ void __launch_bounds__(kThreads)
 k_rs_scatter(const KIn* __restrict__ keys_in, const int32_t* __restrict__ vals_in,
-             const int64_t* __restrict__ nvp, int32_t W, int shift, uint32_t mask,
-             int nbits, int64_t tiles_cap, const uint32_t* __restrict__ hist,
-             uint32_t* __restrict__ keys_out, int32_t* __restrict__ vals_out) {
+             const int64_t* __restrict__ nvp, int32_t W, int shift, uint32_t mask, int nbits,
+             int64_t tiles_cap, const uint32_t* __restrict__ hist,
+             const uint32_t* __restrict__ tot, uint32_t* __restrict__ keys_out,
+             int32_t* __restrict__ vals_out) {
   __shared__ uint32_t cnt[kThreads / kWave][kRadix];
+  __shared__ uint32_t dig_base[kRadix];  // global start of each digit's run of this tile
+  __shared__ uint32_t dig_tile[kRadix];  // start of each digit inside the LDS-sorted tile
+  __shared__ uint32_t skey[kTile];
+  __shared__ int32_t sval[kTile];
+  __shared__ int64_t tmp[17];
   const int64_t n = n_valid_of(nvp, W);
   const int64_t t0 = (int64_t)blockIdx.x * kTile;
   if (t0 >= n) return;
@@ -142,14 +154,29 @@ k_rs_scatter(const KIn* __restrict__ keys_in, const int32_t* __restrict__ vals_i
       cnt[x][b] = run;
       run += c;
     }
+    int64_t all;
+    const int64_t in_tile = block_excl_scan<int64_t>(run, tmp, &all);
+    dig_tile[b] = (uint32_t)in_tile;
+    int64_t gsum;
+    const int64_t gbase = block_excl_scan<int64_t>((int64_t)tot[b], tmp, &gsum);
+    dig_base[b] = (uint32_t)(gbase + hist[(int64_t)b * tiles_cap + blockIdx.x]);
   }
   __syncthreads();
 #pragma unroll
   for (int i = 0; i < kRounds; ++i) {
     if (dig[i] == none) continue;
-    const int64_t pos = (int64_t)hist[(int64_t)dig[i] * tiles_cap + blockIdx.x] + cnt[w][dig[i]] + rk[i];
-    keys_out[pos] = key[i];
-    vals_out[pos] = val[i];
+    const uint32_t p = dig_tile[dig[i]] + cnt[w][dig[i]] + rk[i];
+    skey[p] = key[i];
+    sval[p] = val[i];
+  }
+  __syncthreads();
+  const int m = (int)min((int64_t)kTile, n - t0);
+  for (int p = threadIdx.x; p < m; p += kThreads) {
+    const uint32_t k = skey[p];
+    const uint32_t d = (k >> shift) & mask;
+    const uint32_t pos = dig_base[d] + (uint32_t)p - dig_tile[d];
+    keys_out[pos] = k;
+    vals_out[pos] = sval[p];
   }
 }
 
@@ -203,49 +230,62 @@ k_heads_scan(const int64_t* __restrict__ nvp, int32_t W, int32_t n_groups,
     for (int32_t g = threadIdx.x; g <= n_groups; g += blockDim.x) unique_offsets[g] = 0;
 }
 
-// Blocked layout: thread x owns items [x*16, x*16+16) of the tile.
+// Striped layout: wave w of the tile owns 16 rounds of 64 consecutive items.
+// Head flags by comparing with the left neighbour (shuffle, or the previous
+// round's last lane), counts by ballot; the wave prefix over the tile's
+// waves comes from LDS, the tile's base from the tile scan.
 __global__ void __launch_bounds__(kThreads)
 k_compact(const uint32_t* __restrict__ sk, const int64_t* __restrict__ nvp, Groups g,
           const uint32_t* __restrict__ tile_base, const int64_t* __restrict__ counts,
           int64_t* __restrict__ unique, int32_t* __restrict__ seg_offsets,
           int32_t* __restrict__ occ_uid, int64_t* __restrict__ unique_offsets) {
-  __shared__ uint32_t tmp[17];
+  __shared__ uint32_t wave_heads[kThreads / kWave];
   const int64_t n = n_valid_of(nvp, g.W);
   const int64_t t0 = (int64_t)blockIdx.x * kTile;
   if (t0 >= n) return;
-  const int64_t x0 = t0 + (int64_t)threadIdx.x * kRounds;
-  uint32_t k[kRounds];
-  uint32_t heads = 0;
-  uint32_t prev = x0 > 0 && x0 <= n ? sk[x0 - 1] : 0u;
+  const int w = threadIdx.x / kWave, l = lane();
+  const int64_t x0 = t0 + (int64_t)w * kWaveItems;
+  uint32_t k[kRounds], prevk[kRounds];
+  uint64_t hm[kRounds];
+  uint32_t carry = (x0 > 0 && x0 <= n) ? sk[x0 - 1] : 0u;  // key left of the wave's first item
+  uint32_t total = 0;
 #pragma unroll
   for (int i = 0; i < kRounds; ++i) {
-    const int64_t x = x0 + i;
-    k[i] = x < n ? sk[x] : 0u;
-    const bool h = x < n && (x == 0 || k[i] != prev);
-    heads |= (uint32_t)h << i;
-    prev = k[i];
+    const int64_t x = x0 + i * kWave + l;
+    const bool in = x < n;
+    k[i] = in ? sk[x] : 0u;
+    const uint32_t up = (uint32_t)__shfl_up((int)k[i], 1, kWave);
+    prevk[i] = l == 0 ? carry : up;
+    carry = (uint32_t)__shfl((int)k[i], kWave - 1, kWave);
+    hm[i] = __ballot(in && (x == 0 || k[i] != prevk[i]));
+    total += (uint32_t)popc(hm[i]);
   }
-  uint32_t tile_total;
-  const uint32_t before = block_excl_scan<uint32_t>((uint32_t)__popc(heads), tmp, &tile_total);
+  if (l == 0) wave_heads[w] = total;
+  __syncthreads();
+  uint32_t before = 0;
+  for (int x = 0; x < w; ++x) before += wave_heads[x];
   const int64_t U = counts[0];
   const int32_t n_groups = g.T * g.W;
-  int64_t uid = (int64_t)tile_base[blockIdx.x] + before - 1;
+  int64_t base = (int64_t)tile_base[blockIdx.x] + before;  // heads before this round
+  const uint64_t le = lanemask_lt() | (1ull << l);
 #pragma unroll
   for (int i = 0; i < kRounds; ++i) {
-    const int64_t x = x0 + i;
-    if (x >= n) break;
-    if ((heads >> i) & 1u) {
-      ++uid;
-      unique[uid] = (int64_t)k[i];
-      seg_offsets[uid] = (int32_t)x;
-      // group offsets: every group in (group(prev unique), group(this)] starts here
-      const int32_t gi = group_of(k[i], g);
-      const int32_t gp = uid == 0 ? -1 : group_of(x == 0 ? 0u : sk[x - 1], g);
-      for (int32_t q = gp + 1; q <= gi; ++q) unique_offsets[q] = uid;
-      if (uid == U - 1)
-        for (int32_t q = gi + 1; q <= n_groups; ++q) unique_offsets[q] = U;
+    const int64_t x = x0 + i * kWave + l;
+    const int64_t uid = base + popc(hm[i] & le) - 1;
+    if (x < n) {
+      occ_uid[x] = (int32_t)uid;
+      if ((hm[i] >> l) & 1ull) {
+        unique[uid] = (int64_t)k[i];
+        seg_offsets[uid] = (int32_t)x;
+        // every group in (group(previous unique), group(this)] starts here
+        const int32_t gi = group_of(k[i], g);
+        const int32_t gp = uid == 0 ? -1 : group_of(prevk[i], g);
+        for (int32_t q = gp + 1; q <= gi; ++q) unique_offsets[q] = uid;
+        if (uid == U - 1)
+          for (int32_t q = gi + 1; q <= n_groups; ++q) unique_offsets[q] = U;
+      }
     }
-    occ_uid[x] = (int32_t)uid;
+    base += popc(hm[i]);
   }
 }
 
@@ -253,16 +293,13 @@ k_compact(const uint32_t* __restrict__ sk, const int64_t* __restrict__ nvp, Grou
 constexpr int kMergeThreads = 256;
 constexpr int kMergeTile = 2048;
 
-// Merged order of a (new) and b (prev) with ties taken from b first.
-// Returns how many a-elements are among the first d merged elements.
+// Merged order of a (new) and b (prev) with ties taken from b first: the
+// number of a-elements among the first d merged elements is the smallest i
+// for which a[i] does not precede b[d-i-1], searched by a whole wave.
 __device__ __forceinline__ int64_t merge_split(const int64_t* a, int64_t na, const int64_t* b,
                                                int64_t nb, int64_t d) {
-  int64_t lo = d > nb ? d - nb : 0, hi = d < na ? d : na;
-  while (lo < hi) {
-    const int64_t mid = (lo + hi) >> 1;
-    if (a[mid] < b[d - mid - 1]) lo = mid + 1; else hi = mid;
-  }
-  return lo;
+  const int64_t lo = d > nb ? d - nb : 0, hi = d < na ? d : na;
+  return wave_partition_point(lo, hi, [&](int64_t i) { return a[i] < b[d - i - 1]; });
 }
 
 __device__ __forceinline__ int lds_upper(const int64_t* s, int n, int64_t v) {  // # s <= v
@@ -286,8 +323,8 @@ __device__ __forceinline__ int lds_lower(const int64_t* s, int n, int64_t v) {  
 __global__ void __launch_bounds__(kMergeThreads)
 k_collide(const int64_t* __restrict__ a, const int64_t* __restrict__ counts_a, int64_t cap_a,
           const int64_t* __restrict__ b, const int64_t* __restrict__ counts_b, int64_t cap_b,
-          uint8_t* __restrict__ cls, uint8_t* __restrict__ prev_cls, int64_t* __restrict__ counts,
-          uint32_t* __restrict__ ticket) {
+          uint8_t* __restrict__ cls, uint8_t* __restrict__ prev_cls,
+          uint32_t* __restrict__ block_hits) {
   __shared__ int64_t sa[kMergeTile + 1], sb[kMergeTile + 1];
   __shared__ int64_t span[4];
   __shared__ uint32_t hits[kMergeThreads / kWave];
@@ -297,14 +334,14 @@ k_collide(const int64_t* __restrict__ a, const int64_t* __restrict__ counts_a, i
   const int64_t d0 = (int64_t)blockIdx.x * kMergeTile;
   uint32_t mine = 0;
   if (d0 < M) {
-    if (threadIdx.x == 0) {
-      const int64_t d1 = min(M, d0 + kMergeTile);
-      const int64_t i0 = merge_split(a, na, b, nb, d0);
-      const int64_t i1 = merge_split(a, na, b, nb, d1);
-      span[0] = i0;
-      span[1] = i1;
-      span[2] = d0 - i0;
-      span[3] = d1 - i1;
+    const int w = threadIdx.x / kWave;
+    if (w < 2) {  // wave 0 splits at the tile's start, wave 1 at its end
+      const int64_t d = w == 0 ? d0 : min(M, d0 + kMergeTile);
+      const int64_t i = merge_split(a, na, b, nb, d);
+      if (lane() == 0) {
+        span[w] = i;
+        span[2 + w] = d - i;
+      }
     }
     __syncthreads();
     const int64_t i0 = span[0], i1 = span[1], j0 = span[2], j1 = span[3];
@@ -338,16 +375,28 @@ k_collide(const int64_t* __restrict__ a, const int64_t* __restrict__ counts_a, i
   if (lane() == 0) hits[threadIdx.x / kWave] = mine;
   __syncthreads();
   if (threadIdx.x == 0) {
-    uint32_t s = 0;
-    for (int k = 0; k < kMergeThreads / kWave; ++k) s += hits[k];
-    if (s) atomicAdd((unsigned long long*)&counts[1], (unsigned long long)s);
-    __threadfence();
-    const uint32_t arrived = atomicAdd(ticket, 1u);
-    if (arrived == gridDim.x - 1) {  // last block: every count is in
-      const int64_t C = (int64_t)atomicAdd((unsigned long long*)&counts[1], 0ull);
-      counts[2] = na - C;
-      counts[3] = nb - C;
-    }
+    uint32_t sum = 0;
+    for (int k = 0; k < kMergeThreads / kWave; ++k) sum += hits[k];
+    block_hits[blockIdx.x] = sum;
+  }
+}
+
+// counts[1..3] from the per-block collision counts (one block).
+__global__ void __launch_bounds__(1024)
+k_collide_counts(const uint32_t* __restrict__ block_hits, int64_t n_blocks,
+                 const int64_t* __restrict__ counts_b, int64_t cap_b,
+                 int64_t* __restrict__ counts) {
+  __shared__ int64_t tmp[17];
+  int64_t local = 0;
+  for (int64_t i = threadIdx.x; i < n_blocks; i += blockDim.x) local += block_hits[i];
+  int64_t C;
+  (void)block_excl_scan<int64_t>(local, tmp, &C);
+  if (threadIdx.x == 0) {
+    const int64_t na = counts[0];
+    const int64_t nb = counts_b ? max((int64_t)0, min(counts_b[0], cap_b)) : 0;
+    counts[1] = C;
+    counts[2] = na - C;
+    counts[3] = nb - C;
   }
 }
 
@@ -362,7 +411,8 @@ static int key_bits(int64_t key_space) {
   return b;
 }
 
-extern "C" size_t fs_unique_workspace_size(int64_t n_cap, int32_t T, int32_t W) {
+extern "C" size_t fs_unique_workspace_size(int64_t n_cap, int64_t prev_cap, int32_t T,
+                                           int32_t W) {
   (void)T;
   (void)W;
   const int64_t cap = n_cap > 0 ? n_cap : 1;
@@ -375,8 +425,9 @@ extern "C" size_t fs_unique_workspace_size(int64_t n_cap, int32_t T, int32_t W) 
   c.take<uint32_t>((size_t)kRadix * tiles);     // histograms
   c.take<uint32_t>((size_t)kRadix * kMaxPasses);  // digit totals
   c.take<uint32_t>((size_t)tiles);              // heads per tile
-  c.take<uint32_t>(1);                          // ticket
   c.take<int64_t>(1);                           // valid item count
+  c.take<uint32_t>((size_t)cdiv(cap + (prev_cap > 0 ? prev_cap : 0), kMergeTile) + 1);
+                                                // collisions per merge tile
   return c.used + 256;
 }
 
@@ -409,8 +460,8 @@ extern "C" int fs_unique_collision_split(const int64_t* shard_keys, const int32_
     base += tables[t].rows;
   }
   g.row_base[T] = base;
-  if (base > (int64_t)UINT32_MAX + 1) return FS_ERR_UNSUPPORTED;
-  if (!ws || ws_bytes < fs_unique_workspace_size(n_cap, T, W)) return FS_ERR_WORKSPACE;
+  if (base > (int64_t)UINT32_MAX) return FS_ERR_UNSUPPORTED;
+  if (!ws || ws_bytes < fs_unique_workspace_size(n_cap, prev_cap, T, W)) return FS_ERR_WORKSPACE;
 
   const int64_t cap = n_cap > 0 ? n_cap : 1;
   const int64_t tiles = cdiv(cap, kTile);
@@ -420,15 +471,15 @@ extern "C" int fs_unique_collision_split(const int64_t* shard_keys, const int32_
   int32_t* va = c.take<int32_t>((size_t)cap);
   int32_t* vb = c.take<int32_t>((size_t)cap);
   uint32_t* hist = c.take<uint32_t>((size_t)kRadix * tiles);
-  uint32_t* tot = c.take<uint32_t>((size_t)kRadix * kMaxPasses);
+  uint32_t* tot = c.take<uint32_t>((size_t)kRadix * kMaxPasses);  // digit totals per pass
   uint32_t* tile_heads = c.take<uint32_t>((size_t)tiles);
-  uint32_t* ticket = c.take<uint32_t>(1);
   int64_t* n_valid = c.take<int64_t>(1);
+  const int64_t merge_blocks = cdiv(cap + prev_cap, kMergeTile);
+  uint32_t* block_hits = c.take<uint32_t>((size_t)merge_blocks);
 
   const int kbits = key_bits(base);
   const int passes = (kbits + kRadixBits - 1) / kRadixBits;
-  hipLaunchKernelGGL(k_init, dim3(1), dim3(256), 0, stream, tot, kRadix * kMaxPasses, ticket,
-                     shard_offsets, W, n_cap, n_valid);
+  hipLaunchKernelGGL(k_init, dim3(1), dim3(64), 0, stream, shard_offsets, W, n_cap, n_valid);
   FS_LAUNCH_CHECK();
   uint32_t* kbuf[2] = {ka, kb};
   int32_t* vbuf[2] = {va, vb};
@@ -442,10 +493,10 @@ extern "C" int fs_unique_collision_split(const int64_t* shard_keys, const int32_
     int32_t* vout = (p == passes - 1) ? occ_bm : vbuf[p & 1];
     if (p == 0) {
       hipLaunchKernelGGL(k_rs_hist<int64_t>, dim3(grid), dim3(kThreads), 0, stream, shard_keys,
-                         n_valid, W, shift, mask, tiles, hist, tp);
+                         n_valid, W, shift, mask, tiles, hist);
     } else {
       hipLaunchKernelGGL(k_rs_hist<uint32_t>, dim3(grid), dim3(kThreads), 0, stream,
-                         kbuf[(p - 1) & 1], n_valid, W, shift, mask, tiles, hist, tp);
+                         kbuf[(p - 1) & 1], n_valid, W, shift, mask, tiles, hist);
     }
     FS_LAUNCH_CHECK();
     hipLaunchKernelGGL(k_rs_scan, dim3(kRadix), dim3(kThreads), 0, stream, n_valid, W,
@@ -453,11 +504,11 @@ extern "C" int fs_unique_collision_split(const int64_t* shard_keys, const int32_
     FS_LAUNCH_CHECK();
     if (p == 0) {
       hipLaunchKernelGGL(k_rs_scatter<int64_t>, dim3(grid), dim3(kThreads), 0, stream, shard_keys,
-                         shard_bm, n_valid, W, shift, mask, bits, tiles, hist, kout, vout);
+                         shard_bm, n_valid, W, shift, mask, bits, tiles, hist, tp, kout, vout);
     } else {
       hipLaunchKernelGGL(k_rs_scatter<uint32_t>, dim3(grid), dim3(kThreads), 0, stream,
                          kbuf[(p - 1) & 1], vbuf[(p - 1) & 1], n_valid, W, shift, mask,
-                         bits, tiles, hist, kout, vout);
+                         bits, tiles, hist, tp, kout, vout);
     }
     FS_LAUNCH_CHECK();
   }
@@ -471,10 +522,12 @@ extern "C" int fs_unique_collision_split(const int64_t* shard_keys, const int32_
   hipLaunchKernelGGL(k_compact, dim3(grid), dim3(kThreads), 0, stream, sk, n_valid, g,
                      tile_heads, counts, unique, seg_offsets, occ_uid, unique_offsets);
   FS_LAUNCH_CHECK();
-  const int64_t merge_blocks = cdiv(cap + prev_cap, kMergeTile);
   hipLaunchKernelGGL(k_collide, dim3((unsigned)merge_blocks), dim3(kMergeThreads), 0, stream,
-                     unique, counts, n_cap, prev_unique, prev_counts, prev_cap, cls, prev_cls, counts,
-                     ticket);
+                     unique, counts, n_cap, prev_unique, prev_counts, prev_cap, cls, prev_cls,
+                     block_hits);
+  FS_LAUNCH_CHECK();
+  hipLaunchKernelGGL(k_collide_counts, dim3(1), dim3(1024), 0, stream, block_hits, merge_blocks,
+                     prev_counts, prev_cap, counts);
   FS_LAUNCH_CHECK();
   return FS_OK;
 }

@@ -55,7 +55,7 @@ _c_bucketize = _sig("fs_bucketize_permute", C.c_int, _P, _i64, _P, _i32, _TP, _i
 _c_bucketize_ws = _sig("fs_bucketize_workspace_size", _sz, _i64, _i32, _i32, _i32)
 _c_unique = _sig("fs_unique_collision_split", C.c_int, _P, _P, _P, _i64, _TP, _i32, _i32, _P, _P,
                  _i64, _P, _P, _P, _P, _P, _P, _P, _P, _P, _sz, _P)
-_c_unique_ws = _sig("fs_unique_workspace_size", _sz, _i64, _i32, _i32)
+_c_unique_ws = _sig("fs_unique_workspace_size", _sz, _i64, _i64, _i32, _i32)
 _c_lookup = _sig("fs_jagged_lookup", C.c_int, _TP, _i32, _i32, _P, _P, _P, _P, _P, _P, _i32,
                  C.POINTER(_P), _i64, _P)
 _c_reduce = _sig("fs_grad_reduce_update", C.c_int, _TP, _i32, _i32, C.POINTER(_P), _i64, _P, _P,
@@ -201,8 +201,8 @@ def fs_bucketize_permute(ids, sample_offsets, rows, perm, rank_offsets, W, out=N
     return dict(bal_offsets=bal, shard_keys=keys, shard_bm=bm, splits=splits, shard_offsets=sho)
 
 
-def unique_workspace_size(n_cap, T, W):
-    return int(_c_unique_ws(n_cap, T, W))
+def unique_workspace_size(n_cap, T, W, prev_cap=None):
+    return int(_c_unique_ws(n_cap, n_cap if prev_cap is None else prev_cap, T, W))
 
 
 def fs_unique_collision_split(shard_keys, shard_bm, shard_offsets, n_cap, rows, W,
@@ -223,7 +223,7 @@ def fs_unique_collision_split(shard_keys, shard_bm, shard_offsets, n_cap, rows, 
         pcls = torch.empty(max(int(prev_cap), 1), dtype=torch.uint8, device=d)
     counts = _get(o, "counts", lambda: torch.empty(4, dtype=torch.int64, device=d))
     tabs = make_row_tables(rows)
-    ws = _ws(unique_workspace_size(n_cap, T, W), ws)
+    ws = _ws(unique_workspace_size(n_cap, T, W, prev_cap), ws)
     _check("fs_unique_collision_split",
            _c_unique(_ptr(shard_keys), _ptr(shard_bm), _ptr(shard_offsets), int(n_cap), tabs, T,
                      W, _ptr(prev_unique), _ptr(prev_counts), int(prev_cap) if prev_unique

@@ -2,18 +2,24 @@
 
 One step consumes the gradients of iteration i and the IDs of iteration i+1
 and leaves the embeddings of iteration i+1 in HBM ("FreeScale: distributed
-training for sequence recommendation models", section 3.2 and Algorithm 2):
+training for sequence recommendation models", section 3.2 and Algorithm 2:
+collision rows keep a strict write-then-read order, exclusive rows are
+fetched ahead of the update):
 
-  stream A  balance(i+1) -> bucketize(i+1) -> split(i+1 vs i) --event-->
-            update(i, collision rows) -> lookup(i+1, collision rows)
-  stream B  (waits for the split) lookup(i+1, exclusive rows) ->
-            update(i, exclusive rows)
-  join      stream A waits for stream B.
+  stream A  balance(i+1) -> bucketize(i+1) -> split(i+1 vs i) ->
+            lookup(i+1, exclusive rows)          [prefetched past the update]
+  stream B  update(i, every row of iteration i)  [concurrent with stream A]
+  stream A  (waits for B) lookup(i+1, collision rows)
 
-Collision rows are written before they are read; exclusive rows of i+1 are
-never written by step i and exclusive rows of i are never read by i+1, so
-the two streams touch disjoint rows and the result equals the synchronous
-loop (update everything of i, then look up everything of i+1).
+Exclusive rows of i+1 are never written by the update of i, so their lookup
+may run before or during it; collision rows are read only after it. The
+result equals the synchronous loop (update everything of i, then look up
+everything of i+1), which `step_sync` runs on one stream for reference.
+
+On one GPU the update of i does not wait for the index stages of i+1 (that
+wait exists across GPUs only because the collision split decides which
+gradients travel first), so the latency-bound index kernels overlap the
+bandwidth-bound update.
 
 Buffers are allocated once at capacity; per-iteration state is double
 buffered. Every stream keeps the default priority.
@@ -26,6 +32,45 @@ from dataclasses import dataclass, field
 import torch
 
 from . import lib
+
+
+_CLS = {lib.FS_ALL: "all", lib.FS_COLLISION: "co", lib.FS_EXCLUSIVE: "ex"}
+
+
+class _nullspan:
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *a):
+        return False
+
+
+class StageTimer:
+    """HIP event pairs around each C call, on the stream the call runs on."""
+
+    def __init__(self):
+        self.pairs = {}
+
+    def span(self, name, stream):
+        timer = self
+
+        class _Span:
+            def __enter__(self):
+                self.a = torch.cuda.Event(enable_timing=True)
+                self.b = torch.cuda.Event(enable_timing=True)
+                self.a.record(stream)
+                return self
+
+            def __exit__(self, *exc):
+                self.b.record(stream)
+                timer.pairs.setdefault(name, []).append((self.a, self.b))
+                return False
+
+        return _Span()
+
+    def ms(self):
+        """name -> list of per-call milliseconds (call after synchronising)."""
+        return {k: [a.elapsed_time(b) for a, b in v] for k, v in self.pairs.items()}
 
 
 @dataclass
@@ -71,6 +116,11 @@ class SparseStep:
         self.ev_b = torch.cuda.Event()
         self.cur = None  # IterState of iteration i (already looked up)
         self.slot = 0
+        self.timer = None  # optional StageTimer
+
+    def _t(self, name, stream):
+        """Context that brackets one C call with HIP events on its stream."""
+        return self.timer.span(name, stream) if self.timer is not None else _nullspan()
 
     def _alloc_iter(self):
         d, W, T, cap = self.dev, self.W, self.T, self.cap
@@ -105,35 +155,40 @@ class SparseStep:
         W, T = self.W, self.T
         n_tok = int(batch["ids"].shape[1])
         st.n_tok = n_tok
-        if self.w.balancer == "fbs":
-            lib.fs_balance_fbs(batch["uih_len"], W, st.perm, st.rank_offsets, err=self.err,
-                               stream=stream)
-        else:
-            lib.fs_balance_vbs(batch["uih_len"], W, self.w.alpha, st.perm, st.rank_offsets,
-                               st.rank_weight, err=self.err, ws=self.ws_bal, stream=stream)
-        lib.fs_bucketize_permute(batch["ids"], batch["sample_offsets"], self.rows, st.perm,
-                                 st.rank_offsets, W, out=st.bucket, err=self.err, ws=self.ws_bkt,
-                                 stream=stream)
+        with self._t("balance", stream):
+            if self.w.balancer == "fbs":
+                lib.fs_balance_fbs(batch["uih_len"], W, st.perm, st.rank_offsets, err=self.err,
+                                   stream=stream)
+            else:
+                lib.fs_balance_vbs(batch["uih_len"], W, self.w.alpha, st.perm, st.rank_offsets,
+                                   st.rank_weight, err=self.err, ws=self.ws_bal, stream=stream)
+        with self._t("bucketize", stream):
+            lib.fs_bucketize_permute(batch["ids"], batch["sample_offsets"], self.rows, st.perm,
+                                     st.rank_offsets, W, out=st.bucket, err=self.err,
+                                     ws=self.ws_bkt, stream=stream)
         out = dict(st.uq)
         if prev is not None:
             out["prev_cls"] = prev.cls_next
-        lib.fs_unique_collision_split(
-            st.bucket["shard_keys"], st.bucket["shard_bm"], st.bucket["shard_offsets"],
-            T * n_tok, self.rows, W,
-            prev_unique=prev.uq["unique"] if prev is not None else None,
-            prev_counts=prev.uq["counts"] if prev is not None else None,
-            prev_cap=T * prev.n_tok if prev is not None else 0, out=out, ws=self.ws_uq,
-            stream=stream)
+        with self._t("unique_split", stream):
+            lib.fs_unique_collision_split(
+                st.bucket["shard_keys"], st.bucket["shard_bm"], st.bucket["shard_offsets"],
+                T * n_tok, self.rows, W,
+                prev_unique=prev.uq["unique"] if prev is not None else None,
+                prev_counts=prev.uq["counts"] if prev is not None else None,
+                prev_cap=T * prev.n_tok if prev is not None else 0, out=out, ws=self.ws_uq,
+                stream=stream)
 
     def _lookup(self, st, which, stream):
         outs = [o[:st.n_tok] for o in st.out]
-        lib.fs_jagged_lookup(self.weights, self.W, st.uq, st.n_tok, which=which,
-                             cls=st.uq["cls"], out=outs, stream=stream)
+        with self._t(f"lookup_{_CLS[which]}", stream):
+            lib.fs_jagged_lookup(self.weights, self.W, st.uq, st.n_tok, which=which,
+                                 cls=st.uq["cls"], out=outs, stream=stream)
 
     def _update(self, st, grads, which, stream, ws):
-        lib.fs_grad_reduce_update(self.weights, self.states, self.W, grads, st.n_tok, st.uq,
-                                  self.w.optim, self.w.lr, self.w.eps, which=which,
-                                  cls=st.cls_next, ws=ws, stream=stream)
+        with self._t(f"update_{_CLS[which]}", stream):
+            lib.fs_grad_reduce_update(self.weights, self.states, self.W, grads, st.n_tok, st.uq,
+                                      self.w.optim, self.w.lr, self.w.eps, which=which,
+                                      cls=st.cls_next, ws=ws, stream=stream)
 
     # ------------------------------------------------------------------ schedule
     def prologue(self, batch):
@@ -150,15 +205,19 @@ class SparseStep:
         cur = self.cur
         nxt = self.states_buf[1 - self.slot]
         sA, sB = self.sA, self.sB
-        self._index_stages(batch_next, nxt, cur, sA)
-        self.ev_split.record(sA)
-        self._update(cur, grads_cur, lib.FS_COLLISION, sA, self.ws_red[0])
-        self._lookup(nxt, lib.FS_COLLISION, sA)
-        sB.wait_event(self.ev_split)
-        self._lookup(nxt, lib.FS_EXCLUSIVE, sB)
-        self._update(cur, grads_cur, lib.FS_EXCLUSIVE, sB, self.ws_red[1])
+        sA.wait_stream(torch.cuda.current_stream())  # inputs made on the caller's stream
+        # B may start once A has finished the previous step (iteration i's
+        # index outputs and lookups; the slot A is about to overwrite is free)
+        sB.wait_stream(sA)
+        with self._t("update_all", sB):
+            lib.fs_grad_reduce_update(self.weights, self.states, self.W, grads_cur, cur.n_tok,
+                                      cur.uq, self.w.optim, self.w.lr, self.w.eps,
+                                      which=lib.FS_ALL, ws=self.ws_red[1], stream=sB)
         self.ev_b.record(sB)
+        self._index_stages(batch_next, nxt, cur, sA)
+        self._lookup(nxt, lib.FS_EXCLUSIVE, sA)
         sA.wait_event(self.ev_b)
+        self._lookup(nxt, lib.FS_COLLISION, sA)
         self.cur = nxt
         self.slot = 1 - self.slot
         return nxt
@@ -168,10 +227,12 @@ class SparseStep:
         cur = self.cur
         nxt = self.states_buf[1 - self.slot]
         sA = self.sA
+        sA.wait_stream(torch.cuda.current_stream())
         self._index_stages(batch_next, nxt, cur, sA)
-        lib.fs_grad_reduce_update(self.weights, self.states, self.W, grads_cur, cur.n_tok,
-                                  cur.uq, self.w.optim, self.w.lr, self.w.eps, which=lib.FS_ALL,
-                                  ws=self.ws_red[0], stream=sA)
+        with self._t("update_all", sA):
+            lib.fs_grad_reduce_update(self.weights, self.states, self.W, grads_cur, cur.n_tok,
+                                      cur.uq, self.w.optim, self.w.lr, self.w.eps,
+                                      which=lib.FS_ALL, ws=self.ws_red[0], stream=sA)
         self._lookup(nxt, lib.FS_ALL, sA)
         self.cur = nxt
         self.slot = 1 - self.slot
@@ -180,6 +241,7 @@ class SparseStep:
     def epilogue(self, grads_last):
         """Update of the last iteration (no lookahead: every row exclusive)."""
         cur = self.cur
+        self.sA.wait_stream(torch.cuda.current_stream())
         lib.fs_grad_reduce_update(self.weights, self.states, self.W, grads_last, cur.n_tok,
                                   cur.uq, self.w.optim, self.w.lr, self.w.eps, which=lib.FS_ALL,
                                   ws=self.ws_red[0], stream=self.sA)

@@ -48,6 +48,8 @@ def test_workspace_queries_are_host_only_and_monotone(L):
     b = L.bucketize_workspace_size(1 << 22, 4096, 1, 512)
     assert 0 < a < b
     assert L.unique_workspace_size(1 << 22, 1, 512) >= 16 * (1 << 22)
+    assert L.unique_workspace_size(1 << 20, 1, 512, prev_cap=1 << 24) > \
+        L.unique_workspace_size(1 << 20, 1, 512, prev_cap=1 << 20)
     assert L.reduce_workspace_size(1 << 20, 256) > L.reduce_workspace_size(1 << 20, 64)
 
 

@@ -186,6 +186,8 @@ def test_prioritized_equals_synchronous(k):
         weights, states = gpu_tables(w, 50 + k)
         step = SparseStep(w, weights, states, cap)
         st = step.prologue(to_dev(batches[0]))
+        step.join()
+        torch.cuda.synchronize()
         looks = [[_bits(o[:st.n_tok]).copy() for o in st.out]]
         for i in range(K - 1):
             g = [torch.from_numpy(x).cuda() for x in balanced_grads(
