@@ -8,14 +8,25 @@
 //
 // The shard-major order (shard d, source rank r, table t, balanced sample q,
 // token j) is a stable counting sort by d of the items enumerated in (r, t,
-// q, j) order. Items are cut into tiles of 4096 that never straddle an (r, t)
-// segment, so:
-//   * every tile knows its rank and table without a search per item,
-//   * splits[d][r] is a difference of the per-shard tile-count prefix sums.
-// Four launches: prep (balanced offsets + tile table), per-tile histograms,
-// per-shard column scans (+ splits, shard totals), stable per-tile scatter
-// staged through LDS (+ shard offsets). No device-scope atomics.
+// q, j) order. Items are cut into tiles of 4096 tokens that never straddle a
+// (rank, table) segment and are numbered in (r, t, chunk) order, so an
+// item's output position is its shard's base, plus the shard's count in all
+// earlier tiles, plus its stable rank inside its tile:
+//   k_prep     balanced offsets, per-sample shifts, tile descriptors (one
+//              workgroup; every load chain is two deep)
+//   k_hist     per-tile shard histograms -> rows of a tiles x shards matrix;
+//              each item's 32-bit key, batch-major
+//   k_colsum, k_colscan   exclusive column scans of that matrix in place,
+//              with coalesced row loads (lanes = shards)
+//   k_splits   shard offsets; splits[d][r] as differences of the scanned
+//              matrix at rank boundaries (transposed through LDS)
+//   k_scatter  per tile: the keys back, stable ranks (LDS lane masks), sort
+//              by shard in LDS, one contiguous run per shard.
+// Consecutive tiles run on the same XCD (workgroups are dealt to the 8 XCDs
+// round-robin), so the short runs that neighbouring tiles of one segment
+// write next to each other meet in one L2. No device-scope atomics.
 #include "common.hpp"
+#include "divu32.hpp"
 
 namespace fs {
 namespace {
@@ -23,75 +34,118 @@ namespace {
 constexpr int kThreads = 256;  // 4 waves
 constexpr int kRounds = 16;    // items per lane
 constexpr int kWaveItems = kWave * kRounds;
-constexpr int kTile = kThreads * kRounds;  // 4096
+constexpr int kTile = kThreads * kRounds;  // 4096 tokens per tile
+constexpr int kXcd = 8;
 
 struct TableRows {
   int64_t rows[FS_MAX_TABLES];
   int64_t row_base[FS_MAX_TABLES];
   int64_t block[FS_MAX_TABLES];  // ceil(rows / W)
+  DivU32 div[FS_MAX_TABLES];     // division by block
 };
 
+constexpr uint32_t kDropKey = 0xFFFFFFFFu;  // item key of a dropped ID (keys < 2^32 - 1)
+
+struct TileDesc {
+  int64_t bm_lo;       // first batch-major token
+  int32_t n;           // tokens (<= kTile)
+  int32_t seg;         // r * T + t
+  int32_t q_lo, q_hi;  // rank r's balanced samples
+  int32_t pad[2];
+};
+
+// Grid sizes are multiples of 8; XCD x runs the x-th eighth of the tiles.
+__device__ __forceinline__ int32_t xcd_tile(int32_t bid, int32_t G) {
+  return (bid % kXcd) * (G / kXcd) + bid / kXcd;
+}
+
 // ---------------------------------------------------------------- prep
-// bal_offsets, input validation, tile table.
-__global__ void __launch_bounds__(1024)
+constexpr int kPrepThreads = 1024;
+constexpr int kPrepPer = FS_MAX_SAMPLES / kPrepThreads;  // samples per thread
+
+// Validation, bal_offsets, shift[q] = so[perm[q]] - bal[q], the tile table.
+// Thread i owns balanced samples [16 i, 16 i + 16) and rank i. Invalid input
+// (offsets not rising from 0 to n_tok, a perm entry out of range, rank
+// offsets not rising from 0 to n, or lengths under perm not summing to
+// n_tok) flags FS_EF_SHAPE and leaves zero tiles, so nothing is written
+// past the outputs.
+__global__ void __launch_bounds__(kPrepThreads)
 k_prep(const int64_t* __restrict__ so, int32_t n, int64_t n_tok, const int32_t* __restrict__ perm,
        const int32_t* __restrict__ ro, int32_t W, int32_t T, int64_t* __restrict__ bal,
-       int32_t* __restrict__ tile_pref, int32_t* __restrict__ err) {
+       int64_t* __restrict__ shift, int32_t* __restrict__ tile_pref, TileDesc* __restrict__ tiles,
+       int32_t* __restrict__ err) {
   __shared__ int64_t tmp64[17];
   __shared__ int32_t tmp32[17];
   __shared__ int bad_s;
   if (threadIdx.x == 0) bad_s = 0;
-  __syncthreads();
   bool bad = false;
-  // validate offsets and the partition
-  for (int32_t s = threadIdx.x; s <= n; s += blockDim.x) {
-    int64_t v = so[s];
-    if (s == 0 && v != 0) bad = true;
-    if (s == n && v != n_tok) bad = true;
-    if (s < n && so[s + 1] < v) bad = true;
+  for (int32_t s = threadIdx.x; s <= n; s += kPrepThreads) {
+    const int64_t v = so[s];
+    if ((s == 0 && v != 0) || (s == n && v != n_tok) || (s < n && so[s + 1] < v)) bad = true;
   }
-  for (int32_t q = threadIdx.x; q < n; q += blockDim.x) {
-    int32_t p = perm[q];
-    if (p < 0 || p >= n) bad = true;
+  const int32_t q0 = threadIdx.x * kPrepPer;
+  int64_t beg[kPrepPer];
+  int32_t len[kPrepPer];
+#pragma unroll
+  for (int k = 0; k < kPrepPer; ++k) {
+    const int32_t q = q0 + k;
+    const int32_t p = q < n ? perm[q] : 0;
+    const bool pin = p >= 0 && p < n;
+    if (q < n && !pin) bad = true;
+    beg[k] = (q < n && pin) ? so[p] : 0;
+    len[k] = (q < n && pin) ? (int32_t)(so[p + 1] - beg[k]) : 0;
   }
-  for (int32_t r = threadIdx.x; r <= W; r += blockDim.x) {
-    int32_t v = ro[r];
-    if ((r == 0 && v != 0) || (r == W && v != n) || (r < W && ro[r + 1] < v)) bad = true;
-  }
+  const int32_t r = threadIdx.x;  // W <= 1024 = blockDim.x
+  const int32_t ro_r = r <= W ? ro[r] : 0;
+  const int32_t ro_n = r < W ? ro[r + 1] : n;
+  if (r <= W && ((r == 0 && ro_r != 0) || (r == W && ro_r != n) || ro_n < ro_r)) bad = true;
+  __syncthreads();
   if (bad) atomicOr(&bad_s, 1);
   __syncthreads();
-  const bool ok = bad_s == 0;
-  if (!ok && threadIdx.x == 0 && err) atomicOr(err, FS_EF_SHAPE);
+  bool ok = bad_s == 0;
 
-  // balanced offsets: per-thread contiguous slices, then a block scan
-  const int32_t per = (n + blockDim.x - 1) / blockDim.x;
-  const int32_t q0 = min(n, (int32_t)threadIdx.x * per), q1 = min(n, q0 + per);
   int64_t local = 0;
-  for (int32_t q = q0; q < q1; ++q) {
-    int32_t s = perm[q];
-    if (ok) local += so[s + 1] - so[s];
-  }
+#pragma unroll
+  for (int k = 0; k < kPrepPer; ++k) local += ok ? len[k] : 0;
   int64_t total;
   int64_t run = block_excl_scan<int64_t>(local, tmp64, &total);
-  for (int32_t q = q0; q < q1; ++q) {
-    bal[q] = run;
-    int32_t s = perm[q];
-    if (ok) run += so[s + 1] - so[s];
+  ok = ok && total == n_tok;  // perm repeats a sample: refuse before any tile exists
+  if (!ok && threadIdx.x == 0 && err) atomicOr(err, FS_EF_SHAPE);
+#pragma unroll
+  for (int k = 0; k < kPrepPer; ++k) {
+    const int32_t q = q0 + k;
+    if (q < n) {
+      bal[q] = run;
+      shift[q] = beg[k] - run;
+    }
+    run += len[k];
   }
   if (threadIdx.x == 0) bal[n] = total;
-  __syncthreads();
+  __syncthreads();  // bal visible to the workgroup
 
-  // tile table: rank r owns T * ceil(m_r / kTile) tiles (t-major)
-  int32_t r = threadIdx.x;  // W <= 1024 = blockDim.x
-  int32_t my_tiles = 0;
+  // rank r owns T * ceil(m_r / kTile) tiles, t-major
+  int64_t A = 0, m = 0;
+  int32_t c = 0;
   if (ok && r < W) {
-    int64_t m = bal[ro[r + 1]] - bal[ro[r]];
-    my_tiles = (int32_t)(T * cdiv(m, kTile));
+    A = bal[ro_r];
+    m = bal[ro_n] - A;
+    c = (int32_t)cdiv(m, kTile);
   }
   int32_t ttot;
-  int32_t pref = block_excl_scan<int32_t>(my_tiles, tmp32, &ttot);
+  const int32_t pref = block_excl_scan<int32_t>(T * c, tmp32, &ttot);
   if (r < W) tile_pref[r] = pref;
   if (threadIdx.x == 0) tile_pref[W] = ttot;
+  for (int32_t t = 0; t < T; ++t)
+    for (int32_t k = 0; k < c; ++k) {
+      TileDesc d;
+      d.bm_lo = A + (int64_t)k * kTile;
+      d.n = (int32_t)min((int64_t)kTile, m - (int64_t)k * kTile);
+      d.seg = r * T + t;
+      d.q_lo = ro_r;
+      d.q_hi = ro_n;
+      d.pad[0] = d.pad[1] = 0;
+      tiles[pref + t * c + k] = d;
+    }
 }
 
 // ---------------------------------------------------------------- tiles
@@ -102,25 +156,15 @@ struct TileInfo {
 };
 
 __device__ __forceinline__ bool tile_info(int32_t tile, const int32_t* tile_pref, int32_t W,
-                                          int32_t T, const int64_t* bal, const int32_t* ro,
-                                          TileInfo& ti) {
+                                          int32_t T, const TileDesc* tiles, TileInfo& ti) {
   if (tile >= tile_pref[W]) return false;
-  int32_t lo = 0, hi = W;  // largest r with tile_pref[r] <= tile
-  while (hi - lo > 1) {
-    int32_t mid = (lo + hi) >> 1;
-    if (tile_pref[mid] <= tile) lo = mid; else hi = mid;
-  }
-  const int32_t r = lo;
-  const int32_t per_t = (tile_pref[r + 1] - tile_pref[r]) / T;
-  const int32_t local = tile - tile_pref[r];
-  ti.r = r;
-  ti.t = local / per_t;
-  const int32_t k = local % per_t;
-  ti.q_lo = ro[r];
-  ti.q_hi = ro[r + 1];
-  const int64_t A = bal[ti.q_lo], B = bal[ti.q_hi];
-  ti.bm_lo = A + (int64_t)k * kTile;
-  ti.bm_hi = min(B, ti.bm_lo + kTile);
+  const TileDesc d = tiles[tile];
+  ti.r = d.seg / T;
+  ti.t = d.seg % T;
+  ti.bm_lo = d.bm_lo;
+  ti.bm_hi = d.bm_lo + d.n;
+  ti.q_lo = d.q_lo;
+  ti.q_hi = d.q_hi;
   return true;
 }
 
@@ -129,20 +173,20 @@ __device__ __forceinline__ bool tile_info(int32_t tile, const int32_t* tile_pref
 // and bin (shard, -1 for a dropped ID, `sentinel` past the tile's end).
 //
 // The wave finds the balanced sample of its first token with one cooperative
-// search, then loads a window of 64 samples: their end offsets and the shift
-// from batch-major to original token index (so[perm[q]] - bal[q]). A lane
-// finds its token's sample in the window by binary lifting over the window
-// with shuffles; the window restarts at each round's first sample, and a lane
-// whose token lies past the window (only possible with runs of empty
-// samples) walks forward on its own. All 16 ID loads are independent.
+// search, then loads a window of 64 samples: their end offsets and shifts
+// from batch-major to original token index. A lane finds its token's sample
+// in the window by binary lifting over the window with shuffles; the window
+// restarts at each round's first sample, and a lane whose token lies past
+// the window (only possible with runs of empty samples) walks forward on its
+// own. All 16 ID loads are independent.
 struct Window {
-  int32_t qa;    // first sample of the window
-  int64_t bnd;   // this lane: end offset of sample qa + lane (INT64_MAX past q_hi)
-  int64_t shift; // this lane: so[perm[q]] - bal[q] for q = qa + lane
+  int32_t qa;     // first sample of the window
+  int64_t bnd;    // this lane: end offset of sample qa + lane (INT64_MAX past q_hi)
+  int64_t shift;  // this lane: shift[qa + lane]
 };
 
 __device__ __forceinline__ Window load_window(int32_t qa, int32_t q_hi, const int64_t* bal,
-                                              const int32_t* perm, const int64_t* so) {
+                                              const int64_t* shift) {
   Window win;
   win.qa = qa;
   const int32_t q = qa + lane();
@@ -150,16 +194,15 @@ __device__ __forceinline__ Window load_window(int32_t qa, int32_t q_hi, const in
   win.shift = 0;
   if (q < q_hi) {
     win.bnd = bal[q + 1];
-    win.shift = so[perm[q]] - bal[q];
+    win.shift = shift[q];
   }
   return win;
 }
 
 __device__ __forceinline__ void wave_items(const TileInfo& ti, int32_t w, const int64_t* ids,
-                                           const int64_t* so, const int32_t* perm,
-                                           const int64_t* bal, int64_t n_tok,
-                                           const TableRows& tr, int32_t sentinel,
-                                           int64_t (&key)[kRounds], int32_t (&bin)[kRounds]) {
+                                           const int64_t* shift, const int64_t* bal,
+                                           int64_t n_tok, const TableRows& tr, int32_t sentinel,
+                                           uint32_t (&key)[kRounds], int32_t (&bin)[kRounds]) {
   const int64_t first = ti.bm_lo + (int64_t)w * kWaveItems;
 #pragma unroll
   for (int i = 0; i < kRounds; ++i) {
@@ -170,9 +213,10 @@ __device__ __forceinline__ void wave_items(const TileInfo& ti, int32_t w, const 
   // sample of the first token: one past the last q in (q_lo, q_hi) with bal[q] <= first
   const int32_t qa = (int32_t)wave_partition_point(
       ti.q_lo + 1, ti.q_hi, [&](int64_t q) { return bal[q] <= first; }) - 1;
-  Window win = load_window(qa, ti.q_hi, bal, perm, so);
+  Window win = load_window(qa, ti.q_hi, bal, shift);
   const int t = ti.t;
-  const int64_t rows = tr.rows[t], rbase = tr.row_base[t], block = tr.block[t];
+  const int64_t rows = tr.rows[t], rbase = tr.row_base[t];
+  const DivU32 div = tr.div[t];
   int64_t tok[kRounds];
   bool valid[kRounds];
 #pragma unroll
@@ -182,7 +226,7 @@ __device__ __forceinline__ void wave_items(const TileInfo& ti, int32_t w, const 
       // restart the window at the round's first sample (a round of 64
       // tokens then spans at most the window, unless samples are empty)
       const int kf = popc(__ballot(win.bnd <= rb));
-      if (kf > 0) win = load_window(win.qa + kf, ti.q_hi, bal, perm, so);
+      if (kf > 0) win = load_window(win.qa + kf, ti.q_hi, bal, shift);
     }
     const int64_t bm = rb + lane();
     valid[i] = bm < ti.bm_hi;
@@ -198,7 +242,7 @@ __device__ __forceinline__ void wave_items(const TileInfo& ti, int32_t w, const 
     if (valid[i] && pos >= kWave) {  // past the window: walk (rare)
       int32_t q = win.qa + kWave - 1;
       while (q + 1 < ti.q_hi && bal[q + 1] <= bm) ++q;
-      sh = so[perm[q]] - bal[q];
+      sh = shift[q];
     }
     tok[i] = bm + sh;
   }
@@ -207,196 +251,270 @@ __device__ __forceinline__ void wave_items(const TileInfo& ti, int32_t w, const 
     if (!valid[i]) continue;
     const int64_t id = ids[(int64_t)t * n_tok + tok[i]];
     const bool in = id >= 0 && id < rows;
-    key[i] = rbase + id;
-    bin[i] = in ? (int32_t)(id / block) : -1;
+    key[i] = (uint32_t)(rbase + id);
+    bin[i] = in ? (int32_t)divu32((uint32_t)id, div) : -1;
   }
 }
 
 // ---------------------------------------------------------------- histogram
+// One row of the tiles x shards count matrix per tile (zeros for unused
+// tiles); column W counts dropped IDs. Also stores every item's 32-bit key
+// (kDropKey for a dropped ID) at ikey[t * n_tok + bm], so the scatter reads
+// its tile's items back coalesced instead of walking the samples again.
 __global__ void __launch_bounds__(kThreads)
-k_hist(const int64_t* __restrict__ ids, int64_t n_tok, const int64_t* __restrict__ so,
-       const int32_t* __restrict__ perm, const int32_t* __restrict__ ro,
-       const int64_t* __restrict__ bal, const int32_t* __restrict__ tile_pref, TableRows tr,
-       int32_t W, int32_t T, int64_t tiles_cap, uint32_t* __restrict__ hist,
+k_hist(const int64_t* __restrict__ ids, int64_t n_tok, const int64_t* __restrict__ shift,
+       const int64_t* __restrict__ bal, const int32_t* __restrict__ tile_pref,
+       const TileDesc* __restrict__ tiles, TableRows tr, int32_t W, int32_t T, int32_t nbits,
+       uint32_t* __restrict__ counts, int32_t ld, uint32_t* __restrict__ ikey,
        int32_t* __restrict__ err) {
   __shared__ uint32_t h[FS_MAX_RANKS + 1];
-  TileInfo ti;
-  const int32_t tile = blockIdx.x;
-  if (!tile_info(tile, tile_pref, W, T, bal, ro, ti)) return;
+  const int32_t tile = xcd_tile(blockIdx.x, gridDim.x);
   for (int b = threadIdx.x; b <= W; b += kThreads) h[b] = 0;
   __syncthreads();
-  const int32_t w = threadIdx.x / kWave;
-  int64_t key[kRounds];
-  int32_t bin[kRounds];
-  wave_items(ti, w, ids, so, perm, bal, n_tok, tr, W + 1, key, bin);
-  bool dropped_any = false;
-  int nbits = 1;
-  while ((1 << nbits) - 1 <= W + 1) ++nbits;
-  const uint64_t lt = lanemask_lt();
-#pragma unroll
-  for (int i = 0; i < kRounds; ++i) {
-    int32_t b = bin[i];
-    if (b < 0) {
-      b = W;
-      dropped_any = true;
-    }
-    // one LDS add per distinct shard of the round (hot rows share a shard)
-    const uint64_t peers = match_bits((uint32_t)b, nbits);
-    if (b != W + 1 && (peers & lt) == 0) atomicAdd(&h[b], (uint32_t)popc(peers));
-  }
-  flag_err(err, dropped_any, FS_EF_ID_RANGE);
-  __syncthreads();
-  for (int b = threadIdx.x; b <= W; b += kThreads) hist[(int64_t)b * tiles_cap + tile] = h[b];
-}
-
-// ---------------------------------------------------------------- column scan
-// One workgroup per bin b (shard d = b, or b == W for dropped items): the
-// bin's tile counts become exclusive offsets within the bin, in place; the
-// bin total goes to tot[b]; splits[b][r] sums rank r's tiles (the tiles of a
-// rank are contiguous). The bins' global bases are formed by the scatter.
-__global__ void __launch_bounds__(kThreads)
-k_scan(const int32_t* __restrict__ tile_pref, int32_t W, int64_t tiles_cap,
-       uint32_t* __restrict__ hist, uint32_t* __restrict__ tot, int64_t* __restrict__ splits) {
-  __shared__ int64_t tmp[17];
-  const int32_t b = blockIdx.x;
-  const int32_t n_tiles = tile_pref[W];
-  uint32_t* col = hist + (int64_t)b * tiles_cap;
-  int64_t carry = 0;
-  for (int32_t c0 = 0; c0 < n_tiles; c0 += kThreads) {
-    const int32_t c = c0 + threadIdx.x;
-    const int64_t v = c < n_tiles ? col[c] : 0;
-    int64_t sum;
-    const int64_t ex = block_excl_scan<int64_t>(v, tmp, &sum);
-    if (c < n_tiles) col[c] = (uint32_t)(carry + ex);
-    carry += sum;
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) tot[b] = (uint32_t)carry;
-  if (b < W) {
-    for (int32_t r = threadIdx.x; r < W; r += kThreads) {
-      const int32_t a = tile_pref[r], z = tile_pref[r + 1];
-      const int64_t pa = a < n_tiles ? (int64_t)col[a] : carry;
-      const int64_t pz = z < n_tiles ? (int64_t)col[z] : carry;
-      splits[(int64_t)b * W + r] = pz - pa;
-    }
-  }
-}
-
-// ---------------------------------------------------------------- scatter
-// Each tile ranks its items stably per bin (ballot match inside a wave, wave
-// order across waves), derives every bin's global base from the bin totals,
-// sorts the tile by bin in LDS and writes each bin's run contiguously.
-// Workgroup 0 also publishes the shard offsets.
-__global__ void __launch_bounds__(kThreads)
-k_scatter(const int64_t* __restrict__ ids, int64_t n_tok, const int64_t* __restrict__ so,
-          const int32_t* __restrict__ perm, const int32_t* __restrict__ ro,
-          const int64_t* __restrict__ bal, const int32_t* __restrict__ tile_pref, TableRows tr,
-          int32_t W, int32_t T, int32_t nbits, int64_t tiles_cap,
-          const uint32_t* __restrict__ hist, const uint32_t* __restrict__ tot,
-          int64_t* __restrict__ shard_keys, int32_t* __restrict__ shard_bm,
-          int64_t* __restrict__ shard_offsets) {
-  __shared__ uint32_t cnt[kThreads / kWave][FS_MAX_RANKS + 1];
-  __shared__ uint32_t gbase[FS_MAX_RANKS + 1];  // global start of each bin
-  __shared__ uint32_t tbin[FS_MAX_RANKS + 1];   // start of each bin in the sorted tile
-  __shared__ uint32_t skey[kTile];
-  __shared__ int32_t sbm[kTile];
-  __shared__ uint16_t sbin[kTile];
-  __shared__ int64_t tmp[17];
   TileInfo ti;
-  const int32_t tile = blockIdx.x;
-  const bool has_tile = tile_info(tile, tile_pref, W, T, bal, ro, ti);
-  if (!has_tile && tile != 0) return;
-  const int32_t w = threadIdx.x / kWave;
-  const int32_t nb = W + 1;
-  // global bin bases: exclusive scan of the bin totals (4+ bins per thread)
-  {
+  if (tile_info(tile, tile_pref, W, T, tiles, ti)) {
+    const int32_t sentinel = (1 << nbits) - 1;  // > W: lanes without an item
+    const int32_t w = threadIdx.x / kWave;
+    uint32_t key[kRounds];
+    int32_t bin[kRounds];
+    wave_items(ti, w, ids, shift, bal, n_tok, tr, sentinel, key, bin);
+    uint32_t* out = ikey + (int64_t)ti.t * n_tok + ti.bm_lo + (int64_t)w * kWaveItems + lane();
+    bool dropped_any = false;
+#pragma unroll
+    for (int i = 0; i < kRounds; ++i) {
+      const int32_t b = bin[i];
+      if (b == sentinel) continue;
+      dropped_any |= b < 0;
+      atomicAdd(&h[b < 0 ? W : b], 1u);
+      out[i * kWave] = b < 0 ? kDropKey : key[i];
+    }
+    flag_err(err, dropped_any, FS_EF_ID_RANGE);
+  }
+  __syncthreads();
+  for (int b = threadIdx.x; b <= W; b += kThreads) counts[(int64_t)tile * ld + b] = h[b];
+}
+
+// ---------------------------------------------------------------- column scans
+// Lanes are columns (64 per workgroup, coalesced row loads); each wave takes
+// 32 consecutive rows, a workgroup 128.
+constexpr int kColRows = 32;
+constexpr int kColBlockRows = kColRows * (kThreads / kWave);
+
+__global__ void __launch_bounds__(kThreads)
+k_colsum(const uint32_t* __restrict__ counts, int32_t ld, int32_t G, int32_t C,
+         uint32_t* __restrict__ part) {
+  __shared__ uint32_t wsum[kThreads / kWave][kWave];
+  const int w = threadIdx.x / kWave, l = lane();
+  const int32_t c = blockIdx.y * kWave + l;
+  const int32_t r0 = blockIdx.x * kColBlockRows + w * kColRows;
+  uint32_t s = 0;
+  if (c < C) {
+#pragma unroll
+    for (int i = 0; i < kColRows; ++i)
+      if (r0 + i < G) s += counts[(int64_t)(r0 + i) * ld + c];
+  }
+  wsum[w][l] = s;
+  __syncthreads();
+  if (w == 0 && c < C)
+    part[(int64_t)blockIdx.x * ld + c] = wsum[0][l] + wsum[1][l] + wsum[2][l] + wsum[3][l];
+}
+
+// counts[r][c] <- sum of counts[r'][c] over r' < r; tot[c] <- column total.
+__global__ void __launch_bounds__(kThreads)
+k_colscan(uint32_t* __restrict__ counts, int32_t ld, int32_t G, int32_t C,
+          const uint32_t* __restrict__ part, uint32_t* __restrict__ tot) {
+  __shared__ uint32_t wsum[kThreads / kWave][kWave];
+  const int w = threadIdx.x / kWave, l = lane();
+  const int32_t c = blockIdx.y * kWave + l;
+  const int32_t r0 = blockIdx.x * kColBlockRows + w * kColRows;
+  const bool on = c < C;
+  uint32_t base = 0;
+  if (on)
+    for (int32_t k = 0; k < (int32_t)blockIdx.x; ++k) base += part[(int64_t)k * ld + c];
+  uint32_t v[kColRows];
+  uint32_t s = 0;
+#pragma unroll
+  for (int i = 0; i < kColRows; ++i) {
+    v[i] = (on && r0 + i < G) ? counts[(int64_t)(r0 + i) * ld + c] : 0u;
+    s += v[i];
+  }
+  wsum[w][l] = s;
+  __syncthreads();
+  for (int x = 0; x < w; ++x) base += wsum[x][l];
+  if (!on) return;
+#pragma unroll
+  for (int i = 0; i < kColRows; ++i) {
+    if (r0 + i < G) counts[(int64_t)(r0 + i) * ld + c] = base;
+    base += v[i];
+  }
+  if (blockIdx.x == gridDim.x - 1 && w == kThreads / kWave - 1) tot[c] = base;
+}
+
+// ---------------------------------------------------------------- splits
+// Workgroup (x, y): ranks [64x, 64x + 64) x shards [64y, 64y + 64) of
+// splits[d][r] = (scanned count of shard d at rank r + 1's first tile) -
+// (at rank r's first tile); rows past the matrix read the column totals.
+// Workgroup (0, 0) also writes shard_offsets = exclusive scan of the totals
+// (entry W: the valid items; dropped IDs follow it).
+__global__ void __launch_bounds__(kThreads)
+k_splits(const uint32_t* __restrict__ counts, int32_t ld, int32_t G,
+         const int32_t* __restrict__ tile_pref, const uint32_t* __restrict__ tot, int32_t W,
+         int64_t* __restrict__ splits, int64_t* __restrict__ shard_offsets) {
+  __shared__ int64_t tr_[kWave][kWave + 1];
+  __shared__ int64_t tmp[17];
+  const int w = threadIdx.x / kWave, l = lane();
+  if (blockIdx.x == 0 && blockIdx.y == 0) {
     constexpr int kPer = (FS_MAX_RANKS + 1 + kThreads - 1) / kThreads;
     uint32_t v[kPer];
     int64_t local = 0;
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
       const int b = threadIdx.x * kPer + k;
-      v[k] = b < nb ? tot[b] : 0u;
+      v[k] = b <= W ? tot[b] : 0u;
       local += v[k];
     }
     int64_t all;
-    int64_t run = block_excl_scan<int64_t>(local, tmp, &all);
+    int64_t base = block_excl_scan<int64_t>(local, tmp, &all);
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
       const int b = threadIdx.x * kPer + k;
-      if (b < nb) {
-        gbase[b] = (uint32_t)run;
-        if (tile == 0) shard_offsets[b] = run;
-      }
-      run += v[k];
+      if (b <= W) shard_offsets[b] = base;
+      base += v[k];
     }
   }
-  if (!has_tile) return;
-  const int32_t sentinel = (1 << nbits) - 1;  // > W: lanes without an item
-  for (int b = lane(); b <= W; b += kWave) cnt[w][b] = 0;
-  int64_t key[kRounds];
-  int32_t bin[kRounds], rk[kRounds];
-  wave_items(ti, w, ids, so, perm, bal, n_tok, tr, sentinel, key, bin);
-  const uint64_t lt = lanemask_lt();
-#pragma unroll
-  for (int i = 0; i < kRounds; ++i) {
-    int32_t b = bin[i];
-    if (b < 0) b = W;
-    bin[i] = b;
-    const uint64_t peers = match_bits((uint32_t)b, nbits);
-    const uint32_t before = cnt[w][b == sentinel ? 0 : b];
-    rk[i] = (int32_t)before + popc(peers & lt);
-    if (b != sentinel && (peers & lt) == 0) cnt[w][b] = before + (uint32_t)popc(peers);
+  const int32_t d = blockIdx.y * kWave + l;
+  for (int rl = w; rl < kWave; rl += kThreads / kWave) {
+    const int32_t r = blockIdx.x * kWave + rl;
+    int64_t val = 0;
+    if (r < W && d < W) {
+      const int32_t a = tile_pref[r], z = tile_pref[r + 1];
+      const uint32_t va = a < G ? counts[(int64_t)a * ld + d] : tot[d];
+      const uint32_t vz = z < G ? counts[(int64_t)z * ld + d] : tot[d];
+      val = (int64_t)vz - (int64_t)va;
+    }
+    tr_[rl][l] = val;
   }
   __syncthreads();
-  // per bin: exclusive prefix over the waves, then the bins' starts in the tile
+  const int32_t r = blockIdx.x * kWave + l;
+  for (int dl = w; dl < kWave; dl += kThreads / kWave) {
+    const int32_t dd = blockIdx.y * kWave + dl;
+    if (r < W && dd < W) splits[(int64_t)dd * W + r] = tr_[l][dl];
+  }
+}
+
+// ---------------------------------------------------------------- scatter
+// Staging area of one tile: first the per-wave lane-mask tables of the
+// ranking, then the tile's items sorted by shard.
+union ScatterStage {
+  uint64_t peers[kThreads / kWave][FS_MAX_RANKS + 1];
+  struct {
+    uint32_t key[kTile];
+    int32_t bm[kTile];
+    uint16_t bin[kTile];
+  } s;
+};
+
+__global__ void __launch_bounds__(kThreads)
+k_scatter(const uint32_t* __restrict__ ikey, int64_t n_tok, const int32_t* __restrict__ tile_pref,
+          const TileDesc* __restrict__ tiles, TableRows tr, int32_t W, int32_t T, int32_t nbits,
+          const uint32_t* __restrict__ offs, int32_t ld, const int64_t* __restrict__ shard_offsets,
+          int64_t* __restrict__ shard_keys, int32_t* __restrict__ shard_bm) {
+  __shared__ uint16_t cnt[kThreads / kWave][FS_MAX_RANKS + 1];
+  __shared__ uint32_t run[FS_MAX_RANKS + 1];   // output position of each shard's run
+  __shared__ uint32_t tbin[FS_MAX_RANKS + 1];  // start of each shard in the sorted tile
+  __shared__ ScatterStage st;
+  __shared__ int64_t tmp[17];
+  constexpr int kPer = (FS_MAX_RANKS + 1 + kThreads - 1) / kThreads;
+  const int32_t tile = xcd_tile(blockIdx.x, gridDim.x);
+  TileInfo ti;
+  if (!tile_info(tile, tile_pref, W, T, tiles, ti)) return;  // uniform per workgroup
+  const int32_t nb = W + 1;
+  const int32_t w = threadIdx.x / kWave;
+  for (int b = threadIdx.x; b < nb; b += kThreads)
+    run[b] = (uint32_t)(shard_offsets[b] + offs[(int64_t)tile * ld + b]);
+  for (int b = lane(); b < nb; b += kWave) {
+    cnt[w][b] = 0;
+    st.peers[w][b] = 0;
+  }
+  const int32_t sentinel = (1 << nbits) - 1;  // > W: lanes without an item
+  const int t = ti.t;
+  const uint32_t rbase = (uint32_t)tr.row_base[t];
+  const DivU32 div = tr.div[t];
+  const int64_t first = ti.bm_lo + (int64_t)w * kWaveItems;
+  const uint32_t* in = ikey + (int64_t)t * n_tok + first + lane();
+  uint32_t key[kRounds];
+  int32_t bin[kRounds];
+#pragma unroll
+  for (int i = 0; i < kRounds; ++i) {
+    const bool valid = first + i * kWave + lane() < ti.bm_hi;
+    key[i] = valid ? in[i * kWave] : 0u;
+    bin[i] = !valid ? sentinel : key[i] == kDropKey ? W : (int32_t)divu32(key[i] - rbase, div);
+  }
+  // stable rank of each item among the wave's items of its shard
+  const uint64_t lt = lanemask_lt();
+  int32_t rk[kRounds];
+#pragma unroll
+  for (int i = 0; i < kRounds; ++i) {
+    const int32_t b = bin[i];
+    const bool on = b != sentinel;
+    const uint64_t peers = lds_peers(st.peers[w], (uint32_t)(on ? b : 0), on);
+    const uint32_t before = cnt[w][on ? b : 0];
+    rk[i] = (int32_t)before + popc(peers & lt);
+    if (on && (peers & lt) == 0) cnt[w][b] = (uint16_t)(before + (uint32_t)popc(peers));
+  }
+  __syncthreads();
+  // per shard: exclusive prefix over the waves, then the shards' starts in the tile
   {
-    constexpr int kPer = (FS_MAX_RANKS + 1 + kThreads - 1) / kThreads;
-    uint32_t tot_b[kPer];
+    uint32_t tb[kPer];
     int64_t local = 0;
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
       const int b = threadIdx.x * kPer + k;
-      uint32_t run = 0;
+      uint32_t r = 0;
       if (b < nb) {
 #pragma unroll
         for (int x = 0; x < kThreads / kWave; ++x) {
           const uint32_t c = cnt[x][b];
-          cnt[x][b] = run;
-          run += c;
+          cnt[x][b] = (uint16_t)r;
+          r += c;
         }
       }
-      tot_b[k] = run;
-      local += run;
+      tb[k] = r;
+      local += r;
     }
     int64_t all;
-    int64_t run = block_excl_scan<int64_t>(local, tmp, &all);
+    int64_t r0 = block_excl_scan<int64_t>(local, tmp, &all);
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
       const int b = threadIdx.x * kPer + k;
-      if (b < nb) tbin[b] = (uint32_t)run;
-      run += tot_b[k];
+      if (b < nb) tbin[b] = (uint32_t)r0;
+      r0 += tb[k];
     }
   }
-  __syncthreads();
-  const int32_t bm_base = (int32_t)(ti.bm_lo + (int64_t)w * kWaveItems);
+  __syncthreads();  // also ends every wave's use of the mask tables
 #pragma unroll
   for (int i = 0; i < kRounds; ++i) {
     const int32_t b = bin[i];
     if (b == sentinel) continue;
     const uint32_t p = tbin[b] + cnt[w][b] + (uint32_t)rk[i];
-    skey[p] = (uint32_t)key[i];
-    sbm[p] = bm_base + i * kWave + lane();
-    sbin[p] = (uint16_t)b;
+    st.s.key[p] = key[i];
+    st.s.bm[p] = (int32_t)(first + i * kWave + lane());
+    st.s.bin[p] = (uint16_t)b;
   }
   __syncthreads();
   const int m = (int)(ti.bm_hi - ti.bm_lo);
   for (int p = threadIdx.x; p < m; p += kThreads) {
-    const int b = sbin[p];
-    const int64_t pos = (int64_t)gbase[b] + hist[(int64_t)b * tiles_cap + tile] + (p - (int)tbin[b]);
-    shard_keys[pos] = (int64_t)skey[p];
-    shard_bm[pos] = sbm[p];
+    const int b = st.s.bin[p];
+    const int64_t pos = (int64_t)run[b] + (p - (int)tbin[b]);
+    shard_keys[pos] = (int64_t)st.s.key[p];
+    shard_bm[pos] = st.s.bm[p];
   }
+}
+
+// tiles the launches cover: an upper bound on sum_r T * ceil(m_r / 4096),
+// rounded up to a multiple of the XCD count
+int32_t grid_tiles(int64_t n_tok, int32_t T, int32_t W) {
+  return (int32_t)align_up((size_t)(T * (cdiv(n_tok, kTile) + W)), kXcd);
 }
 
 }  // namespace
@@ -404,16 +522,17 @@ k_scatter(const int64_t* __restrict__ ids, int64_t n_tok, const int64_t* __restr
 
 using namespace fs;
 
-static int64_t tiles_capacity(int64_t n_tok, int32_t T, int32_t W) {
-  return (int64_t)T * (cdiv(n_tok, kTile) + W);
-}
-
 extern "C" size_t fs_bucketize_workspace_size(int64_t n_tok, int32_t n, int32_t T, int32_t W) {
-  (void)n;
+  const int64_t G = grid_tiles(n_tok > 0 ? n_tok : 0, T, W);
+  const int64_t ld = (int64_t)align_up((size_t)W + 1, kWave);
   Carve c(nullptr);
-  c.take<int32_t>((size_t)W + 1);                                       // tile_pref
-  c.take<uint32_t>((size_t)W + 1);                                      // tot
-  c.take<uint32_t>((size_t)(W + 1) * (size_t)tiles_capacity(n_tok, T, W));  // hist
+  c.take<int64_t>((size_t)(n > 0 ? n : 1));                 // shift
+  c.take<int32_t>((size_t)W + 1);                           // tile_pref
+  c.take<TileDesc>((size_t)G);                              // tiles
+  c.take<uint32_t>((size_t)(G * ld));                       // counts, then offsets
+  c.take<uint32_t>((size_t)(cdiv(G, kColBlockRows) * ld));  // column partials
+  c.take<uint32_t>((size_t)ld);                             // column totals
+  c.take<uint32_t>((size_t)(T * (n_tok > 0 ? n_tok : 1)));  // item keys, batch-major
   return c.used + 256;
 }
 
@@ -439,35 +558,41 @@ extern "C" int fs_bucketize_permute(const int64_t* ids, int64_t n_tok,
     tr.row_base[t] = base;
     tr.block[t] = cdiv(tables[t].rows, W);
     base += tables[t].rows;
+    if (base <= (int64_t)UINT32_MAX) tr.div[t] = make_divu32((uint32_t)tr.block[t]);
   }
   if (base > (int64_t)UINT32_MAX) return FS_ERR_UNSUPPORTED;
   if (!ws || ws_bytes < fs_bucketize_workspace_size(n_tok, n, T, W)) return FS_ERR_WORKSPACE;
-  const int64_t tiles_cap = tiles_capacity(n_tok, T, W);
-  if (tiles_cap >= INT32_MAX) return FS_ERR_UNSUPPORTED;
+  const int32_t G = grid_tiles(n_tok, T, W);
+  const int32_t ld = (int32_t)align_up((size_t)W + 1, kWave);
   Carve c(ws);
+  int64_t* shift = c.take<int64_t>((size_t)(n > 0 ? n : 1));
   int32_t* tile_pref = c.take<int32_t>((size_t)W + 1);
-  uint32_t* tot = c.take<uint32_t>((size_t)W + 1);
-  uint32_t* hist = c.take<uint32_t>((size_t)(W + 1) * (size_t)tiles_cap);
+  TileDesc* tiles = c.take<TileDesc>((size_t)G);
+  uint32_t* counts = c.take<uint32_t>((size_t)G * ld);
+  uint32_t* part = c.take<uint32_t>((size_t)cdiv(G, kColBlockRows) * ld);
+  uint32_t* tot = c.take<uint32_t>((size_t)ld);
+  uint32_t* ikey = c.take<uint32_t>((size_t)(T * (n_tok > 0 ? n_tok : 1)));
   int nbits = 1;
   while ((1 << nbits) - 1 <= W) ++nbits;  // sentinel (2^nbits - 1) > W
+  const dim3 col_grid((unsigned)cdiv(G, kColBlockRows), (unsigned)cdiv(W + 1, kWave));
+  const dim3 split_grid((unsigned)cdiv(W, kWave), (unsigned)cdiv(W, kWave));
 
-  hipLaunchKernelGGL(k_prep, dim3(1), dim3(1024), 0, stream, sample_offsets, n, n_tok, perm,
-                     rank_offsets, W, T, bal_offsets, tile_pref, err);
+  hipLaunchKernelGGL(k_prep, dim3(1), dim3(kPrepThreads), 0, stream, sample_offsets, n, n_tok,
+                     perm, rank_offsets, W, T, bal_offsets, shift, tile_pref, tiles, err);
   FS_LAUNCH_CHECK();
-  if (tiles_cap > 0) {
-    hipLaunchKernelGGL(k_hist, dim3((unsigned)tiles_cap), dim3(kThreads), 0, stream, ids, n_tok,
-                       sample_offsets, perm, rank_offsets, bal_offsets, tile_pref, tr, W, T,
-                       tiles_cap, hist, err);
-    FS_LAUNCH_CHECK();
-  }
-  hipLaunchKernelGGL(k_scan, dim3(W + 1), dim3(kThreads), 0, stream, tile_pref, W, tiles_cap, hist,
-                     tot, splits);
+  hipLaunchKernelGGL(k_hist, dim3(G), dim3(kThreads), 0, stream, ids, n_tok, shift, bal_offsets,
+                     tile_pref, tiles, tr, W, T, nbits, counts, ld, ikey, err);
   FS_LAUNCH_CHECK();
-  // at least one workgroup runs: workgroup 0 writes the shard offsets
-  hipLaunchKernelGGL(k_scatter, dim3((unsigned)(tiles_cap > 0 ? tiles_cap : 1)), dim3(kThreads),
-                     0, stream, ids, n_tok, sample_offsets, perm, rank_offsets, bal_offsets,
-                     tile_pref, tr, W, T, nbits, tiles_cap, hist, tot, shard_keys, shard_bm,
-                     shard_offsets);
+  hipLaunchKernelGGL(k_colsum, col_grid, dim3(kThreads), 0, stream, counts, ld, G, W + 1, part);
+  FS_LAUNCH_CHECK();
+  hipLaunchKernelGGL(k_colscan, col_grid, dim3(kThreads), 0, stream, counts, ld, G, W + 1, part,
+                     tot);
+  FS_LAUNCH_CHECK();
+  hipLaunchKernelGGL(k_splits, split_grid, dim3(kThreads), 0, stream, counts, ld, G, tile_pref,
+                     tot, W, splits, shard_offsets);
+  FS_LAUNCH_CHECK();
+  hipLaunchKernelGGL(k_scatter, dim3(G), dim3(kThreads), 0, stream, ikey, n_tok, tile_pref,
+                     tiles, tr, W, T, nbits, counts, ld, shard_offsets, shard_keys, shard_bm);
   FS_LAUNCH_CHECK();
   return FS_OK;
 }

@@ -34,6 +34,24 @@ __device__ __forceinline__ uint64_t match_bits(uint32_t v, int bits) {
   return m;
 }
 
+// Same as match_bits for any value below the table size, at a few LDS
+// operations instead of two VALU steps per bit: every active lane sets its
+// bit in tab[v] (a per-wave table of 64-bit lane masks, all zero on entry),
+// reads the entry back and the lowest peer clears it again. A wave's LDS
+// operations complete in issue order, so the read sees every peer's bit and
+// the clear follows every peer's read. Inactive lanes get 0.
+__device__ __forceinline__ uint64_t lds_peers(uint64_t* tab, uint32_t v, bool active) {
+  const uint64_t me = 1ull << lane();
+  uint64_t peers = 0;
+  if (active) {
+    __hip_atomic_fetch_or(&tab[v], me, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT);
+    peers = __hip_atomic_load(&tab[v], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT);
+  }
+  if (active && (peers & (me - 1)) == 0)
+    __hip_atomic_store(&tab[v], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT);
+  return peers;
+}
+
 template <typename T>
 __device__ __forceinline__ T wave_incl_scan(T v) {
   int l = lane();

@@ -44,9 +44,12 @@ def test_strerror_and_version(L):
 
 def test_workspace_queries_are_host_only_and_monotone(L):
     assert L.balance_workspace_size(4096, 512) >= 4096 * 16
+    # per-tile shard counts: grows with the batch, the tables and W
     a = L.bucketize_workspace_size(1 << 20, 4096, 1, 512)
-    b = L.bucketize_workspace_size(1 << 22, 4096, 1, 512)
-    assert 0 < a < b
+    assert 0 < a < L.bucketize_workspace_size(1 << 22, 4096, 1, 512)
+    assert a >= 4 * 513 * 512
+    assert a < L.bucketize_workspace_size(1 << 20, 4096, 2, 512) < \
+        L.bucketize_workspace_size(1 << 20, 4096, 2, 1024)
     assert L.unique_workspace_size(1 << 22, 1, 512) >= 16 * (1 << 22)
     assert L.unique_workspace_size(1 << 20, 1, 512, prev_cap=1 << 24) > \
         L.unique_workspace_size(1 << 20, 1, 512, prev_cap=1 << 20)

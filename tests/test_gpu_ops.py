@@ -377,3 +377,19 @@ def test_reduce_update_parity(case):
         assert np.array_equal(got, ref)
     if optim == "rw_adagrad":
         np.testing.assert_allclose(host(st.index_select(0, cu(rid))), stores[0].state, rtol=1e-6)
+
+
+def test_bucketize_repeated_sample_flags_shape():
+    # perm holds in-range entries but repeats the longest sample: the
+    # lengths under perm overrun n_tok, so the call must write no items
+    say("bucketize-perm-repeat")
+    b = _tiny_batch(3, 20, [100], 10)
+    so = b["sample_offsets"]
+    lens = np.diff(so)
+    perm_h = np.full(len(lens), int(np.argmax(lens)), np.int32)
+    ro_h = np.array([0, len(lens) // 2, len(lens)], np.int32)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    bk = lib.fs_bucketize_permute(cu(b["ids"]), cu(so), [100], cu(perm_h), cu(ro_h), 2, err=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) & lib.FS_EF_SHAPE
+    assert np.all(host(bk["shard_offsets"]) == 0) and np.all(host(bk["splits"]) == 0)
