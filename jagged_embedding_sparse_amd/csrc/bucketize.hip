@@ -26,6 +26,7 @@
 // round-robin), so the short runs that neighbouring tiles of one segment
 // write next to each other meet in one L2. No device-scope atomics.
 #include "common.hpp"
+#include "colscan.hpp"
 #include "divu32.hpp"
 
 namespace fs {
@@ -35,7 +36,6 @@ constexpr int kThreads = 256;  // 4 waves
 constexpr int kRounds = 16;    // items per lane
 constexpr int kWaveItems = kWave * kRounds;
 constexpr int kTile = kThreads * kRounds;  // 4096 tokens per tile
-constexpr int kXcd = 8;
 
 struct TableRows {
   int64_t rows[FS_MAX_TABLES];
@@ -53,11 +53,6 @@ struct TileDesc {
   int32_t q_lo, q_hi;  // rank r's balanced samples
   int32_t pad[2];
 };
-
-// Grid sizes are multiples of 8; XCD x runs the x-th eighth of the tiles.
-__device__ __forceinline__ int32_t xcd_tile(int32_t bid, int32_t G) {
-  return (bid % kXcd) * (G / kXcd) + bid / kXcd;
-}
 
 // ---------------------------------------------------------------- prep
 constexpr int kPrepThreads = 1024;
@@ -294,62 +289,6 @@ k_hist(const int64_t* __restrict__ ids, int64_t n_tok, const int64_t* __restrict
   for (int b = threadIdx.x; b <= W; b += kThreads) counts[(int64_t)tile * ld + b] = h[b];
 }
 
-// ---------------------------------------------------------------- column scans
-// Lanes are columns (64 per workgroup, coalesced row loads); each wave takes
-// 32 consecutive rows, a workgroup 128.
-constexpr int kColRows = 32;
-constexpr int kColBlockRows = kColRows * (kThreads / kWave);
-
-__global__ void __launch_bounds__(kThreads)
-k_colsum(const uint32_t* __restrict__ counts, int32_t ld, int32_t G, int32_t C,
-         uint32_t* __restrict__ part) {
-  __shared__ uint32_t wsum[kThreads / kWave][kWave];
-  const int w = threadIdx.x / kWave, l = lane();
-  const int32_t c = blockIdx.y * kWave + l;
-  const int32_t r0 = blockIdx.x * kColBlockRows + w * kColRows;
-  uint32_t s = 0;
-  if (c < C) {
-#pragma unroll
-    for (int i = 0; i < kColRows; ++i)
-      if (r0 + i < G) s += counts[(int64_t)(r0 + i) * ld + c];
-  }
-  wsum[w][l] = s;
-  __syncthreads();
-  if (w == 0 && c < C)
-    part[(int64_t)blockIdx.x * ld + c] = wsum[0][l] + wsum[1][l] + wsum[2][l] + wsum[3][l];
-}
-
-// counts[r][c] <- sum of counts[r'][c] over r' < r; tot[c] <- column total.
-__global__ void __launch_bounds__(kThreads)
-k_colscan(uint32_t* __restrict__ counts, int32_t ld, int32_t G, int32_t C,
-          const uint32_t* __restrict__ part, uint32_t* __restrict__ tot) {
-  __shared__ uint32_t wsum[kThreads / kWave][kWave];
-  const int w = threadIdx.x / kWave, l = lane();
-  const int32_t c = blockIdx.y * kWave + l;
-  const int32_t r0 = blockIdx.x * kColBlockRows + w * kColRows;
-  const bool on = c < C;
-  uint32_t base = 0;
-  if (on)
-    for (int32_t k = 0; k < (int32_t)blockIdx.x; ++k) base += part[(int64_t)k * ld + c];
-  uint32_t v[kColRows];
-  uint32_t s = 0;
-#pragma unroll
-  for (int i = 0; i < kColRows; ++i) {
-    v[i] = (on && r0 + i < G) ? counts[(int64_t)(r0 + i) * ld + c] : 0u;
-    s += v[i];
-  }
-  wsum[w][l] = s;
-  __syncthreads();
-  for (int x = 0; x < w; ++x) base += wsum[x][l];
-  if (!on) return;
-#pragma unroll
-  for (int i = 0; i < kColRows; ++i) {
-    if (r0 + i < G) counts[(int64_t)(r0 + i) * ld + c] = base;
-    base += v[i];
-  }
-  if (blockIdx.x == gridDim.x - 1 && w == kThreads / kWave - 1) tot[c] = base;
-}
-
 // ---------------------------------------------------------------- splits
 // Workgroup (x, y): ranks [64x, 64x + 64) x shards [64y, 64y + 64) of
 // splits[d][r] = (scanned count of shard d at rank r + 1's first tile) -
@@ -574,7 +513,6 @@ extern "C" int fs_bucketize_permute(const int64_t* ids, int64_t n_tok,
   uint32_t* ikey = c.take<uint32_t>((size_t)(T * (n_tok > 0 ? n_tok : 1)));
   int nbits = 1;
   while ((1 << nbits) - 1 <= W) ++nbits;  // sentinel (2^nbits - 1) > W
-  const dim3 col_grid((unsigned)cdiv(G, kColBlockRows), (unsigned)cdiv(W + 1, kWave));
   const dim3 split_grid((unsigned)cdiv(W, kWave), (unsigned)cdiv(W, kWave));
 
   hipLaunchKernelGGL(k_prep, dim3(1), dim3(kPrepThreads), 0, stream, sample_offsets, n, n_tok,
@@ -583,11 +521,8 @@ extern "C" int fs_bucketize_permute(const int64_t* ids, int64_t n_tok,
   hipLaunchKernelGGL(k_hist, dim3(G), dim3(kThreads), 0, stream, ids, n_tok, shift, bal_offsets,
                      tile_pref, tiles, tr, W, T, nbits, counts, ld, ikey, err);
   FS_LAUNCH_CHECK();
-  hipLaunchKernelGGL(k_colsum, col_grid, dim3(kThreads), 0, stream, counts, ld, G, W + 1, part);
-  FS_LAUNCH_CHECK();
-  hipLaunchKernelGGL(k_colscan, col_grid, dim3(kThreads), 0, stream, counts, ld, G, W + 1, part,
-                     tot);
-  FS_LAUNCH_CHECK();
+  int rc = launch_colscan(counts, ld, G, W + 1, part, tot, stream);
+  if (rc) return rc;
   hipLaunchKernelGGL(k_splits, split_grid, dim3(kThreads), 0, stream, counts, ld, G, tile_pref,
                      tot, W, splits, shard_offsets);
   FS_LAUNCH_CHECK();

@@ -1,0 +1,93 @@
+// Exclusive column scans of a row-major matrix of 32-bit counts (rows =
+// tiles in output order, columns = bins), in place. Lanes are columns, so
+// every row load is coalesced; each wave takes 32 consecutive rows, each
+// workgroup 128. Two launches over (row blocks) x (column groups of 64):
+// k_colsum stores each row block's column sums, k_colscan adds the sums of
+// the row blocks before its own and rewrites the rows as exclusive prefixes.
+#pragma once
+
+#include "common.hpp"
+
+namespace fs {
+namespace {
+
+constexpr int kColThreads = 256;
+constexpr int kColRows = 32;
+constexpr int kColBlockRows = kColRows * (kColThreads / kWave);
+
+__global__ void __launch_bounds__(kColThreads)
+k_colsum(const uint32_t* __restrict__ counts, int32_t ld, int32_t G, int32_t C,
+         uint32_t* __restrict__ part) {
+  __shared__ uint32_t wsum[kColThreads / kWave][kWave];
+  const int w = threadIdx.x / kWave, l = lane();
+  const int32_t c = blockIdx.y * kWave + l;
+  const int32_t r0 = blockIdx.x * kColBlockRows + w * kColRows;
+  // rows past G read row G - 1 and count zero: the loads stay unconditional,
+  // so all 32 are in flight at once
+  const int32_t cc = c < C ? c : C - 1;
+  uint32_t s = 0;
+#pragma unroll
+  for (int i = 0; i < kColRows; ++i) {
+    const uint32_t x = counts[(int64_t)min(r0 + i, G - 1) * ld + cc];
+    s += (c < C && r0 + i < G) ? x : 0u;
+  }
+  wsum[w][l] = s;
+  __syncthreads();
+  if (w == 0 && c < C)
+    part[(int64_t)blockIdx.x * ld + c] = wsum[0][l] + wsum[1][l] + wsum[2][l] + wsum[3][l];
+}
+
+// counts[r][c] <- sum of counts[r'][c] over r' < r; tot[c] <- column total.
+__global__ void __launch_bounds__(kColThreads)
+k_colscan(uint32_t* __restrict__ counts, int32_t ld, int32_t G, int32_t C,
+          const uint32_t* __restrict__ part, uint32_t* __restrict__ tot) {
+  __shared__ uint32_t wsum[kColThreads / kWave][kWave];
+  const int w = threadIdx.x / kWave, l = lane();
+  const int32_t c = blockIdx.y * kWave + l;
+  const int32_t r0 = blockIdx.x * kColBlockRows + w * kColRows;
+  const bool on = c < C;
+  const int32_t cc = on ? c : C - 1;
+  uint32_t v[kColRows];
+  uint32_t s = 0;
+#pragma unroll
+  for (int i = 0; i < kColRows; ++i) {
+    const uint32_t x = counts[(int64_t)min(r0 + i, G - 1) * ld + cc];
+    v[i] = (on && r0 + i < G) ? x : 0u;
+    s += v[i];
+  }
+  // sums of the earlier row blocks, 8 independent loads at a time
+  uint32_t base = 0;
+  for (int32_t k0 = 0; k0 < (int32_t)blockIdx.x; k0 += 8) {
+    uint32_t b8[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      b8[j] = part[(int64_t)min(k0 + j, (int32_t)blockIdx.x - 1) * ld + cc];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) base += (k0 + j < (int32_t)blockIdx.x) ? b8[j] : 0u;
+  }
+  wsum[w][l] = s;
+  __syncthreads();
+  for (int x = 0; x < w; ++x) base += wsum[x][l];
+  if (!on) return;
+#pragma unroll
+  for (int i = 0; i < kColRows; ++i) {
+    if (r0 + i < G) counts[(int64_t)(r0 + i) * ld + c] = base;
+    base += v[i];
+  }
+  if (blockIdx.x == gridDim.x - 1 && w == kColThreads / kWave - 1) tot[c] = base;
+}
+
+// Both launches for a G x C matrix with leading dimension ld; part holds
+// cdiv(G, 128) * ld entries, tot C.
+inline int launch_colscan(uint32_t* counts, int32_t ld, int32_t G, int32_t C, uint32_t* part,
+                          uint32_t* tot, hipStream_t stream) {
+  const dim3 grid((unsigned)cdiv(G, kColBlockRows), (unsigned)cdiv(C, kWave));
+  hipLaunchKernelGGL(k_colsum, grid, dim3(kColThreads), 0, stream, counts, ld, G, C, part);
+  FS_LAUNCH_CHECK();
+  hipLaunchKernelGGL(k_colscan, grid, dim3(kColThreads), 0, stream, counts, ld, G, C, part, tot);
+  FS_LAUNCH_CHECK();
+  return FS_OK;
+}
+
+}  // namespace
+}  // namespace fs

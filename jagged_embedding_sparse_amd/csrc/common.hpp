@@ -113,6 +113,16 @@ __device__ __forceinline__ int64_t wave_partition_point(int64_t lo, int64_t hi, 
   return lo + popc(__ballot(t));
 }
 
+// ---------------------------------------------------------------- XCDs
+// Workgroups are dealt to the 8 XCDs round-robin. With a grid that is a
+// multiple of 8, XCD x runs the x-th eighth of the tiles, so neighbouring
+// tiles (whose outputs often share cache lines) meet in one L2.
+constexpr int kXcd = 8;
+
+__device__ __forceinline__ int32_t xcd_tile(int32_t bid, int32_t G) {
+  return (bid % kXcd) * (G / kXcd) + bid / kXcd;
+}
+
 // ---------------------------------------------------------------- errors
 __device__ __forceinline__ void flag_err(int32_t* err, bool bad, int bit) {
   if (__ballot(bad) && err != nullptr) {

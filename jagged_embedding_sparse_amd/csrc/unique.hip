@@ -4,17 +4,19 @@
 // section 3.2 and Algorithm 2: the collision and exclusive index sets of
 // iterations i and i+1 are computed on the shard-major (post-AllToAll) IDs.
 //
-//  1. LSD radix sort of (key, bm) over the shard-major items, 8-bit digits,
-//     only as many passes as the key space needs. Every pass is a stable
-//     counting sort (per-tile histograms, per-digit column scans, per-tile
-//     ranked scatter), so equal keys keep their shard-major order, which for
-//     one key is ascending bm: the CSR's occurrence order falls out.
+//  1. LSD radix sort of (key, bm) over the shard-major items with digits of
+//     up to 10 bits, as few passes as the key space needs (28-bit keys: 3).
+//     Every pass is a stable counting sort (per-tile digit histograms as rows
+//     of a tiles x digits matrix, coalesced column scans, per-tile ranked
+//     scatter), so equal keys keep their shard-major order, which for one
+//     key is ascending bm: the CSR's occurrence order falls out.
 //  2. Head flags (key differs from its left neighbour), one scan over tiles,
 //     compaction: unique keys, CSR segment starts, occurrence -> unique index,
 //     and the (table, shard) group offsets, written where the group changes.
 //  3. Set intersection of the new and previous unique lists by merge path:
 //     one search per 2048-element tile of the merged order, then exact
 //     membership tests inside LDS.
+#include "colscan.hpp"
 #include "common.hpp"
 
 namespace fs {
@@ -24,9 +26,8 @@ constexpr int kThreads = 256;
 constexpr int kRounds = 16;
 constexpr int kWaveItems = kWave * kRounds;
 constexpr int kTile = kThreads * kRounds;  // 4096
-constexpr int kRadixBits = 8;
-constexpr int kRadix = 1 << kRadixBits;
-constexpr int kMaxPasses = 4;  // keys < 2^32
+constexpr int kMaxDigitBits = 10;
+constexpr int kMaxBins = 1 << kMaxDigitBits;  // also the count matrix's row length
 
 struct Groups {
   int64_t row_base[FS_MAX_TABLES + 1];
@@ -58,125 +59,150 @@ __global__ void k_init(const int64_t* __restrict__ shard_offsets, int32_t W, int
 }
 
 // ---------------------------------------------------------------- radix pass
-// Per pass: k_rs_hist writes each tile's digit histogram (LDS atomics only);
-// k_rs_scan turns each digit's column of tile counts into exclusive offsets
-// and the digit's total; k_rs_scatter derives the digit bases from the
-// totals, ranks its tile stably, sorts it by digit in LDS and writes every
-// digit's run contiguously. No device-scope atomics anywhere.
+// Per pass: k_rs_hist writes each tile's digit histogram as one row of the
+// count matrix (LDS atomics; zeros past the valid items); the column scans
+// turn every digit's column into exclusive offsets and the digit's total;
+// k_rs_scatter adds the digit bases, ranks its tile stably, sorts it by digit
+// in LDS and writes every digit's run contiguously. Tiles follow the XCD
+// order. No device-scope atomics anywhere.
 template <typename KIn>
 __global__ void __launch_bounds__(kThreads)
 k_rs_hist(const KIn* __restrict__ keys, const int64_t* __restrict__ nvp, int32_t W, int shift,
-          uint32_t mask, int64_t tiles_cap, uint32_t* __restrict__ hist) {
-  __shared__ uint32_t h[kRadix];
+          uint32_t mask, uint32_t* __restrict__ hist) {
+  __shared__ uint32_t h[kMaxBins];
   const int64_t n = n_valid_of(nvp, W);
-  const int64_t t0 = (int64_t)blockIdx.x * kTile;
-  if (t0 >= n) return;
-  h[threadIdx.x] = 0;  // kThreads == kRadix
+  const int32_t tile = xcd_tile(blockIdx.x, gridDim.x);
+  const int64_t t0 = (int64_t)tile * kTile;
+  const int nb = (int)mask + 1;
+  for (int b = threadIdx.x; b < nb; b += kThreads) h[b] = 0;
   __syncthreads();
-  // one LDS add per distinct digit of each wave round: hot keys (many equal
-  // digits) would otherwise serialise on one counter
-  const uint32_t none = mask + 1;
-  int nbits = 0;
-  while ((1u << nbits) <= mask) ++nbits;
-  const uint64_t lt = lanemask_lt();
-#pragma unroll 4
-  for (int i = 0; i < kRounds; ++i) {
-    const int64_t x = t0 + i * kThreads + threadIdx.x;
-    const uint32_t d = x < n ? (((uint32_t)keys[x] >> shift) & mask) : none;
-    const uint64_t peers = match_bits(d, nbits + 1);
-    if (d != none && (peers & lt) == 0) atomicAdd(&h[d], (uint32_t)popc(peers));
+  if (t0 < n) {
+    // all 16 loads in flight (past n: the last item, not counted)
+    uint32_t d[kRounds];
+#pragma unroll
+    for (int i = 0; i < kRounds; ++i) {
+      const int64_t x = t0 + i * kThreads + threadIdx.x;
+      d[i] = ((uint32_t)keys[x < n ? x : n - 1] >> shift) & mask;
+    }
+#pragma unroll
+    for (int i = 0; i < kRounds; ++i)
+      if (t0 + i * kThreads + threadIdx.x < n) atomicAdd(&h[d[i]], 1u);
   }
   __syncthreads();
-  hist[(int64_t)threadIdx.x * tiles_cap + blockIdx.x] = h[threadIdx.x];
+  for (int b = threadIdx.x; b < nb; b += kThreads) hist[(int64_t)tile * kMaxBins + b] = h[b];
 }
 
-__global__ void __launch_bounds__(kThreads)
-k_rs_scan(const int64_t* __restrict__ nvp, int32_t W, int64_t tiles_cap,
-          uint32_t* __restrict__ hist, uint32_t* __restrict__ tot) {
-  __shared__ int64_t tmp[17];
-  const int32_t b = blockIdx.x;
-  const int64_t n_tiles = cdiv(n_valid_of(nvp, W), kTile);
-  uint32_t* col = hist + (int64_t)b * tiles_cap;
-  int64_t carry = 0;
-  for (int64_t c0 = 0; c0 < n_tiles; c0 += kThreads) {
-    const int64_t c = c0 + threadIdx.x;
-    const int64_t v = c < n_tiles ? col[c] : 0;
-    int64_t sum;
-    const int64_t ex = block_excl_scan<int64_t>(v, tmp, &sum);
-    if (c < n_tiles) col[c] = (uint32_t)(carry + ex);
-    carry += sum;
-  }
-  if (threadIdx.x == 0) tot[b] = (uint32_t)carry;
-}
+// Staging area of one tile: first the per-wave lane-mask tables of the
+// ranking, then the tile's items sorted by digit.
+union RadixStage {
+  uint64_t peers[kThreads / kWave][kMaxBins];
+  struct {
+    uint32_t key[kTile];
+    int32_t val[kTile];
+  } s;
+};
 
 template <typename KIn>
 __global__ void __launch_bounds__(kThreads)
 k_rs_scatter(const KIn* __restrict__ keys_in, const int32_t* __restrict__ vals_in,
-             const int64_t* __restrict__ nvp, int32_t W, int shift, uint32_t mask, int nbits,
-             int64_t tiles_cap, const uint32_t* __restrict__ hist,
-             const uint32_t* __restrict__ tot, uint32_t* __restrict__ keys_out,
-             int32_t* __restrict__ vals_out) {
-  __shared__ uint32_t cnt[kThreads / kWave][kRadix];
-  __shared__ uint32_t dig_base[kRadix];  // global start of each digit's run of this tile
-  __shared__ uint32_t dig_tile[kRadix];  // start of each digit inside the LDS-sorted tile
-  __shared__ uint32_t skey[kTile];
-  __shared__ int32_t sval[kTile];
+             const int64_t* __restrict__ nvp, int32_t W, int shift, uint32_t mask,
+             const uint32_t* __restrict__ offs, const uint32_t* __restrict__ tot,
+             uint32_t* __restrict__ keys_out, int32_t* __restrict__ vals_out) {
+  __shared__ uint16_t cnt[kThreads / kWave][kMaxBins];
+  __shared__ uint32_t dig_base[kMaxBins];  // global start of each digit's run of this tile
+  __shared__ uint32_t dig_tile[kMaxBins];  // start of each digit inside the LDS-sorted tile
+  __shared__ RadixStage st;
   __shared__ int64_t tmp[17];
+  constexpr int kPer = kMaxBins / kThreads;
   const int64_t n = n_valid_of(nvp, W);
-  const int64_t t0 = (int64_t)blockIdx.x * kTile;
-  if (t0 >= n) return;
+  const int32_t tile = xcd_tile(blockIdx.x, gridDim.x);
+  const int64_t t0 = (int64_t)tile * kTile;
+  if (t0 >= n) return;  // uniform per workgroup
+  const int nb = (int)mask + 1;
   const int w = threadIdx.x / kWave;
-  for (int b = lane(); b < kRadix; b += kWave) cnt[w][b] = 0;
-  const uint64_t lt = lanemask_lt();
+  for (int b = lane(); b < nb; b += kWave) {
+    cnt[w][b] = 0;
+    st.peers[w][b] = 0;
+  }
   uint32_t key[kRounds], dig[kRounds], rk[kRounds];
   int32_t val[kRounds];
-  const uint32_t none = mask + 1;  // lanes without an item (fits nbits + 1 bits)
+  const uint32_t none = mask + 1;  // lanes without an item
 #pragma unroll
   for (int i = 0; i < kRounds; ++i) {
     const int64_t x = t0 + (int64_t)w * kWaveItems + i * kWave + lane();
     const bool valid = x < n;
-    key[i] = valid ? (uint32_t)keys_in[x] : 0u;
-    val[i] = valid ? vals_in[x] : 0;
-    const uint32_t d = valid ? ((key[i] >> shift) & mask) : none;
-    dig[i] = d;
-    const uint64_t peers = match_bits(d, nbits + 1);
-    const uint32_t before = cnt[w][valid ? d : 0];
+    const int64_t xc = valid ? x : n - 1;  // unconditional loads, all in flight
+    key[i] = (uint32_t)keys_in[xc];
+    val[i] = vals_in[xc];
+    dig[i] = valid ? ((key[i] >> shift) & mask) : none;
+  }
+  // stable rank of each item among the wave's items of its digit
+  const uint64_t lt = lanemask_lt();
+#pragma unroll
+  for (int i = 0; i < kRounds; ++i) {
+    const bool on = dig[i] != none;
+    const uint32_t d = on ? dig[i] : 0u;
+    const uint64_t peers = lds_peers(st.peers[w], d, on);
+    const uint32_t before = cnt[w][d];
     rk[i] = before + (uint32_t)popc(peers & lt);
-    if (valid && (peers & lt) == 0) cnt[w][d] = before + (uint32_t)popc(peers);
+    if (on && (peers & lt) == 0) cnt[w][d] = (uint16_t)(before + (uint32_t)popc(peers));
   }
   __syncthreads();
   {
-    const int b = threadIdx.x;  // kThreads == kRadix
-    uint32_t run = 0;
+    // per digit: exclusive prefix over the waves, the digits' starts in the
+    // tile, and the global bases (exclusive scan of the totals + this
+    // tile's column offsets)
+    uint32_t tb[kPer], tt[kPer];
+    int64_t local = 0, tlocal = 0;
 #pragma unroll
-    for (int x = 0; x < kThreads / kWave; ++x) {
-      const uint32_t c = cnt[x][b];
-      cnt[x][b] = run;
-      run += c;
+    for (int k = 0; k < kPer; ++k) {
+      const int b = threadIdx.x * kPer + k;
+      uint32_t run = 0;
+      tt[k] = 0;
+      if (b < nb) {
+#pragma unroll
+        for (int x = 0; x < kThreads / kWave; ++x) {
+          const uint32_t c = cnt[x][b];
+          cnt[x][b] = (uint16_t)run;
+          run += c;
+        }
+        tt[k] = tot[b];
+      }
+      tb[k] = run;
+      local += run;
+      tlocal += tt[k];
     }
     int64_t all;
-    const int64_t in_tile = block_excl_scan<int64_t>(run, tmp, &all);
-    dig_tile[b] = (uint32_t)in_tile;
+    int64_t r0 = block_excl_scan<int64_t>(local, tmp, &all);
     int64_t gsum;
-    const int64_t gbase = block_excl_scan<int64_t>((int64_t)tot[b], tmp, &gsum);
-    dig_base[b] = (uint32_t)(gbase + hist[(int64_t)b * tiles_cap + blockIdx.x]);
+    int64_t g0 = block_excl_scan<int64_t>(tlocal, tmp, &gsum);
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int b = threadIdx.x * kPer + k;
+      if (b < nb) {
+        dig_tile[b] = (uint32_t)r0;
+        dig_base[b] = (uint32_t)(g0 + offs[(int64_t)tile * kMaxBins + b]);
+      }
+      r0 += tb[k];
+      g0 += tt[k];
+    }
   }
-  __syncthreads();
+  __syncthreads();  // also ends every wave's use of the mask tables
 #pragma unroll
   for (int i = 0; i < kRounds; ++i) {
     if (dig[i] == none) continue;
     const uint32_t p = dig_tile[dig[i]] + cnt[w][dig[i]] + rk[i];
-    skey[p] = key[i];
-    sval[p] = val[i];
+    st.s.key[p] = key[i];
+    st.s.val[p] = val[i];
   }
   __syncthreads();
   const int m = (int)min((int64_t)kTile, n - t0);
   for (int p = threadIdx.x; p < m; p += kThreads) {
-    const uint32_t k = skey[p];
+    const uint32_t k = st.s.key[p];
     const uint32_t d = (k >> shift) & mask;
     const uint32_t pos = dig_base[d] + (uint32_t)p - dig_tile[d];
     keys_out[pos] = k;
-    vals_out[pos] = sval[p];
+    vals_out[pos] = st.s.val[p];
   }
 }
 
@@ -417,13 +443,15 @@ extern "C" size_t fs_unique_workspace_size(int64_t n_cap, int64_t prev_cap, int3
   (void)W;
   const int64_t cap = n_cap > 0 ? n_cap : 1;
   const int64_t tiles = cdiv(cap, kTile);
+  const int64_t G = (int64_t)align_up((size_t)tiles, kXcd);
   Carve c(nullptr);
   c.take<uint32_t>((size_t)cap);                // keys A
   c.take<uint32_t>((size_t)cap);                // keys B
   c.take<int32_t>((size_t)cap);                 // vals A
   c.take<int32_t>((size_t)cap);                 // vals B
-  c.take<uint32_t>((size_t)kRadix * tiles);     // histograms
-  c.take<uint32_t>((size_t)kRadix * kMaxPasses);  // digit totals
+  c.take<uint32_t>((size_t)(G * kMaxBins));     // tiles x digits counts, then offsets
+  c.take<uint32_t>((size_t)(cdiv(G, kColBlockRows) * kMaxBins));  // column partials
+  c.take<uint32_t>((size_t)kMaxBins);           // digit totals
   c.take<uint32_t>((size_t)tiles);              // heads per tile
   c.take<int64_t>(1);                           // valid item count
   c.take<uint32_t>((size_t)cdiv(cap + (prev_cap > 0 ? prev_cap : 0), kMergeTile) + 1);
@@ -470,47 +498,50 @@ extern "C" int fs_unique_collision_split(const int64_t* shard_keys, const int32_
   uint32_t* kb = c.take<uint32_t>((size_t)cap);
   int32_t* va = c.take<int32_t>((size_t)cap);
   int32_t* vb = c.take<int32_t>((size_t)cap);
-  uint32_t* hist = c.take<uint32_t>((size_t)kRadix * tiles);
-  uint32_t* tot = c.take<uint32_t>((size_t)kRadix * kMaxPasses);  // digit totals per pass
+  const int64_t G = (int64_t)align_up((size_t)tiles, kXcd);
+  uint32_t* hist = c.take<uint32_t>((size_t)(G * kMaxBins));
+  uint32_t* part = c.take<uint32_t>((size_t)(cdiv(G, kColBlockRows) * kMaxBins));
+  uint32_t* tot = c.take<uint32_t>((size_t)kMaxBins);
   uint32_t* tile_heads = c.take<uint32_t>((size_t)tiles);
   int64_t* n_valid = c.take<int64_t>(1);
   const int64_t merge_blocks = cdiv(cap + prev_cap, kMergeTile);
   uint32_t* block_hits = c.take<uint32_t>((size_t)merge_blocks);
 
   const int kbits = key_bits(base);
-  const int passes = (kbits + kRadixBits - 1) / kRadixBits;
+  const int passes = (kbits + kMaxDigitBits - 1) / kMaxDigitBits;
   hipLaunchKernelGGL(k_init, dim3(1), dim3(64), 0, stream, shard_offsets, W, n_cap, n_valid);
   FS_LAUNCH_CHECK();
   uint32_t* kbuf[2] = {ka, kb};
   int32_t* vbuf[2] = {va, vb};
   const unsigned grid = (unsigned)tiles;
+  const unsigned rgrid = (unsigned)G;
+  int shift = 0;
   for (int p = 0; p < passes; ++p) {
-    const int shift = p * kRadixBits;
-    const int bits = (kbits - shift) < kRadixBits ? (kbits - shift) : kRadixBits;
+    // digits as even as the passes allow: 28 bits -> 10, 9, 9
+    const int bits = (kbits - shift + (passes - p) - 1) / (passes - p);
     const uint32_t mask = (1u << bits) - 1u;
-    uint32_t* tp = tot + kRadix * p;
     uint32_t* kout = kbuf[p & 1];
     int32_t* vout = (p == passes - 1) ? occ_bm : vbuf[p & 1];
     if (p == 0) {
-      hipLaunchKernelGGL(k_rs_hist<int64_t>, dim3(grid), dim3(kThreads), 0, stream, shard_keys,
-                         n_valid, W, shift, mask, tiles, hist);
+      hipLaunchKernelGGL(k_rs_hist<int64_t>, dim3(rgrid), dim3(kThreads), 0, stream, shard_keys,
+                         n_valid, W, shift, mask, hist);
     } else {
-      hipLaunchKernelGGL(k_rs_hist<uint32_t>, dim3(grid), dim3(kThreads), 0, stream,
-                         kbuf[(p - 1) & 1], n_valid, W, shift, mask, tiles, hist);
+      hipLaunchKernelGGL(k_rs_hist<uint32_t>, dim3(rgrid), dim3(kThreads), 0, stream,
+                         kbuf[(p - 1) & 1], n_valid, W, shift, mask, hist);
     }
     FS_LAUNCH_CHECK();
-    hipLaunchKernelGGL(k_rs_scan, dim3(kRadix), dim3(kThreads), 0, stream, n_valid, W,
-                       tiles, hist, tp);
-    FS_LAUNCH_CHECK();
+    int rc = launch_colscan(hist, kMaxBins, (int32_t)G, (int32_t)mask + 1, part, tot, stream);
+    if (rc) return rc;
     if (p == 0) {
-      hipLaunchKernelGGL(k_rs_scatter<int64_t>, dim3(grid), dim3(kThreads), 0, stream, shard_keys,
-                         shard_bm, n_valid, W, shift, mask, bits, tiles, hist, tp, kout, vout);
+      hipLaunchKernelGGL(k_rs_scatter<int64_t>, dim3(rgrid), dim3(kThreads), 0, stream,
+                         shard_keys, shard_bm, n_valid, W, shift, mask, hist, tot, kout, vout);
     } else {
-      hipLaunchKernelGGL(k_rs_scatter<uint32_t>, dim3(grid), dim3(kThreads), 0, stream,
-                         kbuf[(p - 1) & 1], vbuf[(p - 1) & 1], n_valid, W, shift, mask,
-                         bits, tiles, hist, tp, kout, vout);
+      hipLaunchKernelGGL(k_rs_scatter<uint32_t>, dim3(rgrid), dim3(kThreads), 0, stream,
+                         kbuf[(p - 1) & 1], vbuf[(p - 1) & 1], n_valid, W, shift, mask, hist,
+                         tot, kout, vout);
     }
     FS_LAUNCH_CHECK();
+    shift += bits;
   }
   const uint32_t* sk = kbuf[(passes - 1) & 1];
   hipLaunchKernelGGL(k_heads, dim3(grid), dim3(kThreads), 0, stream, sk, n_valid, W,
