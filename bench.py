@@ -109,10 +109,11 @@ def main():
     step = SparseStep(w, weights, states, cap)
     n_tok = [b["n_tok"] for b in host_batches]
     step.prologue(dev_batches[0])
+    run_step = step.step_sync if args.sync else step.step
     k = 0
     for _ in range(args.warmup):
         k += 1
-        step.step(dev_batches[k % NB], [g[:n_tok[(k - 1) % NB]] for g in grads_dev])
+        run_step(dev_batches[k % NB], [g[:n_tok[(k - 1) % NB]] for g in grads_dev])
     step.join()
     torch.cuda.synchronize()
 
@@ -125,7 +126,6 @@ def main():
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     ev0.record(step.sA)
-    run_step = step.step_sync if args.sync else step.step
     for _ in range(args.steps):
         p = k % NB
         k += 1
@@ -150,7 +150,7 @@ def main():
         p = k % NB
         k += 1
         prev = step.cur
-        nxt = step.step(dev_batches[k % NB], [g[:n_tok[p]] for g in grads_dev])
+        nxt = run_step(dev_batches[k % NB], [g[:n_tok[p]] for g in grads_dev])
         step.join()
         torch.cuda.synchronize()
         T, W = len(w.tables), w.world

@@ -10,14 +10,18 @@
 // Sort: the batch is small (n <= 16384) and every key (length, index) is
 // distinct, so the sorted position of sample s is the number of keys below
 // its own. One lane per sample counts over a slice of the batch, a workgroup
-// sums the 16 slices: O(n^2 / 64) wave instructions spread over n/64
+// sums the 4 slices: O(n^2 / 64) wave instructions spread over n/64
 // workgroups, no passes, no atomics, stable by construction.
 #include "common.hpp"
 
 namespace fs {
 namespace {
 
-constexpr int kRankThreads = 1024;  // 16 waves, one comparand slice each
+// 4 waves, one comparand slice each. Workgroups of the index path stay at 256
+// threads: a larger one needs that many free wave slots on one CU at once,
+// which it does not get while bandwidth-bound kernels of another stream keep
+// refilling every slot they free.
+constexpr int kRankThreads = 256;
 
 __device__ __forceinline__ uint32_t clamp_len(int32_t L) {
   return (uint32_t)(L < 0 ? 0 : (L > FS_MAX_UIH ? FS_MAX_UIH : L));
@@ -108,7 +112,7 @@ k_sort_place(const int32_t* __restrict__ len, int32_t n, int32_t W, int32_t* __r
 
 // VBS cuts: prefix sums S of the sorted weights, then for each rank r the
 // first k with W*S_k >= r*T (binary search; S is non-decreasing).
-constexpr int kCutThreads = 1024;
+constexpr int kCutThreads = 256;
 
 __global__ void __launch_bounds__(kCutThreads)
 k_vbs_cut(const int64_t* __restrict__ wsorted, int32_t n, int32_t W, int64_t* __restrict__ S,

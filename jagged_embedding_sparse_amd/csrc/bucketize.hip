@@ -13,7 +13,7 @@
 // item's output position is its shard's base, plus the shard's count in all
 // earlier tiles, plus its stable rank inside its tile:
 //   k_prep     balanced offsets, per-sample shifts, tile descriptors (one
-//              workgroup; every load chain is two deep)
+//              workgroup of 256 threads)
 //   k_hist     per-tile shard histograms -> rows of a tiles x shards matrix;
 //              each item's 32-bit key, batch-major
 //   k_colsum, k_colscan   exclusive column scans of that matrix in place,
@@ -55,15 +55,20 @@ struct TileDesc {
 };
 
 // ---------------------------------------------------------------- prep
-constexpr int kPrepThreads = 1024;
-constexpr int kPrepPer = FS_MAX_SAMPLES / kPrepThreads;  // samples per thread
+// One workgroup of 256 threads (larger ones wait for free slots while another
+// stream's kernels hold the CUs). Thread i owns balanced samples
+// [64 i, 64 i + 64) and ranks 4 i .. 4 i + 3.
+constexpr int kPrepThreads = 256;
+constexpr int kPrepPer = FS_MAX_SAMPLES / kPrepThreads;       // samples per thread
+constexpr int kPrepRanks = (FS_MAX_RANKS + 1) / kPrepThreads;  // ranks per thread (+ W)
+constexpr int kPrepUnroll = 8;  // offset validation: loads in flight per thread
+constexpr int kPrepBatch = 16;  // samples whose loads are in flight together
 
 // Validation, bal_offsets, shift[q] = so[perm[q]] - bal[q], the tile table.
-// Thread i owns balanced samples [16 i, 16 i + 16) and rank i. Invalid input
-// (offsets not rising from 0 to n_tok, a perm entry out of range, rank
-// offsets not rising from 0 to n, or lengths under perm not summing to
-// n_tok) flags FS_EF_SHAPE and leaves zero tiles, so nothing is written
-// past the outputs.
+// Invalid input (offsets not rising from 0 to n_tok, a perm entry out of
+// range, rank offsets not rising from 0 to n, or lengths under perm not
+// summing to n_tok) flags FS_EF_SHAPE and leaves zero tiles, so nothing is
+// written past the outputs.
 __global__ void __launch_bounds__(kPrepThreads)
 k_prep(const int64_t* __restrict__ so, int32_t n, int64_t n_tok, const int32_t* __restrict__ perm,
        const int32_t* __restrict__ ro, int32_t W, int32_t T, int64_t* __restrict__ bal,
@@ -74,73 +79,110 @@ k_prep(const int64_t* __restrict__ so, int32_t n, int64_t n_tok, const int32_t* 
   __shared__ int bad_s;
   if (threadIdx.x == 0) bad_s = 0;
   bool bad = false;
-  for (int32_t s = threadIdx.x; s <= n; s += kPrepThreads) {
-    const int64_t v = so[s];
-    if ((s == 0 && v != 0) || (s == n && v != n_tok) || (s < n && so[s + 1] < v)) bad = true;
-  }
-  const int32_t q0 = threadIdx.x * kPrepPer;
-  int64_t beg[kPrepPer];
-  int32_t len[kPrepPer];
+  for (int32_t s0 = threadIdx.x; s0 <= n; s0 += kPrepThreads * kPrepUnroll) {
 #pragma unroll
-  for (int k = 0; k < kPrepPer; ++k) {
-    const int32_t q = q0 + k;
-    const int32_t p = q < n ? perm[q] : 0;
-    const bool pin = p >= 0 && p < n;
-    if (q < n && !pin) bad = true;
-    beg[k] = (q < n && pin) ? so[p] : 0;
-    len[k] = (q < n && pin) ? (int32_t)(so[p + 1] - beg[k]) : 0;
+    for (int k = 0; k < kPrepUnroll; ++k) {
+      const int32_t s = s0 + k * kPrepThreads;
+      if (s <= n) {
+        const int64_t v = so[s];
+        if ((s == 0 && v != 0) || (s == n && v != n_tok) || (s < n && so[s + 1] < v)) bad = true;
+      }
+    }
   }
-  const int32_t r = threadIdx.x;  // W <= 1024 = blockDim.x
-  const int32_t ro_r = r <= W ? ro[r] : 0;
-  const int32_t ro_n = r < W ? ro[r + 1] : n;
-  if (r <= W && ((r == 0 && ro_r != 0) || (r == W && ro_r != n) || ro_n < ro_r)) bad = true;
+  // lengths of the thread's balanced samples, 16 at a time (perm loads, then
+  // offset loads, each batch in flight together; few registers, so that the
+  // workgroup fits beside another stream's kernels)
+  const int32_t q0 = threadIdx.x * kPrepPer;
+  int64_t local = 0;
+  for (int k0 = 0; k0 < kPrepPer; k0 += kPrepBatch) {
+    int32_t pp[kPrepBatch];
+#pragma unroll
+    for (int k = 0; k < kPrepBatch; ++k) pp[k] = q0 + k0 + k < n ? perm[q0 + k0 + k] : -1;
+#pragma unroll
+    for (int k = 0; k < kPrepBatch; ++k) {
+      const bool pin = pp[k] >= 0 && pp[k] < n;
+      if (q0 + k0 + k < n && !pin) bad = true;
+      if (pin) local += so[pp[k] + 1] - so[pp[k]];
+    }
+  }
+  int32_t ro_v[kPrepRanks + 1];
+#pragma unroll
+  for (int k = 0; k <= kPrepRanks; ++k) {
+    const int32_t r = threadIdx.x * kPrepRanks + k;
+    ro_v[k] = r <= W ? ro[r] : n;
+    if (r <= W && ((r == 0 && ro_v[k] != 0) || (r == W && ro_v[k] != n))) bad = true;
+    if (k > 0 && r <= W && ro_v[k] < ro_v[k - 1]) bad = true;
+  }
   __syncthreads();
   if (bad) atomicOr(&bad_s, 1);
   __syncthreads();
   bool ok = bad_s == 0;
-
-  int64_t local = 0;
-#pragma unroll
-  for (int k = 0; k < kPrepPer; ++k) local += ok ? len[k] : 0;
   int64_t total;
-  int64_t run = block_excl_scan<int64_t>(local, tmp64, &total);
+  int64_t run = block_excl_scan<int64_t>(ok ? local : 0, tmp64, &total);
   ok = ok && total == n_tok;  // perm repeats a sample: refuse before any tile exists
   if (!ok && threadIdx.x == 0 && err) atomicOr(err, FS_EF_SHAPE);
+  if (ok) {
+    for (int k0 = 0; k0 < kPrepPer && q0 + k0 < n; k0 += kPrepBatch) {
+      int32_t pp[kPrepBatch];
+      int64_t b0[kPrepBatch], b1[kPrepBatch];
 #pragma unroll
-  for (int k = 0; k < kPrepPer; ++k) {
-    const int32_t q = q0 + k;
-    if (q < n) {
-      bal[q] = run;
-      shift[q] = beg[k] - run;
+      for (int k = 0; k < kPrepBatch; ++k) pp[k] = q0 + k0 + k < n ? perm[q0 + k0 + k] : 0;
+#pragma unroll
+      for (int k = 0; k < kPrepBatch; ++k) {
+        b0[k] = so[pp[k]];
+        b1[k] = so[pp[k] + 1];
+      }
+#pragma unroll
+      for (int k = 0; k < kPrepBatch; ++k) {
+        const int32_t q = q0 + k0 + k;
+        if (q < n) {
+          bal[q] = run;
+          shift[q] = b0[k] - run;
+          run += b1[k] - b0[k];
+        }
+      }
     }
-    run += len[k];
   }
-  if (threadIdx.x == 0) bal[n] = total;
+  if (threadIdx.x == 0) bal[n] = ok ? total : 0;
   __syncthreads();  // bal visible to the workgroup
 
   // rank r owns T * ceil(m_r / kTile) tiles, t-major
-  int64_t A = 0, m = 0;
-  int32_t c = 0;
-  if (ok && r < W) {
-    A = bal[ro_r];
-    m = bal[ro_n] - A;
-    c = (int32_t)cdiv(m, kTile);
+  int64_t A[kPrepRanks], m[kPrepRanks];
+  int32_t c[kPrepRanks];
+  int32_t mine = 0;
+#pragma unroll
+  for (int k = 0; k < kPrepRanks; ++k) {
+    const int32_t r = threadIdx.x * kPrepRanks + k;
+    A[k] = 0;
+    m[k] = 0;
+    c[k] = 0;
+    if (ok && r < W) {
+      A[k] = bal[ro_v[k]];
+      m[k] = bal[ro_v[k + 1]] - A[k];
+      c[k] = (int32_t)cdiv(m[k], kTile);
+    }
+    mine += T * c[k];
   }
   int32_t ttot;
-  const int32_t pref = block_excl_scan<int32_t>(T * c, tmp32, &ttot);
-  if (r < W) tile_pref[r] = pref;
+  int32_t pref = block_excl_scan<int32_t>(mine, tmp32, &ttot);
   if (threadIdx.x == 0) tile_pref[W] = ttot;
-  for (int32_t t = 0; t < T; ++t)
-    for (int32_t k = 0; k < c; ++k) {
-      TileDesc d;
-      d.bm_lo = A + (int64_t)k * kTile;
-      d.n = (int32_t)min((int64_t)kTile, m - (int64_t)k * kTile);
-      d.seg = r * T + t;
-      d.q_lo = ro_r;
-      d.q_hi = ro_n;
-      d.pad[0] = d.pad[1] = 0;
-      tiles[pref + t * c + k] = d;
-    }
+#pragma unroll
+  for (int k = 0; k < kPrepRanks; ++k) {
+    const int32_t r = threadIdx.x * kPrepRanks + k;
+    if (r < W) tile_pref[r] = pref;
+    for (int32_t t = 0; t < T; ++t)
+      for (int32_t kk = 0; kk < c[k]; ++kk) {
+        TileDesc d;
+        d.bm_lo = A[k] + (int64_t)kk * kTile;
+        d.n = (int32_t)min((int64_t)kTile, m[k] - (int64_t)kk * kTile);
+        d.seg = r * T + t;
+        d.q_lo = ro_v[k];
+        d.q_hi = ro_v[k + 1];
+        d.pad[0] = d.pad[1] = 0;
+        tiles[pref + t * c[k] + kk] = d;
+      }
+    pref += T * c[k];
+  }
 }
 
 // ---------------------------------------------------------------- tiles

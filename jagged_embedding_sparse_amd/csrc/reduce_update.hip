@@ -189,7 +189,9 @@ __device__ __forceinline__ void update_row(const RUArgs& a, int64_t u, int sub,
 template <int D, typename WT>
 __global__ void __launch_bounds__(kThreads) k_short(RUArgs a) {
   using M = Map<D>;
-  constexpr int R = M::CPL <= 4 ? 4 : (M::CPL <= 8 ? 2 : 1);
+  // rows per lane group and batch: 2 keeps the register count at 90 (five
+  // waves per SIMD), which measured faster than 4 rows at four waves
+  constexpr int R = M::CPL <= 8 ? 2 : 1;
   constexpr int PER = M::GPW * R;  // rows per batch of the wave
   const int64_t u_lo = a.unique_offsets[a.g_lo], u_hi = a.unique_offsets[a.g_hi];
   const int l = lane(), grp = l / M::LPG, sub = l % M::LPG;

@@ -229,7 +229,7 @@ k_heads(const uint32_t* __restrict__ sk, const int64_t* __restrict__ nvp, int32_
   }
 }
 
-__global__ void __launch_bounds__(1024)
+__global__ void __launch_bounds__(kThreads)
 k_heads_scan(const int64_t* __restrict__ nvp, int32_t W, int32_t n_groups,
              uint32_t* __restrict__ tile_heads, int64_t* __restrict__ counts,
              int32_t* __restrict__ seg_offsets, int64_t* __restrict__ unique_offsets) {
@@ -408,7 +408,7 @@ k_collide(const int64_t* __restrict__ a, const int64_t* __restrict__ counts_a, i
 }
 
 // counts[1..3] from the per-block collision counts (one block).
-__global__ void __launch_bounds__(1024)
+__global__ void __launch_bounds__(kThreads)
 k_collide_counts(const uint32_t* __restrict__ block_hits, int64_t n_blocks,
                  const int64_t* __restrict__ counts_b, int64_t cap_b,
                  int64_t* __restrict__ counts) {
@@ -547,7 +547,7 @@ extern "C" int fs_unique_collision_split(const int64_t* shard_keys, const int32_
   hipLaunchKernelGGL(k_heads, dim3(grid), dim3(kThreads), 0, stream, sk, n_valid, W,
                      tile_heads);
   FS_LAUNCH_CHECK();
-  hipLaunchKernelGGL(k_heads_scan, dim3(1), dim3(1024), 0, stream, n_valid, W, T * W,
+  hipLaunchKernelGGL(k_heads_scan, dim3(1), dim3(kThreads), 0, stream, n_valid, W, T * W,
                      tile_heads, counts, seg_offsets, unique_offsets);
   FS_LAUNCH_CHECK();
   hipLaunchKernelGGL(k_compact, dim3(grid), dim3(kThreads), 0, stream, sk, n_valid, g,
@@ -557,7 +557,7 @@ extern "C" int fs_unique_collision_split(const int64_t* shard_keys, const int32_
                      unique, counts, n_cap, prev_unique, prev_counts, prev_cap, cls, prev_cls,
                      block_hits);
   FS_LAUNCH_CHECK();
-  hipLaunchKernelGGL(k_collide_counts, dim3(1), dim3(1024), 0, stream, block_hits, merge_blocks,
+  hipLaunchKernelGGL(k_collide_counts, dim3(1), dim3(kThreads), 0, stream, block_hits, merge_blocks,
                      prev_counts, prev_cap, counts);
   FS_LAUNCH_CHECK();
   return FS_OK;
