@@ -1,10 +1,11 @@
 """Benchmark of the prioritized jagged sparse step on one MI355X.
 
-A step is one pass of the whole hot path over one batch: balance (FBS or
-VBS), indexed permute + shard bucketize, dedup + collision split against the
-previous batch, the collision-row update of the previous iteration and the
-lookup of the new one on stream A, the exclusive-row lookup and update on
-stream B, and the join. Inputs (IDs, lengths, gradients, tables) are resident
+A step is one pass of the whole hot path over one batch: on stream B the
+update of every unique row of iteration i (segment-reduce + optimizer); on
+stream A balance (FBS or VBS), indexed permute + shard bucketize, dedup +
+collision split of batch i+1 against batch i, and the lookup of its exclusive
+rows; then, once B is done, the lookup of its collision rows on A. With
+--sync everything runs on one stream in the order index, update, lookup. Inputs (IDs, lengths, gradients, tables) are resident
 in HBM before the timed region; the timed region is K steps bracketed by
 torch.cuda.synchronize().
 
@@ -210,6 +211,12 @@ def main():
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, seed, host_batches, grads_host, weights, states)
 
+    # HBM bytes per launch of the dominant stage from the committed counter
+    # summary (rocprofv3 FETCH_SIZE / WRITE_SIZE, copy-calibrated), when it was
+    # taken on the kernel sources built here
+    from jagged_embedding_sparse_amd.traffic import load_traffic
+    traffic = load_traffic(args.config, dom)
+
     tables = "+".join(f"{t.rows // 1_000_000}Mx{t.dim}-{t.dtype}" if t.rows >= 1_000_000 else
                       f"{t.rows // 1000}Kx{t.dim}-{t.dtype}" for t in w.tables)
     out = {
@@ -233,7 +240,8 @@ def main():
             "distinct_batches": NB},
         "roofline": {
             "bound": "hbm", "achieved": dom_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-            "frac": dom_gbps / HBM_PEAK_GBPS, "traffic": None, "kernel": kernel_of[dom],
+            "frac": dom_gbps / HBM_PEAK_GBPS, "traffic": traffic,
+            "kernel": kernel_of[dom],
             "bytes_per_launch": dom_bytes_per_launch,
             "ms_per_launch": stage_avg[dom]},
         "step_hbm": {
