@@ -46,18 +46,40 @@ class _nullspan:
 
 
 class StageTimer:
-    """HIP event pairs around each C call, on the stream the call runs on."""
+    """HIP event pairs around each C call, on the stream the call runs on.
 
-    def __init__(self):
+    Events come from a pool made before timing starts and recorded once on
+    the streams that will use them. Records of timing events that need fresh
+    runtime resources cost tens of microseconds of host time each, which
+    inside the timed loop would let the host, not the GPU, set the pace of
+    small steps; the runtime recycles those resources when events are
+    dropped, so a larger pool made and dropped first keeps the timed
+    records cheap."""
+
+    def __init__(self, capacity=0, streams=None):
         self.pairs = {}
+        self.pool = []
+        ss = list(streams) if streams else [torch.cuda.current_stream()]
+        for i in range(capacity):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(ss[i % len(ss)])
+            b.record(ss[i % len(ss)])
+            self.pool.append((a, b))
+        torch.cuda.synchronize()
+        self.pool.reverse()
+
+    def _pair(self):
+        if self.pool:
+            return self.pool.pop()
+        return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
     def span(self, name, stream):
         timer = self
 
         class _Span:
             def __enter__(self):
-                self.a = torch.cuda.Event(enable_timing=True)
-                self.b = torch.cuda.Event(enable_timing=True)
+                self.a, self.b = timer._pair()
                 self.a.record(stream)
                 return self
 
