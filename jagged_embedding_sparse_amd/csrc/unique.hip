@@ -4,12 +4,15 @@
 // section 3.2 and Algorithm 2: the collision and exclusive index sets of
 // iterations i and i+1 are computed on the shard-major (post-AllToAll) IDs.
 //
-//  1. LSD radix sort of (key, bm) over the shard-major items with digits of
-//     up to 10 bits, as few passes as the key space needs (28-bit keys: 3).
-//     Every pass is a stable counting sort (per-tile digit histograms as rows
-//     of a tiles x digits matrix, coalesced column scans, per-tile ranked
-//     scatter), so equal keys keep their shard-major order, which for one
-//     key is ascending bm: the CSR's occurrence order falls out.
+//  1. LSD radix sort of (key, bm) inside every shard of the shard-major
+//     items, on the shard-local key (rows of one shard of every table,
+//     numbered densely: ~19 bits at 200M rows over 512 shards, so two passes
+//     of up to 10-bit digits), stable; the last pass writes global keys and,
+//     with several tables, moves each (table, shard) group to its place in
+//     table-major order. Every pass is a stable counting sort (per-tile digit
+//     histograms as rows of a tiles x digits matrix, coalesced column scans,
+//     per-tile ranked scatter), so equal keys keep their shard-major order,
+//     which for one key is ascending bm: the CSR's occurrence order falls out.
 //  2. Head flags (key differs from its left neighbour), one scan over tiles,
 //     compaction: unique keys, CSR segment starts, occurrence -> unique index,
 //     and the (table, shard) group offsets, written where the group changes.
@@ -38,58 +41,231 @@ struct Groups {
 __device__ __forceinline__ int32_t group_of(uint32_t key, const Groups& g) {
   int t = 0;
   while (t + 1 < g.T && (int64_t)key >= g.row_base[t + 1]) ++t;
-  // row within the table and the shard block both fit 32 bits
-  return t * g.W + (int32_t)((uint32_t)((int64_t)key - g.row_base[t]) / (uint32_t)g.block[t]);
+  // row within the table and the shard block both fit 32 bits; clamped so
+  // that keys which are no row still name a group
+  const uint32_t d = (uint32_t)((int64_t)key - g.row_base[t]) / (uint32_t)g.block[t];
+  return t * g.W + (int32_t)min(d, (uint32_t)(g.W - 1));
 }
 
 // Valid item count of the call: shard_offsets[W] clamped to the capacity the
-// host sized every buffer for (k_init stores it; later kernels read it).
+// host sized every buffer for (the prep kernel stores it; later kernels read
+// it).
 __device__ __forceinline__ int64_t n_valid_of(const int64_t* n_valid, int32_t W) {
   (void)W;
   return *n_valid;
 }
 
-// ---------------------------------------------------------------- init
-__global__ void k_init(const int64_t* __restrict__ shard_offsets, int32_t W, int64_t n_cap,
-                       int64_t* __restrict__ n_valid) {
-  if (threadIdx.x == 0) {
-    const int64_t v = shard_offsets[W];
-    *n_valid = v < 0 ? 0 : (v > n_cap ? n_cap : v);
+// ---------------------------------------------------------------- shard-local keys
+// Shard d holds rows [d*block_t, (d+1)*block_t) of every table t. Inside the
+// shard a key is (t, row - d*block_t); numbered densely over the tables,
+// local = shard_off[t] + row - d*block_t < shard_off[T] = sum_t block_t, it
+// sorts exactly as the global key and needs far fewer bits.
+struct SegKeys {
+  int64_t row_base[FS_MAX_TABLES + 1];
+  int64_t block[FS_MAX_TABLES];
+  uint32_t shard_off[FS_MAX_TABLES + 1];
+  int32_t T, W;
+};
+
+__device__ __forceinline__ int table_of_key(int64_t key, const SegKeys& k) {
+  int t = 0;
+  while (t + 1 < k.T && key >= k.row_base[t + 1]) ++t;
+  return t;
+}
+
+// shard-local key of a global key in shard d (rows outside the shard clamp)
+__device__ __forceinline__ uint32_t local_key(int64_t key, int32_t d, const SegKeys& k) {
+  const int t = table_of_key(key, k);
+  int64_t r = key - k.row_base[t] - (int64_t)d * k.block[t];
+  r = r < 0 ? 0 : (r >= k.block[t] ? k.block[t] - 1 : r);
+  return k.shard_off[t] + (uint32_t)r;
+}
+
+__device__ __forceinline__ int table_of_local(uint32_t lk, const SegKeys& k) {
+  int t = 0;
+  while (t + 1 < k.T && lk >= k.shard_off[t + 1]) ++t;
+  return t;
+}
+
+__device__ __forceinline__ uint32_t global_key(uint32_t lk, int32_t d, const SegKeys& k) {
+  const int t = table_of_local(lk, k);
+  return (uint32_t)(k.row_base[t] + (int64_t)d * k.block[t] + (lk - k.shard_off[t]));
+}
+
+// A tile: items [lo, lo + n) of shard d, n <= 4096; tiles never straddle a
+// shard and are numbered in position order.
+struct UTile {
+  int32_t lo, n, d, pad;
+};
+
+// ---------------------------------------------------------------- prep
+// Segment bounds (shard_offsets clamped into [0, n_cap] and made
+// non-decreasing, segment 0 from 0; with one segment: all valid items), the
+// valid item count and the tile table. Thread i owns segments 5i .. 5i + 4
+// (and the end bound W).
+constexpr int kSegPer = (FS_MAX_RANKS + 1 + kThreads - 1) / kThreads;
+
+__global__ void __launch_bounds__(kThreads)
+k_seg_prep(const int64_t* __restrict__ so, int32_t W_so, int32_t W, int64_t n_cap,
+           int64_t* __restrict__ n_valid, int32_t* __restrict__ seg_lo,
+           int32_t* __restrict__ tile_first, UTile* __restrict__ tiles) {
+  __shared__ int32_t wmax[kThreads / kWave];
+  __shared__ int32_t tmp32[17];
+  int32_t v[kSegPer];
+  int32_t run = 0;
+#pragma unroll
+  for (int k = 0; k < kSegPer; ++k) {
+    const int32_t d = threadIdx.x * kSegPer + k;
+    // one segment (W == 1): all valid items; else shard d starts at so[d]
+    int64_t x = (d > 0 && d <= W) ? so[W == 1 ? W_so : d] : 0;
+    x = x < 0 ? 0 : (x > n_cap ? n_cap : x);
+    run = max(run, (int32_t)x);
+    v[k] = run;  // running maximum inside the thread
+  }
+  // exclusive maximum over the threads before this one
+  int32_t inc = run;
+#pragma unroll
+  for (int dd = 1; dd < kWave; dd <<= 1) {
+    const int32_t t = __shfl_up(inc, dd, kWave);
+    if (lane() >= dd) inc = max(inc, t);
+  }
+  const int w = threadIdx.x / kWave;
+  if (lane() == kWave - 1) wmax[w] = inc;
+  __syncthreads();
+  int32_t before = 0;
+  for (int x = 0; x < w; ++x) before = max(before, wmax[x]);
+  int32_t ex = __shfl_up(inc, 1, kWave);
+  before = max(before, lane() == 0 ? 0 : ex);
+  int32_t lo[kSegPer];
+#pragma unroll
+  for (int k = 0; k < kSegPer; ++k) lo[k] = max(before, v[k]);
+#pragma unroll
+  for (int k = 0; k < kSegPer; ++k) {
+    const int32_t d = threadIdx.x * kSegPer + k;
+    if (d <= W) seg_lo[d] = lo[k];
+    if (d == W) *n_valid = lo[k];
+  }
+  __syncthreads();  // seg_lo visible to the workgroup
+  int32_t c[kSegPer], size[kSegPer];
+  int32_t mine = 0;
+#pragma unroll
+  for (int k = 0; k < kSegPer; ++k) {
+    const int32_t d = threadIdx.x * kSegPer + k;
+    size[k] = d < W ? seg_lo[d + 1] - lo[k] : 0;
+    c[k] = (int32_t)cdiv(size[k], kTile);
+    mine += c[k];
+  }
+  int32_t tt;
+  int32_t pref = block_excl_scan<int32_t>(mine, tmp32, &tt);
+  if (threadIdx.x == 0) tile_first[W] = tt;
+#pragma unroll
+  for (int k = 0; k < kSegPer; ++k) {
+    const int32_t d = threadIdx.x * kSegPer + k;
+    if (d < W) tile_first[d] = pref;
+    for (int32_t j = 0; j < c[k]; ++j) {
+      UTile u;
+      u.lo = lo[k] + j * kTile;
+      u.n = min(kTile, size[k] - j * kTile);
+      u.d = d;
+      u.pad = 0;
+      tiles[pref + j] = u;
+    }
+    pref += c[k];
   }
 }
 
 // ---------------------------------------------------------------- radix pass
-// Per pass: k_rs_hist writes each tile's digit histogram as one row of the
-// count matrix (LDS atomics; zeros past the valid items); the column scans
-// turn every digit's column into exclusive offsets and the digit's total;
-// k_rs_scatter adds the digit bases, ranks its tile stably, sorts it by digit
-// in LDS and writes every digit's run contiguously. Tiles follow the XCD
-// order. No device-scope atomics anywhere.
-template <typename KIn>
+// LSD radix sort of every shard's items by shard-local key, stable, digits of
+// up to 10 bits. Per pass: k_seg_hist writes each tile's digit histogram as
+// one row of the count matrix (LDS atomics; zero rows for unused tiles; the
+// first pass also counts items per table); the column scans turn each
+// digit's column into exclusive offsets over all tiles; k_seg_scatter takes
+// its shard's digit counts as differences of the scanned rows at the shard's
+// first tile and the next shard's, so positions restart at every shard,
+// ranks its tile stably, sorts it in LDS and writes each digit's run
+// contiguously. The last pass writes global keys, moved to their (table,
+// shard) group when there are several tables. Tiles follow the XCD order.
+template <typename KIn, bool kFirst>
 __global__ void __launch_bounds__(kThreads)
-k_rs_hist(const KIn* __restrict__ keys, const int64_t* __restrict__ nvp, int32_t W, int shift,
-          uint32_t mask, uint32_t* __restrict__ hist) {
+k_seg_hist(const KIn* __restrict__ keys, const UTile* __restrict__ tiles,
+           const int32_t* __restrict__ tile_first, SegKeys sk, int shift, uint32_t mask,
+           uint32_t* __restrict__ hist, uint32_t* __restrict__ cnt_t) {
   __shared__ uint32_t h[kMaxBins];
-  const int64_t n = n_valid_of(nvp, W);
+  __shared__ uint32_t ht[FS_MAX_TABLES];
   const int32_t tile = xcd_tile(blockIdx.x, gridDim.x);
-  const int64_t t0 = (int64_t)tile * kTile;
   const int nb = (int)mask + 1;
   for (int b = threadIdx.x; b < nb; b += kThreads) h[b] = 0;
+  if (threadIdx.x < FS_MAX_TABLES) ht[threadIdx.x] = 0;
   __syncthreads();
-  if (t0 < n) {
-    // all 16 loads in flight (past n: the last item, not counted)
-    uint32_t d[kRounds];
+  if (tile < tile_first[sk.W]) {
+    const UTile u = tiles[tile];
+    // all 16 loads in flight (past the tile: its last item, not counted)
+    uint32_t dg[kRounds];
+    int tb[kRounds];
 #pragma unroll
     for (int i = 0; i < kRounds; ++i) {
-      const int64_t x = t0 + i * kThreads + threadIdx.x;
-      d[i] = ((uint32_t)keys[x < n ? x : n - 1] >> shift) & mask;
+      const int x = i * kThreads + threadIdx.x;
+      const KIn kv = keys[u.lo + (x < u.n ? x : u.n - 1)];
+      uint32_t lk;
+      if constexpr (kFirst) {
+        lk = local_key((int64_t)kv, u.d, sk);
+        tb[i] = table_of_local(lk, sk);
+      } else {
+        lk = (uint32_t)kv;
+        tb[i] = 0;
+      }
+      dg[i] = (lk >> shift) & mask;
     }
 #pragma unroll
-    for (int i = 0; i < kRounds; ++i)
-      if (t0 + i * kThreads + threadIdx.x < n) atomicAdd(&h[d[i]], 1u);
+    for (int i = 0; i < kRounds; ++i) {
+      if (i * kThreads + (int)threadIdx.x < u.n) {
+        atomicAdd(&h[dg[i]], 1u);
+        if (kFirst && cnt_t) atomicAdd(&ht[tb[i]], 1u);
+      }
+    }
   }
   __syncthreads();
   for (int b = threadIdx.x; b < nb; b += kThreads) hist[(int64_t)tile * kMaxBins + b] = h[b];
+  if (kFirst && cnt_t && threadIdx.x < FS_MAX_TABLES)
+    cnt_t[(int64_t)tile * FS_MAX_TABLES + threadIdx.x] = ht[threadIdx.x];
+}
+
+// Several tables: shard d's sorted items are table-major; group (t, d) must
+// move to its place in (table, shard) order. delta[t*W + d] = that place
+// minus where the group starts inside the shard-sorted order.
+__global__ void __launch_bounds__(kThreads)
+k_seg_groups(const uint32_t* __restrict__ cnt_t, const int32_t* __restrict__ tile_first,
+             const int32_t* __restrict__ seg_lo, int32_t W, int32_t T,
+             int32_t* __restrict__ delta) {
+  __shared__ int64_t tmp[17];
+  int32_t size[kSegPer][FS_MAX_TABLES];
+#pragma unroll
+  for (int k = 0; k < kSegPer; ++k) {
+    const int32_t d = threadIdx.x * kSegPer + k;
+    for (int t = 0; t < FS_MAX_TABLES; ++t) size[k][t] = 0;
+    if (d < W)
+      for (int32_t q = tile_first[d]; q < tile_first[d + 1]; ++q)
+        for (int t = 0; t < T; ++t) size[k][t] += (int32_t)cnt_t[(int64_t)q * FS_MAX_TABLES + t];
+  }
+  int64_t table_base = 0;
+  for (int t = 0; t < T; ++t) {
+    int64_t local = 0;
+#pragma unroll
+    for (int k = 0; k < kSegPer; ++k) local += size[k][t];
+    int64_t tot;
+    int64_t g = table_base + block_excl_scan<int64_t>(local, tmp, &tot);
+#pragma unroll
+    for (int k = 0; k < kSegPer; ++k) {
+      const int32_t d = threadIdx.x * kSegPer + k;
+      if (d < W) {
+        int64_t inside = seg_lo[d];
+        for (int t2 = 0; t2 < t; ++t2) inside += size[k][t2];
+        delta[t * W + d] = (int32_t)(g - inside);
+      }
+      g += size[k][t];
+    }
+    table_base += tot;
+  }
 }
 
 // Staging area of one tile: first the per-wave lane-mask tables of the
@@ -102,22 +278,24 @@ union RadixStage {
   } s;
 };
 
-template <typename KIn>
+template <typename KIn, bool kFirst, bool kLast>
 __global__ void __launch_bounds__(kThreads)
-k_rs_scatter(const KIn* __restrict__ keys_in, const int32_t* __restrict__ vals_in,
-             const int64_t* __restrict__ nvp, int32_t W, int shift, uint32_t mask,
-             const uint32_t* __restrict__ offs, const uint32_t* __restrict__ tot,
-             uint32_t* __restrict__ keys_out, int32_t* __restrict__ vals_out) {
+k_seg_scatter(const KIn* __restrict__ keys_in, const int32_t* __restrict__ vals_in,
+              const UTile* __restrict__ tiles, const int32_t* __restrict__ tile_first,
+              const int32_t* __restrict__ seg_lo, SegKeys sk, int shift, uint32_t mask,
+              const uint32_t* __restrict__ offs, const uint32_t* __restrict__ tot,
+              const int32_t* __restrict__ delta, uint32_t* __restrict__ keys_out,
+              int32_t* __restrict__ vals_out) {
   __shared__ uint16_t cnt[kThreads / kWave][kMaxBins];
-  __shared__ uint32_t dig_base[kMaxBins];  // global start of each digit's run of this tile
+  __shared__ uint32_t dig_base[kMaxBins];  // output start of each digit's run of this tile
   __shared__ uint32_t dig_tile[kMaxBins];  // start of each digit inside the LDS-sorted tile
   __shared__ RadixStage st;
   __shared__ int64_t tmp[17];
   constexpr int kPer = kMaxBins / kThreads;
-  const int64_t n = n_valid_of(nvp, W);
   const int32_t tile = xcd_tile(blockIdx.x, gridDim.x);
-  const int64_t t0 = (int64_t)tile * kTile;
-  if (t0 >= n) return;  // uniform per workgroup
+  const int32_t n_tiles = tile_first[sk.W];
+  if (tile >= n_tiles) return;  // uniform per workgroup
+  const UTile u = tiles[tile];
   const int nb = (int)mask + 1;
   const int w = threadIdx.x / kWave;
   for (int b = lane(); b < nb; b += kWave) {
@@ -129,10 +307,11 @@ k_rs_scatter(const KIn* __restrict__ keys_in, const int32_t* __restrict__ vals_i
   const uint32_t none = mask + 1;  // lanes without an item
 #pragma unroll
   for (int i = 0; i < kRounds; ++i) {
-    const int64_t x = t0 + (int64_t)w * kWaveItems + i * kWave + lane();
-    const bool valid = x < n;
-    const int64_t xc = valid ? x : n - 1;  // unconditional loads, all in flight
-    key[i] = (uint32_t)keys_in[xc];
+    const int x = w * kWaveItems + i * kWave + lane();
+    const bool valid = x < u.n;
+    const int xc = u.lo + (valid ? x : u.n - 1);  // unconditional loads, all in flight
+    if constexpr (kFirst) key[i] = local_key((int64_t)keys_in[xc], u.d, sk);
+    else key[i] = (uint32_t)keys_in[xc];
     val[i] = vals_in[xc];
     dig[i] = valid ? ((key[i] >> shift) & mask) : none;
   }
@@ -141,24 +320,29 @@ k_rs_scatter(const KIn* __restrict__ keys_in, const int32_t* __restrict__ vals_i
 #pragma unroll
   for (int i = 0; i < kRounds; ++i) {
     const bool on = dig[i] != none;
-    const uint32_t d = on ? dig[i] : 0u;
-    const uint64_t peers = lds_peers(st.peers[w], d, on);
-    const uint32_t before = cnt[w][d];
+    const uint32_t dd = on ? dig[i] : 0u;
+    const uint64_t peers = lds_peers(st.peers[w], dd, on);
+    const uint32_t before = cnt[w][dd];
     rk[i] = before + (uint32_t)popc(peers & lt);
-    if (on && (peers & lt) == 0) cnt[w][d] = (uint16_t)(before + (uint32_t)popc(peers));
+    if (on && (peers & lt) == 0) cnt[w][dd] = (uint16_t)(before + (uint32_t)popc(peers));
   }
   __syncthreads();
   {
     // per digit: exclusive prefix over the waves, the digits' starts in the
-    // tile, and the global bases (exclusive scan of the totals + this
-    // tile's column offsets)
-    uint32_t tb[kPer], tt[kPer];
-    int64_t local = 0, tlocal = 0;
+    // tile, and the output bases: the shard's start, plus the shard's items
+    // of smaller digits, plus the digit's items in the shard's earlier tiles
+    const int32_t f = tile_first[u.d], nx = tile_first[u.d + 1];
+    const uint32_t* pf = offs + (int64_t)f * kMaxBins;
+    const uint32_t* pn = nx < (int32_t)gridDim.x ? offs + (int64_t)nx * kMaxBins : tot;
+    const uint32_t* pt = offs + (int64_t)tile * kMaxBins;
+    uint32_t tb[kPer], sc[kPer], mine[kPer];
+    int64_t local = 0, slocal = 0;
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
       const int b = threadIdx.x * kPer + k;
       uint32_t run = 0;
-      tt[k] = 0;
+      sc[k] = 0;
+      mine[k] = 0;
       if (b < nb) {
 #pragma unroll
         for (int x = 0; x < kThreads / kWave; ++x) {
@@ -166,25 +350,28 @@ k_rs_scatter(const KIn* __restrict__ keys_in, const int32_t* __restrict__ vals_i
           cnt[x][b] = (uint16_t)run;
           run += c;
         }
-        tt[k] = tot[b];
+        const uint32_t first = pf[b];
+        sc[k] = pn[b] - first;  // the shard's items with digit b
+        mine[k] = pt[b] - first;  // ... in the shard's tiles before this one
       }
       tb[k] = run;
       local += run;
-      tlocal += tt[k];
+      slocal += sc[k];
     }
     int64_t all;
     int64_t r0 = block_excl_scan<int64_t>(local, tmp, &all);
-    int64_t gsum;
-    int64_t g0 = block_excl_scan<int64_t>(tlocal, tmp, &gsum);
+    int64_t ssum;
+    int64_t s0 = block_excl_scan<int64_t>(slocal, tmp, &ssum);
+    const int64_t base = seg_lo[u.d];
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
       const int b = threadIdx.x * kPer + k;
       if (b < nb) {
         dig_tile[b] = (uint32_t)r0;
-        dig_base[b] = (uint32_t)(g0 + offs[(int64_t)tile * kMaxBins + b]);
+        dig_base[b] = (uint32_t)(base + s0 + mine[k]);
       }
       r0 += tb[k];
-      g0 += tt[k];
+      s0 += sc[k];
     }
   }
   __syncthreads();  // also ends every wave's use of the mask tables
@@ -196,12 +383,16 @@ k_rs_scatter(const KIn* __restrict__ keys_in, const int32_t* __restrict__ vals_i
     st.s.val[p] = val[i];
   }
   __syncthreads();
-  const int m = (int)min((int64_t)kTile, n - t0);
-  for (int p = threadIdx.x; p < m; p += kThreads) {
+  for (int p = threadIdx.x; p < u.n; p += kThreads) {
     const uint32_t k = st.s.key[p];
-    const uint32_t d = (k >> shift) & mask;
-    const uint32_t pos = dig_base[d] + (uint32_t)p - dig_tile[d];
-    keys_out[pos] = k;
+    const uint32_t dd = (k >> shift) & mask;
+    uint32_t pos = dig_base[dd] + (uint32_t)p - dig_tile[dd];
+    uint32_t kout = k;
+    if constexpr (kLast) {
+      kout = global_key(k, u.d, sk);
+      if (sk.T > 1 && sk.W > 1) pos += (uint32_t)delta[table_of_local(k, sk) * sk.W + u.d];
+    }
+    keys_out[pos] = kout;
     vals_out[pos] = st.s.val[p];
   }
 }
@@ -437,13 +628,16 @@ static int key_bits(int64_t key_space) {
   return b;
 }
 
+// tiles of the radix passes: sum over shards of ceil(items / 4096) <= this
+static int64_t seg_tiles(int64_t cap, int32_t W) {
+  return (int64_t)align_up((size_t)(cdiv(cap, kTile) + W), kXcd);
+}
+
 extern "C" size_t fs_unique_workspace_size(int64_t n_cap, int64_t prev_cap, int32_t T,
                                            int32_t W) {
-  (void)T;
-  (void)W;
   const int64_t cap = n_cap > 0 ? n_cap : 1;
   const int64_t tiles = cdiv(cap, kTile);
-  const int64_t G = (int64_t)align_up((size_t)tiles, kXcd);
+  const int64_t G = seg_tiles(cap, W);
   Carve c(nullptr);
   c.take<uint32_t>((size_t)cap);                // keys A
   c.take<uint32_t>((size_t)cap);                // keys B
@@ -452,6 +646,11 @@ extern "C" size_t fs_unique_workspace_size(int64_t n_cap, int64_t prev_cap, int3
   c.take<uint32_t>((size_t)(G * kMaxBins));     // tiles x digits counts, then offsets
   c.take<uint32_t>((size_t)(cdiv(G, kColBlockRows) * kMaxBins));  // column partials
   c.take<uint32_t>((size_t)kMaxBins);           // digit totals
+  c.take<UTile>((size_t)G);                     // radix tiles
+  c.take<uint32_t>((size_t)(G * FS_MAX_TABLES));  // items per tile and table
+  c.take<int32_t>((size_t)W + 1);               // shard starts
+  c.take<int32_t>((size_t)W + 1);               // first tile of each shard
+  c.take<int32_t>((size_t)T * W);               // group moves (several tables)
   c.take<uint32_t>((size_t)tiles);              // heads per tile
   c.take<int64_t>(1);                           // valid item count
   c.take<uint32_t>((size_t)cdiv(cap + (prev_cap > 0 ? prev_cap : 0), kMergeTile) + 1);
@@ -491,25 +690,55 @@ extern "C" int fs_unique_collision_split(const int64_t* shard_keys, const int32_
   if (base > (int64_t)UINT32_MAX) return FS_ERR_UNSUPPORTED;
   if (!ws || ws_bytes < fs_unique_workspace_size(n_cap, prev_cap, T, W)) return FS_ERR_WORKSPACE;
 
+  // Sort inside the W shards (shard-local keys: fewer bits, so often one pass
+  // fewer) or over all items as one segment (local key = global key): one
+  // tile pass costs about its tile count, and the shard tiling adds up to one
+  // partial tile per shard.
+  int64_t span_w = 0, span_1 = base;
+  for (int t = 0; t < T; ++t) span_w += g.block[t];
+  const int64_t cap_tiles = cdiv(n_cap > 0 ? n_cap : 1, kTile);
+  const int passes_w = (key_bits(span_w) + kMaxDigitBits - 1) / kMaxDigitBits;
+  const int passes_1 = (key_bits(span_1) + kMaxDigitBits - 1) / kMaxDigitBits;
+  const bool by_shard = W > 1 && passes_w * (cap_tiles + W) < passes_1 * cap_tiles;
+  const int32_t nseg = by_shard ? W : 1;
+  SegKeys lk;
+  lk.T = T;
+  lk.W = nseg;
+  uint32_t span = 0;
+  for (int t = 0; t < T; ++t) {
+    lk.row_base[t] = g.row_base[t];
+    lk.block[t] = by_shard ? g.block[t] : tables[t].rows;
+    lk.shard_off[t] = span;
+    span += (uint32_t)lk.block[t];  // at most the sum of rows < 2^32
+  }
+  lk.row_base[T] = base;
+  lk.shard_off[T] = span;
+
   const int64_t cap = n_cap > 0 ? n_cap : 1;
   const int64_t tiles = cdiv(cap, kTile);
+  const int64_t G = seg_tiles(cap, W);
   Carve c(ws);
   uint32_t* ka = c.take<uint32_t>((size_t)cap);
   uint32_t* kb = c.take<uint32_t>((size_t)cap);
   int32_t* va = c.take<int32_t>((size_t)cap);
   int32_t* vb = c.take<int32_t>((size_t)cap);
-  const int64_t G = (int64_t)align_up((size_t)tiles, kXcd);
   uint32_t* hist = c.take<uint32_t>((size_t)(G * kMaxBins));
   uint32_t* part = c.take<uint32_t>((size_t)(cdiv(G, kColBlockRows) * kMaxBins));
   uint32_t* tot = c.take<uint32_t>((size_t)kMaxBins);
+  UTile* utiles = c.take<UTile>((size_t)G);
+  uint32_t* cnt_t = c.take<uint32_t>((size_t)(G * FS_MAX_TABLES));
+  int32_t* seg_lo = c.take<int32_t>((size_t)W + 1);
+  int32_t* tile_first = c.take<int32_t>((size_t)W + 1);
+  int32_t* delta = c.take<int32_t>((size_t)T * W);
   uint32_t* tile_heads = c.take<uint32_t>((size_t)tiles);
   int64_t* n_valid = c.take<int64_t>(1);
   const int64_t merge_blocks = cdiv(cap + prev_cap, kMergeTile);
   uint32_t* block_hits = c.take<uint32_t>((size_t)merge_blocks);
 
-  const int kbits = key_bits(base);
+  const int kbits = key_bits(span);
   const int passes = (kbits + kMaxDigitBits - 1) / kMaxDigitBits;
-  hipLaunchKernelGGL(k_init, dim3(1), dim3(64), 0, stream, shard_offsets, W, n_cap, n_valid);
+  hipLaunchKernelGGL(k_seg_prep, dim3(1), dim3(kThreads), 0, stream, shard_offsets, W, nseg,
+                     n_cap, n_valid, seg_lo, tile_first, utiles);
   FS_LAUNCH_CHECK();
   uint32_t* kbuf[2] = {ka, kb};
   int32_t* vbuf[2] = {va, vb};
@@ -517,29 +746,44 @@ extern "C" int fs_unique_collision_split(const int64_t* shard_keys, const int32_
   const unsigned rgrid = (unsigned)G;
   int shift = 0;
   for (int p = 0; p < passes; ++p) {
-    // digits as even as the passes allow: 28 bits -> 10, 9, 9
+    // digits as even as the passes allow: 19 bits -> 10, 9
     const int bits = (kbits - shift + (passes - p) - 1) / (passes - p);
     const uint32_t mask = (1u << bits) - 1u;
+    const bool first = p == 0, last = p == passes - 1;
     uint32_t* kout = kbuf[p & 1];
-    int32_t* vout = (p == passes - 1) ? occ_bm : vbuf[p & 1];
-    if (p == 0) {
-      hipLaunchKernelGGL(k_rs_hist<int64_t>, dim3(rgrid), dim3(kThreads), 0, stream, shard_keys,
-                         n_valid, W, shift, mask, hist);
-    } else {
-      hipLaunchKernelGGL(k_rs_hist<uint32_t>, dim3(rgrid), dim3(kThreads), 0, stream,
-                         kbuf[(p - 1) & 1], n_valid, W, shift, mask, hist);
-    }
+    int32_t* vout = last ? occ_bm : vbuf[p & 1];
+    if (first)
+      hipLaunchKernelGGL((k_seg_hist<int64_t, true>), dim3(rgrid), dim3(kThreads), 0, stream,
+                         shard_keys, utiles, tile_first, lk, shift, mask, hist,
+                         (T > 1 && nseg > 1) ? cnt_t : (uint32_t*)nullptr);
+    else
+      hipLaunchKernelGGL((k_seg_hist<uint32_t, false>), dim3(rgrid), dim3(kThreads), 0, stream,
+                         kbuf[(p - 1) & 1], utiles, tile_first, lk, shift, mask, hist,
+                         (uint32_t*)nullptr);
     FS_LAUNCH_CHECK();
     int rc = launch_colscan(hist, kMaxBins, (int32_t)G, (int32_t)mask + 1, part, tot, stream);
     if (rc) return rc;
-    if (p == 0) {
-      hipLaunchKernelGGL(k_rs_scatter<int64_t>, dim3(rgrid), dim3(kThreads), 0, stream,
-                         shard_keys, shard_bm, n_valid, W, shift, mask, hist, tot, kout, vout);
-    } else {
-      hipLaunchKernelGGL(k_rs_scatter<uint32_t>, dim3(rgrid), dim3(kThreads), 0, stream,
-                         kbuf[(p - 1) & 1], vbuf[(p - 1) & 1], n_valid, W, shift, mask, hist,
-                         tot, kout, vout);
+    if (last && T > 1 && nseg > 1) {
+      hipLaunchKernelGGL(k_seg_groups, dim3(1), dim3(kThreads), 0, stream, cnt_t, tile_first,
+                         seg_lo, W, T, delta);
+      FS_LAUNCH_CHECK();
     }
+    if (first && last)
+      hipLaunchKernelGGL((k_seg_scatter<int64_t, true, true>), dim3(rgrid), dim3(kThreads), 0,
+                         stream, shard_keys, shard_bm, utiles, tile_first, seg_lo, lk, shift,
+                         mask, hist, tot, delta, kout, vout);
+    else if (first)
+      hipLaunchKernelGGL((k_seg_scatter<int64_t, true, false>), dim3(rgrid), dim3(kThreads), 0,
+                         stream, shard_keys, shard_bm, utiles, tile_first, seg_lo, lk, shift,
+                         mask, hist, tot, delta, kout, vout);
+    else if (last)
+      hipLaunchKernelGGL((k_seg_scatter<uint32_t, false, true>), dim3(rgrid), dim3(kThreads), 0,
+                         stream, kbuf[(p - 1) & 1], vbuf[(p - 1) & 1], utiles, tile_first,
+                         seg_lo, lk, shift, mask, hist, tot, delta, kout, vout);
+    else
+      hipLaunchKernelGGL((k_seg_scatter<uint32_t, false, false>), dim3(rgrid), dim3(kThreads), 0,
+                         stream, kbuf[(p - 1) & 1], vbuf[(p - 1) & 1], utiles, tile_first,
+                         seg_lo, lk, shift, mask, hist, tot, delta, kout, vout);
     FS_LAUNCH_CHECK();
     shift += bits;
   }

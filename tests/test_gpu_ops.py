@@ -223,9 +223,15 @@ def _cmp_unique(uq, ouq, cls, pcls, counts):
         assert np.array_equal(host(uq["prev_cls"])[:len(pcls)], pcls)
 
 
+# s11-s16 sort all items as one segment; s17-s19 are sized so that sorting
+# inside the shards saves a pass (2^21 rows: 21-bit global keys, 3 passes;
+# 20-bit shard-local keys, 2 passes; ~100-150 tiles against 2-3 shards), with
+# one, two and three tables (the (table, shard) group moves)
 UQ_CASES = [(11, 64, [100_000], 4, 60), (12, 512, [300, 5000], 16, 200),
             (13, 2048, [20_000, 20_000, 9000, 500], 256, 40), (14, 37, [50], 8, 30),
-            (15, 4096, [200_000_000], 512, 60), (16, 3, [7], 2, 3)]
+            (15, 4096, [200_000_000], 512, 60), (16, 3, [7], 2, 3),
+            (17, 2048, [1 << 21], 2, 400), (18, 2048, [1 << 20, 1 << 20], 2, 200),
+            (19, 2048, [1 << 20, 700_000, 300_000], 3, 100)]
 
 
 @pytest.mark.parametrize("case", UQ_CASES, ids=lambda c: f"s{c[0]}")
