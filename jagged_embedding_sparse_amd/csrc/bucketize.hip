@@ -12,16 +12,17 @@
 // (rank, table) segment and are numbered in (r, t, chunk) order, so an
 // item's output position is its shard's base, plus the shard's count in all
 // earlier tiles, plus its stable rank inside its tile:
-//   k_prep     balanced offsets, per-sample shifts, tile descriptors (one
-//              workgroup of 256 threads)
+//   k_lens, k_bal, k_tiles   balanced offsets, per-sample shifts, tile
+//              descriptors (short dependent-load chains)
 //   k_hist     per-tile shard histograms -> rows of a tiles x shards matrix;
 //              each item's 32-bit key, batch-major
 //   k_colsum, k_colscan   exclusive column scans of that matrix in place,
 //              with coalesced row loads (lanes = shards)
-//   k_splits   shard offsets; splits[d][r] as differences of the scanned
-//              matrix at rank boundaries (transposed through LDS)
-//   k_scatter  per tile: the keys back, stable ranks (LDS lane masks), sort
-//              by shard in LDS, one contiguous run per shard.
+//   k_scatter  per tile: shard bases from the totals, the keys back, stable
+//              ranks (LDS lane masks), sort by shard in LDS, one contiguous
+//              run per shard; extra workgroups of the same launch write the
+//              shard offsets and splits[d][r] (differences of the scanned
+//              matrix at rank boundaries, transposed through LDS).
 // Consecutive tiles run on the same XCD (workgroups are dealt to the 8 XCDs
 // round-robin), so the short runs that neighbouring tiles of one segment
 // write next to each other meet in one L2. No device-scope atomics.
@@ -55,55 +56,88 @@ struct TileDesc {
 };
 
 // ---------------------------------------------------------------- prep
-// One workgroup of 256 threads (larger ones wait for free slots while another
-// stream's kernels hold the CUs). Thread i owns balanced samples
-// [64 i, 64 i + 64) and ranks 4 i .. 4 i + 3.
-constexpr int kPrepThreads = 256;
-constexpr int kPrepPer = FS_MAX_SAMPLES / kPrepThreads;       // samples per thread
-constexpr int kPrepRanks = (FS_MAX_RANKS + 1) / kPrepThreads;  // ranks per thread (+ W)
-constexpr int kPrepUnroll = 8;  // offset validation: loads in flight per thread
-constexpr int kPrepBatch = 16;  // samples whose loads are in flight together
-
-// Validation, bal_offsets, shift[q] = so[perm[q]] - bal[q], the tile table.
+// Three launches, each with short chains of dependent loads (the index path
+// runs beside the bandwidth-bound update of another stream, where every
+// dependent round trip to memory waits in deep queues):
+//   k_lens   one thread per balanced sample: its length and first token
+//            under perm, validation of perm and the sample offsets, per
+//            workgroup sums and flags
+//   k_bal    one thread per balanced sample: bal_offsets and shift from the
+//            workgroup sums and a workgroup scan
+//   k_tiles  one workgroup: rank offsets validated, the tile table
 // Invalid input (offsets not rising from 0 to n_tok, a perm entry out of
 // range, rank offsets not rising from 0 to n, or lengths under perm not
 // summing to n_tok) flags FS_EF_SHAPE and leaves zero tiles, so nothing is
 // written past the outputs.
+constexpr int kPrepThreads = 256;
+constexpr int kPrepRanks = (FS_MAX_RANKS + 1) / kPrepThreads;  // ranks per thread (+ W)
+constexpr int kMaxLenBlocks = FS_MAX_SAMPLES / kPrepThreads + 1;
+
 __global__ void __launch_bounds__(kPrepThreads)
-k_prep(const int64_t* __restrict__ so, int32_t n, int64_t n_tok, const int32_t* __restrict__ perm,
-       const int32_t* __restrict__ ro, int32_t W, int32_t T, int64_t* __restrict__ bal,
-       int64_t* __restrict__ shift, int32_t* __restrict__ tile_pref, TileDesc* __restrict__ tiles,
-       int32_t* __restrict__ err) {
+k_lens(const int64_t* __restrict__ so, int32_t n, int64_t n_tok, const int32_t* __restrict__ perm,
+       int32_t* __restrict__ lens, int32_t* __restrict__ begs, int64_t* __restrict__ bsum,
+       int32_t* __restrict__ flags) {
+  __shared__ int64_t tmp64[17];
+  const int32_t q = blockIdx.x * kPrepThreads + threadIdx.x;
+  bool bad = false;
+  int64_t len = 0;
+  if (q < n) {
+    const int32_t p = perm[q];
+    const bool pin = p >= 0 && p < n;
+    bad |= !pin;
+    const int64_t b0 = pin ? so[p] : 0, b1 = pin ? so[p + 1] : 0;
+    len = b1 - b0;
+    lens[q] = (int32_t)len;  // offsets fit 32 bits (T * n_tok < 2^31)
+    begs[q] = (int32_t)b0;
+  }
+  if (q <= n) {
+    const int64_t v = so[q];
+    if ((q == 0 && v != 0) || (q == n && v != n_tok) || (q < n && so[q + 1] < v)) bad = true;
+  }
+  int64_t tot;
+  (void)block_excl_scan<int64_t>(len, tmp64, &tot);
+  const int any = __syncthreads_or(bad ? 1 : 0);
+  if (threadIdx.x == 0) {
+    bsum[blockIdx.x] = tot;
+    flags[blockIdx.x] = any;
+  }
+}
+
+__global__ void __launch_bounds__(kPrepThreads)
+k_bal(int32_t n, const int32_t* __restrict__ lens, const int32_t* __restrict__ begs,
+      const int64_t* __restrict__ bsum, int64_t* __restrict__ bal, int64_t* __restrict__ shift) {
+  __shared__ int64_t tmp64[17];
+  __shared__ int64_t base_s;
+  const int32_t q = blockIdx.x * kPrepThreads + threadIdx.x;
+  const int32_t len = q < n ? lens[q] : 0;
+  const int32_t beg = q < n ? begs[q] : 0;
+  if (threadIdx.x < kWave) {  // sums of the earlier workgroups (at most 65)
+    int64_t x = 0;
+    for (int32_t k = threadIdx.x; k < (int32_t)blockIdx.x; k += kWave) x += bsum[k];
+    x = wave_sum(x);
+    if (threadIdx.x == 0) base_s = x;
+  }
+  int64_t tot;
+  const int64_t ex = block_excl_scan<int64_t>(len, tmp64, &tot);  // barriers publish base_s
+  if (q < n) {
+    const int64_t b = base_s + ex;
+    bal[q] = b;
+    shift[q] = (int64_t)beg - b;
+  }
+}
+
+__global__ void __launch_bounds__(kPrepThreads)
+k_tiles(int32_t n, int64_t n_tok, int32_t n_len_blocks, const int64_t* __restrict__ bsum,
+        const int32_t* __restrict__ flags, const int32_t* __restrict__ ro, int32_t W, int32_t T,
+        int64_t* __restrict__ bal, int32_t* __restrict__ tile_pref,
+        TileDesc* __restrict__ tiles, int32_t* __restrict__ err) {
   __shared__ int64_t tmp64[17];
   __shared__ int32_t tmp32[17];
-  __shared__ int bad_s;
-  if (threadIdx.x == 0) bad_s = 0;
   bool bad = false;
-  for (int32_t s0 = threadIdx.x; s0 <= n; s0 += kPrepThreads * kPrepUnroll) {
-#pragma unroll
-    for (int k = 0; k < kPrepUnroll; ++k) {
-      const int32_t s = s0 + k * kPrepThreads;
-      if (s <= n) {
-        const int64_t v = so[s];
-        if ((s == 0 && v != 0) || (s == n && v != n_tok) || (s < n && so[s + 1] < v)) bad = true;
-      }
-    }
-  }
-  // lengths of the thread's balanced samples, 16 at a time (perm loads, then
-  // offset loads, each batch in flight together; few registers, so that the
-  // workgroup fits beside another stream's kernels)
-  const int32_t q0 = threadIdx.x * kPrepPer;
-  int64_t local = 0;
-  for (int k0 = 0; k0 < kPrepPer; k0 += kPrepBatch) {
-    int32_t pp[kPrepBatch];
-#pragma unroll
-    for (int k = 0; k < kPrepBatch; ++k) pp[k] = q0 + k0 + k < n ? perm[q0 + k0 + k] : -1;
-#pragma unroll
-    for (int k = 0; k < kPrepBatch; ++k) {
-      const bool pin = pp[k] >= 0 && pp[k] < n;
-      if (q0 + k0 + k < n && !pin) bad = true;
-      if (pin) local += so[pp[k] + 1] - so[pp[k]];
-    }
+  int64_t part = 0;
+  for (int32_t k = threadIdx.x; k < n_len_blocks; k += kPrepThreads) {
+    bad |= flags[k] != 0;
+    part += bsum[k];
   }
   int32_t ro_v[kPrepRanks + 1];
 #pragma unroll
@@ -112,41 +146,17 @@ k_prep(const int64_t* __restrict__ so, int32_t n, int64_t n_tok, const int32_t* 
     ro_v[k] = r <= W ? ro[r] : n;
     if (r <= W && ((r == 0 && ro_v[k] != 0) || (r == W && ro_v[k] != n))) bad = true;
     if (k > 0 && r <= W && ro_v[k] < ro_v[k - 1]) bad = true;
+    if (r <= W && (ro_v[k] < 0 || ro_v[k] > n)) bad = true;
   }
-  __syncthreads();
-  if (bad) atomicOr(&bad_s, 1);
-  __syncthreads();
-  bool ok = bad_s == 0;
   int64_t total;
-  int64_t run = block_excl_scan<int64_t>(ok ? local : 0, tmp64, &total);
-  ok = ok && total == n_tok;  // perm repeats a sample: refuse before any tile exists
-  if (!ok && threadIdx.x == 0 && err) atomicOr(err, FS_EF_SHAPE);
-  if (ok) {
-    for (int k0 = 0; k0 < kPrepPer && q0 + k0 < n; k0 += kPrepBatch) {
-      int32_t pp[kPrepBatch];
-      int64_t b0[kPrepBatch], b1[kPrepBatch];
-#pragma unroll
-      for (int k = 0; k < kPrepBatch; ++k) pp[k] = q0 + k0 + k < n ? perm[q0 + k0 + k] : 0;
-#pragma unroll
-      for (int k = 0; k < kPrepBatch; ++k) {
-        b0[k] = so[pp[k]];
-        b1[k] = so[pp[k] + 1];
-      }
-#pragma unroll
-      for (int k = 0; k < kPrepBatch; ++k) {
-        const int32_t q = q0 + k0 + k;
-        if (q < n) {
-          bal[q] = run;
-          shift[q] = b0[k] - run;
-          run += b1[k] - b0[k];
-        }
-      }
-    }
+  (void)block_excl_scan<int64_t>(part, tmp64, &total);
+  const bool ok = !__syncthreads_or(bad ? 1 : 0) && total == n_tok;
+  if (threadIdx.x == 0) {
+    bal[n] = ok ? total : 0;
+    if (!ok && err) atomicOr(err, FS_EF_SHAPE);
   }
-  if (threadIdx.x == 0) bal[n] = ok ? total : 0;
-  __syncthreads();  // bal visible to the workgroup
-
-  // rank r owns T * ceil(m_r / kTile) tiles, t-major
+  // rank r owns T * ceil(m_r / kTile) tiles, t-major (bal[n] is read only
+  // through ranks that end at n, where it equals total)
   int64_t A[kPrepRanks], m[kPrepRanks];
   int32_t c[kPrepRanks];
   int32_t mine = 0;
@@ -157,8 +167,8 @@ k_prep(const int64_t* __restrict__ so, int32_t n, int64_t n_tok, const int32_t* 
     m[k] = 0;
     c[k] = 0;
     if (ok && r < W) {
-      A[k] = bal[ro_v[k]];
-      m[k] = bal[ro_v[k + 1]] - A[k];
+      A[k] = ro_v[k] < n ? bal[ro_v[k]] : total;
+      m[k] = (ro_v[k + 1] < n ? bal[ro_v[k + 1]] : total) - A[k];
       c[k] = (int32_t)cdiv(m[k], kTile);
     }
     mine += T * c[k];
@@ -213,9 +223,9 @@ __device__ __forceinline__ bool tile_info(int32_t tile, const int32_t* tile_pref
 // search, then loads a window of 64 samples: their end offsets and shifts
 // from batch-major to original token index. A lane finds its token's sample
 // in the window by binary lifting over the window with shuffles; the window
-// restarts at each round's first sample, and a lane whose token lies past
-// the window (only possible with runs of empty samples) walks forward on its
-// own. All 16 ID loads are independent.
+// restarts at a round's first sample only when the round reaches past it, and
+// a lane whose token still lies past the window (only possible with runs of
+// empty samples) walks forward on its own. All 16 ID loads are independent.
 struct Window {
   int32_t qa;     // first sample of the window
   int64_t bnd;    // this lane: end offset of sample qa + lane (INT64_MAX past q_hi)
@@ -259,9 +269,10 @@ __device__ __forceinline__ void wave_items(const TileInfo& ti, int32_t w, const 
 #pragma unroll
   for (int i = 0; i < kRounds; ++i) {
     const int64_t rb = first + i * kWave;  // the round's first token
-    if (rb < ti.bm_hi) {
-      // restart the window at the round's first sample (a round of 64
-      // tokens then spans at most the window, unless samples are empty)
+    if (rb < ti.bm_hi && __shfl(win.bnd, kWave - 1, kWave) <= rb + kWave - 1) {
+      // the round reaches past the window: restart it at the round's first
+      // sample (64 tokens then span at most the window, unless samples are
+      // empty)
       const int kf = popc(__ballot(win.bnd <= rb));
       if (kf > 0) win = load_window(win.qa + kf, ti.q_hi, bal, shift);
     }
@@ -331,61 +342,10 @@ k_hist(const int64_t* __restrict__ ids, int64_t n_tok, const int64_t* __restrict
   for (int b = threadIdx.x; b <= W; b += kThreads) counts[(int64_t)tile * ld + b] = h[b];
 }
 
-// ---------------------------------------------------------------- splits
-// Workgroup (x, y): ranks [64x, 64x + 64) x shards [64y, 64y + 64) of
-// splits[d][r] = (scanned count of shard d at rank r + 1's first tile) -
-// (at rank r's first tile); rows past the matrix read the column totals.
-// Workgroup (0, 0) also writes shard_offsets = exclusive scan of the totals
-// (entry W: the valid items; dropped IDs follow it).
-__global__ void __launch_bounds__(kThreads)
-k_splits(const uint32_t* __restrict__ counts, int32_t ld, int32_t G,
-         const int32_t* __restrict__ tile_pref, const uint32_t* __restrict__ tot, int32_t W,
-         int64_t* __restrict__ splits, int64_t* __restrict__ shard_offsets) {
-  __shared__ int64_t tr_[kWave][kWave + 1];
-  __shared__ int64_t tmp[17];
-  const int w = threadIdx.x / kWave, l = lane();
-  if (blockIdx.x == 0 && blockIdx.y == 0) {
-    constexpr int kPer = (FS_MAX_RANKS + 1 + kThreads - 1) / kThreads;
-    uint32_t v[kPer];
-    int64_t local = 0;
-#pragma unroll
-    for (int k = 0; k < kPer; ++k) {
-      const int b = threadIdx.x * kPer + k;
-      v[k] = b <= W ? tot[b] : 0u;
-      local += v[k];
-    }
-    int64_t all;
-    int64_t base = block_excl_scan<int64_t>(local, tmp, &all);
-#pragma unroll
-    for (int k = 0; k < kPer; ++k) {
-      const int b = threadIdx.x * kPer + k;
-      if (b <= W) shard_offsets[b] = base;
-      base += v[k];
-    }
-  }
-  const int32_t d = blockIdx.y * kWave + l;
-  for (int rl = w; rl < kWave; rl += kThreads / kWave) {
-    const int32_t r = blockIdx.x * kWave + rl;
-    int64_t val = 0;
-    if (r < W && d < W) {
-      const int32_t a = tile_pref[r], z = tile_pref[r + 1];
-      const uint32_t va = a < G ? counts[(int64_t)a * ld + d] : tot[d];
-      const uint32_t vz = z < G ? counts[(int64_t)z * ld + d] : tot[d];
-      val = (int64_t)vz - (int64_t)va;
-    }
-    tr_[rl][l] = val;
-  }
-  __syncthreads();
-  const int32_t r = blockIdx.x * kWave + l;
-  for (int dl = w; dl < kWave; dl += kThreads / kWave) {
-    const int32_t dd = blockIdx.y * kWave + dl;
-    if (r < W && dd < W) splits[(int64_t)dd * W + r] = tr_[l][dl];
-  }
-}
-
 // ---------------------------------------------------------------- scatter
-// Staging area of one tile: first the per-wave lane-mask tables of the
-// ranking, then the tile's items sorted by shard.
+// Staging area of one workgroup: for a tile first the per-wave lane-mask
+// tables of the ranking, then the tile's items sorted by shard; for a splits
+// workgroup a 64 x 64 transpose.
 union ScatterStage {
   uint64_t peers[kThreads / kWave][FS_MAX_RANKS + 1];
   struct {
@@ -393,26 +353,105 @@ union ScatterStage {
     int32_t bm[kTile];
     uint16_t bin[kTile];
   } s;
+  int64_t tr[kWave][kWave + 1];
 };
 
+constexpr int kBinPer = (FS_MAX_RANKS + 1 + kThreads - 1) / kThreads;
+
+// base[b] = exclusive scan of the bin totals (start of bin b in the output)
+__device__ __forceinline__ void bin_bases(const uint32_t* tot, int32_t W, int64_t* tmp,
+                                          int64_t (&base)[kBinPer]) {
+  uint32_t v[kBinPer];
+  int64_t local = 0;
+#pragma unroll
+  for (int k = 0; k < kBinPer; ++k) {
+    const int b = threadIdx.x * kBinPer + k;
+    v[k] = b <= W ? tot[b] : 0u;
+    local += v[k];
+  }
+  int64_t all;
+  int64_t x = block_excl_scan<int64_t>(local, tmp, &all);
+#pragma unroll
+  for (int k = 0; k < kBinPer; ++k) {
+    base[k] = x;
+    x += v[k];
+  }
+}
+
+// Splits workgroup (x, y): ranks [64x, 64x + 64) x shards [64y, 64y + 64) of
+// splits[d][r] = (scanned count of shard d at rank r + 1's first tile) -
+// (at rank r's first tile); rows past the matrix read the column totals.
+// Workgroup (0, 0) also writes shard_offsets (entry W: the valid items;
+// dropped IDs follow it).
+__device__ __forceinline__ void splits_part(int32_t x, int32_t y, const uint32_t* counts,
+                                            int32_t ld, int32_t G, const int32_t* tile_pref,
+                                            const uint32_t* tot, int32_t W, int64_t* splits,
+                                            int64_t* shard_offsets, int64_t (&tr)[kWave][kWave + 1],
+                                            int64_t* tmp) {
+  const int w = threadIdx.x / kWave, l = lane();
+  if (x == 0 && y == 0) {
+    int64_t base[kBinPer];
+    bin_bases(tot, W, tmp, base);
+#pragma unroll
+    for (int k = 0; k < kBinPer; ++k) {
+      const int b = threadIdx.x * kBinPer + k;
+      if (b <= W) shard_offsets[b] = base[k];
+    }
+  }
+  const int32_t d = y * kWave + l;
+  for (int rl = w; rl < kWave; rl += kThreads / kWave) {
+    const int32_t r = x * kWave + rl;
+    int64_t val = 0;
+    if (r < W && d < W) {
+      const int32_t a = tile_pref[r], z = tile_pref[r + 1];
+      const uint32_t va = a < G ? counts[(int64_t)a * ld + d] : tot[d];
+      const uint32_t vz = z < G ? counts[(int64_t)z * ld + d] : tot[d];
+      val = (int64_t)vz - (int64_t)va;
+    }
+    tr[rl][l] = val;
+  }
+  __syncthreads();
+  const int32_t r = x * kWave + l;
+  for (int dl = w; dl < kWave; dl += kThreads / kWave) {
+    const int32_t dd = y * kWave + dl;
+    if (r < W && dd < W) splits[(int64_t)dd * W + r] = tr[l][dl];
+  }
+}
+
+// Workgroups [0, G): tiles (XCD order); [G, G + splits workgroups): splits.
 __global__ void __launch_bounds__(kThreads)
 k_scatter(const uint32_t* __restrict__ ikey, int64_t n_tok, const int32_t* __restrict__ tile_pref,
           const TileDesc* __restrict__ tiles, TableRows tr, int32_t W, int32_t T, int32_t nbits,
-          const uint32_t* __restrict__ offs, int32_t ld, const int64_t* __restrict__ shard_offsets,
-          int64_t* __restrict__ shard_keys, int32_t* __restrict__ shard_bm) {
+          const uint32_t* __restrict__ offs, int32_t ld, int32_t G,
+          const uint32_t* __restrict__ tot, int64_t* __restrict__ splits,
+          int64_t* __restrict__ shard_offsets, int64_t* __restrict__ shard_keys,
+          int32_t* __restrict__ shard_bm) {
   __shared__ uint16_t cnt[kThreads / kWave][FS_MAX_RANKS + 1];
   __shared__ uint32_t run[FS_MAX_RANKS + 1];   // output position of each shard's run
   __shared__ uint32_t tbin[FS_MAX_RANKS + 1];  // start of each shard in the sorted tile
   __shared__ ScatterStage st;
   __shared__ int64_t tmp[17];
-  constexpr int kPer = (FS_MAX_RANKS + 1 + kThreads - 1) / kThreads;
-  const int32_t tile = xcd_tile(blockIdx.x, gridDim.x);
+  constexpr int kPer = kBinPer;
+  if ((int32_t)blockIdx.x >= G) {
+    const int32_t sb = blockIdx.x - G, nx = (int32_t)cdiv(W, kWave);
+    splits_part(sb % nx, sb / nx, offs, ld, G, tile_pref, tot, W, splits, shard_offsets, st.tr,
+                tmp);
+    return;
+  }
+  const int32_t tile = xcd_tile(blockIdx.x, G);
   TileInfo ti;
   if (!tile_info(tile, tile_pref, W, T, tiles, ti)) return;  // uniform per workgroup
   const int32_t nb = W + 1;
   const int32_t w = threadIdx.x / kWave;
-  for (int b = threadIdx.x; b < nb; b += kThreads)
-    run[b] = (uint32_t)(shard_offsets[b] + offs[(int64_t)tile * ld + b]);
+  {
+    int64_t base[kBinPer];
+    bin_bases(tot, W, tmp, base);
+#pragma unroll
+    for (int k = 0; k < kBinPer; ++k) {
+      const int b = threadIdx.x * kBinPer + k;
+      if (b < nb) run[b] = (uint32_t)(base[k] + offs[(int64_t)tile * ld + b]);
+    }
+  }
   for (int b = lane(); b < nb; b += kWave) {
     cnt[w][b] = 0;
     st.peers[w][b] = 0;
@@ -514,6 +553,10 @@ extern "C" size_t fs_bucketize_workspace_size(int64_t n_tok, int32_t n, int32_t 
   c.take<uint32_t>((size_t)(cdiv(G, kColBlockRows) * ld));  // column partials
   c.take<uint32_t>((size_t)ld);                             // column totals
   c.take<uint32_t>((size_t)(T * (n_tok > 0 ? n_tok : 1)));  // item keys, batch-major
+  c.take<int32_t>((size_t)(n > 0 ? n : 1));                 // lengths under perm
+  c.take<int32_t>((size_t)(n > 0 ? n : 1));                 // first tokens under perm
+  c.take<int64_t>((size_t)kMaxLenBlocks);                   // per-workgroup length sums
+  c.take<int32_t>((size_t)kMaxLenBlocks);                   // per-workgroup input flags
   return c.used + 256;
 }
 
@@ -553,23 +596,34 @@ extern "C" int fs_bucketize_permute(const int64_t* ids, int64_t n_tok,
   uint32_t* part = c.take<uint32_t>((size_t)cdiv(G, kColBlockRows) * ld);
   uint32_t* tot = c.take<uint32_t>((size_t)ld);
   uint32_t* ikey = c.take<uint32_t>((size_t)(T * (n_tok > 0 ? n_tok : 1)));
+  int32_t* lens = c.take<int32_t>((size_t)(n > 0 ? n : 1));
+  int32_t* begs = c.take<int32_t>((size_t)(n > 0 ? n : 1));
+  int64_t* bsum = c.take<int64_t>((size_t)kMaxLenBlocks);
+  int32_t* flags = c.take<int32_t>((size_t)kMaxLenBlocks);
   int nbits = 1;
   while ((1 << nbits) - 1 <= W) ++nbits;  // sentinel (2^nbits - 1) > W
-  const dim3 split_grid((unsigned)cdiv(W, kWave), (unsigned)cdiv(W, kWave));
+  const int32_t n_len_blocks = (int32_t)cdiv(n + 1, kPrepThreads);  // <= kMaxLenBlocks
+  const int32_t split_blocks = (int32_t)(cdiv(W, kWave) * cdiv(W, kWave));
 
-  hipLaunchKernelGGL(k_prep, dim3(1), dim3(kPrepThreads), 0, stream, sample_offsets, n, n_tok,
-                     perm, rank_offsets, W, T, bal_offsets, shift, tile_pref, tiles, err);
+  hipLaunchKernelGGL(k_lens, dim3(n_len_blocks), dim3(kPrepThreads), 0, stream, sample_offsets,
+                     n, n_tok, perm, lens, begs, bsum, flags);
+  FS_LAUNCH_CHECK();
+  if (n > 0) {
+    hipLaunchKernelGGL(k_bal, dim3((unsigned)cdiv(n, kPrepThreads)), dim3(kPrepThreads), 0,
+                       stream, n, lens, begs, bsum, bal_offsets, shift);
+    FS_LAUNCH_CHECK();
+  }
+  hipLaunchKernelGGL(k_tiles, dim3(1), dim3(kPrepThreads), 0, stream, n, n_tok, n_len_blocks, bsum,
+                     flags, rank_offsets, W, T, bal_offsets, tile_pref, tiles, err);
   FS_LAUNCH_CHECK();
   hipLaunchKernelGGL(k_hist, dim3(G), dim3(kThreads), 0, stream, ids, n_tok, shift, bal_offsets,
                      tile_pref, tiles, tr, W, T, nbits, counts, ld, ikey, err);
   FS_LAUNCH_CHECK();
   int rc = launch_colscan(counts, ld, G, W + 1, part, tot, stream);
   if (rc) return rc;
-  hipLaunchKernelGGL(k_splits, split_grid, dim3(kThreads), 0, stream, counts, ld, G, tile_pref,
-                     tot, W, splits, shard_offsets);
-  FS_LAUNCH_CHECK();
-  hipLaunchKernelGGL(k_scatter, dim3(G), dim3(kThreads), 0, stream, ikey, n_tok, tile_pref,
-                     tiles, tr, W, T, nbits, counts, ld, shard_offsets, shard_keys, shard_bm);
+  hipLaunchKernelGGL(k_scatter, dim3((unsigned)(G + split_blocks)), dim3(kThreads), 0, stream,
+                     ikey, n_tok, tile_pref, tiles, tr, W, T, nbits, counts, ld, G, tot, splits,
+                     shard_offsets, shard_keys, shard_bm);
   FS_LAUNCH_CHECK();
   return FS_OK;
 }
