@@ -92,8 +92,9 @@ def step_rowbase(w):
 
 
 def run_parity(k, balancer=None, iters=None, seed=None):
-    w = synth.workload(k, balancer)
-    seed = k if seed is None else seed
+    """k: a workload number, or a synth.Workload."""
+    w = k if isinstance(k, synth.Workload) else synth.workload(k, balancer)
+    seed = (k if isinstance(k, int) else 77) if seed is None else seed
     K = iters or w.iterations
     say("workload", k, w.name, w.balancer, "iterations", K)
     bt = synth.Batches(w, seed)
@@ -170,6 +171,23 @@ def test_workload4_vbs_four_tables():
 @pytest.mark.parametrize("bal", ["fbs", "vbs"])
 def test_workload5_full_size(bal):
     run_parity(5, balancer=bal, iters=2)
+
+
+# The call limits at once: 16384 samples, 1024 ranks, 8 tables of every row
+# width the update takes (64 .. 1024 columns, fp32 and bf16, the widest at the
+# lookup's 2 KB row limit) and a table of 1500 rows, two per shard.
+LIMITS = synth.Workload(
+    "B16384-W1024-8tables-limits", 16384, 1024,
+    (synth.TableSpec(5_000_000, 64, "f32", 1.05), synth.TableSpec(2_000_000, 128, "bf16", 1.1),
+     synth.TableSpec(1_000_000, 256, "f32", 1.0), synth.TableSpec(500_000, 512, "bf16", 1.2),
+     synth.TableSpec(100_000, 64, "f32", 1.05), synth.TableSpec(20_000, 128, "f32", 1.1),
+     synth.TableSpec(200_000, 1024, "bf16", 1.05), synth.TableSpec(1500, 64, "bf16", 1.3)),
+    "rw_adagrad", 0.05, 1e-8, "vbs", (3, 2), 2, ("lognormal", 2.0, 0.8), 64, 4)
+
+
+@pytest.mark.timeout(900)
+def test_call_limits_full_step():
+    run_parity(LIMITS)
 
 
 @pytest.mark.parametrize("k", [2, 3])
