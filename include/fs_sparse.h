@@ -148,8 +148,12 @@ size_t fs_balance_workspace_size(int32_t n, int32_t W);
 /*                 unspecified.                                               */
 /*  splits         [W*W] int64: splits[d*W + r] = items rank r sends to d.    */
 /*  shard_offsets  [W+1] int64: shard d's items are [so_d, so_{d+1}).        */
-/*  err            IDs outside [0, rows_t) are dropped (FS_EF_ID_RANGE); a   */
-/*                 bad so[n] flags FS_EF_SHAPE and the output is undefined.  */
+/*  err            IDs outside [0, rows_t) are dropped (FS_EF_ID_RANGE).     */
+/*                 Sample offsets not rising from 0 to n_tok, a perm entry   */
+/*                 outside [0, n), rank offsets not rising from 0 to n, or   */
+/*                 lengths under perm not summing to n_tok flag FS_EF_SHAPE: */
+/*                 then no item is written, shard_offsets and splits are     */
+/*                 all zero and bal_offsets is unspecified.                  */
 int fs_bucketize_permute(const int64_t* ids, int64_t n_tok, const int64_t* sample_offsets,
                          int32_t n, const fs_table* tables, int32_t T, const int32_t* perm,
                          const int32_t* rank_offsets, int32_t W, int64_t* bal_offsets,
@@ -165,7 +169,12 @@ size_t fs_bucketize_workspace_size(int64_t n_tok, int32_t n, int32_t T, int32_t 
 /* collides when iteration i updates it; only those rows need the write-    */
 /* then-read order, every other (exclusive) row can be fetched ahead.       */
 /*                                                                          */
-/*  shard_keys, shard_bm, shard_offsets: a bucketize call's output.          */
+/*  shard_keys, shard_bm, shard_offsets: a bucketize call's output (items   */
+/*                 of shard d in [so_d, so_{d+1}), each a row of shard d).   */
+/*                 Offsets are clamped into [0, n_cap] and made rising, and  */
+/*                 a key outside its range's shard is clamped into it: such  */
+/*                 input gives unspecified results but writes nothing past    */
+/*                 the outputs.                                               */
 /*  n_cap          host: capacity of the shard arrays (T*n_tok).             */
 /*  prev_unique, prev_counts: the previous call's unique and counts (device), */
 /*                 or both NULL for the first iteration (all rows exclusive). */
