@@ -29,6 +29,9 @@ constexpr int kThreads = 256;
 constexpr int kLong = 4;      // longer segments take the chunked path
 constexpr int kChunk = 512;   // occurrences per long-path chunk (one wave)
 constexpr int kShortBlocks = 4096;
+// waves of the short-row kernel the GPU holds at once (256 CUs x 4 SIMDs x
+// 5 waves of ~90 registers); the unit size aims at two or more units each
+constexpr int64_t kResident = 256 * 4 * 5;
 
 struct RUArgs {
   void* weights;
@@ -181,11 +184,14 @@ __device__ __forceinline__ void update_row(const RUArgs& a, int64_t u, int sub,
 }
 
 // ---------------------------------------------------------------- short rows
-// Grid-stride over the table's unique rows, 64 per wave. The wave loads the
-// rows' CSR bounds, keys, classes, first occurrence and Adagrad state with one
-// coalesced or gathered load each; lane groups then take the rows in turn, R
-// at a time, fetch their metadata by shuffle and keep R weight rows and R
-// gradient rows in flight.
+// Grid-stride over the table's unique rows in units of `unit` rows per wave.
+// The wave loads the unit's CSR bounds, keys, classes and Adagrad state with
+// one coalesced or gathered load each; lane groups then take the rows in
+// turn, R at a time, fetch their metadata by shuffle and keep R weight rows
+// and R gradient rows in flight. The unit is 64 rows when the table has
+// enough rows to give every wave of the grid several units, and shrinks to
+// 32 or 16 otherwise, so that small batches spread over more waves and each
+// wave's chain of dependent rounds stays short.
 template <int D, typename WT>
 __global__ void __launch_bounds__(kThreads) k_short(RUArgs a) {
   using M = Map<D>;
@@ -198,9 +204,12 @@ __global__ void __launch_bounds__(kThreads) k_short(RUArgs a) {
   const bool ada = a.optim == FS_RW_ADAGRAD;
   const int64_t wid = (int64_t)blockIdx.x * (kThreads / kWave) + threadIdx.x / kWave;
   const int64_t nwaves = (int64_t)gridDim.x * (kThreads / kWave);
-  for (int64_t ub = u_lo + wid * kWave; ub < u_hi; ub += nwaves * kWave) {
+  const int64_t n_rows = u_hi - u_lo;
+  const int unit = n_rows >= 2 * kWave * kResident ? kWave
+                   : (n_rows >= 2 * 32 * kResident ? 32 : 16);
+  for (int64_t ub = u_lo + wid * unit; ub < u_hi; ub += nwaves * unit) {
     const int64_t uu = ub + l;
-    const bool in = uu < u_hi;
+    const bool in = l < unit && uu < u_hi;
     const int32_t lo = in ? a.seg_offsets[uu] : 0;
     const int32_t hi = in ? a.seg_offsets[uu + 1] : 0;
     const bool act = in && (hi - lo) <= kLong && class_ok(a, uu);
@@ -209,7 +218,7 @@ __global__ void __launch_bounds__(kThreads) k_short(RUArgs a) {
     const uint32_t row = act ? (uint32_t)(a.unique[uu] - a.row_base) : 0u;
     const float st = (act && ada) ? a.state[row] : 0.f;
 #pragma unroll 1
-    for (int j0 = 0; j0 < kWave; j0 += PER) {
+    for (int j0 = 0; j0 < unit; j0 += PER) {
       const uint64_t win = (PER >= kWave) ? ~0ull : (((1ull << PER) - 1ull) << j0);
       if (!(actm & win)) continue;
       int32_t jlo[R], jhi[R];
@@ -360,10 +369,17 @@ __global__ void __launch_bounds__(kThreads) k_long(RUArgs a) {
 // ---------------------------------------------------------------- fix-up
 // Chunk c owns the long row that starts in it and runs past its end: sum the
 // row's partials (slot 1 of c, slot 0 of each later chunk it covers), four
-// waves in contiguous slices, combined in wave order.
+// waves in contiguous slices with E partials in flight per lane group,
+// combined in wave order.
+template <int D>
+struct FixShape {
+  static constexpr int E = D >= 1024 ? 1 : (D >= 512 ? 2 : 4);
+};
+
 template <int D, typename WT>
 __global__ void __launch_bounds__(kThreads) k_fix(RUArgs a) {
   using M = Map<D>;
+  constexpr int E = FixShape<D>::E;
   __shared__ double part[kThreads / kWave][D];
   const int64_t o_lo = a.seg_offsets[a.unique_offsets[a.g_lo]];
   const int64_t o_hi = a.seg_offsets[a.unique_offsets[a.g_hi]];
@@ -384,12 +400,24 @@ __global__ void __launch_bounds__(kThreads) k_fix(RUArgs a) {
   double acc[M::CPL];
 #pragma unroll
   for (int x = 0; x < M::CPL; ++x) acc[x] = 0.0;
-  for (int64_t k = k0 + grp; k < k1; k += M::GPW) {
-    const double* p = a.partials + ((c + k) * 2 + (k == 0 ? 1 : 0)) * D;
+  for (int64_t kb = k0; kb < k1; kb += E * M::GPW) {
+    double pv[E][M::CPL];
 #pragma unroll
-    for (int v = 0; v < M::NV; ++v)
+    for (int e = 0; e < E; ++e) {
+      const int64_t k = kb + e * M::GPW + grp;
+      if (k < k1) {
+        const double* p = a.partials + ((c + k) * 2 + (k == 0 ? 1 : 0)) * D;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc[4 * v + e] += p[M::col(sub, v) + e];
+        for (int v = 0; v < M::NV; ++v)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) pv[e][4 * v + q] = p[M::col(sub, v) + q];
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      if (kb + e * M::GPW + grp < k1)
+#pragma unroll
+        for (int x = 0; x < M::CPL; ++x) acc[x] += pv[e][x];
   }
 #pragma unroll
   for (int off = M::LPG; off < kWave; off <<= 1)
@@ -399,7 +427,7 @@ __global__ void __launch_bounds__(kThreads) k_fix(RUArgs a) {
 #pragma unroll
     for (int v = 0; v < M::NV; ++v)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) part[w][M::col(sub, v) + e] = acc[4 * v + e];
+      for (int q = 0; q < 4; ++q) part[w][M::col(sub, v) + q] = acc[4 * v + q];
   }
   __syncthreads();
   if (w == 0) {
@@ -409,7 +437,7 @@ __global__ void __launch_bounds__(kThreads) k_fix(RUArgs a) {
 #pragma unroll
       for (int v = 0; v < M::NV; ++v)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc[4 * v + e] += part[ww][M::col(sub, v) + e];
+        for (int q = 0; q < 4; ++q) acc[4 * v + q] += part[ww][M::col(sub, v) + q];
     update_row<D, WT>(a, u, sub, acc, grp == 0);
   }
 }
