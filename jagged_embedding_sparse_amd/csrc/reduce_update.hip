@@ -13,7 +13,9 @@
 //   short rows (<= kLong = 4 occurrences, most rows): one lane group per row,
 //     grid-stride over the table's unique rows; all of a row's loads are in
 //     flight at once, then the group sums and updates the row.
-//   long rows: the table's occurrence range is cut into chunks of kChunk;
+//   long rows: the table's occurrence range is cut into chunks (128 to 512
+//     occurrences, smaller for smaller batches so that the grid still has
+//     about two chunks per resident wave);
 //     a wave streams each long row's piece of its chunk (all lane groups of
 //     the wave interleaved), updates rows that lie inside the chunk and
 //     leaves fp64 partials for the rest; a fix-up sums each row's partials
@@ -27,7 +29,12 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kLong = 4;      // longer segments take the chunked path
-constexpr int kChunk = 512;   // occurrences per long-path chunk (one wave)
+// occurrences per long-path chunk (one wave): the largest of 512, 256, 128
+// that leaves about two chunks per resident wave (5 per SIMD)
+inline int64_t chunk_for(int64_t n_tok) {
+  const int64_t target = 2 * 256 * 4 * 5;
+  return n_tok >= 512 * target ? 512 : (n_tok >= 256 * target ? 256 : 128);
+}
 constexpr int kShortBlocks = 4096;
 // waves of the short-row kernel the GPU holds at once (256 CUs x 4 SIMDs x
 // 5 waves of ~90 registers); the unit size aims at two or more units each
@@ -45,6 +52,7 @@ struct RUArgs {
   const int32_t* occ_uid;
   const uint8_t* cls;
   double* partials;  // [chunks][2][D]
+  int64_t chunk;     // occurrences per long-path chunk
   int64_t row_base;
   int64_t n_cap;  // occurrences this table can have
   int32_t g_lo, g_hi;
@@ -287,9 +295,9 @@ __global__ void __launch_bounds__(kThreads) k_long(RUArgs a) {
   const int64_t o_lo = a.seg_offsets[a.unique_offsets[a.g_lo]];
   const int64_t o_hi = a.seg_offsets[a.unique_offsets[a.g_hi]];
   const int64_t c = (int64_t)blockIdx.x * (kThreads / kWave) + threadIdx.x / kWave;
-  const int64_t cb = o_lo + c * kChunk;
+  const int64_t cb = o_lo + c * a.chunk;
   if (cb >= o_hi) return;
-  const int64_t ce = min(cb + (int64_t)kChunk, o_hi);
+  const int64_t ce = min(cb + a.chunk, o_hi);
   const int grp = lane() / M::LPG, sub = lane() % M::LPG;
   const int32_t u_first = a.occ_uid[cb], u_last = a.occ_uid[ce - 1];
   for (int32_t ub = u_first; ub <= u_last; ub += kWave) {
@@ -384,13 +392,13 @@ __global__ void __launch_bounds__(kThreads) k_fix(RUArgs a) {
   const int64_t o_lo = a.seg_offsets[a.unique_offsets[a.g_lo]];
   const int64_t o_hi = a.seg_offsets[a.unique_offsets[a.g_hi]];
   const int64_t c = blockIdx.x;
-  const int64_t cb = o_lo + c * kChunk;
+  const int64_t cb = o_lo + c * a.chunk;
   if (cb >= o_hi) return;
-  const int64_t ce = min(cb + (int64_t)kChunk, o_hi);
+  const int64_t ce = min(cb + a.chunk, o_hi);
   const int64_t u = a.occ_uid[ce - 1];
   const int64_t s_lo = a.seg_offsets[u], s_hi = a.seg_offsets[u + 1];
   if (!(s_hi - s_lo > kLong && s_lo >= cb && s_hi > ce && class_ok(a, u))) return;
-  const int64_t c_last = (s_hi - 1 - o_lo) / kChunk;  // slot 0 of chunks c+1..c_last
+  const int64_t c_last = (s_hi - 1 - o_lo) / a.chunk;  // slot 0 of chunks c+1..c_last
   const int64_t n_parts = 1 + (c_last - c);
   const int w = threadIdx.x / kWave;
   const int grp = lane() / M::LPG, sub = lane() % M::LPG;
@@ -449,7 +457,7 @@ int launch_all(const RUArgs& a, hipStream_t stream) {
   if (sb < 1) sb = 1;
   hipLaunchKernelGGL((k_short<D, WT>), dim3((unsigned)sb), dim3(kThreads), 0, stream, a);
   FS_LAUNCH_CHECK();
-  const int64_t chunks = cdiv(a.n_cap, kChunk);
+  const int64_t chunks = cdiv(a.n_cap, a.chunk);
   if (chunks > 0) {
     hipLaunchKernelGGL((k_long<D, WT>), dim3((unsigned)cdiv(chunks, kThreads / kWave)),
                        dim3(kThreads), 0, stream, a);
@@ -481,7 +489,8 @@ using namespace fs;
 
 extern "C" size_t fs_grad_reduce_update_workspace_size(int64_t n_tok, int32_t max_dim) {
   Carve c(nullptr);
-  c.take<double>((size_t)(cdiv(n_tok > 0 ? n_tok : 1, kChunk) * 2) * (size_t)max_dim);
+  const int64_t n = n_tok > 0 ? n_tok : 1;
+  c.take<double>((size_t)(cdiv(n, chunk_for(n)) * 2) * (size_t)max_dim);
   return c.used + 256;
 }
 
@@ -529,6 +538,7 @@ extern "C" int fs_grad_reduce_update(const fs_table* tables, int32_t T, int32_t 
     a.occ_uid = occ_uid;
     a.cls = cls;
     a.partials = (double*)ws;
+    a.chunk = chunk_for(n_tok > 0 ? n_tok : 1);
     a.row_base = base;
     a.n_cap = n_tok;
     a.g_lo = t * W;
