@@ -99,6 +99,9 @@ typedef struct fs_table {
 /*               samples are perm[rank_offsets[r] .. rank_offsets[r+1]).      */
 /*  rank_offsets [W+1] int32 out.                                            */
 /*  err          sticky flags (may be NULL: faults then go unreported).      */
+/*  ws, ws_bytes workspace of at least fs_balance_workspace_size(n, W) bytes */
+/*               (else FS_ERR_WORKSPACE): per-slice sort counts, and VBS's    */
+/*               weights and prefix sums.                                    */
 /* n in [0, FS_MAX_SAMPLES], W in [1, FS_MAX_RANKS].                         */
 
 /* FBS: zig-zag (snake) deal of the sorted samples. [FS] 4.1 prints rank i's */

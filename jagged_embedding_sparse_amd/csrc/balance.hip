@@ -9,19 +9,22 @@
 //
 // Sort: the batch is small (n <= 16384) and every key (length, index) is
 // distinct, so the sorted position of sample s is the number of keys below
-// its own. One lane per sample counts over a slice of the batch, a workgroup
-// sums the 4 slices: O(n^2 / 64) wave instructions spread over n/64
-// workgroups, no passes, no atomics, stable by construction.
+// its own. Workgroup (x, y) takes samples 64x .. 64x + 63 and slice y of Q
+// slices of the comparands, one lane per sample and a quarter slice per
+// wave, and stores the slice's count; a second launch sums the Q counts of
+// each sample and places it. O(n^2 / 64) wave instructions over about 512
+// workgroups, no atomics, stable by construction.
 #include "common.hpp"
 
 namespace fs {
 namespace {
 
-// 4 waves, one comparand slice each. Workgroups of the index path stay at 256
+// 4 waves, a quarter of the comparand slice each. Workgroups of the index path stay at 256
 // threads: a larger one needs that many free wave slots on one CU at once,
 // which it does not get while bandwidth-bound kernels of another stream keep
 // refilling every slot they free.
 constexpr int kRankThreads = 256;
+constexpr int kMaxSlices = 16;
 
 __device__ __forceinline__ uint32_t clamp_len(int32_t L) {
   return (uint32_t)(L < 0 ? 0 : (L > FS_MAX_UIH ? FS_MAX_UIH : L));
@@ -61,24 +64,31 @@ __device__ __forceinline__ int32_t fbs_rank_start(int32_t r, int32_t n, int32_t 
   return r * F + extra;
 }
 
-template <bool kFbs>
+// comparand slices per sample block: about 512 workgroups in all
+inline int32_t rank_slices(int32_t n) {
+  const int32_t xb = (int32_t)cdiv(n > 0 ? n : 1, kWave);
+  const int32_t q = 512 / xb;
+  return q < 1 ? 1 : (q > kMaxSlices ? kMaxSlices : q);
+}
+
+// cnt[y * n + s] = keys below sample s's among comparand slice y.
 __global__ void __launch_bounds__(kRankThreads)
-k_sort_place(const int32_t* __restrict__ len, int32_t n, int32_t W, int32_t* __restrict__ perm,
-             int32_t* __restrict__ rank_offsets, int64_t* __restrict__ wsorted, int anum,
-             int aden, int32_t* __restrict__ err) {
+k_rank_part(const int32_t* __restrict__ len, int32_t n, int32_t* __restrict__ cnt,
+            int32_t* __restrict__ err) {
   __shared__ int32_t part[kRankThreads / kWave][kWave];
   const int w = threadIdx.x / kWave, l = lane();
   const int nw = kRankThreads / kWave;
   const int32_t s = blockIdx.x * kWave + l;
   const bool valid = s < n;
   const int32_t Ls = valid ? len[s] : 0;
-  if (w == 0) flag_err(err, valid && (Ls < 0 || Ls > FS_MAX_UIH), FS_EF_LEN_RANGE);
+  if (blockIdx.y == 0 && w == 0)
+    flag_err(err, valid && (Ls < 0 || Ls > FS_MAX_UIH), FS_EF_LEN_RANGE);
   const uint64_t mine = sort_key(Ls, s);
-
-  // this wave's slice of comparands, 64 per coalesced load, broadcast lane
-  // by lane with readlane (uniform operands for the 64-bit compares)
-  const int32_t chunk = ((n + nw - 1) / nw + kWave - 1) / kWave * kWave;
-  const int32_t c0 = w * chunk, c1 = min(n, c0 + chunk);
+  // slice y of the comparands, a quarter per wave, in whole 64-key loads
+  // broadcast lane by lane with readlane (uniform operands for the compares)
+  const int32_t q = gridDim.y;
+  const int32_t chunk = (int32_t)cdiv(cdiv(n, (int64_t)q * nw), kWave) * kWave;
+  const int32_t c0 = min(n, ((int32_t)blockIdx.y * nw + w) * chunk), c1 = min(n, c0 + chunk);
   int32_t below = 0;
   for (int32_t cb = c0; cb < c1; cb += kWave) {
     const int32_t c = cb + l;
@@ -92,17 +102,32 @@ k_sort_place(const int32_t* __restrict__ len, int32_t n, int32_t W, int32_t* __r
   }
   part[w][l] = below;
   __syncthreads();
-
   if (w == 0 && valid) {
     int32_t p = 0;
     for (int k = 0; k < nw; ++k) p += part[k][l];
+    cnt[(int64_t)blockIdx.y * n + s] = p;
+  }
+}
+
+// Sorted position p of sample s = its Q counts summed; FBS deals p to its
+// rank, VBS stores s at p with its weight. With FBS, the first workgroup also
+// writes rank_offsets (also for an empty batch).
+template <bool kFbs>
+__global__ void __launch_bounds__(kRankThreads)
+k_place(const int32_t* __restrict__ len, int32_t n, int32_t W, int32_t q,
+        const int32_t* __restrict__ cnt, int32_t* __restrict__ perm,
+        int32_t* __restrict__ rank_offsets, int64_t* __restrict__ wsorted, int anum, int aden) {
+  const int32_t s = blockIdx.x * kRankThreads + threadIdx.x;
+  if (s < n) {
+    int32_t p = 0;
+    for (int32_t y = 0; y < q; ++y) p += cnt[(int64_t)y * n + s];
     if (kFbs) {
       int32_t round = p / W, off = p % W;
       int32_t r = (round % 2 == 0) ? off : (W - 1 - off);
       perm[fbs_rank_start(r, n, W) + round] = s;
     } else {
       perm[p] = s;
-      wsorted[p] = vbs_weight(clamp_len(Ls), anum, aden);
+      wsorted[p] = vbs_weight(clamp_len(len[s]), anum, aden);
     }
   }
   if (kFbs && blockIdx.x == 0)
@@ -161,25 +186,47 @@ using namespace fs;
 
 extern "C" size_t fs_balance_workspace_size(int32_t n, int32_t W) {
   (void)W;
+  const size_t m = (size_t)(n > 0 ? n : 1);
   Carve c(nullptr);
-  c.take<int64_t>((size_t)(n > 0 ? n : 1));      // sorted weights
-  c.take<int64_t>((size_t)(n > 0 ? n : 1) + 1);  // prefix sums
+  c.take<int64_t>(m);                             // sorted weights
+  c.take<int64_t>(m + 1);                         // prefix sums
+  c.take<int32_t>(m * (size_t)rank_slices(n));    // per-slice counts
   return c.used + 256;
 }
+
+namespace {
+// both partitions: per-slice counts, then placement
+template <bool kFbs>
+int launch_sort(const int32_t* uih_len, int32_t n, int32_t W, int32_t* perm,
+                int32_t* rank_offsets, int64_t* wsorted, int anum, int aden, int32_t* cnt,
+                int32_t* err, hipStream_t stream) {
+  const int32_t q = rank_slices(n);
+  if (n > 0) {
+    hipLaunchKernelGGL(k_rank_part, dim3((unsigned)cdiv(n, kWave), (unsigned)q),
+                       dim3(kRankThreads), 0, stream, uih_len, n, cnt, err);
+    FS_LAUNCH_CHECK();
+  }
+  if (n > 0 || kFbs) {
+    const int blocks = n > 0 ? (int)cdiv(n, kRankThreads) : 1;
+    hipLaunchKernelGGL(k_place<kFbs>, dim3(blocks), dim3(kRankThreads), 0, stream, uih_len, n, W,
+                       q, cnt, perm, rank_offsets, wsorted, anum, aden);
+    FS_LAUNCH_CHECK();
+  }
+  return FS_OK;
+}
+}  // namespace
 
 extern "C" int fs_balance_fbs(const int32_t* uih_len, int32_t n, int32_t W, int32_t* perm,
                               int32_t* rank_offsets, int32_t* err, void* ws, size_t ws_bytes,
                               hipStream_t stream) {
-  (void)ws;
-  (void)ws_bytes;
   int rc = check_common(uih_len, n, W, perm, rank_offsets);
   if (rc) return rc;
-  int blocks = (int)cdiv(n, kWave);
-  if (blocks == 0) blocks = 1;  // still writes rank_offsets
-  hipLaunchKernelGGL(k_sort_place<true>, dim3(blocks), dim3(kRankThreads), 0, stream, uih_len, n,
-                     W, perm, rank_offsets, (int64_t*)nullptr, 0, 1, err);
-  FS_LAUNCH_CHECK();
-  return FS_OK;
+  if (!ws || ws_bytes < fs_balance_workspace_size(n, W)) return FS_ERR_WORKSPACE;
+  Carve c(ws);
+  c.take<int64_t>((size_t)(n > 0 ? n : 1));
+  c.take<int64_t>((size_t)(n > 0 ? n : 1) + 1);
+  int32_t* cnt = c.take<int32_t>((size_t)(n > 0 ? n : 1) * (size_t)rank_slices(n));
+  return launch_sort<true>(uih_len, n, W, perm, rank_offsets, nullptr, 0, 1, cnt, err, stream);
 }
 
 extern "C" int fs_balance_vbs(const int32_t* uih_len, int32_t n, int32_t W, int32_t alpha_num,
@@ -195,12 +242,10 @@ extern "C" int fs_balance_vbs(const int32_t* uih_len, int32_t n, int32_t W, int3
   Carve c(ws);
   int64_t* wsorted = c.take<int64_t>((size_t)(n > 0 ? n : 1));
   int64_t* S = c.take<int64_t>((size_t)(n > 0 ? n : 1) + 1);
-  if (n > 0) {
-    hipLaunchKernelGGL(k_sort_place<false>, dim3((int)cdiv(n, kWave)), dim3(kRankThreads), 0,
-                       stream, uih_len, n, W, perm, rank_offsets, wsorted, alpha_num, alpha_den,
-                       err);
-    FS_LAUNCH_CHECK();
-  }
+  int32_t* cnt = c.take<int32_t>((size_t)(n > 0 ? n : 1) * (size_t)rank_slices(n));
+  rc = launch_sort<false>(uih_len, n, W, perm, rank_offsets, wsorted, alpha_num, alpha_den, cnt,
+                          err, stream);
+  if (rc) return rc;
   hipLaunchKernelGGL(k_vbs_cut, dim3(1), dim3(kCutThreads), 0, stream, wsorted, n, W, S,
                      rank_offsets, rank_weight);
   FS_LAUNCH_CHECK();

@@ -36,6 +36,7 @@ inline int64_t chunk_for(int64_t n_tok) {
   return n_tok >= 512 * target ? 512 : (n_tok >= 256 * target ? 256 : 128);
 }
 constexpr int kShortBlocks = 4096;
+constexpr int64_t kUpdateCap = 0;  // workgroups per update kernel (0: no cap)
 // waves of the short-row kernel the GPU holds at once (256 CUs x 4 SIMDs x
 // 5 waves of ~90 registers); the unit size aims at two or more units each
 constexpr int64_t kResident = 256 * 4 * 5;
@@ -290,13 +291,10 @@ __global__ void __launch_bounds__(kThreads) k_short(RUArgs a) {
 
 // ---------------------------------------------------------------- long rows
 template <int D, typename WT>
-__global__ void __launch_bounds__(kThreads) k_long(RUArgs a) {
+__device__ __forceinline__ void long_chunk(const RUArgs& a, int64_t o_lo, int64_t o_hi,
+                                           int64_t c) {
   using M = Map<D>;
-  const int64_t o_lo = a.seg_offsets[a.unique_offsets[a.g_lo]];
-  const int64_t o_hi = a.seg_offsets[a.unique_offsets[a.g_hi]];
-  const int64_t c = (int64_t)blockIdx.x * (kThreads / kWave) + threadIdx.x / kWave;
   const int64_t cb = o_lo + c * a.chunk;
-  if (cb >= o_hi) return;
   const int64_t ce = min(cb + a.chunk, o_hi);
   const int grp = lane() / M::LPG, sub = lane() % M::LPG;
   const int32_t u_first = a.occ_uid[cb], u_last = a.occ_uid[ce - 1];
@@ -372,6 +370,17 @@ __global__ void __launch_bounds__(kThreads) k_long(RUArgs a) {
       }
     }
   }
+}
+
+// Chunks in grid-stride order, one per wave at a time.
+template <int D, typename WT>
+__global__ void __launch_bounds__(kThreads) k_long(RUArgs a) {
+  const int64_t o_lo = a.seg_offsets[a.unique_offsets[a.g_lo]];
+  const int64_t o_hi = a.seg_offsets[a.unique_offsets[a.g_hi]];
+  const int64_t nwaves = (int64_t)gridDim.x * (kThreads / kWave);
+  for (int64_t c = (int64_t)blockIdx.x * (kThreads / kWave) + threadIdx.x / kWave;
+       o_lo + c * a.chunk < o_hi; c += nwaves)
+    long_chunk<D, WT>(a, o_lo, o_hi, c);
 }
 
 // ---------------------------------------------------------------- fix-up
@@ -454,13 +463,15 @@ template <int D, typename WT>
 int launch_all(const RUArgs& a, hipStream_t stream) {
   int64_t sb = cdiv(a.n_cap, kThreads);  // 64 rows per wave, 4 waves per block
   if (sb > kShortBlocks) sb = kShortBlocks;
+  if (kUpdateCap > 0 && sb > kUpdateCap) sb = kUpdateCap;
   if (sb < 1) sb = 1;
   hipLaunchKernelGGL((k_short<D, WT>), dim3((unsigned)sb), dim3(kThreads), 0, stream, a);
   FS_LAUNCH_CHECK();
   const int64_t chunks = cdiv(a.n_cap, a.chunk);
   if (chunks > 0) {
-    hipLaunchKernelGGL((k_long<D, WT>), dim3((unsigned)cdiv(chunks, kThreads / kWave)),
-                       dim3(kThreads), 0, stream, a);
+    int64_t lb = cdiv(chunks, kThreads / kWave);
+    if (kUpdateCap > 0 && lb > kUpdateCap) lb = kUpdateCap;
+    hipLaunchKernelGGL((k_long<D, WT>), dim3((unsigned)lb), dim3(kThreads), 0, stream, a);
     FS_LAUNCH_CHECK();
     hipLaunchKernelGGL((k_fix<D, WT>), dim3((unsigned)chunks), dim3(kThreads), 0, stream, a);
     FS_LAUNCH_CHECK();

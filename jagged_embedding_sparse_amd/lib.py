@@ -154,8 +154,9 @@ def fs_balance_fbs(uih_len, W, perm=None, rank_offsets=None, err=None, ws=None, 
     perm = perm if perm is not None else torch.empty(n, dtype=torch.int32, device=_dev())
     ro = rank_offsets if rank_offsets is not None else torch.empty(W + 1, dtype=torch.int32,
                                                                    device=_dev())
+    ws = _ws(balance_workspace_size(n, W), ws)
     _check("fs_balance_fbs", _c_balance_fbs(_ptr(uih_len), n, W, _ptr(perm), _ptr(ro), _ptr(err),
-                                            None, 0, _stream(stream)))
+                                            _ptr(ws), ws.numel(), _stream(stream)))
     return perm, ro
 
 

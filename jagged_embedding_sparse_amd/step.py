@@ -180,7 +180,7 @@ class SparseStep:
         with self._t("balance", stream):
             if self.w.balancer == "fbs":
                 lib.fs_balance_fbs(batch["uih_len"], W, st.perm, st.rank_offsets, err=self.err,
-                                   stream=stream)
+                                   ws=self.ws_bal, stream=stream)
             else:
                 lib.fs_balance_vbs(batch["uih_len"], W, self.w.alpha, st.perm, st.rank_offsets,
                                    st.rank_weight, err=self.err, ws=self.ws_bal, stream=stream)

@@ -66,6 +66,9 @@ def test_balance_rejects(L):
     assert f(FAKE, 10, L.FS_MAX_RANKS + 1, FAKE, FAKE, None, None, 0, None) == L.FS_ERR_INVALID_ARG
     assert f(FAKE, L.FS_MAX_SAMPLES + 1, 4, FAKE, FAKE, None, None, 0, None) == \
         L.FS_ERR_INVALID_ARG
+    # the sort's per-slice counts need the workspace
+    assert f(FAKE, 10, 4, FAKE, FAKE, None, None, 0, None) == L.FS_ERR_WORKSPACE
+    assert f(FAKE, 10, 4, FAKE, FAKE, None, FAKE, 8, None) == L.FS_ERR_WORKSPACE
     v = L._c_balance_vbs
     assert v(FAKE, 10, 4, 1, 3, FAKE, FAKE, None, None, FAKE, 1 << 20, None) == \
         L.FS_ERR_UNSUPPORTED
