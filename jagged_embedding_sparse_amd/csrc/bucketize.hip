@@ -8,7 +8,7 @@
 //
 // The shard-major order (shard d, source rank r, table t, balanced sample q,
 // token j) is a stable counting sort by d of the items enumerated in (r, t,
-// q, j) order. Items are cut into tiles of 4096 tokens that never straddle a
+// q, j) order. Items are cut into tiles of 2048 tokens that never straddle a
 // (rank, table) segment and are numbered in (r, t, chunk) order, so an
 // item's output position is its shard's base, plus the shard's count in all
 // earlier tiles, plus its stable rank inside its tile:
@@ -34,9 +34,11 @@ namespace fs {
 namespace {
 
 constexpr int kThreads = 256;  // 4 waves
-constexpr int kRounds = 16;    // items per lane
+// items per lane: 8 keeps the tile kernels' register counts low enough (42
+// and 78) to share SIMDs with the update kernels of the other stream
+constexpr int kRounds = 8;
 constexpr int kWaveItems = kWave * kRounds;
-constexpr int kTile = kThreads * kRounds;  // 4096 tokens per tile
+constexpr int kTile = kThreads * kRounds;  // 2048 tokens per tile
 
 struct TableRows {
   int64_t rows[FS_MAX_TABLES];
@@ -215,7 +217,7 @@ __device__ __forceinline__ bool tile_info(int32_t tile, const int32_t* tile_pref
   return true;
 }
 
-// Loads one wave's 16 rounds of 64 consecutive tokens of a tile (table t,
+// Loads one wave's kRounds rounds of 64 consecutive tokens of a tile (table t,
 // batch-major positions bm) and returns, per round and lane, the item's key
 // and bin (shard, -1 for a dropped ID, `sentinel` past the tile's end).
 //
@@ -225,7 +227,7 @@ __device__ __forceinline__ bool tile_info(int32_t tile, const int32_t* tile_pref
 // in the window by binary lifting over the window with shuffles; the window
 // restarts at a round's first sample only when the round reaches past it, and
 // a lane whose token still lies past the window (only possible with runs of
-// empty samples) walks forward on its own. All 16 ID loads are independent.
+// empty samples) walks forward on its own. All the ID loads are independent.
 struct Window {
   int32_t qa;     // first sample of the window
   int64_t bnd;    // this lane: end offset of sample qa + lane (INT64_MAX past q_hi)
@@ -531,7 +533,7 @@ k_scatter(const uint32_t* __restrict__ ikey, int64_t n_tok, const int32_t* __res
   }
 }
 
-// tiles the launches cover: an upper bound on sum_r T * ceil(m_r / 4096),
+// tiles the launches cover: an upper bound on sum_r T * ceil(m_r / kTile),
 // rounded up to a multiple of the XCD count
 int32_t grid_tiles(int64_t n_tok, int32_t T, int32_t W) {
   return (int32_t)align_up((size_t)(T * (cdiv(n_tok, kTile) + W)), kXcd);

@@ -26,9 +26,9 @@ namespace fs {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kRounds = 16;
+constexpr int kRounds = 8;  // items per lane (register counts stay low)
 constexpr int kWaveItems = kWave * kRounds;
-constexpr int kTile = kThreads * kRounds;  // 4096
+constexpr int kTile = kThreads * kRounds;  // 2048
 constexpr int kMaxDigitBits = 10;
 constexpr int kMaxBins = 1 << kMaxDigitBits;  // also the count matrix's row length
 
@@ -92,7 +92,7 @@ __device__ __forceinline__ uint32_t global_key(uint32_t lk, int32_t d, const Seg
   return (uint32_t)(k.row_base[t] + (int64_t)d * k.block[t] + (lk - k.shard_off[t]));
 }
 
-// A tile: items [lo, lo + n) of shard d, n <= 4096; tiles never straddle a
+// A tile: items [lo, lo + n) of shard d, n <= kTile; tiles never straddle a
 // shard and are numbered in position order.
 struct UTile {
   int32_t lo, n, d, pad;
@@ -199,7 +199,7 @@ k_seg_hist(const KIn* __restrict__ keys, const UTile* __restrict__ tiles,
   __syncthreads();
   if (tile < tile_first[sk.W]) {
     const UTile u = tiles[tile];
-    // all 16 loads in flight (past the tile: its last item, not counted)
+    // all loads in flight (past the tile: its last item, not counted)
     uint32_t dg[kRounds];
     int tb[kRounds];
 #pragma unroll
@@ -447,7 +447,7 @@ k_heads_scan(const int64_t* __restrict__ nvp, int32_t W, int32_t n_groups,
     for (int32_t g = threadIdx.x; g <= n_groups; g += blockDim.x) unique_offsets[g] = 0;
 }
 
-// Striped layout: wave w of the tile owns 16 rounds of 64 consecutive items.
+// Striped layout: wave w of the tile owns kRounds rounds of 64 consecutive items.
 // Head flags by comparing with the left neighbour (shuffle, or the previous
 // round's last lane), counts by ballot; the wave prefix over the tile's
 // waves comes from LDS, the tile's base from the tile scan.
@@ -628,7 +628,7 @@ static int key_bits(int64_t key_space) {
   return b;
 }
 
-// tiles of the radix passes: sum over shards of ceil(items / 4096) <= this
+// tiles of the radix passes: sum over shards of ceil(items / kTile) <= this
 static int64_t seg_tiles(int64_t cap, int32_t W) {
   return (int64_t)align_up((size_t)(cdiv(cap, kTile) + W), kXcd);
 }
