@@ -345,18 +345,53 @@ k_hist(const int64_t* __restrict__ ids, int64_t n_tok, const int64_t* __restrict
 }
 
 // ---------------------------------------------------------------- scatter
-// Staging area of one workgroup: for a tile first the per-wave lane-mask
-// tables of the ranking, then the tile's items sorted by shard; for a splits
-// workgroup a 64 x 64 transpose.
-union ScatterStage {
-  uint64_t peers[kThreads / kWave][FS_MAX_RANKS + 1];
-  struct {
-    uint32_t key[kTile];
-    int32_t bm[kTile];
-    uint16_t bin[kTile];
-  } s;
-  int64_t tr[kWave][kWave + 1];
+// LDS of one workgroup, sized for nb = W + 1 bins at launch (the bins in use,
+// not the call limit, so more workgroups fit on a CU): per-wave shard counts,
+// each shard's output position and start in the sorted tile, then a staging
+// area that holds, in turn, the per-wave lane-mask tables of the ranking and
+// the tile's items sorted by shard -- or, for a splits workgroup, a 64 x 64
+// transpose.
+struct ScatterLds {
+  uint16_t* cnt;    // [4][nbp]
+  uint32_t* run;    // [nbp]
+  uint32_t* tbin;   // [nbp]
+  uint64_t* peers;  // [4][nb]  (staging)
+  uint32_t* skey;   // [kTile]  (staging)
+  int32_t* sbm;     // [kTile]  (staging)
+  uint16_t* sbin;   // [kTile]  (staging)
+  int32_t* tr;      // [64][65] (staging)
 };
+
+__host__ __device__ __forceinline__ size_t scatter_lds_bytes(int32_t nb, ScatterLds* l,
+                                                              char* base) {
+  const size_t nbp = align_up((size_t)nb, 8);
+  const size_t nw = kThreads / kWave;
+  size_t off = 0;
+  const size_t o_cnt = off;
+  off += align_up(nw * nbp * sizeof(uint16_t), 16);
+  const size_t o_run = off;
+  off += nbp * sizeof(uint32_t);
+  const size_t o_tbin = off;
+  off += nbp * sizeof(uint32_t);
+  const size_t o_stage = off;
+  const size_t peers = nw * (size_t)nb * sizeof(uint64_t);
+  const size_t items = (size_t)kTile * (sizeof(uint32_t) + sizeof(int32_t) + sizeof(uint16_t));
+  const size_t trans = (size_t)kWave * (kWave + 1) * sizeof(int32_t);
+  size_t stage = peers > items ? peers : items;
+  stage = stage > trans ? stage : trans;
+  off += stage;
+  if (l) {
+    l->cnt = (uint16_t*)(base + o_cnt);
+    l->run = (uint32_t*)(base + o_run);
+    l->tbin = (uint32_t*)(base + o_tbin);
+    l->peers = (uint64_t*)(base + o_stage);
+    l->skey = (uint32_t*)(base + o_stage);
+    l->sbm = (int32_t*)(base + o_stage + kTile * sizeof(uint32_t));
+    l->sbin = (uint16_t*)(base + o_stage + kTile * (sizeof(uint32_t) + sizeof(int32_t)));
+    l->tr = (int32_t*)(base + o_stage);
+  }
+  return off;
+}
 
 constexpr int kBinPer = (FS_MAX_RANKS + 1 + kThreads - 1) / kThreads;
 
@@ -388,8 +423,7 @@ __device__ __forceinline__ void bin_bases(const uint32_t* tot, int32_t W, int64_
 __device__ __forceinline__ void splits_part(int32_t x, int32_t y, const uint32_t* counts,
                                             int32_t ld, int32_t G, const int32_t* tile_pref,
                                             const uint32_t* tot, int32_t W, int64_t* splits,
-                                            int64_t* shard_offsets, int64_t (&tr)[kWave][kWave + 1],
-                                            int64_t* tmp) {
+                                            int64_t* shard_offsets, int32_t* tr, int64_t* tmp) {
   const int w = threadIdx.x / kWave, l = lane();
   if (x == 0 && y == 0) {
     int64_t base[kBinPer];
@@ -403,20 +437,20 @@ __device__ __forceinline__ void splits_part(int32_t x, int32_t y, const uint32_t
   const int32_t d = y * kWave + l;
   for (int rl = w; rl < kWave; rl += kThreads / kWave) {
     const int32_t r = x * kWave + rl;
-    int64_t val = 0;
+    int32_t val = 0;  // items of one rank for one shard: fewer than 2^31
     if (r < W && d < W) {
       const int32_t a = tile_pref[r], z = tile_pref[r + 1];
       const uint32_t va = a < G ? counts[(int64_t)a * ld + d] : tot[d];
       const uint32_t vz = z < G ? counts[(int64_t)z * ld + d] : tot[d];
-      val = (int64_t)vz - (int64_t)va;
+      val = (int32_t)(vz - va);
     }
-    tr[rl][l] = val;
+    tr[rl * (kWave + 1) + l] = val;
   }
   __syncthreads();
   const int32_t r = x * kWave + l;
   for (int dl = w; dl < kWave; dl += kThreads / kWave) {
     const int32_t dd = y * kWave + dl;
-    if (r < W && dd < W) splits[(int64_t)dd * W + r] = tr[l][dl];
+    if (r < W && dd < W) splits[(int64_t)dd * W + r] = (int64_t)tr[l * (kWave + 1) + dl];
   }
 }
 
@@ -428,15 +462,15 @@ k_scatter(const uint32_t* __restrict__ ikey, int64_t n_tok, const int32_t* __res
           const uint32_t* __restrict__ tot, int64_t* __restrict__ splits,
           int64_t* __restrict__ shard_offsets, int64_t* __restrict__ shard_keys,
           int32_t* __restrict__ shard_bm) {
-  __shared__ uint16_t cnt[kThreads / kWave][FS_MAX_RANKS + 1];
-  __shared__ uint32_t run[FS_MAX_RANKS + 1];   // output position of each shard's run
-  __shared__ uint32_t tbin[FS_MAX_RANKS + 1];  // start of each shard in the sorted tile
-  __shared__ ScatterStage st;
+  extern __shared__ __align__(16) char lds_dyn[];
   __shared__ int64_t tmp[17];
   constexpr int kPer = kBinPer;
+  ScatterLds L;
+  (void)scatter_lds_bytes(W + 1, &L, lds_dyn);
+  const int32_t nbp = (int32_t)align_up((size_t)W + 1, 8);
   if ((int32_t)blockIdx.x >= G) {
     const int32_t sb = blockIdx.x - G, nx = (int32_t)cdiv(W, kWave);
-    splits_part(sb % nx, sb / nx, offs, ld, G, tile_pref, tot, W, splits, shard_offsets, st.tr,
+    splits_part(sb % nx, sb / nx, offs, ld, G, tile_pref, tot, W, splits, shard_offsets, L.tr,
                 tmp);
     return;
   }
@@ -451,12 +485,14 @@ k_scatter(const uint32_t* __restrict__ ikey, int64_t n_tok, const int32_t* __res
 #pragma unroll
     for (int k = 0; k < kBinPer; ++k) {
       const int b = threadIdx.x * kBinPer + k;
-      if (b < nb) run[b] = (uint32_t)(base[k] + offs[(int64_t)tile * ld + b]);
+      if (b < nb) L.run[b] = (uint32_t)(base[k] + offs[(int64_t)tile * ld + b]);
     }
   }
+  uint16_t* cnt_w = L.cnt + w * nbp;
+  uint64_t* peers_w = L.peers + (int64_t)w * nb;
   for (int b = lane(); b < nb; b += kWave) {
-    cnt[w][b] = 0;
-    st.peers[w][b] = 0;
+    cnt_w[b] = 0;
+    peers_w[b] = 0;
   }
   const int32_t sentinel = (1 << nbits) - 1;  // > W: lanes without an item
   const int t = ti.t;
@@ -479,10 +515,10 @@ k_scatter(const uint32_t* __restrict__ ikey, int64_t n_tok, const int32_t* __res
   for (int i = 0; i < kRounds; ++i) {
     const int32_t b = bin[i];
     const bool on = b != sentinel;
-    const uint64_t peers = lds_peers(st.peers[w], (uint32_t)(on ? b : 0), on);
-    const uint32_t before = cnt[w][on ? b : 0];
+    const uint64_t peers = lds_peers(peers_w, (uint32_t)(on ? b : 0), on);
+    const uint32_t before = cnt_w[on ? b : 0];
     rk[i] = (int32_t)before + popc(peers & lt);
-    if (on && (peers & lt) == 0) cnt[w][b] = (uint16_t)(before + (uint32_t)popc(peers));
+    if (on && (peers & lt) == 0) cnt_w[b] = (uint16_t)(before + (uint32_t)popc(peers));
   }
   __syncthreads();
   // per shard: exclusive prefix over the waves, then the shards' starts in the tile
@@ -496,8 +532,8 @@ k_scatter(const uint32_t* __restrict__ ikey, int64_t n_tok, const int32_t* __res
       if (b < nb) {
 #pragma unroll
         for (int x = 0; x < kThreads / kWave; ++x) {
-          const uint32_t c = cnt[x][b];
-          cnt[x][b] = (uint16_t)r;
+          const uint32_t c = L.cnt[x * nbp + b];
+          L.cnt[x * nbp + b] = (uint16_t)r;
           r += c;
         }
       }
@@ -509,7 +545,7 @@ k_scatter(const uint32_t* __restrict__ ikey, int64_t n_tok, const int32_t* __res
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
       const int b = threadIdx.x * kPer + k;
-      if (b < nb) tbin[b] = (uint32_t)r0;
+      if (b < nb) L.tbin[b] = (uint32_t)r0;
       r0 += tb[k];
     }
   }
@@ -518,18 +554,18 @@ k_scatter(const uint32_t* __restrict__ ikey, int64_t n_tok, const int32_t* __res
   for (int i = 0; i < kRounds; ++i) {
     const int32_t b = bin[i];
     if (b == sentinel) continue;
-    const uint32_t p = tbin[b] + cnt[w][b] + (uint32_t)rk[i];
-    st.s.key[p] = key[i];
-    st.s.bm[p] = (int32_t)(first + i * kWave + lane());
-    st.s.bin[p] = (uint16_t)b;
+    const uint32_t p = L.tbin[b] + cnt_w[b] + (uint32_t)rk[i];
+    L.skey[p] = key[i];
+    L.sbm[p] = (int32_t)(first + i * kWave + lane());
+    L.sbin[p] = (uint16_t)b;
   }
   __syncthreads();
   const int m = (int)(ti.bm_hi - ti.bm_lo);
   for (int p = threadIdx.x; p < m; p += kThreads) {
-    const int b = st.s.bin[p];
-    const int64_t pos = (int64_t)run[b] + (p - (int)tbin[b]);
-    shard_keys[pos] = (int64_t)st.s.key[p];
-    shard_bm[pos] = st.s.bm[p];
+    const int b = L.sbin[p];
+    const int64_t pos = (int64_t)L.run[b] + (p - (int)L.tbin[b]);
+    shard_keys[pos] = (int64_t)L.skey[p];
+    shard_bm[pos] = L.sbm[p];
   }
 }
 
@@ -623,7 +659,8 @@ extern "C" int fs_bucketize_permute(const int64_t* ids, int64_t n_tok,
   FS_LAUNCH_CHECK();
   int rc = launch_colscan(counts, ld, G, W + 1, part, tot, stream);
   if (rc) return rc;
-  hipLaunchKernelGGL(k_scatter, dim3((unsigned)(G + split_blocks)), dim3(kThreads), 0, stream,
+  const size_t lds = scatter_lds_bytes(W + 1, nullptr, nullptr);
+  hipLaunchKernelGGL(k_scatter, dim3((unsigned)(G + split_blocks)), dim3(kThreads), lds, stream,
                      ikey, n_tok, tile_pref, tiles, tr, W, T, nbits, counts, ld, G, tot, splits,
                      shard_offsets, shard_keys, shard_bm);
   FS_LAUNCH_CHECK();
