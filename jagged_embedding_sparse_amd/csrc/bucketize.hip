@@ -135,6 +135,8 @@ k_tiles(int32_t n, int64_t n_tok, int32_t n_len_blocks, const int64_t* __restric
         TileDesc* __restrict__ tiles, int32_t* __restrict__ err) {
   __shared__ int64_t tmp64[17];
   __shared__ int32_t tmp32[17];
+  __shared__ int64_t s_A[FS_MAX_RANKS], s_m[FS_MAX_RANKS];
+  __shared__ int32_t s_pref[FS_MAX_RANKS + 1], s_q[FS_MAX_RANKS + 1];
   bool bad = false;
   int64_t part = 0;
   for (int32_t k = threadIdx.x; k < n_len_blocks; k += kPrepThreads) {
@@ -177,23 +179,42 @@ k_tiles(int32_t n, int64_t n_tok, int32_t n_len_blocks, const int64_t* __restric
   }
   int32_t ttot;
   int32_t pref = block_excl_scan<int32_t>(mine, tmp32, &ttot);
-  if (threadIdx.x == 0) tile_pref[W] = ttot;
+  if (threadIdx.x == 0) {
+    tile_pref[W] = ttot;
+    s_pref[W] = ttot;
+  }
 #pragma unroll
   for (int k = 0; k < kPrepRanks; ++k) {
     const int32_t r = threadIdx.x * kPrepRanks + k;
-    if (r < W) tile_pref[r] = pref;
-    for (int32_t t = 0; t < T; ++t)
-      for (int32_t kk = 0; kk < c[k]; ++kk) {
-        TileDesc d;
-        d.bm_lo = A[k] + (int64_t)kk * kTile;
-        d.n = (int32_t)min((int64_t)kTile, m[k] - (int64_t)kk * kTile);
-        d.seg = r * T + t;
-        d.q_lo = ro_v[k];
-        d.q_hi = ro_v[k + 1];
-        d.pad[0] = d.pad[1] = 0;
-        tiles[pref + t * c[k] + kk] = d;
-      }
+    if (r < W) {
+      tile_pref[r] = pref;
+      s_pref[r] = pref;
+      s_A[r] = A[k];
+      s_m[r] = m[k];
+      s_q[r] = ro_v[k];
+      if (r == W - 1) s_q[W] = ro_v[k + 1];
+    }
     pref += T * c[k];
+  }
+  __syncthreads();
+  // the tile table, all threads over all tiles: tile u belongs to the last
+  // rank r with s_pref[r] <= u (ranks without tokens share their first tile)
+  for (int32_t u = threadIdx.x; u < ttot; u += kPrepThreads) {
+    int32_t a = 0, b = W;  // s_pref[0] = 0 <= u < ttot = s_pref[W]
+    while (b - a > 1) {
+      const int32_t mid = (a + b) >> 1;
+      if (s_pref[mid] <= u) a = mid; else b = mid;
+    }
+    const int32_t c_r = (int32_t)cdiv(s_m[a], kTile);  // > 0: rank a owns tile u
+    const int32_t i = u - s_pref[a], t = i / c_r, kk = i % c_r;
+    TileDesc d;
+    d.bm_lo = s_A[a] + (int64_t)kk * kTile;
+    d.n = (int32_t)min((int64_t)kTile, s_m[a] - (int64_t)kk * kTile);
+    d.seg = a * T + t;
+    d.q_lo = s_q[a];
+    d.q_hi = s_q[a + 1];
+    d.pad[0] = d.pad[1] = 0;
+    tiles[u] = d;
   }
 }
 

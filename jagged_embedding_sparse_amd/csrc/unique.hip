@@ -111,6 +111,7 @@ k_seg_prep(const int64_t* __restrict__ so, int32_t W_so, int32_t W, int64_t n_ca
            int32_t* __restrict__ tile_first, UTile* __restrict__ tiles) {
   __shared__ int32_t wmax[kThreads / kWave];
   __shared__ int32_t tmp32[17];
+  __shared__ int32_t s_lo[FS_MAX_RANKS + 1], s_first[FS_MAX_RANKS + 1];
   int32_t v[kSegPer];
   int32_t run = 0;
 #pragma unroll
@@ -142,35 +143,49 @@ k_seg_prep(const int64_t* __restrict__ so, int32_t W_so, int32_t W, int64_t n_ca
 #pragma unroll
   for (int k = 0; k < kSegPer; ++k) {
     const int32_t d = threadIdx.x * kSegPer + k;
-    if (d <= W) seg_lo[d] = lo[k];
+    if (d <= W) {
+      seg_lo[d] = lo[k];
+      s_lo[d] = lo[k];
+    }
     if (d == W) *n_valid = lo[k];
   }
-  __syncthreads();  // seg_lo visible to the workgroup
-  int32_t c[kSegPer], size[kSegPer];
+  __syncthreads();  // s_lo visible to the workgroup
+  int32_t c[kSegPer];
   int32_t mine = 0;
 #pragma unroll
   for (int k = 0; k < kSegPer; ++k) {
     const int32_t d = threadIdx.x * kSegPer + k;
-    size[k] = d < W ? seg_lo[d + 1] - lo[k] : 0;
-    c[k] = (int32_t)cdiv(size[k], kTile);
+    c[k] = d < W ? (int32_t)cdiv(s_lo[d + 1] - lo[k], kTile) : 0;
     mine += c[k];
   }
   int32_t tt;
   int32_t pref = block_excl_scan<int32_t>(mine, tmp32, &tt);
-  if (threadIdx.x == 0) tile_first[W] = tt;
 #pragma unroll
   for (int k = 0; k < kSegPer; ++k) {
     const int32_t d = threadIdx.x * kSegPer + k;
-    if (d < W) tile_first[d] = pref;
-    for (int32_t j = 0; j < c[k]; ++j) {
-      UTile u;
-      u.lo = lo[k] + j * kTile;
-      u.n = min(kTile, size[k] - j * kTile);
-      u.d = d;
-      u.pad = 0;
-      tiles[pref + j] = u;
+    if (d <= W) {
+      const int32_t f = d < W ? pref : tt;
+      tile_first[d] = f;
+      s_first[d] = f;
     }
     pref += c[k];
+  }
+  __syncthreads();
+  // the tile table, all threads over all tiles: tile t belongs to the last
+  // segment d with s_first[d] <= t (empty segments share their first tile)
+  for (int32_t t = threadIdx.x; t < tt; t += kThreads) {
+    int32_t a = 0, b = W;  // s_first[0] = 0 <= t < tt = s_first[W]
+    while (b - a > 1) {
+      const int32_t m = (a + b) >> 1;
+      if (s_first[m] <= t) a = m; else b = m;
+    }
+    const int32_t j = t - s_first[a];
+    UTile u;
+    u.lo = s_lo[a] + j * kTile;
+    u.n = min(kTile, s_lo[a + 1] - u.lo);
+    u.d = a;
+    u.pad = 0;
+    tiles[t] = u;
   }
 }
 
@@ -427,13 +442,26 @@ k_heads_scan(const int64_t* __restrict__ nvp, int32_t W, int32_t n_groups,
   __shared__ int64_t tmp[17];
   const int64_t n = n_valid_of(nvp, W);
   const int64_t n_tiles = cdiv(n, kTile);
+  // thread i scans a contiguous slice of the tile counts: its loads are all
+  // in flight, and one workgroup scan joins the slices
+  constexpr int kSlice = 16;
   int64_t carry = 0;
-  for (int64_t c0 = 0; c0 < n_tiles; c0 += blockDim.x) {
-    const int64_t c = c0 + threadIdx.x;
-    const int64_t v = c < n_tiles ? tile_heads[c] : 0;
+  for (int64_t c0 = 0; c0 < n_tiles; c0 += (int64_t)kSlice * blockDim.x) {
+    const int64_t lo = c0 + (int64_t)threadIdx.x * kSlice;
+    uint32_t v[kSlice];
+    int64_t local = 0;
+#pragma unroll
+    for (int k = 0; k < kSlice; ++k) {
+      v[k] = lo + k < n_tiles ? tile_heads[lo + k] : 0u;
+      local += v[k];
+    }
     int64_t sum;
-    const int64_t ex = block_excl_scan<int64_t>(v, tmp, &sum);
-    if (c < n_tiles) tile_heads[c] = (uint32_t)(carry + ex);
+    int64_t ex = carry + block_excl_scan<int64_t>(local, tmp, &sum);
+#pragma unroll
+    for (int k = 0; k < kSlice; ++k) {
+      if (lo + k < n_tiles) tile_heads[lo + k] = (uint32_t)ex;
+      ex += v[k];
+    }
     carry += sum;
   }
   if (threadIdx.x == 0) {
