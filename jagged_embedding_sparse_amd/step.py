@@ -54,11 +54,14 @@ class StageTimer:
     inside the timed loop would let the host, not the GPU, set the pace of
     small steps; the runtime recycles those resources when events are
     dropped, so a larger pool made and dropped first keeps the timed
-    records cheap."""
+    records cheap. Each record also costs the GPU a few microseconds between
+    kernels, so `only` limits the timed stages where that would distort the
+    measurement."""
 
-    def __init__(self, capacity=0, streams=None):
+    def __init__(self, capacity=0, streams=None, only=None):
         self.pairs = {}
         self.pool = []
+        self.only = set(only) if only is not None else None  # stage names to time
         ss = list(streams) if streams else [torch.cuda.current_stream()]
         for i in range(capacity):
             a = torch.cuda.Event(enable_timing=True)
@@ -75,6 +78,8 @@ class StageTimer:
         return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
     def span(self, name, stream):
+        if self.only is not None and name not in self.only:
+            return _nullspan()
         timer = self
 
         class _Span:
