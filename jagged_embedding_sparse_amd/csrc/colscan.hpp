@@ -1,9 +1,10 @@
 // Exclusive column scans of a row-major matrix of 32-bit counts (rows =
 // tiles in output order, columns = bins), in place. Lanes are columns, so
-// every row load is coalesced; each wave takes 32 consecutive rows, each
-// workgroup 128. Two launches over (row blocks) x (column groups of 64):
-// k_colsum stores each row block's column sums, k_colscan adds the sums of
-// the row blocks before its own and rewrites the rows as exclusive prefixes.
+// every row load is coalesced. Large matrices: each wave takes 32
+// consecutive rows, each workgroup 128, in two launches over (row blocks) x
+// (column groups of 64): k_colsum stores each row block's column sums,
+// k_colscan adds the sums of the row blocks before its own and rewrites the
+// rows as exclusive prefixes. Small matrices: one launch (k_colscan1).
 #pragma once
 
 #include "common.hpp"
@@ -77,10 +78,65 @@ k_colscan(uint32_t* __restrict__ counts, int32_t ld, int32_t G, int32_t C,
   if (blockIdx.x == gridDim.x - 1 && w == kColThreads / kWave - 1) tot[c] = base;
 }
 
-// Both launches for a G x C matrix with leading dimension ld; part holds
-// cdiv(G, 128) * ld entries, tot C.
+// Small matrices (G <= kColOneRows): one launch, one workgroup per group of
+// 64 columns. Each wave sums a contiguous slice of the rows (kColBatch loads
+// in flight per lane), the waves' slice sums are combined in LDS, then each
+// wave rereads its slice and writes the exclusive prefixes.
+constexpr int kColOneRows = 1024;
+constexpr int kColBatch = 16;
+
+__global__ void __launch_bounds__(kColThreads)
+k_colscan1(uint32_t* __restrict__ counts, int32_t ld, int32_t G, int32_t C,
+           uint32_t* __restrict__ tot) {
+  __shared__ uint32_t wsum[kColThreads / kWave][kWave];
+  constexpr int nw = kColThreads / kWave;
+  const int w = threadIdx.x / kWave, l = lane();
+  const int32_t c = blockIdx.x * kWave + l;
+  const bool on = c < C;
+  const int32_t cc = on ? c : C - 1;
+  const int32_t per = (int32_t)cdiv(G, nw);
+  const int32_t r0 = min(G, w * per), r1 = min(G, r0 + per);
+  uint32_t s = 0;
+  for (int32_t rb = r0; rb < r1; rb += kColBatch) {
+    uint32_t v[kColBatch];
+#pragma unroll
+    for (int i = 0; i < kColBatch; ++i)
+      v[i] = counts[(int64_t)min(rb + i, G - 1) * ld + cc];
+#pragma unroll
+    for (int i = 0; i < kColBatch; ++i) s += rb + i < r1 ? v[i] : 0u;
+  }
+  wsum[w][l] = s;
+  __syncthreads();
+  uint32_t base = 0;
+  for (int x = 0; x < w; ++x) base += wsum[x][l];
+  if (w == nw - 1 && on) tot[c] = base + s;
+  if (!on) return;
+  for (int32_t rb = r0; rb < r1; rb += kColBatch) {
+    uint32_t v[kColBatch];
+#pragma unroll
+    for (int i = 0; i < kColBatch; ++i)
+      v[i] = counts[(int64_t)min(rb + i, G - 1) * ld + c];
+#pragma unroll
+    for (int i = 0; i < kColBatch; ++i) {
+      if (rb + i < r1) {
+        counts[(int64_t)(rb + i) * ld + c] = base;
+        base += v[i];
+      }
+    }
+  }
+}
+
+// The column scan of a G x C matrix with leading dimension ld: one launch
+// for small G, else block sums then prefixes; part holds cdiv(G, 128) * ld
+// entries, tot C.
 inline int launch_colscan(uint32_t* counts, int32_t ld, int32_t G, int32_t C, uint32_t* part,
                           uint32_t* tot, hipStream_t stream) {
+  if (G <= kColOneRows) {
+    hipLaunchKernelGGL(k_colscan1, dim3((unsigned)cdiv(C, kWave)), dim3(kColThreads), 0, stream,
+                       counts, ld, G, C, tot);
+    FS_LAUNCH_CHECK();
+    return FS_OK;
+  }
   const dim3 grid((unsigned)cdiv(G, kColBlockRows), (unsigned)cdiv(C, kWave));
   hipLaunchKernelGGL(k_colsum, grid, dim3(kColThreads), 0, stream, counts, ld, G, C, part);
   FS_LAUNCH_CHECK();
