@@ -536,7 +536,7 @@ k_compact(const uint32_t* __restrict__ sk, const int64_t* __restrict__ nvp, Grou
 
 // ---------------------------------------------------------------- collision
 constexpr int kMergeThreads = 256;
-constexpr int kMergeTile = 2048;
+constexpr int kMergeTile = 2048;  // merged elements per workgroup
 
 // Merged order of a (new) and b (prev) with ties taken from b first: the
 // number of a-elements among the first d merged elements is the smallest i
@@ -547,7 +547,7 @@ __device__ __forceinline__ int64_t merge_split(const int64_t* a, int64_t na, con
   return wave_partition_point(lo, hi, [&](int64_t i) { return a[i] < b[d - i - 1]; });
 }
 
-__device__ __forceinline__ int lds_upper(const int64_t* s, int n, int64_t v) {  // # s <= v
+__device__ __forceinline__ int lds_upper(const uint32_t* s, int n, uint32_t v) {  // # s <= v
   int lo = 0, hi = n;
   while (lo < hi) {
     int mid = (lo + hi) >> 1;
@@ -556,7 +556,7 @@ __device__ __forceinline__ int lds_upper(const int64_t* s, int n, int64_t v) {  
   return lo;
 }
 
-__device__ __forceinline__ int lds_lower(const int64_t* s, int n, int64_t v) {  // # s < v
+__device__ __forceinline__ int lds_lower(const uint32_t* s, int n, uint32_t v) {  // # s < v
   int lo = 0, hi = n;
   while (lo < hi) {
     int mid = (lo + hi) >> 1;
@@ -570,7 +570,8 @@ k_collide(const int64_t* __restrict__ a, const int64_t* __restrict__ counts_a, i
           const int64_t* __restrict__ b, const int64_t* __restrict__ counts_b, int64_t cap_b,
           uint8_t* __restrict__ cls, uint8_t* __restrict__ prev_cls,
           uint32_t* __restrict__ block_hits) {
-  __shared__ int64_t sa[kMergeTile + 1], sb[kMergeTile + 1];
+  // slices as 32-bit keys (every key is below 2^32)
+  __shared__ uint32_t sa[kMergeTile + 1], sb[kMergeTile + 1];
   __shared__ int64_t span[4];
   __shared__ uint32_t hits[kMergeThreads / kWave];
   const int64_t na = min(counts_a[0], cap_a);
@@ -592,25 +593,26 @@ k_collide(const int64_t* __restrict__ a, const int64_t* __restrict__ counts_a, i
     const int64_t i0 = span[0], i1 = span[1], j0 = span[2], j1 = span[3];
     const int ca = (int)(i1 - i0), cb = (int)(j1 - j0);
     // sa[0] = a[i1] sentinel area is after the slice; sb holds b[j0-1] first
-    for (int x = threadIdx.x; x < ca; x += kMergeThreads) sa[x] = a[i0 + x];
-    for (int x = threadIdx.x; x < cb; x += kMergeThreads) sb[x + 1] = b[j0 + x];
+    for (int x = threadIdx.x; x < ca; x += kMergeThreads) sa[x] = (uint32_t)a[i0 + x];
+    for (int x = threadIdx.x; x < cb; x += kMergeThreads) sb[x + 1] = (uint32_t)b[j0 + x];
     if (threadIdx.x == 0) {
-      sb[0] = j0 > 0 ? b[j0 - 1] : INT64_MIN;  // b element before the slice
-      sa[ca] = i1 < na ? a[i1] : INT64_MAX;    // a element after the slice
+      // b element before the slice, a element after it (read only when they exist)
+      sb[0] = j0 > 0 ? (uint32_t)b[j0 - 1] : 0u;
+      sa[ca] = i1 < na ? (uint32_t)a[i1] : 0xFFFFFFFFu;
     }
     __syncthreads();
     // a side: a[i] collides iff the last b <= a[i] equals it
     for (int x = threadIdx.x; x < ca; x += kMergeThreads) {
-      const int64_t v = sa[x];
+      const uint32_t v = sa[x];
       const int jj = lds_upper(sb + 1, cb, v);  // b elements of the slice <= v
-      const int64_t last = sb[jj];              // sb[0] when none in the slice
+      const uint32_t last = sb[jj];             // sb[0] when none in the slice
       const bool hit = (j0 + jj > 0) && last == v;
       cls[i0 + x] = hit ? FS_COLLISION : FS_EXCLUSIVE;
       mine += hit;
     }
     // b side: b[j] collides iff the first a >= b[j] equals it
     for (int x = threadIdx.x; x < cb; x += kMergeThreads) {
-      const int64_t v = sb[x + 1];
+      const uint32_t v = sb[x + 1];
       const int ii = lds_lower(sa, ca, v);  // a elements of the slice < v
       const bool hit = (i0 + ii < na) && sa[ii] == v;
       prev_cls[j0 + x] = hit ? FS_COLLISION : FS_EXCLUSIVE;
