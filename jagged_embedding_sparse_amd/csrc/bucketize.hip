@@ -320,7 +320,8 @@ __device__ __forceinline__ void wave_items(const TileInfo& ti, int32_t w, const 
 #pragma unroll
   for (int i = 0; i < kRounds; ++i) {
     if (!valid[i]) continue;
-    const int64_t id = ids[(int64_t)t * n_tok + tok[i]];
+    // read once (streaming load: keeps the sample tables in the caches)
+    const int64_t id = __builtin_nontemporal_load(ids + (int64_t)t * n_tok + tok[i]);
     const bool in = id >= 0 && id < rows;
     key[i] = (uint32_t)(rbase + id);
     bin[i] = in ? (int32_t)divu32((uint32_t)id, div) : -1;
@@ -526,7 +527,7 @@ k_scatter(const uint32_t* __restrict__ ikey, int64_t n_tok, const int32_t* __res
 #pragma unroll
   for (int i = 0; i < kRounds; ++i) {
     const bool valid = first + i * kWave + lane() < ti.bm_hi;
-    key[i] = valid ? in[i * kWave] : 0u;
+    key[i] = valid ? __builtin_nontemporal_load(in + i * kWave) : 0u;  // last read
     bin[i] = !valid ? sentinel : key[i] == kDropKey ? W : (int32_t)divu32(key[i] - rbase, div);
   }
   // stable rank of each item among the wave's items of its shard

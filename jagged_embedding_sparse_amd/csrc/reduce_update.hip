@@ -36,6 +36,7 @@ inline int64_t chunk_for(int64_t n_tok) {
   return n_tok >= 512 * target ? 512 : (n_tok >= 256 * target ? 256 : 128);
 }
 constexpr int kShortBlocks = 4096;
+constexpr int kLongBatch = 8;  // gradient rows in flight per lane group (long rows)
 constexpr int64_t kUpdateCap = 0;  // workgroups per update kernel (0: no cap)
 // waves of the short-row kernel the GPU holds at once (256 CUs x 4 SIMDs x
 // 5 waves of ~90 registers); the unit size aims at two or more units each
@@ -69,6 +70,15 @@ struct Map {
   static constexpr int GPW = kWave / LPG;                        // groups per wave
   __device__ static int col(int sub, int v) { return 4 * (sub + v * LPG); }
 };
+
+// Gradient rows are read exactly once: streaming (non-temporal) loads keep
+// them from displacing the weight rows, Adagrad state and fp64 partials in
+// the caches (measured: 1060 -> 1021 us per update at workload 5).
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ float4 ld_stream(const float4* p) {
+  const f32x4 v = __builtin_nontemporal_load((const f32x4*)p);
+  return make_float4(v.x, v.y, v.z, v.w);
+}
 
 __device__ __forceinline__ bool class_ok(const RUArgs& a, int64_t u) {
   return a.which < 0 || a.cls[u] == (uint8_t)a.which;
@@ -263,7 +273,7 @@ __global__ void __launch_bounds__(kThreads) k_short(RUArgs a) {
           if (m < len) {
             const float4* gp = (const float4*)(a.grad + (int64_t)bm * D);
 #pragma unroll
-            for (int v = 0; v < M::NV; ++v) gv[m][v] = gp[sub + v * M::LPG];
+            for (int v = 0; v < M::NV; ++v) gv[m][v] = ld_stream(gp + sub + v * M::LPG);
           }
         }
 #pragma unroll
@@ -327,20 +337,20 @@ __device__ __forceinline__ void long_chunk(const RUArgs& a, int64_t o_lo, int64_
         const int nblk = (int)min((int64_t)kWave, p1 - ob);
         const int32_t bmv = lane() < nblk ? a.occ_bm[ob + lane()] : 0;
         // group g takes rows g, g + GPW, ... of this block of 64
-        for (int m0 = 0; m0 < nblk; m0 += 8 * M::GPW) {
-          float4 gv[8][M::NV];
+        for (int m0 = 0; m0 < nblk; m0 += kLongBatch * M::GPW) {
+          float4 gv[kLongBatch][M::NV];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
+          for (int e = 0; e < kLongBatch; ++e) {
             const int m = m0 + e * M::GPW + grp;
             const int32_t bm = __shfl(bmv, m < kWave ? m : 0, kWave);
             if (m < nblk) {
               const float4* gp = (const float4*)(a.grad + (int64_t)bm * D);
 #pragma unroll
-              for (int v = 0; v < M::NV; ++v) gv[e][v] = gp[sub + v * M::LPG];
+              for (int v = 0; v < M::NV; ++v) gv[e][v] = ld_stream(gp + sub + v * M::LPG);
             }
           }
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
+          for (int e = 0; e < kLongBatch; ++e) {
             if (m0 + e * M::GPW + grp < nblk) {
 #pragma unroll
               for (int v = 0; v < M::NV; ++v) {

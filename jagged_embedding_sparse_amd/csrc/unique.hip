@@ -325,9 +325,12 @@ k_seg_scatter(const KIn* __restrict__ keys_in, const int32_t* __restrict__ vals_
     const int x = w * kWaveItems + i * kWave + lane();
     const bool valid = x < u.n;
     const int xc = u.lo + (valid ? x : u.n - 1);  // unconditional loads, all in flight
-    if constexpr (kFirst) key[i] = local_key((int64_t)keys_in[xc], u.d, sk);
-    else key[i] = (uint32_t)keys_in[xc];
-    val[i] = vals_in[xc];
+    // the pass's last read of its input (the histogram read it before):
+    // streaming loads
+    const KIn kv = __builtin_nontemporal_load(keys_in + xc);
+    if constexpr (kFirst) key[i] = local_key((int64_t)kv, u.d, sk);
+    else key[i] = (uint32_t)kv;
+    val[i] = __builtin_nontemporal_load(vals_in + xc);
     dig[i] = valid ? ((key[i] >> shift) & mask) : none;
   }
   // stable rank of each item among the wave's items of its digit
