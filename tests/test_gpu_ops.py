@@ -345,6 +345,10 @@ RU_CASES = [
     (1024, "f32", "rw_adagrad", [(7, 900)], 4000, 3, 5000),
     (128, "f32", "rw_adagrad", [], 10000, 4, 10_000_000),  # all rows short
     (128, "f32", "sgd", [(0, 30000)], 30000, 4, 100),       # one row owns every token
+    # ~0.6M unique rows: the short-row kernel takes 32-row units per wave
+    (64, "f32", "sgd", [(7, 20_000)], 600_000, 8, 50_000_000),
+    # 2.7M tokens: 256-occurrence long-row chunks, one row split over ~1560 of them
+    (64, "bf16", "rw_adagrad", [(5, 400_000), (6, 3000)], 2_700_000, 16, 5_000_000),
 ]
 
 
