@@ -36,8 +36,9 @@ inline int64_t chunk_for(int64_t n_tok) {
   return n_tok >= 512 * target ? 512 : (n_tok >= 256 * target ? 256 : 128);
 }
 constexpr int kShortBlocks = 4096;
-constexpr int kLongBatch = 8;  // gradient rows in flight per lane group (long rows)
-constexpr int64_t kUpdateCap = 0;  // workgroups per update kernel (0: no cap)
+// gradient rows in flight per lane group on the long-row path (8, 12 and 16
+// measured the same: the path runs at the device's rate for random 512-B rows)
+constexpr int kLongBatch = 8;
 // waves of the short-row kernel the GPU holds at once (256 CUs x 4 SIMDs x
 // 5 waves of ~90 registers); the unit size aims at two or more units each
 constexpr int64_t kResident = 256 * 4 * 5;
@@ -473,14 +474,12 @@ template <int D, typename WT>
 int launch_all(const RUArgs& a, hipStream_t stream) {
   int64_t sb = cdiv(a.n_cap, kThreads);  // 64 rows per wave, 4 waves per block
   if (sb > kShortBlocks) sb = kShortBlocks;
-  if (kUpdateCap > 0 && sb > kUpdateCap) sb = kUpdateCap;
   if (sb < 1) sb = 1;
   hipLaunchKernelGGL((k_short<D, WT>), dim3((unsigned)sb), dim3(kThreads), 0, stream, a);
   FS_LAUNCH_CHECK();
   const int64_t chunks = cdiv(a.n_cap, a.chunk);
   if (chunks > 0) {
     int64_t lb = cdiv(chunks, kThreads / kWave);
-    if (kUpdateCap > 0 && lb > kUpdateCap) lb = kUpdateCap;
     hipLaunchKernelGGL((k_long<D, WT>), dim3((unsigned)lb), dim3(kThreads), 0, stream, a);
     FS_LAUNCH_CHECK();
     hipLaunchKernelGGL((k_fix<D, WT>), dim3((unsigned)chunks), dim3(kThreads), 0, stream, a);
