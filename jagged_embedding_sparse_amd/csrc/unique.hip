@@ -249,24 +249,33 @@ k_seg_hist(const KIn* __restrict__ keys, const UTile* __restrict__ tiles,
 // move to its place in (table, shard) order. delta[t*W + d] = that place
 // minus where the group starts inside the shard-sorted order.
 __global__ void __launch_bounds__(kThreads)
-k_seg_groups(const uint32_t* __restrict__ cnt_t, const int32_t* __restrict__ tile_first,
-             const int32_t* __restrict__ seg_lo, int32_t W, int32_t T,
-             int32_t* __restrict__ delta) {
+k_seg_groups(const uint32_t* __restrict__ cnt_t, const UTile* __restrict__ tiles,
+             const int32_t* __restrict__ tile_first, const int32_t* __restrict__ seg_lo,
+             int32_t W, int32_t T, int32_t* __restrict__ delta) {
   __shared__ int64_t tmp[17];
-  int32_t size[kSegPer][FS_MAX_TABLES];
-#pragma unroll
-  for (int k = 0; k < kSegPer; ++k) {
-    const int32_t d = threadIdx.x * kSegPer + k;
-    for (int t = 0; t < FS_MAX_TABLES; ++t) size[k][t] = 0;
-    if (d < W)
-      for (int32_t q = tile_first[d]; q < tile_first[d + 1]; ++q)
-        for (int t = 0; t < T; ++t) size[k][t] += (int32_t)cnt_t[(int64_t)q * FS_MAX_TABLES + t];
+  __shared__ uint32_t gsize[FS_MAX_RANKS][FS_MAX_TABLES];  // items of group (t, d), [d][t]
+  for (int32_t x = threadIdx.x; x < W * FS_MAX_TABLES; x += kThreads) (&gsize[0][0])[x] = 0;
+  __syncthreads();
+  // every tile adds its per-table counts to its shard's row (all threads)
+  const int32_t n_tiles = tile_first[W];
+  for (int32_t q = threadIdx.x; q < n_tiles; q += kThreads) {
+    const int32_t d = tiles[q].d;
+    for (int t = 0; t < T; ++t) {
+      const uint32_t c = cnt_t[(int64_t)q * FS_MAX_TABLES + t];
+      if (c) atomicAdd(&gsize[d][t], c);
+    }
   }
+  __syncthreads();
+  // per table: groups in shard order after the earlier tables; inside the
+  // shard-sorted order the group follows the shard's earlier tables
   int64_t table_base = 0;
   for (int t = 0; t < T; ++t) {
     int64_t local = 0;
 #pragma unroll
-    for (int k = 0; k < kSegPer; ++k) local += size[k][t];
+    for (int k = 0; k < kSegPer; ++k) {
+      const int32_t d = threadIdx.x * kSegPer + k;
+      local += d < W ? gsize[d][t] : 0u;
+    }
     int64_t tot;
     int64_t g = table_base + block_excl_scan<int64_t>(local, tmp, &tot);
 #pragma unroll
@@ -274,10 +283,10 @@ k_seg_groups(const uint32_t* __restrict__ cnt_t, const int32_t* __restrict__ til
       const int32_t d = threadIdx.x * kSegPer + k;
       if (d < W) {
         int64_t inside = seg_lo[d];
-        for (int t2 = 0; t2 < t; ++t2) inside += size[k][t2];
+        for (int t2 = 0; t2 < t; ++t2) inside += gsize[d][t2];
         delta[t * W + d] = (int32_t)(g - inside);
+        g += gsize[d][t];
       }
-      g += size[k][t];
     }
     table_base += tot;
   }
@@ -797,8 +806,8 @@ extern "C" int fs_unique_collision_split(const int64_t* shard_keys, const int32_
     int rc = launch_colscan(hist, kMaxBins, (int32_t)G, (int32_t)mask + 1, part, tot, stream);
     if (rc) return rc;
     if (last && T > 1 && nseg > 1) {
-      hipLaunchKernelGGL(k_seg_groups, dim3(1), dim3(kThreads), 0, stream, cnt_t, tile_first,
-                         seg_lo, W, T, delta);
+      hipLaunchKernelGGL(k_seg_groups, dim3(1), dim3(kThreads), 0, stream, cnt_t, utiles,
+                         tile_first, seg_lo, W, T, delta);
       FS_LAUNCH_CHECK();
     }
     if (first && last)
