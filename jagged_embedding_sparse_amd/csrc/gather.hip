@@ -35,22 +35,36 @@ struct LookupArgs {
   int32_t which;
 };
 
+// The tables of one row size share a launch: workgroups [lo_i, lo_{i+1}) copy
+// table i of the batch.
+struct LookupBatch {
+  LookupArgs t[FS_MAX_TABLES];
+  int32_t block_lo[FS_MAX_TABLES + 1];
+  int32_t n;
+};
+
 // One wave per 64 consecutive occurrences (CSR order). Index data is read
 // coalesced once per wave -- occurrence -> (unique, slot), then the <= 64
 // unique rows those occurrences span -> (key, class) -- and handed to the
 // copying lanes with cross-lane shuffles, so rows start loading after two
 // dependent index loads and up to 16 rows per lane group are in flight.
 template <int VPR>  // 16-byte vectors per row
-__global__ void __launch_bounds__(kThreads) k_lookup(LookupArgs a) {
+__global__ void __launch_bounds__(kThreads) k_lookup(LookupBatch batch) {
+  int ti = 0;
+  while (ti + 1 < batch.n && (int32_t)blockIdx.x >= batch.block_lo[ti + 1]) ++ti;
+  const LookupArgs& a = batch.t[ti];
+  const int64_t blk = (int64_t)blockIdx.x - batch.block_lo[ti];
   constexpr int LPR = VPR < kWave ? VPR : kWave;  // lanes per row
   constexpr int RPW = kWave / LPR;                // rows per wave instruction
   constexpr int VPL = VPR / LPR;                  // vectors per lane
   constexpr int STEPS = kWave / RPW;              // row steps for 64 occurrences
-  constexpr int BATCH = STEPS < 16 / VPL ? STEPS : 16 / VPL;
+  // rows per lane group in flight; 128-B rows take two batches of four (all
+  // eight at once compiled to 252 VGPRs, four to 90)
+  constexpr int BATCH = VPR == 8 ? 4 : (STEPS < 16 / VPL ? STEPS : 16 / VPL);
   const int64_t o_lo = a.seg_offsets[a.unique_offsets[a.g_lo]];
   const int64_t o_hi = a.seg_offsets[a.unique_offsets[a.g_hi]];
   const int w = threadIdx.x / kWave, l = lane();
-  const int64_t o0 = o_lo + ((int64_t)blockIdx.x * (kThreads / kWave) + w) * kWave;
+  const int64_t o0 = o_lo + (blk * (kThreads / kWave) + w) * kWave;
   if (o0 >= o_hi) return;
   const int nvalid = (int)min((int64_t)kWave, o_hi - o0);
   const bool valid = l < nvalid;
@@ -95,14 +109,26 @@ __global__ void __launch_bounds__(kThreads) k_lookup(LookupArgs a) {
   }
 }
 
+constexpr int kOccPerBlock = kWave * (kThreads / kWave);
+
 template <int VPR>
-int launch(const LookupArgs& a, hipStream_t stream) {
-  constexpr int OPB = kWave * (kThreads / kWave);  // occurrences per block
-  const int64_t blocks = cdiv(a.n_cap, OPB);
-  if (blocks == 0) return FS_OK;
-  hipLaunchKernelGGL(k_lookup<VPR>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
+int launch(const LookupBatch& b, hipStream_t stream) {
+  if (b.block_lo[b.n] == 0) return FS_OK;
+  hipLaunchKernelGGL(k_lookup<VPR>, dim3((unsigned)b.block_lo[b.n]), dim3(kThreads), 0, stream,
+                     b);
   FS_LAUNCH_CHECK();
   return FS_OK;
+}
+
+int launch_vpr(int vpr, const LookupBatch& b, hipStream_t stream) {
+  switch (vpr) {
+    case 4: return launch<4>(b, stream);
+    case 8: return launch<8>(b, stream);
+    case 16: return launch<16>(b, stream);
+    case 32: return launch<32>(b, stream);
+    case 64: return launch<64>(b, stream);
+    default: return launch<128>(b, stream);
+  }
 }
 
 }  // namespace
@@ -133,10 +159,13 @@ extern "C" int fs_jagged_lookup(const fs_table* tables, int32_t T, int32_t W,
     base += tb.rows;
   }
   if (base > (int64_t)UINT32_MAX) return FS_ERR_UNSUPPORTED;
+  // one launch per row size, covering every table of that size
+  LookupArgs args[FS_MAX_TABLES];
+  int vpr[FS_MAX_TABLES];
   base = 0;
   for (int t = 0; t < T; ++t) {
     const fs_table& tb = tables[t];
-    LookupArgs a;
+    LookupArgs& a = args[t];
     a.weights = (const char*)tb.weights;
     a.out = (char*)out[t];
     a.row_base = base;
@@ -151,16 +180,22 @@ extern "C" int fs_jagged_lookup(const fs_table* tables, int32_t T, int32_t W,
     a.g_hi = (t + 1) * W;
     a.which = which;
     base += tb.rows;
-    const int64_t rb = (int64_t)tb.dim * (tb.dtype == FS_F32 ? 4 : 2);
-    int rc;
-    switch (rb) {
-      case 64: rc = launch<4>(a, stream); break;
-      case 128: rc = launch<8>(a, stream); break;
-      case 256: rc = launch<16>(a, stream); break;
-      case 512: rc = launch<32>(a, stream); break;
-      case 1024: rc = launch<64>(a, stream); break;
-      default: rc = launch<128>(a, stream); break;
+    vpr[t] = (int)(tb.dim * (tb.dtype == FS_F32 ? 4 : 2) / 16);
+  }
+  bool done[FS_MAX_TABLES] = {};
+  for (int t = 0; t < T; ++t) {
+    if (done[t]) continue;
+    LookupBatch b;
+    b.n = 0;
+    b.block_lo[0] = 0;
+    for (int u = t; u < T; ++u) {
+      if (done[u] || vpr[u] != vpr[t]) continue;
+      done[u] = true;
+      b.t[b.n] = args[u];
+      b.block_lo[b.n + 1] = b.block_lo[b.n] + (int32_t)cdiv(n_tok, kOccPerBlock);
+      ++b.n;
     }
+    const int rc = launch_vpr(vpr[t], b, stream);
     if (rc) return rc;
   }
   return FS_OK;
