@@ -43,8 +43,15 @@ struct LookupBatch {
   int32_t n;
 };
 
-// One wave per 64 consecutive occurrences (CSR order). Index data is read
-// coalesced once per wave -- occurrence -> (unique, slot), then the <= 64
+// Occurrences per wave: 64 for rows of up to 256 B, fewer for larger rows,
+// so that a wave copies its rows in one batch and more waves share the work.
+template <int VPR>
+struct LookupShape {
+  static constexpr int OPW = VPR <= 16 ? kWave : (VPR == 32 ? 32 : 16);
+};
+
+// One wave per OPW consecutive occurrences (CSR order). Index data is read
+// coalesced once per wave -- occurrence -> (unique, slot), then the <= OPW
 // unique rows those occurrences span -> (key, class) -- and handed to the
 // copying lanes with cross-lane shuffles, so rows start loading after two
 // dependent index loads and up to 16 rows per lane group are in flight.
@@ -57,21 +64,22 @@ __global__ void __launch_bounds__(kThreads) k_lookup(LookupBatch batch) {
   constexpr int LPR = VPR < kWave ? VPR : kWave;  // lanes per row
   constexpr int RPW = kWave / LPR;                // rows per wave instruction
   constexpr int VPL = VPR / LPR;                  // vectors per lane
-  constexpr int STEPS = kWave / RPW;              // row steps for 64 occurrences
+  constexpr int OPW = LookupShape<VPR>::OPW;      // occurrences per wave
+  constexpr int STEPS = OPW / RPW;                // row steps for OPW occurrences
   // rows per lane group in flight; 128-B rows take two batches of four (all
   // eight at once compiled to 252 VGPRs, four to 90)
   constexpr int BATCH = VPR == 8 ? 4 : (STEPS < 16 / VPL ? STEPS : 16 / VPL);
   const int64_t o_lo = a.seg_offsets[a.unique_offsets[a.g_lo]];
   const int64_t o_hi = a.seg_offsets[a.unique_offsets[a.g_hi]];
   const int w = threadIdx.x / kWave, l = lane();
-  const int64_t o0 = o_lo + (blk * (kThreads / kWave) + w) * kWave;
+  const int64_t o0 = o_lo + (blk * (kThreads / kWave) + w) * OPW;
   if (o0 >= o_hi) return;
-  const int nvalid = (int)min((int64_t)kWave, o_hi - o0);
+  const int nvalid = (int)min((int64_t)OPW, o_hi - o0);
   const bool valid = l < nvalid;
   const int32_t u = valid ? a.occ_uid[o0 + l] : 0;
   const int32_t bm = valid ? a.occ_bm[o0 + l] : -1;
   const int32_t u0 = __shfl(u, 0, kWave);
-  const int32_t span = __shfl(u, nvalid - 1, kWave) - u0 + 1;  // <= 64
+  const int32_t span = __shfl(u, nvalid - 1, kWave) - u0 + 1;  // <= OPW
   uint32_t key = 0;
   int c = 0;
   if (l < span) {
@@ -109,10 +117,11 @@ __global__ void __launch_bounds__(kThreads) k_lookup(LookupBatch batch) {
   }
 }
 
-constexpr int kOccPerBlock = kWave * (kThreads / kWave);
-
 template <int VPR>
-int launch(const LookupBatch& b, hipStream_t stream) {
+int launch(LookupBatch b, hipStream_t stream) {
+  // the host built the block ranges for 64 occurrences per wave
+  constexpr int scale = kWave / LookupShape<VPR>::OPW;
+  for (int i = 0; i <= b.n; ++i) b.block_lo[i] *= scale;
   if (b.block_lo[b.n] == 0) return FS_OK;
   hipLaunchKernelGGL(k_lookup<VPR>, dim3((unsigned)b.block_lo[b.n]), dim3(kThreads), 0, stream,
                      b);
@@ -192,7 +201,7 @@ extern "C" int fs_jagged_lookup(const fs_table* tables, int32_t T, int32_t W,
       if (done[u] || vpr[u] != vpr[t]) continue;
       done[u] = true;
       b.t[b.n] = args[u];
-      b.block_lo[b.n + 1] = b.block_lo[b.n] + (int32_t)cdiv(n_tok, kOccPerBlock);
+      b.block_lo[b.n + 1] = b.block_lo[b.n] + (int32_t)cdiv(n_tok, kWave * (kThreads / kWave));
       ++b.n;
     }
     const int rc = launch_vpr(vpr[t], b, stream);
