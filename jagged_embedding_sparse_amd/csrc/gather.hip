@@ -33,10 +33,11 @@ struct LookupArgs {
   const uint8_t* cls;
   int32_t g_lo, g_hi;  // group range of the table: [t*W, (t+1)*W]
   int32_t which;
+  int32_t vpr;  // 16-byte vectors per row
 };
 
-// The tables of one row size share a launch: workgroups [lo_i, lo_{i+1}) copy
-// table i of the batch.
+// Every table of a call in one launch: workgroups [lo_t, lo_{t+1}) copy
+// table t.
 struct LookupBatch {
   LookupArgs t[FS_MAX_TABLES];
   int32_t block_lo[FS_MAX_TABLES + 1];
@@ -56,11 +57,7 @@ struct LookupShape {
 // copying lanes with cross-lane shuffles, so rows start loading after two
 // dependent index loads and up to 16 rows per lane group are in flight.
 template <int VPR>  // 16-byte vectors per row
-__global__ void __launch_bounds__(kThreads) k_lookup(LookupBatch batch) {
-  int ti = 0;
-  while (ti + 1 < batch.n && (int32_t)blockIdx.x >= batch.block_lo[ti + 1]) ++ti;
-  const LookupArgs& a = batch.t[ti];
-  const int64_t blk = (int64_t)blockIdx.x - batch.block_lo[ti];
+__device__ __forceinline__ void lookup_rows(const LookupArgs& a, int64_t blk) {
   constexpr int LPR = VPR < kWave ? VPR : kWave;  // lanes per row
   constexpr int RPW = kWave / LPR;                // rows per wave instruction
   constexpr int VPL = VPR / LPR;                  // vectors per lane
@@ -117,26 +114,31 @@ __global__ void __launch_bounds__(kThreads) k_lookup(LookupBatch batch) {
   }
 }
 
-template <int VPR>
-int launch(LookupBatch b, hipStream_t stream) {
-  // the host built the block ranges for 64 occurrences per wave
-  constexpr int scale = kWave / LookupShape<VPR>::OPW;
-  for (int i = 0; i <= b.n; ++i) b.block_lo[i] *= scale;
-  if (b.block_lo[b.n] == 0) return FS_OK;
-  hipLaunchKernelGGL(k_lookup<VPR>, dim3((unsigned)b.block_lo[b.n]), dim3(kThreads), 0, stream,
-                     b);
-  FS_LAUNCH_CHECK();
-  return FS_OK;
+// Each workgroup takes its table's row-size instance of the copy (all share
+// one register allocation: the largest instance needs 102 VGPRs).
+__global__ void __launch_bounds__(kThreads) k_lookup(LookupBatch batch) {
+  int ti = 0;
+  while (ti + 1 < batch.n && (int32_t)blockIdx.x >= batch.block_lo[ti + 1]) ++ti;
+  const LookupArgs& a = batch.t[ti];
+  const int64_t blk = (int64_t)blockIdx.x - batch.block_lo[ti];
+  switch (a.vpr) {
+    case 4: lookup_rows<4>(a, blk); break;
+    case 8: lookup_rows<8>(a, blk); break;
+    case 16: lookup_rows<16>(a, blk); break;
+    case 32: lookup_rows<32>(a, blk); break;
+    case 64: lookup_rows<64>(a, blk); break;
+    default: lookup_rows<128>(a, blk); break;
+  }
 }
 
-int launch_vpr(int vpr, const LookupBatch& b, hipStream_t stream) {
+int occ_per_wave(int vpr) {
   switch (vpr) {
-    case 4: return launch<4>(b, stream);
-    case 8: return launch<8>(b, stream);
-    case 16: return launch<16>(b, stream);
-    case 32: return launch<32>(b, stream);
-    case 64: return launch<64>(b, stream);
-    default: return launch<128>(b, stream);
+    case 4: return LookupShape<4>::OPW;
+    case 8: return LookupShape<8>::OPW;
+    case 16: return LookupShape<16>::OPW;
+    case 32: return LookupShape<32>::OPW;
+    case 64: return LookupShape<64>::OPW;
+    default: return LookupShape<128>::OPW;
   }
 }
 
@@ -168,13 +170,14 @@ extern "C" int fs_jagged_lookup(const fs_table* tables, int32_t T, int32_t W,
     base += tb.rows;
   }
   if (base > (int64_t)UINT32_MAX) return FS_ERR_UNSUPPORTED;
-  // one launch per row size, covering every table of that size
-  LookupArgs args[FS_MAX_TABLES];
-  int vpr[FS_MAX_TABLES];
+  // one launch for every table
+  LookupBatch b;
+  b.n = T;
+  b.block_lo[0] = 0;
   base = 0;
   for (int t = 0; t < T; ++t) {
     const fs_table& tb = tables[t];
-    LookupArgs& a = args[t];
+    LookupArgs& a = b.t[t];
     a.weights = (const char*)tb.weights;
     a.out = (char*)out[t];
     a.row_base = base;
@@ -188,24 +191,14 @@ extern "C" int fs_jagged_lookup(const fs_table* tables, int32_t T, int32_t W,
     a.g_lo = t * W;
     a.g_hi = (t + 1) * W;
     a.which = which;
+    a.vpr = (int32_t)(tb.dim * (tb.dtype == FS_F32 ? 4 : 2) / 16);
     base += tb.rows;
-    vpr[t] = (int)(tb.dim * (tb.dtype == FS_F32 ? 4 : 2) / 16);
+    const int64_t occ_per_block = (int64_t)occ_per_wave(a.vpr) * (kThreads / kWave);
+    b.block_lo[t + 1] = b.block_lo[t] + (int32_t)cdiv(n_tok, occ_per_block);
   }
-  bool done[FS_MAX_TABLES] = {};
-  for (int t = 0; t < T; ++t) {
-    if (done[t]) continue;
-    LookupBatch b;
-    b.n = 0;
-    b.block_lo[0] = 0;
-    for (int u = t; u < T; ++u) {
-      if (done[u] || vpr[u] != vpr[t]) continue;
-      done[u] = true;
-      b.t[b.n] = args[u];
-      b.block_lo[b.n + 1] = b.block_lo[b.n] + (int32_t)cdiv(n_tok, kWave * (kThreads / kWave));
-      ++b.n;
-    }
-    const int rc = launch_vpr(vpr[t], b, stream);
-    if (rc) return rc;
+  if (b.block_lo[T] > 0) {
+    hipLaunchKernelGGL(k_lookup, dim3((unsigned)b.block_lo[T]), dim3(kThreads), 0, stream, b);
+    FS_LAUNCH_CHECK();
   }
   return FS_OK;
 }
