@@ -135,41 +135,51 @@ k_place(const int32_t* __restrict__ len, int32_t n, int32_t W, int32_t q,
       rank_offsets[r] = r == W ? n : fbs_rank_start(r, n, W);
 }
 
-// VBS cuts: prefix sums S of the sorted weights, then for each rank r the
-// first k with W*S_k >= r*T (binary search; S is non-decreasing).
+// VBS cuts. With S_k the weight of the first k sorted samples (S_0 = 0,
+// S_n = T), rank r starts at the first k with W*S_k >= r*T. S does not
+// decrease, so the ranks starting at k+1 are exactly those with
+// W*S_k < r*T <= W*S_{k+1}: the thread that holds sample k writes them, and
+// the weight at every cut, without a search.
 constexpr int kCutThreads = 256;
 
 __global__ void __launch_bounds__(kCutThreads)
-k_vbs_cut(const int64_t* __restrict__ wsorted, int32_t n, int32_t W, int64_t* __restrict__ S,
+k_vbs_cut(const int64_t* __restrict__ wsorted, int32_t n, int32_t W,
           int32_t* __restrict__ rank_offsets, int64_t* __restrict__ rank_weight) {
   __shared__ int64_t tmp[17];
-  __shared__ int32_t cut[FS_MAX_RANKS + 1];
+  __shared__ int64_t scut[FS_MAX_RANKS + 1];  // S at each rank's first sample
   const int32_t per = (n + kCutThreads - 1) / kCutThreads;
   const int32_t k0 = min(n, (int32_t)threadIdx.x * per), k1 = min(n, k0 + per);
   int64_t local = 0;
   for (int32_t k = k0; k < k1; ++k) local += wsorted[k];
-  int64_t total;
-  int64_t run = block_excl_scan<int64_t>(local, tmp, &total);
-  for (int32_t k = k0; k < k1; ++k) {
-    S[k] = run;
-    run += wsorted[k];
-  }
-  if (threadIdx.x == 0) S[n] = total;
-  __syncthreads();
-  const int64_t T = total;
-  for (int32_t r = threadIdx.x; r <= W; r += kCutThreads) {
-    int32_t lo = 0, hi = n;  // answer in [0, n]
-    const int64_t goal = (int64_t)r * T;
-    while (lo < hi) {
-      int32_t mid = (lo + hi) >> 1;
-      if ((int64_t)W * S[mid] >= goal) hi = mid; else lo = mid + 1;
+  int64_t T;
+  int64_t run = block_excl_scan<int64_t>(local, tmp, &T);
+  if (T == 0) {  // no samples: every rank starts at 0, the last ends at n
+    for (int32_t r = threadIdx.x; r <= W; r += kCutThreads) {
+      rank_offsets[r] = r == W ? n : 0;
+      if (rank_weight && r < W) rank_weight[r] = 0;
     }
-    cut[r] = (r == W) ? n : lo;
-    rank_offsets[r] = cut[r];
+    return;
+  }
+  if (threadIdx.x == 0) {
+    rank_offsets[0] = 0;
+    rank_offsets[W] = n;
+    scut[0] = 0;
+    scut[W] = T;
+  }
+  for (int32_t k = k0; k < k1; ++k) {
+    const int64_t s1 = run + wsorted[k];  // S_{k+1}; run = S_k
+    // ranks r in [1, W-1] with r > W*S_k / T and r <= W*S_{k+1} / T
+    const int64_t r_lo = (int64_t)W * run / T + 1;
+    const int64_t r_hi = min((int64_t)W * s1 / T, (int64_t)W - 1);
+    for (int64_t r = r_lo; r <= r_hi; ++r) {
+      rank_offsets[r] = k + 1;
+      scut[r] = s1;
+    }
+    run = s1;
   }
   __syncthreads();
   if (rank_weight)
-    for (int32_t r = threadIdx.x; r < W; r += kCutThreads) rank_weight[r] = S[cut[r + 1]] - S[cut[r]];
+    for (int32_t r = threadIdx.x; r < W; r += kCutThreads) rank_weight[r] = scut[r + 1] - scut[r];
 }
 
 int check_common(const int32_t* uih_len, int32_t n, int32_t W, const int32_t* perm,
@@ -189,7 +199,6 @@ extern "C" size_t fs_balance_workspace_size(int32_t n, int32_t W) {
   const size_t m = (size_t)(n > 0 ? n : 1);
   Carve c(nullptr);
   c.take<int64_t>(m);                             // sorted weights
-  c.take<int64_t>(m + 1);                         // prefix sums
   c.take<int32_t>(m * (size_t)rank_slices(n));    // per-slice counts
   return c.used + 256;
 }
@@ -224,7 +233,6 @@ extern "C" int fs_balance_fbs(const int32_t* uih_len, int32_t n, int32_t W, int3
   if (!ws || ws_bytes < fs_balance_workspace_size(n, W)) return FS_ERR_WORKSPACE;
   Carve c(ws);
   c.take<int64_t>((size_t)(n > 0 ? n : 1));
-  c.take<int64_t>((size_t)(n > 0 ? n : 1) + 1);
   int32_t* cnt = c.take<int32_t>((size_t)(n > 0 ? n : 1) * (size_t)rank_slices(n));
   return launch_sort<true>(uih_len, n, W, perm, rank_offsets, nullptr, 0, 1, cnt, err, stream);
 }
@@ -241,12 +249,11 @@ extern "C" int fs_balance_vbs(const int32_t* uih_len, int32_t n, int32_t W, int3
   if (ws_bytes < fs_balance_workspace_size(n, W) || !ws) return FS_ERR_WORKSPACE;
   Carve c(ws);
   int64_t* wsorted = c.take<int64_t>((size_t)(n > 0 ? n : 1));
-  int64_t* S = c.take<int64_t>((size_t)(n > 0 ? n : 1) + 1);
   int32_t* cnt = c.take<int32_t>((size_t)(n > 0 ? n : 1) * (size_t)rank_slices(n));
   rc = launch_sort<false>(uih_len, n, W, perm, rank_offsets, wsorted, alpha_num, alpha_den, cnt,
                           err, stream);
   if (rc) return rc;
-  hipLaunchKernelGGL(k_vbs_cut, dim3(1), dim3(kCutThreads), 0, stream, wsorted, n, W, S,
+  hipLaunchKernelGGL(k_vbs_cut, dim3(1), dim3(kCutThreads), 0, stream, wsorted, n, W,
                      rank_offsets, rank_weight);
   FS_LAUNCH_CHECK();
   return FS_OK;

@@ -83,17 +83,19 @@ k_colscan(uint32_t* __restrict__ counts, int32_t ld, int32_t G, int32_t C,
 // in flight per lane), the waves' slice sums are combined in LDS, then each
 // wave rereads its slice and writes the exclusive prefixes.
 constexpr int kColOneRows = 1024;
-constexpr int kColBatch = 16;
+constexpr int kColBatch = 32;
 
 __global__ void __launch_bounds__(kColThreads)
 k_colscan1(uint32_t* __restrict__ counts, int32_t ld, int32_t G, int32_t C,
            uint32_t* __restrict__ tot) {
   __shared__ uint32_t wsum[kColThreads / kWave][kWave];
   constexpr int nw = kColThreads / kWave;
-  const int w = threadIdx.x / kWave, l = lane();
+  // the wave index made provably uniform: row addresses then live in scalar
+  // registers and each load needs only the lane's column offset
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), l = lane();
   const int32_t c = blockIdx.x * kWave + l;
   const bool on = c < C;
-  const int32_t cc = on ? c : C - 1;
+  const uint32_t cc = (uint32_t)(on ? c : C - 1);
   const int32_t per = (int32_t)cdiv(G, nw);
   const int32_t r0 = min(G, w * per), r1 = min(G, r0 + per);
   uint32_t s = 0;
@@ -101,7 +103,7 @@ k_colscan1(uint32_t* __restrict__ counts, int32_t ld, int32_t G, int32_t C,
     uint32_t v[kColBatch];
 #pragma unroll
     for (int i = 0; i < kColBatch; ++i)
-      v[i] = counts[(int64_t)min(rb + i, G - 1) * ld + cc];
+      v[i] = (counts + (int64_t)min(rb + i, G - 1) * ld)[cc];
 #pragma unroll
     for (int i = 0; i < kColBatch; ++i) s += rb + i < r1 ? v[i] : 0u;
   }
@@ -115,11 +117,11 @@ k_colscan1(uint32_t* __restrict__ counts, int32_t ld, int32_t G, int32_t C,
     uint32_t v[kColBatch];
 #pragma unroll
     for (int i = 0; i < kColBatch; ++i)
-      v[i] = counts[(int64_t)min(rb + i, G - 1) * ld + c];
+      v[i] = (counts + (int64_t)min(rb + i, G - 1) * ld)[cc];
 #pragma unroll
     for (int i = 0; i < kColBatch; ++i) {
       if (rb + i < r1) {
-        counts[(int64_t)(rb + i) * ld + c] = base;
+        (counts + (int64_t)(rb + i) * ld)[cc] = base;
         base += v[i];
       }
     }
