@@ -45,6 +45,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sync", action="store_true",
                     help="one-stream synchronous schedule (analysis: isolated kernel times)")
+    ap.add_argument("--lookup", choices=["auto", "split", "joined"], default="auto",
+                    help="exclusive-row lookup ahead of the update (split), one lookup after "
+                         "it (joined), or chosen from the first steps' timing (auto)")
     return ap.parse_args()
 
 
@@ -107,7 +110,7 @@ def main():
     grads_dev = [torch.from_numpy(g).cuda() for g in grads_host]
     log(f"gradients {cap} x {[s.dim for s in w.tables]} in {time.time() - t0:.1f}s")
 
-    step = SparseStep(w, weights, states, cap)
+    step = SparseStep(w, weights, states, cap, lookup=args.lookup)
     n_tok = [b["n_tok"] for b in host_batches]
     step.prologue(dev_batches[0])
     run_step = step.step_sync if args.sync else step.step
@@ -149,6 +152,7 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     step.timer = None
+    schedule = "sync" if args.sync else ("joined" if step.joined else "split")
     ms_total = ev0.elapsed_time(ev1)
     ms_step = ms_total / args.steps
     upd_ms = timer.ms()["update_all"]
@@ -262,7 +266,7 @@ def main():
             "global_batch": w.batch, "virtual_ranks": w.world, "tables": tables,
             "optimizer": w.optim, "ids_per_step": ids_timed / args.steps,
             "weights": sorted({t.dtype for t in w.tables}), "grad_accumulate": "f64",
-            "distinct_batches": NB},
+            "distinct_batches": NB, "schedule": schedule},
         "roofline": {
             "bound": "hbm", "achieved": dom_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": dom_gbps / HBM_PEAK_GBPS, "traffic": traffic,

@@ -21,6 +21,13 @@ wait exists across GPUs only because the collision split decides which
 gradients travel first), so the latency-bound index kernels overlap the
 bandwidth-bound update.
 
+When the update finishes before the index stages do, prefetching the
+exclusive rows gains nothing and the split costs a second pass over the
+occurrence indices; the lookup then runs once, for all rows, after the
+update ("joined"). `lookup="auto"` times its first steps with HIP events and
+keeps the split only if the update was still running when the index stages
+ended; "split" and "joined" fix the choice. All three give the same result.
+
 Buffers are allocated once at capacity; per-iteration state is double
 buffered. Every stream keeps the default priority.
 """
@@ -114,8 +121,14 @@ class IterState:
     out: list = field(default_factory=list)  # lookup output per table
 
 
+_LOOKUP_MODES = ("split", "joined", "auto")
+_CALIB_STEPS = 3  # steps timed by lookup="auto" before it decides
+
+
 class SparseStep:
-    def __init__(self, workload, weights, states, n_tok_cap, device=None):
+    def __init__(self, workload, weights, states, n_tok_cap, device=None, lookup="auto"):
+        if lookup not in _LOOKUP_MODES:
+            raise ValueError(f"lookup must be one of {_LOOKUP_MODES}, not {lookup!r}")
         self.w = workload
         self.W = workload.world
         self.T = len(weights)
@@ -144,6 +157,10 @@ class SparseStep:
         self.cur = None  # IterState of iteration i (already looked up)
         self.slot = 0
         self.timer = None  # optional StageTimer
+        self.lookup = lookup
+        self.joined = lookup == "joined"  # current choice
+        self._calib = []  # (start, update end, index end) event triples
+        self._calib_left = _CALIB_STEPS if lookup == "auto" else 0
 
     def _t(self, name, stream):
         """Context that brackets one C call with HIP events on its stream."""
@@ -227,12 +244,29 @@ class SparseStep:
         self.cur = st
         return st
 
+    def _decide(self):
+        """lookup="auto": once the calibration steps have run on the GPU, join
+        the lookups if the update ended before the index stages in most of
+        them. Checks events without waiting for them."""
+        if self._calib_left > 0 or not self._calib:
+            return
+        if not all(e.query() for trip in self._calib for e in trip):
+            return
+        ahead = [e0.elapsed_time(ei) - e0.elapsed_time(eu) for e0, eu, ei in self._calib]
+        self.joined = sum(a > 0 for a in ahead) * 2 > len(ahead)
+        self._calib = []
+
     def step(self, batch_next, grads_cur):
         """Prioritized step: update iteration i, look up iteration i+1."""
+        self._decide()
         cur = self.cur
         nxt = self.states_buf[1 - self.slot]
         sA, sB = self.sA, self.sB
         sA.wait_stream(torch.cuda.current_stream())  # inputs made on the caller's stream
+        calib = None
+        if self._calib_left > 0:
+            calib = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            calib[0].record(sA)
         # B may start once A has finished the previous step (iteration i's
         # index outputs and lookups; the slot A is about to overwrite is free)
         sB.wait_stream(sA)
@@ -241,10 +275,20 @@ class SparseStep:
                                       cur.uq, self.w.optim, self.w.lr, self.w.eps,
                                       which=lib.FS_ALL, ws=self.ws_red[1], stream=sB)
         self.ev_b.record(sB)
+        if calib:
+            calib[1].record(sB)
         self._index_stages(batch_next, nxt, cur, sA)
-        self._lookup(nxt, lib.FS_EXCLUSIVE, sA)
-        sA.wait_event(self.ev_b)
-        self._lookup(nxt, lib.FS_COLLISION, sA)
+        if calib:
+            calib[2].record(sA)
+            self._calib.append(tuple(calib))
+            self._calib_left -= 1
+        if self.joined:
+            sA.wait_event(self.ev_b)
+            self._lookup(nxt, lib.FS_ALL, sA)
+        else:
+            self._lookup(nxt, lib.FS_EXCLUSIVE, sA)
+            sA.wait_event(self.ev_b)
+            self._lookup(nxt, lib.FS_COLLISION, sA)
         self.cur = nxt
         self.slot = 1 - self.slot
         return nxt

@@ -137,3 +137,9 @@ def test_lookup_and_update_reject_unsupported_rows(L):
     tab = _tables(L, [(1000, 128, L.FS_F32, True)])
     assert ru(tab, 1, 4, grads, 10, FAKE, FAKE, FAKE, FAKE, FAKE, None, L.FS_ALL,
               L.FS_RW_ADAGRAD, 0.1, 0.0, None, FAKE, 8, None) == L.FS_ERR_WORKSPACE
+
+
+def test_step_rejects_unknown_lookup_schedule():
+    from jagged_embedding_sparse_amd.step import SparseStep
+    with pytest.raises(ValueError):
+        SparseStep(None, [], [], 1, lookup="eager")

@@ -192,17 +192,19 @@ def test_call_limits_full_step():
 
 @pytest.mark.parametrize("k", [2, 3])
 def test_prioritized_equals_synchronous(k):
-    """Two-stream prioritized schedule == one-stream synchronous, bit for bit."""
+    """Two-stream prioritized schedule (exclusive-row lookup ahead of the
+    update, one lookup after it, and the timed choice between them) ==
+    one-stream synchronous, bit for bit."""
     w = synth.workload(k)
-    K = 4
+    K = 5
     bt = synth.Batches(w, 50 + k)
     batches = [bt.batch(i) for i in range(K)]
     cap = max(b["n_tok"] for b in batches)
     runs = []
-    for mode in ("prio", "sync"):
+    for mode in ("split", "joined", "auto", "sync"):
         say("schedule", k, mode)
         weights, states = gpu_tables(w, 50 + k)
-        step = SparseStep(w, weights, states, cap)
+        step = SparseStep(w, weights, states, cap, lookup="split" if mode == "sync" else mode)
         st = step.prologue(to_dev(batches[0]))
         step.join()
         torch.cuda.synchronize()
@@ -212,7 +214,7 @@ def test_prioritized_equals_synchronous(k):
                 w, 50 + k, i, batches[i], host(st.perm), host(st.bucket["bal_offsets"]))]
             step.join()
             torch.cuda.synchronize()
-            st = (step.step if mode == "prio" else step.step_sync)(to_dev(batches[i + 1]), g)
+            st = (step.step_sync if mode == "sync" else step.step)(to_dev(batches[i + 1]), g)
             step.join()
             torch.cuda.synchronize()
             looks.append([_bits(o[:st.n_tok]).copy() for o in st.out])
@@ -220,9 +222,10 @@ def test_prioritized_equals_synchronous(k):
         final = [_bits(weights[t].index_select(0, torch.from_numpy(r).cuda()))
                  for t, r in enumerate(rows_t)]
         runs.append((looks, final))
-    (la, fa), (lb, fb) = runs
-    for x, y in zip(la, lb):
-        for a, b in zip(x, y):
+    (lb, fb) = runs[-1]
+    for la, fa in runs[:-1]:
+        for x, y in zip(la, lb):
+            for a, b in zip(x, y):
+                assert np.array_equal(a, b)
+        for a, b in zip(fa, fb):
             assert np.array_equal(a, b)
-    for a, b in zip(fa, fb):
-        assert np.array_equal(a, b)
