@@ -31,6 +31,10 @@ constexpr int kWaveItems = kWave * kRounds;
 constexpr int kTile = kThreads * kRounds;  // 2048
 constexpr int kMaxDigitBits = 10;
 constexpr int kMaxBins = 1 << kMaxDigitBits;  // also the count matrix's row length
+// fixed cost of a radix pass, in tiles: its three dependent launches take
+// about as long as streaming 400-500 tiles (measured: a pass over 432 tiles
+// ~30 us, of which ~15 us is the floor of three launches)
+constexpr int64_t kPassTiles = 512;
 
 struct Groups {
   int64_t row_base[FS_MAX_TABLES + 1];
@@ -733,15 +737,17 @@ extern "C" int fs_unique_collision_split(const int64_t* shard_keys, const int32_
   if (!ws || ws_bytes < fs_unique_workspace_size(n_cap, prev_cap, T, W)) return FS_ERR_WORKSPACE;
 
   // Sort inside the W shards (shard-local keys: fewer bits, so often one pass
-  // fewer) or over all items as one segment (local key = global key): one
-  // tile pass costs about its tile count, and the shard tiling adds up to one
+  // fewer) or over all items as one segment (local key = global key). A pass
+  // costs a fixed part (three dependent launches, about as long as streaming
+  // kPassTiles tiles) plus its tile count; the shard tiling adds up to one
   // partial tile per shard.
   int64_t span_w = 0, span_1 = base;
   for (int t = 0; t < T; ++t) span_w += g.block[t];
   const int64_t cap_tiles = cdiv(n_cap > 0 ? n_cap : 1, kTile);
   const int passes_w = (key_bits(span_w) + kMaxDigitBits - 1) / kMaxDigitBits;
   const int passes_1 = (key_bits(span_1) + kMaxDigitBits - 1) / kMaxDigitBits;
-  const bool by_shard = W > 1 && passes_w * (cap_tiles + W) < passes_1 * cap_tiles;
+  const bool by_shard = W > 1 && passes_w * (cap_tiles + W + kPassTiles) <
+                                     passes_1 * (cap_tiles + kPassTiles);
   const int32_t nseg = by_shard ? W : 1;
   SegKeys lk;
   lk.T = T;
