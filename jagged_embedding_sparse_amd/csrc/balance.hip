@@ -119,8 +119,13 @@ k_place(const int32_t* __restrict__ len, int32_t n, int32_t W, int32_t q,
         int32_t* __restrict__ rank_offsets, int64_t* __restrict__ wsorted, int anum, int aden) {
   const int32_t s = blockIdx.x * kRankThreads + threadIdx.x;
   if (s < n) {
+    // the q slice counts, all loads in flight at once
+    int32_t v[kMaxSlices];
+#pragma unroll
+    for (int32_t y = 0; y < kMaxSlices; ++y) v[y] = y < q ? cnt[(int64_t)y * n + s] : 0;
     int32_t p = 0;
-    for (int32_t y = 0; y < q; ++y) p += cnt[(int64_t)y * n + s];
+#pragma unroll
+    for (int32_t y = 0; y < kMaxSlices; ++y) p += v[y];
     if (kFbs) {
       int32_t round = p / W, off = p % W;
       int32_t r = (round % 2 == 0) ? off : (W - 1 - off);
@@ -141,6 +146,7 @@ k_place(const int32_t* __restrict__ len, int32_t n, int32_t W, int32_t q,
 // W*S_k < r*T <= W*S_{k+1}: the thread that holds sample k writes them, and
 // the weight at every cut, without a search.
 constexpr int kCutThreads = 256;
+constexpr int kCutBatch = 16;
 
 __global__ void __launch_bounds__(kCutThreads)
 k_vbs_cut(const int64_t* __restrict__ wsorted, int32_t n, int32_t W,
@@ -149,8 +155,16 @@ k_vbs_cut(const int64_t* __restrict__ wsorted, int32_t n, int32_t W,
   __shared__ int64_t scut[FS_MAX_RANKS + 1];  // S at each rank's first sample
   const int32_t per = (n + kCutThreads - 1) / kCutThreads;
   const int32_t k0 = min(n, (int32_t)threadIdx.x * per), k1 = min(n, k0 + per);
+  // a thread's weights in batches of kCutBatch independent loads (one
+  // memory round trip per batch, not per sample)
   int64_t local = 0;
-  for (int32_t k = k0; k < k1; ++k) local += wsorted[k];
+  for (int32_t kb = k0; kb < k1; kb += kCutBatch) {
+    int64_t v[kCutBatch];
+#pragma unroll
+    for (int i = 0; i < kCutBatch; ++i) v[i] = kb + i < k1 ? wsorted[kb + i] : 0;
+#pragma unroll
+    for (int i = 0; i < kCutBatch; ++i) local += v[i];
+  }
   int64_t T;
   int64_t run = block_excl_scan<int64_t>(local, tmp, &T);
   if (T == 0) {  // no samples: every rank starts at 0, the last ends at n
@@ -166,16 +180,22 @@ k_vbs_cut(const int64_t* __restrict__ wsorted, int32_t n, int32_t W,
     scut[0] = 0;
     scut[W] = T;
   }
-  for (int32_t k = k0; k < k1; ++k) {
-    const int64_t s1 = run + wsorted[k];  // S_{k+1}; run = S_k
-    // ranks r in [1, W-1] with r > W*S_k / T and r <= W*S_{k+1} / T
-    const int64_t r_lo = (int64_t)W * run / T + 1;
-    const int64_t r_hi = min((int64_t)W * s1 / T, (int64_t)W - 1);
-    for (int64_t r = r_lo; r <= r_hi; ++r) {
-      rank_offsets[r] = k + 1;
-      scut[r] = s1;
+  for (int32_t kb = k0; kb < k1; kb += kCutBatch) {
+    int64_t v[kCutBatch];
+#pragma unroll
+    for (int i = 0; i < kCutBatch; ++i) v[i] = kb + i < k1 ? wsorted[kb + i] : 0;
+    for (int i = 0; i < kCutBatch && kb + i < k1; ++i) {
+      const int32_t k = kb + i;
+      const int64_t s1 = run + v[i];  // S_{k+1}; run = S_k
+      // ranks r in [1, W-1] with r > W*S_k / T and r <= W*S_{k+1} / T
+      const int64_t r_lo = (int64_t)W * run / T + 1;
+      const int64_t r_hi = min((int64_t)W * s1 / T, (int64_t)W - 1);
+      for (int64_t r = r_lo; r <= r_hi; ++r) {
+        rank_offsets[r] = k + 1;
+        scut[r] = s1;
+      }
+      run = s1;
     }
-    run = s1;
   }
   __syncthreads();
   if (rank_weight)
