@@ -8,10 +8,11 @@
 //
 // The shard-major order (shard d, source rank r, table t, balanced sample q,
 // token j) is a stable counting sort by d of the items enumerated in (r, t,
-// q, j) order. Items are cut into tiles of 2048 tokens that never straddle a
-// (rank, table) segment and are numbered in (r, t, chunk) order, so an
-// item's output position is its shard's base, plus the shard's count in all
-// earlier tiles, plus its stable rank inside its tile:
+// q, j) order. Each (rank, table) segment is cut into chunks of 512 tokens,
+// one per wave; a tile is four consecutive chunks of one rank (several tables
+// share a tile when their segments are short), numbered in (r, t, chunk)
+// order, so an item's output position is its shard's base, plus the shard's
+// count in all earlier tiles, plus its stable rank inside its tile:
 //   k_lens, k_bal, k_tiles   balanced offsets, per-sample shifts, tile
 //              descriptors (short dependent-load chains)
 //   k_hist     per-tile shard histograms -> rows of a tiles x shards matrix;
@@ -49,11 +50,17 @@ struct TableRows {
 
 constexpr uint32_t kDropKey = 0xFFFFFFFFu;  // item key of a dropped ID (keys < 2^32 - 1)
 
+constexpr int kTileWaves = kThreads / kWave;
+// one-launch column scan up to this many tile rows: the scan stops at the
+// tiles in use, which several tables leave well below the launch bound
+constexpr int32_t kColOneRowsUsed = 1536;
+
+// A tile: one chunk of at most kWaveItems tokens per wave, all of one rank.
 struct TileDesc {
-  int64_t bm_lo;       // first batch-major token
-  int32_t n;           // tokens (<= kTile)
-  int32_t seg;         // r * T + t
-  int32_t q_lo, q_hi;  // rank r's balanced samples
+  int64_t bm_lo[kTileWaves];  // each chunk's first batch-major token
+  int32_t n[kTileWaves];      // each chunk's tokens (0: the wave has none)
+  int32_t t[kTileWaves];      // each chunk's table
+  int32_t q_lo, q_hi;         // the rank's balanced samples
   int32_t pad[2];
 };
 
@@ -159,8 +166,9 @@ k_tiles(int32_t n, int64_t n_tok, int32_t n_len_blocks, const int64_t* __restric
     bal[n] = ok ? total : 0;
     if (!ok && err) atomicOr(err, FS_EF_SHAPE);
   }
-  // rank r owns T * ceil(m_r / kTile) tiles, t-major (bal[n] is read only
-  // through ranks that end at n, where it equals total)
+  // rank r's T segments of m_r tokens make T * ceil(m_r / kWaveItems)
+  // chunks, t-major, and ceil(chunks / 4) tiles (bal[n] is read only through
+  // ranks that end at n, where it equals total)
   int64_t A[kPrepRanks], m[kPrepRanks];
   int32_t c[kPrepRanks];
   int32_t mine = 0;
@@ -173,9 +181,9 @@ k_tiles(int32_t n, int64_t n_tok, int32_t n_len_blocks, const int64_t* __restric
     if (ok && r < W) {
       A[k] = ro_v[k] < n ? bal[ro_v[k]] : total;
       m[k] = (ro_v[k + 1] < n ? bal[ro_v[k + 1]] : total) - A[k];
-      c[k] = (int32_t)cdiv(m[k], kTile);
+      c[k] = (int32_t)cdiv((int64_t)T * cdiv(m[k], kWaveItems), kTileWaves);
     }
-    mine += T * c[k];
+    mine += c[k];
   }
   int32_t ttot;
   int32_t pref = block_excl_scan<int32_t>(mine, tmp32, &ttot);
@@ -194,7 +202,7 @@ k_tiles(int32_t n, int64_t n_tok, int32_t n_len_blocks, const int64_t* __restric
       s_q[r] = ro_v[k];
       if (r == W - 1) s_q[W] = ro_v[k + 1];
     }
-    pref += T * c[k];
+    pref += c[k];
   }
   __syncthreads();
   // the tile table, all threads over all tiles: tile u belongs to the last
@@ -205,12 +213,20 @@ k_tiles(int32_t n, int64_t n_tok, int32_t n_len_blocks, const int64_t* __restric
       const int32_t mid = (a + b) >> 1;
       if (s_pref[mid] <= u) a = mid; else b = mid;
     }
-    const int32_t c_r = (int32_t)cdiv(s_m[a], kTile);  // > 0: rank a owns tile u
-    const int32_t i = u - s_pref[a], t = i / c_r, kk = i % c_r;
+    // rank a owns tile u (it has tokens): chunk c of the rank is chunk
+    // c % cpt of table c / cpt
+    const int32_t cpt = (int32_t)cdiv(s_m[a], kWaveItems);
+    const int32_t i = u - s_pref[a];
     TileDesc d;
-    d.bm_lo = s_A[a] + (int64_t)kk * kTile;
-    d.n = (int32_t)min((int64_t)kTile, s_m[a] - (int64_t)kk * kTile);
-    d.seg = a * T + t;
+#pragma unroll
+    for (int w = 0; w < kTileWaves; ++w) {
+      const int32_t ch = i * kTileWaves + w;
+      const int32_t t = ch / cpt, kk = ch % cpt;
+      const bool on = t < T;
+      d.bm_lo[w] = s_A[a] + (on ? (int64_t)kk * kWaveItems : 0);
+      d.n[w] = on ? (int32_t)min((int64_t)kWaveItems, s_m[a] - (int64_t)kk * kWaveItems) : 0;
+      d.t[w] = on ? t : 0;
+    }
     d.q_lo = s_q[a];
     d.q_hi = s_q[a + 1];
     d.pad[0] = d.pad[1] = 0;
@@ -219,28 +235,29 @@ k_tiles(int32_t n, int64_t n_tok, int32_t n_len_blocks, const int64_t* __restric
 }
 
 // ---------------------------------------------------------------- tiles
+// One wave's chunk of a tile.
 struct TileInfo {
-  int32_t r, t;
-  int64_t bm_lo, bm_hi;  // this tile's batch-major token range
-  int32_t q_lo, q_hi;    // rank r's balanced samples
+  int32_t t;
+  int64_t bm_lo, bm_hi;  // the chunk's batch-major token range (table t)
+  int32_t q_lo, q_hi;    // the rank's balanced samples
 };
 
-__device__ __forceinline__ bool tile_info(int32_t tile, const int32_t* tile_pref, int32_t W,
-                                          int32_t T, const TileDesc* tiles, TileInfo& ti) {
+__device__ __forceinline__ bool tile_info(int32_t tile, int w, const int32_t* tile_pref,
+                                          int32_t W, const TileDesc* tiles, TileInfo& ti) {
   if (tile >= tile_pref[W]) return false;
-  const TileDesc d = tiles[tile];
-  ti.r = d.seg / T;
-  ti.t = d.seg % T;
-  ti.bm_lo = d.bm_lo;
-  ti.bm_hi = d.bm_lo + d.n;
+  const TileDesc& d = tiles[tile];
+  ti.t = d.t[w];
+  ti.bm_lo = d.bm_lo[w];
+  ti.bm_hi = d.bm_lo[w] + d.n[w];
   ti.q_lo = d.q_lo;
   ti.q_hi = d.q_hi;
   return true;
 }
 
-// Loads one wave's kRounds rounds of 64 consecutive tokens of a tile (table t,
-// batch-major positions bm) and returns, per round and lane, the item's key
-// and bin (shard, -1 for a dropped ID, `sentinel` past the tile's end).
+// Loads one wave's kRounds rounds of 64 consecutive tokens of its chunk
+// (table t, batch-major positions bm) and returns, per round and lane, the
+// item's key and bin (shard, -1 for a dropped ID, `sentinel` past the
+// chunk's end).
 //
 // The wave finds the balanced sample of its first token with one cooperative
 // search, then loads a window of 64 samples: their end offsets and shifts
@@ -269,11 +286,11 @@ __device__ __forceinline__ Window load_window(int32_t qa, int32_t q_hi, const in
   return win;
 }
 
-__device__ __forceinline__ void wave_items(const TileInfo& ti, int32_t w, const int64_t* ids,
+__device__ __forceinline__ void wave_items(const TileInfo& ti, const int64_t* ids,
                                            const int64_t* shift, const int64_t* bal,
                                            int64_t n_tok, const TableRows& tr, int32_t sentinel,
                                            uint32_t (&key)[kRounds], int32_t (&bin)[kRounds]) {
-  const int64_t first = ti.bm_lo + (int64_t)w * kWaveItems;
+  const int64_t first = ti.bm_lo;
 #pragma unroll
   for (int i = 0; i < kRounds; ++i) {
     key[i] = 0;
@@ -344,13 +361,14 @@ k_hist(const int64_t* __restrict__ ids, int64_t n_tok, const int64_t* __restrict
   for (int b = threadIdx.x; b <= W; b += kThreads) h[b] = 0;
   __syncthreads();
   TileInfo ti;
-  if (tile_info(tile, tile_pref, W, T, tiles, ti)) {
+  // the wave index made provably uniform: the chunk's fields load into scalar registers
+  if (tile_info(tile, __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), tile_pref, W, tiles,
+                ti)) {
     const int32_t sentinel = (1 << nbits) - 1;  // > W: lanes without an item
-    const int32_t w = threadIdx.x / kWave;
     uint32_t key[kRounds];
     int32_t bin[kRounds];
-    wave_items(ti, w, ids, shift, bal, n_tok, tr, sentinel, key, bin);
-    uint32_t* out = ikey + (int64_t)ti.t * n_tok + ti.bm_lo + (int64_t)w * kWaveItems + lane();
+    wave_items(ti, ids, shift, bal, n_tok, tr, sentinel, key, bin);
+    uint32_t* out = ikey + (int64_t)ti.t * n_tok + ti.bm_lo + lane();
     bool dropped_any = false;
 #pragma unroll
     for (int i = 0; i < kRounds; ++i) {
@@ -439,7 +457,8 @@ __device__ __forceinline__ void bin_bases(const uint32_t* tot, int32_t W, int64_
 
 // Splits workgroup (x, y): ranks [64x, 64x + 64) x shards [64y, 64y + 64) of
 // splits[d][r] = (scanned count of shard d at rank r + 1's first tile) -
-// (at rank r's first tile); rows past the matrix read the column totals.
+// (at rank r's first tile); rows past the tiles in use read the column
+// totals.
 // Workgroup (0, 0) also writes shard_offsets (entry W: the valid items;
 // dropped IDs follow it).
 __device__ __forceinline__ void splits_part(int32_t x, int32_t y, const uint32_t* counts,
@@ -457,13 +476,14 @@ __device__ __forceinline__ void splits_part(int32_t x, int32_t y, const uint32_t
     }
   }
   const int32_t d = y * kWave + l;
+  const int32_t used = min(G, tile_pref[W]);  // the column scan rewrote only these rows
   for (int rl = w; rl < kWave; rl += kThreads / kWave) {
     const int32_t r = x * kWave + rl;
     int32_t val = 0;  // items of one rank for one shard: fewer than 2^31
     if (r < W && d < W) {
       const int32_t a = tile_pref[r], z = tile_pref[r + 1];
-      const uint32_t va = a < G ? counts[(int64_t)a * ld + d] : tot[d];
-      const uint32_t vz = z < G ? counts[(int64_t)z * ld + d] : tot[d];
+      const uint32_t va = a < used ? counts[(int64_t)a * ld + d] : tot[d];
+      const uint32_t vz = z < used ? counts[(int64_t)z * ld + d] : tot[d];
       val = (int32_t)(vz - va);
     }
     tr[rl * (kWave + 1) + l] = val;
@@ -497,10 +517,10 @@ k_scatter(const uint32_t* __restrict__ ikey, int64_t n_tok, const int32_t* __res
     return;
   }
   const int32_t tile = xcd_tile(blockIdx.x, G);
+  const int32_t w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // provably uniform
   TileInfo ti;
-  if (!tile_info(tile, tile_pref, W, T, tiles, ti)) return;  // uniform per workgroup
+  if (!tile_info(tile, w, tile_pref, W, tiles, ti)) return;  // uniform per workgroup
   const int32_t nb = W + 1;
-  const int32_t w = threadIdx.x / kWave;
   {
     int64_t base[kBinPer];
     bin_bases(tot, W, tmp, base);
@@ -520,7 +540,7 @@ k_scatter(const uint32_t* __restrict__ ikey, int64_t n_tok, const int32_t* __res
   const int t = ti.t;
   const uint32_t rbase = (uint32_t)tr.row_base[t];
   const DivU32 div = tr.div[t];
-  const int64_t first = ti.bm_lo + (int64_t)w * kWaveItems;
+  const int64_t first = ti.bm_lo;
   const uint32_t* in = ikey + (int64_t)t * n_tok + first + lane();
   uint32_t key[kRounds];
   int32_t bin[kRounds];
@@ -544,6 +564,7 @@ k_scatter(const uint32_t* __restrict__ ikey, int64_t n_tok, const int32_t* __res
   }
   __syncthreads();
   // per shard: exclusive prefix over the waves, then the shards' starts in the tile
+  int m;  // the tile's items
   {
     uint32_t tb[kPer];
     int64_t local = 0;
@@ -564,6 +585,7 @@ k_scatter(const uint32_t* __restrict__ ikey, int64_t n_tok, const int32_t* __res
     }
     int64_t all;
     int64_t r0 = block_excl_scan<int64_t>(local, tmp, &all);
+    m = (int)all;
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
       const int b = threadIdx.x * kPer + k;
@@ -582,7 +604,6 @@ k_scatter(const uint32_t* __restrict__ ikey, int64_t n_tok, const int32_t* __res
     L.sbin[p] = (uint16_t)b;
   }
   __syncthreads();
-  const int m = (int)(ti.bm_hi - ti.bm_lo);
   for (int p = threadIdx.x; p < m; p += kThreads) {
     const int b = L.sbin[p];
     const int64_t pos = (int64_t)L.run[b] + (p - (int)L.tbin[b]);
@@ -591,10 +612,14 @@ k_scatter(const uint32_t* __restrict__ ikey, int64_t n_tok, const int32_t* __res
   }
 }
 
-// tiles the launches cover: an upper bound on sum_r T * ceil(m_r / kTile),
+// tiles the launches cover: sum_r ceil(T * ceil(m_r / 512) / 4) with
+// sum_r m_r = n_tok is at most (T * n_tok + W * (511 T + 1536)) / 2048,
 // rounded up to a multiple of the XCD count
 int32_t grid_tiles(int64_t n_tok, int32_t T, int32_t W) {
-  return (int32_t)align_up((size_t)(T * (cdiv(n_tok, kTile) + W)), kXcd);
+  const int64_t b = ((int64_t)T * n_tok +
+                     (int64_t)W * ((kWaveItems - 1) * T + (kTileWaves - 1) * kWaveItems)) /
+                    ((int64_t)kTileWaves * kWaveItems);
+  return (int32_t)align_up((size_t)(b > 0 ? b : 1), kXcd);
 }
 
 }  // namespace
@@ -679,7 +704,9 @@ extern "C" int fs_bucketize_permute(const int64_t* ids, int64_t n_tok,
   hipLaunchKernelGGL(k_hist, dim3(G), dim3(kThreads), 0, stream, ids, n_tok, shift, bal_offsets,
                      tile_pref, tiles, tr, W, T, nbits, counts, ld, ikey, err);
   FS_LAUNCH_CHECK();
-  int rc = launch_colscan(counts, ld, G, W + 1, part, tot, stream);
+  // rows past the tiles in use (tile_pref[W], known on the device) stay zero
+  int rc = launch_colscan(counts, ld, G, W + 1, part, tot, stream, tile_pref + W,
+                          kColOneRowsUsed);
   if (rc) return rc;
   const size_t lds = scatter_lds_bytes(W + 1, nullptr, nullptr);
   hipLaunchKernelGGL(k_scatter, dim3((unsigned)(G + split_blocks)), dim3(kThreads), lds, stream,

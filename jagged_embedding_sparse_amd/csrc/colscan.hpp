@@ -5,6 +5,9 @@
 // (column groups of 64): k_colsum stores each row block's column sums,
 // k_colscan adds the sums of the row blocks before its own and rewrites the
 // rows as exclusive prefixes. Small matrices: one launch (k_colscan1).
+// A caller that knows on the device how many leading rows are in use passes
+// that count (g_used, nullable): rows past it are all zero, so they are
+// neither read nor rewritten.
 #pragma once
 
 #include "common.hpp"
@@ -18,8 +21,9 @@ constexpr int kColBlockRows = kColRows * (kColThreads / kWave);
 
 __global__ void __launch_bounds__(kColThreads)
 k_colsum(const uint32_t* __restrict__ counts, int32_t ld, int32_t G, int32_t C,
-         uint32_t* __restrict__ part) {
+         uint32_t* __restrict__ part, const int32_t* __restrict__ g_used) {
   __shared__ uint32_t wsum[kColThreads / kWave][kWave];
+  if (g_used) G = max(1, min(G, *g_used));
   const int w = threadIdx.x / kWave, l = lane();
   const int32_t c = blockIdx.y * kWave + l;
   const int32_t r0 = blockIdx.x * kColBlockRows + w * kColRows;
@@ -41,8 +45,10 @@ k_colsum(const uint32_t* __restrict__ counts, int32_t ld, int32_t G, int32_t C,
 // counts[r][c] <- sum of counts[r'][c] over r' < r; tot[c] <- column total.
 __global__ void __launch_bounds__(kColThreads)
 k_colscan(uint32_t* __restrict__ counts, int32_t ld, int32_t G, int32_t C,
-          const uint32_t* __restrict__ part, uint32_t* __restrict__ tot) {
+          const uint32_t* __restrict__ part, uint32_t* __restrict__ tot,
+          const int32_t* __restrict__ g_used) {
   __shared__ uint32_t wsum[kColThreads / kWave][kWave];
+  if (g_used) G = max(1, min(G, *g_used));
   const int w = threadIdx.x / kWave, l = lane();
   const int32_t c = blockIdx.y * kWave + l;
   const int32_t r0 = blockIdx.x * kColBlockRows + w * kColRows;
@@ -87,8 +93,9 @@ constexpr int kColBatch = 32;
 
 __global__ void __launch_bounds__(kColThreads)
 k_colscan1(uint32_t* __restrict__ counts, int32_t ld, int32_t G, int32_t C,
-           uint32_t* __restrict__ tot) {
+           uint32_t* __restrict__ tot, const int32_t* __restrict__ g_used) {
   __shared__ uint32_t wsum[kColThreads / kWave][kWave];
+  if (g_used) G = min(G, *g_used);
   constexpr int nw = kColThreads / kWave;
   // the wave index made provably uniform: row addresses then live in scalar
   // registers and each load needs only the lane's column offset
@@ -129,20 +136,23 @@ k_colscan1(uint32_t* __restrict__ counts, int32_t ld, int32_t G, int32_t C,
 }
 
 // The column scan of a G x C matrix with leading dimension ld: one launch
-// for small G, else block sums then prefixes; part holds cdiv(G, 128) * ld
-// entries, tot C.
+// when G <= one_rows, else block sums then prefixes; part holds
+// cdiv(G, 128) * ld entries, tot C. g_used: see above.
 inline int launch_colscan(uint32_t* counts, int32_t ld, int32_t G, int32_t C, uint32_t* part,
-                          uint32_t* tot, hipStream_t stream) {
-  if (G <= kColOneRows) {
+                          uint32_t* tot, hipStream_t stream, const int32_t* g_used = nullptr,
+                          int32_t one_rows = kColOneRows) {
+  if (G <= one_rows) {
     hipLaunchKernelGGL(k_colscan1, dim3((unsigned)cdiv(C, kWave)), dim3(kColThreads), 0, stream,
-                       counts, ld, G, C, tot);
+                       counts, ld, G, C, tot, g_used);
     FS_LAUNCH_CHECK();
     return FS_OK;
   }
   const dim3 grid((unsigned)cdiv(G, kColBlockRows), (unsigned)cdiv(C, kWave));
-  hipLaunchKernelGGL(k_colsum, grid, dim3(kColThreads), 0, stream, counts, ld, G, C, part);
+  hipLaunchKernelGGL(k_colsum, grid, dim3(kColThreads), 0, stream, counts, ld, G, C, part,
+                     g_used);
   FS_LAUNCH_CHECK();
-  hipLaunchKernelGGL(k_colscan, grid, dim3(kColThreads), 0, stream, counts, ld, G, C, part, tot);
+  hipLaunchKernelGGL(k_colscan, grid, dim3(kColThreads), 0, stream, counts, ld, G, C, part, tot,
+                     g_used);
   FS_LAUNCH_CHECK();
   return FS_OK;
 }
