@@ -48,6 +48,9 @@ def parse():
     ap.add_argument("--lookup", choices=["auto", "split", "joined"], default="auto",
                     help="exclusive-row lookup ahead of the update (split), one lookup after "
                          "it (joined), or chosen from the first steps' timing (auto)")
+    ap.add_argument("--lookahead", type=int, choices=[1, 2], default=2,
+                    help="iterations the index stages run ahead of the lookup (2: beside the "
+                         "update and the lookup of the iteration before)")
     return ap.parse_args()
 
 
@@ -110,14 +113,23 @@ def main():
     grads_dev = [torch.from_numpy(g).cuda() for g in grads_host]
     log(f"gradients {cap} x {[s.dim for s in w.tables]} in {time.time() - t0:.1f}s")
 
-    step = SparseStep(w, weights, states, cap, lookup=args.lookup)
+    ahead = args.lookahead == 2 and not args.sync
+    step = SparseStep(w, weights, states, cap, lookup=args.lookup,
+                      lookahead=2 if ahead else 1)
     n_tok = [b["n_tok"] for b in host_batches]
-    step.prologue(dev_batches[0])
-    run_step = step.step_sync if args.sync else step.step
+    step.prologue(dev_batches[0], batch_after=dev_batches[1 % NB] if ahead else None)
+    if args.sync:
+        def run_step(batch_next, grads, k_next):
+            return step.step_sync(batch_next, grads)
+    else:
+        def run_step(batch_next, grads, k_next):
+            # with lookahead 2 the step also indexes the batch after next
+            return step.step(batch_next, grads,
+                             batch_after=dev_batches[(k_next + 1) % NB] if ahead else None)
     k = 0
     for _ in range(args.warmup):
         k += 1
-        run_step(dev_batches[k % NB], [g[:n_tok[(k - 1) % NB]] for g in grads_dev])
+        run_step(dev_batches[k % NB], [g[:n_tok[(k - 1) % NB]] for g in grads_dev], k)
     step.join()
     torch.cuda.synchronize()
 
@@ -144,7 +156,7 @@ def main():
     for _ in range(args.steps):
         p = k % NB
         k += 1
-        run_step(dev_batches[k % NB], [g[:n_tok[p]] for g in grads_dev])
+        run_step(dev_batches[k % NB], [g[:n_tok[p]] for g in grads_dev], k)
         pairs.append(p)
         ids_timed += n_tok[k % NB] * len(w.tables)
     ev1.record(step.sA)
@@ -152,7 +164,8 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     step.timer = None
-    schedule = "sync" if args.sync else ("joined" if step.joined else "split")
+    schedule = ("sync" if args.sync else "index two ahead, joined lookup" if ahead else
+                ("joined" if step.joined else "split"))
     ms_total = ev0.elapsed_time(ev1)
     ms_step = ms_total / args.steps
     upd_ms = timer.ms()["update_all"]
@@ -164,7 +177,7 @@ def main():
     for _ in range(n_brk):
         p = k % NB
         k += 1
-        run_step(dev_batches[k % NB], [g[:n_tok[p]] for g in grads_dev])
+        run_step(dev_batches[k % NB], [g[:n_tok[p]] for g in grads_dev], k)
     step.join()
     torch.cuda.synchronize()
     step.timer = None
@@ -178,7 +191,7 @@ def main():
         p = k % NB
         k += 1
         prev = step.cur
-        nxt = run_step(dev_batches[k % NB], [g[:n_tok[p]] for g in grads_dev])
+        nxt = run_step(dev_batches[k % NB], [g[:n_tok[p]] for g in grads_dev], k)
         step.join()
         torch.cuda.synchronize()
         T, W = len(w.tables), w.world

@@ -28,6 +28,18 @@ update ("joined"). `lookup="auto"` times its first steps with HIP events and
 keeps the split only if the update was still running when the index stages
 ended; "split" and "joined" fix the choice. All three give the same result.
 
+The index stages depend on nothing but the IDs (and the previous
+iteration's unique rows), so with `lookahead=2` they run one more iteration
+ahead, on the prefetched batch after next:
+
+  stream B  update(i) -> lookup(i+1, every row)   [index(i+1) done last step]
+  stream A  balance(i+2) -> bucketize(i+2) -> split(i+2 vs i+1)
+
+The latency-bound index kernels then overlap both bandwidth-bound stages
+instead of only the update. Three iteration states are alive at once (i being
+updated, i+1 looked up, i+2 indexed); the result is again the synchronous
+loop's.
+
 Buffers are allocated once at capacity; per-iteration state is double
 buffered. Every stream keeps the default priority.
 """
@@ -126,9 +138,12 @@ _CALIB_STEPS = 3  # steps timed by lookup="auto" before it decides
 
 
 class SparseStep:
-    def __init__(self, workload, weights, states, n_tok_cap, device=None, lookup="auto"):
+    def __init__(self, workload, weights, states, n_tok_cap, device=None, lookup="auto",
+                 lookahead=1):
         if lookup not in _LOOKUP_MODES:
             raise ValueError(f"lookup must be one of {_LOOKUP_MODES}, not {lookup!r}")
+        if lookahead not in (1, 2):
+            raise ValueError(f"lookahead must be 1 or 2, not {lookahead!r}")
         self.w = workload
         self.W = workload.world
         self.T = len(weights)
@@ -149,18 +164,22 @@ class SparseStep:
                                  device=d)
         rws = lib.reduce_workspace_size(cap, max(self.dims))
         self.ws_red = [torch.empty(rws, dtype=torch.uint8, device=d) for _ in range(2)]
-        self.states_buf = [self._alloc_iter() for _ in range(2)]
+        self.lookahead = lookahead
+        self.states_buf = [self._alloc_iter() for _ in range(lookahead + 1)]
         self.sA = torch.cuda.Stream(device=d)
         self.sB = torch.cuda.Stream(device=d)
-        self.ev_split = torch.cuda.Event()
         self.ev_b = torch.cuda.Event()
+        self.ev_idx = torch.cuda.Event()  # index stages of the iteration after i done
+        self.ev_upd = torch.cuda.Event()  # the last update done (its state slot is free)
+        self._pre = False  # lookahead=2: the iteration after i already indexed
         self.cur = None  # IterState of iteration i (already looked up)
         self.slot = 0
         self.timer = None  # optional StageTimer
         self.lookup = lookup
-        self.joined = lookup == "joined"  # current choice
+        # current choice (lookahead=2 always looks every row up after the update)
+        self.joined = lookup == "joined" or lookahead == 2
         self._calib = []  # (start, update end, index end) event triples
-        self._calib_left = _CALIB_STEPS if lookup == "auto" else 0
+        self._calib_left = _CALIB_STEPS if (lookup == "auto" and lookahead == 1) else 0
 
     def _t(self, name, stream):
         """Context that brackets one C call with HIP events on its stream."""
@@ -235,13 +254,23 @@ class SparseStep:
                                       cls=st.cls_next, ws=ws, stream=stream)
 
     # ------------------------------------------------------------------ schedule
-    def prologue(self, batch):
-        """Index stages + full lookup of the first iteration."""
+    def _nslots(self):
+        return len(self.states_buf)
+
+    def prologue(self, batch, batch_after=None):
+        """Index stages + full lookup of the first iteration; with
+        lookahead=2 and `batch_after`, also the index stages of the second."""
         st = self.states_buf[self.slot]
         self.sA.wait_stream(torch.cuda.current_stream())
         self._index_stages(batch, st, None, self.sA)
         self._lookup(st, lib.FS_ALL, self.sA)
         self.cur = st
+        self._pre = False
+        if self.lookahead == 2 and batch_after is not None:
+            nxt = self.states_buf[(self.slot + 1) % self._nslots()]
+            self._index_stages(batch_after, nxt, st, self.sA)
+            self.ev_idx.record(self.sA)
+            self._pre = True
         return st
 
     def _decide(self):
@@ -256,8 +285,11 @@ class SparseStep:
         self.joined = sum(a > 0 for a in ahead) * 2 > len(ahead)
         self._calib = []
 
-    def step(self, batch_next, grads_cur):
-        """Prioritized step: update iteration i, look up iteration i+1."""
+    def step(self, batch_next, grads_cur, batch_after=None):
+        """Prioritized step: update iteration i, look up iteration i+1 (and,
+        with lookahead=2, index `batch_after`, iteration i+2)."""
+        if self.lookahead == 2:
+            return self._step_ahead(batch_next, grads_cur, batch_after)
         self._decide()
         cur = self.cur
         nxt = self.states_buf[1 - self.slot]
@@ -293,12 +325,47 @@ class SparseStep:
         self.slot = 1 - self.slot
         return nxt
 
+    def _step_ahead(self, batch_next, grads_cur, batch_after):
+        cur = self.cur
+        n = self._nslots()
+        nxt = self.states_buf[(self.slot + 1) % n]
+        sA, sB = self.sA, self.sB
+        cs = torch.cuda.current_stream()
+        sA.wait_stream(cs)  # batches made on the caller's stream
+        sB.wait_stream(cs)  # gradients made on the caller's stream
+        # stream A may overwrite the slot of iteration i-1 once its update
+        # (the previous step's, on B) is done; enqueued before ev_upd is
+        # recorded again below
+        sA.wait_event(self.ev_upd)
+        if not self._pre:  # iteration i+1 was not indexed ahead: index it now
+            self._index_stages(batch_next, nxt, cur, sA)
+            self.ev_idx.record(sA)
+        sB.wait_event(self.ev_idx)
+        with self._t("update_all", sB):
+            lib.fs_grad_reduce_update(self.weights, self.states, self.W, grads_cur, cur.n_tok,
+                                      cur.uq, self.w.optim, self.w.lr, self.w.eps,
+                                      which=lib.FS_ALL, ws=self.ws_red[1], stream=sB)
+        self.ev_upd.record(sB)
+        self._lookup(nxt, lib.FS_ALL, sB)
+        self._pre = False
+        if batch_after is not None:
+            aft = self.states_buf[(self.slot + 2) % n]
+            self._index_stages(batch_after, aft, nxt, sA)
+            self.ev_idx.record(sA)
+            self._pre = True
+        self.cur = nxt
+        self.slot = (self.slot + 1) % n
+        return nxt
+
     def step_sync(self, batch_next, grads_cur):
         """Reference schedule on one stream: update all of i, then look up all of i+1."""
+        if self._pre:
+            raise RuntimeError("step_sync after a step that indexed its batch_after")
         cur = self.cur
-        nxt = self.states_buf[1 - self.slot]
+        nxt = self.states_buf[(self.slot + 1) % self._nslots()]
         sA = self.sA
         sA.wait_stream(torch.cuda.current_stream())
+        sA.wait_stream(self.sB)
         self._index_stages(batch_next, nxt, cur, sA)
         with self._t("update_all", sA):
             lib.fs_grad_reduce_update(self.weights, self.states, self.W, grads_cur, cur.n_tok,
@@ -306,16 +373,18 @@ class SparseStep:
                                       which=lib.FS_ALL, ws=self.ws_red[0], stream=sA)
         self._lookup(nxt, lib.FS_ALL, sA)
         self.cur = nxt
-        self.slot = 1 - self.slot
+        self.slot = (self.slot + 1) % self._nslots()
         return nxt
 
     def epilogue(self, grads_last):
         """Update of the last iteration (no lookahead: every row exclusive)."""
         cur = self.cur
         self.sA.wait_stream(torch.cuda.current_stream())
+        self.sA.wait_stream(self.sB)
         lib.fs_grad_reduce_update(self.weights, self.states, self.W, grads_last, cur.n_tok,
                                   cur.uq, self.w.optim, self.w.lr, self.w.eps, which=lib.FS_ALL,
                                   ws=self.ws_red[0], stream=self.sA)
 
     def join(self):
         torch.cuda.current_stream().wait_stream(self.sA)
+        torch.cuda.current_stream().wait_stream(self.sB)

@@ -143,3 +143,5 @@ def test_step_rejects_unknown_lookup_schedule():
     from jagged_embedding_sparse_amd.step import SparseStep
     with pytest.raises(ValueError):
         SparseStep(None, [], [], 1, lookup="eager")
+    with pytest.raises(ValueError):
+        SparseStep(None, [], [], 1, lookahead=3)

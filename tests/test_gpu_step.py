@@ -193,37 +193,48 @@ def test_call_limits_full_step():
 @pytest.mark.parametrize("k", [2, 3])
 def test_prioritized_equals_synchronous(k):
     """Two-stream prioritized schedule (exclusive-row lookup ahead of the
-    update, one lookup after it, and the timed choice between them) ==
-    one-stream synchronous, bit for bit."""
+    update, one lookup after it, the timed choice between them, and index
+    stages two iterations ahead) == one-stream synchronous, bit for bit.
+    The synchronous run comes first and fixes the gradients; the two-stream
+    runs then go through all steps without a host synchronisation, copying
+    each lookup on the caller's stream, so the streams really overlap."""
     w = synth.workload(k)
     K = 5
     bt = synth.Batches(w, 50 + k)
     batches = [bt.batch(i) for i in range(K)]
+    dev_b = [to_dev(b) for b in batches]
     cap = max(b["n_tok"] for b in batches)
     runs = []
-    for mode in ("split", "joined", "auto", "sync"):
+    grads = []
+    for mode in ("sync", "split", "joined", "auto", "ahead"):
         say("schedule", k, mode)
         weights, states = gpu_tables(w, 50 + k)
-        step = SparseStep(w, weights, states, cap, lookup="split" if mode == "sync" else mode)
-        st = step.prologue(to_dev(batches[0]))
+        ahead = mode == "ahead"
+        step = SparseStep(w, weights, states, cap,
+                          lookup="split" if mode in ("sync", "ahead") else mode,
+                          lookahead=2 if ahead else 1)
+        st = step.prologue(dev_b[0], batch_after=dev_b[1] if ahead else None)
         step.join()
-        torch.cuda.synchronize()
-        looks = [[_bits(o[:st.n_tok]).copy() for o in st.out]]
+        looks = [[o[:st.n_tok].clone() for o in st.out]]
         for i in range(K - 1):
-            g = [torch.from_numpy(x).cuda() for x in balanced_grads(
-                w, 50 + k, i, batches[i], host(st.perm), host(st.bucket["bal_offsets"]))]
+            if mode == "sync":
+                torch.cuda.synchronize()
+                grads.append([torch.from_numpy(x).cuda() for x in balanced_grads(
+                    w, 50 + k, i, batches[i], host(st.perm), host(st.bucket["bal_offsets"]))])
+                st = step.step_sync(dev_b[i + 1], grads[i])
+            else:
+                after = dev_b[i + 2] if ahead and i + 2 < K else None
+                st = step.step(dev_b[i + 1], grads[i], batch_after=after)
             step.join()
-            torch.cuda.synchronize()
-            st = (step.step_sync if mode == "sync" else step.step)(to_dev(batches[i + 1]), g)
-            step.join()
-            torch.cuda.synchronize()
-            looks.append([_bits(o[:st.n_tok]).copy() for o in st.out])
+            looks.append([o[:st.n_tok].clone() for o in st.out])
+        torch.cuda.synchronize()
+        looks = [[_bits(o).copy() for o in x] for x in looks]
         rows_t = touched_rows(batches, w)
         final = [_bits(weights[t].index_select(0, torch.from_numpy(r).cuda()))
                  for t, r in enumerate(rows_t)]
         runs.append((looks, final))
-    (lb, fb) = runs[-1]
-    for la, fa in runs[:-1]:
+    (lb, fb) = runs[0]
+    for la, fa in runs[1:]:
         for x, y in zip(la, lb):
             for a, b in zip(x, y):
                 assert np.array_equal(a, b)
