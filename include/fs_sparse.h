@@ -241,8 +241,11 @@ int fs_jagged_lookup(const fs_table* tables, int32_t T, int32_t W, const int64_t
 /*               next split call's prev_cls (NULL with which == FS_ALL).      */
 /*  reduced_out  host [T] of device fp32 [U_t][dim_t] (or NULL array / NULL   */
 /*               entries): row u of table t is written at u - unique_offsets[t*W]. */
-/* dim_t must be a multiple of 64 in [64, 1024] (else FS_ERR_UNSUPPORTED);    */
+/* dim_t must be 64, 128, 256, 512 or 1024 (else FS_ERR_UNSUPPORTED);        */
 /* FS_RW_ADAGRAD needs every table's state.                                   */
+/*  ws, ws_bytes  at least fs_grad_reduce_update_workspace_size(n_tok,       */
+/*               max dim_t) bytes (fp64 partial sums of rows longer than a   */
+/*               chunk), else FS_ERR_WORKSPACE.                               */
 int fs_grad_reduce_update(const fs_table* tables, int32_t T, int32_t W,
                           const float* const* grad, int64_t n_tok, const int64_t* unique,
                           const int64_t* unique_offsets, const int32_t* seg_offsets,
