@@ -152,15 +152,18 @@ def main():
     ids_timed = 0
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
-    ev0.record(step.sA)
+    # both events on the caller's stream: the steps' streams wait for it at
+    # the start of each step, and it waits for both of them at the end
+    ev0.record()
     for _ in range(args.steps):
         p = k % NB
         k += 1
         run_step(dev_batches[k % NB], [g[:n_tok[p]] for g in grads_dev], k)
         pairs.append(p)
         ids_timed += n_tok[k % NB] * len(w.tables)
-    ev1.record(step.sA)
+    submit = time.perf_counter() - wall0
     step.join()
+    ev1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     step.timer = None
@@ -169,7 +172,8 @@ def main():
     ms_total = ev0.elapsed_time(ev1)
     ms_step = ms_total / args.steps
     upd_ms = timer.ms()["update_all"]
-    log(f"timed {args.steps} steps: {ms_total:.3f} ms (wall {wall * 1e3:.3f} ms)")
+    log(f"timed {args.steps} steps: {ms_total:.3f} ms (wall {wall * 1e3:.3f} ms, host "
+        f"submission {submit * 1e3:.3f} ms)")
 
     # ---------------------------------------------------------------- stage breakdown
     brk = StageTimer(capacity=8 * n_brk, streams=(step.sA, step.sB))
