@@ -32,8 +32,8 @@ The index stages depend on nothing but the IDs (and the previous
 iteration's unique rows), so with `lookahead=2` they run one more iteration
 ahead, on the prefetched batch after next:
 
-  stream B  update(i) -> lookup(i+1, every row)   [index(i+1) done last step]
-  stream A  balance(i+2) -> bucketize(i+2) -> split(i+2 vs i+1)
+  caller's stream  update(i) -> lookup(i+1, every row)  [index(i+1) done last step]
+  stream A         balance(i+2) -> bucketize(i+2) -> split(i+2 vs i+1)
 
 The latency-bound index kernels then overlap both bandwidth-bound stages
 instead of only the update. Three iteration states are alive at once (i being
@@ -170,7 +170,6 @@ class SparseStep:
         self.sB = torch.cuda.Stream(device=d)
         self.ev_b = torch.cuda.Event()
         self.ev_idx = torch.cuda.Event()  # index stages of the iteration after i done
-        self.ev_upd = torch.cuda.Event()  # the last update done (its state slot is free)
         self._pre = False  # lookahead=2: the iteration after i already indexed
         self.cur = None  # IterState of iteration i (already looked up)
         self.slot = 0
@@ -326,27 +325,27 @@ class SparseStep:
         return nxt
 
     def _step_ahead(self, batch_next, grads_cur, batch_after):
+        # The update and the lookup run on the caller's stream (its inputs are
+        # there, and so are the lookup results it reads next); stream A runs the
+        # index stages. Each stream wait costs the host ~15 us, so there are two.
         cur = self.cur
         n = self._nslots()
         nxt = self.states_buf[(self.slot + 1) % n]
-        sA, sB = self.sA, self.sB
+        sA = self.sA
         cs = torch.cuda.current_stream()
-        sA.wait_stream(cs)  # batches made on the caller's stream
-        sB.wait_stream(cs)  # gradients made on the caller's stream
-        # stream A may overwrite the slot of iteration i-1 once its update
-        # (the previous step's, on B) is done; enqueued before ev_upd is
-        # recorded again below
-        sA.wait_event(self.ev_upd)
+        # stream A after everything enqueued so far on the caller's stream: the
+        # batches, and the update of i-1, whose state slot the index stages of
+        # i+2 overwrite; enqueued before this step's update, so they overlap it
+        sA.wait_stream(cs)
         if not self._pre:  # iteration i+1 was not indexed ahead: index it now
             self._index_stages(batch_next, nxt, cur, sA)
             self.ev_idx.record(sA)
-        sB.wait_event(self.ev_idx)
-        with self._t("update_all", sB):
+        cs.wait_event(self.ev_idx)
+        with self._t("update_all", cs):
             lib.fs_grad_reduce_update(self.weights, self.states, self.W, grads_cur, cur.n_tok,
                                       cur.uq, self.w.optim, self.w.lr, self.w.eps,
-                                      which=lib.FS_ALL, ws=self.ws_red[1], stream=sB)
-        self.ev_upd.record(sB)
-        self._lookup(nxt, lib.FS_ALL, sB)
+                                      which=lib.FS_ALL, ws=self.ws_red[1], stream=cs)
+        self._lookup(nxt, lib.FS_ALL, cs)
         self._pre = False
         if batch_after is not None:
             aft = self.states_buf[(self.slot + 2) % n]
