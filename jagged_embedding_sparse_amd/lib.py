@@ -275,3 +275,89 @@ def fs_grad_reduce_update(weights, states, W, grads, n_tok, uq, optim, lr, eps=0
                      _ptr(uq["occ_uid"]), _ptr(cls) if which != FS_ALL else None, which,
                      FS_RW_ADAGRAD if optim in ("rw_adagrad", FS_RW_ADAGRAD) else FS_SGD,
                      float(lr), float(eps), red, _ptr(ws), ws.numel(), _stream(stream)))
+
+
+# ---------------------------------------------------------------------------- prepared calls
+
+
+class Prepared:
+    """One C call marshalled once for fixed buffers: only the arguments named
+    in `var` change between calls (raw values: pointers as ints, counts, the
+    stream handle), and `arrays` holds host pointer arrays the caller refills
+    in place. For a loop that issues the same call on the same buffers many
+    times, where the per-call marshalling of the wrappers above would cost
+    more host time than the launches."""
+
+    __slots__ = ("name", "fn", "args", "pos", "arrays")
+
+    def __init__(self, name, fn, args, var, arrays=None):
+        self.name, self.fn, self.args = name, fn, list(args)
+        self.pos = dict(var)
+        self.arrays = arrays or {}
+
+    def __call__(self, **kw):
+        a = self.args
+        for k, v in kw.items():
+            a[self.pos[k]] = v
+        rc = self.fn(*a)
+        if rc != FS_OK:
+            raise FsError(self.name, rc)
+
+
+def prepare_balance(balancer, W, alpha, perm, rank_offsets, rank_weight, err, ws):
+    """fs_balance_fbs / fs_balance_vbs; call with uih=, n=, stream=."""
+    if balancer == "fbs":
+        args = [None, 0, W, _ptr(perm), _ptr(rank_offsets), _ptr(err), _ptr(ws), ws.numel(), None]
+        return Prepared("fs_balance_fbs", _c_balance_fbs, args, dict(uih=0, n=1, stream=8))
+    args = [None, 0, W, int(alpha[0]), int(alpha[1]), _ptr(perm), _ptr(rank_offsets),
+            _ptr(rank_weight), _ptr(err), _ptr(ws), ws.numel(), None]
+    return Prepared("fs_balance_vbs", _c_balance_vbs, args, dict(uih=0, n=1, stream=11))
+
+
+def prepare_bucketize(rows, perm, rank_offsets, W, out, err, ws):
+    """fs_bucketize_permute into `out` (the dict fs_bucketize_permute returns);
+    call with ids=, n_tok=, so=, n=, stream=."""
+    tabs = make_row_tables(rows)
+    args = [None, 0, None, 0, tabs, len(rows), _ptr(perm), _ptr(rank_offsets), W,
+            _ptr(out["bal_offsets"]), _ptr(out["shard_keys"]), _ptr(out["shard_bm"]),
+            _ptr(out["splits"]), _ptr(out["shard_offsets"]), _ptr(err), _ptr(ws), ws.numel(), None]
+    return Prepared("fs_bucketize_permute", _c_bucketize, args,
+                    dict(ids=0, n_tok=1, so=2, n=3, stream=17))
+
+
+def prepare_unique(bucket, rows, W, uq, prev_uq, prev_cls, ws):
+    """fs_unique_collision_split of `bucket` into `uq` against `prev_uq` (None:
+    first iteration); call with n_cap=, prev_cap=, stream=."""
+    tabs = make_row_tables(rows)
+    has = prev_uq is not None
+    args = [_ptr(bucket["shard_keys"]), _ptr(bucket["shard_bm"]), _ptr(bucket["shard_offsets"]),
+            0, tabs, len(rows), W, _ptr(prev_uq["unique"]) if has else None,
+            _ptr(prev_uq["counts"]) if has else None, 0, _ptr(uq["unique"]),
+            _ptr(uq["unique_offsets"]), _ptr(uq["seg_offsets"]), _ptr(uq["occ_bm"]),
+            _ptr(uq["occ_uid"]), _ptr(uq["cls"]), _ptr(prev_cls) if has else None,
+            _ptr(uq["counts"]), _ptr(ws), ws.numel(), None]
+    return Prepared("fs_unique_collision_split", _c_unique, args,
+                    dict(n_cap=3, prev_cap=9, stream=20))
+
+
+def prepare_lookup(weights, W, uq, out, which=FS_ALL, cls=None):
+    """fs_jagged_lookup into the tensors `out` (one per table, at least n_tok
+    rows); call with n_tok=, stream=."""
+    args = [make_tables(weights), len(weights), W, _ptr(uq["unique"]),
+            _ptr(uq["unique_offsets"]), _ptr(uq["seg_offsets"]), _ptr(uq["occ_bm"]),
+            _ptr(uq["occ_uid"]), _ptr(cls) if which != FS_ALL else None, which, _ptr_array(out),
+            0, None]
+    return Prepared("fs_jagged_lookup", _c_lookup, args, dict(n_tok=11, stream=12))
+
+
+def prepare_update(weights, states, W, uq, optim, lr, eps, which, cls, ws):
+    """fs_grad_reduce_update with the gradient pointers in arrays["grads"]
+    (set them before each call); call with n_tok=, stream=."""
+    grads = (C.c_void_p * len(weights))()
+    args = [make_tables(weights, states), len(weights), W, grads, 0, _ptr(uq["unique"]),
+            _ptr(uq["unique_offsets"]), _ptr(uq["seg_offsets"]), _ptr(uq["occ_bm"]),
+            _ptr(uq["occ_uid"]), _ptr(cls) if which != FS_ALL else None, which,
+            FS_RW_ADAGRAD if optim in ("rw_adagrad", FS_RW_ADAGRAD) else FS_SGD, float(lr),
+            float(eps), None, _ptr(ws), ws.numel(), None]
+    return Prepared("fs_grad_reduce_update", _c_reduce, args, dict(n_tok=4, stream=18),
+                    arrays=dict(grads=grads))

@@ -124,6 +124,7 @@ class IterState:
     """Everything one iteration's index stages produce (device tensors)."""
 
     n_tok: int = 0
+    slot: int = -1  # index among the step's iteration states
     perm: torch.Tensor = None
     rank_offsets: torch.Tensor = None
     rank_weight: torch.Tensor = None
@@ -166,6 +167,9 @@ class SparseStep:
         self.ws_red = [torch.empty(rws, dtype=torch.uint8, device=d) for _ in range(2)]
         self.lookahead = lookahead
         self.states_buf = [self._alloc_iter() for _ in range(lookahead + 1)]
+        for i, st in enumerate(self.states_buf):
+            st.slot = i
+        self._calls = {}  # prepared C calls by (stage, slots, ...)
         self.sA = torch.cuda.Stream(device=d)
         self.sB = torch.cuda.Stream(device=d)
         self.ev_b = torch.cuda.Event()
@@ -212,45 +216,57 @@ class SparseStep:
         return st
 
     # ------------------------------------------------------------------ stages
+    # Every call goes through a C call prepared once per state slot (the
+    # buffers never move): the generic wrappers' marshalling costs tens of us
+    # of host time per call, which on small batches would set the pace.
+    def _prep(self, key, make):
+        c = self._calls.get(key)
+        if c is None:
+            c = self._calls[key] = make()
+        return c
+
     def _index_stages(self, batch, st, prev, stream):
         """balance + bucketize + split of `batch` (device dict) into st."""
         W, T = self.W, self.T
-        n_tok = int(batch["ids"].shape[1])
+        ids, so, uih = batch["ids"], batch["sample_offsets"], batch["uih_len"]
+        n_tok = int(ids.shape[1])
         st.n_tok = n_tok
+        sh = stream.cuda_stream
+        pb = self._prep(("bal", st.slot), lambda: lib.prepare_balance(
+            self.w.balancer, W, self.w.alpha, st.perm, st.rank_offsets, st.rank_weight, self.err,
+            self.ws_bal))
+        pk = self._prep(("bkt", st.slot), lambda: lib.prepare_bucketize(
+            self.rows, st.perm, st.rank_offsets, W, st.bucket, self.err, self.ws_bkt))
+        pu = self._prep(("uq", st.slot, prev.slot if prev is not None else -1),
+                        lambda: lib.prepare_unique(
+                            st.bucket, self.rows, W, st.uq,
+                            prev.uq if prev is not None else None,
+                            prev.cls_next if prev is not None else None, self.ws_uq))
         with self._t("balance", stream):
-            if self.w.balancer == "fbs":
-                lib.fs_balance_fbs(batch["uih_len"], W, st.perm, st.rank_offsets, err=self.err,
-                                   ws=self.ws_bal, stream=stream)
-            else:
-                lib.fs_balance_vbs(batch["uih_len"], W, self.w.alpha, st.perm, st.rank_offsets,
-                                   st.rank_weight, err=self.err, ws=self.ws_bal, stream=stream)
+            pb(uih=lib._ptr(uih), n=uih.numel(), stream=sh)
         with self._t("bucketize", stream):
-            lib.fs_bucketize_permute(batch["ids"], batch["sample_offsets"], self.rows, st.perm,
-                                     st.rank_offsets, W, out=st.bucket, err=self.err,
-                                     ws=self.ws_bkt, stream=stream)
-        out = dict(st.uq)
-        if prev is not None:
-            out["prev_cls"] = prev.cls_next
+            pk(ids=lib._ptr(ids), n_tok=n_tok, so=lib._ptr(so), n=so.numel() - 1, stream=sh)
         with self._t("unique_split", stream):
-            lib.fs_unique_collision_split(
-                st.bucket["shard_keys"], st.bucket["shard_bm"], st.bucket["shard_offsets"],
-                T * n_tok, self.rows, W,
-                prev_unique=prev.uq["unique"] if prev is not None else None,
-                prev_counts=prev.uq["counts"] if prev is not None else None,
-                prev_cap=T * prev.n_tok if prev is not None else 0, out=out, ws=self.ws_uq,
-                stream=stream)
+            pu(n_cap=T * n_tok, prev_cap=T * prev.n_tok if prev is not None else 0, stream=sh)
 
     def _lookup(self, st, which, stream):
-        outs = [o[:st.n_tok] for o in st.out]
+        pl = self._prep(("lk", st.slot, which), lambda: lib.prepare_lookup(
+            self.weights, self.W, st.uq, st.out, which, st.uq["cls"]))
         with self._t(f"lookup_{_CLS[which]}", stream):
-            lib.fs_jagged_lookup(self.weights, self.W, st.uq, st.n_tok, which=which,
-                                 cls=st.uq["cls"], out=outs, stream=stream)
+            pl(n_tok=st.n_tok, stream=stream.cuda_stream)
+
+    def _run_update(self, st, grads, which, ws, stream, name=None):
+        pu = self._prep(("upd", st.slot, which, id(ws)), lambda: lib.prepare_update(
+            self.weights, self.states, self.W, st.uq, self.w.optim, self.w.lr, self.w.eps, which,
+            st.cls_next, ws))
+        g = pu.arrays["grads"]
+        for t, x in enumerate(grads):
+            g[t] = lib._ptr(x)
+        with self._t(name or f"update_{_CLS[which]}", stream):
+            pu(n_tok=st.n_tok, stream=stream.cuda_stream)
 
     def _update(self, st, grads, which, stream, ws):
-        with self._t(f"update_{_CLS[which]}", stream):
-            lib.fs_grad_reduce_update(self.weights, self.states, self.W, grads, st.n_tok, st.uq,
-                                      self.w.optim, self.w.lr, self.w.eps, which=which,
-                                      cls=st.cls_next, ws=ws, stream=stream)
+        self._run_update(st, grads, which, ws, stream)
 
     # ------------------------------------------------------------------ schedule
     def _nslots(self):
@@ -301,10 +317,7 @@ class SparseStep:
         # B may start once A has finished the previous step (iteration i's
         # index outputs and lookups; the slot A is about to overwrite is free)
         sB.wait_stream(sA)
-        with self._t("update_all", sB):
-            lib.fs_grad_reduce_update(self.weights, self.states, self.W, grads_cur, cur.n_tok,
-                                      cur.uq, self.w.optim, self.w.lr, self.w.eps,
-                                      which=lib.FS_ALL, ws=self.ws_red[1], stream=sB)
+        self._run_update(cur, grads_cur, lib.FS_ALL, self.ws_red[1], sB)
         self.ev_b.record(sB)
         if calib:
             calib[1].record(sB)
@@ -341,10 +354,7 @@ class SparseStep:
             self._index_stages(batch_next, nxt, cur, sA)
             self.ev_idx.record(sA)
         cs.wait_event(self.ev_idx)
-        with self._t("update_all", cs):
-            lib.fs_grad_reduce_update(self.weights, self.states, self.W, grads_cur, cur.n_tok,
-                                      cur.uq, self.w.optim, self.w.lr, self.w.eps,
-                                      which=lib.FS_ALL, ws=self.ws_red[1], stream=cs)
+        self._run_update(cur, grads_cur, lib.FS_ALL, self.ws_red[1], cs)
         self._lookup(nxt, lib.FS_ALL, cs)
         self._pre = False
         if batch_after is not None:
@@ -366,10 +376,7 @@ class SparseStep:
         sA.wait_stream(torch.cuda.current_stream())
         sA.wait_stream(self.sB)
         self._index_stages(batch_next, nxt, cur, sA)
-        with self._t("update_all", sA):
-            lib.fs_grad_reduce_update(self.weights, self.states, self.W, grads_cur, cur.n_tok,
-                                      cur.uq, self.w.optim, self.w.lr, self.w.eps,
-                                      which=lib.FS_ALL, ws=self.ws_red[0], stream=sA)
+        self._run_update(cur, grads_cur, lib.FS_ALL, self.ws_red[0], sA)
         self._lookup(nxt, lib.FS_ALL, sA)
         self.cur = nxt
         self.slot = (self.slot + 1) % self._nslots()
@@ -380,9 +387,7 @@ class SparseStep:
         cur = self.cur
         self.sA.wait_stream(torch.cuda.current_stream())
         self.sA.wait_stream(self.sB)
-        lib.fs_grad_reduce_update(self.weights, self.states, self.W, grads_last, cur.n_tok,
-                                  cur.uq, self.w.optim, self.w.lr, self.w.eps, which=lib.FS_ALL,
-                                  ws=self.ws_red[0], stream=self.sA)
+        self._run_update(cur, grads_last, lib.FS_ALL, self.ws_red[0], self.sA)
 
     def join(self):
         torch.cuda.current_stream().wait_stream(self.sA)
