@@ -265,9 +265,6 @@ class SparseStep:
         with self._t(name or f"update_{_CLS[which]}", stream):
             pu(n_tok=st.n_tok, stream=stream.cuda_stream)
 
-    def _update(self, st, grads, which, stream, ws):
-        self._run_update(st, grads, which, ws, stream)
-
     # ------------------------------------------------------------------ schedule
     def _nslots(self):
         return len(self.states_buf)
