@@ -135,21 +135,19 @@ k_bal(int32_t n, const int32_t* __restrict__ lens, const int32_t* __restrict__ b
   }
 }
 
-__global__ void __launch_bounds__(kPrepThreads)
-k_tiles(int32_t n, int64_t n_tok, int32_t n_len_blocks, const int64_t* __restrict__ bsum,
-        const int32_t* __restrict__ flags, const int32_t* __restrict__ ro, int32_t W, int32_t T,
-        int64_t* __restrict__ bal, int32_t* __restrict__ tile_pref,
-        TileDesc* __restrict__ tiles, int32_t* __restrict__ err) {
+// The tile table (one workgroup): rank offsets validated, ranks' token
+// ranges from bal, tiles per rank and their descriptors. `part` is this
+// thread's share of the token count and `bad` its input-check verdict; bal
+// holds the balanced offsets of samples 0..n-1 (bal[n] is written here).
+__device__ __forceinline__ void tile_table(int32_t n, int64_t n_tok, bool bad, int64_t part,
+                                           const int32_t* __restrict__ ro, int32_t W, int32_t T,
+                                           int64_t* __restrict__ bal,
+                                           int32_t* __restrict__ tile_pref,
+                                           TileDesc* __restrict__ tiles, int32_t* __restrict__ err) {
   __shared__ int64_t tmp64[17];
   __shared__ int32_t tmp32[17];
   __shared__ int64_t s_A[FS_MAX_RANKS], s_m[FS_MAX_RANKS];
   __shared__ int32_t s_pref[FS_MAX_RANKS + 1], s_q[FS_MAX_RANKS + 1];
-  bool bad = false;
-  int64_t part = 0;
-  for (int32_t k = threadIdx.x; k < n_len_blocks; k += kPrepThreads) {
-    bad |= flags[k] != 0;
-    part += bsum[k];
-  }
   int32_t ro_v[kPrepRanks + 1];
 #pragma unroll
   for (int k = 0; k <= kPrepRanks; ++k) {
@@ -232,6 +230,73 @@ k_tiles(int32_t n, int64_t n_tok, int32_t n_len_blocks, const int64_t* __restric
     d.pad[0] = d.pad[1] = 0;
     tiles[u] = d;
   }
+}
+
+__global__ void __launch_bounds__(kPrepThreads)
+k_tiles(int32_t n, int64_t n_tok, int32_t n_len_blocks, const int64_t* __restrict__ bsum,
+        const int32_t* __restrict__ flags, const int32_t* __restrict__ ro, int32_t W, int32_t T,
+        int64_t* __restrict__ bal, int32_t* __restrict__ tile_pref,
+        TileDesc* __restrict__ tiles, int32_t* __restrict__ err) {
+  bool bad = false;
+  int64_t part = 0;
+  for (int32_t k = threadIdx.x; k < n_len_blocks; k += kPrepThreads) {
+    bad |= flags[k] != 0;
+    part += bsum[k];
+  }
+  tile_table(n, n_tok, bad, part, ro, W, T, bal, tile_pref, tiles, err);
+}
+
+// Batches of at most kPrepThreads * P samples: the three prep steps in one
+// workgroup (each launch on the index path waits for wave slots beside the
+// update, so two fewer launches save more than the one workgroup costs).
+// Thread i owns samples iP .. iP + P - 1: their lengths and first tokens under
+// perm (all loads in flight), then bal and shift from one workgroup scan.
+template <int P>
+__global__ void __launch_bounds__(kPrepThreads)
+k_prep1(const int64_t* __restrict__ so, int32_t n, int64_t n_tok,
+        const int32_t* __restrict__ perm, const int32_t* __restrict__ ro, int32_t W, int32_t T,
+        int64_t* __restrict__ bal, int64_t* __restrict__ shift, int32_t* __restrict__ tile_pref,
+        TileDesc* __restrict__ tiles, int32_t* __restrict__ err) {
+  __shared__ int64_t tmp[17];
+  const int32_t q0 = threadIdx.x * P;
+  bool bad = false;
+  int32_t pv[P];
+#pragma unroll
+  for (int k = 0; k < P; ++k) pv[k] = q0 + k < n ? perm[q0 + k] : 0;
+  int64_t beg[P], len[P];
+#pragma unroll
+  for (int k = 0; k < P; ++k) {
+    const bool on = q0 + k < n;
+    const bool pin = pv[k] >= 0 && pv[k] < n;
+    bad |= on && !pin;
+    beg[k] = (on && pin) ? so[pv[k]] : 0;
+    len[k] = (on && pin) ? so[pv[k] + 1] - beg[k] : 0;
+  }
+  // the sample offsets rise from 0 to n_tok: this thread checks so[q0 .. q0 + P]
+  int64_t sv[P + 1];
+#pragma unroll
+  for (int k = 0; k <= P; ++k) sv[k] = q0 + k <= n ? so[q0 + k] : 0;
+#pragma unroll
+  for (int k = 0; k <= P; ++k) {
+    const int32_t q = q0 + k;
+    if (q <= n && ((q == 0 && sv[k] != 0) || (q == n && sv[k] != n_tok))) bad = true;
+    if (k < P && q < n && sv[k + 1] < sv[k]) bad = true;
+  }
+  int64_t local = 0;
+#pragma unroll
+  for (int k = 0; k < P; ++k) local += len[k];
+  int64_t tot;
+  int64_t b = block_excl_scan<int64_t>(local, tmp, &tot);
+#pragma unroll
+  for (int k = 0; k < P; ++k) {
+    if (q0 + k < n) {
+      bal[q0 + k] = b;
+      shift[q0 + k] = beg[k] - b;
+    }
+    b += len[k];
+  }
+  __syncthreads();  // bal of every sample visible to the workgroup
+  tile_table(n, n_tok, bad, local, ro, W, T, bal, tile_pref, tiles, err);
 }
 
 // ---------------------------------------------------------------- tiles
@@ -690,17 +755,25 @@ extern "C" int fs_bucketize_permute(const int64_t* ids, int64_t n_tok,
   const int32_t n_len_blocks = (int32_t)cdiv(n + 1, kPrepThreads);  // <= kMaxLenBlocks
   const int32_t split_blocks = (int32_t)(cdiv(W, kWave) * cdiv(W, kWave));
 
-  hipLaunchKernelGGL(k_lens, dim3(n_len_blocks), dim3(kPrepThreads), 0, stream, sample_offsets,
-                     n, n_tok, perm, lens, begs, bsum, flags);
-  FS_LAUNCH_CHECK();
-  if (n > 0) {
+  if (n <= kPrepThreads * 4) {
+    hipLaunchKernelGGL(k_prep1<4>, dim3(1), dim3(kPrepThreads), 0, stream, sample_offsets, n,
+                       n_tok, perm, rank_offsets, W, T, bal_offsets, shift, tile_pref, tiles, err);
+    FS_LAUNCH_CHECK();
+  } else if (n <= kPrepThreads * 8) {
+    hipLaunchKernelGGL(k_prep1<8>, dim3(1), dim3(kPrepThreads), 0, stream, sample_offsets, n,
+                       n_tok, perm, rank_offsets, W, T, bal_offsets, shift, tile_pref, tiles, err);
+    FS_LAUNCH_CHECK();
+  } else {
+    hipLaunchKernelGGL(k_lens, dim3(n_len_blocks), dim3(kPrepThreads), 0, stream,
+                       sample_offsets, n, n_tok, perm, lens, begs, bsum, flags);
+    FS_LAUNCH_CHECK();
     hipLaunchKernelGGL(k_bal, dim3((unsigned)cdiv(n, kPrepThreads)), dim3(kPrepThreads), 0,
                        stream, n, lens, begs, bsum, bal_offsets, shift);
     FS_LAUNCH_CHECK();
+    hipLaunchKernelGGL(k_tiles, dim3(1), dim3(kPrepThreads), 0, stream, n, n_tok, n_len_blocks,
+                       bsum, flags, rank_offsets, W, T, bal_offsets, tile_pref, tiles, err);
+    FS_LAUNCH_CHECK();
   }
-  hipLaunchKernelGGL(k_tiles, dim3(1), dim3(kPrepThreads), 0, stream, n, n_tok, n_len_blocks, bsum,
-                     flags, rank_offsets, W, T, bal_offsets, tile_pref, tiles, err);
-  FS_LAUNCH_CHECK();
   hipLaunchKernelGGL(k_hist, dim3(G), dim3(kThreads), 0, stream, ids, n_tok, shift, bal_offsets,
                      tile_pref, tiles, tr, W, T, nbits, counts, ld, ikey, err);
   FS_LAUNCH_CHECK();
