@@ -41,7 +41,8 @@ updated, i+1 looked up, i+2 indexed); the result is again the synchronous
 loop's.
 
 Buffers are allocated once at capacity; per-iteration state is double
-buffered. Every stream keeps the default priority.
+buffered (triple with lookahead=2), and every C call is marshalled once per
+state slot. Every stream keeps the default priority.
 """
 
 from __future__ import annotations
