@@ -60,8 +60,8 @@ struct TileDesc {
   int64_t bm_lo[kTileWaves];  // each chunk's first batch-major token
   int32_t n[kTileWaves];      // each chunk's tokens (0: the wave has none)
   int32_t t[kTileWaves];      // each chunk's table
+  int32_t q0[kTileWaves];     // the sample of each chunk's first token, or -1: unknown
   int32_t q_lo, q_hi;         // the rank's balanced samples
-  int32_t pad[2];
 };
 
 // ---------------------------------------------------------------- prep
@@ -139,9 +139,12 @@ k_bal(int32_t n, const int32_t* __restrict__ lens, const int32_t* __restrict__ b
 // ranges from bal, tiles per rank and their descriptors. `part` is this
 // thread's share of the token count and `bad` its input-check verdict; bal
 // holds the balanced offsets of samples 0..n-1 (bal[n] is written here).
+// With a copy of bal[0..n] in LDS (bal_lds), each chunk's first sample is
+// found here by an LDS search and stored, so the tile kernels need not
+// search bal in memory.
 __device__ __forceinline__ void tile_table(int32_t n, int64_t n_tok, bool bad, int64_t part,
                                            const int32_t* __restrict__ ro, int32_t W, int32_t T,
-                                           int64_t* __restrict__ bal,
+                                           int64_t* __restrict__ bal, const int64_t* bal_lds,
                                            int32_t* __restrict__ tile_pref,
                                            TileDesc* __restrict__ tiles, int32_t* __restrict__ err) {
   __shared__ int64_t tmp64[17];
@@ -224,10 +227,19 @@ __device__ __forceinline__ void tile_table(int32_t n, int64_t n_tok, bool bad, i
       d.bm_lo[w] = s_A[a] + (on ? (int64_t)kk * kWaveItems : 0);
       d.n[w] = on ? (int32_t)min((int64_t)kWaveItems, s_m[a] - (int64_t)kk * kWaveItems) : 0;
       d.t[w] = on ? t : 0;
+      d.q0[w] = -1;
+      if (bal_lds && on) {
+        // the last sample q in [q_lo, q_hi) with bal[q] <= the chunk's first token
+        int32_t lo = s_q[a], hi = s_q[a + 1];  // bal[lo] <= first < bal[hi]
+        while (hi - lo > 1) {
+          const int32_t mid = (lo + hi) >> 1;
+          if (bal_lds[mid] <= d.bm_lo[w]) lo = mid; else hi = mid;
+        }
+        d.q0[w] = lo;
+      }
     }
     d.q_lo = s_q[a];
     d.q_hi = s_q[a + 1];
-    d.pad[0] = d.pad[1] = 0;
     tiles[u] = d;
   }
 }
@@ -243,7 +255,7 @@ k_tiles(int32_t n, int64_t n_tok, int32_t n_len_blocks, const int64_t* __restric
     bad |= flags[k] != 0;
     part += bsum[k];
   }
-  tile_table(n, n_tok, bad, part, ro, W, T, bal, tile_pref, tiles, err);
+  tile_table(n, n_tok, bad, part, ro, W, T, bal, nullptr, tile_pref, tiles, err);
 }
 
 // Batches of at most kPrepThreads * P samples: the three prep steps in one
@@ -258,6 +270,7 @@ k_prep1(const int64_t* __restrict__ so, int32_t n, int64_t n_tok,
         int64_t* __restrict__ bal, int64_t* __restrict__ shift, int32_t* __restrict__ tile_pref,
         TileDesc* __restrict__ tiles, int32_t* __restrict__ err) {
   __shared__ int64_t tmp[17];
+  __shared__ int64_t s_bal[kPrepThreads * P + 1];
   const int32_t q0 = threadIdx.x * P;
   bool bad = false;
   int32_t pv[P];
@@ -292,11 +305,13 @@ k_prep1(const int64_t* __restrict__ so, int32_t n, int64_t n_tok,
     if (q0 + k < n) {
       bal[q0 + k] = b;
       shift[q0 + k] = beg[k] - b;
+      s_bal[q0 + k] = b;
     }
     b += len[k];
   }
+  if (threadIdx.x == kPrepThreads - 1) s_bal[n] = b;  // the last thread's b is the total
   __syncthreads();  // bal of every sample visible to the workgroup
-  tile_table(n, n_tok, bad, local, ro, W, T, bal, tile_pref, tiles, err);
+  tile_table(n, n_tok, bad, local, ro, W, T, bal, s_bal, tile_pref, tiles, err);
 }
 
 // ---------------------------------------------------------------- tiles
@@ -305,6 +320,7 @@ struct TileInfo {
   int32_t t;
   int64_t bm_lo, bm_hi;  // the chunk's batch-major token range (table t)
   int32_t q_lo, q_hi;    // the rank's balanced samples
+  int32_t q0;            // the sample of the chunk's first token, or -1
 };
 
 __device__ __forceinline__ bool tile_info(int32_t tile, int w, const int32_t* tile_pref,
@@ -316,6 +332,7 @@ __device__ __forceinline__ bool tile_info(int32_t tile, int w, const int32_t* ti
   ti.bm_hi = d.bm_lo[w] + d.n[w];
   ti.q_lo = d.q_lo;
   ti.q_hi = d.q_hi;
+  ti.q0 = d.q0[w];
   return true;
 }
 
@@ -362,9 +379,12 @@ __device__ __forceinline__ void wave_items(const TileInfo& ti, const int64_t* id
     bin[i] = sentinel;
   }
   if (first >= ti.bm_hi) return;
-  // sample of the first token: one past the last q in (q_lo, q_hi) with bal[q] <= first
-  const int32_t qa = (int32_t)wave_partition_point(
-      ti.q_lo + 1, ti.q_hi, [&](int64_t q) { return bal[q] <= first; }) - 1;
+  // sample of the first token: one past the last q in (q_lo, q_hi) with
+  // bal[q] <= first (stored in the tile table when it was known there)
+  const int32_t qa = ti.q0 >= 0 ? ti.q0
+                                : (int32_t)wave_partition_point(
+                                      ti.q_lo + 1, ti.q_hi,
+                                      [&](int64_t q) { return bal[q] <= first; }) - 1;
   Window win = load_window(qa, ti.q_hi, bal, shift);
   const int t = ti.t;
   const int64_t rows = tr.rows[t], rbase = tr.row_base[t];
