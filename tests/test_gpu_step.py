@@ -91,8 +91,9 @@ def step_rowbase(w):
     return np.concatenate([[0], np.cumsum(rows)[:-1]])
 
 
-def run_parity(k, balancer=None, iters=None, seed=None):
-    """k: a workload number, or a synth.Workload."""
+def run_parity(k, balancer=None, iters=None, seed=None, lookahead=1):
+    """k: a workload number, or a synth.Workload. lookahead=2 runs the step
+    with the index stages two iterations ahead (the bench's schedule)."""
     w = k if isinstance(k, synth.Workload) else synth.workload(k, balancer)
     seed = (k if isinstance(k, int) else 77) if seed is None else seed
     K = iters or w.iterations
@@ -115,10 +116,12 @@ def run_parity(k, balancer=None, iters=None, seed=None):
     say("oracle done")
     # GPU: prioritized schedule
     cap = max(b["n_tok"] for b in batches)
-    step = SparseStep(w, weights, states, cap)
+    step = SparseStep(w, weights, states, cap, lookahead=lookahead)
+    ahead = lookahead == 2
     exact = w.optim == "sgd" and all(t.dtype == "f32" for t in w.tables)
     worst = 0.0
-    st = step.prologue(to_dev(batches[0]))
+    st = step.prologue(to_dev(batches[0]),
+                       batch_after=to_dev(batches[1]) if ahead and K > 1 else None)
     step.join()
     torch.cuda.synchronize()
     _cmp_index(st, outs[0], None, None, w.world, len(w.tables), batches[0]["n_tok"])
@@ -127,7 +130,8 @@ def run_parity(k, balancer=None, iters=None, seed=None):
         say("step", i)
         prev = st
         gdev = [torch.from_numpy(g).cuda() for g in grads[i]]
-        st = step.step(to_dev(batches[i + 1]), gdev)
+        after = to_dev(batches[i + 2]) if ahead and i + 2 < K else None
+        st = step.step(to_dev(batches[i + 1]), gdev, batch_after=after)
         step.join()
         torch.cuda.synchronize()
         _cmp_index(st, outs[i + 1], outs[i], prev, w.world, len(w.tables), batches[i + 1]["n_tok"])
@@ -165,6 +169,12 @@ def test_workload3_vbs():
 @pytest.mark.timeout(600)
 def test_workload4_vbs_four_tables():
     run_parity(4, iters=3)
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("k", [2, 3, 4])
+def test_index_two_ahead_vs_oracle(k):
+    run_parity(k, iters=4, lookahead=2)
 
 
 @pytest.mark.timeout(900)
