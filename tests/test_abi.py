@@ -145,3 +145,32 @@ def test_step_rejects_unknown_lookup_schedule():
         SparseStep(None, [], [], 1, lookup="eager")
     with pytest.raises(ValueError):
         SparseStep(None, [], [], 1, lookahead=3)
+
+
+def test_prepared_calls_match_the_c_signatures(L, monkeypatch):
+    """Each prepared call holds exactly as many arguments as its C function
+    takes, and the per-call arguments sit at placeholder positions (checked
+    without a GPU: pointers are stand-in integers, nothing is called)."""
+    import torch
+    monkeypatch.setattr(L, "_ptr", lambda t: None if t is None else 0x1000)
+    t = torch.zeros(4)
+    ws = torch.zeros(16, dtype=torch.uint8)
+    weights = [torch.zeros((8, 64)), torch.zeros((8, 128), dtype=torch.bfloat16)]
+    bucket = dict(bal_offsets=t, shard_keys=t, shard_bm=t, splits=t, shard_offsets=t)
+    uq = dict(unique=t, unique_offsets=t, seg_offsets=t, occ_bm=t, occ_uid=t, cls=t, counts=t)
+    calls = [
+        L.prepare_balance("fbs", 4, (3, 2), t, t, t, t, ws),
+        L.prepare_balance("vbs", 4, (3, 2), t, t, t, t, ws),
+        L.prepare_bucketize([8, 8], t, t, 4, bucket, t, ws),
+        L.prepare_unique(bucket, [8, 8], 4, uq, None, None, ws),
+        L.prepare_unique(bucket, [8, 8], 4, uq, uq, t, ws),
+        L.prepare_lookup(weights, 4, uq, [t, t]),
+        L.prepare_lookup(weights, 4, uq, [t, t], L.FS_COLLISION, t),
+        L.prepare_update(weights, [t, t], 4, uq, "rw_adagrad", 0.1, 1e-8, L.FS_ALL, None, ws),
+    ]
+    for p in calls:
+        assert len(p.args) == len(p.fn.argtypes), p.name
+        for name, i in p.pos.items():
+            assert 0 <= i < len(p.args), (p.name, name)
+            assert p.args[i] in (None, 0), (p.name, name)
+        assert p.pos["stream"] == len(p.args) - 1, p.name
