@@ -13,8 +13,8 @@
 // share a tile when their segments are short), numbered in (r, t, chunk)
 // order, so an item's output position is its shard's base, plus the shard's
 // count in all earlier tiles, plus its stable rank inside its tile:
-//   k_lens, k_bal, k_tiles   balanced offsets, per-sample shifts, tile
-//              descriptors (short dependent-load chains)
+//   k_lens, k_bal, k_tiles (or k_prep1)   balanced offsets, per-sample
+//              shifts, tile descriptors (short dependent-load chains)
 //   k_hist     per-tile shard histograms -> rows of a tiles x shards matrix;
 //              each item's 32-bit key, batch-major
 //   k_colsum, k_colscan   exclusive column scans of that matrix in place,
@@ -67,7 +67,8 @@ struct TileDesc {
 // ---------------------------------------------------------------- prep
 // Three launches, each with short chains of dependent loads (the index path
 // runs beside the bandwidth-bound update of another stream, where every
-// dependent round trip to memory waits in deep queues):
+// dependent round trip to memory waits in deep queues); batches of up to
+// 2048 samples take one workgroup for all three (k_prep1):
 //   k_lens   one thread per balanced sample: its length and first token
 //            under perm, validation of perm and the sample offsets, per
 //            workgroup sums and flags
