@@ -351,8 +351,10 @@ class SparseStep:
         if not self._pre:  # iteration i+1 was not indexed ahead: index it now
             self._index_stages(batch_next, nxt, cur, sA)
             self.ev_idx.record(sA)
-        cs.wait_event(self.ev_idx)
+        # the update of i needs nothing from the index stages of i+1 (they
+        # only read iteration i's unique rows), so only the lookup waits
         self._run_update(cur, grads_cur, lib.FS_ALL, self.ws_red[1], cs)
+        cs.wait_event(self.ev_idx)
         self._lookup(nxt, lib.FS_ALL, cs)
         self._pre = False
         if batch_after is not None:
