@@ -214,6 +214,25 @@ int64_t or_bucketize(const int64_t* ids, int64_t n_tok, const int64_t* sample_of
 }
 
 /* ------------------------------------------------------------------------ */
+/* Ranged combine: [FS] 4.2 names the kernel that lays out the output of the  */
+/* embedding AllToAll. Reading for one GPU that holds every virtual rank: row */
+/* k of src belongs to item k of the shard-major order (what the shards send  */
+/* back, block by block), and the combine puts it in the item's batch-major   */
+/* slot of its own table: out_t[shard_bm[k]] = src_k, where t is the table    */
+/* whose key range [row_base[t], row_base[t+1]) holds shard_keys[k]. Rows are */
+/* opaque bytes (row_bytes[t] of them); slots no item maps to are untouched.  */
+void or_ranged_combine(const uint8_t* src, int64_t src_stride, const int64_t* shard_keys,
+                       const int32_t* shard_bm, int64_t n_valid, int32_t T,
+                       const int64_t* row_base, const int64_t* row_bytes, uint8_t** out) {
+  for (int64_t k = 0; k < n_valid; ++k) {
+    int32_t t = 0;
+    while (t + 1 < T && shard_keys[k] >= row_base[t + 1]) ++t;
+    memcpy(out[t] + (int64_t)shard_bm[k] * row_bytes[t], src + k * src_stride,
+           (size_t)row_bytes[t]);
+  }
+}
+
+/* ------------------------------------------------------------------------ */
 /* Dedup: [FS] 3.2 / Algorithm 2 compute the collision sets on shard-major   */
 /* unique rows. Reading of the layout: unique rows ascending by key         */
 /* (= by table, then row); since shards are contiguous row blocks of a      */

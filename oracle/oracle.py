@@ -61,6 +61,8 @@ def lib():
         L.or_unique.restype = i64
         L.or_collision.argtypes = [P, i64, P, i64, P, P, P]
         L.or_collision.restype = None
+        L.or_ranged_combine.argtypes = [P, i64, P, P, i64, i32, P, P, C.POINTER(P)]
+        L.or_ranged_combine.restype = None
         L.or_lookup.argtypes = [C.POINTER(_Store), i64, i64, i64, P, P, P, P, i32, P]
         L.or_lookup.restype = i64
         L.or_reduce.argtypes = [i32, i64, i64, P, P, P, P]
@@ -138,6 +140,24 @@ def bucketize(ids, sample_offsets, rows, perm, rank_offsets, W):
                             _p(bal), _p(keys), _p(bm), _p(splits), _p(sho), _p(err))
     return dict(bal_offsets=bal, shard_keys=keys[:nv], shard_bm=bm[:nv],
                 splits=splits.reshape(W, W), shard_offsets=sho, err=int(err[0]), row_base=rb)
+
+
+def ranged_combine(src, shard_keys, shard_bm, rows, row_bytes, n_tok):
+    """[FS] 4.2 ranged combine (one GPU, every virtual rank): row k of src
+    (uint8 [n_valid, stride]) goes to slot shard_bm[k] of its table's output
+    (uint8 [n_tok, row_bytes[t]], zero where no item maps)."""
+    src = _c(src, np.uint8)
+    keys = _c(shard_keys, np.int64)
+    bm = _c(shard_bm, np.int32)
+    T = len(rows)
+    rb = np.zeros(T + 1, np.int64)
+    rb[1:] = np.cumsum(_c(rows, np.int64))
+    rbytes = _c(row_bytes, np.int64)
+    outs = [np.zeros((n_tok, int(r)), np.uint8) for r in rbytes]
+    arr = (C.c_void_p * T)(*[o.ctypes.data for o in outs])
+    lib().or_ranged_combine(_p(src), src.shape[1] if src.ndim == 2 else 0, _p(keys), _p(bm),
+                            len(keys), T, _p(rb), _p(rbytes), arr)
+    return outs
 
 
 def unique(shard_keys, shard_bm, rows, W):

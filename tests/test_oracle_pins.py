@@ -238,6 +238,51 @@ def test_bucketize_drops_out_of_range_ids():
     assert bk["shard_offsets"][-1] == 3
 
 
+@pytest.mark.parametrize("W,T", [(1, 1), (3, 2), (5, 3)])
+def test_ranged_combine_inverts_the_dispatch(W, T):
+    """Combine after dispatch is the identity: a row that carries an item's
+    key lands in the batch-major slot of the token that holds that ID. The
+    slot's token is found from the balanced order directly (sample perm[q],
+    token j), not through the dispatch; dropped IDs leave their slot empty."""
+    rng = np.random.default_rng(100 + W * 10 + T)
+    R = [int(x) for x in rng.integers(4, 30, size=T)]
+    N = 11
+    _, so, ids = _tiny_batch(rng, N, T, R)
+    ids[0, 0] = R[0] + 3  # one dropped ID
+    L = rng.integers(1, 6, size=N).astype(np.int32)
+    perm, ro = O.balance_fbs(L, W)
+    bk = O.bucketize(ids, so, R, perm, ro, W)
+    n_tok = ids.shape[1]
+    nv = len(bk["shard_keys"])
+    # row k: the item's key as 8 little-endian int64 copies (64 bytes), then
+    # bytes (31 key + c) % 251 + 1 at column c, so a short or long copy shows
+    row_bytes = [64 * (t + 1) for t in range(T)]  # row sizes differ per table
+    stride = max(row_bytes) + 16
+    src = np.zeros((nv, stride), np.uint8)
+    src[:, :64] = np.repeat(bk["shard_keys"][:, None], 8, axis=1).view(np.uint8)
+    cols = np.arange(64, stride)
+    src[:, 64:] = ((31 * bk["shard_keys"][:, None] + cols[None, :]) % 251 + 1).astype(np.uint8)
+    outs = O.ranged_combine(src, bk["shard_keys"], bk["shard_bm"], R, row_bytes, n_tok)
+    row_base = np.concatenate([[0], np.cumsum(R)[:-1]])
+    bm = 0
+    for q in range(N):
+        s_ = perm[q]
+        for j in range(int(so[s_ + 1] - so[s_])):
+            for t in range(T):
+                id_ = int(ids[t, so[s_] + j])
+                got = outs[t][bm]
+                if 0 <= id_ < R[t]:
+                    keys = got[:64].view(np.int64)
+                    key = row_base[t] + id_
+                    assert keys.tolist() == [key] * 8
+                    c = np.arange(64, row_bytes[t])
+                    assert np.array_equal(got[64:], ((31 * key + c) % 251 + 1).astype(np.uint8))
+                else:
+                    assert not got.any()
+            bm += 1
+    assert bm == n_tok
+
+
 # ----------------------------------------------------------------------------
 # dedup / CSR and collision
 
