@@ -225,6 +225,31 @@ int fs_jagged_lookup(const fs_table* tables, int32_t T, int32_t W, const int64_t
                      int32_t which, void* const* out, int64_t n_tok, hipStream_t stream);
 
 /* ------------------------------------------------------------------------ */
+/* Ranged combine -- [FS] 4.2: the kernel that lays out the output of the    */
+/* embedding AllToAll (the rows a rank receives from the shards, range by    */
+/* range) in the rank's batch-major order. With every virtual rank on one GPU */
+/* the rows come in the dispatch's shard-major order: row k of src belongs   */
+/* to item k of fs_bucketize_permute's output and is copied to              */
+/*   out[t][shard_bm[k]],  t = the table whose key range holds shard_keys[k], */
+/* for k < shard_offsets[W] (the valid items; dropped IDs are not combined). */
+/* Slots no item maps to are not written. The sparse step does not need it   */
+/* (fs_jagged_lookup writes batch-major slots itself); it is the standalone  */
+/* combine of the dispatch.                                                  */
+/*  src, src_stride  device rows, 16-byte aligned, src_stride bytes apart    */
+/*               (a multiple of 16, at least every table's row size).        */
+/*  shard_keys, shard_bm, shard_offsets, W: fs_bucketize_permute's outputs   */
+/*               for this batch (shard_bm < n_tok; other values write out of  */
+/*               bounds).                                                    */
+/*  tables   host [T]: rows, dim and dtype set the key ranges and row sizes  */
+/*           (dim_t * sizeof(dtype) in {64, 128, ..., 2048} bytes, else      */
+/*           FS_ERR_UNSUPPORTED); weights are not read.                      */
+/*  out      host [T] of device [n_tok][dim_t] pointers, 16-byte aligned.    */
+int fs_ranged_combine(const void* src, int64_t src_stride, const int64_t* shard_keys,
+                      const int32_t* shard_bm, const int64_t* shard_offsets, int32_t W,
+                      const fs_table* tables, int32_t T, void* const* out, int64_t n_tok,
+                      hipStream_t stream);
+
+/* ------------------------------------------------------------------------ */
 /* Gradient segment-reduce + row update -- Algorithm 2's backward (split the */
 /* batch-major gradients into collision and exclusive parts, send them to    */
 /* the shards, update_embedding) and its forward (the previous iteration's   */

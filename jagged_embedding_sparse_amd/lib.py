@@ -58,6 +58,8 @@ _c_unique = _sig("fs_unique_collision_split", C.c_int, _P, _P, _P, _i64, _TP, _i
 _c_unique_ws = _sig("fs_unique_workspace_size", _sz, _i64, _i64, _i32, _i32)
 _c_lookup = _sig("fs_jagged_lookup", C.c_int, _TP, _i32, _i32, _P, _P, _P, _P, _P, _P, _i32,
                  C.POINTER(_P), _i64, _P)
+_c_combine = _sig("fs_ranged_combine", C.c_int, _P, _i64, _P, _P, _P, _i32, _TP, _i32,
+                  C.POINTER(_P), _i64, _P)
 _c_reduce = _sig("fs_grad_reduce_update", C.c_int, _TP, _i32, _i32, C.POINTER(_P), _i64, _P, _P,
                  _P, _P, _P, _P, _i32, _i32, _f, _f, C.POINTER(_P), _P, _sz, _P)
 _c_reduce_ws = _sig("fs_grad_reduce_update_workspace_size", _sz, _i64, _i32)
@@ -66,7 +68,8 @@ _c_version = _sig("fs_version", C.c_int)
 
 EXPORTED = ["fs_balance_fbs", "fs_balance_vbs", "fs_balance_workspace_size",
             "fs_bucketize_permute", "fs_bucketize_workspace_size", "fs_unique_collision_split",
-            "fs_unique_workspace_size", "fs_jagged_lookup", "fs_grad_reduce_update",
+            "fs_unique_workspace_size", "fs_jagged_lookup", "fs_ranged_combine",
+            "fs_grad_reduce_update",
             "fs_grad_reduce_update_workspace_size", "fs_strerror", "fs_version"]
 
 
@@ -255,6 +258,29 @@ def fs_jagged_lookup(weights, W, uq, n_tok, which=FS_ALL, cls=None, out=None, st
                      _ptr(uq["seg_offsets"]), _ptr(uq["occ_bm"]), _ptr(uq["occ_uid"]),
                      _ptr(cls_t) if which != FS_ALL else None, which, _ptr_array(out), n_tok,
                      _stream(stream)))
+    return out
+
+
+def fs_ranged_combine(src, bucket, W, dims, dtypes, rows, n_tok, out=None, stream=None):
+    """src: device uint8 [n_items, stride] rows in the dispatch's shard-major
+    order; bucket: fs_bucketize_permute's outputs; dims / dtypes / rows: per
+    table (dtype torch.float32 or torch.bfloat16). Returns one device tensor
+    per table, [n_tok, dim] of that dtype (slots no item maps to: zeros when
+    the outputs are allocated here)."""
+    T = len(dims)
+    tabs = (FsTable * T)()
+    for t in range(T):
+        tabs[t].rows = int(rows[t])
+        tabs[t].dim = int(dims[t])
+        tabs[t].dtype = FS_F32 if dtypes[t] == torch.float32 else FS_BF16
+    if out is None:
+        out = [torch.zeros((n_tok, int(dims[t])), dtype=dtypes[t], device=_dev())
+               for t in range(T)]
+    stride = src.shape[1] * src.element_size() if src.dim() == 2 else 0
+    _check("fs_ranged_combine",
+           _c_combine(_ptr(src), stride, _ptr(bucket["shard_keys"]), _ptr(bucket["shard_bm"]),
+                      _ptr(bucket["shard_offsets"]), W, tabs, T, _ptr_array(out), n_tok,
+                      _stream(stream)))
     return out
 
 

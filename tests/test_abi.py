@@ -174,3 +174,18 @@ def test_prepared_calls_match_the_c_signatures(L, monkeypatch):
             assert 0 <= i < len(p.args), (p.name, name)
             assert p.args[i] in (None, 0), (p.name, name)
         assert p.pos["stream"] == len(p.args) - 1, p.name
+
+
+def test_combine_rejects_bad_rows_and_strides(L):
+    cb = L._c_combine
+    outs = (C.c_void_p * 2)(FAKE, FAKE)
+
+    def call(dims, stride, src=FAKE, T=None):
+        tab = _tables(L, [(1000, d, L.FS_F32, False) for d in dims])
+        return cb(src, stride, FAKE, FAKE, FAKE, 4, tab, T if T is not None else len(dims), outs,
+                  10, None)
+    assert call([48], 256) == L.FS_ERR_UNSUPPORTED      # 192-byte rows
+    assert call([64, 128], 256) == L.FS_ERR_INVALID_ARG  # stride below the 512-byte row
+    assert call([64], 264) == L.FS_ERR_INVALID_ARG       # stride not a multiple of 16
+    assert call([64], 256, src=FAKE + 8) == L.FS_ERR_INVALID_ARG  # src not 16-byte aligned
+    assert call([64], 256, T=0) == L.FS_ERR_INVALID_ARG

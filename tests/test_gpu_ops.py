@@ -198,6 +198,56 @@ def test_bucketize_bad_offsets_flag_shape():
     assert np.all(host(bk["shard_offsets"]) == 0) and np.all(host(bk["splits"]) == 0)
 
 
+# ----------------------------------------------------------------------------- combine
+
+# (seed, N, rows, dims, dtypes, W, bad IDs): one table and several, row sizes
+# 64 B .. 2 KB, W above N, dropped IDs
+COMBINE_CASES = [
+    (41, 300, [5000], [64], ["f32"], 4, 0),
+    (42, 500, [3000, 700, 90000], [64, 128, 256], ["f32", "bf16", "f32"], 16, 9),
+    (43, 40, [1500, 20000], [512, 1024], ["bf16", "bf16"], 64, 3),
+    (44, 200, [100000], [512], ["f32"], 7, 0),
+]
+
+
+@pytest.mark.parametrize("case", COMBINE_CASES)
+def test_ranged_combine_parity(case):
+    """GPU combine vs the oracle's on the same shard-major rows (random bytes,
+    a stride wider than every row): every slot bit-exact, untouched slots
+    keep their fill."""
+    seed, N, rows, dims, dts, W, bad = case
+    say("combine", case)
+    b = _tiny_batch(seed, N, rows, 40, bad)
+    _, _, bk, err = _gpu_bucketize(b, rows, W)
+    torch.cuda.synchronize()
+    nv = int(host(bk["shard_offsets"])[-1])
+    torch_dt = [torch.float32 if d == "f32" else torch.bfloat16 for d in dts]
+    row_bytes = [d * (4 if dt == "f32" else 2) for d, dt in zip(dims, dts)]
+    stride = max(row_bytes) + 32
+    rng = np.random.default_rng(seed)
+    src_h = rng.integers(0, 256, size=(max(nv, 1), stride), dtype=np.uint8)
+    src = torch.from_numpy(src_h).cuda()
+    n_tok = b["n_tok"]
+    fill = [torch.full((n_tok, d), 3, dtype=dt, device="cuda") for d, dt in zip(dims, torch_dt)]
+    out = lib.fs_ranged_combine(src, bk, W, dims, torch_dt, rows, n_tok, out=fill)
+    torch.cuda.synchronize()
+    keys = host(bk["shard_keys"])[:nv]
+    bm = host(bk["shard_bm"])[:nv]
+    ref = O.ranged_combine(src_h[:nv], keys, bm, rows, row_bytes, n_tok)
+    for t in range(len(rows)):
+        got = host(out[t].view(torch.uint8) if out[t].dtype == torch.float32 else
+                   out[t].view(torch.int16)).view(np.uint8).reshape(n_tok, row_bytes[t])
+        hit = np.zeros(n_tok, bool)
+        hit[bm[(keys >= sum(rows[:t])) & (keys < sum(rows[:t + 1]))]] = True
+        assert np.array_equal(got[hit], ref[t][hit])
+        three = np.full((1, dims[t]), 3, dtype=np.float32)
+        pattern = (three.view(np.uint8) if dts[t] == "f32" else
+                   torch.full((1, dims[t]), 3, dtype=torch.bfloat16).view(torch.int16)
+                   .numpy().view(np.uint8))
+        assert np.array_equal(got[~hit], np.repeat(pattern, int((~hit).sum()), axis=0))
+    assert int(err.item()) == (lib.FS_EF_ID_RANGE if bad else 0)
+
+
 # ----------------------------------------------------------------------------- unique
 
 
