@@ -233,6 +233,38 @@ void or_ranged_combine(const uint8_t* src, int64_t src_stride, const int64_t* sh
 }
 
 /* ------------------------------------------------------------------------ */
+/* Keyed transpose: [FS] 4.2 names the kernel that turns a jagged tensor from */
+/* the feature-major form to the batch-major form. Reading: F features, B    */
+/* samples, lengths[f*B + b] values of feature f for sample b; the input     */
+/* lists feature 0's values sample by sample, then feature 1's, and so on;   */
+/* the output lists sample 0's values feature by feature, then sample 1's.   */
+/* out_offsets[b*F + f] = where (b, f) starts in the output; its last entry  */
+/* is the total.                                                            */
+void or_keyed_transpose(const int64_t* values, const int32_t* lengths, int32_t F, int32_t B,
+                        int64_t* out_values, int64_t* out_offsets) {
+  int64_t* in_off = (int64_t*)malloc(sizeof(int64_t) * ((size_t)F * B + 1));
+  int64_t x = 0;
+  for (int64_t e = 0; e < (int64_t)F * B; ++e) {  /* feature-major starts */
+    in_off[e] = x;
+    x += lengths[e];
+  }
+  x = 0;
+  for (int32_t b = 0; b < B; ++b)  /* batch-major starts */
+    for (int32_t f = 0; f < F; ++f) {
+      out_offsets[(int64_t)b * F + f] = x;
+      x += lengths[(int64_t)f * B + b];
+    }
+  out_offsets[(int64_t)F * B] = x;
+  for (int32_t b = 0; b < B; ++b)
+    for (int32_t f = 0; f < F; ++f) {
+      int64_t n = lengths[(int64_t)f * B + b];
+      for (int64_t j = 0; j < n; ++j)
+        out_values[out_offsets[(int64_t)b * F + f] + j] = values[in_off[(int64_t)f * B + b] + j];
+    }
+  free(in_off);
+}
+
+/* ------------------------------------------------------------------------ */
 /* Dedup: [FS] 3.2 / Algorithm 2 compute the collision sets on shard-major   */
 /* unique rows. Reading of the layout: unique rows ascending by key         */
 /* (= by table, then row); since shards are contiguous row blocks of a      */

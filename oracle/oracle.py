@@ -63,6 +63,8 @@ def lib():
         L.or_collision.restype = None
         L.or_ranged_combine.argtypes = [P, i64, P, P, i64, i32, P, P, C.POINTER(P)]
         L.or_ranged_combine.restype = None
+        L.or_keyed_transpose.argtypes = [P, P, i32, i32, P, P]
+        L.or_keyed_transpose.restype = None
         L.or_lookup.argtypes = [C.POINTER(_Store), i64, i64, i64, P, P, P, P, i32, P]
         L.or_lookup.restype = i64
         L.or_reduce.argtypes = [i32, i64, i64, P, P, P, P]
@@ -158,6 +160,19 @@ def ranged_combine(src, shard_keys, shard_bm, rows, row_bytes, n_tok):
     lib().or_ranged_combine(_p(src), src.shape[1] if src.ndim == 2 else 0, _p(keys), _p(bm),
                             len(keys), T, _p(rb), _p(rbytes), arr)
     return outs
+
+
+def keyed_transpose(values, lengths):
+    """[FS] 4.2 keyed transpose: lengths int [F, B] (feature-major), values the
+    feature-major concatenation. Returns (batch-major values, out_offsets
+    [B*F + 1] with out_offsets[b*F + f] the start of (b, f))."""
+    lengths = _c(lengths, np.int32)
+    F, B = lengths.shape
+    values = _c(values, np.int64)
+    out = np.empty(max(len(values), 1), np.int64)
+    off = np.empty(F * B + 1, np.int64)
+    lib().or_keyed_transpose(_p(values), _p(lengths), F, B, _p(out), _p(off))
+    return out[:len(values)], off
 
 
 def unique(shard_keys, shard_bm, rows, W):

@@ -238,6 +238,33 @@ def test_bucketize_drops_out_of_range_ids():
     assert bk["shard_offsets"][-1] == 3
 
 
+def test_keyed_transpose_hand_example():
+    """Two features, three samples; feature 0 has lengths 2, 0, 1 and feature 1
+    has 1, 2, 0. Feature-major input: f0 = [10 11 | - | 12], f1 = [20 | 21 22 | -].
+    Batch-major output: sample 0 = 10 11 20, sample 1 = 21 22, sample 2 = 12."""
+    lengths = np.array([[2, 0, 1], [1, 2, 0]])
+    values = np.array([10, 11, 12, 20, 21, 22])
+    out, off = O.keyed_transpose(values, lengths)
+    assert out.tolist() == [10, 11, 20, 21, 22, 12]
+    # (b, f) starts: (0,0)=0 (0,1)=2 (1,0)=3 (1,1)=3 (2,0)=5 (2,1)=6, total 6
+    assert off.tolist() == [0, 2, 3, 3, 5, 6, 6]
+
+
+@pytest.mark.parametrize("F,B", [(1, 7), (3, 5), (6, 1), (4, 9)])
+def test_keyed_transpose_twice_is_identity(F, B):
+    """The batch-major output is a feature-major jagged tensor of B
+    "features" over F "samples" (lengths transposed); transposing it back
+    returns the input, and both offset lists agree with cumulative sums."""
+    rng = np.random.default_rng(F * 31 + B)
+    lengths = rng.integers(0, 5, size=(F, B))
+    values = rng.integers(-10**12, 10**12, size=int(lengths.sum()))
+    out, off = O.keyed_transpose(values, lengths)
+    assert np.array_equal(off, np.concatenate([[0], np.cumsum(lengths.T.reshape(-1))]))
+    back, off2 = O.keyed_transpose(out, lengths.T)
+    assert np.array_equal(back, values)
+    assert np.array_equal(off2, np.concatenate([[0], np.cumsum(lengths.reshape(-1))]))
+
+
 @pytest.mark.parametrize("W,T", [(1, 1), (3, 2), (5, 3)])
 def test_ranged_combine_inverts_the_dispatch(W, T):
     """Combine after dispatch is the identity: a row that carries an item's
