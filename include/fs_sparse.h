@@ -250,6 +250,31 @@ int fs_ranged_combine(const void* src, int64_t src_stride, const int64_t* shard_
                       hipStream_t stream);
 
 /* ------------------------------------------------------------------------ */
+/* Keyed transpose -- [FS] 4.2: a jagged tensor of F features (keys) over B  */
+/* samples goes from feature-major to batch-major order. Input list (f, b)   */
+/* holds lengths[f*B + b] values and the lists lie in the order (0,0),       */
+/* (0,1), .., (0,B-1), (1,0), ..; the output holds the same lists in the     */
+/* order (b=0,f=0), (0,1), .., (0,F-1), (1,0), .., each list's values in    */
+/* their input order.                                                        */
+/*  values       device [n_vals] elements of elem_bytes (4 or 8, else        */
+/*               FS_ERR_UNSUPPORTED; aligned to it); copied bit for bit.     */
+/*  lengths      device int32 [F][B]; negative lengths count as zero and     */
+/*               flag FS_EF_SHAPE. F * B < 2^31; F or B may be 0.            */
+/*  out_values   device [n_vals] elements, not aliasing values.              */
+/*  out_offsets  device int64 [F*B + 1]: out_offsets[b*F + f] = where list   */
+/*               (b, f) starts in out_values; out_offsets[F*B] = the total.  */
+/*  err          nullable; FS_EF_SHAPE when the lengths do not sum to       */
+/*               n_vals -- then values whose output position or input       */
+/*               position is not below n_vals are not copied.               */
+/*  ws, ws_bytes at least fs_keyed_transpose_workspace_size(F, B) bytes.    */
+int fs_keyed_transpose(const void* values, int64_t n_vals, int32_t elem_bytes,
+                       const int32_t* lengths, int32_t F, int32_t B, void* out_values,
+                       int64_t* out_offsets, int32_t* err, void* ws, size_t ws_bytes,
+                       hipStream_t stream);
+
+size_t fs_keyed_transpose_workspace_size(int32_t F, int32_t B);
+
+/* ------------------------------------------------------------------------ */
 /* Gradient segment-reduce + row update -- Algorithm 2's backward (split the */
 /* batch-major gradients into collision and exclusive parts, send them to    */
 /* the shards, update_embedding) and its forward (the previous iteration's   */

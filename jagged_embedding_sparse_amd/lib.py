@@ -60,6 +60,9 @@ _c_lookup = _sig("fs_jagged_lookup", C.c_int, _TP, _i32, _i32, _P, _P, _P, _P, _
                  C.POINTER(_P), _i64, _P)
 _c_combine = _sig("fs_ranged_combine", C.c_int, _P, _i64, _P, _P, _P, _i32, _TP, _i32,
                   C.POINTER(_P), _i64, _P)
+_c_kt = _sig("fs_keyed_transpose", C.c_int, _P, _i64, _i32, _P, _i32, _i32, _P, _P, _P, _P, _sz,
+             _P)
+_c_kt_ws = _sig("fs_keyed_transpose_workspace_size", _sz, _i32, _i32)
 _c_reduce = _sig("fs_grad_reduce_update", C.c_int, _TP, _i32, _i32, C.POINTER(_P), _i64, _P, _P,
                  _P, _P, _P, _P, _i32, _i32, _f, _f, C.POINTER(_P), _P, _sz, _P)
 _c_reduce_ws = _sig("fs_grad_reduce_update_workspace_size", _sz, _i64, _i32)
@@ -69,6 +72,7 @@ _c_version = _sig("fs_version", C.c_int)
 EXPORTED = ["fs_balance_fbs", "fs_balance_vbs", "fs_balance_workspace_size",
             "fs_bucketize_permute", "fs_bucketize_workspace_size", "fs_unique_collision_split",
             "fs_unique_workspace_size", "fs_jagged_lookup", "fs_ranged_combine",
+            "fs_keyed_transpose", "fs_keyed_transpose_workspace_size",
             "fs_grad_reduce_update",
             "fs_grad_reduce_update_workspace_size", "fs_strerror", "fs_version"]
 
@@ -282,6 +286,31 @@ def fs_ranged_combine(src, bucket, W, dims, dtypes, rows, n_tok, out=None, strea
                       _ptr(bucket["shard_offsets"]), W, tabs, T, _ptr_array(out), n_tok,
                       _stream(stream)))
     return out
+
+
+def keyed_transpose_workspace_size(F, B):
+    return int(_c_kt_ws(F, B))
+
+
+def fs_keyed_transpose(values, lengths, out=None, out_offsets=None, err=None, ws=None,
+                       stream=None):
+    """values: device 1-D tensor of 4- or 8-byte elements, the feature-major
+    concatenation of the lists; lengths: device int32 [F, B] (feature-major).
+    Returns (batch-major values, int64 out_offsets [B*F + 1], out_offsets[b*F + f]
+    being where list (b, f) starts)."""
+    assert lengths.dtype == torch.int32 and lengths.dim() == 2
+    F, B = lengths.shape
+    n = values.numel()
+    if out is None:
+        out = torch.empty_like(values)
+    if out_offsets is None:
+        out_offsets = torch.empty(F * B + 1, dtype=torch.int64, device=_dev())
+    ws = _ws(keyed_transpose_workspace_size(F, B), ws)
+    _check("fs_keyed_transpose",
+           _c_kt(_ptr(values) if n else None, n, values.element_size(), _ptr(lengths), F, B,
+                 _ptr(out) if n else None, _ptr(out_offsets), _ptr(err), _ptr(ws),
+                 ws.numel() * ws.element_size(), _stream(stream)))
+    return out, out_offsets
 
 
 def reduce_workspace_size(n_tok, max_dim):

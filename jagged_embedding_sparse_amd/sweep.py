@@ -11,10 +11,17 @@ batch of a workload while W varies:
   combine   fs_ranged_combine: one row per dispatched ID (dim x dtype of the
             workload's first table) back to the batch-major slots
 
+The same section names the keyed transpose (feature-major to batch-major
+jagged tensors) among those kernels; `--transpose` times fs_keyed_transpose
+on the workload's samples as F sequence features, each list as long as the
+sample's token count, for F in `--features`, against HBM bytes
+2 * n * 8 (values) + 4 * F * B (lengths) + 8 * (F * B + 1) (offsets).
+
 Each figure is the median over `--reps` calls timed with HIP events on the
 calling stream, inputs resident in HBM. Usage:
 
   python -m jagged_embedding_sparse_amd.sweep [--config 5] [--reps 20] [--out FILE]
+  python -m jagged_embedding_sparse_amd.sweep --transpose [--features 1,4,8,16]
 """
 
 from __future__ import annotations
@@ -42,13 +49,47 @@ def _time(fn, reps):
     return float(np.median(ts))
 
 
+def transpose_lines(k, features, reps):
+    w = synth.workload(k)
+    b = synth.Batches(w, k).batch(0)
+    per = np.diff(b["sample_offsets"]).astype(np.int32)
+    B = len(per)
+    lines = [f"workload {k}: {w.name}; keyed transpose of F features x {B} samples, "
+             "int64 values, list (f, b) = sample b's token count",
+             f"{'F':>4s} {'values':>11s} {'us':>9s} {'GB/s':>7s} {'of 8 TB/s':>10s}"]
+    for F in features:
+        lengths = torch.from_numpy(np.tile(per, (F, 1))).cuda()
+        n = int(per.sum()) * F
+        vals = torch.randint(0, 1 << 40, (n,), dtype=torch.int64, device="cuda")
+        out = torch.empty_like(vals)
+        offs = torch.empty(F * B + 1, dtype=torch.int64, device="cuda")
+        ws = torch.empty(lib.keyed_transpose_workspace_size(F, B), dtype=torch.uint8,
+                         device="cuda")
+        t = _time(lambda: lib.fs_keyed_transpose(vals, lengths, out=out, out_offsets=offs,
+                                                 ws=ws), reps)
+        gbs = (16 * n + 12 * F * B + 8) / t / 1e3
+        lines.append(f"{F:4d} {n:11d} {t:9.1f} {gbs:7.0f} {gbs / 8000:10.1%}")
+        del vals, out
+    return lines
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--config", type=int, default=5)
     ap.add_argument("--worlds", default="32,64,128,256,512")
     ap.add_argument("--reps", type=int, default=20)
     ap.add_argument("--out", default=None)
+    ap.add_argument("--transpose", action="store_true")
+    ap.add_argument("--features", default="1,4,8,16")
     args = ap.parse_args(argv)
+    if args.transpose:
+        text = "\n".join(transpose_lines(args.config, [int(x) for x in args.features.split(",")],
+                                         args.reps))
+        print(text, flush=True)
+        if args.out:
+            with open(args.out, "w") as f:
+                f.write(text + "\n")
+        return 0
     w = synth.workload(args.config)
     b = synth.Batches(w, args.config).batch(0)
     dev = lambda x: torch.from_numpy(x).cuda()

@@ -189,3 +189,26 @@ def test_combine_rejects_bad_rows_and_strides(L):
     assert call([64], 264) == L.FS_ERR_INVALID_ARG       # stride not a multiple of 16
     assert call([64], 256, src=FAKE + 8) == L.FS_ERR_INVALID_ARG  # src not 16-byte aligned
     assert call([64], 256, T=0) == L.FS_ERR_INVALID_ARG
+
+
+def test_keyed_transpose_rejects(L):
+    kt = L._c_kt
+    ws_n = L.keyed_transpose_workspace_size(4, 6)
+    assert ws_n >= 8 * 24 and L.keyed_transpose_workspace_size(40, 600) > ws_n
+    assert L.keyed_transpose_workspace_size(-1, 3) == 0
+
+    def call(n=100, eb=8, F=4, B=6, vals=FAKE, outv=FAKE, lens=FAKE, offs=FAKE, ws=FAKE,
+             ws_bytes=ws_n):
+        return kt(vals, n, eb, lens, F, B, outv, offs, None, ws, ws_bytes, None)
+    assert call(eb=2) == L.FS_ERR_UNSUPPORTED
+    assert call(eb=16) == L.FS_ERR_UNSUPPORTED
+    assert call(F=-1) == L.FS_ERR_INVALID_ARG
+    assert call(F=1 << 16, B=1 << 15) == L.FS_ERR_INVALID_ARG  # F * B >= 2^31
+    assert call(n=-1) == L.FS_ERR_INVALID_ARG
+    assert call(offs=None) == L.FS_ERR_INVALID_ARG
+    assert call(lens=None) == L.FS_ERR_INVALID_ARG
+    assert call(vals=None) == L.FS_ERR_INVALID_ARG
+    assert call(vals=FAKE + 4) == L.FS_ERR_INVALID_ARG       # 8-byte elements, 4-aligned
+    assert call(outv=FAKE + 2, eb=4) == L.FS_ERR_INVALID_ARG
+    assert call(ws_bytes=ws_n - 1) == L.FS_ERR_WORKSPACE
+    assert call(ws=None) == L.FS_ERR_WORKSPACE

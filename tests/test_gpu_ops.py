@@ -248,6 +248,126 @@ def test_ranged_combine_parity(case):
     assert int(err.item()) == (lib.FS_EF_ID_RANGE if bad else 0)
 
 
+# ----------------------------------------------------------------------------- keyed transpose
+
+# (seed, F, B, length mix, element bytes)
+KT_CASES = [
+    (51, 3, 5, "short", 8),
+    (52, 7, 1000, "short", 8),      # four offset tiles and a ragged tail
+    (53, 8, 300, "long", 4),        # lists of up to 3000 values
+    (54, 40, 300, "sparse", 8),     # four lists in five empty
+    (55, 1, 1, "one", 8),           # one list of 10000 values
+    (56, 1, 5000, "short", 4),      # one feature: a plain copy
+    (57, 3000, 1, "short", 8),      # one sample
+    (58, 6, 7, "empty", 8),         # every list empty
+    (59, 0, 9, "empty", 8),         # no features at all
+    (60, 16, 4096, "mixed", 8),     # 2^16 lists, lognormal lengths, a third empty
+    (61, 5, 2048, "mixed", 4),
+]
+
+
+def _kt_lengths(rng, F, B, kind):
+    if kind == "long":
+        x = rng.integers(0, 3000, (F, B))
+    elif kind == "sparse":
+        x = np.where(rng.random((F, B)) < 0.8, 0, rng.integers(1, 5, (F, B)))
+    elif kind == "one":
+        x = np.full((F, B), 10000)
+    elif kind == "empty":
+        x = np.zeros((F, B))
+    elif kind == "mixed":
+        x = np.minimum(np.floor(rng.lognormal(3.0, 1.5, (F, B))), 20000)
+        x[rng.random((F, B)) < 0.33] = 0
+    else:
+        x = rng.integers(0, 7, (F, B))
+    return x.astype(np.int32)
+
+
+def _kt_values(rng, n, eb):
+    if eb == 8:
+        return rng.integers(-2 ** 62, 2 ** 62, n, dtype=np.int64)
+    return rng.integers(-2 ** 31, 2 ** 31, n, dtype=np.int32)
+
+
+@pytest.mark.parametrize("case", KT_CASES)
+def test_keyed_transpose_parity(case):
+    """Batch-major values and offsets bit-exact against the oracle; the
+    element past the output is not touched. 4-byte values are compared
+    widened to int64 (the transpose only moves them)."""
+    seed, F, B, kind, eb = case
+    say("keyed transpose", case)
+    rng = np.random.default_rng(seed)
+    lengths = _kt_lengths(rng, F, B, kind)
+    n = int(lengths.sum())
+    vals = _kt_values(rng, n, eb)
+    dt = torch.int64 if eb == 8 else torch.int32
+    out = torch.full((n + 64,), 77, dtype=dt, device="cuda")
+    offs = torch.full((F * B + 1,), -5, dtype=torch.int64, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    lib.fs_keyed_transpose(cu(vals), cu(lengths), out=out[:n], out_offsets=offs, err=err)
+    ref, ro = O.keyed_transpose(vals.astype(np.int64), lengths)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(offs), ro)
+    got = host(out)
+    assert np.array_equal(got[:n].astype(np.int64), ref)
+    assert (got[n:] == 77).all()
+    assert int(err.item()) == 0
+
+
+@pytest.mark.parametrize("k", [4, 5])
+def test_keyed_transpose_workload(k):
+    """The jagged IDs of a workload batch as F features keyed by sample: F
+    sequence features of each sample's token count (workload 4's four tables,
+    eight features for workload 5: 51M int64 values, every one compared)."""
+    w = synth.workload(k)
+    b = synth.Batches(w, k).batch(0)
+    so = b["sample_offsets"]
+    F = 4 if k == 4 else 8
+    say("keyed transpose workload", k, F)
+    lengths = np.tile(np.diff(so).astype(np.int32), (F, 1))
+    n = int(lengths.sum())
+    vals = (np.ascontiguousarray(b["ids"]).ravel() if k == 4 else
+            np.random.default_rng(k).integers(0, 2 ** 40, n, dtype=np.int64))
+    assert len(vals) == n
+    got, go = lib.fs_keyed_transpose(cu(vals), cu(lengths))
+    ref, ro = O.keyed_transpose(vals, lengths)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(go), ro)
+    assert np.array_equal(host(got), ref)
+
+
+def test_keyed_transpose_bad_lengths_flag_shape():
+    """Negative lengths count as zero; a value count other than the lengths'
+    sum flags FS_EF_SHAPE and copies only what lies inside both arrays."""
+    rng = np.random.default_rng(70)
+    F, B = 6, 900
+    lengths = rng.integers(0, 40, (F, B)).astype(np.int32)
+    lengths[rng.random((F, B)) < 0.05] = -3
+    clean = np.maximum(lengths, 0)
+    total = int(clean.sum())
+    ref_idx, ro = O.keyed_transpose(np.arange(total, dtype=np.int64), clean)
+    for n_vals in (total, total - 1000, total + 500):
+        say("keyed transpose bad", n_vals)
+        err = torch.zeros(1, dtype=torch.int32, device="cuda")
+        out = torch.full((n_vals + 64,), -1, dtype=torch.int64, device="cuda")
+        offs = torch.empty(F * B + 1, dtype=torch.int64, device="cuda")
+        vals = torch.arange(n_vals, dtype=torch.int64, device="cuda")
+        lib.fs_keyed_transpose(vals, cu(lengths), out=out[:n_vals], out_offsets=offs, err=err)
+        torch.cuda.synchronize()
+        assert int(err.item()) == lib.FS_EF_SHAPE
+        assert np.array_equal(host(offs), ro)
+        got = host(out)
+        p = np.arange(n_vals)
+        want = np.full(n_vals, -1, np.int64)
+        inside = p < total
+        src = np.full(n_vals, -1, np.int64)
+        src[inside] = ref_idx[p[inside]]
+        ok = inside & (src < n_vals)
+        want[ok] = src[ok]
+        assert np.array_equal(got[:n_vals], want)
+        assert (got[n_vals:] == -1).all()
+
+
 # ----------------------------------------------------------------------------- unique
 
 
