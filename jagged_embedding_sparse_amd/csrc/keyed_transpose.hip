@@ -8,11 +8,12 @@
 // f' = f and b' < b) and leave sample by sample (list (b, f) after every
 // (b', f') with b' < b, or b' = b and f' < f); each list keeps its order.
 //
-// Offsets, three launches over tiles of kTile list entries:
+// Offsets: the feature-major starts go to the workspace, the batch-major
+// ones to out_offsets. Up to kOneMax lists one workgroup scans both orders
+// (k_kt_offsets1); beyond that, three launches over tiles of kTile lists:
 //   k_kt_sums     each tile's length sum in both orders
 //   k_kt_scan     one workgroup: exclusive prefixes of the tile sums
-//   k_kt_offsets  each tile's exclusive prefixes -- the feature-major starts
-//                 to the workspace, the batch-major ones to out_offsets
+//   k_kt_offsets  each tile's exclusive prefixes
 // Values, one launch (k_kt_copy): a merge-path split of the batch-major
 // sequence in which every list contributes one start item followed by one
 // item per value. Each workgroup takes kItems consecutive items, so lists of
@@ -27,10 +28,16 @@ namespace fs {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kPer = 8;                    // list entries (or values) per thread
-constexpr int kTile = kThreads * kPer;     // list entries per offsets tile
-constexpr int kItems = kThreads * kPer;    // merged items per copy workgroup
+constexpr int kPer = 8;                     // list entries per thread
+constexpr int kTile = kThreads * kPer;      // list entries per offsets tile
 constexpr int kScanThreads = 1024;
+// lists for the one-workgroup offsets (measured at 4096 lists: 10.5 us
+// against 14 us for the tiled launches; at 16384, 24 us against 14) ...
+constexpr int kOneMax = 8192;
+constexpr int kOneLds = 9216;  // ... whose rows padded to an odd length fit this
+constexpr int kCopyThreads = 512;
+constexpr int kCopyPer = 8;                        // values per thread
+constexpr int kItems = kCopyThreads * kCopyPer;    // merged items per copy workgroup
 
 // Sums of the lengths of tile blockIdx.x in feature-major order (entries
 // e = f*B + b) and in batch-major order (entries e = b*F + f, length
@@ -156,38 +163,151 @@ k_kt_offsets(const int32_t* __restrict__ lengths, uint32_t F, uint32_t B, uint32
   }
 }
 
+// Both orders' exclusive prefixes in one workgroup (F*B <= kOneMax): the
+// lengths are staged in LDS with coalesced loads, all of a thread's loads
+// in flight at once (the rows of Bp = B | 1 entries: an odd row stride puts
+// the F lists of one sample in different banks); wave w then owns a
+// contiguous chunk of entries of each order, sums it, and after the wave
+// sums are combined scans it, eight consecutive entries per lane. Writes the
+// total to out_offsets[FB]; flags FS_EF_SHAPE for negative lengths (counted
+// as zero) and when the total is not n_vals.
+__global__ void __launch_bounds__(kScanThreads)
+k_kt_offsets1(const int32_t* __restrict__ lengths, uint32_t F, uint32_t B, uint32_t FB,
+              DivU32 divF, DivU32 divB, int64_t n_vals, int64_t* __restrict__ in_off,
+              int64_t* __restrict__ out_offsets, int32_t* __restrict__ err) {
+  constexpr int nw = kScanThreads / kWave;
+  constexpr int kStage = kOneMax / kScanThreads;
+  __shared__ int32_t s_len[kOneLds];
+  __shared__ int64_t s_wf[nw], s_wb[nw];
+  const int w = threadIdx.x / kWave, l = lane();
+  const uint32_t Bp = B | 1u;
+  int32_t x[kStage];
+#pragma unroll
+  for (int i = 0; i < kStage; ++i) {
+    const uint32_t e = threadIdx.x + i * kScanThreads;
+    x[i] = e < FB ? lengths[e] : 0;
+  }
+  bool neg = false;
+#pragma unroll
+  for (int i = 0; i < kStage; ++i) {
+    const uint32_t e = threadIdx.x + i * kScanThreads;
+    neg |= x[i] < 0;
+    if (e < FB) {
+      const uint32_t f = divu32(e, divB), b = e - f * B;
+      s_len[f * Bp + b] = x[i] > 0 ? x[i] : 0;
+    }
+  }
+  flag_err(err, neg, FS_EF_SHAPE);
+  __syncthreads();
+  // wave w owns entries [c0, c1) of each order, taken 512 at a time: lane l
+  // scans entries 8l .. 8l+7 of the 512 in registers, so one wave scan (a
+  // chain of cross-lane steps) serves 512 entries
+  constexpr int R = 8;
+  const uint32_t C = (uint32_t)cdiv(FB, nw * kWave * R) * (kWave * R);
+  const uint32_t c0 = min(FB, w * C), c1 = min(FB, c0 + C);
+  // entry e of the feature-major order is list (e / B, e % B), entry e of
+  // the batch-major order list (e % F, e / F)
+  auto at_f = [&](uint32_t e) {
+    const uint32_t f = divu32(e, divB);
+    return s_len[f * Bp + (e - f * B)];
+  };
+  auto at_b = [&](uint32_t e) {
+    const uint32_t b = divu32(e, divF);
+    return s_len[(e - b * F) * Bp + b];
+  };
+  int64_t sf = 0, sb = 0;
+  for (uint32_t e = c0 + l; e < c1; e += kWave) {
+    sf += at_f(e);
+    sb += at_b(e);
+  }
+  sf = wave_sum(sf);
+  sb = wave_sum(sb);
+  if (l == 0) {
+    s_wf[w] = sf;
+    s_wb[w] = sb;
+  }
+  __syncthreads();
+  int64_t xf = 0, xb = 0, tot = 0;
+  for (int k = 0; k < nw; ++k) {
+    xf += k < w ? s_wf[k] : 0;
+    xb += k < w ? s_wb[k] : 0;
+    tot += s_wb[k];
+  }
+  for (uint32_t e0 = c0; e0 < c1; e0 += kWave * R) {
+    const uint32_t e1 = e0 + l * R;
+    int32_t vf[R], vb[R];
+    int64_t lf = 0, lb = 0;
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      vf[i] = e1 + i < c1 ? at_f(e1 + i) : 0;
+      vb[i] = e1 + i < c1 ? at_b(e1 + i) : 0;
+      lf += vf[i];
+      lb += vb[i];
+    }
+    const int64_t incf = wave_incl_scan(lf), incb = wave_incl_scan(lb);
+    int64_t pf = xf + incf - lf, pb = xb + incb - lb;
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      if (e1 + i < c1) {
+        in_off[e1 + i] = pf;
+        out_offsets[e1 + i] = pb;
+      }
+      pf += vf[i];
+      pb += vb[i];
+    }
+    xf += __shfl(incf, kWave - 1, kWave);
+    xb += __shfl(incb, kWave - 1, kWave);
+  }
+  if (threadIdx.x == 0) {
+    out_offsets[FB] = tot;
+    if (tot != n_vals && err) atomicOr(err, FS_EF_SHAPE);
+  }
+}
+
 // Values: workgroup blockIdx.x copies the values among merged items
 // [d0, d0 + kItems). List s (batch-major index s = b*F + f) has its start
 // item at out_offsets[s] + s, followed by its values; a value at output
 // position p belongs to the last list whose start is at or before p.
 template <typename V>
-__global__ void __launch_bounds__(kThreads)
+__global__ void __launch_bounds__(kCopyThreads)
 k_kt_copy(const V* __restrict__ values, V* __restrict__ out,
           const int64_t* __restrict__ out_offsets, const int64_t* __restrict__ in_off,
           uint32_t F, uint32_t B, uint32_t FB, DivU32 divF, int64_t n_vals) {
   __shared__ int32_t s_rel[kItems + 1];    // list start - p0, clamped at 0
   __shared__ int64_t s_delta[kItems + 1];  // input start - output start
-  __shared__ int64_t s_c[2];
-  const int64_t n_dev = out_offsets[FB];
-  const int64_t d_end = (int64_t)FB + min(n_dev, n_vals);
+  __shared__ int64_t s_c[3];
   const int64_t d0 = (int64_t)blockIdx.x * kItems;
-  if (d0 >= d_end) return;
-  const int64_t d1 = min(d0 + kItems, d_end);
-  // lists with a start item before d0 and before d1
+  // lists with a start item before d0 and before d0 + kItems, and the value
+  // count, fetched side by side
   const int w = threadIdx.x / kWave;
+  auto lists_before = [&](int64_t d) {
+    return wave_partition_point(0, (int64_t)FB,
+                                [&](int64_t s) { return out_offsets[s] + s < d; });
+  };
   if (w < 2) {
-    const int64_t d = w == 0 ? d0 : d1;
-    const int64_t c = wave_partition_point(
-        0, (int64_t)FB, [&](int64_t s) { return out_offsets[s] + s < d; });
+    const int64_t c = lists_before(d0 + w * kItems);
     if (lane() == 0) s_c[w] = c;
+  } else if (w == 2 && lane() == 0) {
+    s_c[2] = out_offsets[FB];
   }
   __syncthreads();
+  const int64_t d_end = (int64_t)FB + min(s_c[2], n_vals);
+  if (d0 >= d_end) return;
+  int64_t d1 = d0 + kItems;
+  if (d1 > d_end) {  // the last workgroup: the sequence ends inside it
+    d1 = d_end;
+    if (w == 0) {
+      const int64_t c = lists_before(d1);
+      if (lane() == 0) s_c[1] = c;
+    }
+    __syncthreads();
+  }
   const int64_t c0 = s_c[0], c1 = s_c[1];
   const int64_t p0 = d0 - c0, p1 = d1 - c1;  // output positions [p0, p1)
   // lists sa .. c1-1 cover them; list sa starts at or before p0
   const int64_t sa = c0 > 0 ? c0 - 1 : 0;
   const int32_t nseg = (int32_t)(c1 - sa);
-  for (int32_t j = threadIdx.x; j < nseg; j += kThreads) {
+  for (int32_t j = threadIdx.x; j < nseg; j += kCopyThreads) {
     const uint32_t s = (uint32_t)(sa + j);
     const int64_t lo = out_offsets[s];
     const uint32_t b = divu32(s, divF), f = s - b * F;
@@ -197,11 +317,11 @@ k_kt_copy(const V* __restrict__ values, V* __restrict__ out,
   __syncthreads();
   if (nseg <= 0) return;
   const int32_t m = (int32_t)(p1 - p0);
-  int64_t src[kPer];
+  int64_t src[kCopyPer];
   int32_t jlo = 0;  // a thread's positions ascend: each search starts at the last hit
 #pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    const int32_t q = threadIdx.x + i * kThreads;
+  for (int i = 0; i < kCopyPer; ++i) {
+    const int32_t q = threadIdx.x + i * kCopyThreads;
     int32_t lo = jlo, hi = nseg;  // last j with s_rel[j] <= q
     while (hi - lo > 1) {
       const int32_t mid = (lo + hi) >> 1;
@@ -213,14 +333,14 @@ k_kt_copy(const V* __restrict__ values, V* __restrict__ out,
     const int64_t sp = s_delta[lo] + p;
     src[i] = (q < m && p < n_vals && sp >= 0 && sp < n_vals) ? sp : -1;
   }
-  V v[kPer];
+  V v[kCopyPer];
 #pragma unroll
-  for (int i = 0; i < kPer; ++i)
+  for (int i = 0; i < kCopyPer; ++i)
     if (src[i] >= 0) v[i] = __builtin_nontemporal_load(values + src[i]);
 #pragma unroll
-  for (int i = 0; i < kPer; ++i)
+  for (int i = 0; i < kCopyPer; ++i)
     if (src[i] >= 0)
-      __builtin_nontemporal_store(v[i], out + p0 + threadIdx.x + i * kThreads);
+      __builtin_nontemporal_store(v[i], out + p0 + threadIdx.x + i * kCopyThreads);
 }
 
 struct KtLayout {
@@ -268,27 +388,32 @@ extern "C" int fs_keyed_transpose(const void* values, int64_t n_vals, int32_t el
   if (!ws || ws_bytes < L.bytes) return FS_ERR_WORKSPACE;
   const int32_t G = (int32_t)cdiv(FB, kTile);
   const DivU32 divF = make_divu32(F > 0 ? (uint32_t)F : 1u);
-  if (G > 0) {
+  if (FB <= kOneMax && (int64_t)F * (B | 1) <= kOneLds) {
+    hipLaunchKernelGGL(k_kt_offsets1, dim3(1), dim3(kScanThreads), 0, stream, lengths,
+                       (uint32_t)F, (uint32_t)B, (uint32_t)FB, divF,
+                       make_divu32(B > 0 ? (uint32_t)B : 1u), n_vals, L.in_off, out_offsets,
+                       err);
+    FS_LAUNCH_CHECK();
+  } else {
     hipLaunchKernelGGL(k_kt_sums, dim3((unsigned)G), dim3(kThreads), 0, stream, lengths,
                        (uint32_t)F, (uint32_t)B, (uint32_t)FB, divF, L.tsum_f, L.tsum_b, err);
     FS_LAUNCH_CHECK();
+    hipLaunchKernelGGL(k_kt_scan, dim3(1), dim3(kScanThreads), 0, stream, L.tsum_f, L.tsum_b,
+                       G, (uint32_t)FB, n_vals, out_offsets, err);
+    FS_LAUNCH_CHECK();
+    hipLaunchKernelGGL(k_kt_offsets, dim3((unsigned)G), dim3(kThreads), 0, stream, lengths,
+                       (uint32_t)F, (uint32_t)B, (uint32_t)FB, divF, L.tsum_f, L.tsum_b,
+                       L.in_off, out_offsets);
+    FS_LAUNCH_CHECK();
   }
-  hipLaunchKernelGGL(k_kt_scan, dim3(1), dim3(kScanThreads), 0, stream, L.tsum_f, L.tsum_b, G,
-                     (uint32_t)FB, n_vals, out_offsets, err);
-  FS_LAUNCH_CHECK();
-  if (G == 0) return FS_OK;
-  hipLaunchKernelGGL(k_kt_offsets, dim3((unsigned)G), dim3(kThreads), 0, stream, lengths,
-                     (uint32_t)F, (uint32_t)B, (uint32_t)FB, divF, L.tsum_f, L.tsum_b, L.in_off,
-                     out_offsets);
-  FS_LAUNCH_CHECK();
-  if (n_vals == 0) return FS_OK;
+  if (FB == 0 || n_vals == 0) return FS_OK;
   if (elem_bytes == 8)
-    hipLaunchKernelGGL(k_kt_copy<uint64_t>, dim3((unsigned)blocks), dim3(kThreads), 0, stream,
-                       (const uint64_t*)values, (uint64_t*)out_values, out_offsets, L.in_off,
+    hipLaunchKernelGGL(k_kt_copy<uint64_t>, dim3((unsigned)blocks), dim3(kCopyThreads), 0,
+                       stream, (const uint64_t*)values, (uint64_t*)out_values, out_offsets, L.in_off,
                        (uint32_t)F, (uint32_t)B, (uint32_t)FB, divF, n_vals);
   else
-    hipLaunchKernelGGL(k_kt_copy<uint32_t>, dim3((unsigned)blocks), dim3(kThreads), 0, stream,
-                       (const uint32_t*)values, (uint32_t*)out_values, out_offsets, L.in_off,
+    hipLaunchKernelGGL(k_kt_copy<uint32_t>, dim3((unsigned)blocks), dim3(kCopyThreads), 0,
+                       stream, (const uint32_t*)values, (uint32_t*)out_values, out_offsets, L.in_off,
                        (uint32_t)F, (uint32_t)B, (uint32_t)FB, divF, n_vals);
   FS_LAUNCH_CHECK();
   return FS_OK;

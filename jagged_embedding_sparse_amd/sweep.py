@@ -15,7 +15,8 @@ The same section names the keyed transpose (feature-major to batch-major
 jagged tensors) among those kernels; `--transpose` times fs_keyed_transpose
 on the workload's samples as F sequence features, each list as long as the
 sample's token count, for F in `--features`, against HBM bytes
-2 * n * 8 (values) + 4 * F * B (lengths) + 8 * (F * B + 1) (offsets).
+2 * n * 8 (values) + 4 * F * B (lengths) + 8 * (F * B + 1) (offsets), with
+torch's device copy of the same n values beside it for context.
 
 Each figure is the median over `--reps` calls timed with HIP events on the
 calling stream, inputs resident in HBM. Usage:
@@ -56,7 +57,8 @@ def transpose_lines(k, features, reps):
     B = len(per)
     lines = [f"workload {k}: {w.name}; keyed transpose of F features x {B} samples, "
              "int64 values, list (f, b) = sample b's token count",
-             f"{'F':>4s} {'values':>11s} {'us':>9s} {'GB/s':>7s} {'of 8 TB/s':>10s}"]
+             f"{'F':>4s} {'values':>11s} {'us':>9s} {'GB/s':>7s} {'of 8 TB/s':>10s} "
+             f"{'copy us':>8s} {'copy GB/s':>10s}"]
     for F in features:
         lengths = torch.from_numpy(np.tile(per, (F, 1))).cuda()
         n = int(per.sum()) * F
@@ -68,7 +70,10 @@ def transpose_lines(k, features, reps):
         t = _time(lambda: lib.fs_keyed_transpose(vals, lengths, out=out, out_offsets=offs,
                                                  ws=ws), reps)
         gbs = (16 * n + 12 * F * B + 8) / t / 1e3
-        lines.append(f"{F:4d} {n:11d} {t:9.1f} {gbs:7.0f} {gbs / 8000:10.1%}")
+        # context: torch's device copy of the same values
+        tc = _time(lambda: out.copy_(vals), reps)
+        lines.append(f"{F:4d} {n:11d} {t:9.1f} {gbs:7.0f} {gbs / 8000:10.1%} {tc:8.1f} "
+                     f"{16 * n / tc / 1e3:10.0f}")
         del vals, out
     return lines
 

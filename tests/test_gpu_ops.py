@@ -263,6 +263,11 @@ KT_CASES = [
     (59, 0, 9, "empty", 8),         # no features at all
     (60, 16, 4096, "mixed", 8),     # 2^16 lists, lognormal lengths, a third empty
     (61, 5, 2048, "mixed", 4),
+    (62, 32, 256, "short", 8),      # 8192 lists: the largest one-workgroup offsets
+    (63, 1, 8193, "short", 4),      # one more: tiled offsets, a one-list tail tile
+    (64, 2048, 2, "short", 8),      # two samples: rows padded to three in LDS
+    (65, 4096, 2, "sparse", 8),     # padded rows too long for LDS: tiled offsets
+    (66, 1, 32769, "short", 8),     # seventeen offset tiles
 ]
 
 
