@@ -148,6 +148,96 @@ int or_balance_vbs(const int32_t* len, int32_t N, int32_t W, int32_t num, int32_
 }
 
 /* ------------------------------------------------------------------------ */
+/* VBS AutoTune: [FS] 4.1 (VBS: the weights L^alpha may not track the real   */
+/* execution time, so an autotune step raises or lowers a rank's local      */
+/* batch size by how its execution time compares with the global average;   */
+/* Figure 4's AutoTune module) and 3.1 (Algorithm 1's input R, the runtime  */
+/* execution time information). The pages name the mechanism, not its       */
+/* arithmetic. Readings:                                                    */
+/*  - rank r holds a share s_r >= 1 of the batch weight; with Q_r = s_0 +   */
+/*    ... + s_{r-1} and Q = Q_W, rank r starts at                           */
+/*      c_r = min{ k in [0, N] : Q * S_k >= Q_r * T },                      */
+/*    the lower bound of the ideal cut T * Q_r / Q. Equal shares give the   */
+/*    plain VBS cut above.                                                  */
+/*  - one AutoTune step: with times t_r and their mean m = (t_0 + ... +     */
+/*    t_{W-1}) / W, a rank slower than m (1 + tol) gives up                 */
+/*    d_r = max(1, floor(s_r * step)) of its share, a rank faster than      */
+/*    m (1 - tol) gains d_r, the others keep theirs; shares stay in         */
+/*    [1, 2^40]. The comparisons are made in integers:                      */
+/*    W t_r tol_den > (sum t)(tol_den + tol_num), and < with tol_den - tol_num. */
+/*  - without a dense model, R is modelled: t_r = the sum over the rank's   */
+/*    samples of c2 L^2 + c1 L + c0 (quadratic attention plus linear work). */
+
+#define OR_SHARE_MAX ((int64_t)1 << 40)
+
+int or_balance_vbs_shares(const int32_t* len, int32_t N, int32_t W, int32_t num, int32_t den,
+                          const int64_t* shares, int32_t* perm, int32_t* rank_offsets,
+                          int64_t* rank_weight) {
+  if (N < 0 || W < 1) return -1;
+  for (int32_t r = 0; r < W; ++r)
+    if (shares[r] < 1 || shares[r] > OR_SHARE_MAX) return -1;
+  int32_t* order = (int32_t*)malloc(sizeof(int32_t) * (size_t)(N > 0 ? N : 1));
+  int64_t* S = (int64_t*)malloc(sizeof(int64_t) * (size_t)(N + 1));
+  or_sorted_order(len, N, order);
+  S[0] = 0;
+  for (int32_t k = 0; k < N; ++k) {
+    int64_t w = or_vbs_weight(len[order[k]], num, den);
+    if (w < 0) { free(order); free(S); return -2; }
+    S[k + 1] = S[k] + w;
+  }
+  int64_t T = S[N];
+  int64_t Q = 0;
+  for (int32_t r = 0; r < W; ++r) Q += shares[r];
+  int64_t Qr = 0;
+  for (int32_t r = 0; r <= W; ++r) {
+    int32_t c = 0;
+    while (c < N && (__int128)Q * S[c] < (__int128)Qr * T) ++c; /* linear search: plain */
+    rank_offsets[r] = c;
+    if (r < W) Qr += shares[r];
+  }
+  rank_offsets[W] = N;
+  for (int32_t k = 0; k < N; ++k) perm[k] = order[k];
+  if (rank_weight)
+    for (int32_t r = 0; r < W; ++r) rank_weight[r] = S[rank_offsets[r + 1]] - S[rank_offsets[r]];
+  free(order);
+  free(S);
+  return 0;
+}
+
+/* cost[r] = sum over positions j in [rank_offsets[r], rank_offsets[r+1]) of */
+/* c2 L^2 + c1 L + c0, L = len[perm[j]].                                     */
+void or_rank_cost(const int32_t* len, const int32_t* perm, const int32_t* rank_offsets,
+                  int32_t W, int64_t c2, int64_t c1, int64_t c0, int64_t* cost) {
+  for (int32_t r = 0; r < W; ++r) {
+    int64_t t = 0;
+    for (int32_t j = rank_offsets[r]; j < rank_offsets[r + 1]; ++j) {
+      int64_t L = len[perm[j]];
+      t += c2 * L * L + c1 * L + c0;
+    }
+    cost[r] = t;
+  }
+}
+
+/* One AutoTune step on shares[W] in place (readings above). */
+void or_vbs_autotune(const int64_t* times, int32_t W, int32_t step_num, int32_t step_den,
+                     int32_t tol_num, int32_t tol_den, int64_t* shares) {
+  int64_t sum = 0;
+  for (int32_t r = 0; r < W; ++r) sum += times[r];
+  for (int32_t r = 0; r < W; ++r) {
+    __int128 lhs = (__int128)W * times[r] * tol_den;
+    int64_t d = shares[r] * step_num / step_den;
+    if (d < 1) d = 1;
+    if (lhs > (__int128)sum * (tol_den + tol_num)) {        /* slower than the mean */
+      shares[r] -= d;
+      if (shares[r] < 1) shares[r] = 1;
+    } else if (lhs < (__int128)sum * (tol_den - tol_num)) { /* faster */
+      shares[r] += d;
+      if (shares[r] > OR_SHARE_MAX) shares[r] = OR_SHARE_MAX;
+    }
+  }
+}
+
+/* ------------------------------------------------------------------------ */
 /* Indexed permute and bucketize: [FS] 4.2 ("indexed permute" applies the    */
 /* partition to the gathered IDs; "ranged dispatch" builds the per-destination */
 /* ranges that the ID AllToAll sends) and 3.2 (batch-major vs shard-major).  */

@@ -55,6 +55,12 @@ def lib():
         L.or_vbs_weight.restype = i64
         L.or_balance_vbs.argtypes = [P, i32, i32, i32, i32, P, P, P]
         L.or_balance_vbs.restype = C.c_int
+        L.or_balance_vbs_shares.argtypes = [P, i32, i32, i32, i32, P, P, P, P]
+        L.or_balance_vbs_shares.restype = C.c_int
+        L.or_rank_cost.argtypes = [P, P, P, i32, i64, i64, i64, P]
+        L.or_rank_cost.restype = None
+        L.or_vbs_autotune.argtypes = [P, i32, i32, i32, i32, i32, P]
+        L.or_vbs_autotune.restype = None
         L.or_bucketize.argtypes = [P, i64, P, i32, i32, P, P, P, P, i32, P, P, P, P, P, P]
         L.or_bucketize.restype = i64
         L.or_unique.argtypes = [P, P, i64, i32, P, P, i32, P, P, P, P, P]
@@ -111,6 +117,43 @@ def balance_vbs(uih_len, W, alpha=(3, 2)):
     if rc != 0:
         raise ValueError(f"or_balance_vbs failed ({rc})")
     return perm, ro, rw
+
+
+def balance_vbs_shares(uih_len, W, shares, alpha=(3, 2)):
+    """[FS] 4.1 VBS with per-rank shares of the weight (the AutoTune reading)."""
+    L = _c(uih_len, np.int32)
+    sh = _c(shares, np.int64)
+    assert len(sh) == W
+    perm = np.empty(len(L), np.int32)
+    ro = np.empty(W + 1, np.int32)
+    rw = np.empty(W, np.int64)
+    rc = lib().or_balance_vbs_shares(_p(L), len(L), W, int(alpha[0]), int(alpha[1]), _p(sh),
+                                     _p(perm), _p(ro), _p(rw))
+    if rc != 0:
+        raise ValueError(f"or_balance_vbs_shares failed ({rc})")
+    return perm, ro, rw
+
+
+def rank_cost(uih_len, perm, rank_offsets, coef):
+    """Modelled per-rank time: sum of c2 L^2 + c1 L + c0 over the rank's samples."""
+    L = _c(uih_len, np.int32)
+    pm = _c(perm, np.int32)
+    ro = _c(rank_offsets, np.int32)
+    W = len(ro) - 1
+    out = np.empty(W, np.int64)
+    c2, c1, c0 = (int(c) for c in coef)
+    lib().or_rank_cost(_p(L), _p(pm), _p(ro), W, c2, c1, c0, _p(out))
+    return out
+
+
+def vbs_autotune(times, shares, step=(1, 16), tol=(1, 20)):
+    """One AutoTune step; returns the new shares (the input is not changed)."""
+    t = _c(times, np.int64)
+    sh = np.array(shares, dtype=np.int64, copy=True)
+    assert len(t) == len(sh)
+    lib().or_vbs_autotune(_p(t), len(t), int(step[0]), int(step[1]), int(tol[0]), int(tol[1]),
+                          _p(sh))
+    return sh
 
 
 def vbs_weight(L, alpha):

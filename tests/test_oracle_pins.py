@@ -159,6 +159,110 @@ def test_vbs_alpha_zero_is_equal_counts():
     assert set(c.tolist()) <= {100 // 7, 100 // 7 + 1}
 
 
+# ---- VBS AutoTune ([FS] 4.1 autotune, Figure 4; Algorithm 1's input R)
+
+@pytest.mark.parametrize("alpha", [(0, 1), (1, 2), (1, 1), (3, 2), (2, 1)])
+@pytest.mark.parametrize("N,W", [(0, 3), (9, 4), (1024, 64), (4096, 512), (5, 8)])
+def test_vbs_equal_shares_is_plain_vbs(N, W, alpha):
+    """Equal shares (of any size) reduce to the plain VBS cut."""
+    rng = np.random.default_rng(N * 7 + W)
+    L = np.minimum(np.ceil(rng.lognormal(5, 1.3, size=N)), 32768).astype(np.int32)
+    ref = O.balance_vbs(L, W, alpha)
+    for c in (1, 7, 1 << 40):
+        got = O.balance_vbs_shares(L, W, np.full(W, c), alpha)
+        for a, b in zip(got, ref):
+            assert np.array_equal(a, b)
+
+
+def test_vbs_shares_hand_examples():
+    # four unit weights (alpha = 1, L = 1): shares 1:3 and 3:1
+    assert O.balance_vbs_shares([1, 1, 1, 1], 2, [1, 3], (1, 1))[1].tolist() == [0, 1, 4]
+    assert O.balance_vbs_shares([1, 1, 1, 1], 2, [3, 1], (1, 1))[1].tolist() == [0, 3, 4]
+    # eight samples of weight 5, shares 1:1:2 -> 2, 2 and 4 samples
+    perm, ro, rw = O.balance_vbs_shares([5] * 8, 3, [1, 1, 2], (1, 1))
+    assert ro.tolist() == [0, 2, 4, 8] and rw.tolist() == [10, 10, 20]
+    # a share of 1 against 2^40: the first rank's ideal cut is below one sample
+    assert O.balance_vbs_shares([3] * 6, 2, [1, 1 << 40], (1, 1))[1].tolist() == [0, 1, 6]
+    with pytest.raises(ValueError):
+        O.balance_vbs_shares([1, 2], 2, [0, 1], (1, 1))
+
+
+@pytest.mark.parametrize("W", [2, 7, 64, 300])
+def test_vbs_shares_segments_track_their_targets(W):
+    """Every cut is the lower bound of its ideal point T * Q_r / Q, so each
+    segment differs from T * s_r / Q by less than one boundary sample."""
+    rng = np.random.default_rng(W)
+    N = 3000
+    L = np.minimum(np.ceil(rng.lognormal(5, 1.3, size=N)), 32768).astype(np.int32)
+    shares = rng.integers(1, 1000, size=W)
+    perm, ro, rw = O.balance_vbs_shares(L, W, shares, (3, 2))
+    w = [_decimal_round_pow(int(L[s]), 3, 2) for s in _py_order(L)]
+    S = np.concatenate([[0], np.cumsum(w)]).astype(object)
+    T, Q = int(S[-1]), int(shares.sum())
+    Qr = np.concatenate([[0], np.cumsum(shares)]).astype(object)
+    assert ro[0] == 0 and ro[-1] == N
+    for r in range(1, W):
+        c = int(ro[r])
+        assert S[c] * Q >= Qr[r] * T
+        assert c == 0 or S[c - 1] * Q < Qr[r] * T
+    for r in range(W):
+        seg = int(S[ro[r + 1]] - S[ro[r]])
+        assert seg == rw[r]
+        assert abs(seg * Q - T * int(shares[r])) < Q * max(w)
+
+
+def test_rank_cost_hand_example_and_total():
+    L = np.array([3, 1, 4, 1, 5], np.int32)
+    perm = np.array([1, 3, 0, 2, 4], np.int32)
+    ro = np.array([0, 2, 5], np.int32)
+    # rank 0: L = 1, 1 -> 2 (2*1 + 3*1 + 7); rank 1: L = 3, 4, 5
+    got = O.rank_cost(L, perm, ro, (2, 3, 7))
+    assert got.tolist() == [24, (18 + 9 + 7) + (32 + 12 + 7) + (50 + 15 + 7)]
+    rng = np.random.default_rng(5)
+    L = rng.integers(0, 20000, 4000).astype(np.int32)
+    perm, ro, _ = O.balance_vbs(L, 37, (1, 1))
+    c = O.rank_cost(L, perm, ro, (1, 0, 0))
+    assert c.sum() == int((L.astype(np.int64) ** 2).sum())
+
+
+def test_autotune_hand_examples():
+    assert O.vbs_autotune([10, 20, 30], [100, 100, 100], (1, 10), (0, 1)).tolist() == \
+        [110, 100, 90]
+    # inside the tolerance band: nothing moves
+    assert O.vbs_autotune([19, 20, 21], [100, 100, 100], (1, 10), (1, 10)).tolist() == \
+        [100, 100, 100]
+    # just outside it (mean 20, band 18 .. 22)
+    assert O.vbs_autotune([17, 20, 23], [100, 100, 100], (1, 10), (1, 10)).tolist() == \
+        [110, 100, 90]
+    # the step is at least one, shares never drop below one or exceed 2^40
+    assert O.vbs_autotune([1, 9], [3, 1], (1, 16), (0, 1)).tolist() == [4, 1]
+    assert O.vbs_autotune([0, 5], [1 << 40, 5], (1, 2), (0, 1)).tolist() == [1 << 40, 3]
+    # equal times: no change
+    assert O.vbs_autotune([7] * 5, [1, 2, 3, 4, 5], (1, 2), (0, 1)).tolist() == [1, 2, 3, 4, 5]
+
+
+def test_autotune_closes_the_cost_gap():
+    """Weights L^1 under-count a quadratic cost: with shares fed back from the
+    modelled time the ranks' costs converge (the purpose of the mechanism) to
+    near the floor that the single costliest sample sets."""
+    rng = np.random.default_rng(11)
+    L = np.minimum(np.ceil(rng.lognormal(6.5, 1.3, size=4096)), 32768).astype(np.int32)
+    W = 64
+    shares = np.full(W, 1 << 16, np.int64)
+
+    def spread(sh):
+        perm, ro, _ = O.balance_vbs_shares(L, W, sh, (1, 1))
+        t = O.rank_cost(L, perm, ro, (1, 0, 0))
+        return t, t.max() / t.mean()
+    t, first = spread(shares)
+    for _ in range(60):
+        shares = O.vbs_autotune(t, shares, (1, 16), (1, 50))
+        t, last = spread(shares)
+    c = L.astype(np.int64) ** 2
+    floor = c.max() / (c.sum() / W)  # one sample's cost over the mean rank's
+    assert first > 3 * last and last < 1.3 * floor
+
+
 # ----------------------------------------------------------------------------
 # bucketize (indexed permute + ranged dispatch)
 
