@@ -127,6 +127,52 @@ int fs_balance_vbs(const int32_t* uih_len, int32_t n, int32_t W, int32_t alpha_n
 size_t fs_balance_workspace_size(int32_t n, int32_t W);
 
 /* ------------------------------------------------------------------------ */
+/* VBS AutoTune -- [FS] 4.1: because the weights L^alpha need not match the */
+/* real execution time, VBS raises or lowers each rank's local batch size by */
+/* how its execution time compares with the global average (Figure 4's      */
+/* AutoTune module; Algorithm 1's input R). The pages give no arithmetic;   */
+/* the built reading moves per-rank shares s_r of the weight:               */
+/*                                                                          */
+/* fs_balance_vbs_shares: fs_balance_vbs with the cut at the shares: with   */
+/* Q_r = s_0 + ... + s_{r-1}, Q = Q_W and S_k the weight of the first k     */
+/* sorted samples (T = S_n), rank r starts at the first k with              */
+/* Q * S_k >= Q_r * T, so each segment is within one boundary sample's      */
+/* weight of T * s_r / Q. Equal shares give exactly fs_balance_vbs's cuts.  */
+/*  shares       device int64 [W], each in [1, 2^40]; others are clamped and */
+/*               flag FS_EF_SHAPE. Other arguments as fs_balance_vbs.        */
+int fs_balance_vbs_shares(const int32_t* uih_len, int32_t n, int32_t W, int32_t alpha_num,
+                          int32_t alpha_den, const int64_t* shares, int32_t* perm,
+                          int32_t* rank_offsets, int64_t* rank_weight, int32_t* err, void* ws,
+                          size_t ws_bytes, hipStream_t stream);
+
+/* fs_rank_cost: modelled execution time of each rank of a partition, for   */
+/* when no measured time exists: cost[r] = the sum over positions j in      */
+/* [rank_offsets[r], rank_offsets[r+1]) of c2 L^2 + c1 L + c0 with          */
+/* L = uih_len[perm[j]] clamped to [0, FS_MAX_UIH] (quadratic attention-like */
+/* plus linear work). Coefficients in [0, 2^16] (else FS_ERR_INVALID_ARG).  */
+/* Offsets are clipped to [0, n]; perm entries outside [0, n) count nothing. */
+/*  uih_len [n], perm [n], rank_offsets [W+1]: a balance call's inputs and  */
+/*  outputs; cost [W] int64 out.                                            */
+int fs_rank_cost(const int32_t* uih_len, int32_t n, const int32_t* perm,
+                 const int32_t* rank_offsets, int32_t W, int64_t c2, int64_t c1, int64_t c0,
+                 int64_t* cost, hipStream_t stream);
+
+/* fs_vbs_autotune: one AutoTune step on shares[W] in place. With the mean  */
+/* m = (t_0 + ... + t_{W-1}) / W of the per-rank times, a rank with         */
+/* t_r > m (1 + tol) gives up d_r = max(1, floor(s_r * step)) of its share,  */
+/* one with t_r < m (1 - tol) gains d_r, the rest keep theirs; shares stay  */
+/* in [1, 2^40]. All integer: W t_r tol_den is compared with                 */
+/* (sum t)(tol_den +- tol_num), step = step_num / step_den.                 */
+/*  times   device int64 [W] in [0, 2^52] (measured, e.g. in ns, or           */
+/*          fs_rank_cost's); values outside are clamped and flag FS_EF_SHAPE, */
+/*          as do shares outside [1, 2^40].                                  */
+/*  0 <= step_num <= step_den <= 2^20, 0 <= tol_num <= tol_den <= 2^20       */
+/*  (else FS_ERR_INVALID_ARG).                                              */
+int fs_vbs_autotune(const int64_t* times, int32_t W, int32_t step_num, int32_t step_den,
+                    int32_t tol_num, int32_t tol_den, int64_t* shares, int32_t* err,
+                    hipStream_t stream);
+
+/* ------------------------------------------------------------------------ */
 /* Indexed permute + ranged dispatch -- [FS] 4.2 (the indexed-permute kernel */
 /* applies the partition to the gathered IDs; the ranged-dispatch kernel    */
 /* prepares the ID AllToAll's per-destination ranges) and 3.2 (batch-major  */

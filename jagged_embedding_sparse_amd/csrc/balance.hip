@@ -202,6 +202,102 @@ k_vbs_cut(const int64_t* __restrict__ wsorted, int32_t n, int32_t W,
     for (int32_t r = threadIdx.x; r < W; r += kCutThreads) rank_weight[r] = scut[r + 1] - scut[r];
 }
 
+// VBS cuts with per-rank shares s_r of the weight (the AutoTune mechanism of
+// section 4.1 and Figure 4 moves them): with Q_r = s_0 + ... + s_{r-1} and
+// Q = Q_W, rank r starts at the first k with Q*S_k >= Q_r*T; equal shares
+// give k_vbs_cut's cuts. The products reach 2^96 (Q < 2^50, T < 2^47), so
+// they are taken in 128 bits. Shares outside [1, 2^40] are clamped and flag
+// FS_EF_SHAPE. Each thread walks its samples in order with a pointer to the
+// next rank to place, found once by binary search over the Q_r in LDS.
+typedef unsigned __int128 u128;
+constexpr int64_t kShareMax = (int64_t)1 << 40;
+
+__device__ __forceinline__ int64_t clamp_share(int64_t x) {
+  return x < 1 ? 1 : (x > kShareMax ? kShareMax : x);
+}
+
+__global__ void __launch_bounds__(kCutThreads)
+k_vbs_cut_shares(const int64_t* __restrict__ wsorted, int32_t n, int32_t W,
+                 const int64_t* __restrict__ shares, int32_t* __restrict__ rank_offsets,
+                 int64_t* __restrict__ rank_weight, int32_t* __restrict__ err) {
+  __shared__ int64_t tmp[17];
+  __shared__ int64_t sQ[FS_MAX_RANKS + 1];    // Q_r
+  __shared__ int64_t scut[FS_MAX_RANKS + 1];  // S at each rank's first sample
+  // prefix of the shares: a few ranks per thread
+  const int32_t pw = (W + kCutThreads - 1) / kCutThreads;
+  const int32_t q0 = min(W, (int32_t)threadIdx.x * pw), q1 = min(W, q0 + pw);
+  int64_t qloc = 0;
+  bool bad = false;
+  for (int32_t r = q0; r < q1; ++r) {
+    const int64_t x = shares[r];
+    bad |= x != clamp_share(x);
+    qloc += clamp_share(x);
+  }
+  flag_err(err, bad, FS_EF_SHAPE);
+  int64_t Q;
+  int64_t qrun = block_excl_scan<int64_t>(qloc, tmp, &Q);
+  for (int32_t r = q0; r < q1; ++r) {
+    sQ[r] = qrun;
+    qrun += clamp_share(shares[r]);
+  }
+  if (threadIdx.x == 0) sQ[W] = Q;
+  // weight prefix, as in k_vbs_cut
+  const int32_t per = (n + kCutThreads - 1) / kCutThreads;
+  const int32_t k0 = min(n, (int32_t)threadIdx.x * per), k1 = min(n, k0 + per);
+  int64_t local = 0;
+  for (int32_t kb = k0; kb < k1; kb += kCutBatch) {
+    int64_t v[kCutBatch];
+#pragma unroll
+    for (int i = 0; i < kCutBatch; ++i) v[i] = kb + i < k1 ? wsorted[kb + i] : 0;
+#pragma unroll
+    for (int i = 0; i < kCutBatch; ++i) local += v[i];
+  }
+  int64_t T;
+  int64_t run = block_excl_scan<int64_t>(local, tmp, &T);  // its barriers publish sQ
+  if (T == 0) {  // no weight: every rank starts at 0, the last ends at n
+    for (int32_t r = threadIdx.x; r <= W; r += kCutThreads) {
+      rank_offsets[r] = r == W ? n : 0;
+      if (rank_weight && r < W) rank_weight[r] = 0;
+    }
+    return;
+  }
+  if (threadIdx.x == 0) {
+    rank_offsets[0] = 0;
+    rank_offsets[W] = n;
+    scut[0] = 0;
+    scut[W] = T;
+  }
+  const u128 uQ = (u128)(uint64_t)Q, uT = (u128)(uint64_t)T;
+  // the first rank r >= 1 whose cut lies beyond S_{k0}: Q_r*T > Q*S_{k0}
+  int32_t lo = 1, hi = W;
+  const u128 a0 = uQ * (uint64_t)run;
+  while (lo < hi) {
+    const int32_t mid = (lo + hi) >> 1;
+    if ((u128)(uint64_t)sQ[mid] * uT > a0) hi = mid;
+    else lo = mid + 1;
+  }
+  int32_t r = lo;
+  for (int32_t kb = k0; kb < k1; kb += kCutBatch) {
+    int64_t v[kCutBatch];
+#pragma unroll
+    for (int i = 0; i < kCutBatch; ++i) v[i] = kb + i < k1 ? wsorted[kb + i] : 0;
+    for (int i = 0; i < kCutBatch && kb + i < k1; ++i) {
+      const int64_t s1 = run + v[i];  // S_{k+1}
+      const u128 b1 = uQ * (uint64_t)s1;
+      // ranks with Q*S_k < Q_r*T <= Q*S_{k+1} start at k + 1
+      while (r < W && (u128)(uint64_t)sQ[r] * uT <= b1) {
+        rank_offsets[r] = kb + i + 1;
+        scut[r] = s1;
+        ++r;
+      }
+      run = s1;
+    }
+  }
+  __syncthreads();
+  if (rank_weight)
+    for (int32_t q = threadIdx.x; q < W; q += kCutThreads) rank_weight[q] = scut[q + 1] - scut[q];
+}
+
 int check_common(const int32_t* uih_len, int32_t n, int32_t W, const int32_t* perm,
                  const int32_t* rank_offsets) {
   if (n < 0 || n > FS_MAX_SAMPLES || W < 1 || W > FS_MAX_RANKS) return FS_ERR_INVALID_ARG;
@@ -275,6 +371,29 @@ extern "C" int fs_balance_vbs(const int32_t* uih_len, int32_t n, int32_t W, int3
   if (rc) return rc;
   hipLaunchKernelGGL(k_vbs_cut, dim3(1), dim3(kCutThreads), 0, stream, wsorted, n, W,
                      rank_offsets, rank_weight);
+  FS_LAUNCH_CHECK();
+  return FS_OK;
+}
+
+extern "C" int fs_balance_vbs_shares(const int32_t* uih_len, int32_t n, int32_t W,
+                                     int32_t alpha_num, int32_t alpha_den, const int64_t* shares,
+                                     int32_t* perm, int32_t* rank_offsets, int64_t* rank_weight,
+                                     int32_t* err, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int rc = check_common(uih_len, n, W, perm, rank_offsets);
+  if (rc) return rc;
+  if (!shares) return FS_ERR_INVALID_ARG;
+  bool ok = (alpha_den == 1 && alpha_num >= 0 && alpha_num <= 2) ||
+            (alpha_den == 2 && alpha_num >= 0 && alpha_num <= 4);
+  if (!ok) return FS_ERR_UNSUPPORTED;
+  if (ws_bytes < fs_balance_workspace_size(n, W) || !ws) return FS_ERR_WORKSPACE;
+  Carve c(ws);
+  int64_t* wsorted = c.take<int64_t>((size_t)(n > 0 ? n : 1));
+  int32_t* cnt = c.take<int32_t>((size_t)(n > 0 ? n : 1) * (size_t)rank_slices(n));
+  rc = launch_sort<false>(uih_len, n, W, perm, rank_offsets, wsorted, alpha_num, alpha_den, cnt,
+                          err, stream);
+  if (rc) return rc;
+  hipLaunchKernelGGL(k_vbs_cut_shares, dim3(1), dim3(kCutThreads), 0, stream, wsorted, n, W,
+                     shares, rank_offsets, rank_weight, err);
   FS_LAUNCH_CHECK();
   return FS_OK;
 }

@@ -50,6 +50,10 @@ _c_balance_fbs = _sig("fs_balance_fbs", C.c_int, _P, _i32, _i32, _P, _P, _P, _P,
 _c_balance_vbs = _sig("fs_balance_vbs", C.c_int, _P, _i32, _i32, _i32, _i32, _P, _P, _P, _P, _P,
                       _sz, _P)
 _c_balance_ws = _sig("fs_balance_workspace_size", _sz, _i32, _i32)
+_c_balance_shares = _sig("fs_balance_vbs_shares", C.c_int, _P, _i32, _i32, _i32, _i32, _P, _P,
+                         _P, _P, _P, _P, _sz, _P)
+_c_rank_cost = _sig("fs_rank_cost", C.c_int, _P, _i32, _P, _P, _i32, _i64, _i64, _i64, _P, _P)
+_c_autotune = _sig("fs_vbs_autotune", C.c_int, _P, _i32, _i32, _i32, _i32, _i32, _P, _P, _P)
 _c_bucketize = _sig("fs_bucketize_permute", C.c_int, _P, _i64, _P, _i32, _TP, _i32, _P, _P, _i32,
                     _P, _P, _P, _P, _P, _P, _P, _sz, _P)
 _c_bucketize_ws = _sig("fs_bucketize_workspace_size", _sz, _i64, _i32, _i32, _i32)
@@ -70,6 +74,7 @@ _c_strerror = _sig("fs_strerror", C.c_char_p, C.c_int)
 _c_version = _sig("fs_version", C.c_int)
 
 EXPORTED = ["fs_balance_fbs", "fs_balance_vbs", "fs_balance_workspace_size",
+            "fs_balance_vbs_shares", "fs_rank_cost", "fs_vbs_autotune",
             "fs_bucketize_permute", "fs_bucketize_workspace_size", "fs_unique_collision_split",
             "fs_unique_workspace_size", "fs_jagged_lookup", "fs_ranged_combine",
             "fs_keyed_transpose", "fs_keyed_transpose_workspace_size",
@@ -181,6 +186,46 @@ def fs_balance_vbs(uih_len, W, alpha=(3, 2), perm=None, rank_offsets=None, rank_
                                             _ptr(perm), _ptr(ro), _ptr(rw), _ptr(err), _ptr(ws),
                                             ws.numel(), _stream(stream)))
     return perm, ro, rw
+
+
+def fs_balance_vbs_shares(uih_len, W, shares, alpha=(3, 2), perm=None, rank_offsets=None,
+                          rank_weight=None, err=None, ws=None, stream=None):
+    """VBS cut at per-rank shares (device int64 [W]) of the weight."""
+    n = uih_len.numel()
+    perm = perm if perm is not None else torch.empty(n, dtype=torch.int32, device=_dev())
+    ro = rank_offsets if rank_offsets is not None else torch.empty(W + 1, dtype=torch.int32,
+                                                                   device=_dev())
+    rw = rank_weight if rank_weight is not None else torch.empty(W, dtype=torch.int64,
+                                                                 device=_dev())
+    assert shares.dtype == torch.int64 and shares.numel() == W
+    ws = _ws(balance_workspace_size(n, W), ws)
+    _check("fs_balance_vbs_shares",
+           _c_balance_shares(_ptr(uih_len), n, W, int(alpha[0]), int(alpha[1]), _ptr(shares),
+                             _ptr(perm), _ptr(ro), _ptr(rw), _ptr(err), _ptr(ws), ws.numel(),
+                             _stream(stream)))
+    return perm, ro, rw
+
+
+def fs_rank_cost(uih_len, perm, rank_offsets, coef=(1, 0, 0), cost=None, stream=None):
+    """Modelled per-rank time: sum of c2 L^2 + c1 L + c0 over each rank's samples."""
+    W = rank_offsets.numel() - 1
+    cost = cost if cost is not None else torch.empty(W, dtype=torch.int64, device=_dev())
+    c2, c1, c0 = (int(c) for c in coef)
+    _check("fs_rank_cost", _c_rank_cost(_ptr(uih_len), uih_len.numel(), _ptr(perm),
+                                        _ptr(rank_offsets), W, c2, c1, c0, _ptr(cost),
+                                        _stream(stream)))
+    return cost
+
+
+def fs_vbs_autotune(times, shares, step=(1, 16), tol=(1, 20), err=None, stream=None):
+    """One AutoTune step on shares (device int64 [W], in place) from per-rank
+    times (device int64 [W])."""
+    W = shares.numel()
+    assert times.dtype == torch.int64 and times.numel() == W
+    _check("fs_vbs_autotune", _c_autotune(_ptr(times), W, int(step[0]), int(step[1]),
+                                          int(tol[0]), int(tol[1]), _ptr(shares), _ptr(err),
+                                          _stream(stream)))
+    return shares
 
 
 def bucketize_workspace_size(n_tok, n, T, W):

@@ -212,3 +212,35 @@ def test_keyed_transpose_rejects(L):
     assert call(outv=FAKE + 2, eb=4) == L.FS_ERR_INVALID_ARG
     assert call(ws_bytes=ws_n - 1) == L.FS_ERR_WORKSPACE
     assert call(ws=None) == L.FS_ERR_WORKSPACE
+
+
+def test_autotune_calls_reject(L):
+    ws_n = L.balance_workspace_size(100, 8)
+    sh = L._c_balance_shares
+
+    def cut(shares=FAKE, a=(3, 2), ws_bytes=ws_n, W=8):
+        return sh(FAKE, 100, W, a[0], a[1], shares, FAKE, FAKE, None, None, FAKE, ws_bytes, None)
+    assert cut(shares=None) == L.FS_ERR_INVALID_ARG
+    assert cut(a=(1, 3)) == L.FS_ERR_UNSUPPORTED
+    assert cut(W=0) == L.FS_ERR_INVALID_ARG
+    assert cut(ws_bytes=ws_n - 1) == L.FS_ERR_WORKSPACE
+    rc = L._c_rank_cost
+
+    def cost(c=(1, 0, 0), n=100, W=8, perm=FAKE):
+        return rc(FAKE, n, perm, FAKE, W, c[0], c[1], c[2], FAKE, None)
+    assert cost(c=(-1, 0, 0)) == L.FS_ERR_INVALID_ARG
+    assert cost(c=(1, 1 << 17, 0)) == L.FS_ERR_INVALID_ARG
+    assert cost(n=L.FS_MAX_SAMPLES + 1) == L.FS_ERR_INVALID_ARG
+    assert cost(W=L.FS_MAX_RANKS + 1) == L.FS_ERR_INVALID_ARG
+    assert cost(perm=None) == L.FS_ERR_INVALID_ARG
+    at = L._c_autotune
+
+    def tune(step=(1, 16), tol=(1, 20), W=8, shares=FAKE):
+        return at(FAKE, W, step[0], step[1], tol[0], tol[1], shares, None, None)
+    assert tune(step=(2, 1)) == L.FS_ERR_INVALID_ARG
+    assert tune(step=(1, 0)) == L.FS_ERR_INVALID_ARG
+    assert tune(step=(1, (1 << 20) + 1)) == L.FS_ERR_INVALID_ARG
+    assert tune(tol=(3, 2)) == L.FS_ERR_INVALID_ARG
+    assert tune(tol=(-1, 2)) == L.FS_ERR_INVALID_ARG
+    assert tune(W=0) == L.FS_ERR_INVALID_ARG
+    assert tune(shares=None) == L.FS_ERR_INVALID_ARG

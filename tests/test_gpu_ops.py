@@ -95,6 +95,134 @@ def test_balance_workload_lengths(k):
         assert np.array_equal(host(vrw), ovrw)
 
 
+# ----------------------------------------------------------------------------- VBS AutoTune
+
+SHARE_CASES = [(64, 4), (1024, 64), (4096, 512), (16384, 1024), (0, 3), (1, 1), (7, 8), (100, 1024),
+               (4097, 512)]
+
+
+def _shares(rng, W, kind):
+    if kind == "equal":
+        return np.full(W, 1 << 16, np.int64)
+    if kind == "wide":  # a few ranks with huge shares, many with tiny ones
+        x = rng.integers(1, 50, W).astype(np.int64)
+        x[rng.random(W) < 0.1] = 1 << 40
+        return x
+    return rng.integers(1, 1 << 20, W).astype(np.int64)
+
+
+@pytest.mark.parametrize("kind", ["equal", "random", "wide"])
+@pytest.mark.parametrize("alpha", [(3, 2), (1, 1), (2, 1)])
+@pytest.mark.parametrize("N,W", SHARE_CASES)
+def test_vbs_shares_parity(N, W, alpha, kind):
+    say("vbs shares", N, W, alpha, kind)
+    rng = np.random.default_rng(N + 3 * W)
+    L = _lengths(N, N + W, "skew")
+    sh = _shares(rng, W, kind)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    perm, ro, rw = lib.fs_balance_vbs_shares(cu(L), W, cu(sh), alpha, err=err)
+    operm, oro, orw = O.balance_vbs_shares(L, W, sh, alpha)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(ro), oro)
+    assert np.array_equal(host(perm), operm)
+    assert np.array_equal(host(rw), orw)
+    assert int(err.item()) == 0
+    if kind == "equal":  # the same cuts as the plain VBS call
+        _, ro2, rw2 = lib.fs_balance_vbs(cu(L), W, alpha)
+        torch.cuda.synchronize()
+        assert np.array_equal(host(ro2), oro) and np.array_equal(host(rw2), orw)
+
+
+def test_vbs_shares_out_of_range_are_clamped_and_flagged():
+    L = _lengths(3000, 9, "skew")
+    sh = np.array([0, -5, 1, 7, (1 << 40) + 1, 1 << 62, 3, 1], np.int64)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    perm, ro, rw = lib.fs_balance_vbs_shares(cu(L), 8, cu(sh), (3, 2), err=err)
+    clamped = np.clip(sh, 1, 1 << 40)
+    operm, oro, orw = O.balance_vbs_shares(L, 8, clamped, (3, 2))
+    torch.cuda.synchronize()
+    assert int(err.item()) == lib.FS_EF_SHAPE
+    assert np.array_equal(host(ro), oro) and np.array_equal(host(rw), orw)
+
+
+@pytest.mark.parametrize("coef", [(1, 0, 0), (3, 700, 50000), (0, 1, 0), (65536, 65536, 65536)])
+@pytest.mark.parametrize("N,W", [(4096, 512), (16384, 1024), (1000, 7), (0, 5), (5, 64)])
+def test_rank_cost_parity(N, W, coef):
+    say("rank cost", N, W, coef)
+    L = _lengths(N, N * 5 + W, "skew")
+    perm, ro, _ = lib.fs_balance_vbs(cu(L), W, (1, 1))
+    cost = lib.fs_rank_cost(cu(L), perm, ro, coef)
+    torch.cuda.synchronize()
+    ref = O.rank_cost(L, host(perm), host(ro), coef)
+    assert np.array_equal(host(cost), ref)
+
+
+@pytest.mark.parametrize("step,tol", [((1, 16), (1, 20)), ((1, 2), (0, 1)), ((0, 1), (1, 1)),
+                                      ((1, 1), (1, 1000)), ((3, 1 << 20), (1 << 19, 1 << 20))])
+@pytest.mark.parametrize("W", [1, 2, 64, 513, 1024])
+def test_vbs_autotune_parity(W, step, tol):
+    say("autotune", W, step, tol)
+    rng = np.random.default_rng(W * 31 + step[1])
+    times = rng.integers(0, 1 << 40, W).astype(np.int64)
+    times[rng.random(W) < 0.2] = int(np.median(times))  # exact ties with other ranks
+    sh = rng.integers(1, 1 << 40, W).astype(np.int64)
+    sh[rng.random(W) < 0.1] = 1
+    d_sh = cu(sh)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    lib.fs_vbs_autotune(cu(times), d_sh, step, tol, err=err)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(d_sh), O.vbs_autotune(times, sh, step, tol))
+    assert int(err.item()) == 0
+
+
+def test_vbs_autotune_clamps_and_flags():
+    times = np.array([-4, 10, (1 << 52) + 9, 30], np.int64)
+    sh = np.array([0, 1 << 41, 100, 100], np.int64)
+    d_sh = cu(sh)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    lib.fs_vbs_autotune(cu(times), d_sh, (1, 10), (1, 20), err=err)
+    torch.cuda.synchronize()
+    ref = O.vbs_autotune(np.clip(times, 0, 1 << 52), np.clip(sh, 1, 1 << 40), (1, 10), (1, 20))
+    assert np.array_equal(host(d_sh), ref)
+    assert int(err.item()) == lib.FS_EF_SHAPE
+
+
+@pytest.mark.parametrize("k", [3, 4])
+def test_autotune_loop_on_device(k):
+    """Forty iterations of cut -> modelled cost -> AutoTune on the device,
+    with no host synchronisation between them, replayed by the oracle: every
+    iteration's cuts and shares bit-exact. On workload 3 the cost spread
+    shrinks; workload 4's (weights L^2, 256 ranks for 2048 samples) is set
+    by single samples, which no share can split."""
+    w = synth.workload(k)
+    bat = synth.Batches(w, k)
+    W = w.world
+    alpha = w.alpha
+    sh = torch.full((W,), 1 << 16, dtype=torch.int64, device="cuda")
+    osh = np.full(W, 1 << 16, np.int64)
+    lens = [bat.batch(i)["uih_len"] for i in range(4)]
+    d_lens = [cu(x) for x in lens]
+    got = []
+    for it in range(40):
+        perm, ro, _ = lib.fs_balance_vbs_shares(d_lens[it % 4], W, sh, alpha)
+        cost = lib.fs_rank_cost(d_lens[it % 4], perm, ro, (1, 64, 0))
+        got.append((ro.clone(), sh.clone()))
+        lib.fs_vbs_autotune(cost, sh, (1, 16), (1, 50))
+    torch.cuda.synchronize()
+    spreads = []
+    for it in range(40):
+        L = lens[it % 4]
+        operm, oro, _ = O.balance_vbs_shares(L, W, osh, alpha)
+        assert np.array_equal(host(got[it][0]), oro), it
+        assert np.array_equal(host(got[it][1]), osh), it
+        c = O.rank_cost(L, operm, oro, (1, 64, 0))
+        spreads.append(c.max() / c.mean())
+        osh = O.vbs_autotune(c, osh, (1, 16), (1, 50))
+    assert np.array_equal(host(sh), osh)
+    if k == 3:
+        assert min(spreads[-5:]) < 0.9 * spreads[0]
+
+
 # ----------------------------------------------------------------------------- bucketize
 
 
