@@ -51,6 +51,9 @@ def parse():
     ap.add_argument("--lookahead", type=int, choices=[1, 2], default=2,
                     help="iterations the index stages run ahead of the lookup (2: beside the "
                          "update and the lookup of the iteration before)")
+    ap.add_argument("--autotune", action="store_true",
+                    help="VBS AutoTune: shares of the weight moved every step by the modelled "
+                         "per-rank time (VBS workloads only)")
     return ap.parse_args()
 
 
@@ -115,7 +118,7 @@ def main():
 
     ahead = args.lookahead == 2 and not args.sync
     step = SparseStep(w, weights, states, cap, lookup=args.lookup,
-                      lookahead=2 if ahead else 1)
+                      lookahead=2 if ahead else 1, autotune={} if args.autotune else None)
     n_tok = [b["n_tok"] for b in host_batches]
     step.prologue(dev_batches[0], batch_after=dev_batches[1 % NB] if ahead else None)
     if args.sync:
@@ -283,7 +286,8 @@ def main():
             "global_batch": w.batch, "virtual_ranks": w.world, "tables": tables,
             "optimizer": w.optim, "ids_per_step": ids_timed / args.steps,
             "weights": sorted({t.dtype for t in w.tables}), "grad_accumulate": "f64",
-            "distinct_batches": NB, "schedule": schedule},
+            "distinct_batches": NB, "schedule": schedule,
+            "autotune": bool(args.autotune)},
         "roofline": {
             "bound": "hbm", "achieved": dom_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": dom_gbps / HBM_PEAK_GBPS, "traffic": traffic,

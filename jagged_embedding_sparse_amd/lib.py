@@ -414,6 +414,28 @@ def prepare_balance(balancer, W, alpha, perm, rank_offsets, rank_weight, err, ws
     return Prepared("fs_balance_vbs", _c_balance_vbs, args, dict(uih=0, n=1, stream=11))
 
 
+def prepare_balance_shares(W, alpha, shares, perm, rank_offsets, rank_weight, err, ws):
+    """fs_balance_vbs_shares; call with uih=, n=, stream=."""
+    args = [None, 0, W, int(alpha[0]), int(alpha[1]), _ptr(shares), _ptr(perm),
+            _ptr(rank_offsets), _ptr(rank_weight), _ptr(err), _ptr(ws), ws.numel(), None]
+    return Prepared("fs_balance_vbs_shares", _c_balance_shares, args, dict(uih=0, n=1, stream=12))
+
+
+def prepare_rank_cost(perm, rank_offsets, coef, cost):
+    """fs_rank_cost into `cost`; call with uih=, n=, stream=."""
+    c2, c1, c0 = (int(c) for c in coef)
+    args = [None, 0, _ptr(perm), _ptr(rank_offsets), rank_offsets.numel() - 1, c2, c1, c0,
+            _ptr(cost), None]
+    return Prepared("fs_rank_cost", _c_rank_cost, args, dict(uih=0, n=1, stream=9))
+
+
+def prepare_autotune(times, shares, step, tol, err):
+    """fs_vbs_autotune on `shares` from `times`; call with stream=."""
+    args = [_ptr(times), shares.numel(), int(step[0]), int(step[1]), int(tol[0]), int(tol[1]),
+            _ptr(shares), _ptr(err), None]
+    return Prepared("fs_vbs_autotune", _c_autotune, args, dict(stream=8))
+
+
 def prepare_bucketize(rows, perm, rank_offsets, W, out, err, ws):
     """fs_bucketize_permute into `out` (the dict fs_bucketize_permute returns);
     call with ids=, n_tok=, so=, n=, stream=."""

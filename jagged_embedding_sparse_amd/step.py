@@ -40,6 +40,11 @@ instead of only the update. Three iteration states are alive at once (i being
 updated, i+1 looked up, i+2 indexed); the result is again the synchronous
 loop's.
 
+With `autotune` (VBS only; section 4.1's AutoTune), the balance cuts at
+per-rank shares of the weight, and right after each balance the modelled time
+of the partition it made moves the shares for the next one -- two small
+launches on the index stream, no host synchronisation.
+
 Buffers are allocated once at capacity; per-iteration state is double
 buffered (triple with lookahead=2), and every C call is marshalled once per
 state slot. Every stream keeps the default priority.
@@ -136,16 +141,22 @@ class IterState:
 
 
 _LOOKUP_MODES = ("split", "joined", "auto")
+# VBS AutoTune: modelled time c2 L^2 + c1 L + c0 per sample (coef), shares
+# moved by max(1, share * step) outside a band of +-tol around the mean time,
+# every share starting at init
+AUTOTUNE_DEFAULTS = dict(coef=(1, 64, 0), step=(1, 16), tol=(1, 50), init=1 << 16)
 _CALIB_STEPS = 3  # steps timed by lookup="auto" before it decides
 
 
 class SparseStep:
     def __init__(self, workload, weights, states, n_tok_cap, device=None, lookup="auto",
-                 lookahead=1):
+                 lookahead=1, autotune=None):
         if lookup not in _LOOKUP_MODES:
             raise ValueError(f"lookup must be one of {_LOOKUP_MODES}, not {lookup!r}")
         if lookahead not in (1, 2):
             raise ValueError(f"lookahead must be 1 or 2, not {lookahead!r}")
+        if autotune is not None and workload.balancer != "vbs":
+            raise ValueError("autotune needs the VBS balancer")
         self.w = workload
         self.W = workload.world
         self.T = len(weights)
@@ -184,6 +195,14 @@ class SparseStep:
         self.joined = lookup == "joined" or lookahead == 2
         self._calib = []  # (start, update end, index end) event triples
         self._calib_left = _CALIB_STEPS if (lookup == "auto" and lookahead == 1) else 0
+        # VBS AutoTune: per-rank shares of the weight, moved after every
+        # balance by the modelled time of the partition just made
+        self.autotune = None
+        if autotune is not None:
+            self.autotune = {**AUTOTUNE_DEFAULTS, **autotune}
+            self.shares = torch.full((W,), int(self.autotune["init"]), dtype=torch.int64,
+                                     device=d)
+            self.rank_cost = torch.empty(W, dtype=torch.int64, device=d)
 
     def _t(self, name, stream):
         """Context that brackets one C call with HIP events on its stream."""
@@ -233,9 +252,19 @@ class SparseStep:
         n_tok = int(ids.shape[1])
         st.n_tok = n_tok
         sh = stream.cuda_stream
-        pb = self._prep(("bal", st.slot), lambda: lib.prepare_balance(
-            self.w.balancer, W, self.w.alpha, st.perm, st.rank_offsets, st.rank_weight, self.err,
-            self.ws_bal))
+        at = self.autotune
+        if at is None:
+            pb = self._prep(("bal", st.slot), lambda: lib.prepare_balance(
+                self.w.balancer, W, self.w.alpha, st.perm, st.rank_offsets, st.rank_weight,
+                self.err, self.ws_bal))
+        else:
+            pb = self._prep(("bal", st.slot), lambda: lib.prepare_balance_shares(
+                W, self.w.alpha, self.shares, st.perm, st.rank_offsets, st.rank_weight, self.err,
+                self.ws_bal))
+            pc = self._prep(("cost", st.slot), lambda: lib.prepare_rank_cost(
+                st.perm, st.rank_offsets, at["coef"], self.rank_cost))
+            pa = self._prep(("tune",), lambda: lib.prepare_autotune(
+                self.rank_cost, self.shares, at["step"], at["tol"], self.err))
         pk = self._prep(("bkt", st.slot), lambda: lib.prepare_bucketize(
             self.rows, st.perm, st.rank_offsets, W, st.bucket, self.err, self.ws_bkt))
         pu = self._prep(("uq", st.slot, prev.slot if prev is not None else -1),
@@ -245,6 +274,10 @@ class SparseStep:
                             prev.cls_next if prev is not None else None, self.ws_uq))
         with self._t("balance", stream):
             pb(uih=lib._ptr(uih), n=uih.numel(), stream=sh)
+        if at is not None:  # the shares for the next balance
+            with self._t("autotune", stream):
+                pc(uih=lib._ptr(uih), n=uih.numel(), stream=sh)
+                pa(stream=sh)
         with self._t("bucketize", stream):
             pk(ids=lib._ptr(ids), n_tok=n_tok, so=lib._ptr(so), n=so.numel() - 1, stream=sh)
         with self._t("unique_split", stream):

@@ -318,9 +318,15 @@ class SyncRun:
     gradient of the balanced batch.
     """
 
-    def __init__(self, workload, stores):
+    def __init__(self, workload, stores, autotune=None):
+        """autotune: None, or dict(coef, step, tol, init) -- VBS cut at
+        per-rank shares, moved after each balance by the modelled time of
+        the partition it made ([FS] 4.1 autotune)."""
         self.w = workload
         self.stores = stores
+        self.autotune = autotune
+        if autotune is not None:
+            self.shares = np.full(workload.world, int(autotune["init"]), np.int64)
         self.rows = np.array([t.rows for t in workload.tables], np.int64)
         self.row_base = np.zeros(len(self.rows), np.int64)
         self.row_base[1:] = np.cumsum(self.rows)[:-1]
@@ -331,8 +337,13 @@ class SyncRun:
         if w.balancer == "fbs":
             perm, ro = balance_fbs(batch["uih_len"], w.world)
             rw = None
-        else:
+        elif self.autotune is None:
             perm, ro, rw = balance_vbs(batch["uih_len"], w.world, w.alpha)
+        else:
+            at = self.autotune
+            perm, ro, rw = balance_vbs_shares(batch["uih_len"], w.world, self.shares, w.alpha)
+            cost = rank_cost(batch["uih_len"], perm, ro, at["coef"])
+            self.shares = vbs_autotune(cost, self.shares, at["step"], at["tol"])
         bk = bucketize(batch["ids"], batch["sample_offsets"], self.rows, perm, ro, w.world)
         uq = unique(bk["shard_keys"], bk["shard_bm"], self.rows, w.world)
         cls, pcls, counts = collision(uq["unique"], self.prev_unique)

@@ -145,6 +145,9 @@ def test_step_rejects_unknown_lookup_schedule():
         SparseStep(None, [], [], 1, lookup="eager")
     with pytest.raises(ValueError):
         SparseStep(None, [], [], 1, lookahead=3)
+    from jagged_embedding_sparse_amd import synth
+    with pytest.raises(ValueError):  # AutoTune moves VBS shares: no FBS
+        SparseStep(synth.workload(1), [], [], 1, autotune={})
 
 
 def test_prepared_calls_match_the_c_signatures(L, monkeypatch):
@@ -167,6 +170,9 @@ def test_prepared_calls_match_the_c_signatures(L, monkeypatch):
         L.prepare_lookup(weights, 4, uq, [t, t]),
         L.prepare_lookup(weights, 4, uq, [t, t], L.FS_COLLISION, t),
         L.prepare_update(weights, [t, t], 4, uq, "rw_adagrad", 0.1, 1e-8, L.FS_ALL, None, ws),
+        L.prepare_balance_shares(4, (3, 2), t, t, t, t, t, ws),
+        L.prepare_rank_cost(t, torch.zeros(5), (1, 64, 0), t),
+        L.prepare_autotune(t, t, (1, 16), (1, 50), t),
     ]
     for p in calls:
         assert len(p.args) == len(p.fn.argtypes), p.name

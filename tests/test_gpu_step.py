@@ -16,7 +16,7 @@ import torch
 from harness import (balanced_grads, gpu_tables, host, rel_err_rows, rows_now, snapshot_stores,
                      store_vals_f32, to_dev, touched_rows)
 from jagged_embedding_sparse_amd import synth
-from jagged_embedding_sparse_amd.step import SparseStep
+from jagged_embedding_sparse_amd.step import AUTOTUNE_DEFAULTS, SparseStep
 from oracle import oracle as O
 
 pytestmark = pytest.mark.gpu
@@ -91,9 +91,11 @@ def step_rowbase(w):
     return np.concatenate([[0], np.cumsum(rows)[:-1]])
 
 
-def run_parity(k, balancer=None, iters=None, seed=None, lookahead=1):
+def run_parity(k, balancer=None, iters=None, seed=None, lookahead=1, autotune=None):
     """k: a workload number, or a synth.Workload. lookahead=2 runs the step
-    with the index stages two iterations ahead (the bench's schedule)."""
+    with the index stages two iterations ahead (the bench's schedule);
+    autotune (a dict of AUTOTUNE_DEFAULTS' keys) tunes the VBS shares on both
+    sides."""
     w = k if isinstance(k, synth.Workload) else synth.workload(k, balancer)
     seed = (k if isinstance(k, int) else 77) if seed is None else seed
     K = iters or w.iterations
@@ -105,7 +107,8 @@ def run_parity(k, balancer=None, iters=None, seed=None, lookahead=1):
     stores = snapshot_stores(weights, states, rows_t)
     init_vals = [store_vals_f32(s).copy() for s in stores]
     # oracle: synchronous loop
-    orun = O.SyncRun(w, stores)
+    at = None if autotune is None else {**AUTOTUNE_DEFAULTS, **autotune}
+    orun = O.SyncRun(w, stores, at)
     outs, grads = [], []
     for i, b in enumerate(batches):
         def gfn(o, i=i, b=b):
@@ -116,7 +119,7 @@ def run_parity(k, balancer=None, iters=None, seed=None, lookahead=1):
     say("oracle done")
     # GPU: prioritized schedule
     cap = max(b["n_tok"] for b in batches)
-    step = SparseStep(w, weights, states, cap, lookahead=lookahead)
+    step = SparseStep(w, weights, states, cap, lookahead=lookahead, autotune=at)
     ahead = lookahead == 2
     exact = w.optim == "sgd" and all(t.dtype == "f32" for t in w.tables)
     worst = 0.0
@@ -169,6 +172,14 @@ def test_workload3_vbs():
 @pytest.mark.timeout(600)
 def test_workload4_vbs_four_tables():
     run_parity(4, iters=3)
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("lookahead", [1, 2])
+def test_workload3_vbs_autotune(lookahead):
+    """The step with AutoTune moving the VBS shares every iteration (a large
+    step, so that the cuts really move) equals the oracle's loop."""
+    run_parity(3, iters=5, lookahead=lookahead, autotune=dict(step=(1, 4), tol=(0, 1)))
 
 
 @pytest.mark.timeout(600)
