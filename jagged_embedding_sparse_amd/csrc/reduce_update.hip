@@ -237,40 +237,43 @@ __global__ void __launch_bounds__(kThreads) k_short(RUArgs a) {
     if (!actm) continue;
     const uint32_t row = act ? (uint32_t)(a.unique[uu] - a.row_base) : 0u;
     const float st = (act && ada) ? a.state[row] : 0.f;
+    // the row's (at most kLong) gradient slots, loaded once per unit beside
+    // its key and state: a batch below then waits for one round of loads
+    // (its gradient and weight rows), not for the slots first
+    int32_t obm[kLong];
+#pragma unroll
+    for (int m = 0; m < kLong; ++m) obm[m] = (act && m < hi - lo) ? a.occ_bm[lo + m] : 0;
 #pragma unroll 1
     for (int j0 = 0; j0 < unit; j0 += PER) {
       const uint64_t win = (PER >= kWave) ? ~0ull : (((1ull << PER) - 1ull) << j0);
       if (!(actm & win)) continue;
-      int32_t jlo[R], jhi[R];
+      int32_t jlen[R], jj[R];
       uint32_t jrow[R];
       float jst[R];
       bool ja[R];
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         const int j = j0 + r * M::GPW + grp;
+        jj[r] = j;
         ja[r] = (actm >> j) & 1ull;
-        jlo[r] = __shfl(lo, j, kWave);
-        jhi[r] = __shfl(hi, j, kWave);
+        jlen[r] = __shfl(hi - lo, j, kWave);
         jrow[r] = (uint32_t)__shfl((int)row, j, kWave);
         jst[r] = __shfl(st, j, kWave);
       }
-      // a short row has at most kLong occurrences: lanes sub < kLong of the
-      // group load their indices, then all of its gradient rows load at once
+      // a short row has at most kLong occurrences: its weight row and all of
+      // its gradient rows load at once
       RowW<D, WT> wr[R];
       double acc[R][M::CPL];
-      int32_t bmv[R];
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        bmv[r] = (ja[r] && sub < jhi[r] - jlo[r]) ? a.occ_bm[jlo[r] + sub] : 0;
+      for (int r = 0; r < R; ++r)
         if (ja[r]) load_w<D, WT>(a, jrow[r], sub, wr[r]);
-      }
 #pragma unroll
       for (int r = 0; r < R; ++r) {
-        const int len = ja[r] ? jhi[r] - jlo[r] : 0;
+        const int len = ja[r] ? jlen[r] : 0;
         float4 gv[kLong][M::NV];
 #pragma unroll
         for (int m = 0; m < kLong; ++m) {
-          const int32_t bm = __shfl(bmv[r], grp * M::LPG + m, kWave);
+          const int32_t bm = __shfl(obm[m], jj[r], kWave);
           if (m < len) {
             const float4* gp = (const float4*)(a.grad + (int64_t)bm * D);
 #pragma unroll
