@@ -1,16 +1,21 @@
 """Benchmark of the prioritized jagged sparse step on one MI355X.
 
-A step is one pass of the whole hot path over one batch: on stream B the
-update of every unique row of iteration i (segment-reduce + optimizer); on
-stream A balance (FBS or VBS), indexed permute + shard bucketize, dedup +
-collision split of batch i+1 against batch i, and the lookup of its exclusive
-rows; then, once B is done, the lookup of its collision rows on A. With
---sync everything runs on one stream in the order index, update, lookup. Inputs (IDs, lengths, gradients, tables) are resident
-in HBM before the timed region; the timed region is K steps bracketed by
+A step is one pass of the whole hot path over one batch. Default schedule
+(--lookahead 2): on the caller's stream the update of every unique row of
+iteration i (segment-reduce + optimizer), then the lookup of every row of
+iteration i+1; beside them, on stream A, balance (FBS or VBS), indexed
+permute + shard bucketize and dedup + collision split of the batch after
+next. --lookahead 1 runs the index stages one iteration ahead instead, with
+the exclusive rows' lookup ahead of the update where that pays (--lookup);
+--sync runs everything on one stream in the order index, update, lookup.
+Inputs (IDs, lengths, gradients, tables) are resident in HBM before the
+timed region; the timed region is K steps bracketed by
 torch.cuda.synchronize().
 
 value = IDs/s (token x table lookups of the new batch per step, summed over
-the K steps, divided by the elapsed time of the K steps).
+the K steps, divided by the elapsed time of the K steps). Extra steps after
+the timed ones give the per-stage breakdown and the per-step median, minimum
+and maximum.
 
 Defaults: workload 5 (B=4096, W=512, one 200M x 128 bf16 table with row-wise
 Adagrad, lognormal(6.5, 1.3) lengths capped at 32768, ~6.3M IDs per batch).
@@ -190,6 +195,27 @@ def main():
     step.timer = None
     stage_ms = brk.ms()
 
+    # ---------------------------------------------------------------- per-step spread
+    # K more steps with one event per step on the stream that ends each step
+    # (kept out of the timed region: each record costs the GPU a few
+    # microseconds): with the index stages two ahead the caller's stream,
+    # whose lookup waits for the index stream; otherwise stream A, whose
+    # last lookup waits for the update (and with --sync runs everything).
+    end_stream = torch.cuda.current_stream() if ahead else step.sA
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    for e in evs:  # first records take fresh runtime resources: not in the loop
+        e.record(end_stream)
+    torch.cuda.synchronize()
+    evs[0].record(end_stream)
+    for j in range(args.steps):
+        p = k % NB
+        k += 1
+        run_step(dev_batches[k % NB], [g[:n_tok[p]] for g in grads_dev], k)
+        evs[j + 1].record(end_stream)
+    step.join()
+    torch.cuda.synchronize()
+    per_step = np.array([evs[j].elapsed_time(evs[j + 1]) for j in range(args.steps)])
+
     # ---------------------------------------------------------------- accounting
     # Units per batch pair (p -> p+1) depend only on the IDs, so one more cycle
     # of steps, synchronised, gives them for every pair the timed steps used.
@@ -299,6 +325,10 @@ def main():
             "frac": step_gbps / HBM_PEAK_GBPS},
         "stages_ms": stage_avg,
         "stages_note": f"stage breakdown from {n_brk} extra steps with every stage timed",
+        "per_step_ms": {"median": float(np.median(per_step)), "min": float(per_step.min()),
+                        "max": float(per_step.max()),
+                        "note": f"{args.steps} extra steps, one event per step on the stream "
+                                "that ends it"},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out))
