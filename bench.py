@@ -363,7 +363,19 @@ def cpu_baseline(w, seed, host_batches, grads_host, weights, states):
     return {"value": ids / dt, "unit": "IDs/s", "cores": 1, "kind": "oracle",
             "sample": f"one synchronous iteration (balance, bucketize, dedup, collision split, "
                       f"lookup, fp64 reduce, update) of batch 1 of the same workload, {ids} IDs, "
-                      f"{dt:.2f} s"}
+                      f"{dt:.2f} s",
+            "host": f"{_cpu_model()}, {os.cpu_count()} logical CPUs visible, 1 used"}
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown CPU"
 
 
 if __name__ == "__main__":
