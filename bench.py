@@ -56,6 +56,9 @@ def parse():
     ap.add_argument("--lookahead", type=int, choices=[1, 2], default=2,
                     help="iterations the index stages run ahead of the lookup (2: beside the "
                          "update and the lookup of the iteration before)")
+    ap.add_argument("--layout", choices=["dense", "rowstate", "rowstate256"], default="dense",
+                    help="tables as dense [rows][dim] with a separate state array, or each "
+                         "row's Adagrad state in the row's own padding")
     ap.add_argument("--autotune", action="store_true",
                     help="VBS AutoTune: shares of the weight moved every step by the modelled "
                          "per-rank time (VBS workloads only)")
@@ -111,10 +114,20 @@ def main():
                         ids=torch.from_numpy(b["ids"]).cuda()) for b in host_batches]
     cap = max(b["n_tok"] for b in host_batches)
     weights, states = [], []
+    ada = w.optim == "rw_adagrad"
     for t, spec in enumerate(w.tables):
-        weights.append(synth.init_table(spec.rows, spec.dim, spec.dtype, seed, "cuda", table=t))
-        states.append(torch.zeros(spec.rows, dtype=torch.float32, device="cuda")
-                      if w.optim == "rw_adagrad" else None)
+        if args.layout.startswith("rowstate"):
+            tdt = torch.float32 if spec.dtype == "f32" else torch.bfloat16
+            wv, st = lib.alloc_table(spec.rows, spec.dim, tdt, ada, device="cuda",
+                                     align=256 if args.layout == "rowstate256" else 16)
+            weights.append(synth.init_table(spec.rows, spec.dim, spec.dtype, seed, "cuda",
+                                            table=t, out=wv))
+            states.append(st.zero_() if st is not None else None)
+        else:
+            weights.append(synth.init_table(spec.rows, spec.dim, spec.dtype, seed, "cuda",
+                                            table=t))
+            states.append(torch.zeros(spec.rows, dtype=torch.float32, device="cuda")
+                          if ada else None)
     t0 = time.time()
     grads_host = [synth.gradient_rows(seed, 0, t, np.arange(cap), spec.dim)
                   for t, spec in enumerate(w.tables)]
@@ -313,7 +326,7 @@ def main():
             "optimizer": w.optim, "ids_per_step": ids_timed / args.steps,
             "weights": sorted({t.dtype for t in w.tables}), "grad_accumulate": "f64",
             "distinct_batches": NB, "schedule": schedule,
-            "autotune": bool(args.autotune)},
+            "autotune": bool(args.autotune), "layout": args.layout},
         "roofline": {
             "bound": "hbm", "achieved": dom_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": dom_gbps / HBM_PEAK_GBPS, "traffic": traffic,

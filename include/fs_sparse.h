@@ -77,12 +77,25 @@ extern "C" {
 #define FS_COLLISION 1
 
 typedef struct fs_table {
-  void* weights;  /* device [rows][dim], dtype FS_F32 or FS_BF16, row-major */
-  float* state;   /* device [rows] fp32 row-wise Adagrad accumulator, or NULL */
+  void* weights;  /* device: rows rows of dim elements, dtype FS_F32 or FS_BF16 */
+  float* state;   /* device fp32 row-wise Adagrad accumulator per row, or NULL */
   int64_t rows;   /* R_t */
   int32_t dim;    /* D_t */
   int32_t dtype;  /* FS_F32 or FS_BF16 */
+  int64_t stride;       /* bytes from one weight row to the next; 0: dim * sizeof(dtype) */
+  int64_t state_stride; /* bytes from one row's state to the next; 0: 4 */
 } fs_table;
+/* Layouts: dense ([rows][dim] weights and a separate [rows] state, strides  */
+/* 0), rows spaced `stride` bytes apart, or each row's state in its own row */
+/* slot -- stride >= dim * sizeof(dtype) + 4, state = weights + dim *        */
+/* sizeof(dtype) bytes, state_stride = stride -- so that a row's update     */
+/* reads and writes one slot instead of a slot and a separate state entry.  */
+/* Slots of a power of two keep rows aligned to the memory's 128-byte lines */
+/* (a 256-byte row in a 272-byte slot straddles an extra line). The lookup  */
+/* and the update need weights 16-byte aligned, a stride that is a multiple */
+/* of 16 and at least the row size, and a state stride that is a multiple  */
+/* of 4 and at least 4 (else FS_ERR_INVALID_ARG); the state of a row must   */
+/* not overlap its weights. Other calls read only rows, dim and dtype.      */
 
 /* ------------------------------------------------------------------------ */
 /* Load balancing -- [FS] section 4.1 (partitioning algorithms), run inside  */

@@ -143,6 +143,35 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
   return u >> 16;
 }
 
+// ---------------------------------------------------------------- tables
+// Row and state strides of a table (0 = dense) and their checks for the
+// calls that touch weights: weights 16-byte aligned, row stride a multiple of
+// 16 covering the row; with the state (the update): state stride a multiple
+// of 4 of at least 4, and a state inside the first row's stride must sit
+// past that row's weights.
+__host__ inline int64_t table_row_bytes(const fs_table& t) {
+  return (int64_t)t.dim * (t.dtype == FS_F32 ? 4 : 2);
+}
+__host__ inline int64_t table_stride(const fs_table& t) {
+  return t.stride ? t.stride : table_row_bytes(t);
+}
+__host__ inline int64_t table_state_stride(const fs_table& t) {
+  return t.state_stride ? t.state_stride : 4;
+}
+__host__ inline bool table_layout_ok(const fs_table& t, bool with_state) {
+  const int64_t rb = table_row_bytes(t), st = table_stride(t), ss = table_state_stride(t);
+  if (st < rb || (st & 15) || t.stride < 0) return false;
+  if (t.weights && ((uintptr_t)t.weights & 15)) return false;
+  if (!with_state) return true;
+  if (ss < 4 || (ss & 3) || t.state_stride < 0) return false;
+  if (t.state) {
+    if ((uintptr_t)t.state & 3) return false;
+    const intptr_t off = (intptr_t)t.state - (intptr_t)t.weights;
+    if (t.weights && off >= 0 && off < st && (off < rb || off + 4 > st)) return false;
+  }
+  return true;
+}
+
 // ---------------------------------------------------------------- misc
 __host__ __device__ __forceinline__ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 

@@ -23,6 +23,7 @@ constexpr int kThreads = 256;
 struct LookupArgs {
   const char* weights;
   char* out;
+  int64_t stride;  // bytes between weight rows
   int64_t row_base;
   int64_t n_cap;  // occurrences this table can have (n_tok)
   const int64_t* unique;
@@ -99,7 +100,7 @@ __device__ __forceinline__ void lookup_rows(const LookupArgs& a, int64_t blk) {
       const uint32_t r = (uint32_t)__shfl((int)row, j, kWave);
       d[b] = __shfl(dst, j, kWave);
       if (d[b] >= 0) {
-        const u32x4* sp = (const u32x4*)(a.weights + (int64_t)r * (VPR * 16));
+        const u32x4* sp = (const u32x4*)(a.weights + (int64_t)r * a.stride);
 #pragma unroll
         for (int k = 0; k < VPL; ++k) v[b][k] = sp[sub + k * LPR];
       }
@@ -167,6 +168,7 @@ extern "C" int fs_jagged_lookup(const fs_table* tables, int32_t T, int32_t W,
     const int64_t rb = (int64_t)tb.dim * (tb.dtype == FS_F32 ? 4 : 2);
     if (rb != 64 && rb != 128 && rb != 256 && rb != 512 && rb != 1024 && rb != 2048)
       return FS_ERR_UNSUPPORTED;
+    if (!table_layout_ok(tb, false)) return FS_ERR_INVALID_ARG;
     base += tb.rows;
   }
   if (base > (int64_t)UINT32_MAX) return FS_ERR_UNSUPPORTED;
@@ -180,6 +182,7 @@ extern "C" int fs_jagged_lookup(const fs_table* tables, int32_t T, int32_t W,
     LookupArgs& a = b.t[t];
     a.weights = (const char*)tb.weights;
     a.out = (char*)out[t];
+    a.stride = table_stride(tb);
     a.row_base = base;
     a.n_cap = n_tok;
     a.unique = unique;

@@ -46,6 +46,8 @@ constexpr int64_t kResident = 256 * 4 * 5;
 struct RUArgs {
   void* weights;
   float* state;
+  int64_t stride;        // bytes between weight rows
+  int64_t state_stride;  // bytes between rows' states
   const float* grad;
   float* reduced;  // may be null
   const int64_t* unique;
@@ -81,6 +83,10 @@ __device__ __forceinline__ float4 ld_stream(const float4* p) {
   return make_float4(v.x, v.y, v.z, v.w);
 }
 
+__device__ __forceinline__ float* state_at(const RUArgs& a, int64_t row) {
+  return (float*)((char*)a.state + row * a.state_stride);
+}
+
 __device__ __forceinline__ bool class_ok(const RUArgs& a, int64_t u) {
   return a.which < 0 || a.cls[u] == (uint8_t)a.which;
 }
@@ -110,7 +116,7 @@ template <int D, typename WT>
 __device__ __forceinline__ void load_w(const RUArgs& a, int64_t row, int sub, RowW<D, WT>& r) {
   using M = Map<D>;
   if constexpr (sizeof(WT) == 4) {
-    const float4* w = (const float4*)((const float*)a.weights + row * D);
+    const float4* w = (const float4*)((const char*)a.weights + row * a.stride);
 #pragma unroll
     for (int v = 0; v < M::NV; ++v) {
       const float4 x = w[sub + v * M::LPG];
@@ -120,7 +126,7 @@ __device__ __forceinline__ void load_w(const RUArgs& a, int64_t row, int sub, Ro
       r.w[4 * v + 3] = x.w;
     }
   } else {
-    const uint2* w = (const uint2*)((const uint16_t*)a.weights + row * D);
+    const uint2* w = (const uint2*)((const char*)a.weights + row * a.stride);
 #pragma unroll
     for (int v = 0; v < M::NV; ++v) {
       const uint2 x = w[sub + v * M::LPG];
@@ -154,7 +160,7 @@ __device__ __forceinline__ void apply_row(const RUArgs& a, int64_t u, int64_t ro
     if (active) {
       const float mean_sq = (float)(ss / (double)D);
       const float s = st + mean_sq;
-      if (sub == 0) a.state[row] = s;
+      if (sub == 0) *state_at(a, row) = s;
       const float denom = sqrtf(s) + a.eps;
       m = a.lr / denom;
     }
@@ -173,12 +179,12 @@ __device__ __forceinline__ void apply_row(const RUArgs& a, int64_t u, int64_t ro
     r.w[c] = r.w[c] - step;
   }
   if constexpr (sizeof(WT) == 4) {
-    float4* w = (float4*)((float*)a.weights + row * D);
+    float4* w = (float4*)((char*)a.weights + row * a.stride);
 #pragma unroll
     for (int v = 0; v < M::NV; ++v)
       w[sub + v * M::LPG] = make_float4(r.w[4 * v], r.w[4 * v + 1], r.w[4 * v + 2], r.w[4 * v + 3]);
   } else {
-    uint2* w = (uint2*)((uint16_t*)a.weights + row * D);
+    uint2* w = (uint2*)((char*)a.weights + row * a.stride);
 #pragma unroll
     for (int v = 0; v < M::NV; ++v) {
       uint2 x;
@@ -198,7 +204,7 @@ __device__ __forceinline__ void update_row(const RUArgs& a, int64_t u, int sub,
   if (active) {
     row = a.unique[u] - a.row_base;
     load_w<D, WT>(a, row, sub, r);
-    if (a.optim == FS_RW_ADAGRAD) st = a.state[row];
+    if (a.optim == FS_RW_ADAGRAD) st = *state_at(a, row);
   }
   apply_row<D, WT>(a, u, row, st, sub, acc, r, active);
 }
@@ -236,7 +242,7 @@ __global__ void __launch_bounds__(kThreads) k_short(RUArgs a) {
     const uint64_t actm = __ballot(act);
     if (!actm) continue;
     const uint32_t row = act ? (uint32_t)(a.unique[uu] - a.row_base) : 0u;
-    const float st = (act && ada) ? a.state[row] : 0.f;
+    const float st = (act && ada) ? *state_at(a, row) : 0.f;
     // the row's (at most kLong) gradient slots, loaded once per unit beside
     // its key and state: a batch below then waits for one round of loads
     // (its gradient and weight rows), not for the slots first
@@ -332,7 +338,7 @@ __device__ __forceinline__ void long_chunk(const RUArgs& a, int64_t o_lo, int64_
       if (complete) {
         row = a.unique[u] - a.row_base;
         if (grp == 0) load_w<D, WT>(a, row, sub, wr);
-        if (a.optim == FS_RW_ADAGRAD) st = a.state[row];
+        if (a.optim == FS_RW_ADAGRAD) st = *state_at(a, row);
       }
       double acc[M::CPL];
 #pragma unroll
@@ -540,6 +546,7 @@ extern "C" int fs_grad_reduce_update(const fs_table* tables, int32_t T, int32_t 
     if (!dim_ok(tb.dim)) return FS_ERR_UNSUPPORTED;
     if (n_tok > 0 && (!tb.weights || !grad[t])) return FS_ERR_INVALID_ARG;
     if (optim == FS_RW_ADAGRAD && n_tok > 0 && !tb.state) return FS_ERR_INVALID_ARG;
+    if (!table_layout_ok(tb, optim == FS_RW_ADAGRAD)) return FS_ERR_INVALID_ARG;
     max_dim = tb.dim > max_dim ? tb.dim : max_dim;
     base += tb.rows;
   }
@@ -552,6 +559,8 @@ extern "C" int fs_grad_reduce_update(const fs_table* tables, int32_t T, int32_t 
     RUArgs a;
     a.weights = tb.weights;
     a.state = tb.state;
+    a.stride = table_stride(tb);
+    a.state_stride = table_state_stride(tb);
     a.grad = grad[t];
     a.reduced = reduced_out ? reduced_out[t] : nullptr;
     a.unique = unique;

@@ -31,7 +31,8 @@ if not os.path.exists(LIB_PATH):
 
 class FsTable(C.Structure):
     _fields_ = [("weights", C.c_void_p), ("state", C.c_void_p), ("rows", C.c_int64),
-                ("dim", C.c_int32), ("dtype", C.c_int32)]
+                ("dim", C.c_int32), ("dtype", C.c_int32), ("stride", C.c_int64),
+                ("state_stride", C.c_int64)]
 
 
 _L = C.CDLL(LIB_PATH)
@@ -129,19 +130,50 @@ def _ws(nbytes, ws):
     return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=_dev())
 
 
+def _rows_ptr(t):
+    """Device pointer and row stride in bytes of a [rows, dim] tensor whose
+    rows are contiguous (the rows themselves may be spaced further apart)."""
+    assert t.is_cuda and t.stride(-1) == 1, "table rows must be contiguous CUDA memory"
+    return t.data_ptr(), (t.stride(0) * t.element_size() if t.dim() == 2 else 0)
+
+
+def _state_ptr(st):
+    """Device pointer and spacing in bytes of a [rows] fp32 state tensor."""
+    assert st.is_cuda and st.dtype == torch.float32 and st.dim() == 1
+    return st.data_ptr(), st.stride(0) * 4
+
+
 def make_tables(weights, states=None):
-    """Host array of fs_table for a list of [rows, dim] weight tensors."""
+    """Host array of fs_table for a list of [rows, dim] weight tensors (dense,
+    or row views of a wider buffer as alloc_table makes) and their [rows]
+    states (dense, or views with the rows' spacing)."""
     T = len(weights)
     arr = (FsTable * T)()
     for t, w in enumerate(weights):
         st = states[t] if states is not None else None
         assert w.dtype in (torch.float32, torch.bfloat16) and w.dim() == 2
-        arr[t].weights = _ptr(w)
-        arr[t].state = _ptr(st) if st is not None else None
+        arr[t].weights, arr[t].stride = _rows_ptr(w)
+        if st is not None:
+            arr[t].state, arr[t].state_stride = _state_ptr(st)
         arr[t].rows = w.shape[0]
         arr[t].dim = w.shape[1]
         arr[t].dtype = FS_F32 if w.dtype == torch.float32 else FS_BF16
     return arr
+
+
+def alloc_table(rows, dim, dtype, with_state, device=None, align=16):
+    """Table memory with each row's fp32 state in the row's own padding: one
+    buffer of rows x stride bytes (stride = the row plus 4 bytes, rounded up
+    to `align`, a multiple of 16). Returns (weights [rows, dim] view, state
+    [rows] view or None)."""
+    assert align % 16 == 0
+    e = 4 if dtype == torch.float32 else 2
+    rb = dim * e
+    stride = (rb + (4 if with_state else 0) + align - 1) // align * align
+    buf = torch.empty((rows, stride), dtype=torch.uint8, device=device or _dev())
+    w = buf[:, :rb].view(dtype)
+    st = buf[:, rb:rb + 4].view(torch.float32)[:, 0] if with_state else None
+    return w, st
 
 
 def make_row_tables(rows, dims=None):

@@ -364,14 +364,18 @@ def gradient_rows(seed: int, it: int, table: int, tok: np.ndarray, dim: int,
     return out
 
 
-def init_table(rows: int, dim: int, dtype: str, seed: int, device="cpu", table: int = 0):
-    """N(0, 0.01**2) table from torch's seeded generator, rounded to ``dtype``."""
+def init_table(rows: int, dim: int, dtype: str, seed: int, device="cpu", table: int = 0,
+               out=None):
+    """N(0, 0.01**2) table from torch's seeded generator, rounded to ``dtype``;
+    written into ``out`` (a [rows, dim] tensor or row view) when given."""
     import torch
 
     g = torch.Generator(device=device)
     g.manual_seed(int(seed) * 1000 + int(table))
     tdt = torch.float32 if dtype == "f32" else torch.bfloat16
-    out = torch.empty((rows, dim), dtype=tdt, device=device)
+    if out is None:
+        out = torch.empty((rows, dim), dtype=tdt, device=device)
+    assert out.shape == (rows, dim) and out.dtype == tdt
     chunk = max(1, (1 << 28) // max(dim, 1))
     for lo in range(0, rows, chunk):
         hi = min(rows, lo + chunk)

@@ -10,7 +10,7 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from jagged_embedding_sparse_amd import synth
+from jagged_embedding_sparse_amd import lib, synth
 from oracle import oracle as O
 
 
@@ -51,12 +51,23 @@ def touched_rows(batches, w):
     return out
 
 
-def gpu_tables(w, seed):
+def gpu_tables(w, seed, align=0):
+    """Device tables of workload w: dense (align 0), or each row's state in
+    the row's own slot of `align`-rounded bytes (lib.alloc_table)."""
     weights, states = [], []
+    ada = w.optim == "rw_adagrad"
     for t, spec in enumerate(w.tables):
-        weights.append(synth.init_table(spec.rows, spec.dim, spec.dtype, seed, "cuda", table=t))
-        states.append(torch.zeros(spec.rows, dtype=torch.float32, device="cuda")
-                      if w.optim == "rw_adagrad" else None)
+        if align:
+            tdt = torch.float32 if spec.dtype == "f32" else torch.bfloat16
+            wv, st = lib.alloc_table(spec.rows, spec.dim, tdt, ada, device="cuda", align=align)
+            weights.append(synth.init_table(spec.rows, spec.dim, spec.dtype, seed, "cuda",
+                                            table=t, out=wv))
+            states.append(st.zero_() if st is not None else None)
+        else:
+            weights.append(synth.init_table(spec.rows, spec.dim, spec.dtype, seed, "cuda",
+                                            table=t))
+            states.append(torch.zeros(spec.rows, dtype=torch.float32, device="cuda")
+                          if ada else None)
     return weights, states
 
 

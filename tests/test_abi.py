@@ -81,7 +81,7 @@ def _tables(L, specs):
     arr = (L.FsTable * len(specs))()
     for i, (rows, dim, dt, st) in enumerate(specs):
         arr[i].weights = FAKE
-        arr[i].state = FAKE if st else None
+        arr[i].state = FAKE + (1 << 20) if st else None
         arr[i].rows = rows
         arr[i].dim = dim
         arr[i].dtype = dt
@@ -139,6 +139,43 @@ def test_lookup_and_update_reject_unsupported_rows(L):
               L.FS_RW_ADAGRAD, 0.1, 0.0, None, FAKE, 8, None) == L.FS_ERR_WORKSPACE
 
 
+def test_lookup_and_update_reject_bad_table_layouts(L):
+    """Row strides and in-row states: checked on the host before any launch."""
+    lk, ru = L._c_lookup, L._c_reduce
+    outs = (C.c_void_p * 1)(FAKE)
+    grads = (C.c_void_p * 1)(FAKE)
+
+    def tab(stride=0, state_stride=0, weights=FAKE, state=None, dim=128, dt=None):
+        t = _tables(L, [(1000, dim, L.FS_BF16 if dt is None else dt, False)])
+        t[0].weights, t[0].state = weights, state
+        t[0].stride, t[0].state_stride = stride, state_stride
+        return t
+
+    def look(t):
+        return lk(t, 1, 4, FAKE, FAKE, FAKE, FAKE, FAKE, None, L.FS_ALL, outs, 10, None)
+
+    def upd(t, optim=None):
+        return ru(t, 1, 4, grads, 10, FAKE, FAKE, FAKE, FAKE, FAKE, None, L.FS_ALL,
+                  L.FS_RW_ADAGRAD if optim is None else optim, 0.1, 0.0, None, FAKE, 8, None)
+    bad = L.FS_ERR_INVALID_ARG
+    # bf16 x 128 = 256-byte rows
+    assert look(tab(stride=264)) == bad             # not a multiple of 16
+    assert look(tab(stride=240)) == bad             # shorter than the row
+    assert look(tab(weights=FAKE + 8)) == bad       # weights not 16-byte aligned
+    assert upd(tab(stride=272, state=FAKE + (1 << 20), state_stride=2)) == bad
+    assert upd(tab(stride=272, state=FAKE + (1 << 20) + 2)) == bad  # state not 4-aligned
+    # a state inside the row's stride that overlaps the row's weights
+    assert upd(tab(stride=272, state=FAKE + 252, state_stride=272)) == bad
+    assert upd(tab(stride=272, state=FAKE + 270, state_stride=272)) == bad  # past the stride
+    # valid layouts get past the layout check (and stop at the workspace)
+    ws = L.FS_ERR_WORKSPACE
+    assert upd(tab(stride=272, state=FAKE + 256, state_stride=272)) == ws
+    assert upd(tab(stride=272, state=FAKE + 268, state_stride=272)) == ws
+    assert upd(tab(state=FAKE + (1 << 20))) == ws
+    # SGD ignores the state's layout
+    assert upd(tab(stride=272, state=FAKE + 252, state_stride=2), optim=L.FS_SGD) == ws
+
+
 def test_step_rejects_unknown_lookup_schedule():
     from jagged_embedding_sparse_amd.step import SparseStep
     with pytest.raises(ValueError):
@@ -156,6 +193,8 @@ def test_prepared_calls_match_the_c_signatures(L, monkeypatch):
     without a GPU: pointers are stand-in integers, nothing is called)."""
     import torch
     monkeypatch.setattr(L, "_ptr", lambda t: None if t is None else 0x1000)
+    monkeypatch.setattr(L, "_rows_ptr", lambda t: (0x1000, 0))
+    monkeypatch.setattr(L, "_state_ptr", lambda t: (0x2000, 0))
     t = torch.zeros(4)
     ws = torch.zeros(16, dtype=torch.uint8)
     weights = [torch.zeros((8, 64)), torch.zeros((8, 128), dtype=torch.bfloat16)]

@@ -583,19 +583,37 @@ def _table(rows, dim, dtype, seed):
     return synth.init_table(rows, dim, dtype, seed, "cuda")
 
 
+def _table_rowstate(rows, dim, dtype, seed, align=16):
+    """The same values in rows of a wider buffer, each row's state in its own
+    padding (slots rounded up to `align` bytes); returns (weights view, state
+    view, the whole buffer as bytes)."""
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    w, st = lib.alloc_table(rows, dim, tdt, True, device="cuda", align=align)
+    synth.init_table(rows, dim, dtype, seed, "cuda", out=w)
+    st.zero_()
+    buf = torch.empty(0, dtype=torch.uint8, device="cuda").set_(w.untyped_storage())
+    return w, st, buf
+
+
 LK_CASES = [([100_000], [64], ["f32"], 4), ([5000, 300], [128, 256], ["bf16", "f32"], 16),
             ([4000, 4000, 9000, 20], [64, 128, 256, 64], ["f32"] * 4, 8),
             ([777], [512], ["f32"], 2), ([3000], [1024], ["bf16"], 3), ([100], [32], ["f32"], 4),
             ([200], [16], ["f32"], 4), ([1000], [512], ["bf16"], 5)]
 
 
+@pytest.mark.parametrize("layout", ["dense", "rowstate", "rowstate256"])
 @pytest.mark.parametrize("case", LK_CASES, ids=lambda c: f"D{c[1]}")
-def test_lookup_parity(case):
+def test_lookup_parity(case, layout):
     rows, dims, dts, W = case
-    say("lookup", case)
+    say("lookup", case, layout)
     b0 = _tiny_batch(21, 300, rows, 50)
     b1 = _tiny_batch(22, 300, rows, 50)
-    ws = [_table(r, d, dt, 5 + t) for t, (r, d, dt) in enumerate(zip(rows, dims, dts))]
+    if layout == "dense":
+        ws = [_table(r, d, dt, 5 + t) for t, (r, d, dt) in enumerate(zip(rows, dims, dts))]
+    else:  # rows spaced wider than they are (the state's padding)
+        al = 256 if layout == "rowstate256" else 16
+        ws = [_table_rowstate(r, d, dt, 5 + t, al)[0]
+              for t, (r, d, dt) in enumerate(zip(rows, dims, dts))]
     stores = snapshot_stores(ws, [None] * len(ws), [np.arange(r) for r in rows])
     outs = {}
     oq = []
@@ -655,18 +673,30 @@ RU_CASES = [
 ]
 
 
+@pytest.mark.parametrize("layout", ["dense", "rowstate", "rowstate256"])
 @pytest.mark.parametrize("case", RU_CASES, ids=lambda c: f"D{c[0]}-{c[1]}-{c[2]}-{c[4]}")
-def test_reduce_update_parity(case):
+def test_reduce_update_parity(case, layout):
+    """Reduced gradients bit-exact, rows and states to the fp32 / bf16
+    tolerance; with each row's state in its own padding, every byte outside
+    the touched rows' weights and states is left as it was."""
     dim, dt, optim, hot, n_tok, W, rows = case
-    say("reduce-update", case)
+    if layout != "dense" and rows * dim > 2e9:
+        pytest.skip("table too large for a second layout")
+    say("reduce-update", case, layout)
     b = _hot_batch(dim + n_tok, rows, n_tok, hot)
     _, _, obk = _oracle_bucketize(b, [rows], W)
     ouq = O.unique(obk["shard_keys"], obk["shard_bm"], [rows], W)
     U = len(ouq["unique"])
     cls = (np.random.default_rng(1).random(U) < 0.5).astype(np.uint8)
     grad = synth.gradient_rows(7, 0, 0, np.arange(n_tok), dim)
-    wt = _table(rows, dim, dt, 9)
-    st = torch.zeros(rows, dtype=torch.float32, device="cuda") if optim == "rw_adagrad" else None
+    if layout == "dense":
+        wt = _table(rows, dim, dt, 9)
+        st = torch.zeros(rows, dtype=torch.float32, device="cuda") if optim == "rw_adagrad" \
+            else None
+    else:
+        wt, st, buf = _table_rowstate(rows, dim, dt, 9, 256 if layout == "rowstate256" else 16)
+        before = buf.clone()
+        st = st if optim == "rw_adagrad" else None
     stores = snapshot_stores([wt], [st], [np.unique(b["ids"][0])])
     dq = _csr_to_dev(ouq)
     dcls = cu(cls)
@@ -690,6 +720,16 @@ def test_reduce_update_parity(case):
         assert np.array_equal(got, ref)
     if optim == "rw_adagrad":
         np.testing.assert_allclose(host(st.index_select(0, cu(rid))), stores[0].state, rtol=1e-6)
+    if layout != "dense":
+        e = 4 if dt == "f32" else 2
+        stride = wt.stride(0) * e
+        mine = torch.zeros(rows, stride, dtype=torch.bool, device="cuda")
+        touched = cu(rid.astype(np.int64))
+        mine[touched, :dim * e] = True
+        if optim == "rw_adagrad":
+            mine[touched, dim * e:dim * e + 4] = True
+        b2, b1 = buf.view(rows, stride), before.view(rows, stride)
+        assert torch.equal(b2.masked_fill(mine, 0), b1.masked_fill(mine, 0))
 
 
 def test_bucketize_repeated_sample_flags_shape():

@@ -91,18 +91,19 @@ def step_rowbase(w):
     return np.concatenate([[0], np.cumsum(rows)[:-1]])
 
 
-def run_parity(k, balancer=None, iters=None, seed=None, lookahead=1, autotune=None):
+def run_parity(k, balancer=None, iters=None, seed=None, lookahead=1, autotune=None, align=0):
     """k: a workload number, or a synth.Workload. lookahead=2 runs the step
     with the index stages two iterations ahead (the bench's schedule);
     autotune (a dict of AUTOTUNE_DEFAULTS' keys) tunes the VBS shares on both
-    sides."""
+    sides; align > 0 keeps each row's state in the row's own slot of that
+    many bytes."""
     w = k if isinstance(k, synth.Workload) else synth.workload(k, balancer)
     seed = (k if isinstance(k, int) else 77) if seed is None else seed
     K = iters or w.iterations
     say("workload", k, w.name, w.balancer, "iterations", K)
     bt = synth.Batches(w, seed)
     batches = [bt.batch(i) for i in range(K)]
-    weights, states = gpu_tables(w, seed)
+    weights, states = gpu_tables(w, seed, align)
     rows_t = touched_rows(batches, w)
     stores = snapshot_stores(weights, states, rows_t)
     init_vals = [store_vals_f32(s).copy() for s in stores]
@@ -172,6 +173,14 @@ def test_workload3_vbs():
 @pytest.mark.timeout(600)
 def test_workload4_vbs_four_tables():
     run_parity(4, iters=3)
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("align", [16, 256])
+def test_workload3_rows_with_their_state(align):
+    """Each row's Adagrad state in its own row slot: the step equals the
+    oracle's loop."""
+    run_parity(3, iters=4, lookahead=2, align=align)
 
 
 @pytest.mark.timeout(600)
