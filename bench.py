@@ -301,9 +301,9 @@ def main():
 
     # HBM bytes per launch of the dominant stage from the committed counter
     # summary (rocprofv3 FETCH_SIZE / WRITE_SIZE, copy-calibrated), when it was
-    # taken on the kernel sources built here
+    # taken on the kernel sources built here and on the same (dense) tables
     from jagged_embedding_sparse_amd.traffic import load_traffic
-    traffic = load_traffic(args.config, dom)
+    traffic = load_traffic(args.config, dom) if args.layout == "dense" else None
 
     tables = "+".join(f"{t.rows // 1_000_000}Mx{t.dim}-{t.dtype}" if t.rows >= 1_000_000 else
                       f"{t.rows // 1000}Kx{t.dim}-{t.dtype}" for t in w.tables)
