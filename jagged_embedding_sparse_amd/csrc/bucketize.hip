@@ -138,7 +138,7 @@ k_bal(int32_t n, const int32_t* __restrict__ lens, const int32_t* __restrict__ b
 
 // The tile table (one workgroup): rank offsets validated, ranks' token
 // ranges from bal, tiles per rank and their descriptors. `part` is this
-// thread's share of the token count and `bad` its input-check verdict; bal
+// thread's share of the token count and `bad` the result of its input checks; bal
 // holds the balanced offsets of samples 0..n-1 (bal[n] is written here).
 // With a copy of bal[0..n] in LDS (bal_lds), each chunk's first sample is
 // found here by an LDS search and stored, so the tile kernels need not
