@@ -422,28 +422,34 @@ def _kt_values(rng, n, eb):
     return rng.integers(-2 ** 31, 2 ** 31, n, dtype=np.int32)
 
 
+@pytest.mark.parametrize("shift", [0, 1])
 @pytest.mark.parametrize("case", KT_CASES)
-def test_keyed_transpose_parity(case):
+def test_keyed_transpose_parity(case, shift):
     """Batch-major values and offsets bit-exact against the oracle; the
-    element past the output is not touched. 4-byte values are compared
-    widened to int64 (the transpose only moves them)."""
+    elements around the output are not touched. 4-byte values are compared
+    widened to int64 (the transpose only moves them). shift = 1 puts values
+    and output one element past a 16-byte boundary (the element-wise copy);
+    shift = 0 keeps them aligned (the 16-byte copy)."""
     seed, F, B, kind, eb = case
-    say("keyed transpose", case)
+    say("keyed transpose", case, shift)
     rng = np.random.default_rng(seed)
     lengths = _kt_lengths(rng, F, B, kind)
     n = int(lengths.sum())
     vals = _kt_values(rng, n, eb)
     dt = torch.int64 if eb == 8 else torch.int32
+    vbuf = torch.zeros(n + 8, dtype=dt, device="cuda")
+    vbuf[shift:shift + n] = cu(vals)
     out = torch.full((n + 64,), 77, dtype=dt, device="cuda")
     offs = torch.full((F * B + 1,), -5, dtype=torch.int64, device="cuda")
     err = torch.zeros(1, dtype=torch.int32, device="cuda")
-    lib.fs_keyed_transpose(cu(vals), cu(lengths), out=out[:n], out_offsets=offs, err=err)
+    lib.fs_keyed_transpose(vbuf[shift:shift + n], cu(lengths), out=out[shift:shift + n],
+                           out_offsets=offs, err=err)
     ref, ro = O.keyed_transpose(vals.astype(np.int64), lengths)
     torch.cuda.synchronize()
     assert np.array_equal(host(offs), ro)
     got = host(out)
-    assert np.array_equal(got[:n].astype(np.int64), ref)
-    assert (got[n:] == 77).all()
+    assert np.array_equal(got[shift:shift + n].astype(np.int64), ref)
+    assert (got[:shift] == 77).all() and (got[shift + n:] == 77).all()
     assert int(err.item()) == 0
 
 
