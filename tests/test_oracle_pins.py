@@ -625,3 +625,120 @@ def test_bf16_update_rounds_once():
     O.update(st, 0, 0, 1, np.arange(1), g, "sgd", 0.01, 0.0)
     ref = (w0.float() - torch.from_numpy(g) * np.float32(0.01)).to(torch.bfloat16)
     assert np.array_equal(st.vals, ref.view(torch.int16).numpy().astype(np.uint16))
+
+
+# ----------------------------------------------------------------------------
+# the synchronous loop (FreeScale section 3.2: the synchronized baseline that a
+# strict write-then-read order on collision rows reproduces)
+
+
+def _loop_workload(optim="sgd", lr=0.25, eps=0.0, rows=16, dim=4, W=2):
+    from jagged_embedding_sparse_amd import synth
+    return synth.Workload("loop-pin", 4, W, (synth.TableSpec(rows, dim, "f32", 1.0),), optim,
+                          lr, eps, "fbs", (1, 1), 2, ("lognormal", 1.0, 1.0), 8, 0)
+
+
+def _hand_batch(samples):
+    """One table; sample s holds the IDs samples[s] (all UIH tokens)."""
+    lens = np.array([len(x) for x in samples], np.int32)
+    so = np.zeros(len(samples) + 1, np.int64)
+    so[1:] = np.cumsum(lens)
+    ids = np.array([[i for x in samples for i in x]], np.int64)
+    return dict(uih_len=lens, num_cand=np.zeros(len(samples), np.int32), sample_offsets=so,
+                ids=ids, n_tok=int(so[-1]))
+
+
+def _row_grid(rows, dim):
+    # row r, column c holds r + c/16: every value and every SGD step below is exact
+    return (np.arange(rows, dtype=np.float32)[:, None]
+            + np.arange(dim, dtype=np.float32)[None, :] / 16).astype(np.float32)
+
+
+def _ids_by_bm(batch, out):
+    """Row ID at every balanced batch-major slot of one iteration's outputs."""
+    perm, bal = out["perm"], out["bucket"]["bal_offsets"]
+    so = batch["sample_offsets"]
+    tok = np.concatenate([np.arange(so[s], so[s + 1]) for s in perm]) if len(perm) else []
+    assert len(tok) == bal[-1]
+    return batch["ids"][0][np.asarray(tok, np.int64)]
+
+
+def _run_loop(w, batches, grad_value=1.0):
+    rows, dim = w.tables[0].rows, w.tables[0].dim
+    w0 = _row_grid(rows, dim)
+    store = O.RowStore(np.arange(rows), w0.copy())
+    run = O.SyncRun(w, [store])
+    outs = []
+    for b in batches:
+        outs.append(run.step(b, lambda o, b=b: [np.full((b["n_tok"], dim), grad_value,
+                                                        np.float32)]))
+    return w0, store, outs
+
+
+def _occ(batch):
+    ids, cnt = np.unique(batch["ids"][0], return_counts=True)
+    return dict(zip(ids.tolist(), cnt.tolist()))
+
+
+def test_sync_loop_sgd_two_iterations():
+    """Iteration 1 reads the rows as iteration 0 updated them (w0 - lr*k for
+    a row iteration 0 touched k times with all-ones gradients, w0 otherwise);
+    iteration 0 reads the initial rows; the split is against iteration 0's
+    rows; the final rows carry both updates."""
+    w = _loop_workload()
+    b0 = _hand_batch([[1, 3, 3], [5], [1, 7], [9, 9, 9, 1]])
+    b1 = _hand_batch([[1, 2], [3, 11], [9], [12, 1]])
+    w0, store, outs = _run_loop(w, [b0, b1])
+    k0, k1 = _occ(b0), _occ(b1)
+    # iteration 0: the initial rows, at every slot
+    ids0 = _ids_by_bm(b0, outs[0])
+    assert np.array_equal(outs[0]["emb"][0], w0[ids0])
+    # iteration 1: rows seen in iteration 0 moved by lr * k, the others did not
+    ids1 = _ids_by_bm(b1, outs[1])
+    exp1 = np.stack([w0[r] - np.float32(0.25 * k0.get(int(r), 0)) for r in ids1])
+    assert np.array_equal(outs[1]["emb"][0], exp1)
+    # the split: U1 = {1, 2, 3, 9, 11, 12}, C = {1, 3, 9}, U0 = {1, 3, 5, 7, 9}
+    assert outs[0]["counts"].tolist() == [5, 0, 5, 0]
+    assert outs[1]["counts"].tolist() == [6, 3, 3, 2]
+    assert outs[1]["uniq"]["cls"].tolist() == [1, 0, 1, 1, 0, 0]  # rows 1 2 3 9 11 12
+    assert outs[1]["prev_cls"].tolist() == [1, 1, 0, 0, 1]  # rows 1 3 5 7 9
+    # the reduced gradient of each row is its occurrence count
+    assert outs[1]["reduced"][0][:, 0].tolist() == [k1[r] for r in (1, 2, 3, 9, 11, 12)]
+    # final rows: both updates
+    for r in range(16):
+        k = k0.get(r, 0) + k1.get(r, 0)
+        assert np.array_equal(store.vals[r], w0[r] - np.float32(0.25 * k)), r
+
+
+def test_sync_loop_identical_and_disjoint_batches():
+    """Identical consecutive batches give C = U (every row of both iterations
+    collides); disjoint ones give C = 0."""
+    w = _loop_workload()
+    b = _hand_batch([[4, 4], [6], [8, 4], [6, 10, 15]])
+    _, _, outs = _run_loop(w, [b, _hand_batch([[4, 4], [6], [8, 4], [6, 10, 15]])])
+    U = len(np.unique(b["ids"][0]))
+    assert outs[1]["counts"].tolist() == [U, U, 0, 0]
+    assert np.all(outs[1]["uniq"]["cls"] == 1) and np.all(outs[1]["prev_cls"] == 1)
+    _, _, outs = _run_loop(w, [b, _hand_batch([[0, 1], [2], [3, 5], [7, 9, 11]])])
+    assert outs[1]["counts"].tolist() == [8, 0, 8, U]
+    assert np.all(outs[1]["uniq"]["cls"] == 0) and np.all(outs[1]["prev_cls"] == 0)
+
+
+def test_sync_loop_rowwise_adagrad_closed_form():
+    """Row-wise Adagrad with all-ones gradients (eps = 0): a row touched k
+    times gets g = k on every column, so s = k^2 and w - lr * g / sqrt(s) =
+    w - lr; iteration 1 reads that, and a row touched k0 then k1 times ends at
+    s = k0^2 + k1^2."""
+    w = _loop_workload(optim="rw_adagrad", lr=0.25, eps=0.0)
+    b0 = _hand_batch([[1, 3, 3], [5], [1, 7], [9, 9, 9, 1]])
+    b1 = _hand_batch([[1, 2], [3, 11], [9], [12, 1]])
+    w0, store, outs = _run_loop(w, [b0, b1])
+    k0, k1 = _occ(b0), _occ(b1)
+    ids1 = _ids_by_bm(b1, outs[1])
+    exp1 = np.stack([w0[r] - np.float32(0.25 if r in k0 else 0.0) for r in ids1])
+    np.testing.assert_allclose(outs[1]["emb"][0], exp1, rtol=0, atol=1e-6)
+    for r in range(16):
+        s = k0.get(r, 0) ** 2 + k1.get(r, 0) ** 2
+        assert store.state[r] == np.float32(s), r
+        exp = w0[r] - (0.25 if r in k0 else 0) - (0.25 * k1[r] / math.sqrt(s) if r in k1 else 0)
+        np.testing.assert_allclose(store.vals[r], exp, rtol=0, atol=1e-6)
