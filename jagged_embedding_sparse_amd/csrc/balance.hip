@@ -310,12 +310,29 @@ int check_common(const int32_t* uih_len, int32_t n, int32_t W, const int32_t* pe
 
 using namespace fs;
 
+// Per-slice count entries of a call with n samples: n * rank_slices(n), which
+// drops where the slice count steps down; the query takes the largest over
+// every n' <= n (the last n' of each sample-block count), so that a workspace
+// sized for n serves every smaller call. Past 512 blocks one slice remains
+// and the product only grows.
+static size_t max_slice_counts(int32_t n) {
+  const int32_t m = n > 0 ? n : 1;
+  size_t best = (size_t)m * (size_t)rank_slices(m);
+  const int64_t xb_end = cdiv(m, kWave) < 513 ? cdiv(m, kWave) : 513;
+  for (int64_t xb = 1; xb <= xb_end; ++xb) {
+    const int32_t k = (int32_t)(xb * kWave < m ? xb * kWave : m);
+    const size_t v = (size_t)k * (size_t)rank_slices(k);
+    best = v > best ? v : best;
+  }
+  return best;
+}
+
 extern "C" size_t fs_balance_workspace_size(int32_t n, int32_t W) {
   (void)W;
   const size_t m = (size_t)(n > 0 ? n : 1);
   Carve c(nullptr);
-  c.take<int64_t>(m);                             // sorted weights
-  c.take<int32_t>(m * (size_t)rank_slices(n));    // per-slice counts
+  c.take<int64_t>(m);                        // sorted weights
+  c.take<int32_t>(max_slice_counts(n));      // per-slice counts
   return c.used + 256;
 }
 

@@ -31,9 +31,11 @@ constexpr int kThreads = 256;
 constexpr int kLong = 4;      // longer segments take the chunked path
 // occurrences per long-path chunk (one wave): the largest of 512, 256, 128
 // that leaves about two chunks per resident wave (5 per SIMD)
+constexpr int64_t kChunkTarget = 2 * 256 * 4 * 5;
+constexpr int64_t kChunk256From = 256 * kChunkTarget;  // first n_tok with 256-chunks
+constexpr int64_t kChunk512From = 512 * kChunkTarget;  // first n_tok with 512-chunks
 inline int64_t chunk_for(int64_t n_tok) {
-  const int64_t target = 2 * 256 * 4 * 5;
-  return n_tok >= 512 * target ? 512 : (n_tok >= 256 * target ? 256 : 128);
+  return n_tok >= kChunk512From ? 512 : (n_tok >= kChunk256From ? 256 : 128);
 }
 constexpr int kShortBlocks = 4096;
 // gradient rows in flight per lane group on the long-row path (8, 12 and 16
@@ -516,10 +518,24 @@ bool dim_ok(int d) { return d == 64 || d == 128 || d == 256 || d == 512 || d == 
 
 using namespace fs;
 
+// Long-path chunks of a call with n occurrences; the workspace holds two fp64
+// partial rows per chunk. chunk_for grows with n, so the count drops where
+// the chunk size steps up: the query takes the largest count of any n' <= n
+// (the last n' before each step), so that a workspace sized for a capacity
+// serves every smaller call.
+static int64_t max_chunks(int64_t n) {
+  int64_t m = cdiv(n, chunk_for(n));
+  const int64_t last128 = (n < kChunk256From ? n : kChunk256From - 1);
+  const int64_t last256 = (n < kChunk512From ? n : kChunk512From - 1);
+  const int64_t c128 = cdiv(last128, 128), c256 = cdiv(last256, chunk_for(last256));
+  m = c128 > m ? c128 : m;
+  return c256 > m ? c256 : m;
+}
+
 extern "C" size_t fs_grad_reduce_update_workspace_size(int64_t n_tok, int32_t max_dim) {
   Carve c(nullptr);
   const int64_t n = n_tok > 0 ? n_tok : 1;
-  c.take<double>((size_t)(cdiv(n, chunk_for(n)) * 2) * (size_t)max_dim);
+  c.take<double>((size_t)(max_chunks(n) * 2) * (size_t)max_dim);
   return c.used + 256;
 }
 

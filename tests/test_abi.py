@@ -56,6 +56,34 @@ def test_workspace_queries_are_host_only_and_monotone(L):
     assert L.reduce_workspace_size(1 << 20, 256) > L.reduce_workspace_size(1 << 20, 64)
 
 
+def test_workspace_sized_for_a_capacity_serves_every_smaller_call(L):
+    """Each call rejects a workspace below its query's size for the call's own
+    sizes, so a workspace sized for a capacity must be at least the query of
+    every smaller size: the queries never decrease. The update's long-row
+    chunk grows at 2 621 440 and 5 242 880 occurrences and the balance's
+    slice count falls as the batch grows; both are checked around every such
+    step."""
+    for D in (64, 128, 1024):
+        prev = 0
+        for n in list(range(1, 4096)) + [x + d for x in (2_621_440, 5_242_880)
+                                         for d in range(-600, 600)] + [1 << 23, 1 << 24]:
+            sz = L.reduce_workspace_size(n, D)
+            assert sz >= prev, (n, D)
+            prev = sz
+        cap = L.reduce_workspace_size(5_300_000, D)
+        for n in (2_621_439, 2_621_440, 5_242_879, 5_242_880, 5_200_000):
+            assert L.reduce_workspace_size(n, D) <= cap, (n, D)
+    prev = 0
+    for n in range(0, L.FS_MAX_SAMPLES + 1):
+        sz = L.balance_workspace_size(n, 64)
+        assert sz >= prev, n
+        prev = sz
+    for n in (1, 1000, 5000, 16384):
+        assert L.bucketize_workspace_size(n, 64, 2, 64) <= L.bucketize_workspace_size(
+            n + 1, 64, 2, 64)
+        assert L.unique_workspace_size(n, 2, 64) <= L.unique_workspace_size(n + 1, 2, 64)
+
+
 FAKE = 0x1000  # never dereferenced: every case below fails host-side validation
 
 
