@@ -5,8 +5,11 @@ A step is one pass of the whole hot path over one batch. Default schedule
 iteration i (segment-reduce + optimizer), then the lookup of every row of
 iteration i+1; beside them, on stream A, balance (FBS or VBS), indexed
 permute + shard bucketize and dedup + collision split of the batch after
-next. --lookahead 1 runs the index stages one iteration ahead instead, with
-the exclusive rows' lookup ahead of the update where that pays (--lookup);
+next. --schedule prioritized splits update and lookup by class as the pages'
+Algorithm 2 does (collision rows updated, then looked up, on the caller's
+stream; exclusive rows of both iterations on two more streams).
+--lookahead 1 runs the index stages one iteration ahead instead, with the
+exclusive rows' lookup ahead of the update where that pays (--lookup);
 --sync runs everything on one stream in the order index, update, lookup.
 Inputs (IDs, lengths, gradients, tables) are resident in HBM before the
 timed region; the timed region is K steps bracketed by
@@ -17,17 +20,26 @@ the K steps, divided by the elapsed time of the K steps). Extra steps after
 the timed ones give the per-stage breakdown and the per-step median, minimum
 and maximum.
 
-Defaults: workload 5 (B=4096, W=512, one 200M x 128 bf16 table with row-wise
-Adagrad, lognormal(6.5, 1.3) lengths capped at 32768, ~6.3M IDs per batch).
+The headline line is workload 5 (B=4096, W=512, one 200M x 128 bf16 table
+with row-wise Adagrad, lognormal(6.5, 1.3) lengths capped at 32768, ~6.3M IDs
+per batch, FBS). Unless --no-per-config, `per_config` adds the same
+measurement for workloads 1-4 and for workload 5 with VBS (alpha 3/2), each
+from a shorter timed region, and `stats` gives, per workload, the realized
+collision rate (by unique rows and by tokens), the padding sparsity of the
+pages' Equation 1 (global batch, and the mean over each balancer's local
+batches), per-rank token load max/mean under FBS and VBS, empty VBS ranks
+and device memory.
 """
 
 from __future__ import annotations
 
 import argparse
+import gc
 import json
 import os
 import sys
 import time
+from dataclasses import dataclass, replace
 
 import numpy as np
 
@@ -36,6 +48,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "sparse-step IDs/s and achieved HBM GB/s (% of MI355X peak) per config"
 HBM_PEAK_GBPS = 8000.0
+PER_CONFIG = ((1, None), (2, None), (3, None), (4, None), (5, "vbs"))
 
 
 def parse():
@@ -48,11 +61,19 @@ def parse():
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--batches", type=int, default=None, help="distinct batches to cycle")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-per-config", action="store_true",
+                    help="only the headline workload (profiling runs)")
+    ap.add_argument("--per-config-steps", type=int, default=20)
     ap.add_argument("--sync", action="store_true",
                     help="one-stream synchronous schedule (analysis: isolated kernel times)")
+    ap.add_argument("--schedule", choices=["joined", "prioritized"], default="joined",
+                    help="with --lookahead 2: every row updated, then every row looked up "
+                         "(joined), or collision rows updated and looked up first with the "
+                         "exclusive rows beside them (prioritized)")
     ap.add_argument("--lookup", choices=["auto", "split", "joined"], default="auto",
-                    help="exclusive-row lookup ahead of the update (split), one lookup after "
-                         "it (joined), or chosen from the first steps' timing (auto)")
+                    help="with --lookahead 1: exclusive-row lookup ahead of the update (split), "
+                         "one lookup after it (joined), or chosen from the first steps' timing "
+                         "(auto)")
     ap.add_argument("--lookahead", type=int, choices=[1, 2], default=2,
                     help="iterations the index stages run ahead of the lookup (2: beside the "
                          "update and the lookup of the iteration before)")
@@ -85,30 +106,34 @@ def index_bytes(w, n, U):
     return 20 * n + 8 * W * W + 12 * n + 12 * U + 34 * U
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU "
-              "sharding of this path is described, not built.", file=sys.stderr)
-        sys.exit(2)
+@dataclass
+class Ctx:
+    """One workload's inputs, resident on the GPU."""
+    k: int
+    w: object
+    seed: int
+    host_batches: list
+    dev_batches: list
+    weights: list
+    states: list
+    grads_host: list
+    grads_dev: list
+    cap: int
+    n_tok: list
+
+
+def load(k, balancer, seed, nb, layout):
     import torch
 
     from jagged_embedding_sparse_amd import lib, synth
-    from jagged_embedding_sparse_amd.step import SparseStep, StageTimer
-
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
-    torch.cuda.set_device(0)
-    w = synth.workload(args.config, args.balancer)
-    seed = args.seed if args.seed is not None else args.config
-    NB = args.batches or min(w.iterations, args.warmup + args.steps + 1)
-    NB = max(NB, 2)
-    log(f"workload {args.config} {w.name} balancer={w.balancer} batches={NB}")
-
+    w = synth.workload(k, balancer)
+    seed = seed if seed is not None else k
+    NB = max(2, nb or w.iterations)
     t0 = time.time()
     gen = synth.Batches(w, seed)
     host_batches = [gen.batch(i) for i in range(NB)]
-    log(f"generated {NB} batches in {time.time() - t0:.1f}s; IDs/batch "
-        f"{np.mean([b['n_tok'] * len(w.tables) for b in host_batches]):.0f}")
+    log(f"workload {k} {w.name} balancer={w.balancer}: {NB} batches in {time.time() - t0:.1f}s; "
+        f"IDs/batch {np.mean([b['n_tok'] * len(w.tables) for b in host_batches]):.0f}")
     dev_batches = [dict(uih_len=torch.from_numpy(b["uih_len"]).cuda(),
                         sample_offsets=torch.from_numpy(b["sample_offsets"]).cuda(),
                         ids=torch.from_numpy(b["ids"]).cuda()) for b in host_batches]
@@ -116,10 +141,10 @@ def main():
     weights, states = [], []
     ada = w.optim == "rw_adagrad"
     for t, spec in enumerate(w.tables):
-        if args.layout.startswith("rowstate"):
+        if layout.startswith("rowstate"):
             tdt = torch.float32 if spec.dtype == "f32" else torch.bfloat16
             wv, st = lib.alloc_table(spec.rows, spec.dim, tdt, ada, device="cuda",
-                                     align=256 if args.layout == "rowstate256" else 16)
+                                     align=256 if layout == "rowstate256" else 16)
             weights.append(synth.init_table(spec.rows, spec.dim, spec.dtype, seed, "cuda",
                                             table=t, out=wv))
             states.append(st.zero_() if st is not None else None)
@@ -128,16 +153,26 @@ def main():
                                             table=t))
             states.append(torch.zeros(spec.rows, dtype=torch.float32, device="cuda")
                           if ada else None)
-    t0 = time.time()
     grads_host = [synth.gradient_rows(seed, 0, t, np.arange(cap), spec.dim)
                   for t, spec in enumerate(w.tables)]
     grads_dev = [torch.from_numpy(g).cuda() for g in grads_host]
-    log(f"gradients {cap} x {[s.dim for s in w.tables]} in {time.time() - t0:.1f}s")
+    return Ctx(k, w, seed, host_batches, dev_batches, weights, states, grads_host, grads_dev,
+               cap, [b["n_tok"] for b in host_batches])
 
+
+def measure(ctx, steps, warmup, args, full):
+    """Times `steps` steps after `warmup` untimed ones; with `full`, also the
+    per-stage breakdown and the per-step spread from extra steps."""
+    import torch
+
+    from jagged_embedding_sparse_amd.step import SparseStep, StageTimer
+    w, NB, n_tok, grads_dev = ctx.w, len(ctx.dev_batches), ctx.n_tok, ctx.grads_dev
+    dev_batches = ctx.dev_batches
     ahead = args.lookahead == 2 and not args.sync
-    step = SparseStep(w, weights, states, cap, lookup=args.lookup,
-                      lookahead=2 if ahead else 1, autotune={} if args.autotune else None)
-    n_tok = [b["n_tok"] for b in host_batches]
+    sched = args.schedule if ahead else "joined"
+    step = SparseStep(w, ctx.weights, ctx.states, ctx.cap, lookup=args.lookup,
+                      lookahead=2 if ahead else 1, autotune={} if args.autotune else None,
+                      schedule=sched)
     step.prologue(dev_batches[0], batch_after=dev_batches[1 % NB] if ahead else None)
     if args.sync:
         def run_step(batch_next, grads, k_next):
@@ -148,7 +183,7 @@ def main():
             return step.step(batch_next, grads,
                              batch_after=dev_batches[(k_next + 1) % NB] if ahead else None)
     k = 0
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         k += 1
         run_step(dev_batches[k % NB], [g[:n_tok[(k - 1) % NB]] for g in grads_dev], k)
     step.join()
@@ -162,11 +197,12 @@ def main():
     # A first, larger event pool, used and dropped, leaves the runtime enough
     # recycled event resources that the timed pool's records stay cheap
     # (without it, 1.5 ms of host time per step on the smallest workload).
-    n_brk = min(args.steps, 10)
-    warm = StageTimer(capacity=24 * (args.steps + n_brk), streams=(step.sA, step.sB))
+    n_brk = min(steps, 10) if full else 0
+    streams = [s for s in (step.sA, step.sB, step.sC) if s is not None]
+    warm = StageTimer(capacity=24 * (steps + n_brk), streams=streams)
     del warm
-    timer = StageTimer(capacity=2 * args.steps, streams=(step.sA, step.sB),
-                       only=("update_all",))
+    upd_names = ("update_all", "update_co", "update_ex")
+    timer = StageTimer(capacity=4 * steps, streams=streams, only=upd_names)
     step.timer = timer
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     pairs = []
@@ -174,9 +210,9 @@ def main():
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     # both events on the caller's stream: the steps' streams wait for it at
-    # the start of each step, and it waits for both of them at the end
+    # the start of each step, and it waits for all of them at the end
     ev0.record()
-    for _ in range(args.steps):
+    for _ in range(steps):
         p = k % NB
         k += 1
         run_step(dev_batches[k % NB], [g[:n_tok[p]] for g in grads_dev], k)
@@ -188,51 +224,59 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     step.timer = None
-    schedule = ("sync" if args.sync else "index two ahead, joined lookup" if ahead else
-                ("joined" if step.joined else "split"))
+    if args.sync:
+        schedule = "sync"
+    elif ahead:
+        schedule = ("index two ahead, prioritized (collision rows first)" if sched == "prioritized"
+                    else "index two ahead, joined lookup")
+    else:
+        schedule = "joined" if step.joined else "split"
     ms_total = ev0.elapsed_time(ev1)
-    ms_step = ms_total / args.steps
-    upd_ms = timer.ms()["update_all"]
-    log(f"timed {args.steps} steps: {ms_total:.3f} ms (wall {wall * 1e3:.3f} ms, host "
+    ms_step = ms_total / steps
+    upd_ms = timer.ms()
+    log(f"timed {steps} steps: {ms_total:.3f} ms (wall {wall * 1e3:.3f} ms, host "
         f"submission {submit * 1e3:.3f} ms)")
 
-    # ---------------------------------------------------------------- stage breakdown
-    brk = StageTimer(capacity=8 * n_brk, streams=(step.sA, step.sB))
-    step.timer = brk
-    for _ in range(n_brk):
-        p = k % NB
-        k += 1
-        run_step(dev_batches[k % NB], [g[:n_tok[p]] for g in grads_dev], k)
-    step.join()
-    torch.cuda.synchronize()
-    step.timer = None
-    stage_ms = brk.ms()
+    stage_ms, per_step = {}, None
+    if full:
+        # ------------------------------------------------------------ stage breakdown
+        brk = StageTimer(capacity=8 * n_brk, streams=streams)
+        step.timer = brk
+        for _ in range(n_brk):
+            p = k % NB
+            k += 1
+            run_step(dev_batches[k % NB], [g[:n_tok[p]] for g in grads_dev], k)
+        step.join()
+        torch.cuda.synchronize()
+        step.timer = None
+        stage_ms = brk.ms()
 
-    # ---------------------------------------------------------------- per-step spread
-    # K more steps with one event per step on the stream that ends each step
-    # (kept out of the timed region: each record costs the GPU a few
-    # microseconds): with the index stages two ahead the caller's stream,
-    # whose lookup waits for the index stream; otherwise stream A, whose
-    # last lookup waits for the update (and with --sync runs everything).
-    end_stream = torch.cuda.current_stream() if ahead else step.sA
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
-    for e in evs:  # first records take fresh runtime resources: not in the loop
-        e.record(end_stream)
-    torch.cuda.synchronize()
-    evs[0].record(end_stream)
-    for j in range(args.steps):
-        p = k % NB
-        k += 1
-        run_step(dev_batches[k % NB], [g[:n_tok[p]] for g in grads_dev], k)
-        evs[j + 1].record(end_stream)
-    step.join()
-    torch.cuda.synchronize()
-    per_step = np.array([evs[j].elapsed_time(evs[j + 1]) for j in range(args.steps)])
+        # ------------------------------------------------------------ per-step spread
+        # K more steps with one event per step on the stream that ends each
+        # step (kept out of the timed region: each record costs the GPU a few
+        # microseconds): with the index stages two ahead the caller's stream,
+        # whose lookup waits for the index stream; otherwise stream A, whose
+        # last lookup waits for the update (and with --sync runs everything).
+        end_stream = torch.cuda.current_stream() if ahead else step.sA
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        for e in evs:  # first records take fresh runtime resources: not in the loop
+            e.record(end_stream)
+        torch.cuda.synchronize()
+        evs[0].record(end_stream)
+        for j in range(steps):
+            p = k % NB
+            k += 1
+            run_step(dev_batches[k % NB], [g[:n_tok[p]] for g in grads_dev], k)
+            evs[j + 1].record(end_stream)
+        step.join()
+        torch.cuda.synchronize()
+        per_step = np.array([evs[j].elapsed_time(evs[j + 1]) for j in range(steps)])
 
     # ---------------------------------------------------------------- accounting
     # Units per batch pair (p -> p+1) depend only on the IDs, so one more cycle
     # of steps, synchronised, gives them for every pair the timed steps used.
     units = {}
+    T, W = len(w.tables), w.world
     for _ in range(NB):
         p = k % NB
         k += 1
@@ -240,7 +284,6 @@ def main():
         nxt = run_step(dev_batches[k % NB], [g[:n_tok[p]] for g in grads_dev], k)
         step.join()
         torch.cuda.synchronize()
-        T, W = len(w.tables), w.world
 
         def per_table(st, cls_t):
             U = int(st.uq["counts"][0])
@@ -258,7 +301,8 @@ def main():
         lco, lex, U = per_table(nxt, nxt.uq["cls"])
         uco, uex, _ = per_table(prev, prev.cls_next)
         units[p] = dict(lookup_co=lco, lookup_ex=lex, update_co=uco, update_ex=uex,
-                        n_new=n_tok[k % NB] * T, U_new=U)
+                        n_new=n_tok[k % NB] * T, U_new=U,
+                        counts=nxt.uq["counts"].cpu().numpy().tolist())
     assert int(step.err.item()) == 0, f"device error flags {int(step.err.item())}"
 
     # per-stage bytes over the timed launches
@@ -275,46 +319,175 @@ def main():
         for stage, names in parts.items():
             stage_bytes[stage] = stage_bytes.get(stage, 0) + sum(per[x] for x in names)
         step_bytes += sum(per.values()) + index_bytes(w, u["n_new"], u["U_new"])
-    stage_avg = {k2: float(np.mean(v)) for k2, v in stage_ms.items()}
-    cands = [x for x in parts if x in stage_avg]
-    dom = max(cands, key=lambda s: stage_avg[s])
-    # the roofline's kernel is timed inside the timed region (the update, the
-    # dominant stage on every workload); any other stage from the breakdown
-    dom_ms = upd_ms if dom == "update_all" else stage_ms[dom]
+    # the roofline's kernel: the update launch (the dominant stage on every
+    # workload), timed inside the timed region; with the prioritized schedule
+    # the larger of its two class launches
+    upd_avg = {s: float(np.mean(v)) for s, v in upd_ms.items()}
+    dom = max(upd_avg, key=lambda s: upd_avg[s])
     dom_bytes_per_launch = stage_bytes[dom] / len(pairs)
-    dom_gbps = dom_bytes_per_launch / (float(np.mean(dom_ms)) * 1e-3) / 1e9
+    dom_gbps = dom_bytes_per_launch / (upd_avg[dom] * 1e-3) / 1e9
     step_gbps = step_bytes / (ms_total * 1e-3) / 1e9
-    value = ids_timed / (ms_total * 1e-3)
+    res = dict(step=step, schedule=schedule, ms_step=ms_step, value=ids_timed / (ms_total * 1e-3),
+               ids_per_step=ids_timed / steps, dom=dom, dom_gbps=dom_gbps,
+               dom_bytes=dom_bytes_per_launch, dom_ms=upd_avg[dom], upd_avg=upd_avg,
+               step_bytes=step_bytes / steps, step_gbps=step_gbps,
+               stage_avg={k2: float(np.mean(v)) for k2, v in stage_ms.items()},
+               per_step=per_step, units=units, pairs=pairs, n_brk=n_brk)
+    return res
 
-    kernel_of = {
-        "lookup_co": "k_lookup (fs_jagged_lookup, collision rows)",
-        "lookup_ex": "k_lookup (fs_jagged_lookup, exclusive rows)",
-        "update_co": "k_short+k_long+k_fix (fs_grad_reduce_update, collision rows)",
-        "update_ex": "k_short+k_long+k_fix (fs_grad_reduce_update, exclusive rows)",
-        "lookup_all": "k_lookup (fs_jagged_lookup, all rows)",
-        "update_all": "k_short+k_long+k_fix (fs_grad_reduce_update, all rows)"}
 
-    # ---------------------------------------------------------------- CPU baseline
+KERNEL_OF = {
+    "update_co": "k_short+k_long+k_fix (fs_grad_reduce_update, collision rows)",
+    "update_ex": "k_short+k_long+k_fix (fs_grad_reduce_update, exclusive rows)",
+    "update_all": "k_short+k_long+k_fix (fs_grad_reduce_update, all rows)"}
+
+
+def eq1_sparsity(L):
+    """The pages' Equation 1: share of padded items when every sample of the
+    batch is padded to the batch's longest UIH."""
+    L = np.asarray(L, np.float64)
+    return float(1.0 - L.sum() / (L.max() * len(L))) if len(L) and L.max() > 0 else 0.0
+
+
+def stats(ctx, res):
+    """Per-workload statistics: collision rates, Equation 1 sparsity, per-rank
+    load under both balancers, empty VBS ranks, device memory."""
+    import torch
+
+    from jagged_embedding_sparse_amd import lib
+    w, units = ctx.w, res["units"]
+    # collision rate of iteration i+1 against i: by unique rows and by tokens
+    by_u = [u["counts"][1] / max(1, u["counts"][0]) for u in units.values()]
+    by_tok = [sum(n for n, _ in u["lookup_co"]) / max(1, u["n_new"]) for u in units.values()]
+    alpha = w.alpha if w.balancer == "vbs" else (3, 2)
+    fbs, vbs = dict(load=[], local=[]), dict(load=[], local=[], empty=[])
+    glob = []
+    for b, db in zip(ctx.host_batches, ctx.dev_batches):
+        L = b["uih_len"]
+        tok = np.diff(b["sample_offsets"])
+        glob.append(eq1_sparsity(L))
+        pf, rf = lib.fs_balance_fbs(db["uih_len"], w.world)
+        pv, rv, _ = lib.fs_balance_vbs(db["uih_len"], w.world, alpha)
+        for (pm, ro), acc in (((pf, rf), fbs), ((pv, rv), vbs)):
+            pm, ro = pm.cpu().numpy(), ro.cpu().numpy()
+            loads = np.array([tok[pm[ro[r]:ro[r + 1]]].sum() for r in range(w.world)], np.float64)
+            acc["load"].append(float(loads.max() / loads.mean()))
+            acc["local"].append(float(np.mean([eq1_sparsity(L[pm[ro[r]:ro[r + 1]]])
+                                               for r in range(w.world) if ro[r + 1] > ro[r]])))
+            if acc is vbs:
+                acc["empty"].append(int(np.sum(np.diff(ro) == 0)))
+    table_bytes = sum(x.numel() * x.element_size() for x in ctx.weights)
+    state_bytes = sum(x.numel() * x.element_size() for x in ctx.states if x is not None)
+    return {
+        "collision_rate": {"by_unique_rows": float(np.mean(by_u)),
+                           "by_tokens": float(np.mean(by_tok))},
+        "eq1_sparsity": {"global_batch": float(np.mean(glob)),
+                         "local_batches_fbs": float(np.mean(fbs["local"])),
+                         "local_batches_vbs": float(np.mean(vbs["local"]))},
+        "rank_token_load_max_over_mean": {"fbs": float(np.mean(fbs["load"])),
+                                          "vbs": float(np.mean(vbs["load"]))},
+        "vbs_alpha": f"{alpha[0]}/{alpha[1]}",
+        "vbs_empty_ranks": float(np.mean(vbs["empty"])),
+        "unique_rows_per_step": float(np.mean([u["U_new"] for u in units.values()])),
+        "device_bytes": {"tables": int(table_bytes), "state": int(state_bytes),
+                         "peak_allocated": int(torch.cuda.max_memory_allocated())},
+        "note": "means over the distinct batches; load = tokens per virtual rank"}
+
+
+def tables_name(w):
+    return "+".join(f"{t.rows // 1_000_000}Mx{t.dim}-{t.dtype}" if t.rows >= 1_000_000 else
+                    f"{t.rows // 1000}Kx{t.dim}-{t.dtype}" for t in w.tables)
+
+
+def summary(ctx, res):
+    """The per-config entry: throughput, step bandwidth, update roofline, stats."""
+    return {
+        "workload": f"workload {ctx.k}: {ctx.w.name} ({ctx.w.balancer.upper()})",
+        "ids_per_s": res["value"], "ms_per_step": res["ms_step"],
+        "ids_per_step": res["ids_per_step"], "schedule": res["schedule"],
+        "step_hbm": {"algorithmic_bytes_per_step": res["step_bytes"], "GBps": res["step_gbps"],
+                     "frac": res["step_gbps"] / HBM_PEAK_GBPS},
+        "update_roofline": {"kernel": KERNEL_OF[res["dom"]], "achieved": res["dom_gbps"],
+                            "frac": res["dom_gbps"] / HBM_PEAK_GBPS,
+                            "ms_per_launch": res["dom_ms"],
+                            "bytes_per_launch": res["dom_bytes"]},
+        "stats": stats(ctx, res)}
+
+
+def release():
+    """Returns the memory of dropped tensors to the device (after the caller
+    has dropped its references) and restarts the peak-memory count."""
+    import torch
+    gc.collect()
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    torch.cuda.reset_peak_memory_stats()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU "
+              "sharding of this path is described, not built.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    from jagged_embedding_sparse_amd import synth
+    w = synth.workload(args.config, args.balancer)
+    nb = args.batches or min(w.iterations, args.warmup + args.steps + 1)
+    ctx = load(args.config, args.balancer, args.seed, nb, args.layout)
+    res = measure(ctx, args.steps, args.warmup, args, full=True)
+    head_stats = stats(ctx, res) if not args.no_per_config else None
+
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, seed, host_batches, grads_host, weights, states)
+        cpu = cpu_baseline(ctx)
 
     # HBM bytes per launch of the dominant stage from the committed counter
     # summary (rocprofv3 FETCH_SIZE / WRITE_SIZE, copy-calibrated), when it was
     # taken on the kernel sources built here and on the same (dense) tables
     from jagged_embedding_sparse_amd.traffic import load_traffic
-    traffic = load_traffic(args.config, dom) if args.layout == "dense" else None
+    traffic = load_traffic(args.config, res["dom"]) if args.layout == "dense" else None
 
-    tables = "+".join(f"{t.rows // 1_000_000}Mx{t.dim}-{t.dtype}" if t.rows >= 1_000_000 else
-                      f"{t.rows // 1000}Kx{t.dim}-{t.dtype}" for t in w.tables)
+    per_config = None
+    if not args.no_per_config:
+        per_config = []
+        cfg_args = argparse.Namespace(**{**vars(args), "autotune": False, "sync": False})
+        # the headline workload's other balancer first, on the same batches
+        # and tables; then each other workload, loaded after the previous
+        # one's memory is released
+        order = sorted(PER_CONFIG, key=lambda kb: kb[0] != args.config)
+        res.pop("step", None)
+        c2 = None
+        for k, bal in order:
+            wk = synth.workload(k, bal)
+            if k == args.config and wk.balancer == w.balancer:
+                continue
+            if k == args.config:
+                c2 = replace(ctx, w=wk)
+            else:
+                ctx = c2 = None
+                release()
+                c2 = load(k, bal, None, min(wk.iterations, 3 + args.per_config_steps + 1),
+                          "dense")
+            r2 = measure(c2, args.per_config_steps, 3, cfg_args, full=False)
+            entry = summary(c2, r2)
+            r2 = None
+            log(f"{entry['workload']}: {entry['ms_per_step']:.3f} ms/step, "
+                f"{entry['ids_per_s']:.3e} IDs/s, step {entry['step_hbm']['frac'] * 100:.1f}% "
+                f"of peak, update {entry['update_roofline']['frac'] * 100:.1f}%")
+            per_config.append(entry)
+
     out = {
         "metric": METRIC,
-        "value": value,
+        "value": res["value"],
         "unit": "IDs/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms_step,
+        "ms_per_step": res["ms_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -322,61 +495,70 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": f"workload {args.config}: {w.name} ({w.balancer.upper()})",
-            "global_batch": w.batch, "virtual_ranks": w.world, "tables": tables,
-            "optimizer": w.optim, "ids_per_step": ids_timed / args.steps,
+            "global_batch": w.batch, "virtual_ranks": w.world, "tables": tables_name(w),
+            "optimizer": w.optim, "ids_per_step": res["ids_per_step"],
             "weights": sorted({t.dtype for t in w.tables}), "grad_accumulate": "f64",
-            "distinct_batches": NB, "schedule": schedule,
+            "distinct_batches": nb, "schedule": res["schedule"],
             "autotune": bool(args.autotune), "layout": args.layout},
         "roofline": {
-            "bound": "hbm", "achieved": dom_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-            "frac": dom_gbps / HBM_PEAK_GBPS, "traffic": traffic,
-            "kernel": kernel_of[dom],
-            "bytes_per_launch": dom_bytes_per_launch,
-            "ms_per_launch": float(np.mean(dom_ms))},
+            "bound": "hbm", "achieved": res["dom_gbps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": res["dom_gbps"] / HBM_PEAK_GBPS, "traffic": traffic,
+            "kernel": KERNEL_OF[res["dom"]],
+            "bytes_per_launch": res["dom_bytes"],
+            "ms_per_launch": res["dom_ms"]},
         "step_hbm": {
-            "algorithmic_bytes_per_step": step_bytes / args.steps, "GBps": step_gbps,
-            "frac": step_gbps / HBM_PEAK_GBPS},
-        "stages_ms": stage_avg,
-        "stages_note": f"stage breakdown from {n_brk} extra steps with every stage timed",
-        "per_step_ms": {"median": float(np.median(per_step)), "min": float(per_step.min()),
-                        "max": float(per_step.max()),
+            "algorithmic_bytes_per_step": res["step_bytes"], "GBps": res["step_gbps"],
+            "frac": res["step_gbps"] / HBM_PEAK_GBPS},
+        "stages_ms": res["stage_avg"],
+        "stages_note": f"stage breakdown from {res['n_brk']} extra steps with every stage timed",
+        "per_step_ms": {"median": float(np.median(res["per_step"])),
+                        "min": float(res["per_step"].min()),
+                        "max": float(res["per_step"].max()),
                         "note": f"{args.steps} extra steps, one event per step on the stream "
                                 "that ends it"},
         "cpu_baseline": cpu,
+        "stats": head_stats,
+        "per_config": per_config,
     }
     print(json.dumps(out))
 
 
-def cpu_baseline(w, seed, host_batches, grads_host, weights, states):
-    """The oracle, as it stands, on one synchronous iteration of the same
-    workload (batch 1, collision split against batch 0), on one host core."""
+def cpu_baseline(ctx, iters=4):
+    """The oracle, as it stands, on `iters` consecutive synchronous iterations
+    of the same workload (batches 1.., the first split against batch 0), on
+    one host core; per-stage seconds from the oracle loop's own timers."""
     import torch
 
     from oracle import oracle as O
-
-    b0, b1 = host_batches[0], host_batches[1]
+    w, hb = ctx.w, ctx.host_batches
+    iters = min(iters, len(hb) - 1)
     stores = []
     for t, spec in enumerate(w.tables):
-        rid = np.unique(b1["ids"][t])
+        rid = np.unique(np.concatenate([b["ids"][t] for b in hb[1:iters + 1]]))
         idx = torch.from_numpy(rid).cuda()
-        v = weights[t].index_select(0, idx)
+        v = ctx.weights[t].index_select(0, idx)
         vals = (v.view(torch.int16).cpu().numpy().view(np.uint16) if v.dtype == torch.bfloat16
                 else v.cpu().numpy())
-        st = states[t].index_select(0, idx).cpu().numpy() if states[t] is not None else None
+        st = ctx.states[t].index_select(0, idx).cpu().numpy() if ctx.states[t] is not None \
+            else None
         stores.append(O.RowStore(rid, vals, st, bf16=v.dtype == torch.bfloat16))
     run = O.SyncRun(w, stores)
-    run.prev_unique = run.index_stages(b0)["uniq"]["unique"]  # untimed: context for the split
-    n = b1["n_tok"]
-    g = [x[:n] for x in grads_host]
+    run.prev_unique = run.index_stages(hb[0])["uniq"]["unique"]  # untimed: context for the split
+    run.seconds = {}
+    ids = 0
     t0 = time.perf_counter()
-    run.step(b1, lambda o: g)
+    for b in hb[1:iters + 1]:
+        n = b["n_tok"]
+        g = [x[:n] for x in ctx.grads_host]
+        run.step(b, lambda o, g=g: g)
+        ids += n * len(w.tables)
     dt = time.perf_counter() - t0
-    ids = n * len(w.tables)
     log(f"oracle: {ids} IDs in {dt:.2f}s")
     return {"value": ids / dt, "unit": "IDs/s", "cores": 1, "kind": "oracle",
-            "sample": f"one synchronous iteration (balance, bucketize, dedup, collision split, "
-                      f"lookup, fp64 reduce, update) of batch 1 of the same workload, {ids} IDs, "
-                      f"{dt:.2f} s",
+            "sample": f"{iters} consecutive synchronous iterations (balance, bucketize, dedup, "
+                      f"collision split, lookup, fp64 reduce, update) of batches 1..{iters} of "
+                      f"the same workload, {ids} IDs, {dt:.2f} s",
+            "stage_seconds": {k: round(v, 3) for k, v in run.seconds.items()},
             "host": f"{_cpu_model()}, {os.cpu_count()} logical CPUs visible, 1 used"}
 
 

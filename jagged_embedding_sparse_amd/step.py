@@ -40,6 +40,20 @@ instead of only the update. Three iteration states are alive at once (i being
 updated, i+1 looked up, i+2 indexed); the result is again the synchronous
 loop's.
 
+With `schedule="prioritized"` (index stages two ahead) the update is split
+by class as Algorithm 2 splits it, so that the next lookup waits only for the
+rows it shares with the update:
+
+  caller's stream  update(i, collision rows) -> lookup(i+1, collision rows)
+  stream B         update(i, exclusive rows)          [own partial sums]
+  stream C         lookup(i+1, exclusive rows)
+  stream A         balance(i+2) -> bucketize(i+2) -> split(i+2 vs i+1)
+
+Exclusive rows of i are not rows of i+1 and exclusive rows of i+1 are not
+rows of i, so only the collision lookup orders against an update; the result
+is again the synchronous loop's. The classes of i against i+1 must exist when
+the update starts, which the two-ahead index stages provide.
+
 With `autotune` (VBS only; section 4.1's AutoTune), the balance cuts at
 per-rank shares of the weight, and right after each balance the modelled time
 of the partition it made moves the shares for the next one -- two small
@@ -141,6 +155,7 @@ class IterState:
 
 
 _LOOKUP_MODES = ("split", "joined", "auto")
+_SCHEDULES = ("joined", "prioritized")
 # VBS AutoTune: modelled time c2 L^2 + c1 L + c0 per sample (coef), shares
 # moved by max(1, share * step) outside a band of +-tol around the mean time,
 # every share starting at init
@@ -150,11 +165,18 @@ _CALIB_STEPS = 3  # steps timed by lookup="auto" before it decides
 
 class SparseStep:
     def __init__(self, workload, weights, states, n_tok_cap, device=None, lookup="auto",
-                 lookahead=1, autotune=None):
+                 lookahead=1, autotune=None, schedule="joined"):
         if lookup not in _LOOKUP_MODES:
             raise ValueError(f"lookup must be one of {_LOOKUP_MODES}, not {lookup!r}")
         if lookahead not in (1, 2):
             raise ValueError(f"lookahead must be 1 or 2, not {lookahead!r}")
+        if schedule not in _SCHEDULES:
+            raise ValueError(f"schedule must be one of {_SCHEDULES}, not {schedule!r}")
+        if schedule == "prioritized" and lookahead != 2:
+            raise ValueError("the prioritized schedule needs the index stages two ahead "
+                             "(lookahead=2): the update of i starts from the classes of i "
+                             "against i+1")
+        self.schedule = schedule
         if autotune is not None and workload.balancer != "vbs":
             raise ValueError("autotune needs the VBS balancer")
         self.w = workload
@@ -184,6 +206,8 @@ class SparseStep:
         self._calls = {}  # prepared C calls by (stage, slots, ...)
         self.sA = torch.cuda.Stream(device=d)
         self.sB = torch.cuda.Stream(device=d)
+        # exclusive-row lookup of the prioritized schedule
+        self.sC = torch.cuda.Stream(device=d) if schedule == "prioritized" else None
         self.ev_b = torch.cuda.Event()
         self.ev_idx = torch.cuda.Event()  # index stages of the iteration after i done
         self._pre = False  # lookahead=2: the iteration after i already indexed
@@ -334,6 +358,8 @@ class SparseStep:
     def step(self, batch_next, grads_cur, batch_after=None):
         """Prioritized step: update iteration i, look up iteration i+1 (and,
         with lookahead=2, index `batch_after`, iteration i+2)."""
+        if self.schedule == "prioritized":
+            return self._step_prioritized(batch_next, grads_cur, batch_after)
         if self.lookahead == 2:
             return self._step_ahead(batch_next, grads_cur, batch_after)
         self._decide()
@@ -399,6 +425,43 @@ class SparseStep:
         self.slot = (self.slot + 1) % n
         return nxt
 
+    def _step_prioritized(self, batch_next, grads_cur, batch_after):
+        # Algorithm 2's order on one GPU: the collision rows of i are updated
+        # first and their lookup for i+1 follows on the caller's stream; the
+        # exclusive rows of both iterations go beside it on streams B and C.
+        cur = self.cur
+        n = self._nslots()
+        nxt = self.states_buf[(self.slot + 1) % n]
+        sA, sB, sC = self.sA, self.sB, self.sC
+        cs = torch.cuda.current_stream()
+        # every stream after the work on the caller's stream: the batches and
+        # gradients, and the previous step (joined into it), whose buffers
+        # this one reuses
+        sA.wait_stream(cs)
+        if not self._pre:  # iteration i+1 was not indexed ahead: index it now
+            self._index_stages(batch_next, nxt, cur, sA)
+            self.ev_idx.record(sA)
+        sB.wait_stream(cs)
+        sC.wait_stream(cs)
+        # the classes of i against i+1 (the update's) and of i+1 (the lookups')
+        for s_ in (cs, sB, sC):
+            s_.wait_event(self.ev_idx)
+        self._run_update(cur, grads_cur, lib.FS_COLLISION, self.ws_red[1], cs)
+        self._lookup(nxt, lib.FS_COLLISION, cs)
+        self._run_update(cur, grads_cur, lib.FS_EXCLUSIVE, self.ws_red[0], sB)
+        self._lookup(nxt, lib.FS_EXCLUSIVE, sC)
+        self._pre = False
+        if batch_after is not None:
+            aft = self.states_buf[(self.slot + 2) % n]
+            self._index_stages(batch_after, aft, nxt, sA)
+            self.ev_idx.record(sA)
+            self._pre = True
+        cs.wait_stream(sB)
+        cs.wait_stream(sC)
+        self.cur = nxt
+        self.slot = (self.slot + 1) % n
+        return nxt
+
     def step_sync(self, batch_next, grads_cur):
         """Reference schedule on one stream: update all of i, then look up all of i+1."""
         if self._pre:
@@ -425,3 +488,5 @@ class SparseStep:
     def join(self):
         torch.cuda.current_stream().wait_stream(self.sA)
         torch.cuda.current_stream().wait_stream(self.sB)
+        if self.sC is not None:
+            torch.cuda.current_stream().wait_stream(self.sC)

@@ -15,6 +15,7 @@ from __future__ import annotations
 import ctypes as C
 import os
 import subprocess
+import time
 
 import numpy as np
 
@@ -331,22 +332,32 @@ class SyncRun:
         self.row_base = np.zeros(len(self.rows), np.int64)
         self.row_base[1:] = np.cumsum(self.rows)[:-1]
         self.prev_unique = None
+        self.seconds = {}  # wall seconds per stage, summed over the run's iterations
+
+    def _timed(self, name, fn, *a):
+        t0 = time.perf_counter()
+        r = fn(*a)
+        self.seconds[name] = self.seconds.get(name, 0.0) + time.perf_counter() - t0
+        return r
 
     def index_stages(self, batch):
         w = self.w
+        tm = self._timed
         if w.balancer == "fbs":
-            perm, ro = balance_fbs(batch["uih_len"], w.world)
+            perm, ro = tm("balance", balance_fbs, batch["uih_len"], w.world)
             rw = None
         elif self.autotune is None:
-            perm, ro, rw = balance_vbs(batch["uih_len"], w.world, w.alpha)
+            perm, ro, rw = tm("balance", balance_vbs, batch["uih_len"], w.world, w.alpha)
         else:
             at = self.autotune
-            perm, ro, rw = balance_vbs_shares(batch["uih_len"], w.world, self.shares, w.alpha)
+            perm, ro, rw = tm("balance", balance_vbs_shares, batch["uih_len"], w.world,
+                              self.shares, w.alpha)
             cost = rank_cost(batch["uih_len"], perm, ro, at["coef"])
             self.shares = vbs_autotune(cost, self.shares, at["step"], at["tol"])
-        bk = bucketize(batch["ids"], batch["sample_offsets"], self.rows, perm, ro, w.world)
-        uq = unique(bk["shard_keys"], bk["shard_bm"], self.rows, w.world)
-        cls, pcls, counts = collision(uq["unique"], self.prev_unique)
+        bk = tm("bucketize", bucketize, batch["ids"], batch["sample_offsets"], self.rows, perm,
+                ro, w.world)
+        uq = tm("dedup", unique, bk["shard_keys"], bk["shard_bm"], self.rows, w.world)
+        cls, pcls, counts = tm("collision", collision, uq["unique"], self.prev_unique)
         uq["cls"] = cls
         return dict(perm=perm, rank_offsets=ro, rank_weight=rw, bucket=bk, uniq=uq,
                     prev_cls=pcls, counts=counts)
@@ -380,7 +391,8 @@ class SyncRun:
         """One synchronous iteration. grads_fn(index_outputs) -> list of T
         balanced batch-major fp32 gradients."""
         out = self.index_stages(batch)
-        out["emb"] = self.lookup_all(out, batch["n_tok"])
-        out["reduced"] = self.reduce_update(out, grads_fn(out))
+        out["emb"] = self._timed("lookup", self.lookup_all, out, batch["n_tok"])
+        g = grads_fn(out)
+        out["reduced"] = self._timed("reduce_update", self.reduce_update, out, g)
         self.prev_unique = out["uniq"]["unique"]
         return out
