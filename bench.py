@@ -24,7 +24,8 @@ The headline line is workload 5 (B=4096, W=512, one 200M x 128 bf16 table
 with row-wise Adagrad, lognormal(6.5, 1.3) lengths capped at 32768, ~6.3M IDs
 per batch, FBS). Unless --no-per-config, `per_config` adds the same
 measurement for workloads 1-4 and for workload 5 with VBS (alpha 3/2), each
-from a shorter timed region, and `stats` gives, per workload, the realized
+in a process of its own (started after the headline run has released its
+memory) with a shorter timed region, and `stats` gives, per workload, the realized
 collision rate (by unique rows and by tokens), the padding sparsity of the
 pages' Equation 1 (global batch, and the mean over each balancer's local
 batches), per-rank token load max/mean under FBS and VBS, empty VBS ranks
@@ -37,9 +38,10 @@ import argparse
 import gc
 import json
 import os
+import subprocess
 import sys
 import time
-from dataclasses import dataclass, replace
+from dataclasses import dataclass
 
 import numpy as np
 
@@ -64,6 +66,9 @@ def parse():
     ap.add_argument("--no-per-config", action="store_true",
                     help="only the headline workload (profiling runs)")
     ap.add_argument("--per-config-steps", type=int, default=20)
+    ap.add_argument("--entry", action="store_true",
+                    help="print only this workload's per-config entry (one JSON line); the "
+                         "headline run starts one such process per other workload")
     ap.add_argument("--sync", action="store_true",
                     help="one-stream synchronous schedule (analysis: isolated kernel times)")
     ap.add_argument("--schedule", choices=["joined", "prioritized"], default="joined",
@@ -438,6 +443,13 @@ def main():
     w = synth.workload(args.config, args.balancer)
     nb = args.batches or min(w.iterations, args.warmup + args.steps + 1)
     ctx = load(args.config, args.balancer, args.seed, nb, args.layout)
+    if args.entry:
+        entry = summary(ctx, measure(ctx, args.steps, args.warmup, args, full=False))
+        log(f"{entry['workload']}: {entry['ms_per_step']:.3f} ms/step, "
+            f"{entry['ids_per_s']:.3e} IDs/s, step {entry['step_hbm']['frac'] * 100:.1f}% "
+            f"of peak, update {entry['update_roofline']['frac'] * 100:.1f}%")
+        print(json.dumps(entry))
+        return
     res = measure(ctx, args.steps, args.warmup, args, full=True)
     head_stats = stats(ctx, res) if not args.no_per_config else None
 
@@ -453,32 +465,25 @@ def main():
 
     per_config = None
     if not args.no_per_config:
-        per_config = []
-        cfg_args = argparse.Namespace(**{**vars(args), "autotune": False, "sync": False})
-        # the headline workload's other balancer first, on the same batches
-        # and tables; then each other workload, loaded after the previous
-        # one's memory is released
-        order = sorted(PER_CONFIG, key=lambda kb: kb[0] != args.config)
+        # each other workload in a process of its own, as the headline runs:
+        # a workload measured after another one's tables were released in the
+        # same process ran up to 45% slower (workload 4: 0.73 against 0.50 ms)
         res.pop("step", None)
-        c2 = None
-        for k, bal in order:
+        ctx = None
+        release()
+        per_config = []
+        for k, bal in PER_CONFIG:
             wk = synth.workload(k, bal)
             if k == args.config and wk.balancer == w.balancer:
                 continue
-            if k == args.config:
-                c2 = replace(ctx, w=wk)
-            else:
-                ctx = c2 = None
-                release()
-                c2 = load(k, bal, None, min(wk.iterations, 3 + args.per_config_steps + 1),
-                          "dense")
-            r2 = measure(c2, args.per_config_steps, 3, cfg_args, full=False)
-            entry = summary(c2, r2)
-            r2 = None
-            log(f"{entry['workload']}: {entry['ms_per_step']:.3f} ms/step, "
-                f"{entry['ids_per_s']:.3e} IDs/s, step {entry['step_hbm']['frac'] * 100:.1f}% "
-                f"of peak, update {entry['update_roofline']['frac'] * 100:.1f}%")
-            per_config.append(entry)
+            cmd = [sys.executable, os.path.abspath(__file__), "--entry", "--config", str(k),
+                   "--balancer", wk.balancer, "--steps", str(args.per_config_steps),
+                   "--warmup", "3", "--schedule", args.schedule, "--lookup", args.lookup,
+                   "--lookahead", str(args.lookahead)]
+            r = subprocess.run(cmd, stdout=subprocess.PIPE, text=True, timeout=300)
+            if r.returncode != 0:
+                raise RuntimeError(f"per-config run of workload {k} failed ({r.returncode})")
+            per_config.append(json.loads(r.stdout.strip().splitlines()[-1]))
 
     out = {
         "metric": METRIC,
