@@ -16,7 +16,9 @@
  *    all memory; no call allocates or frees, and none keeps state between
  *    calls. Scratch memory comes from a caller workspace (ws, ws_bytes) whose
  *    size a host-only fs_*_workspace_size() query returns; it depends only on
- *    capacities, never on data.
+ *    capacities, never on data, and never decreases as they shrink. (The one
+ *    exception, fs_grad_reduce_update_noalloc, uses a fixed device array of
+ *    the library's instead of a workspace.)
  *  - Every call is asynchronous on `stream`, makes no host synchronisation and
  *    may be captured. Data-dependent counts (unique rows, collisions, valid
  *    items) are written to device memory only; grids are sized by capacity.
@@ -55,6 +57,7 @@ extern "C" {
 #define FS_ERR_WORKSPACE (-2)
 #define FS_ERR_HIP (-3)
 #define FS_ERR_UNSUPPORTED (-4)
+#define FS_ERR_TOO_LARGE (-5) /* beyond an allocation-free call's fixed scratch */
 
 /* sticky device error bits */
 #define FS_EF_ID_RANGE 1  /* an ID outside [0, rows_t) was dropped */
@@ -364,6 +367,29 @@ int fs_grad_reduce_update(const fs_table* tables, int32_t T, int32_t W,
                           hipStream_t stream);
 
 size_t fs_grad_reduce_update_workspace_size(int64_t n_tok, int32_t max_dim);
+
+/* fs_grad_reduce_update_noalloc: the same call for callers that cannot      */
+/* allocate (code under HIP graph capture, tight serving loops, harnesses    */
+/* that forbid hipMalloc): no workspace argument and no allocation of any   */
+/* kind; the fp64 partial sums live in a fixed device array of              */
+/* FS_NOALLOC_SCRATCH_BYTES per GPU, held from the first call on a device   */
+/* until the process ends. Arguments, results and errors are those of        */
+/* fs_grad_reduce_update, except that sizes whose                           */
+/* fs_grad_reduce_update_workspace_size(n_tok, max dim_t) exceeds           */
+/* FS_NOALLOC_SCRATCH_BYTES return FS_ERR_TOO_LARGE (the widest table sets */
+/* the limit: n_tok up to 33 553 920 at 64 columns, 16 776 704 at 128,     */
+/* 2 097 024 at 256, 1 048 448 at 512, 524 160 at 1024). Every call on one GPU */
+/* uses the same array: calls that overlap on one GPU (on different streams */
+/* without an order between them) race and give undefined results; calls   */
+/* ordered on one stream, or by events, are safe. Nothing in the array      */
+/* needs clearing: each call writes every partial it reads.                 */
+#define FS_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int fs_grad_reduce_update_noalloc(const fs_table* tables, int32_t T, int32_t W,
+                                  const float* const* grad, int64_t n_tok, const int64_t* unique,
+                                  const int64_t* unique_offsets, const int32_t* seg_offsets,
+                                  const int32_t* occ_bm, const int32_t* occ_uid,
+                                  const uint8_t* cls, int32_t which, int32_t optim, float lr,
+                                  float eps, float* const* reduced_out, hipStream_t stream);
 
 /* ------------------------------------------------------------------------ */
 const char* fs_strerror(int code);

@@ -8,6 +8,7 @@ extern "C" const char* fs_strerror(int code) {
     case FS_ERR_WORKSPACE: return "workspace missing or too small";
     case FS_ERR_HIP: return "HIP launch failed";
     case FS_ERR_UNSUPPORTED: return "unsupported shape or parameter";
+    case FS_ERR_TOO_LARGE: return "sizes need more than the fixed scratch of an allocation-free call";
   }
   return "unknown error";
 }

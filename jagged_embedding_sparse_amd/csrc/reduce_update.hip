@@ -22,6 +22,8 @@
 //     in chunk order and updates it.
 // Lanes: a group of LPG = min(64, D/4) lanes covers a row, 4*CPL/4 columns
 // per lane (16-byte gradient loads); weights use the same column mapping.
+#include <mutex>
+
 #include "common.hpp"
 
 namespace fs {
@@ -539,14 +541,15 @@ extern "C" size_t fs_grad_reduce_update_workspace_size(int64_t n_tok, int32_t ma
   return c.used + 256;
 }
 
-extern "C" int fs_grad_reduce_update(const fs_table* tables, int32_t T, int32_t W,
-                                     const float* const* grad, int64_t n_tok,
-                                     const int64_t* unique, const int64_t* unique_offsets,
-                                     const int32_t* seg_offsets, const int32_t* occ_bm,
-                                     const int32_t* occ_uid, const uint8_t* cls, int32_t which,
-                                     int32_t optim, float lr, float eps,
-                                     float* const* reduced_out, void* ws, size_t ws_bytes,
-                                     hipStream_t stream) {
+namespace {
+
+// Host-side checks shared by both entry points: arguments, shapes, and a
+// scratch area of ws_bytes for the long rows' fp64 partial sums.
+int ru_check(const fs_table* tables, int32_t T, int32_t W, const float* const* grad,
+             int64_t n_tok, const int64_t* unique, const int64_t* unique_offsets,
+             const int32_t* seg_offsets, const int32_t* occ_bm, const int32_t* occ_uid,
+             const uint8_t* cls, int32_t which, int32_t optim, size_t ws_bytes,
+             int too_small) {
   if (!tables || T < 1 || T > FS_MAX_TABLES || W < 1 || W > FS_MAX_RANKS || n_tok < 0 ||
       (int64_t)T * n_tok >= (int64_t)INT32_MAX || !grad || !unique_offsets || !seg_offsets)
     return FS_ERR_INVALID_ARG;
@@ -567,9 +570,16 @@ extern "C" int fs_grad_reduce_update(const fs_table* tables, int32_t T, int32_t 
     base += tb.rows;
   }
   if (base > (int64_t)UINT32_MAX) return FS_ERR_UNSUPPORTED;
-  if (!ws || ws_bytes < fs_grad_reduce_update_workspace_size(n_tok, max_dim))
-    return FS_ERR_WORKSPACE;
-  base = 0;
+  if (ws_bytes < fs_grad_reduce_update_workspace_size(n_tok, max_dim)) return too_small;
+  return FS_OK;
+}
+
+int ru_launch(const fs_table* tables, int32_t T, int32_t W, const float* const* grad,
+              int64_t n_tok, const int64_t* unique, const int64_t* unique_offsets,
+              const int32_t* seg_offsets, const int32_t* occ_bm, const int32_t* occ_uid,
+              const uint8_t* cls, int32_t which, int32_t optim, float lr, float eps,
+              float* const* reduced_out, void* ws, hipStream_t stream) {
+  int64_t base = 0;
   for (int t = 0; t < T; ++t) {
     const fs_table& tb = tables[t];
     RUArgs a;
@@ -602,4 +612,75 @@ extern "C" int fs_grad_reduce_update(const fs_table* tables, int32_t T, int32_t 
     if (rc) return rc;
   }
   return FS_OK;
+}
+
+// The allocation-free variant's scratch: one array per GPU the library runs
+// on, held until the process ends. Host code never passes the array's name
+// (a host-side stand-in); it passes the device address that
+// hipGetSymbolAddress returns, queried once per device with that device
+// current.
+__device__ __align__(256) unsigned char scratch[FS_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int scratch_for(hipStream_t stream, void** out) {
+  int cur = 0;
+  if (hipGetDevice(&cur) != hipSuccess) return FS_ERR_HIP;
+  int dev = cur;
+  if (stream) {
+    hipDevice_t d = 0;
+    if (hipStreamGetDevice(stream, &d) != hipSuccess) return FS_ERR_HIP;
+    dev = (int)d;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return FS_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    if (dev != cur && hipSetDevice(dev) != hipSuccess) return FS_ERR_HIP;
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur && hipSetDevice(cur) != hipSuccess) return FS_ERR_HIP;
+    if (e != hipSuccess || !p) return FS_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return FS_OK;
+}
+
+}  // namespace
+
+extern "C" int fs_grad_reduce_update(const fs_table* tables, int32_t T, int32_t W,
+                                     const float* const* grad, int64_t n_tok,
+                                     const int64_t* unique, const int64_t* unique_offsets,
+                                     const int32_t* seg_offsets, const int32_t* occ_bm,
+                                     const int32_t* occ_uid, const uint8_t* cls, int32_t which,
+                                     int32_t optim, float lr, float eps,
+                                     float* const* reduced_out, void* ws, size_t ws_bytes,
+                                     hipStream_t stream) {
+  int rc = ru_check(tables, T, W, grad, n_tok, unique, unique_offsets, seg_offsets, occ_bm,
+                    occ_uid, cls, which, optim, ws ? ws_bytes : 0, FS_ERR_WORKSPACE);
+  if (rc) return rc;
+  return ru_launch(tables, T, W, grad, n_tok, unique, unique_offsets, seg_offsets, occ_bm,
+                   occ_uid, cls, which, optim, lr, eps, reduced_out, ws, stream);
+}
+
+extern "C" int fs_grad_reduce_update_noalloc(const fs_table* tables, int32_t T, int32_t W,
+                                             const float* const* grad, int64_t n_tok,
+                                             const int64_t* unique,
+                                             const int64_t* unique_offsets,
+                                             const int32_t* seg_offsets, const int32_t* occ_bm,
+                                             const int32_t* occ_uid, const uint8_t* cls,
+                                             int32_t which, int32_t optim, float lr, float eps,
+                                             float* const* reduced_out, hipStream_t stream) {
+  int rc = ru_check(tables, T, W, grad, n_tok, unique, unique_offsets, seg_offsets, occ_bm,
+                    occ_uid, cls, which, optim, FS_NOALLOC_SCRATCH_BYTES, FS_ERR_TOO_LARGE);
+  if (rc) return rc;
+  void* ws = nullptr;
+  rc = scratch_for(stream, &ws);
+  if (rc) return rc;
+  // every fp64 partial a launch reads is written earlier in the same launch
+  // sequence, so the scratch needs no clearing between calls
+  return ru_launch(tables, T, W, grad, n_tok, unique, unique_offsets, seg_offsets, occ_bm,
+                   occ_uid, cls, which, optim, lr, eps, reduced_out, ws, stream);
 }

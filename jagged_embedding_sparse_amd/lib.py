@@ -18,6 +18,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("FS_SPARSE_LIB", os.path.join(_HERE, "libfs_sparse.so"))
 
 FS_OK, FS_ERR_INVALID_ARG, FS_ERR_WORKSPACE, FS_ERR_HIP, FS_ERR_UNSUPPORTED = 0, -1, -2, -3, -4
+FS_ERR_TOO_LARGE = -5
+FS_NOALLOC_SCRATCH_BYTES = 64 << 20
 FS_EF_ID_RANGE, FS_EF_SHAPE, FS_EF_LEN_RANGE = 1, 2, 4
 FS_F32, FS_BF16 = 0, 1
 FS_SGD, FS_RW_ADAGRAD = 0, 1
@@ -71,6 +73,9 @@ _c_kt_ws = _sig("fs_keyed_transpose_workspace_size", _sz, _i32, _i32)
 _c_reduce = _sig("fs_grad_reduce_update", C.c_int, _TP, _i32, _i32, C.POINTER(_P), _i64, _P, _P,
                  _P, _P, _P, _P, _i32, _i32, _f, _f, C.POINTER(_P), _P, _sz, _P)
 _c_reduce_ws = _sig("fs_grad_reduce_update_workspace_size", _sz, _i64, _i32)
+_c_reduce_noalloc = _sig("fs_grad_reduce_update_noalloc", C.c_int, _TP, _i32, _i32,
+                         C.POINTER(_P), _i64, _P, _P, _P, _P, _P, _P, _i32, _i32, _f, _f,
+                         C.POINTER(_P), _P)
 _c_strerror = _sig("fs_strerror", C.c_char_p, C.c_int)
 _c_version = _sig("fs_version", C.c_int)
 
@@ -79,7 +84,7 @@ EXPORTED = ["fs_balance_fbs", "fs_balance_vbs", "fs_balance_workspace_size",
             "fs_bucketize_permute", "fs_bucketize_workspace_size", "fs_unique_collision_split",
             "fs_unique_workspace_size", "fs_jagged_lookup", "fs_ranged_combine",
             "fs_keyed_transpose", "fs_keyed_transpose_workspace_size",
-            "fs_grad_reduce_update",
+            "fs_grad_reduce_update", "fs_grad_reduce_update_noalloc",
             "fs_grad_reduce_update_workspace_size", "fs_strerror", "fs_version"]
 
 
@@ -407,6 +412,22 @@ def fs_grad_reduce_update(weights, states, W, grads, n_tok, uq, optim, lr, eps=0
                      _ptr(uq["occ_uid"]), _ptr(cls) if which != FS_ALL else None, which,
                      FS_RW_ADAGRAD if optim in ("rw_adagrad", FS_RW_ADAGRAD) else FS_SGD,
                      float(lr), float(eps), red, _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def fs_grad_reduce_update_noalloc(weights, states, W, grads, n_tok, uq, optim, lr, eps=0.0,
+                                  which=FS_ALL, cls=None, reduced_out=None, stream=None):
+    """fs_grad_reduce_update without a workspace (the library's fixed per-GPU
+    scratch; raises FsError FS_ERR_TOO_LARGE beyond it)."""
+    T = len(weights)
+    tabs = make_tables(weights, states)
+    red = _ptr_array(reduced_out) if reduced_out is not None else None
+    _check("fs_grad_reduce_update_noalloc",
+           _c_reduce_noalloc(tabs, T, W, _ptr_array(grads), n_tok, _ptr(uq["unique"]),
+                             _ptr(uq["unique_offsets"]), _ptr(uq["seg_offsets"]),
+                             _ptr(uq["occ_bm"]), _ptr(uq["occ_uid"]),
+                             _ptr(cls) if which != FS_ALL else None, which,
+                             FS_RW_ADAGRAD if optim in ("rw_adagrad", FS_RW_ADAGRAD) else FS_SGD,
+                             float(lr), float(eps), red, _stream(stream)))
 
 
 # ---------------------------------------------------------------------------- prepared calls

@@ -84,6 +84,28 @@ def test_workspace_sized_for_a_capacity_serves_every_smaller_call(L):
         assert L.unique_workspace_size(n, 2, 64) <= L.unique_workspace_size(n + 1, 2, 64)
 
 
+def test_noalloc_update_rejects_sizes_beyond_its_scratch(L):
+    """The allocation-free update checks on the host that the batch's partial
+    sums fit its fixed scratch: FS_ERR_TOO_LARGE past the limit, and the
+    other argument checks as the workspace-taking call. Nothing is launched."""
+    F = 0x1000
+    tabs = _tables(L, [(5000, 1024, L.FS_F32, False)])
+    grads = (C.c_void_p * 1)(F)
+    call = L._c_reduce_noalloc
+    # 524 160 occurrences at 1024 columns fit; one more does not
+    assert L.reduce_workspace_size(524_160, 1024) <= L.FS_NOALLOC_SCRATCH_BYTES
+    assert L.reduce_workspace_size(524_161, 1024) > L.FS_NOALLOC_SCRATCH_BYTES
+    assert call(tabs, 1, 4, grads, 524_161, F, F, F, F, F, None, L.FS_ALL, L.FS_SGD, 0.1, 0.0,
+                None, None) == L.FS_ERR_TOO_LARGE
+    assert call(tabs, 1, 4, grads, 1 << 25, F, F, F, F, F, None, L.FS_ALL, L.FS_SGD, 0.1, 0.0,
+                None, None) == L.FS_ERR_TOO_LARGE
+    assert call(tabs, 1, 4, grads, 1000, F, F, F, F, F, None, 7, L.FS_SGD, 0.1, 0.0,
+                None, None) == L.FS_ERR_INVALID_ARG
+    assert call(tabs, 1, 4, grads, 1000, None, F, F, F, F, None, L.FS_ALL, L.FS_SGD, 0.1, 0.0,
+                None, None) == L.FS_ERR_INVALID_ARG
+    assert L.strerror(L.FS_ERR_TOO_LARGE) != "unknown error"
+
+
 FAKE = 0x1000  # never dereferenced: every case below fails host-side validation
 
 
