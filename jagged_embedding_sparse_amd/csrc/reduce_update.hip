@@ -9,10 +9,13 @@
 //
 // g_u = sum of grad[bm] over u's occurrences, accumulated in fp64 and rounded
 // once to fp32, so the result does not depend on how the sum is split.
-// Zipf IDs make segment lengths span 1 .. ~10^5, so two paths:
-//   short rows (<= kLong = 4 occurrences, most rows): one lane group per row,
-//     grid-stride over the table's unique rows; all of a row's loads are in
-//     flight at once, then the group sums and updates the row.
+// Zipf IDs make segment lengths span 1 .. ~10^5, so three kernels:
+//   short rows (<= kShort = 4 occurrences, most rows): one lane group per
+//     row, grid-stride over the table's unique rows; all of a row's loads
+//     are in flight at once, then the group sums and updates the row.
+//   medium rows (kShort < len < kChunkMin = 65): one lane group per row as
+//     well; the group loads all of the row's occurrence indices with one
+//     load and streams its gradient rows kMedBatch at a time.
 //   long rows: the table's occurrence range is cut into chunks (128 to 512
 //     occurrences, smaller for smaller batches so that the grid still has
 //     about two chunks per resident wave);
@@ -30,7 +33,9 @@ namespace fs {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kLong = 4;      // longer segments take the chunked path
+constexpr int kShort = 4;      // rows whose loads all go out at once
+constexpr int kChunkMin = 65;  // rows this long or longer take the chunked path
+constexpr int kMedBatch = 8;   // gradient rows in flight per lane group (medium rows)
 // occurrences per long-path chunk (one wave): the largest of 512, 256, 128
 // that leaves about two chunks per resident wave (5 per SIMD)
 constexpr int64_t kChunkTarget = 2 * 256 * 4 * 5;
@@ -242,17 +247,18 @@ __global__ void __launch_bounds__(kThreads) k_short(RUArgs a) {
     const bool in = l < unit && uu < u_hi;
     const int32_t lo = in ? a.seg_offsets[uu] : 0;
     const int32_t hi = in ? a.seg_offsets[uu + 1] : 0;
-    const bool act = in && (hi - lo) <= kLong && class_ok(a, uu);
+    const int32_t len = hi - lo;
+    const bool act = in && len <= kShort && class_ok(a, uu);
     const uint64_t actm = __ballot(act);
     if (!actm) continue;
     const uint32_t row = act ? (uint32_t)(a.unique[uu] - a.row_base) : 0u;
     const float st = (act && ada) ? *state_at(a, row) : 0.f;
-    // the row's (at most kLong) gradient slots, loaded once per unit beside
+    // the row's (at most kShort) gradient slots, loaded once per unit beside
     // its key and state: a batch below then waits for one round of loads
     // (its gradient and weight rows), not for the slots first
-    int32_t obm[kLong];
+    int32_t obm[kShort];
 #pragma unroll
-    for (int m = 0; m < kLong; ++m) obm[m] = (act && m < hi - lo) ? a.occ_bm[lo + m] : 0;
+    for (int m = 0; m < kShort; ++m) obm[m] = (act && m < len) ? a.occ_bm[lo + m] : 0;
 #pragma unroll 1
     for (int j0 = 0; j0 < unit; j0 += PER) {
       const uint64_t win = (PER >= kWave) ? ~0ull : (((1ull << PER) - 1ull) << j0);
@@ -270,7 +276,7 @@ __global__ void __launch_bounds__(kThreads) k_short(RUArgs a) {
         jrow[r] = (uint32_t)__shfl((int)row, j, kWave);
         jst[r] = __shfl(st, j, kWave);
       }
-      // a short row has at most kLong occurrences: its weight row and all of
+      // a short row has at most kShort occurrences: its weight row and all of
       // its gradient rows load at once
       RowW<D, WT> wr[R];
       double acc[R][M::CPL];
@@ -279,12 +285,12 @@ __global__ void __launch_bounds__(kThreads) k_short(RUArgs a) {
         if (ja[r]) load_w<D, WT>(a, jrow[r], sub, wr[r]);
 #pragma unroll
       for (int r = 0; r < R; ++r) {
-        const int len = ja[r] ? jlen[r] : 0;
-        float4 gv[kLong][M::NV];
+        const int rlen = ja[r] ? jlen[r] : 0;
+        float4 gv[kShort][M::NV];
 #pragma unroll
-        for (int m = 0; m < kLong; ++m) {
+        for (int m = 0; m < kShort; ++m) {
           const int32_t bm = __shfl(obm[m], jj[r], kWave);
-          if (m < len) {
+          if (m < rlen) {
             const float4* gp = (const float4*)(a.grad + (int64_t)bm * D);
 #pragma unroll
             for (int v = 0; v < M::NV; ++v) gv[m][v] = ld_stream(gp + sub + v * M::LPG);
@@ -293,8 +299,8 @@ __global__ void __launch_bounds__(kThreads) k_short(RUArgs a) {
 #pragma unroll
         for (int c = 0; c < M::CPL; ++c) acc[r][c] = 0.0;
 #pragma unroll
-        for (int m = 0; m < kLong; ++m) {
-          if (m < len) {
+        for (int m = 0; m < kShort; ++m) {
+          if (m < rlen) {
 #pragma unroll
             for (int v = 0; v < M::NV; ++v) {
               acc[r][4 * v + 0] += (double)gv[m][v].x;
@@ -313,6 +319,101 @@ __global__ void __launch_bounds__(kThreads) k_short(RUArgs a) {
   }
 }
 
+// ---------------------------------------------------------------- medium rows
+// Rows of kShort < len < kChunkMin occurrences (about 4% of the rows and 13%
+// of the occurrences at workload 5's Zipf IDs). Grid-stride over the table's
+// unique rows in units of 64: the wave finds the unit's medium rows by one
+// ballot, then each lane group takes one of them: the group's lanes load all
+// of the row's occurrence slots with one load (kMedSlots per lane), its
+// weight row and state go out beside them, and its gradient rows stream
+// kMedBatch at a time. A wave thus has GPW rows in progress instead of
+// walking them one after another inside a chunk.
+template <int D, typename WT>
+__global__ void __launch_bounds__(kThreads) k_medium(RUArgs a) {
+  using M = Map<D>;
+  constexpr int kMedSlots = (kChunkMin - 1 + M::LPG - 1) / M::LPG;
+  static_assert(M::LPG % kMedBatch == 0, "a batch must not straddle slot registers");
+  const int64_t u_lo = a.unique_offsets[a.g_lo], u_hi = a.unique_offsets[a.g_hi];
+  const int l = lane(), grp = l / M::LPG, sub = l % M::LPG;
+  const bool ada = a.optim == FS_RW_ADAGRAD;
+  const int64_t wid = (int64_t)blockIdx.x * (kThreads / kWave) + threadIdx.x / kWave;
+  const int64_t nwaves = (int64_t)gridDim.x * (kThreads / kWave);
+  for (int64_t ub = u_lo + wid * kWave; ub < u_hi; ub += nwaves * kWave) {
+    const int64_t uu = ub + l;
+    const bool in = uu < u_hi;
+    const int32_t lo = in ? a.seg_offsets[uu] : 0;
+    const int32_t len = in ? a.seg_offsets[uu + 1] - lo : 0;
+    const bool med = in && len > kShort && len < kChunkMin && class_ok(a, uu);
+    uint64_t medm = __ballot(med);
+    if (!medm) continue;
+    const uint32_t row = med ? (uint32_t)(a.unique[uu] - a.row_base) : 0u;
+    const float st = (med && ada) ? *state_at(a, row) : 0.f;
+    while (medm) {
+      uint64_t mm = medm;
+      int myj = -1;
+#pragma unroll
+      for (int g = 0; g < M::GPW; ++g) {
+        const int j = mm ? __ffsll((unsigned long long)mm) - 1 : -1;
+        mm &= mm ? mm - 1 : 0ull;
+        if (g == grp) myj = j;
+      }
+      medm = mm;
+      const bool on = myj >= 0;
+      const int js = on ? myj : 0;
+      const int32_t mlen = __shfl(len, js, kWave), mlo = __shfl(lo, js, kWave);
+      const uint32_t mrow = (uint32_t)__shfl((int)row, js, kWave);
+      const float mst = __shfl(st, js, kWave);
+      const int glen = on ? mlen : 0;
+      RowW<D, WT> wr;
+      if (on) load_w<D, WT>(a, mrow, sub, wr);
+      int32_t mb[kMedSlots];
+#pragma unroll
+      for (int q = 0; q < kMedSlots; ++q) {
+        const int m = q * M::LPG + sub;
+        mb[q] = m < glen ? a.occ_bm[mlo + m] : 0;
+      }
+      int wlen = glen;  // longest row of this round (wave-uniform)
+#pragma unroll
+      for (int off = M::LPG; off < kWave; off <<= 1) wlen = max(wlen, __shfl_xor(wlen, off, kWave));
+      double acc[M::CPL];
+#pragma unroll
+      for (int c = 0; c < M::CPL; ++c) acc[c] = 0.0;
+      // a batch of kMedBatch (a divisor of LPG) lies inside one slot register
+#pragma unroll 1
+      for (int m0 = 0; m0 < wlen; m0 += kMedBatch) {
+        const int q = m0 / M::LPG;
+        int32_t slot = mb[0];
+#pragma unroll
+        for (int x = 1; x < kMedSlots; ++x) slot = q == x ? mb[x] : slot;
+        float4 gv[kMedBatch][M::NV];
+#pragma unroll
+        for (int e = 0; e < kMedBatch; ++e) {
+          const int m = m0 + e;
+          const int32_t bm = __shfl(slot, grp * M::LPG + (m % M::LPG), kWave);
+          if (m < glen) {
+            const float4* gp = (const float4*)(a.grad + (int64_t)bm * D);
+#pragma unroll
+            for (int v = 0; v < M::NV; ++v) gv[e][v] = ld_stream(gp + sub + v * M::LPG);
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < kMedBatch; ++e) {
+          if (m0 + e < glen) {
+#pragma unroll
+            for (int v = 0; v < M::NV; ++v) {
+              acc[4 * v + 0] += (double)gv[e][v].x;
+              acc[4 * v + 1] += (double)gv[e][v].y;
+              acc[4 * v + 2] += (double)gv[e][v].z;
+              acc[4 * v + 3] += (double)gv[e][v].w;
+            }
+          }
+        }
+      }
+      apply_row<D, WT>(a, ub + js, mrow, mst, sub, acc, wr, on);
+    }
+  }
+}
+
 // ---------------------------------------------------------------- long rows
 template <int D, typename WT>
 __device__ __forceinline__ void long_chunk(const RUArgs& a, int64_t o_lo, int64_t o_hi,
@@ -326,7 +427,7 @@ __device__ __forceinline__ void long_chunk(const RUArgs& a, int64_t o_lo, int64_
     const int32_t uu = ub + lane();
     const bool in = uu <= u_last;
     const int32_t lo = in ? a.seg_offsets[uu] : 0, hi = in ? a.seg_offsets[uu + 1] : 0;
-    uint64_t todo = __ballot(in && hi - lo > kLong && class_ok(a, uu));
+    uint64_t todo = __ballot(in && hi - lo >= kChunkMin && class_ok(a, uu));
     while (todo) {
       const int j = __ffsll((unsigned long long)todo) - 1;
       todo &= todo - 1;
@@ -430,7 +531,7 @@ __global__ void __launch_bounds__(kThreads) k_fix(RUArgs a) {
   const int64_t ce = min(cb + a.chunk, o_hi);
   const int64_t u = a.occ_uid[ce - 1];
   const int64_t s_lo = a.seg_offsets[u], s_hi = a.seg_offsets[u + 1];
-  if (!(s_hi - s_lo > kLong && s_lo >= cb && s_hi > ce && class_ok(a, u))) return;
+  if (!(s_hi - s_lo >= kChunkMin && s_lo >= cb && s_hi > ce && class_ok(a, u))) return;
   const int64_t c_last = (s_hi - 1 - o_lo) / a.chunk;  // slot 0 of chunks c+1..c_last
   const int64_t n_parts = 1 + (c_last - c);
   const int w = threadIdx.x / kWave;
@@ -489,6 +590,12 @@ int launch_all(const RUArgs& a, hipStream_t stream) {
   if (sb > kShortBlocks) sb = kShortBlocks;
   if (sb < 1) sb = 1;
   hipLaunchKernelGGL((k_short<D, WT>), dim3((unsigned)sb), dim3(kThreads), 0, stream, a);
+  FS_LAUNCH_CHECK();
+  // medium rows: a unit of 64 rows per wave, about two units per wave
+  int64_t mb = cdiv(a.n_cap, 2 * kWave * (kThreads / kWave));
+  if (mb > kShortBlocks) mb = kShortBlocks;
+  if (mb < 1) mb = 1;
+  hipLaunchKernelGGL((k_medium<D, WT>), dim3((unsigned)mb), dim3(kThreads), 0, stream, a);
   FS_LAUNCH_CHECK();
   const int64_t chunks = cdiv(a.n_cap, a.chunk);
   if (chunks > 0) {
