@@ -241,8 +241,11 @@ size_t fs_bucketize_workspace_size(int64_t n_tok, int32_t n, int32_t T, int32_t 
 /*                 input gives unspecified results but writes nothing past    */
 /*                 the outputs.                                               */
 /*  n_cap          host: capacity of the shard arrays (T*n_tok).             */
-/*  prev_unique, prev_counts: the previous call's unique and counts (device), */
-/*                 or both NULL for the first iteration (all rows exclusive). */
+/*  prev_unique, prev_unique_offsets, prev_counts: the previous call's        */
+/*                 unique, unique_offsets and counts (device; a call with the */
+/*                 same tables and W), or all three NULL for the first        */
+/*                 iteration (all rows exclusive). Offsets are clamped into   */
+/*                 [0, prev U] and made rising.                               */
 /*  prev_cap       host: capacity of prev_unique / prev_cls (0 when NULL).   */
 /* Outputs (capacities n_cap unless noted):                                  */
 /*  unique         int64 unique keys, ascending (= by table, then row). The   */
@@ -261,8 +264,9 @@ size_t fs_bucketize_workspace_size(int64_t n_tok, int32_t n, int32_t T, int32_t 
 int fs_unique_collision_split(const int64_t* shard_keys, const int32_t* shard_bm,
                               const int64_t* shard_offsets, int64_t n_cap,
                               const fs_table* tables, int32_t T, int32_t W,
-                              const int64_t* prev_unique, const int64_t* prev_counts,
-                              int64_t prev_cap, int64_t* unique, int64_t* unique_offsets,
+                              const int64_t* prev_unique, const int64_t* prev_unique_offsets,
+                              const int64_t* prev_counts, int64_t prev_cap, int64_t* unique,
+                              int64_t* unique_offsets,
                               int32_t* seg_offsets, int32_t* occ_bm, int32_t* occ_uid,
                               uint8_t* cls, uint8_t* prev_cls, int64_t* counts, void* ws,
                               size_t ws_bytes, hipStream_t stream);

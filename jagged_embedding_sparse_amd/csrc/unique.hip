@@ -16,9 +16,9 @@
 //  2. Head flags (key differs from its left neighbour), one scan over tiles,
 //     compaction: unique keys, CSR segment starts, occurrence -> unique index,
 //     and the (table, shard) group offsets, written where the group changes.
-//  3. Set intersection of the new and previous unique lists by merge path:
-//     one search per 2048-element tile of the merged order, then exact
-//     membership tests inside LDS.
+//  3. Set intersection of the new and previous unique lists, group by
+//     (table, shard) group: chunks of each group's rows and the previous
+//     rows in their key range staged in LDS, membership tests both ways.
 #include "colscan.hpp"
 #include "common.hpp"
 
@@ -551,95 +551,108 @@ k_compact(const uint32_t* __restrict__ sk, const int64_t* __restrict__ nvp, Grou
 }
 
 // ---------------------------------------------------------------- collision
-constexpr int kMergeThreads = 256;
-constexpr int kMergeTile = 2048;  // merged elements per workgroup
+// Both unique lists are ascending and split into the same (table, shard)
+// groups (unique_offsets of this call and of the previous one), and a key of
+// group g can only meet keys of group g, so the intersection runs per group.
+// Group g's new rows are cut into chunks of kCoChunk; workgroup s of the
+// group takes chunks s, s + S, .... Chunk c owns the previous rows whose keys
+// lie from its first key up to the next chunk's first key (the first chunk
+// from the group's start, the last one to its end), so every previous row
+// is classed by exactly one chunk. Each chunk's rows, and its previous rows
+// in pieces of kCoPiece, are staged in LDS as 32-bit keys (every key is
+// below 2^32) and tested for membership both ways by binary search. Reads
+// are one pass over both lists, plus two wave searches per chunk of a group
+// with more than one chunk.
+constexpr int kCoThreads = 512;
+constexpr int kCoChunk = 4096;  // a typical group (a few thousand rows) is one chunk: no search
+constexpr int kCoPer = kCoChunk / kCoThreads;
+constexpr int kCoPiece = 4096;
 
-// Merged order of a (new) and b (prev) with ties taken from b first: the
-// number of a-elements among the first d merged elements is the smallest i
-// for which a[i] does not precede b[d-i-1], searched by a whole wave.
-__device__ __forceinline__ int64_t merge_split(const int64_t* a, int64_t na, const int64_t* b,
-                                               int64_t nb, int64_t d) {
-  const int64_t lo = d > nb ? d - nb : 0, hi = d < na ? d : na;
-  return wave_partition_point(lo, hi, [&](int64_t i) { return a[i] < b[d - i - 1]; });
-}
-
-__device__ __forceinline__ int lds_upper(const uint32_t* s, int n, uint32_t v) {  // # s <= v
-  int lo = 0, hi = n;
+__device__ __forceinline__ bool lds_has(const uint32_t* s, int n, uint32_t v) {
+  int lo = 0, hi = n;  // first s[k] >= v
   while (lo < hi) {
-    int mid = (lo + hi) >> 1;
-    if (s[mid] <= v) lo = mid + 1; else hi = mid;
-  }
-  return lo;
-}
-
-__device__ __forceinline__ int lds_lower(const uint32_t* s, int n, uint32_t v) {  // # s < v
-  int lo = 0, hi = n;
-  while (lo < hi) {
-    int mid = (lo + hi) >> 1;
+    const int mid = (lo + hi) >> 1;
     if (s[mid] < v) lo = mid + 1; else hi = mid;
   }
-  return lo;
+  return lo < n && s[lo] == v;
 }
 
-__global__ void __launch_bounds__(kMergeThreads)
-k_collide(const int64_t* __restrict__ a, const int64_t* __restrict__ counts_a, int64_t cap_a,
-          const int64_t* __restrict__ b, const int64_t* __restrict__ counts_b, int64_t cap_b,
-          uint8_t* __restrict__ cls, uint8_t* __restrict__ prev_cls,
+__global__ void __launch_bounds__(kCoThreads)
+k_collide(const int64_t* __restrict__ a, const int64_t* __restrict__ a_off,
+          const int64_t* __restrict__ counts_a, int64_t cap_a, const int64_t* __restrict__ b,
+          const int64_t* __restrict__ b_off, const int64_t* __restrict__ counts_b, int64_t cap_b,
+          int32_t S, uint8_t* __restrict__ cls, uint8_t* __restrict__ prev_cls,
           uint32_t* __restrict__ block_hits) {
-  // slices as 32-bit keys (every key is below 2^32)
-  __shared__ uint32_t sa[kMergeTile + 1], sb[kMergeTile + 1];
-  __shared__ int64_t span[4];
-  __shared__ uint32_t hits[kMergeThreads / kWave];
+  __shared__ uint32_t sa[kCoChunk], sb[kCoPiece];
+  __shared__ int64_t span[2];
+  __shared__ uint32_t hits[kCoThreads / kWave];
+  const int32_t g = blockIdx.x / S, s0 = blockIdx.x % S;
   const int64_t na = min(counts_a[0], cap_a);
-  const int64_t nb = counts_b ? max((int64_t)0, min(counts_b[0], cap_b)) : 0;
-  const int64_t M = na + nb;
-  const int64_t d0 = (int64_t)blockIdx.x * kMergeTile;
+  const int64_t a_lo = min(max(a_off[g], (int64_t)0), na);
+  const int64_t a_hi = min(max(a_off[g + 1], a_lo), na);
+  int64_t b_lo = 0, b_hi = 0;
+  if (b) {
+    const int64_t nb = max((int64_t)0, min(counts_b[0], cap_b));
+    b_lo = min(max(b_off[g], (int64_t)0), nb);
+    b_hi = min(max(b_off[g + 1], b_lo), nb);
+  }
+  const int64_t nchunks = max((int64_t)1, cdiv(a_hi - a_lo, kCoChunk));
+  const int w = threadIdx.x / kWave;
   uint32_t mine = 0;
-  if (d0 < M) {
-    const int w = threadIdx.x / kWave;
-    if (w < 2) {  // wave 0 splits at the tile's start, wave 1 at its end
-      const int64_t d = w == 0 ? d0 : min(M, d0 + kMergeTile);
-      const int64_t i = merge_split(a, na, b, nb, d);
-      if (lane() == 0) {
-        span[w] = i;
-        span[2 + w] = d - i;
+  for (int64_t c = s0; c < nchunks; c += S) {
+    const int64_t i0 = a_lo + c * kCoChunk, i1 = min(i0 + kCoChunk, a_hi);
+    const int na_c = (int)(i1 - i0);
+    // this chunk's previous rows: wave 0 finds where they start, wave 1
+    // where they end (the first key of the next chunk)
+    if (w < 2) {
+      int64_t r;
+      if (w == 0) {
+        const int64_t key = c == 0 ? -1 : a[i0];
+        r = c == 0 ? b_lo
+                   : wave_partition_point(b_lo, b_hi, [&](int64_t k) { return b[k] < key; });
+      } else {
+        const int64_t key = c + 1 < nchunks ? a[i1] : 0;
+        r = c + 1 < nchunks
+                ? wave_partition_point(b_lo, b_hi, [&](int64_t k) { return b[k] < key; })
+                : b_hi;
+      }
+      if (lane() == 0) span[w] = r;
+    }
+    for (int x = threadIdx.x; x < na_c; x += kCoThreads) sa[x] = (uint32_t)a[i0 + x];
+    __syncthreads();
+    const int64_t j0 = span[0], j1 = span[1];
+    bool found[kCoPer];
+#pragma unroll
+    for (int k = 0; k < kCoPer; ++k) found[k] = false;
+    for (int64_t jp = j0; jp < j1; jp += kCoPiece) {
+      const int nb_p = (int)min((int64_t)kCoPiece, j1 - jp);
+      for (int x = threadIdx.x; x < nb_p; x += kCoThreads) sb[x] = (uint32_t)b[jp + x];
+      __syncthreads();
+#pragma unroll
+      for (int k = 0; k < kCoPer; ++k) {
+        const int x = k * kCoThreads + threadIdx.x;
+        if (x < na_c) found[k] = found[k] || lds_has(sb, nb_p, sa[x]);
+      }
+      for (int x = threadIdx.x; x < nb_p; x += kCoThreads)
+        prev_cls[jp + x] = lds_has(sa, na_c, sb[x]) ? FS_COLLISION : FS_EXCLUSIVE;
+      __syncthreads();  // sb is reused by the next piece
+    }
+#pragma unroll
+    for (int k = 0; k < kCoPer; ++k) {
+      const int x = k * kCoThreads + threadIdx.x;
+      if (x < na_c) {
+        cls[i0 + x] = found[k] ? FS_COLLISION : FS_EXCLUSIVE;
+        mine += found[k];
       }
     }
-    __syncthreads();
-    const int64_t i0 = span[0], i1 = span[1], j0 = span[2], j1 = span[3];
-    const int ca = (int)(i1 - i0), cb = (int)(j1 - j0);
-    // sa[0] = a[i1] sentinel area is after the slice; sb holds b[j0-1] first
-    for (int x = threadIdx.x; x < ca; x += kMergeThreads) sa[x] = (uint32_t)a[i0 + x];
-    for (int x = threadIdx.x; x < cb; x += kMergeThreads) sb[x + 1] = (uint32_t)b[j0 + x];
-    if (threadIdx.x == 0) {
-      // b element before the slice, a element after it (read only when they exist)
-      sb[0] = j0 > 0 ? (uint32_t)b[j0 - 1] : 0u;
-      sa[ca] = i1 < na ? (uint32_t)a[i1] : 0xFFFFFFFFu;
-    }
-    __syncthreads();
-    // a side: a[i] collides iff the last b <= a[i] equals it
-    for (int x = threadIdx.x; x < ca; x += kMergeThreads) {
-      const uint32_t v = sa[x];
-      const int jj = lds_upper(sb + 1, cb, v);  // b elements of the slice <= v
-      const uint32_t last = sb[jj];             // sb[0] when none in the slice
-      const bool hit = (j0 + jj > 0) && last == v;
-      cls[i0 + x] = hit ? FS_COLLISION : FS_EXCLUSIVE;
-      mine += hit;
-    }
-    // b side: b[j] collides iff the first a >= b[j] equals it
-    for (int x = threadIdx.x; x < cb; x += kMergeThreads) {
-      const uint32_t v = sb[x + 1];
-      const int ii = lds_lower(sa, ca, v);  // a elements of the slice < v
-      const bool hit = (i0 + ii < na) && sa[ii] == v;
-      prev_cls[j0 + x] = hit ? FS_COLLISION : FS_EXCLUSIVE;
-    }
+    __syncthreads();  // sa and span are reused by the next chunk
   }
   mine = wave_sum(mine);
-  if (lane() == 0) hits[threadIdx.x / kWave] = mine;
+  if (lane() == 0) hits[w] = mine;
   __syncthreads();
   if (threadIdx.x == 0) {
     uint32_t sum = 0;
-    for (int k = 0; k < kMergeThreads / kWave; ++k) sum += hits[k];
+    for (int k = 0; k < kCoThreads / kWave; ++k) sum += hits[k];
     block_hits[blockIdx.x] = sum;
   }
 }
@@ -679,8 +692,16 @@ static int64_t seg_tiles(int64_t cap, int32_t W) {
   return (int64_t)align_up((size_t)(cdiv(cap, kTile) + W), kXcd);
 }
 
+// Workgroups per (table, shard) group of the collision split: about four
+// chunks of the group's expected rows (a fourth of its items) each
+static int32_t collide_splits(int64_t cap, int32_t T, int32_t W) {
+  const int64_t s = cdiv(cap, (int64_t)T * W * kCoChunk * 4);
+  return (int32_t)(s < 1 ? 1 : (s > 64 ? 64 : s));
+}
+
 extern "C" size_t fs_unique_workspace_size(int64_t n_cap, int64_t prev_cap, int32_t T,
                                            int32_t W) {
+  (void)prev_cap;  // the collision split needs no space per previous row
   const int64_t cap = n_cap > 0 ? n_cap : 1;
   const int64_t tiles = cdiv(cap, kTile);
   const int64_t G = seg_tiles(cap, W);
@@ -699,16 +720,17 @@ extern "C" size_t fs_unique_workspace_size(int64_t n_cap, int64_t prev_cap, int3
   c.take<int32_t>((size_t)T * W);               // group moves (several tables)
   c.take<uint32_t>((size_t)tiles);              // heads per tile
   c.take<int64_t>(1);                           // valid item count
-  c.take<uint32_t>((size_t)cdiv(cap + (prev_cap > 0 ? prev_cap : 0), kMergeTile) + 1);
-                                                // collisions per merge tile
+  c.take<uint32_t>((size_t)T * W * collide_splits(cap, T, W));  // collisions per workgroup
   return c.used + 256;
 }
 
 extern "C" int fs_unique_collision_split(const int64_t* shard_keys, const int32_t* shard_bm,
                                          const int64_t* shard_offsets, int64_t n_cap,
                                          const fs_table* tables, int32_t T, int32_t W,
-                                         const int64_t* prev_unique, const int64_t* prev_counts,
-                                         int64_t prev_cap, int64_t* unique,
+                                         const int64_t* prev_unique,
+                                         const int64_t* prev_unique_offsets,
+                                         const int64_t* prev_counts, int64_t prev_cap,
+                                         int64_t* unique,
                                          int64_t* unique_offsets, int32_t* seg_offsets,
                                          int32_t* occ_bm, int32_t* occ_uid, uint8_t* cls,
                                          uint8_t* prev_cls, int64_t* counts, void* ws,
@@ -719,7 +741,9 @@ extern "C" int fs_unique_collision_split(const int64_t* shard_keys, const int32_
     return FS_ERR_INVALID_ARG;
   if (n_cap > 0 && (!shard_keys || !shard_bm || !unique || !occ_bm || !occ_uid || !cls))
     return FS_ERR_INVALID_ARG;
-  if ((prev_unique == nullptr) != (prev_counts == nullptr)) return FS_ERR_INVALID_ARG;
+  if ((prev_unique == nullptr) != (prev_counts == nullptr) ||
+      (prev_unique == nullptr) != (prev_unique_offsets == nullptr))
+    return FS_ERR_INVALID_ARG;
   if (prev_unique && (prev_cap < 0 || !prev_cls)) return FS_ERR_INVALID_ARG;
   if (!prev_unique) prev_cap = 0;
   Groups g;
@@ -780,8 +804,9 @@ extern "C" int fs_unique_collision_split(const int64_t* shard_keys, const int32_
   int32_t* delta = c.take<int32_t>((size_t)T * W);
   uint32_t* tile_heads = c.take<uint32_t>((size_t)tiles);
   int64_t* n_valid = c.take<int64_t>(1);
-  const int64_t merge_blocks = cdiv(cap + prev_cap, kMergeTile);
-  uint32_t* block_hits = c.take<uint32_t>((size_t)merge_blocks);
+  const int32_t co_split = collide_splits(cap, T, W);
+  const int64_t co_blocks = (int64_t)T * W * co_split;
+  uint32_t* block_hits = c.take<uint32_t>((size_t)co_blocks);
 
   const int kbits = key_bits(span);
   const int passes = (kbits + kMaxDigitBits - 1) / kMaxDigitBits;
@@ -845,11 +870,11 @@ extern "C" int fs_unique_collision_split(const int64_t* shard_keys, const int32_
   hipLaunchKernelGGL(k_compact, dim3(grid), dim3(kThreads), 0, stream, sk, n_valid, g,
                      tile_heads, counts, unique, seg_offsets, occ_uid, unique_offsets);
   FS_LAUNCH_CHECK();
-  hipLaunchKernelGGL(k_collide, dim3((unsigned)merge_blocks), dim3(kMergeThreads), 0, stream,
-                     unique, counts, n_cap, prev_unique, prev_counts, prev_cap, cls, prev_cls,
-                     block_hits);
+  hipLaunchKernelGGL(k_collide, dim3((unsigned)co_blocks), dim3(kCoThreads), 0, stream, unique,
+                     unique_offsets, counts, n_cap, prev_unique, prev_unique_offsets,
+                     prev_counts, prev_cap, co_split, cls, prev_cls, block_hits);
   FS_LAUNCH_CHECK();
-  hipLaunchKernelGGL(k_collide_counts, dim3(1), dim3(kThreads), 0, stream, block_hits, merge_blocks,
+  hipLaunchKernelGGL(k_collide_counts, dim3(1), dim3(kThreads), 0, stream, block_hits, co_blocks,
                      prev_counts, prev_cap, counts);
   FS_LAUNCH_CHECK();
   return FS_OK;

@@ -61,7 +61,7 @@ _c_bucketize = _sig("fs_bucketize_permute", C.c_int, _P, _i64, _P, _i32, _TP, _i
                     _P, _P, _P, _P, _P, _P, _P, _sz, _P)
 _c_bucketize_ws = _sig("fs_bucketize_workspace_size", _sz, _i64, _i32, _i32, _i32)
 _c_unique = _sig("fs_unique_collision_split", C.c_int, _P, _P, _P, _i64, _TP, _i32, _i32, _P, _P,
-                 _i64, _P, _P, _P, _P, _P, _P, _P, _P, _P, _sz, _P)
+                 _P, _i64, _P, _P, _P, _P, _P, _P, _P, _P, _P, _sz, _P)
 _c_unique_ws = _sig("fs_unique_workspace_size", _sz, _i64, _i64, _i32, _i32)
 _c_lookup = _sig("fs_jagged_lookup", C.c_int, _TP, _i32, _i32, _P, _P, _P, _P, _P, _P, _i32,
                  C.POINTER(_P), _i64, _P)
@@ -297,7 +297,7 @@ def unique_workspace_size(n_cap, T, W, prev_cap=None):
 
 def fs_unique_collision_split(shard_keys, shard_bm, shard_offsets, n_cap, rows, W,
                               prev_unique=None, prev_counts=None, prev_cap=0, out=None, ws=None,
-                              stream=None):
+                              stream=None, prev_unique_offsets=None):
     d = _dev()
     T = len(rows)
     cap = max(int(n_cap), 1)
@@ -316,7 +316,8 @@ def fs_unique_collision_split(shard_keys, shard_bm, shard_offsets, n_cap, rows, 
     ws = _ws(unique_workspace_size(n_cap, T, W, prev_cap), ws)
     _check("fs_unique_collision_split",
            _c_unique(_ptr(shard_keys), _ptr(shard_bm), _ptr(shard_offsets), int(n_cap), tabs, T,
-                     W, _ptr(prev_unique), _ptr(prev_counts), int(prev_cap) if prev_unique
+                     W, _ptr(prev_unique), _ptr(prev_unique_offsets), _ptr(prev_counts),
+                     int(prev_cap) if prev_unique
                      is not None else 0, _ptr(uq), _ptr(uo), _ptr(seg), _ptr(occ_bm),
                      _ptr(occ_uid), _ptr(cls), _ptr(pcls) if prev_unique is not None else None,
                      _ptr(counts), _ptr(ws), ws.numel(), _stream(stream)))
@@ -507,12 +508,13 @@ def prepare_unique(bucket, rows, W, uq, prev_uq, prev_cls, ws):
     has = prev_uq is not None
     args = [_ptr(bucket["shard_keys"]), _ptr(bucket["shard_bm"]), _ptr(bucket["shard_offsets"]),
             0, tabs, len(rows), W, _ptr(prev_uq["unique"]) if has else None,
+            _ptr(prev_uq["unique_offsets"]) if has else None,
             _ptr(prev_uq["counts"]) if has else None, 0, _ptr(uq["unique"]),
             _ptr(uq["unique_offsets"]), _ptr(uq["seg_offsets"]), _ptr(uq["occ_bm"]),
             _ptr(uq["occ_uid"]), _ptr(uq["cls"]), _ptr(prev_cls) if has else None,
             _ptr(uq["counts"]), _ptr(ws), ws.numel(), None]
     return Prepared("fs_unique_collision_split", _c_unique, args,
-                    dict(n_cap=3, prev_cap=9, stream=20))
+                    dict(n_cap=3, prev_cap=10, stream=21))
 
 
 def prepare_lookup(weights, W, uq, out, which=FS_ALL, cls=None):

@@ -51,7 +51,8 @@ def test_workspace_queries_are_host_only_and_monotone(L):
     assert a < L.bucketize_workspace_size(1 << 20, 4096, 2, 512) < \
         L.bucketize_workspace_size(1 << 20, 4096, 2, 1024)
     assert L.unique_workspace_size(1 << 22, 1, 512) >= 16 * (1 << 22)
-    assert L.unique_workspace_size(1 << 20, 1, 512, prev_cap=1 << 24) > \
+    # the collision split needs no space per previous row
+    assert L.unique_workspace_size(1 << 20, 1, 512, prev_cap=1 << 24) == \
         L.unique_workspace_size(1 << 20, 1, 512, prev_cap=1 << 20)
     assert L.reduce_workspace_size(1 << 20, 256) > L.reduce_workspace_size(1 << 20, 64)
 
@@ -156,11 +157,14 @@ def test_bucketize_rejects(L):
 def test_unique_rejects(L):
     f = L._c_unique
     tab = _tables(L, [(1000, 64, L.FS_F32, False)])
-    call = lambda prev_u, prev_c, ws: f(FAKE, FAKE, FAKE, 100, tab, 1, 4, prev_u, prev_c, 100,
-                                        FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws,
-                                        None)
-    assert call(FAKE, None, 1 << 20) == L.FS_ERR_INVALID_ARG  # prev arrays come in pairs
-    assert call(None, None, 64) == L.FS_ERR_WORKSPACE
+    call = lambda prev_u, prev_o, prev_c, ws: f(FAKE, FAKE, FAKE, 100, tab, 1, 4, prev_u, prev_o,
+                                                prev_c, 100, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                                FAKE, FAKE, FAKE, ws, None)
+    # the previous iteration's arrays come all three or none
+    assert call(FAKE, FAKE, None, 1 << 20) == L.FS_ERR_INVALID_ARG
+    assert call(FAKE, None, FAKE, 1 << 20) == L.FS_ERR_INVALID_ARG
+    assert call(None, FAKE, None, 1 << 20) == L.FS_ERR_INVALID_ARG
+    assert call(None, None, None, 64) == L.FS_ERR_WORKSPACE
 
 
 def test_lookup_and_update_reject_unsupported_rows(L):

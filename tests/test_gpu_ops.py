@@ -514,7 +514,7 @@ def _gpu_unique(bk, rows, W, n_cap, prev=None, prev_cap=0):
     return lib.fs_unique_collision_split(
         bk["shard_keys"], bk["shard_bm"], bk["shard_offsets"], n_cap, rows, W,
         prev_unique=prev["unique"] if prev else None, prev_counts=prev["counts"] if prev else None,
-        prev_cap=prev_cap)
+        prev_cap=prev_cap, prev_unique_offsets=prev["unique_offsets"] if prev else None)
 
 
 def _cmp_unique(uq, ouq, cls, pcls, counts):
@@ -563,6 +563,29 @@ def test_unique_collision_parity(case):
         _cmp_unique(uq, ouq, cls, pcls if prev else None, counts)
         if it == 2:
             assert counts[1] == counts[0]
+        prev, oprev, prev_cap = uq, ouq, n_cap
+
+
+@pytest.mark.parametrize("W,rows", [(1, [2_000_000]), (3, [300_000, 1_000_000])],
+                         ids=["W1", "W3-2tables"])
+def test_collision_uneven_batches(W, rows):
+    """Consecutive batches of very different sizes (big, small, big, big): a
+    group's rows cut into many chunks and spread over several workgroups,
+    and one chunk's previous rows spanning many LDS pieces; classes and
+    counts equal the oracle's."""
+    T = len(rows)
+    prev, oprev, prev_cap = None, None, 0
+    for it, (N, maxlen) in enumerate([(4096, 120), (16, 20), (4096, 120), (2048, 60)]):
+        say("collision-uneven", W, rows, it)
+        b = _tiny_batch(7000 + it, N, rows, maxlen)
+        _, _, bk, _ = _gpu_bucketize(b, rows, W)
+        _, _, obk = _oracle_bucketize(b, rows, W)
+        n_cap = T * b["n_tok"]
+        uq = _gpu_unique(bk, rows, W, n_cap, prev, prev_cap)
+        ouq = O.unique(obk["shard_keys"], obk["shard_bm"], rows, W)
+        cls, pcls, counts = O.collision(ouq["unique"], oprev["unique"] if oprev else None)
+        torch.cuda.synchronize()
+        _cmp_unique(uq, ouq, cls, pcls if prev else None, counts)
         prev, oprev, prev_cap = uq, ouq, n_cap
 
 
