@@ -342,9 +342,9 @@ def measure(ctx, steps, warmup, args, full):
 
 
 KERNEL_OF = {
-    "update_co": "k_short+k_long+k_fix (fs_grad_reduce_update, collision rows)",
-    "update_ex": "k_short+k_long+k_fix (fs_grad_reduce_update, exclusive rows)",
-    "update_all": "k_short+k_long+k_fix (fs_grad_reduce_update, all rows)"}
+    "update_co": "k_short+k_medium+k_long+k_fix (fs_grad_reduce_update, collision rows)",
+    "update_ex": "k_short+k_medium+k_long+k_fix (fs_grad_reduce_update, exclusive rows)",
+    "update_all": "k_short+k_medium+k_long+k_fix (fs_grad_reduce_update, all rows)"}
 
 
 def eq1_sparsity(L):

@@ -16,9 +16,11 @@ copy kernel: exactly 1 GiB read and 1 GiB written per dispatch), then runs a
 few steps of the synchronous schedule of bench.py. `summarize` divides each
 kernel's counter by what the counter reads for that copy per KiB moved (the
 calibration factor), and records per-dispatch bytes per kernel, the bytes of
-one update launch (k_short + k_long + k_fix) and one lookup launch, and a
-hash of the kernel sources the figures belong to: bench.py reports them only
-while the sources are unchanged.
+one update launch (k_short + k_medium + k_long + k_fix) and one lookup
+launch, and a hash of the kernel sources the figures belong to: bench.py
+reports them only while the sources are unchanged. With --txt it also writes
+a readable table: every kernel's bytes per step and the index kernels' total
+beside their algorithmic bytes.
 """
 
 from __future__ import annotations
@@ -37,7 +39,7 @@ CALIB_BYTES = 1 << 30
 
 # kernels of each stage and the sources they are built from
 STAGES = {
-    "update_all": (("k_short", "k_long", "k_fix"), ("reduce_update.hip", "common.hpp")),
+    "update_all": (("k_short", "k_medium", "k_long", "k_fix"), ("reduce_update.hip", "common.hpp")),
     "lookup_all": (("k_lookup",), ("gather.hip", "common.hpp")),
 }
 
@@ -64,7 +66,7 @@ def run(config: int) -> None:
     import bench
 
     sys.argv = ["bench.py", "--config", str(config), "--sync", "--steps", "3", "--warmup", "1",
-                "--batches", "3", "--no-cpu-baseline"]
+                "--batches", "3", "--no-cpu-baseline", "--no-per-config"]
     bench.main()
 
 
@@ -130,6 +132,41 @@ def summarize(fetch_csv: str, write_csv: str, config: int, out_path: str | None)
     return res
 
 
+# kernels of the index stages (balance, bucketize, dedup + collision split)
+INDEX_KERNELS = ("k_rank_part", "k_place", "k_vbs_cut", "k_lens", "k_bal", "k_tiles", "k_prep1",
+                 "k_hist", "k_colsum", "k_colscan", "k_colscan1", "k_scatter", "k_seg_prep",
+                 "k_seg_hist", "k_seg_groups", "k_seg_scatter", "k_heads", "k_heads_scan",
+                 "k_compact", "k_collide", "k_collide_counts")
+
+
+def table(res: dict, steps: int, index_algorithmic: float | None) -> str:
+    """Per-kernel HBM bytes per step (dispatches / steps per step) and the
+    index kernels' total against their algorithmic bytes."""
+    lines = ["kernel                               dispatches   fetch MB/step  write MB/step"]
+    idx = 0.0
+    for name, v in sorted(res["kernels"].items(), key=lambda kv: kv[1]["short"]):
+        per = v["dispatches"] / steps
+        f = (v["fetch_bytes"] or 0.0) * per / 1e6
+        w = (v["write_bytes"] or 0.0) * per / 1e6
+        label = v["short"] + ("<int64 in>" if "<long" in name else
+                              "<u32 in>" if "<unsigned int" in name else "")
+        lines.append(f"{label:36s} {v['dispatches']:10d} {f:15.2f} {w:14.2f}")
+        if v["short"] in INDEX_KERNELS:
+            idx += (f + w) * 1e6
+    for st, v in res["stages"].items():
+        lines.append(f"{st}: {v['fetch_bytes_per_launch'] / 1e9:.3f} GB fetched + "
+                     f"{v['write_bytes_per_launch'] / 1e9:.3f} GB written = "
+                     f"{v['bytes_per_launch'] / 1e9:.3f} GB per launch ({v['launches']} "
+                     f"launches; kernel sources {v['sources_sha']})")
+    extra = ""
+    if index_algorithmic:
+        extra = (f" against {index_algorithmic / 1e9:.3f} GB algorithmic "
+                 f"({idx / index_algorithmic:.2f}x)")
+    lines.append(f"index kernels (balance, bucketize, dedup, collision split): "
+                 f"{idx / 1e9:.3f} GB per step{extra}")
+    return "\n".join(lines) + "\n"
+
+
 def load_traffic(config: int, stage: str):
     """Bytes per launch of `stage` from profiles/, or None when absent or taken
     on other kernel sources."""
@@ -154,11 +191,20 @@ def main() -> None:
     s.add_argument("write_csv")
     s.add_argument("--config", type=int, default=5)
     s.add_argument("--out", default=None)
+    s.add_argument("--txt", default=None, help="also write the readable table here")
+    s.add_argument("--steps", type=int, default=None,
+                   help="steps the run made (default: the update's launches)")
+    s.add_argument("--index-bytes", type=float, default=None,
+                   help="algorithmic bytes of the index stages per step")
     a = ap.parse_args()
     if a.cmd == "run":
         run(a.config)
     else:
-        summarize(a.fetch_csv, a.write_csv, a.config, a.out)
+        res = summarize(a.fetch_csv, a.write_csv, a.config, a.out)
+        if a.txt:
+            steps = a.steps or res["stages"]["update_all"]["launches"]
+            with open(a.txt, "w") as fh:
+                fh.write(table(res, steps, a.index_bytes))
 
 
 if __name__ == "__main__":

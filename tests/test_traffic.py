@@ -57,3 +57,20 @@ def test_load_traffic_refuses_other_sources(tmp_path, monkeypatch):
     (prof / "traffic_workload9.json").write_text(json.dumps(rec))
     assert traffic.load_traffic(9, "update_all") is None
     assert traffic.load_traffic(8, "update_all") is None
+
+
+def test_table_lists_kernels_per_step_and_index_total(tmp_path):
+    gib_kib = (1 << 30) / 1024
+    f, wr = tmp_path / "f.csv", tmp_path / "w.csv"
+    copies = [("__amd_rocclr_copyBuffer", gib_kib / 2)] * 3
+    KH = "fs::(anonymous namespace)::k_heads(unsigned int const*, long const*, int, unsigned int*)"
+    # two steps: k_heads reads 1000 KiB per dispatch, writes 10 KiB
+    _csv(f, "FETCH_SIZE", copies + [(KS, 1000.0)] * 2 + [(KH, 500.0)] * 2)
+    _csv(wr, "WRITE_SIZE", [(k, v * 2) for k, v in copies] + [(KS, 100.0)] * 2 + [(KH, 10.0)] * 2)
+    res = traffic.summarize(str(f), str(wr), 5, None)
+    txt = traffic.table(res, 2, index_algorithmic=1024.0 * 1000)
+    # per step: fetch 500 KiB / 0.5 = 1 MiB, write 10 KiB
+    heads = [ln for ln in txt.splitlines() if ln.startswith("k_heads")][0].split()
+    assert abs(float(heads[2]) - 1024 * 1000 / 1e6) < 0.006
+    assert abs(float(heads[3]) - 10 * 1024 / 1e6) < 0.006
+    assert "index kernels" in txt and "1.01x" in txt
