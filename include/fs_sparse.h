@@ -359,9 +359,10 @@ size_t fs_keyed_transpose_workspace_size(int32_t F, int32_t B);
 /*               entries): row u of table t is written at u - unique_offsets[t*W]. */
 /* dim_t must be 64, 128, 256, 512 or 1024 (else FS_ERR_UNSUPPORTED);        */
 /* FS_RW_ADAGRAD needs every table's state.                                   */
-/*  ws, ws_bytes  at least fs_grad_reduce_update_workspace_size(n_tok,       */
+/*  ws, ws_bytes  at least fs_grad_reduce_update_workspace_size(n_tok, T,    */
 /*               max dim_t) bytes (fp64 partial sums of rows longer than a   */
-/*               chunk), else FS_ERR_WORKSPACE.                               */
+/*               chunk, a region per table so that the tables' rows run side */
+/*               by side), else FS_ERR_WORKSPACE.                             */
 int fs_grad_reduce_update(const fs_table* tables, int32_t T, int32_t W,
                           const float* const* grad, int64_t n_tok, const int64_t* unique,
                           const int64_t* unique_offsets, const int32_t* seg_offsets,
@@ -370,7 +371,7 @@ int fs_grad_reduce_update(const fs_table* tables, int32_t T, int32_t W,
                           float* const* reduced_out, void* ws, size_t ws_bytes,
                           hipStream_t stream);
 
-size_t fs_grad_reduce_update_workspace_size(int64_t n_tok, int32_t max_dim);
+size_t fs_grad_reduce_update_workspace_size(int64_t n_tok, int32_t T, int32_t max_dim);
 
 /* fs_grad_reduce_update_noalloc: the same call for callers that cannot      */
 /* allocate (code under HIP graph capture, tight serving loops, harnesses    */
@@ -379,10 +380,11 @@ size_t fs_grad_reduce_update_workspace_size(int64_t n_tok, int32_t max_dim);
 /* FS_NOALLOC_SCRATCH_BYTES per GPU, held from the first call on a device   */
 /* until the process ends. Arguments, results and errors are those of        */
 /* fs_grad_reduce_update, except that sizes whose                           */
-/* fs_grad_reduce_update_workspace_size(n_tok, max dim_t) exceeds           */
-/* FS_NOALLOC_SCRATCH_BYTES return FS_ERR_TOO_LARGE (the widest table sets */
-/* the limit: n_tok up to 33 553 920 at 64 columns, 16 776 704 at 128,     */
-/* 2 097 024 at 256, 1 048 448 at 512, 524 160 at 1024). Every call on one GPU */
+/* fs_grad_reduce_update_workspace_size(n_tok, T, max dim_t) exceeds        */
+/* FS_NOALLOC_SCRATCH_BYTES return FS_ERR_TOO_LARGE (one table of the       */
+/* widest width: n_tok up to 33 553 920 at 64 columns, 16 776 704 at 128,  */
+/* 2 097 024 at 256, 1 048 448 at 512, 524 160 at 1024; T tables need T    */
+/* times the space). Every call on one GPU */
 /* uses the same array: calls that overlap on one GPU (on different streams */
 /* without an order between them) race and give undefined results; calls   */
 /* ordered on one stream, or by events, are safe. Nothing in the array      */

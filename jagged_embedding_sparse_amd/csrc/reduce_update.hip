@@ -228,7 +228,7 @@ __device__ __forceinline__ void update_row(const RUArgs& a, int64_t u, int sub,
 // 32 or 16 otherwise, so that small batches spread over more waves and each
 // wave's chain of dependent rounds stays short.
 template <int D, typename WT>
-__global__ void __launch_bounds__(kThreads) k_short(RUArgs a) {
+__device__ __forceinline__ void short_rows(const RUArgs& a, int64_t bid, int64_t nblk) {
   using M = Map<D>;
   // rows per lane group and batch: 2 keeps the register count at 90 (five
   // waves per SIMD), which measured faster than 4 rows at four waves
@@ -237,8 +237,8 @@ __global__ void __launch_bounds__(kThreads) k_short(RUArgs a) {
   const int64_t u_lo = a.unique_offsets[a.g_lo], u_hi = a.unique_offsets[a.g_hi];
   const int l = lane(), grp = l / M::LPG, sub = l % M::LPG;
   const bool ada = a.optim == FS_RW_ADAGRAD;
-  const int64_t wid = (int64_t)blockIdx.x * (kThreads / kWave) + threadIdx.x / kWave;
-  const int64_t nwaves = (int64_t)gridDim.x * (kThreads / kWave);
+  const int64_t wid = bid * (kThreads / kWave) + threadIdx.x / kWave;
+  const int64_t nwaves = nblk * (kThreads / kWave);
   const int64_t n_rows = u_hi - u_lo;
   const int unit = n_rows >= 2 * kWave * kResident ? kWave
                    : (n_rows >= 2 * 32 * kResident ? 32 : 16);
@@ -329,15 +329,15 @@ __global__ void __launch_bounds__(kThreads) k_short(RUArgs a) {
 // kMedBatch at a time. A wave thus has GPW rows in progress instead of
 // walking them one after another inside a chunk.
 template <int D, typename WT>
-__global__ void __launch_bounds__(kThreads) k_medium(RUArgs a) {
+__device__ __forceinline__ void medium_rows(const RUArgs& a, int64_t bid, int64_t nblk) {
   using M = Map<D>;
   constexpr int kMedSlots = (kChunkMin - 1 + M::LPG - 1) / M::LPG;
   static_assert(M::LPG % kMedBatch == 0, "a batch must not straddle slot registers");
   const int64_t u_lo = a.unique_offsets[a.g_lo], u_hi = a.unique_offsets[a.g_hi];
   const int l = lane(), grp = l / M::LPG, sub = l % M::LPG;
   const bool ada = a.optim == FS_RW_ADAGRAD;
-  const int64_t wid = (int64_t)blockIdx.x * (kThreads / kWave) + threadIdx.x / kWave;
-  const int64_t nwaves = (int64_t)gridDim.x * (kThreads / kWave);
+  const int64_t wid = bid * (kThreads / kWave) + threadIdx.x / kWave;
+  const int64_t nwaves = nblk * (kThreads / kWave);
   for (int64_t ub = u_lo + wid * kWave; ub < u_hi; ub += nwaves * kWave) {
     const int64_t uu = ub + l;
     const bool in = uu < u_hi;
@@ -499,12 +499,12 @@ __device__ __forceinline__ void long_chunk(const RUArgs& a, int64_t o_lo, int64_
 
 // Chunks in grid-stride order, one per wave at a time.
 template <int D, typename WT>
-__global__ void __launch_bounds__(kThreads) k_long(RUArgs a) {
+__device__ __forceinline__ void long_rows(const RUArgs& a, int64_t bid, int64_t nblk) {
   const int64_t o_lo = a.seg_offsets[a.unique_offsets[a.g_lo]];
   const int64_t o_hi = a.seg_offsets[a.unique_offsets[a.g_hi]];
-  const int64_t nwaves = (int64_t)gridDim.x * (kThreads / kWave);
-  for (int64_t c = (int64_t)blockIdx.x * (kThreads / kWave) + threadIdx.x / kWave;
-       o_lo + c * a.chunk < o_hi; c += nwaves)
+  const int64_t nwaves = nblk * (kThreads / kWave);
+  for (int64_t c = bid * (kThreads / kWave) + threadIdx.x / kWave; o_lo + c * a.chunk < o_hi;
+       c += nwaves)
     long_chunk<D, WT>(a, o_lo, o_hi, c);
 }
 
@@ -518,14 +518,14 @@ struct FixShape {
   static constexpr int E = D >= 1024 ? 1 : (D >= 512 ? 2 : 4);
 };
 
+// part: LDS of kThreads / kWave rows of D doubles (the waves' sums)
 template <int D, typename WT>
-__global__ void __launch_bounds__(kThreads) k_fix(RUArgs a) {
+__device__ __forceinline__ void fix_rows(const RUArgs& a, int64_t bid, double* part) {
   using M = Map<D>;
   constexpr int E = FixShape<D>::E;
-  __shared__ double part[kThreads / kWave][D];
   const int64_t o_lo = a.seg_offsets[a.unique_offsets[a.g_lo]];
   const int64_t o_hi = a.seg_offsets[a.unique_offsets[a.g_hi]];
-  const int64_t c = blockIdx.x;
+  const int64_t c = bid;
   const int64_t cb = o_lo + c * a.chunk;
   if (cb >= o_hi) return;
   const int64_t ce = min(cb + a.chunk, o_hi);
@@ -569,7 +569,7 @@ __global__ void __launch_bounds__(kThreads) k_fix(RUArgs a) {
 #pragma unroll
     for (int v = 0; v < M::NV; ++v)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) part[w][M::col(sub, v) + q] = acc[4 * v + q];
+      for (int q = 0; q < 4; ++q) part[w * D + M::col(sub, v) + q] = acc[4 * v + q];
   }
   __syncthreads();
   if (w == 0) {
@@ -579,45 +579,178 @@ __global__ void __launch_bounds__(kThreads) k_fix(RUArgs a) {
 #pragma unroll
       for (int v = 0; v < M::NV; ++v)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) acc[4 * v + q] += part[ww][M::col(sub, v) + q];
+        for (int q = 0; q < 4; ++q) acc[4 * v + q] += part[ww * D + M::col(sub, v) + q];
     update_row<D, WT>(a, u, sub, acc, grp == 0);
   }
 }
 
-template <int D, typename WT>
-int launch_all(const RUArgs& a, hipStream_t stream) {
-  int64_t sb = cdiv(a.n_cap, kThreads);  // 64 rows per wave, 4 waves per block
-  if (sb > kShortBlocks) sb = kShortBlocks;
-  if (sb < 1) sb = 1;
-  hipLaunchKernelGGL((k_short<D, WT>), dim3((unsigned)sb), dim3(kThreads), 0, stream, a);
-  FS_LAUNCH_CHECK();
-  // medium rows: a unit of 64 rows per wave, about two units per wave
-  int64_t mb = cdiv(a.n_cap, 2 * kWave * (kThreads / kWave));
-  if (mb > kShortBlocks) mb = kShortBlocks;
-  if (mb < 1) mb = 1;
-  hipLaunchKernelGGL((k_medium<D, WT>), dim3((unsigned)mb), dim3(kThreads), 0, stream, a);
-  FS_LAUNCH_CHECK();
-  const int64_t chunks = cdiv(a.n_cap, a.chunk);
-  if (chunks > 0) {
-    int64_t lb = cdiv(chunks, kThreads / kWave);
-    hipLaunchKernelGGL((k_long<D, WT>), dim3((unsigned)lb), dim3(kThreads), 0, stream, a);
-    FS_LAUNCH_CHECK();
-    hipLaunchKernelGGL((k_fix<D, WT>), dim3((unsigned)chunks), dim3(kThreads), 0, stream, a);
-    FS_LAUNCH_CHECK();
+// ---------------------------------------------------------------- launches
+// One launch per kernel kind for every table of the call: two or more tables
+// of at most kSetMaxDim columns share one launch (workgroup ranges per table,
+// each workgroup running its table's row shape), wider tables get launches
+// of their own (their shapes need more registers, which a shared kernel
+// would impose on every table), and so does a narrow table alone (the shared
+// kernel's registers cost one wave per SIMD on the short rows: workload 5
+// ran 2% slower through it). Multi-table calls thus make four launches
+// instead of four per table (workload 4's update: 0.40 -> 0.26 ms). Each table's fp64 partial sums have their own region of
+// the workspace, so the tables' long rows can run side by side.
+enum Kind { kShortRows = 0, kMediumRows = 1, kLongRows = 2, kFixRows = 3 };
+constexpr int kSetMaxDim = 256;
+
+template <int K, int D, typename WT>
+__device__ __forceinline__ void run_kind(const RUArgs& a, int64_t bid, int64_t nblk,
+                                         double* part) {
+  if constexpr (K == kShortRows) short_rows<D, WT>(a, bid, nblk);
+  else if constexpr (K == kMediumRows) medium_rows<D, WT>(a, bid, nblk);
+  else if constexpr (K == kLongRows) long_rows<D, WT>(a, bid, nblk);
+  else fix_rows<D, WT>(a, bid, part);
+}
+
+// the tables of one shared launch; table k owns workgroups [first[k], first[k+1])
+struct RUSet {
+  RUArgs a[FS_MAX_TABLES];
+  int32_t first[FS_MAX_TABLES + 1];
+  int32_t shape[FS_MAX_TABLES];  // 2 * log2(D / 64) + (bf16 ? 1 : 0), D <= kSetMaxDim
+  int32_t n;
+};
+
+template <int K>
+__device__ __forceinline__ void set_body(const RUSet& s, double* part) {
+  int k = 0;
+  while (k + 1 < s.n && (int32_t)blockIdx.x >= s.first[k + 1]) ++k;
+  const int64_t bid = (int64_t)blockIdx.x - s.first[k], nblk = s.first[k + 1] - s.first[k];
+  switch (s.shape[k]) {
+    case 0: run_kind<K, 64, float>(s.a[k], bid, nblk, part); break;
+    case 1: run_kind<K, 64, uint16_t>(s.a[k], bid, nblk, part); break;
+    case 2: run_kind<K, 128, float>(s.a[k], bid, nblk, part); break;
+    case 3: run_kind<K, 128, uint16_t>(s.a[k], bid, nblk, part); break;
+    case 4: run_kind<K, 256, float>(s.a[k], bid, nblk, part); break;
+    case 5: run_kind<K, 256, uint16_t>(s.a[k], bid, nblk, part); break;
   }
+}
+
+// the shared launches, one kernel per kind
+__global__ void __launch_bounds__(kThreads) k_short_set(RUSet s) {
+  set_body<kShortRows>(s, nullptr);
+}
+__global__ void __launch_bounds__(kThreads) k_medium_set(RUSet s) {
+  set_body<kMediumRows>(s, nullptr);
+}
+__global__ void __launch_bounds__(kThreads) k_long_set(RUSet s) { set_body<kLongRows>(s, nullptr); }
+__global__ void __launch_bounds__(kThreads) k_fix_set(RUSet s) {
+  __shared__ double part[(kThreads / kWave) * kSetMaxDim];
+  set_body<kFixRows>(s, part);
+}
+
+// one table's own launches (a table alone in its width class, or a wide one):
+// each kernel holds one row shape, so its register count is that shape's
+template <int D, typename WT>
+__global__ void __launch_bounds__(kThreads) k_short(RUArgs a) {
+  short_rows<D, WT>(a, blockIdx.x, gridDim.x);
+}
+template <int D, typename WT>
+__global__ void __launch_bounds__(kThreads) k_medium(RUArgs a) {
+  medium_rows<D, WT>(a, blockIdx.x, gridDim.x);
+}
+template <int D, typename WT>
+__global__ void __launch_bounds__(kThreads) k_long(RUArgs a) {
+  long_rows<D, WT>(a, blockIdx.x, gridDim.x);
+}
+template <int D, typename WT>
+__global__ void __launch_bounds__(kThreads) k_fix(RUArgs a) {
+  __shared__ double part[(kThreads / kWave) * D];
+  fix_rows<D, WT>(a, blockIdx.x, part);
+}
+
+// workgroups of each kind for one table with n_cap occurrences
+int64_t blocks_of(int K, int64_t n_cap, int64_t chunk) {
+  int64_t b;
+  if (K == kShortRows) b = cdiv(n_cap, kThreads);  // 64 rows per wave, 4 waves per block
+  else if (K == kMediumRows) b = cdiv(n_cap, 2 * kWave * (kThreads / kWave));  // ~2 units per wave
+  else if (K == kLongRows) return cdiv(cdiv(n_cap, chunk), kThreads / kWave);
+  else return cdiv(n_cap, chunk);
+  return b > kShortBlocks ? kShortBlocks : (b < 1 ? 1 : b);
+}
+
+template <int K, int D, typename WT>
+int launch_one(const RUArgs& a, hipStream_t stream) {
+  const int64_t b = blocks_of(K, a.n_cap, a.chunk);
+  if (b <= 0) return FS_OK;
+  const dim3 g((unsigned)b), tb(kThreads);
+  if constexpr (K == kShortRows) hipLaunchKernelGGL((k_short<D, WT>), g, tb, 0, stream, a);
+  else if constexpr (K == kMediumRows) hipLaunchKernelGGL((k_medium<D, WT>), g, tb, 0, stream, a);
+  else if constexpr (K == kLongRows) hipLaunchKernelGGL((k_long<D, WT>), g, tb, 0, stream, a);
+  else hipLaunchKernelGGL((k_fix<D, WT>), g, tb, 0, stream, a);
+  FS_LAUNCH_CHECK();
   return FS_OK;
 }
 
-template <typename WT>
-int dispatch_dim(int dim, const RUArgs& a, hipStream_t stream) {
+template <int K, typename WT>
+int launch_dim(int dim, const RUArgs& a, hipStream_t stream) {
   switch (dim) {
-    case 64: return launch_all<64, WT>(a, stream);
-    case 128: return launch_all<128, WT>(a, stream);
-    case 256: return launch_all<256, WT>(a, stream);
-    case 512: return launch_all<512, WT>(a, stream);
-    case 1024: return launch_all<1024, WT>(a, stream);
+    case 64: return launch_one<K, 64, WT>(a, stream);
+    case 128: return launch_one<K, 128, WT>(a, stream);
+    case 256: return launch_one<K, 256, WT>(a, stream);
+    case 512: return launch_one<K, 512, WT>(a, stream);
+    case 1024: return launch_one<K, 1024, WT>(a, stream);
   }
   return FS_ERR_UNSUPPORTED;
+}
+
+template <int K>
+int launch_table(int dim, bool bf16, const RUArgs& a, hipStream_t stream) {
+  return bf16 ? launch_dim<K, uint16_t>(dim, a, stream) : launch_dim<K, float>(dim, a, stream);
+}
+
+int shape_of(int dim, bool bf16) {
+  const int l = dim == 64 ? 0 : (dim == 128 ? 1 : 2);
+  return 2 * l + (bf16 ? 1 : 0);
+}
+
+// every kind in order (short, medium and long rows, then the fix-up of the
+// long rows' partial sums), each kind one launch for the narrow tables (a
+// table's own launch when it is the only narrow one) and one per wide table
+int launch_tables(const RUArgs* args, const int* dims, const bool* bf16, int T,
+                  hipStream_t stream) {
+  int narrow = 0;
+  for (int t = 0; t < T; ++t) narrow += dims[t] <= kSetMaxDim;
+  for (int K = 0; K < 4; ++K) {
+    RUSet set;
+    set.n = 0;
+    int64_t total = 0;
+    for (int t = 0; t < T; ++t) {
+      if (dims[t] > kSetMaxDim || narrow < 2) continue;
+      const int64_t b = blocks_of(K, args[t].n_cap, args[t].chunk);
+      set.a[set.n] = args[t];
+      set.shape[set.n] = shape_of(dims[t], bf16[t]);
+      set.first[set.n] = (int32_t)total;
+      total += b > 0 ? b : 0;
+      ++set.n;
+    }
+    if (set.n > 0 && total > 0) {
+      set.first[set.n] = (int32_t)total;
+      const dim3 g((unsigned)total), tb(kThreads);
+      switch (K) {
+        case kShortRows: hipLaunchKernelGGL(k_short_set, g, tb, 0, stream, set); break;
+        case kMediumRows: hipLaunchKernelGGL(k_medium_set, g, tb, 0, stream, set); break;
+        case kLongRows: hipLaunchKernelGGL(k_long_set, g, tb, 0, stream, set); break;
+        default: hipLaunchKernelGGL(k_fix_set, g, tb, 0, stream, set);
+      }
+      FS_LAUNCH_CHECK();
+    }
+    for (int t = 0; t < T; ++t) {
+      if (dims[t] <= kSetMaxDim && narrow >= 2) continue;
+      int rc = FS_OK;
+      switch (K) {
+        case kShortRows: rc = launch_table<kShortRows>(dims[t], bf16[t], args[t], stream); break;
+        case kMediumRows: rc = launch_table<kMediumRows>(dims[t], bf16[t], args[t], stream); break;
+        case kLongRows: rc = launch_table<kLongRows>(dims[t], bf16[t], args[t], stream); break;
+        default: rc = launch_table<kFixRows>(dims[t], bf16[t], args[t], stream);
+      }
+      if (rc) return rc;
+    }
+  }
+  return FS_OK;
 }
 
 bool dim_ok(int d) { return d == 64 || d == 128 || d == 256 || d == 512 || d == 1024; }
@@ -641,10 +774,16 @@ static int64_t max_chunks(int64_t n) {
   return c256 > m ? c256 : m;
 }
 
-extern "C" size_t fs_grad_reduce_update_workspace_size(int64_t n_tok, int32_t max_dim) {
-  Carve c(nullptr);
+// doubles of one table's region of partial sums
+static size_t partial_doubles(int64_t n_tok, int32_t max_dim) {
   const int64_t n = n_tok > 0 ? n_tok : 1;
-  c.take<double>((size_t)(max_chunks(n) * 2) * (size_t)max_dim);
+  return (size_t)(max_chunks(n) * 2) * (size_t)(max_dim > 0 ? max_dim : 1);
+}
+
+extern "C" size_t fs_grad_reduce_update_workspace_size(int64_t n_tok, int32_t T,
+                                                      int32_t max_dim) {
+  Carve c(nullptr);
+  c.take<double>(partial_doubles(n_tok, max_dim) * (size_t)(T > 0 ? T : 1));
   return c.used + 256;
 }
 
@@ -677,7 +816,7 @@ int ru_check(const fs_table* tables, int32_t T, int32_t W, const float* const* g
     base += tb.rows;
   }
   if (base > (int64_t)UINT32_MAX) return FS_ERR_UNSUPPORTED;
-  if (ws_bytes < fs_grad_reduce_update_workspace_size(n_tok, max_dim)) return too_small;
+  if (ws_bytes < fs_grad_reduce_update_workspace_size(n_tok, T, max_dim)) return too_small;
   return FS_OK;
 }
 
@@ -686,10 +825,16 @@ int ru_launch(const fs_table* tables, int32_t T, int32_t W, const float* const* 
               const int32_t* seg_offsets, const int32_t* occ_bm, const int32_t* occ_uid,
               const uint8_t* cls, int32_t which, int32_t optim, float lr, float eps,
               float* const* reduced_out, void* ws, hipStream_t stream) {
+  RUArgs args[FS_MAX_TABLES];
+  int dims[FS_MAX_TABLES];
+  bool bf16[FS_MAX_TABLES];
+  int max_dim = 0;
+  for (int t = 0; t < T; ++t) max_dim = tables[t].dim > max_dim ? tables[t].dim : max_dim;
+  const size_t region = partial_doubles(n_tok, max_dim);
   int64_t base = 0;
   for (int t = 0; t < T; ++t) {
     const fs_table& tb = tables[t];
-    RUArgs a;
+    RUArgs& a = args[t];
     a.weights = tb.weights;
     a.state = tb.state;
     a.stride = table_stride(tb);
@@ -702,7 +847,7 @@ int ru_launch(const fs_table* tables, int32_t T, int32_t W, const float* const* 
     a.occ_bm = occ_bm;
     a.occ_uid = occ_uid;
     a.cls = cls;
-    a.partials = (double*)ws;
+    a.partials = (double*)ws + region * (size_t)t;  // each table its own region
     a.chunk = chunk_for(n_tok > 0 ? n_tok : 1);
     a.row_base = base;
     a.n_cap = n_tok;
@@ -713,12 +858,11 @@ int ru_launch(const fs_table* tables, int32_t T, int32_t W, const float* const* 
     a.lr = lr;
     a.eps = eps;
     base += tb.rows;
-    if (n_tok == 0) continue;
-    const int rc = tb.dtype == FS_F32 ? dispatch_dim<float>(tb.dim, a, stream)
-                                      : dispatch_dim<uint16_t>(tb.dim, a, stream);
-    if (rc) return rc;
+    dims[t] = tb.dim;
+    bf16[t] = tb.dtype == FS_BF16;
   }
-  return FS_OK;
+  if (n_tok == 0) return FS_OK;
+  return launch_tables(args, dims, bf16, T, stream);
 }
 
 // The allocation-free variant's scratch: one array per GPU the library runs

@@ -72,7 +72,7 @@ _c_kt = _sig("fs_keyed_transpose", C.c_int, _P, _i64, _i32, _P, _i32, _i32, _P, 
 _c_kt_ws = _sig("fs_keyed_transpose_workspace_size", _sz, _i32, _i32)
 _c_reduce = _sig("fs_grad_reduce_update", C.c_int, _TP, _i32, _i32, C.POINTER(_P), _i64, _P, _P,
                  _P, _P, _P, _P, _i32, _i32, _f, _f, C.POINTER(_P), _P, _sz, _P)
-_c_reduce_ws = _sig("fs_grad_reduce_update_workspace_size", _sz, _i64, _i32)
+_c_reduce_ws = _sig("fs_grad_reduce_update_workspace_size", _sz, _i64, _i32, _i32)
 _c_reduce_noalloc = _sig("fs_grad_reduce_update_noalloc", C.c_int, _TP, _i32, _i32,
                          C.POINTER(_P), _i64, _P, _P, _P, _P, _P, _P, _i32, _i32, _f, _f,
                          C.POINTER(_P), _P)
@@ -396,8 +396,8 @@ def fs_keyed_transpose(values, lengths, out=None, out_offsets=None, err=None, ws
     return out, out_offsets
 
 
-def reduce_workspace_size(n_tok, max_dim):
-    return int(_c_reduce_ws(n_tok, max_dim))
+def reduce_workspace_size(n_tok, max_dim, T=1):
+    return int(_c_reduce_ws(n_tok, T, max_dim))
 
 
 def fs_grad_reduce_update(weights, states, W, grads, n_tok, uq, optim, lr, eps=0.0,
@@ -405,7 +405,7 @@ def fs_grad_reduce_update(weights, states, W, grads, n_tok, uq, optim, lr, eps=0
     T = len(weights)
     tabs = make_tables(weights, states)
     max_dim = max(w.shape[1] for w in weights)
-    ws = _ws(reduce_workspace_size(n_tok, max_dim), ws)
+    ws = _ws(reduce_workspace_size(n_tok, max_dim, T), ws)
     red = _ptr_array(reduced_out) if reduced_out is not None else None
     _check("fs_grad_reduce_update",
            _c_reduce(tabs, T, W, _ptr_array(grads), n_tok, _ptr(uq["unique"]),

@@ -197,7 +197,7 @@ class SparseStep:
                                   device=d)
         self.ws_uq = torch.empty(lib.unique_workspace_size(ncap, T, W), dtype=torch.uint8,
                                  device=d)
-        rws = lib.reduce_workspace_size(cap, max(self.dims))
+        rws = lib.reduce_workspace_size(cap, max(self.dims), T)
         self.ws_red = [torch.empty(rws, dtype=torch.uint8, device=d) for _ in range(2)]
         self.lookahead = lookahead
         self.states_buf = [self._alloc_iter() for _ in range(lookahead + 1)]

@@ -39,7 +39,8 @@ CALIB_BYTES = 1 << 30
 
 # kernels of each stage and the sources they are built from
 STAGES = {
-    "update_all": (("k_short", "k_medium", "k_long", "k_fix"), ("reduce_update.hip", "common.hpp")),
+    "update_all": (("k_short", "k_short_set", "k_medium", "k_medium_set", "k_long",
+                    "k_long_set", "k_fix", "k_fix_set"), ("reduce_update.hip", "common.hpp")),
     "lookup_all": (("k_lookup",), ("gather.hip", "common.hpp")),
 }
 
@@ -113,8 +114,11 @@ def summarize(fetch_csv: str, write_csv: str, config: int, out_path: str | None)
             if v["short"] in names and v["fetch_bytes"] is not None and v["write_bytes"] is not None:
                 tot_f += v["fetch_bytes"] * v["dispatches"]
                 tot_w += v["write_bytes"] * v["dispatches"]
-                if v["short"] == names[0]:
-                    launches = v["dispatches"]
+                # a launch of the stage starts with its first kernel (a
+                # table's own or the shared one; several tables' own
+                # launches count once per table)
+                if v["short"] in names[:2]:
+                    launches = max(launches or 0, v["dispatches"])
         if launches:
             stages[stage] = {"fetch_bytes_per_launch": tot_f / launches,
                              "write_bytes_per_launch": tot_w / launches,

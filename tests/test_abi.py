@@ -55,6 +55,9 @@ def test_workspace_queries_are_host_only_and_monotone(L):
     assert L.unique_workspace_size(1 << 20, 1, 512, prev_cap=1 << 24) == \
         L.unique_workspace_size(1 << 20, 1, 512, prev_cap=1 << 20)
     assert L.reduce_workspace_size(1 << 20, 256) > L.reduce_workspace_size(1 << 20, 64)
+    # a region of partial sums per table: the tables' rows run side by side
+    one = L.reduce_workspace_size(1 << 20, 128) - 256
+    assert L.reduce_workspace_size(1 << 20, 128, T=4) - 256 == 4 * one
 
 
 def test_workspace_sized_for_a_capacity_serves_every_smaller_call(L):
