@@ -1,11 +1,12 @@
 """Benchmark of the prioritized jagged sparse step on one MI355X.
 
 A step is one pass of the whole hot path over one batch. Default schedule
-(--lookahead 2): on the caller's stream the update of every unique row of
+(--lookahead 3): on the caller's stream the update of every unique row of
 iteration i (segment-reduce + optimizer), then the lookup of every row of
-iteration i+1; beside them, on stream A, balance (FBS or VBS), indexed
-permute + shard bucketize and dedup + collision split of the batch after
-next. --schedule prioritized splits update and lookup by class as the pages'
+iteration i+1; beside them, on two index streams taken in turn, balance (FBS
+or VBS), indexed permute + shard bucketize and dedup + collision split of
+iteration i+3 (its balance and bucketize overlapping the dedup of i+2;
+--lookahead 2: one index stream, iteration i+2). --schedule prioritized splits update and lookup by class as the pages'
 Algorithm 2 does (collision rows updated, then looked up, on the caller's
 stream; exclusive rows of both iterations on two more streams).
 --lookahead 1 runs the index stages one iteration ahead instead, with the
@@ -79,9 +80,11 @@ def parse():
                     help="with --lookahead 1: exclusive-row lookup ahead of the update (split), "
                          "one lookup after it (joined), or chosen from the first steps' timing "
                          "(auto)")
-    ap.add_argument("--lookahead", type=int, choices=[1, 2], default=2,
+    ap.add_argument("--lookahead", type=int, choices=[1, 2, 3], default=3,
                     help="iterations the index stages run ahead of the lookup (2: beside the "
-                         "update and the lookup of the iteration before)")
+                         "update and the lookup of the iteration before; 3: on two index "
+                         "streams, so that one iteration's balance and bucketize overlap the "
+                         "dedup of the one before)")
     ap.add_argument("--layout", choices=["dense", "rowstate", "rowstate256"], default="dense",
                     help="tables as dense [rows][dim] with a separate state array, or each "
                          "row's Adagrad state in the row's own padding")
@@ -173,20 +176,21 @@ def measure(ctx, steps, warmup, args, full):
     from jagged_embedding_sparse_amd.step import SparseStep, StageTimer
     w, NB, n_tok, grads_dev = ctx.w, len(ctx.dev_batches), ctx.n_tok, ctx.grads_dev
     dev_batches = ctx.dev_batches
-    ahead = args.lookahead == 2 and not args.sync
+    L = 1 if args.sync else args.lookahead
+    ahead = L >= 2
     sched = args.schedule if ahead else "joined"
     step = SparseStep(w, ctx.weights, ctx.states, ctx.cap, lookup=args.lookup,
-                      lookahead=2 if ahead else 1, autotune={} if args.autotune else None,
-                      schedule=sched)
-    step.prologue(dev_batches[0], batch_after=dev_batches[1 % NB] if ahead else None)
+                      lookahead=L, autotune={} if args.autotune else None, schedule=sched)
+    step.prologue(dev_batches[0],
+                  batch_after=[dev_batches[j % NB] for j in range(1, L)] if ahead else None)
     if args.sync:
         def run_step(batch_next, grads, k_next):
             return step.step_sync(batch_next, grads)
     else:
         def run_step(batch_next, grads, k_next):
-            # with lookahead 2 the step also indexes the batch after next
+            # with lookahead L >= 2 the step also indexes batch k_next + L - 1
             return step.step(batch_next, grads,
-                             batch_after=dev_batches[(k_next + 1) % NB] if ahead else None)
+                             batch_after=dev_batches[(k_next + L - 1) % NB] if ahead else None)
     k = 0
     for _ in range(warmup):
         k += 1
@@ -203,7 +207,7 @@ def measure(ctx, steps, warmup, args, full):
     # recycled event resources that the timed pool's records stay cheap
     # (without it, 1.5 ms of host time per step on the smallest workload).
     n_brk = min(steps, 10) if full else 0
-    streams = [s for s in (step.sA, step.sB, step.sC) if s is not None]
+    streams = [s for s in step.s_idx + [step.sB, step.sC] if s is not None]
     warm = StageTimer(capacity=24 * (steps + n_brk), streams=streams)
     del warm
     upd_names = ("update_all", "update_co", "update_ex")
@@ -232,8 +236,9 @@ def measure(ctx, steps, warmup, args, full):
     if args.sync:
         schedule = "sync"
     elif ahead:
-        schedule = ("index two ahead, prioritized (collision rows first)" if sched == "prioritized"
-                    else "index two ahead, joined lookup")
+        far = {2: "index two ahead", 3: "index three ahead on two index streams"}[L]
+        schedule = (f"{far}, prioritized (collision rows first)" if sched == "prioritized"
+                    else f"{far}, joined lookup")
     else:
         schedule = "joined" if step.joined else "split"
     ms_total = ev0.elapsed_time(ev1)

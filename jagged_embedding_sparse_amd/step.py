@@ -40,6 +40,15 @@ instead of only the update. Three iteration states are alive at once (i being
 updated, i+1 looked up, i+2 indexed); the result is again the synchronous
 loop's.
 
+With `lookahead=3` the index stages run three iterations ahead on two index
+streams taken in turn, so that the balance and bucketize of i+3 overlap the
+dedup of i+2: only the dedup (its collision split reads the previous
+iteration's unique rows, and the dedup workspace is shared) waits for the one
+before it. Where the index stages are a chain of latency-bound launches
+longer than the update and the lookup, a step then costs about one dedup
+instead of a whole index chain. Each index stream has its own balance and
+bucketize workspace; four iteration states are alive at once.
+
 With `schedule="prioritized"` (index stages two ahead) the update is split
 by class as Algorithm 2 splits it, so that the next lookup waits only for the
 rows it shares with the update:
@@ -66,6 +75,7 @@ state slot. Every stream keeps the default priority.
 
 from __future__ import annotations
 
+from collections import deque
 from dataclasses import dataclass, field
 
 import torch
@@ -152,6 +162,9 @@ class IterState:
     uq: dict = field(default_factory=dict)
     cls_next: torch.Tensor = None  # class of this iteration's rows vs the next one
     out: list = field(default_factory=list)  # lookup output per table
+    idx_x: int = 0  # index stream that ran this iteration's index stages
+    ev_done: torch.cuda.Event = None  # index stages done (after the dedup)
+    ev_bal: torch.cuda.Event = None  # balance (and AutoTune's share update) done
 
 
 _LOOKUP_MODES = ("split", "joined", "auto")
@@ -168,14 +181,14 @@ class SparseStep:
                  lookahead=1, autotune=None, schedule="joined"):
         if lookup not in _LOOKUP_MODES:
             raise ValueError(f"lookup must be one of {_LOOKUP_MODES}, not {lookup!r}")
-        if lookahead not in (1, 2):
-            raise ValueError(f"lookahead must be 1 or 2, not {lookahead!r}")
+        if lookahead not in (1, 2, 3):
+            raise ValueError(f"lookahead must be 1, 2 or 3, not {lookahead!r}")
         if schedule not in _SCHEDULES:
             raise ValueError(f"schedule must be one of {_SCHEDULES}, not {schedule!r}")
-        if schedule == "prioritized" and lookahead != 2:
-            raise ValueError("the prioritized schedule needs the index stages two ahead "
-                             "(lookahead=2): the update of i starts from the classes of i "
-                             "against i+1")
+        if schedule == "prioritized" and lookahead < 2:
+            raise ValueError("the prioritized schedule needs the index stages at least two "
+                             "ahead (lookahead=2 or 3): the update of i starts from the classes "
+                             "of i against i+1")
         self.schedule = schedule
         if autotune is not None and workload.balancer != "vbs":
             raise ValueError("autotune needs the VBS balancer")
@@ -192,9 +205,12 @@ class SparseStep:
         N = workload.batch
         ncap = T * cap
         self.err = torch.zeros(1, dtype=torch.int32, device=d)
-        self.ws_bal = torch.empty(lib.balance_workspace_size(N, W), dtype=torch.uint8, device=d)
-        self.ws_bkt = torch.empty(lib.bucketize_workspace_size(cap, N, T, W), dtype=torch.uint8,
-                                  device=d)
+        # one balance and one bucketize workspace per index stream
+        n_idx = 2 if lookahead == 3 else 1
+        self.ws_bal = [torch.empty(lib.balance_workspace_size(N, W), dtype=torch.uint8, device=d)
+                       for _ in range(n_idx)]
+        self.ws_bkt = [torch.empty(lib.bucketize_workspace_size(cap, N, T, W), dtype=torch.uint8,
+                                   device=d) for _ in range(n_idx)]
         self.ws_uq = torch.empty(lib.unique_workspace_size(ncap, T, W), dtype=torch.uint8,
                                  device=d)
         rws = lib.reduce_workspace_size(cap, max(self.dims), T)
@@ -205,18 +221,19 @@ class SparseStep:
             st.slot = i
         self._calls = {}  # prepared C calls by (stage, slots, ...)
         self.sA = torch.cuda.Stream(device=d)
+        self.s_idx = [self.sA] + [torch.cuda.Stream(device=d) for _ in range(n_idx - 1)]
         self.sB = torch.cuda.Stream(device=d)
         # exclusive-row lookup of the prioritized schedule
         self.sC = torch.cuda.Stream(device=d) if schedule == "prioritized" else None
         self.ev_b = torch.cuda.Event()
-        self.ev_idx = torch.cuda.Event()  # index stages of the iteration after i done
-        self._pre = False  # lookahead=2: the iteration after i already indexed
+        self._ahead = deque()  # iterations after i already indexed, oldest first
+        self._n_indexed = 0  # iterations whose index stages were issued
         self.cur = None  # IterState of iteration i (already looked up)
         self.slot = 0
         self.timer = None  # optional StageTimer
         self.lookup = lookup
-        # current choice (lookahead=2 always looks every row up after the update)
-        self.joined = lookup == "joined" or lookahead == 2
+        # current choice (lookahead >= 2 always looks every row up after the update)
+        self.joined = lookup == "joined" or lookahead >= 2
         self._calib = []  # (start, update end, index end) event triples
         self._calib_left = _CALIB_STEPS if (lookup == "auto" and lookahead == 1) else 0
         # VBS AutoTune: per-rank shares of the weight, moved after every
@@ -255,6 +272,8 @@ class SparseStep:
             cls=torch.empty(ncap, dtype=torch.uint8, device=d),
             counts=torch.empty(4, dtype=torch.int64, device=d))
         st.cls_next = torch.empty(ncap, dtype=torch.uint8, device=d)
+        st.ev_done = torch.cuda.Event()
+        st.ev_bal = torch.cuda.Event()
         st.out = [torch.empty((self.cap, D), dtype=w.dtype, device=d)
                   for D, w in zip(self.dims, self.weights)]
         return st
@@ -269,43 +288,61 @@ class SparseStep:
             c = self._calls[key] = make()
         return c
 
-    def _index_stages(self, batch, st, prev, stream):
-        """balance + bucketize + split of `batch` (device dict) into st."""
+    def _index_stream(self):
+        """(number, stream) of the index stream for the next iteration to index."""
+        x = self._n_indexed % len(self.s_idx)
+        return x, self.s_idx[x]
+
+    def _index_stages(self, batch, st, prev, stream, x=0):
+        """balance + bucketize + split of `batch` (device dict) into st, on
+        index stream `x` (`stream`). The split waits for the previous
+        iteration's index stages when another stream ran them (it reads that
+        iteration's unique rows and shares the dedup workspace), and with
+        AutoTune the balance waits for the previous share update."""
         W, T = self.W, self.T
+        other = prev is not None and prev.idx_x != x
+        st.idx_x = x
+        self._n_indexed += 1
         ids, so, uih = batch["ids"], batch["sample_offsets"], batch["uih_len"]
         n_tok = int(ids.shape[1])
         st.n_tok = n_tok
         sh = stream.cuda_stream
         at = self.autotune
         if at is None:
-            pb = self._prep(("bal", st.slot), lambda: lib.prepare_balance(
+            pb = self._prep(("bal", st.slot, x), lambda: lib.prepare_balance(
                 self.w.balancer, W, self.w.alpha, st.perm, st.rank_offsets, st.rank_weight,
-                self.err, self.ws_bal))
+                self.err, self.ws_bal[x]))
         else:
-            pb = self._prep(("bal", st.slot), lambda: lib.prepare_balance_shares(
+            pb = self._prep(("bal", st.slot, x), lambda: lib.prepare_balance_shares(
                 W, self.w.alpha, self.shares, st.perm, st.rank_offsets, st.rank_weight, self.err,
-                self.ws_bal))
+                self.ws_bal[x]))
             pc = self._prep(("cost", st.slot), lambda: lib.prepare_rank_cost(
                 st.perm, st.rank_offsets, at["coef"], self.rank_cost))
             pa = self._prep(("tune",), lambda: lib.prepare_autotune(
                 self.rank_cost, self.shares, at["step"], at["tol"], self.err))
-        pk = self._prep(("bkt", st.slot), lambda: lib.prepare_bucketize(
-            self.rows, st.perm, st.rank_offsets, W, st.bucket, self.err, self.ws_bkt))
+        pk = self._prep(("bkt", st.slot, x), lambda: lib.prepare_bucketize(
+            self.rows, st.perm, st.rank_offsets, W, st.bucket, self.err, self.ws_bkt[x]))
         pu = self._prep(("uq", st.slot, prev.slot if prev is not None else -1),
                         lambda: lib.prepare_unique(
                             st.bucket, self.rows, W, st.uq,
                             prev.uq if prev is not None else None,
                             prev.cls_next if prev is not None else None, self.ws_uq))
+        if at is not None and other:  # the shares the previous balance left
+            stream.wait_event(prev.ev_bal)
         with self._t("balance", stream):
             pb(uih=lib._ptr(uih), n=uih.numel(), stream=sh)
         if at is not None:  # the shares for the next balance
             with self._t("autotune", stream):
                 pc(uih=lib._ptr(uih), n=uih.numel(), stream=sh)
                 pa(stream=sh)
+            st.ev_bal.record(stream)
         with self._t("bucketize", stream):
             pk(ids=lib._ptr(ids), n_tok=n_tok, so=lib._ptr(so), n=so.numel() - 1, stream=sh)
+        if other:
+            stream.wait_event(prev.ev_done)
         with self._t("unique_split", stream):
             pu(n_cap=T * n_tok, prev_cap=T * prev.n_tok if prev is not None else 0, stream=sh)
+        st.ev_done.record(stream)
 
     def _lookup(self, st, which, stream):
         pl = self._prep(("lk", st.slot, which), lambda: lib.prepare_lookup(
@@ -328,19 +365,27 @@ class SparseStep:
         return len(self.states_buf)
 
     def prologue(self, batch, batch_after=None):
-        """Index stages + full lookup of the first iteration; with
-        lookahead=2 and `batch_after`, also the index stages of the second."""
+        """Index stages + full lookup of the first iteration; with lookahead
+        >= 2, also the index stages of the next lookahead - 1 batches
+        (`batch_after`: one batch, or a list of them)."""
         st = self.states_buf[self.slot]
-        self.sA.wait_stream(torch.cuda.current_stream())
-        self._index_stages(batch, st, None, self.sA)
-        self._lookup(st, lib.FS_ALL, self.sA)
+        cs = torch.cuda.current_stream()
+        for s_ in self.s_idx:
+            s_.wait_stream(cs)
+        x, s0 = self._index_stream()
+        self._index_stages(batch, st, None, s0, x)
+        self._lookup(st, lib.FS_ALL, s0)
         self.cur = st
-        self._pre = False
-        if self.lookahead == 2 and batch_after is not None:
-            nxt = self.states_buf[(self.slot + 1) % self._nslots()]
-            self._index_stages(batch_after, nxt, st, self.sA)
-            self.ev_idx.record(self.sA)
-            self._pre = True
+        self._ahead.clear()
+        if self.lookahead >= 2 and batch_after is not None:
+            ahead = batch_after if isinstance(batch_after, (list, tuple)) else [batch_after]
+            prev = st
+            for k, b in enumerate(ahead[:self.lookahead - 1]):
+                nxt = self.states_buf[(self.slot + 1 + k) % self._nslots()]
+                x, s_ = self._index_stream()
+                self._index_stages(b, nxt, prev, s_, x)
+                self._ahead.append(nxt)
+                prev = nxt
         return st
 
     def _decide(self):
@@ -357,10 +402,10 @@ class SparseStep:
 
     def step(self, batch_next, grads_cur, batch_after=None):
         """Prioritized step: update iteration i, look up iteration i+1 (and,
-        with lookahead=2, index `batch_after`, iteration i+2)."""
+        with lookahead L >= 2, index `batch_after`, iteration i+L)."""
         if self.schedule == "prioritized":
             return self._step_prioritized(batch_next, grads_cur, batch_after)
-        if self.lookahead == 2:
+        if self.lookahead >= 2:
             return self._step_ahead(batch_next, grads_cur, batch_after)
         self._decide()
         cur = self.cur
@@ -394,35 +439,54 @@ class SparseStep:
         self.slot = 1 - self.slot
         return nxt
 
-    def _step_ahead(self, batch_next, grads_cur, batch_after):
-        # The update and the lookup run on the caller's stream (its inputs are
-        # there, and so are the lookup results it reads next); stream A runs the
-        # index stages. Each stream wait costs the host ~15 us, so there are two.
+    def _next_states(self, batch_next, batch_after, cs):
+        """Index stream waits at the start of a step, and iteration i+1's
+        state (indexed now if it was not indexed ahead). Returns (nxt, the
+        index stream number and stream for batch_after or None)."""
         cur = self.cur
         n = self._nslots()
-        nxt = self.states_buf[(self.slot + 1) % n]
-        sA = self.sA
+        # the index streams about to work wait for everything enqueued so far
+        # on the caller's stream: the batches, and the update of i-1 and the
+        # lookups whose state slots the new index stages overwrite; enqueued
+        # before this step's update, so they overlap it
+        aft_s = None
+        if not self._ahead:  # iteration i+1 was not indexed ahead: index it now
+            nxt = self.states_buf[(self.slot + 1) % n]
+            x, s_ = self._index_stream()
+            s_.wait_stream(cs)
+            self._index_stages(batch_next, nxt, cur, s_, x)
+        else:
+            nxt = self._ahead.popleft()
+        if batch_after is not None:
+            x, s_ = self._index_stream()
+            s_.wait_stream(cs)
+            aft_s = (x, s_)
+        return nxt, aft_s
+
+    def _index_after(self, batch_after, nxt, aft_s):
+        if batch_after is None:
+            return
+        x, s_ = aft_s
+        prev = self._ahead[-1] if self._ahead else nxt
+        aft = self.states_buf[(self.slot + self.lookahead) % self._nslots()]
+        self._index_stages(batch_after, aft, prev, s_, x)
+        self._ahead.append(aft)
+
+    def _step_ahead(self, batch_next, grads_cur, batch_after):
+        # The update and the lookup run on the caller's stream (its inputs are
+        # there, and so are the lookup results it reads next); the index
+        # streams run the index stages. Each stream wait costs the host ~15 us.
+        cur = self.cur
         cs = torch.cuda.current_stream()
-        # stream A after everything enqueued so far on the caller's stream: the
-        # batches, and the update of i-1, whose state slot the index stages of
-        # i+2 overwrite; enqueued before this step's update, so they overlap it
-        sA.wait_stream(cs)
-        if not self._pre:  # iteration i+1 was not indexed ahead: index it now
-            self._index_stages(batch_next, nxt, cur, sA)
-            self.ev_idx.record(sA)
+        nxt, aft_s = self._next_states(batch_next, batch_after, cs)
         # the update of i needs nothing from the index stages of i+1 (they
         # only read iteration i's unique rows), so only the lookup waits
         self._run_update(cur, grads_cur, lib.FS_ALL, self.ws_red[1], cs)
-        cs.wait_event(self.ev_idx)
+        cs.wait_event(nxt.ev_done)
         self._lookup(nxt, lib.FS_ALL, cs)
-        self._pre = False
-        if batch_after is not None:
-            aft = self.states_buf[(self.slot + 2) % n]
-            self._index_stages(batch_after, aft, nxt, sA)
-            self.ev_idx.record(sA)
-            self._pre = True
+        self._index_after(batch_after, nxt, aft_s)
         self.cur = nxt
-        self.slot = (self.slot + 1) % n
+        self.slot = (self.slot + 1) % self._nslots()
         return nxt
 
     def _step_prioritized(self, batch_next, grads_cur, batch_after):
@@ -430,48 +494,38 @@ class SparseStep:
         # first and their lookup for i+1 follows on the caller's stream; the
         # exclusive rows of both iterations go beside it on streams B and C.
         cur = self.cur
-        n = self._nslots()
-        nxt = self.states_buf[(self.slot + 1) % n]
-        sA, sB, sC = self.sA, self.sB, self.sC
+        sB, sC = self.sB, self.sC
         cs = torch.cuda.current_stream()
-        # every stream after the work on the caller's stream: the batches and
+        nxt, aft_s = self._next_states(batch_next, batch_after, cs)
+        # streams B and C after the work on the caller's stream: the
         # gradients, and the previous step (joined into it), whose buffers
         # this one reuses
-        sA.wait_stream(cs)
-        if not self._pre:  # iteration i+1 was not indexed ahead: index it now
-            self._index_stages(batch_next, nxt, cur, sA)
-            self.ev_idx.record(sA)
         sB.wait_stream(cs)
         sC.wait_stream(cs)
         # the classes of i against i+1 (the update's) and of i+1 (the lookups')
         for s_ in (cs, sB, sC):
-            s_.wait_event(self.ev_idx)
+            s_.wait_event(nxt.ev_done)
         self._run_update(cur, grads_cur, lib.FS_COLLISION, self.ws_red[1], cs)
         self._lookup(nxt, lib.FS_COLLISION, cs)
         self._run_update(cur, grads_cur, lib.FS_EXCLUSIVE, self.ws_red[0], sB)
         self._lookup(nxt, lib.FS_EXCLUSIVE, sC)
-        self._pre = False
-        if batch_after is not None:
-            aft = self.states_buf[(self.slot + 2) % n]
-            self._index_stages(batch_after, aft, nxt, sA)
-            self.ev_idx.record(sA)
-            self._pre = True
+        self._index_after(batch_after, nxt, aft_s)
         cs.wait_stream(sB)
         cs.wait_stream(sC)
         self.cur = nxt
-        self.slot = (self.slot + 1) % n
+        self.slot = (self.slot + 1) % self._nslots()
         return nxt
 
     def step_sync(self, batch_next, grads_cur):
         """Reference schedule on one stream: update all of i, then look up all of i+1."""
-        if self._pre:
+        if self._ahead:
             raise RuntimeError("step_sync after a step that indexed its batch_after")
         cur = self.cur
         nxt = self.states_buf[(self.slot + 1) % self._nslots()]
         sA = self.sA
         sA.wait_stream(torch.cuda.current_stream())
         sA.wait_stream(self.sB)
-        self._index_stages(batch_next, nxt, cur, sA)
+        self._index_stages(batch_next, nxt, cur, sA, 0)
         self._run_update(cur, grads_cur, lib.FS_ALL, self.ws_red[0], sA)
         self._lookup(nxt, lib.FS_ALL, sA)
         self.cur = nxt
@@ -486,7 +540,6 @@ class SparseStep:
         self._run_update(cur, grads_last, lib.FS_ALL, self.ws_red[0], self.sA)
 
     def join(self):
-        torch.cuda.current_stream().wait_stream(self.sA)
-        torch.cuda.current_stream().wait_stream(self.sB)
-        if self.sC is not None:
-            torch.cuda.current_stream().wait_stream(self.sC)
+        cs = torch.cuda.current_stream()
+        for s_ in self.s_idx + [self.sB] + ([self.sC] if self.sC is not None else []):
+            cs.wait_stream(s_)

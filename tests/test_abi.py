@@ -238,7 +238,9 @@ def test_step_rejects_unknown_lookup_schedule():
     with pytest.raises(ValueError):
         SparseStep(None, [], [], 1, lookup="eager")
     with pytest.raises(ValueError):
-        SparseStep(None, [], [], 1, lookahead=3)
+        SparseStep(None, [], [], 1, lookahead=4)
+    with pytest.raises(ValueError):  # the prioritized schedule needs the index stages ahead
+        SparseStep(None, [], [], 1, lookahead=1, schedule="prioritized")
     from jagged_embedding_sparse_amd import synth
     with pytest.raises(ValueError):  # AutoTune moves VBS shares: no FBS
         SparseStep(synth.workload(1), [], [], 1, autotune={})

@@ -144,12 +144,13 @@ def run_parity(k, balancer=None, iters=None, seed=None, lookahead=1, autotune=No
     cap = max(b["n_tok"] for b in batches)
     kw = {} if schedule is None else dict(schedule=schedule)
     step = SparseStep(w, weights, states, cap, lookahead=lookahead, autotune=at, **kw)
-    ahead = lookahead == 2
+    ahead = lookahead >= 2
     exact = w.optim == "sgd" and all(t.dtype == "f32" for t in w.tables)
     worst, n_diff = 0.0, 0
     oracle_step(0)
     st = step.prologue(to_dev(batches[0]),
-                       batch_after=to_dev(batches[1]) if ahead and K > 1 else None)
+                       batch_after=[to_dev(batches[j]) for j in range(1, min(lookahead, K))]
+                       if ahead else None)
     step.join()
     torch.cuda.synchronize()
     _cmp_index(st, outs[0], None, None, w.world, len(w.tables), batches[0]["n_tok"])
@@ -160,7 +161,7 @@ def run_parity(k, balancer=None, iters=None, seed=None, lookahead=1, autotune=No
             "C", int(outs[i + 1]["counts"][1]))
         prev = st
         gdev = [torch.from_numpy(g).cuda() for g in grads.pop(i)]
-        after = to_dev(batches[i + 2]) if ahead and i + 2 < K else None
+        after = to_dev(batches[i + lookahead]) if ahead and i + lookahead < K else None
         st = step.step(to_dev(batches[i + 1]), gdev, batch_after=after)
         step.join()
         torch.cuda.synchronize()
@@ -227,6 +228,21 @@ def test_index_two_ahead_vs_oracle(k):
 
 @pytest.mark.timeout(600)
 @pytest.mark.parametrize("k", [1, 2, 3, 4])
+def test_index_three_ahead_vs_oracle(k):
+    """Index stages three ahead on two index streams (an iteration's balance
+    and bucketize beside the dedup of the one before)."""
+    run_parity(k, iters=6, lookahead=3)
+
+
+@pytest.mark.timeout(600)
+def test_index_three_ahead_autotune_vs_oracle():
+    """AutoTune's shares move between balances that run on the two index
+    streams in turn: each balance waits for the one before."""
+    run_parity(3, iters=6, lookahead=3, autotune=dict(step=(1, 4), tol=(0, 1)))
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("k", [1, 2, 3, 4])
 def test_prioritized_vs_oracle(k):
     """Algorithm 2's order: collision rows of i updated, then looked up for
     i+1; the exclusive rows of both iterations on their own streams."""
@@ -278,15 +294,16 @@ def test_prioritized_equals_synchronous(k):
     cap = max(b["n_tok"] for b in batches)
     runs = []
     grads = []
-    for mode in ("sync", "split", "joined", "auto", "ahead", "prioritized"):
+    for mode in ("sync", "split", "joined", "auto", "ahead", "prioritized", "ahead3",
+                 "prioritized3"):
         say("schedule", k, mode)
         weights, states = gpu_tables(w, 50 + k)
-        ahead = mode in ("ahead", "prioritized")
+        L = 3 if mode.endswith("3") else (2 if mode in ("ahead", "prioritized") else 1)
+        ahead = L >= 2
         step = SparseStep(w, weights, states, cap,
-                          lookup="split" if mode in ("sync", "ahead", "prioritized") else mode,
-                          lookahead=2 if ahead else 1,
-                          schedule="prioritized" if mode == "prioritized" else "joined")
-        st = step.prologue(dev_b[0], batch_after=dev_b[1] if ahead else None)
+                          lookup="split" if (mode == "sync" or ahead) else mode, lookahead=L,
+                          schedule="prioritized" if mode.startswith("prioritized") else "joined")
+        st = step.prologue(dev_b[0], batch_after=dev_b[1:L] if ahead else None)
         step.join()
         looks = [[o[:st.n_tok].clone() for o in st.out]]
         for i in range(K - 1):
@@ -296,7 +313,7 @@ def test_prioritized_equals_synchronous(k):
                     w, 50 + k, i, batches[i], host(st.perm), host(st.bucket["bal_offsets"]))])
                 st = step.step_sync(dev_b[i + 1], grads[i])
             else:
-                after = dev_b[i + 2] if ahead and i + 2 < K else None
+                after = dev_b[i + L] if ahead and i + L < K else None
                 st = step.step(dev_b[i + 1], grads[i], batch_after=after)
             step.join()
             looks.append([o[:st.n_tok].clone() for o in st.out])
