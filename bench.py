@@ -346,6 +346,8 @@ def measure(ctx, steps, warmup, args, full):
     return res
 
 
+# the update's kernels: short, medium and long rows and the long rows' fix-up
+# (k_*_set when several tables share a launch)
 KERNEL_OF = {
     "update_co": "k_short+k_medium+k_long+k_fix (fs_grad_reduce_update, collision rows)",
     "update_ex": "k_short+k_medium+k_long+k_fix (fs_grad_reduce_update, exclusive rows)",

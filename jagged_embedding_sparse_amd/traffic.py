@@ -144,9 +144,9 @@ INDEX_KERNELS = ("k_rank_part", "k_place", "k_vbs_cut", "k_lens", "k_bal", "k_ti
 
 
 def table(res: dict, steps: int, index_algorithmic: float | None) -> str:
-    """Per-kernel HBM bytes per step (dispatches / steps per step) and the
-    index kernels' total against their algorithmic bytes."""
-    lines = ["kernel                               dispatches   fetch MB/step  write MB/step"]
+    """Per-kernel HBM bytes per iteration (`steps` iterations in the run) and
+    the index kernels' total against their algorithmic bytes."""
+    lines = ["kernel                               dispatches   fetch MB/iter  write MB/iter"]
     idx = 0.0
     for name, v in sorted(res["kernels"].items(), key=lambda kv: kv[1]["short"]):
         per = v["dispatches"] / steps
@@ -167,7 +167,7 @@ def table(res: dict, steps: int, index_algorithmic: float | None) -> str:
         extra = (f" against {index_algorithmic / 1e9:.3f} GB algorithmic "
                  f"({idx / index_algorithmic:.2f}x)")
     lines.append(f"index kernels (balance, bucketize, dedup, collision split): "
-                 f"{idx / 1e9:.3f} GB per step{extra}")
+                 f"{idx / 1e9:.3f} GB per iteration{extra}")
     return "\n".join(lines) + "\n"
 
 
@@ -197,7 +197,7 @@ def main() -> None:
     s.add_argument("--out", default=None)
     s.add_argument("--txt", default=None, help="also write the readable table here")
     s.add_argument("--steps", type=int, default=None,
-                   help="steps the run made (default: the update's launches)")
+                   help="iterations the run made (default: the lookup's launches)")
     s.add_argument("--index-bytes", type=float, default=None,
                    help="algorithmic bytes of the index stages per step")
     a = ap.parse_args()
@@ -206,7 +206,8 @@ def main() -> None:
     else:
         res = summarize(a.fetch_csv, a.write_csv, a.config, a.out)
         if a.txt:
-            steps = a.steps or res["stages"]["update_all"]["launches"]
+            # one lookup launch per iteration (the prologue's included)
+            steps = a.steps or res["stages"]["lookup_all"]["launches"]
             with open(a.txt, "w") as fh:
                 fh.write(table(res, steps, a.index_bytes))
 
