@@ -235,7 +235,9 @@ size_t fs_bucketize_workspace_size(int64_t n_tok, int32_t n, int32_t T, int32_t 
 /* then-read order, every other (exclusive) row can be fetched ahead.       */
 /*                                                                          */
 /*  shard_keys, shard_bm, shard_offsets: a bucketize call's output (items   */
-/*                 of shard d in [so_d, so_{d+1}), each a row of shard d).   */
+/*                 of shard d in [so_d, so_{d+1}), each a row of shard d,    */
+/*                 bm rising within a shard; the dedup keeps the items'      */
+/*                 order within each row, so occ_bm rises within each row).  */
 /*                 Offsets are clamped into [0, n_cap] and made rising, and  */
 /*                 a key outside its range's shard is clamped into it: such  */
 /*                 input gives unspecified results but writes nothing past    */

@@ -589,6 +589,69 @@ def test_collision_uneven_batches(W, rows):
         prev, oprev, prev_cap = uq, ouq, n_cap
 
 
+def _shard_major(rng, sizes, rows, W, kinds):
+    """Shard-major keys of one table with exactly sizes[d] items in shard d;
+    kinds[d] picks the key mix: "dup" (few distinct rows), "one" (one row),
+    "edge" (the shard's first and last rows among random ones), else random
+    rows of the shard. bm values are distinct and rise within each shard, as
+    in a bucketize call's output (the dedup keeps that order per row)."""
+    block = -(-rows // W)
+    parts = []
+    for d, (n, kind) in enumerate(zip(sizes, kinds)):
+        lo, hi = d * block, min(rows, (d + 1) * block)
+        if kind == "dup":
+            pool = rng.integers(lo, hi, size=37)
+            k = pool[rng.integers(0, len(pool), size=n)]
+        elif kind == "one":
+            k = np.full(n, lo + (hi - lo) // 2)
+        else:
+            k = rng.integers(lo, hi, size=n)
+            if kind == "edge" and n >= 2:
+                k[rng.choice(n, size=2, replace=False)] = [lo, hi - 1]
+        parts.append(k.astype(np.int64))
+    keys = np.concatenate(parts)
+    pool = rng.permutation(len(keys) * 3)[:len(keys)]
+    bm = np.concatenate([np.sort(x) for x in np.split(pool, np.cumsum(sizes)[:-1])])
+    bm = bm.astype(np.int32)
+    so = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
+    return keys, bm, so
+
+
+# One table sorted inside the shards, shards of exact sizes: empty shards,
+# partial waves and tiles (63/64/65, 2047/2048 items), sizes around 2^14,
+# shards of few distinct rows or of one row, the shard's first and last rows,
+# a short last shard; shard-local keys of 20 bits (two radix passes) and of
+# 8 bits (one pass).
+SS_CASES = [
+    ("wide", 16 << 20, [0, 1, 63, 64, 65, 2047, 2048, 16383, 16384, 16385, 40000, 5000, 0, 777,
+                        30000, 12],
+     ["rand", "rand", "edge", "dup", "rand", "one", "edge", "dup", "edge", "rand", "dup", "rand",
+      "rand", "one", "edge", "rand"]),
+    ("narrow", 16 * 200 - 3, [20000, 16384, 100, 0, 16383, 1, 9000, 16385, 64, 3, 0, 0, 4096, 5,
+                              700, 16384],
+     ["dup", "edge", "rand", "rand", "rand", "one", "edge", "dup", "rand", "rand", "rand", "rand",
+      "edge", "one", "dup", "rand"]),
+    ("all-small", 16 << 20, [16384, 9000, 1, 0] * 4, ["edge", "dup", "rand", "rand"] * 4),
+]
+
+
+@pytest.mark.parametrize("name,rows,sizes,kinds", SS_CASES, ids=[c[0] for c in SS_CASES])
+def test_unique_shard_sizes(name, rows, sizes, kinds):
+    """Unique outputs equal the oracle's, element by element, for shards of
+    exact sizes; each row's occurrences keep their order (occ_bm rising)."""
+    W = len(sizes)
+    rng = np.random.default_rng(sum(sizes) % 1000 + W)
+    keys, bm, so = _shard_major(rng, sizes, rows, W, kinds)
+    n = len(keys)
+    say("unique shard sizes", name, n)
+    for n_cap in (n, n + 5000):
+        uq = lib.fs_unique_collision_split(cu(keys), cu(bm), cu(so), n_cap, [rows], W)
+        ouq = O.unique(keys, bm, [rows], W)
+        cls, _, counts = O.collision(ouq["unique"], None)
+        torch.cuda.synchronize()
+        _cmp_unique(uq, ouq, cls, None, counts)
+
+
 def test_unique_empty_batch():
     say("unique-empty")
     rows = [100]
