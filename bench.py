@@ -88,6 +88,10 @@ def parse():
     ap.add_argument("--layout", choices=["dense", "rowstate", "rowstate256"], default="dense",
                     help="tables as dense [rows][dim] with a separate state array, or each "
                          "row's Adagrad state in the row's own padding")
+    ap.add_argument("--graph", choices=["off", "on"], default="off",
+                    help="replay each step as a HIP graph captured before the warm-up (index "
+                         "stages 2 or 3 ahead; the update's launch time then comes from extra "
+                         "steps run without graphs)")
     ap.add_argument("--autotune", action="store_true",
                     help="VBS AutoTune: shares of the weight moved every step by the modelled "
                          "per-rank time (VBS workloads only)")
@@ -179,10 +183,21 @@ def measure(ctx, steps, warmup, args, full):
     L = 1 if args.sync else args.lookahead
     ahead = L >= 2
     sched = args.schedule if ahead else "joined"
+    graph = args.graph == "on" and ahead and not args.sync
     step = SparseStep(w, ctx.weights, ctx.states, ctx.cap, lookup=args.lookup,
-                      lookahead=L, autotune={} if args.autotune else None, schedule=sched)
+                      lookahead=L, autotune={} if args.autotune else None, schedule=sched,
+                      graph=graph)
     step.prologue(dev_batches[0],
                   batch_after=[dev_batches[j % NB] for j in range(1, L)] if ahead else None)
+    if graph:
+        # the distinct steps repeat after lcm(batches, state slots, index
+        # streams) steps: capture them all now, outside every timed step
+        period = int(np.lcm.reduce([NB, L + 1, len(step.s_idx)]))
+        t0 = time.perf_counter()
+        n_graphs = step.record_graphs([
+            (dev_batches[j % NB], [g[:n_tok[(j - 1) % NB]] for g in grads_dev],
+             dev_batches[(j + L - 1) % NB]) for j in range(1, period + 1)])
+        log(f"captured {n_graphs} step graphs in {time.perf_counter() - t0:.2f}s")
     if args.sync:
         def run_step(batch_next, grads, k_next):
             return step.step_sync(batch_next, grads)
@@ -233,6 +248,21 @@ def measure(ctx, steps, warmup, args, full):
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     step.timer = None
+    if graph:
+        # graphs carry no timing events: the update's launch time from extra
+        # steps issued without graphs (the same kernels on the same buffers)
+        n_upd = min(steps, 10)
+        step.set_graph(False)
+        timer = StageTimer(capacity=4 * n_upd, streams=streams, only=upd_names)
+        step.timer = timer
+        for _ in range(n_upd):
+            p = k % NB
+            k += 1
+            run_step(dev_batches[k % NB], [g[:n_tok[p]] for g in grads_dev], k)
+        step.join()
+        torch.cuda.synchronize()
+        step.timer = None
+        step.set_graph(True)
     if args.sync:
         schedule = "sync"
     elif ahead:
@@ -241,6 +271,8 @@ def measure(ctx, steps, warmup, args, full):
                     else f"{far}, joined lookup")
     else:
         schedule = "joined" if step.joined else "split"
+    if graph:
+        schedule += ", one HIP graph per step"
     ms_total = ev0.elapsed_time(ev1)
     ms_step = ms_total / steps
     upd_ms = timer.ms()
@@ -252,6 +284,8 @@ def measure(ctx, steps, warmup, args, full):
         # ------------------------------------------------------------ stage breakdown
         brk = StageTimer(capacity=8 * n_brk, streams=streams)
         step.timer = brk
+        if graph:
+            step.set_graph(False)  # per-stage events: steps issued without graphs
         for _ in range(n_brk):
             p = k % NB
             k += 1
@@ -259,6 +293,8 @@ def measure(ctx, steps, warmup, args, full):
         step.join()
         torch.cuda.synchronize()
         step.timer = None
+        if graph:
+            step.set_graph(True)
         stage_ms = brk.ms()
 
         # ------------------------------------------------------------ per-step spread

@@ -68,6 +68,15 @@ per-rank shares of the weight, and right after each balance the modelled time
 of the partition it made moves the shares for the next one -- two small
 launches on the index stream, no host synchronisation.
 
+With `graph=True` (index stages two or three ahead) each distinct step --
+the state slots it uses and its input tensors -- is captured once as a HIP
+graph and replayed after that: the host then submits one graph per step
+instead of some 30 launches and their stream waits, which sets the pace of
+small batches. A step's graph starts after the previous one has ended, so it
+waits for nothing outside itself; inside it the index stages still run beside
+the update and the lookup. `record_graphs` captures a known sequence of steps
+ahead of time without running them.
+
 Buffers are allocated once at capacity; per-iteration state is double
 buffered (triple with lookahead=2), and every C call is marshalled once per
 state slot. Every stream keeps the default priority.
@@ -165,6 +174,7 @@ class IterState:
     idx_x: int = 0  # index stream that ran this iteration's index stages
     ev_done: torch.cuda.Event = None  # index stages done (after the dedup)
     ev_bal: torch.cuda.Event = None  # balance (and AutoTune's share update) done
+    graph: object = None  # the step graph whose capture indexed this iteration (graph mode)
 
 
 _LOOKUP_MODES = ("split", "joined", "auto")
@@ -178,7 +188,7 @@ _CALIB_STEPS = 3  # steps timed by lookup="auto" before it decides
 
 class SparseStep:
     def __init__(self, workload, weights, states, n_tok_cap, device=None, lookup="auto",
-                 lookahead=1, autotune=None, schedule="joined"):
+                 lookahead=1, autotune=None, schedule="joined", graph=False):
         if lookup not in _LOOKUP_MODES:
             raise ValueError(f"lookup must be one of {_LOOKUP_MODES}, not {lookup!r}")
         if lookahead not in (1, 2, 3):
@@ -189,6 +199,9 @@ class SparseStep:
             raise ValueError("the prioritized schedule needs the index stages at least two "
                              "ahead (lookahead=2 or 3): the update of i starts from the classes "
                              "of i against i+1")
+        if graph and lookahead < 2:
+            raise ValueError("graph replay needs the index stages ahead (lookahead=2 or 3): "
+                             "a step's graph then holds no wait on work of the step before")
         self.schedule = schedule
         if autotune is not None and workload.balancer != "vbs":
             raise ValueError("autotune needs the VBS balancer")
@@ -244,10 +257,51 @@ class SparseStep:
             self.shares = torch.full((W,), int(self.autotune["init"]), dtype=torch.int64,
                                      device=d)
             self.rank_cost = torch.empty(W, dtype=torch.int64, device=d)
+        # graph mode: one HIP graph per distinct step (state slots, inputs)
+        self.graph = graph
+        self._graphs = {}
+        self._capture = None  # the graph being captured or replayed
+        self._dry = False  # replaying a captured step: Python state only
+        self._record_only = False  # capturing without replaying
+        self._forked = []  # streams forked from the capture stream
+        self._cap_stream = torch.cuda.Stream(device=d) if graph else None
 
     def _t(self, name, stream):
         """Context that brackets one C call with HIP events on its stream."""
-        return self.timer.span(name, stream) if self.timer is not None else _nullspan()
+        if self.timer is None or self._capture is not None:
+            return _nullspan()
+        return self.timer.span(name, stream)
+
+    # ------------------------------------------------------------------ issue
+    # Every GPU operation of a step goes through these, so that a step whose
+    # graph was captured before can replay it after running only the state
+    # bookkeeping. Inside a captured step, waits on events of an earlier step
+    # are left out: a step's graph starts after the previous one has ended.
+    def _call(self, fn, **kw):
+        if not self._dry:
+            fn(**kw)
+
+    def _fork(self, s, cs):
+        """Stream s waits for everything enqueued on cs so far."""
+        if self._capture is not None and s not in self._forked:
+            self._forked.append(s)
+        if not self._dry:
+            s.wait_stream(cs)
+
+    def _join(self, cs, s):
+        if not self._dry:
+            cs.wait_stream(s)
+
+    def _wait(self, s, ev, st):
+        """Stream s waits for event ev of iteration state st."""
+        if self._dry or (self._capture is not None and st.graph is not self._capture):
+            return
+        s.wait_event(ev)
+
+    def _record(self, ev, s, st):
+        st.graph = self._capture
+        if not self._dry:
+            ev.record(s)
 
     def _alloc_iter(self):
         d, W, T, cap = self.dev, self.W, self.T, self.cap
@@ -328,27 +382,29 @@ class SparseStep:
                             prev.uq if prev is not None else None,
                             prev.cls_next if prev is not None else None, self.ws_uq))
         if at is not None and other:  # the shares the previous balance left
-            stream.wait_event(prev.ev_bal)
+            self._wait(stream, prev.ev_bal, prev)
         with self._t("balance", stream):
-            pb(uih=lib._ptr(uih), n=uih.numel(), stream=sh)
+            self._call(pb, uih=lib._ptr(uih), n=uih.numel(), stream=sh)
         if at is not None:  # the shares for the next balance
             with self._t("autotune", stream):
-                pc(uih=lib._ptr(uih), n=uih.numel(), stream=sh)
-                pa(stream=sh)
-            st.ev_bal.record(stream)
+                self._call(pc, uih=lib._ptr(uih), n=uih.numel(), stream=sh)
+                self._call(pa, stream=sh)
+            self._record(st.ev_bal, stream, st)
         with self._t("bucketize", stream):
-            pk(ids=lib._ptr(ids), n_tok=n_tok, so=lib._ptr(so), n=so.numel() - 1, stream=sh)
+            self._call(pk, ids=lib._ptr(ids), n_tok=n_tok, so=lib._ptr(so), n=so.numel() - 1,
+                       stream=sh)
         if other:
-            stream.wait_event(prev.ev_done)
+            self._wait(stream, prev.ev_done, prev)
         with self._t("unique_split", stream):
-            pu(n_cap=T * n_tok, prev_cap=T * prev.n_tok if prev is not None else 0, stream=sh)
-        st.ev_done.record(stream)
+            self._call(pu, n_cap=T * n_tok,
+                       prev_cap=T * prev.n_tok if prev is not None else 0, stream=sh)
+        self._record(st.ev_done, stream, st)
 
     def _lookup(self, st, which, stream):
         pl = self._prep(("lk", st.slot, which), lambda: lib.prepare_lookup(
             self.weights, self.W, st.uq, st.out, which, st.uq["cls"]))
         with self._t(f"lookup_{_CLS[which]}", stream):
-            pl(n_tok=st.n_tok, stream=stream.cuda_stream)
+            self._call(pl, n_tok=st.n_tok, stream=stream.cuda_stream)
 
     def _run_update(self, st, grads, which, ws, stream, name=None):
         pu = self._prep(("upd", st.slot, which, id(ws)), lambda: lib.prepare_update(
@@ -358,7 +414,7 @@ class SparseStep:
         for t, x in enumerate(grads):
             g[t] = lib._ptr(x)
         with self._t(name or f"update_{_CLS[which]}", stream):
-            pu(n_tok=st.n_tok, stream=stream.cuda_stream)
+            self._call(pu, n_tok=st.n_tok, stream=stream.cuda_stream)
 
     # ------------------------------------------------------------------ schedule
     def _nslots(self):
@@ -386,6 +442,9 @@ class SparseStep:
                 self._index_stages(b, nxt, prev, s_, x)
                 self._ahead.append(nxt)
                 prev = nxt
+        if self.graph:  # the first step's graph starts after all of it
+            for s_ in self.s_idx:
+                cs.wait_stream(s_)
         return st
 
     def _decide(self):
@@ -403,6 +462,8 @@ class SparseStep:
     def step(self, batch_next, grads_cur, batch_after=None):
         """Prioritized step: update iteration i, look up iteration i+1 (and,
         with lookahead L >= 2, index `batch_after`, iteration i+L)."""
+        if self.graph:
+            return self._step_graph(batch_next, grads_cur, batch_after)
         if self.schedule == "prioritized":
             return self._step_prioritized(batch_next, grads_cur, batch_after)
         if self.lookahead >= 2:
@@ -453,13 +514,13 @@ class SparseStep:
         if not self._ahead:  # iteration i+1 was not indexed ahead: index it now
             nxt = self.states_buf[(self.slot + 1) % n]
             x, s_ = self._index_stream()
-            s_.wait_stream(cs)
+            self._fork(s_, cs)
             self._index_stages(batch_next, nxt, cur, s_, x)
         else:
             nxt = self._ahead.popleft()
         if batch_after is not None:
             x, s_ = self._index_stream()
-            s_.wait_stream(cs)
+            self._fork(s_, cs)
             aft_s = (x, s_)
         return nxt, aft_s
 
@@ -482,7 +543,7 @@ class SparseStep:
         # the update of i needs nothing from the index stages of i+1 (they
         # only read iteration i's unique rows), so only the lookup waits
         self._run_update(cur, grads_cur, lib.FS_ALL, self.ws_red[1], cs)
-        cs.wait_event(nxt.ev_done)
+        self._wait(cs, nxt.ev_done, nxt)
         self._lookup(nxt, lib.FS_ALL, cs)
         self._index_after(batch_after, nxt, aft_s)
         self.cur = nxt
@@ -500,21 +561,105 @@ class SparseStep:
         # streams B and C after the work on the caller's stream: the
         # gradients, and the previous step (joined into it), whose buffers
         # this one reuses
-        sB.wait_stream(cs)
-        sC.wait_stream(cs)
+        self._fork(sB, cs)
+        self._fork(sC, cs)
         # the classes of i against i+1 (the update's) and of i+1 (the lookups')
         for s_ in (cs, sB, sC):
-            s_.wait_event(nxt.ev_done)
+            self._wait(s_, nxt.ev_done, nxt)
         self._run_update(cur, grads_cur, lib.FS_COLLISION, self.ws_red[1], cs)
         self._lookup(nxt, lib.FS_COLLISION, cs)
         self._run_update(cur, grads_cur, lib.FS_EXCLUSIVE, self.ws_red[0], sB)
         self._lookup(nxt, lib.FS_EXCLUSIVE, sC)
         self._index_after(batch_after, nxt, aft_s)
-        cs.wait_stream(sB)
-        cs.wait_stream(sC)
+        self._join(cs, sB)
+        self._join(cs, sC)
         self.cur = nxt
         self.slot = (self.slot + 1) % self._nslots()
         return nxt
+
+    # ------------------------------------------------------------------ graph mode
+    # A step is a fixed set of launches on fixed buffers, chosen by the state
+    # slots in use and the input tensors: each distinct step is captured once
+    # as a HIP graph (every stream it uses forked from the capture stream and
+    # joined back) and replayed after that, so the host submits one graph
+    # instead of some 30 launches and their stream waits. Graphs of
+    # consecutive steps run one after the other; the index stages still run
+    # ahead, beside the update and the lookup of the same step.
+    def _graph_key(self, batch_next, grads_cur, batch_after):
+        def bk(b):
+            if b is None:
+                return None
+            return (b["ids"].data_ptr(), tuple(b["ids"].shape), b["sample_offsets"].data_ptr(),
+                    b["uih_len"].data_ptr(), b["uih_len"].numel())
+        # the launches depend on the token counts of the iterations alive
+        # (updated, indexed ahead) and on the shapes of the new batches; the
+        # slot about to be overwritten holds nothing they read
+        return (self.slot, tuple(st.slot for st in self._ahead),
+                self._n_indexed % len(self.s_idx),
+                None if self._ahead else bk(batch_next), bk(batch_after),
+                tuple((g.data_ptr(), tuple(g.shape)) for g in grads_cur),
+                self.cur.n_tok, tuple(st.n_tok for st in self._ahead))
+
+    def _step_graph(self, batch_next, grads_cur, batch_after):
+        key = self._graph_key(batch_next, grads_cur, batch_after)
+        body = self._step_prioritized if self.schedule == "prioritized" else self._step_ahead
+        g = self._graphs.get(key)
+        if g is None:
+            g = torch.cuda.CUDAGraph()
+            self._capture, self._forked = g, []
+            try:
+                with torch.cuda.graph(g, stream=self._cap_stream):
+                    cs = torch.cuda.current_stream()
+                    nxt = body(batch_next, grads_cur, batch_after)
+                    for s_ in self._forked:
+                        cs.wait_stream(s_)
+            finally:
+                self._capture, self._forked = None, []
+            self._graphs[key] = g
+        else:
+            self._capture, self._dry = g, True
+            try:
+                nxt = body(batch_next, grads_cur, batch_after)
+            finally:
+                self._capture, self._dry = None, False
+        if not self._record_only:
+            g.replay()
+        return nxt
+
+    def set_graph(self, on):
+        """Switches graph mode on or off between steps (captured graphs are
+        kept). Switching on first makes the caller's stream wait for all work
+        issued without graphs, which a step's graph does not wait for."""
+        if on and self.lookahead < 2:
+            raise ValueError("graph replay needs lookahead=2 or 3")
+        if on and not self.graph:
+            if self._cap_stream is None:
+                self._cap_stream = torch.cuda.Stream(device=self.dev)
+            cs = torch.cuda.current_stream()
+            for s_ in self.s_idx + [self.sB] + ([self.sC] if self.sC is not None else []):
+                cs.wait_stream(s_)
+        self.graph = bool(on)
+
+    def record_graphs(self, calls):
+        """Graph mode: captures the graphs of a sequence of step() calls
+        (argument tuples, in the order they will be made) without running
+        them, and leaves the step's state as it was, so that later calls
+        only replay."""
+        if not self.graph:
+            raise RuntimeError("record_graphs needs graph=True")
+        snap = (self.slot, self.cur, list(self._ahead), self._n_indexed,
+                [(st.idx_x, st.n_tok, st.graph) for st in self.states_buf])
+        self._record_only = True
+        try:
+            for a in calls:
+                self.step(*a)
+        finally:
+            self._record_only = False
+            self.slot, self.cur, ahead, self._n_indexed, per = snap
+            self._ahead = deque(ahead)
+            for st, (x, n, g) in zip(self.states_buf, per):
+                st.idx_x, st.n_tok, st.graph = x, n, g
+        return len(self._graphs)
 
     def step_sync(self, batch_next, grads_cur):
         """Reference schedule on one stream: update all of i, then look up all of i+1."""

@@ -241,6 +241,8 @@ def test_step_rejects_unknown_lookup_schedule():
         SparseStep(None, [], [], 1, lookahead=4)
     with pytest.raises(ValueError):  # the prioritized schedule needs the index stages ahead
         SparseStep(None, [], [], 1, lookahead=1, schedule="prioritized")
+    with pytest.raises(ValueError):  # graph replay needs the index stages ahead
+        SparseStep(None, [], [], 1, lookahead=1, graph=True)
     from jagged_embedding_sparse_amd import synth
     with pytest.raises(ValueError):  # AutoTune moves VBS shares: no FBS
         SparseStep(synth.workload(1), [], [], 1, autotune={})

@@ -330,3 +330,79 @@ def test_prioritized_equals_synchronous(k):
                 assert np.array_equal(a, b)
         for a, b in zip(fa, fb):
             assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("k", [1, 2, 3])
+@pytest.mark.parametrize("mode", ["ahead3", "prioritized2"])
+def test_graph_replays_equal_synchronous(k, mode):
+    """Steps replayed from HIP graphs == the one-stream synchronous loop, bit
+    for bit. The batches cycle (as many distinct ones as state slots, over 13
+    steps) so that each graph is replayed three or four times; the first
+    cycle's graphs are captured ahead (record_graphs), the last steps' (no
+    batch after them) on the fly. Between replays the program's own work runs
+    on the caller's stream: the next step's gradients are copied into one of
+    the fixed buffers, each lookup is copied out, and every third step the
+    host synchronises."""
+    w = synth.workload(k)
+    L = 3 if mode == "ahead3" else 2
+    NB, S = L + 1, 13
+    bt = synth.Batches(w, 70 + k)
+    batches = [bt.batch(i) for i in range(NB)]
+    seq = [j % NB for j in range(S + 1)]  # iteration j looks up batch seq[j]
+    dev_b = [to_dev(b) for b in batches]
+    cap = max(b["n_tok"] for b in batches)
+    rows_t = touched_rows(batches, w)
+
+    say("graph", k, mode, "synchronous reference")
+    weights, states = gpu_tables(w, 70 + k)
+    step = SparseStep(w, weights, states, cap, lookup="split", lookahead=1)
+    st = step.prologue(dev_b[seq[0]])
+    step.join()
+    ref_looks = [[_bits(o[:st.n_tok]).copy() for o in st.out]]
+    grads = []
+    for i in range(S):
+        torch.cuda.synchronize()
+        grads.append(balanced_grads(w, 70 + k, i, batches[seq[i]], host(st.perm),
+                                    host(st.bucket["bal_offsets"])))
+        st = step.step_sync(dev_b[seq[i + 1]], [torch.from_numpy(x).cuda() for x in grads[i]])
+        step.join()
+        ref_looks.append([_bits(o[:st.n_tok]).copy() for o in st.out])
+    torch.cuda.synchronize()
+    ref_final = [_bits(weights[t].index_select(0, torch.from_numpy(r).cuda()))
+                 for t, r in enumerate(rows_t)]
+    del step, weights, states
+
+    say("graph", k, mode, "graph replays")
+    weights, states = gpu_tables(w, 70 + k)
+    step = SparseStep(w, weights, states, cap, lookahead=L, graph=True,
+                      schedule="prioritized" if mode.startswith("prioritized") else "joined")
+    gbuf = [[torch.empty((cap, spec.dim), dtype=torch.float32, device="cuda")
+             for spec in w.tables] for _ in range(NB)]
+
+    def gviews(i):
+        return [b[:len(x)] for b, x in zip(gbuf[i % NB], grads[i])]
+
+    def after(i):
+        return dev_b[seq[i + L]] if i + L <= S else None
+
+    st = step.prologue(dev_b[seq[0]], batch_after=[dev_b[seq[j]] for j in range(1, L)])
+    n_rec = step.record_graphs([(dev_b[seq[i + 1]], gviews(i), after(i)) for i in range(NB)])
+    assert n_rec == NB
+    looks = [[o[:st.n_tok].clone() for o in st.out]]
+    for i in range(S):
+        for b, x in zip(gviews(i), grads[i]):
+            b.copy_(torch.from_numpy(x).cuda())
+        st = step.step(dev_b[seq[i + 1]], gviews(i), batch_after=after(i))
+        looks.append([o[:st.n_tok].clone() for o in st.out])
+        if i % 3 == 2:
+            torch.cuda.synchronize()
+    step.join()
+    torch.cuda.synchronize()
+    say("graph", k, mode, "graphs", len(step._graphs))
+    assert len(step._graphs) < S  # replays happened
+    for x, y in zip(looks, ref_looks):
+        for a, b in zip(x, y):
+            assert np.array_equal(_bits(a), b)
+    for t, r in enumerate(rows_t):
+        got = _bits(weights[t].index_select(0, torch.from_numpy(r).cuda()))
+        assert np.array_equal(got, ref_final[t])
