@@ -78,6 +78,10 @@ extern "C" {
 #define FS_ALL (-1)
 #define FS_EXCLUSIVE 0
 #define FS_COLLISION 1
+/* rows of an update call by occurrence count (a bit mask) */
+#define FS_ROWS_FEW 1  /* at most 64 occurrences: each row summed whole */
+#define FS_ROWS_MANY 2 /* more than 64: summed in chunks, then combined */
+#define FS_ROWS_ALL 3
 
 typedef struct fs_table {
   void* weights;  /* device: rows rows of dim elements, dtype FS_F32 or FS_BF16 */
@@ -357,6 +361,13 @@ size_t fs_keyed_transpose_workspace_size(int32_t F, int32_t B);
 /*  grad         host [T] of device fp32 [n_tok][dim_t], batch-major.         */
 /*  cls          the class of THIS iteration's rows against the next one: the */
 /*               next split call's prev_cls (NULL with which == FS_ALL).      */
+/*  rows         which of those rows by occurrence count: FS_ROWS_ALL,       */
+/*               FS_ROWS_FEW or FS_ROWS_MANY (else FS_ERR_INVALID_ARG). The   */
+/*               two parts update disjoint rows and only FS_ROWS_MANY uses    */
+/*               the workspace, so they may run at the same time on two       */
+/*               streams with one workspace; together they give exactly the  */
+/*               FS_ROWS_ALL result. One update as two concurrent parts has  */
+/*               one launch boundary fewer on each stream.                    */
 /*  reduced_out  host [T] of device fp32 [U_t][dim_t] (or NULL array / NULL   */
 /*               entries): row u of table t is written at u - unique_offsets[t*W]. */
 /* dim_t must be 64, 128, 256, 512 or 1024 (else FS_ERR_UNSUPPORTED);        */
@@ -369,7 +380,7 @@ int fs_grad_reduce_update(const fs_table* tables, int32_t T, int32_t W,
                           const float* const* grad, int64_t n_tok, const int64_t* unique,
                           const int64_t* unique_offsets, const int32_t* seg_offsets,
                           const int32_t* occ_bm, const int32_t* occ_uid, const uint8_t* cls,
-                          int32_t which, int32_t optim, float lr, float eps,
+                          int32_t which, int32_t rows, int32_t optim, float lr, float eps,
                           float* const* reduced_out, void* ws, size_t ws_bytes,
                           hipStream_t stream);
 
@@ -389,15 +400,18 @@ size_t fs_grad_reduce_update_workspace_size(int64_t n_tok, int32_t T, int32_t ma
 /* times the space). Every call on one GPU */
 /* uses the same array: calls that overlap on one GPU (on different streams */
 /* without an order between them) race and give undefined results; calls   */
-/* ordered on one stream, or by events, are safe. Nothing in the array      */
-/* needs clearing: each call writes every partial it reads.                 */
+/* ordered on one stream, or by events, are safe; so are an FS_ROWS_FEW     */
+/* call and an FS_ROWS_MANY call that overlap (only the latter uses the     */
+/* array). Nothing in the array needs clearing: each call writes every      */
+/* partial it reads.                                                         */
 #define FS_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
 int fs_grad_reduce_update_noalloc(const fs_table* tables, int32_t T, int32_t W,
                                   const float* const* grad, int64_t n_tok, const int64_t* unique,
                                   const int64_t* unique_offsets, const int32_t* seg_offsets,
                                   const int32_t* occ_bm, const int32_t* occ_uid,
-                                  const uint8_t* cls, int32_t which, int32_t optim, float lr,
-                                  float eps, float* const* reduced_out, hipStream_t stream);
+                                  const uint8_t* cls, int32_t which, int32_t rows,
+                                  int32_t optim, float lr, float eps, float* const* reduced_out,
+                                  hipStream_t stream);
 
 /* ------------------------------------------------------------------------ */
 const char* fs_strerror(int code);

@@ -707,14 +707,17 @@ int shape_of(int dim, bool bf16) {
   return 2 * l + (bf16 ? 1 : 0);
 }
 
-// every kind in order (short, medium and long rows, then the fix-up of the
-// long rows' partial sums), each kind one launch for the narrow tables (a
-// table's own launch when it is the only narrow one) and one per wide table
-int launch_tables(const RUArgs* args, const int* dims, const bool* bf16, int T,
+// every kind of the requested rows in order (short and medium rows: FS_ROWS_FEW;
+// long rows, then the fix-up of their partial sums: FS_ROWS_MANY), each kind
+// one launch for the narrow tables (a table's own launch when it is the only
+// narrow one) and one per wide table
+int launch_tables(const RUArgs* args, const int* dims, const bool* bf16, int T, int32_t rows,
                   hipStream_t stream) {
   int narrow = 0;
   for (int t = 0; t < T; ++t) narrow += dims[t] <= kSetMaxDim;
   for (int K = 0; K < 4; ++K) {
+    const int32_t part = (K == kShortRows || K == kMediumRows) ? FS_ROWS_FEW : FS_ROWS_MANY;
+    if (!(rows & part)) continue;
     RUSet set;
     set.n = 0;
     int64_t total = 0;
@@ -794,13 +797,15 @@ namespace {
 int ru_check(const fs_table* tables, int32_t T, int32_t W, const float* const* grad,
              int64_t n_tok, const int64_t* unique, const int64_t* unique_offsets,
              const int32_t* seg_offsets, const int32_t* occ_bm, const int32_t* occ_uid,
-             const uint8_t* cls, int32_t which, int32_t optim, size_t ws_bytes,
+             const uint8_t* cls, int32_t which, int32_t rows, int32_t optim, size_t ws_bytes,
              int too_small) {
   if (!tables || T < 1 || T > FS_MAX_TABLES || W < 1 || W > FS_MAX_RANKS || n_tok < 0 ||
       (int64_t)T * n_tok >= (int64_t)INT32_MAX || !grad || !unique_offsets || !seg_offsets)
     return FS_ERR_INVALID_ARG;
   if (which != FS_ALL && which != FS_EXCLUSIVE && which != FS_COLLISION) return FS_ERR_INVALID_ARG;
   if (which != FS_ALL && !cls) return FS_ERR_INVALID_ARG;
+  if (rows != FS_ROWS_FEW && rows != FS_ROWS_MANY && rows != FS_ROWS_ALL)
+    return FS_ERR_INVALID_ARG;
   if (optim != FS_SGD && optim != FS_RW_ADAGRAD) return FS_ERR_INVALID_ARG;
   if (n_tok > 0 && (!unique || !occ_bm || !occ_uid)) return FS_ERR_INVALID_ARG;
   int max_dim = 0;
@@ -823,8 +828,8 @@ int ru_check(const fs_table* tables, int32_t T, int32_t W, const float* const* g
 int ru_launch(const fs_table* tables, int32_t T, int32_t W, const float* const* grad,
               int64_t n_tok, const int64_t* unique, const int64_t* unique_offsets,
               const int32_t* seg_offsets, const int32_t* occ_bm, const int32_t* occ_uid,
-              const uint8_t* cls, int32_t which, int32_t optim, float lr, float eps,
-              float* const* reduced_out, void* ws, hipStream_t stream) {
+              const uint8_t* cls, int32_t which, int32_t rows, int32_t optim, float lr,
+              float eps, float* const* reduced_out, void* ws, hipStream_t stream) {
   RUArgs args[FS_MAX_TABLES];
   int dims[FS_MAX_TABLES];
   bool bf16[FS_MAX_TABLES];
@@ -862,7 +867,7 @@ int ru_launch(const fs_table* tables, int32_t T, int32_t W, const float* const* 
     bf16[t] = tb.dtype == FS_BF16;
   }
   if (n_tok == 0) return FS_OK;
-  return launch_tables(args, dims, bf16, T, stream);
+  return launch_tables(args, dims, bf16, T, rows, stream);
 }
 
 // The allocation-free variant's scratch: one array per GPU the library runs
@@ -906,14 +911,14 @@ extern "C" int fs_grad_reduce_update(const fs_table* tables, int32_t T, int32_t 
                                      const int64_t* unique, const int64_t* unique_offsets,
                                      const int32_t* seg_offsets, const int32_t* occ_bm,
                                      const int32_t* occ_uid, const uint8_t* cls, int32_t which,
-                                     int32_t optim, float lr, float eps,
+                                     int32_t rows, int32_t optim, float lr, float eps,
                                      float* const* reduced_out, void* ws, size_t ws_bytes,
                                      hipStream_t stream) {
   int rc = ru_check(tables, T, W, grad, n_tok, unique, unique_offsets, seg_offsets, occ_bm,
-                    occ_uid, cls, which, optim, ws ? ws_bytes : 0, FS_ERR_WORKSPACE);
+                    occ_uid, cls, which, rows, optim, ws ? ws_bytes : 0, FS_ERR_WORKSPACE);
   if (rc) return rc;
   return ru_launch(tables, T, W, grad, n_tok, unique, unique_offsets, seg_offsets, occ_bm,
-                   occ_uid, cls, which, optim, lr, eps, reduced_out, ws, stream);
+                   occ_uid, cls, which, rows, optim, lr, eps, reduced_out, ws, stream);
 }
 
 extern "C" int fs_grad_reduce_update_noalloc(const fs_table* tables, int32_t T, int32_t W,
@@ -922,10 +927,12 @@ extern "C" int fs_grad_reduce_update_noalloc(const fs_table* tables, int32_t T, 
                                              const int64_t* unique_offsets,
                                              const int32_t* seg_offsets, const int32_t* occ_bm,
                                              const int32_t* occ_uid, const uint8_t* cls,
-                                             int32_t which, int32_t optim, float lr, float eps,
-                                             float* const* reduced_out, hipStream_t stream) {
+                                             int32_t which, int32_t rows, int32_t optim, float lr,
+                                             float eps, float* const* reduced_out,
+                                             hipStream_t stream) {
   int rc = ru_check(tables, T, W, grad, n_tok, unique, unique_offsets, seg_offsets, occ_bm,
-                    occ_uid, cls, which, optim, FS_NOALLOC_SCRATCH_BYTES, FS_ERR_TOO_LARGE);
+                    occ_uid, cls, which, rows, optim, FS_NOALLOC_SCRATCH_BYTES,
+                    FS_ERR_TOO_LARGE);
   if (rc) return rc;
   void* ws = nullptr;
   rc = scratch_for(stream, &ws);
@@ -933,5 +940,5 @@ extern "C" int fs_grad_reduce_update_noalloc(const fs_table* tables, int32_t T, 
   // every fp64 partial a launch reads is written earlier in the same launch
   // sequence, so the scratch needs no clearing between calls
   return ru_launch(tables, T, W, grad, n_tok, unique, unique_offsets, seg_offsets, occ_bm,
-                   occ_uid, cls, which, optim, lr, eps, reduced_out, ws, stream);
+                   occ_uid, cls, which, rows, optim, lr, eps, reduced_out, ws, stream);
 }

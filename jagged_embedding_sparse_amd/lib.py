@@ -24,6 +24,7 @@ FS_EF_ID_RANGE, FS_EF_SHAPE, FS_EF_LEN_RANGE = 1, 2, 4
 FS_F32, FS_BF16 = 0, 1
 FS_SGD, FS_RW_ADAGRAD = 0, 1
 FS_ALL, FS_EXCLUSIVE, FS_COLLISION = -1, 0, 1
+FS_ROWS_FEW, FS_ROWS_MANY, FS_ROWS_ALL = 1, 2, 3
 FS_MAX_SAMPLES, FS_MAX_RANKS, FS_MAX_TABLES, FS_MAX_UIH = 16384, 1024, 8, 65535
 
 if not os.path.exists(LIB_PATH):
@@ -71,10 +72,10 @@ _c_kt = _sig("fs_keyed_transpose", C.c_int, _P, _i64, _i32, _P, _i32, _i32, _P, 
              _P)
 _c_kt_ws = _sig("fs_keyed_transpose_workspace_size", _sz, _i32, _i32)
 _c_reduce = _sig("fs_grad_reduce_update", C.c_int, _TP, _i32, _i32, C.POINTER(_P), _i64, _P, _P,
-                 _P, _P, _P, _P, _i32, _i32, _f, _f, C.POINTER(_P), _P, _sz, _P)
+                 _P, _P, _P, _P, _i32, _i32, _i32, _f, _f, C.POINTER(_P), _P, _sz, _P)
 _c_reduce_ws = _sig("fs_grad_reduce_update_workspace_size", _sz, _i64, _i32, _i32)
 _c_reduce_noalloc = _sig("fs_grad_reduce_update_noalloc", C.c_int, _TP, _i32, _i32,
-                         C.POINTER(_P), _i64, _P, _P, _P, _P, _P, _P, _i32, _i32, _f, _f,
+                         C.POINTER(_P), _i64, _P, _P, _P, _P, _P, _P, _i32, _i32, _i32, _f, _f,
                          C.POINTER(_P), _P)
 _c_strerror = _sig("fs_strerror", C.c_char_p, C.c_int)
 _c_version = _sig("fs_version", C.c_int)
@@ -401,7 +402,8 @@ def reduce_workspace_size(n_tok, max_dim, T=1):
 
 
 def fs_grad_reduce_update(weights, states, W, grads, n_tok, uq, optim, lr, eps=0.0,
-                          which=FS_ALL, cls=None, reduced_out=None, ws=None, stream=None):
+                          which=FS_ALL, cls=None, reduced_out=None, ws=None, stream=None,
+                          rows=FS_ROWS_ALL):
     T = len(weights)
     tabs = make_tables(weights, states)
     max_dim = max(w.shape[1] for w in weights)
@@ -410,13 +412,14 @@ def fs_grad_reduce_update(weights, states, W, grads, n_tok, uq, optim, lr, eps=0
     _check("fs_grad_reduce_update",
            _c_reduce(tabs, T, W, _ptr_array(grads), n_tok, _ptr(uq["unique"]),
                      _ptr(uq["unique_offsets"]), _ptr(uq["seg_offsets"]), _ptr(uq["occ_bm"]),
-                     _ptr(uq["occ_uid"]), _ptr(cls) if which != FS_ALL else None, which,
+                     _ptr(uq["occ_uid"]), _ptr(cls) if which != FS_ALL else None, which, rows,
                      FS_RW_ADAGRAD if optim in ("rw_adagrad", FS_RW_ADAGRAD) else FS_SGD,
                      float(lr), float(eps), red, _ptr(ws), ws.numel(), _stream(stream)))
 
 
 def fs_grad_reduce_update_noalloc(weights, states, W, grads, n_tok, uq, optim, lr, eps=0.0,
-                                  which=FS_ALL, cls=None, reduced_out=None, stream=None):
+                                  which=FS_ALL, cls=None, reduced_out=None, stream=None,
+                                  rows=FS_ROWS_ALL):
     """fs_grad_reduce_update without a workspace (the library's fixed per-GPU
     scratch; raises FsError FS_ERR_TOO_LARGE beyond it)."""
     T = len(weights)
@@ -426,7 +429,7 @@ def fs_grad_reduce_update_noalloc(weights, states, W, grads, n_tok, uq, optim, l
            _c_reduce_noalloc(tabs, T, W, _ptr_array(grads), n_tok, _ptr(uq["unique"]),
                              _ptr(uq["unique_offsets"]), _ptr(uq["seg_offsets"]),
                              _ptr(uq["occ_bm"]), _ptr(uq["occ_uid"]),
-                             _ptr(cls) if which != FS_ALL else None, which,
+                             _ptr(cls) if which != FS_ALL else None, which, rows,
                              FS_RW_ADAGRAD if optim in ("rw_adagrad", FS_RW_ADAGRAD) else FS_SGD,
                              float(lr), float(eps), red, _stream(stream)))
 
@@ -529,12 +532,13 @@ def prepare_lookup(weights, W, uq, out, which=FS_ALL, cls=None):
 
 def prepare_update(weights, states, W, uq, optim, lr, eps, which, cls, ws):
     """fs_grad_reduce_update with the gradient pointers in arrays["grads"]
-    (set them before each call); call with n_tok=, stream=."""
+    (set them before each call); call with n_tok=, stream= (and rows=, all
+    rows unless given)."""
     grads = (C.c_void_p * len(weights))()
     args = [make_tables(weights, states), len(weights), W, grads, 0, _ptr(uq["unique"]),
             _ptr(uq["unique_offsets"]), _ptr(uq["seg_offsets"]), _ptr(uq["occ_bm"]),
-            _ptr(uq["occ_uid"]), _ptr(cls) if which != FS_ALL else None, which,
+            _ptr(uq["occ_uid"]), _ptr(cls) if which != FS_ALL else None, which, FS_ROWS_ALL,
             FS_RW_ADAGRAD if optim in ("rw_adagrad", FS_RW_ADAGRAD) else FS_SGD, float(lr),
             float(eps), None, _ptr(ws), ws.numel(), None]
-    return Prepared("fs_grad_reduce_update", _c_reduce, args, dict(n_tok=4, stream=18),
+    return Prepared("fs_grad_reduce_update", _c_reduce, args, dict(n_tok=4, rows=12, stream=19),
                     arrays=dict(grads=grads))

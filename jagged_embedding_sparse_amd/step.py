@@ -49,6 +49,13 @@ longer than the update and the lookup, a step then costs about one dedup
 instead of a whole index chain. Each index stream has its own balance and
 bucketize workspace; four iteration states are alive at once.
 
+With the index stages ahead (joined lookup) and a batch of at least 2^17
+IDs, the update runs as two concurrent parts: its rows of at most 64
+occurrences on the caller's stream and its longer rows (chunked sums and
+their fix-up) on stream B, joined before the lookup. The parts touch disjoint
+rows, so the result is the same; each stream has one launch boundary fewer
+and the parts' ramps and tails overlap.
+
 With `schedule="prioritized"` (index stages two ahead) the update is split
 by class as Algorithm 2 splits it, so that the next lookup waits only for the
 rows it shares with the update:
@@ -184,11 +191,16 @@ _SCHEDULES = ("joined", "prioritized")
 # every share starting at init
 AUTOTUNE_DEFAULTS = dict(coef=(1, 64, 0), step=(1, 16), tol=(1, 50), init=1 << 16)
 _CALIB_STEPS = 3  # steps timed by lookup="auto" before it decides
+# IDs (token x table) from which the joined schedule runs the update as two
+# concurrent parts: below it the update is a few short launches whose split
+# costs the host more than it saves
+_SPLIT_MIN = 1 << 17
 
 
 class SparseStep:
     def __init__(self, workload, weights, states, n_tok_cap, device=None, lookup="auto",
-                 lookahead=1, autotune=None, schedule="joined", graph=False):
+                 lookahead=1, autotune=None, schedule="joined", graph=False,
+                 split_update="auto"):
         if lookup not in _LOOKUP_MODES:
             raise ValueError(f"lookup must be one of {_LOOKUP_MODES}, not {lookup!r}")
         if lookahead not in (1, 2, 3):
@@ -199,6 +211,8 @@ class SparseStep:
             raise ValueError("the prioritized schedule needs the index stages at least two "
                              "ahead (lookahead=2 or 3): the update of i starts from the classes "
                              "of i against i+1")
+        if split_update not in ("auto", True, False):
+            raise ValueError(f"split_update must be 'auto', True or False, not {split_update!r}")
         if graph and lookahead < 2:
             raise ValueError("graph replay needs the index stages ahead (lookahead=2 or 3): "
                              "a step's graph then holds no wait on work of the step before")
@@ -265,6 +279,10 @@ class SparseStep:
         self._record_only = False  # capturing without replaying
         self._forked = []  # streams forked from the capture stream
         self._cap_stream = torch.cuda.Stream(device=d) if graph else None
+        # the joined schedule's update as two concurrent parts (rows of at
+        # most 64 occurrences on the caller's stream, longer rows on stream B)
+        self.split_update = split_update
+        self._ev_fork, self._ev_join = torch.cuda.Event(), torch.cuda.Event()
 
     def _t(self, name, stream):
         """Context that brackets one C call with HIP events on its stream."""
@@ -281,16 +299,27 @@ class SparseStep:
         if not self._dry:
             fn(**kw)
 
-    def _fork(self, s, cs):
-        """Stream s waits for everything enqueued on cs so far."""
+    def _fork(self, s, cs, ev=None):
+        """Stream s waits for everything enqueued on cs so far (through event
+        ev when given: a reused event costs the host less than a new one)."""
         if self._capture is not None and s not in self._forked:
             self._forked.append(s)
-        if not self._dry:
+        if self._dry:
+            return
+        if ev is None:
             s.wait_stream(cs)
+        else:
+            ev.record(cs)
+            s.wait_event(ev)
 
-    def _join(self, cs, s):
-        if not self._dry:
+    def _join(self, cs, s, ev=None):
+        if self._dry:
+            return
+        if ev is None:
             cs.wait_stream(s)
+        else:
+            ev.record(s)
+            cs.wait_event(ev)
 
     def _wait(self, s, ev, st):
         """Stream s waits for event ev of iteration state st."""
@@ -406,15 +435,29 @@ class SparseStep:
         with self._t(f"lookup_{_CLS[which]}", stream):
             self._call(pl, n_tok=st.n_tok, stream=stream.cuda_stream)
 
-    def _run_update(self, st, grads, which, ws, stream, name=None):
+    def _run_update(self, st, grads, which, ws, stream, name=None, aux=None):
+        """The update of st's rows of class `which` on `stream`; with an `aux`
+        stream and a batch of at least _SPLIT_MIN IDs (or split_update=True),
+        its rows of more than 64 occurrences run on aux beside the rest (the
+        two parts touch disjoint rows; only the long rows use the workspace),
+        so that each stream has one launch boundary fewer and the parts' ramps
+        and tails overlap."""
         pu = self._prep(("upd", st.slot, which, id(ws)), lambda: lib.prepare_update(
             self.weights, self.states, self.W, st.uq, self.w.optim, self.w.lr, self.w.eps, which,
             st.cls_next, ws))
         g = pu.arrays["grads"]
         for t, x in enumerate(grads):
             g[t] = lib._ptr(x)
+        split = aux is not None and (self.split_update is True or (
+            self.split_update == "auto" and st.n_tok * self.T >= _SPLIT_MIN))
         with self._t(name or f"update_{_CLS[which]}", stream):
-            self._call(pu, n_tok=st.n_tok, stream=stream.cuda_stream)
+            if not split:
+                self._call(pu, n_tok=st.n_tok, rows=lib.FS_ROWS_ALL, stream=stream.cuda_stream)
+                return
+            self._fork(aux, stream, self._ev_fork)
+            self._call(pu, n_tok=st.n_tok, rows=lib.FS_ROWS_MANY, stream=aux.cuda_stream)
+            self._call(pu, n_tok=st.n_tok, rows=lib.FS_ROWS_FEW, stream=stream.cuda_stream)
+            self._join(stream, aux, self._ev_join)
 
     # ------------------------------------------------------------------ schedule
     def _nslots(self):
@@ -542,7 +585,7 @@ class SparseStep:
         nxt, aft_s = self._next_states(batch_next, batch_after, cs)
         # the update of i needs nothing from the index stages of i+1 (they
         # only read iteration i's unique rows), so only the lookup waits
-        self._run_update(cur, grads_cur, lib.FS_ALL, self.ws_red[1], cs)
+        self._run_update(cur, grads_cur, lib.FS_ALL, self.ws_red[1], cs, aux=self.sB)
         self._wait(cs, nxt.ev_done, nxt)
         self._lookup(nxt, lib.FS_ALL, cs)
         self._index_after(batch_after, nxt, aft_s)

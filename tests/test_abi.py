@@ -99,14 +99,17 @@ def test_noalloc_update_rejects_sizes_beyond_its_scratch(L):
     # 524 160 occurrences at 1024 columns fit; one more does not
     assert L.reduce_workspace_size(524_160, 1024) <= L.FS_NOALLOC_SCRATCH_BYTES
     assert L.reduce_workspace_size(524_161, 1024) > L.FS_NOALLOC_SCRATCH_BYTES
-    assert call(tabs, 1, 4, grads, 524_161, F, F, F, F, F, None, L.FS_ALL, L.FS_SGD, 0.1, 0.0,
+    assert call(tabs, 1, 4, grads, 524_161, F, F, F, F, F, None, L.FS_ALL, L.FS_ROWS_ALL, L.FS_SGD, 0.1, 0.0,
                 None, None) == L.FS_ERR_TOO_LARGE
-    assert call(tabs, 1, 4, grads, 1 << 25, F, F, F, F, F, None, L.FS_ALL, L.FS_SGD, 0.1, 0.0,
+    assert call(tabs, 1, 4, grads, 1 << 25, F, F, F, F, F, None, L.FS_ALL, L.FS_ROWS_ALL, L.FS_SGD, 0.1, 0.0,
                 None, None) == L.FS_ERR_TOO_LARGE
-    assert call(tabs, 1, 4, grads, 1000, F, F, F, F, F, None, 7, L.FS_SGD, 0.1, 0.0,
+    assert call(tabs, 1, 4, grads, 1000, F, F, F, F, F, None, 7, L.FS_ROWS_ALL, L.FS_SGD, 0.1, 0.0,
                 None, None) == L.FS_ERR_INVALID_ARG
-    assert call(tabs, 1, 4, grads, 1000, None, F, F, F, F, None, L.FS_ALL, L.FS_SGD, 0.1, 0.0,
+    assert call(tabs, 1, 4, grads, 1000, None, F, F, F, F, None, L.FS_ALL, L.FS_ROWS_ALL, L.FS_SGD, 0.1, 0.0,
                 None, None) == L.FS_ERR_INVALID_ARG
+    for rows in (0, 4, -1):  # the row parts are a mask of FS_ROWS_FEW and FS_ROWS_MANY
+        assert call(tabs, 1, 4, grads, 1000, F, F, F, F, F, None, L.FS_ALL, rows, L.FS_SGD, 0.1,
+                    0.0, None, None) == L.FS_ERR_INVALID_ARG
     assert L.strerror(L.FS_ERR_TOO_LARGE) != "unknown error"
 
 
@@ -186,13 +189,13 @@ def test_lookup_and_update_reject_unsupported_rows(L):
     grads = (C.c_void_p * 1)(FAKE)
     for dim in (96, 32, 2048):
         tab = _tables(L, [(1000, dim, L.FS_F32, True)])
-        assert ru(tab, 1, 4, grads, 10, FAKE, FAKE, FAKE, FAKE, FAKE, None, L.FS_ALL, L.FS_SGD,
-                  0.1, 0.0, None, FAKE, 1 << 30, None) == L.FS_ERR_UNSUPPORTED
+        assert ru(tab, 1, 4, grads, 10, FAKE, FAKE, FAKE, FAKE, FAKE, None, L.FS_ALL, L.FS_ROWS_ALL,
+                  L.FS_SGD, 0.1, 0.0, None, FAKE, 1 << 30, None) == L.FS_ERR_UNSUPPORTED
     tab = _tables(L, [(1000, 128, L.FS_F32, False)])  # Adagrad needs state
-    assert ru(tab, 1, 4, grads, 10, FAKE, FAKE, FAKE, FAKE, FAKE, None, L.FS_ALL,
+    assert ru(tab, 1, 4, grads, 10, FAKE, FAKE, FAKE, FAKE, FAKE, None, L.FS_ALL, L.FS_ROWS_ALL,
               L.FS_RW_ADAGRAD, 0.1, 0.0, None, FAKE, 1 << 30, None) == L.FS_ERR_INVALID_ARG
     tab = _tables(L, [(1000, 128, L.FS_F32, True)])
-    assert ru(tab, 1, 4, grads, 10, FAKE, FAKE, FAKE, FAKE, FAKE, None, L.FS_ALL,
+    assert ru(tab, 1, 4, grads, 10, FAKE, FAKE, FAKE, FAKE, FAKE, None, L.FS_ALL, L.FS_ROWS_ALL,
               L.FS_RW_ADAGRAD, 0.1, 0.0, None, FAKE, 8, None) == L.FS_ERR_WORKSPACE
 
 
@@ -212,7 +215,7 @@ def test_lookup_and_update_reject_bad_table_layouts(L):
         return lk(t, 1, 4, FAKE, FAKE, FAKE, FAKE, FAKE, None, L.FS_ALL, outs, 10, None)
 
     def upd(t, optim=None):
-        return ru(t, 1, 4, grads, 10, FAKE, FAKE, FAKE, FAKE, FAKE, None, L.FS_ALL,
+        return ru(t, 1, 4, grads, 10, FAKE, FAKE, FAKE, FAKE, FAKE, None, L.FS_ALL, L.FS_ROWS_ALL,
                   L.FS_RW_ADAGRAD if optim is None else optim, 0.1, 0.0, None, FAKE, 8, None)
     bad = L.FS_ERR_INVALID_ARG
     # bf16 x 128 = 256-byte rows
@@ -278,7 +281,10 @@ def test_prepared_calls_match_the_c_signatures(L, monkeypatch):
         assert len(p.args) == len(p.fn.argtypes), p.name
         for name, i in p.pos.items():
             assert 0 <= i < len(p.args), (p.name, name)
-            assert p.args[i] in (None, 0), (p.name, name)
+            if name == "rows":  # defaults to every row, right after the class filter
+                assert p.args[i] == L.FS_ROWS_ALL and p.args[i - 1] == L.FS_ALL, p.name
+            else:
+                assert p.args[i] in (None, 0), (p.name, name)
         assert p.pos["stream"] == len(p.args) - 1, p.name
 
 

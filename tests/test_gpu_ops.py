@@ -824,6 +824,66 @@ def test_reduce_update_parity(case, layout):
         assert torch.equal(b2.masked_fill(mine, 0), b1.masked_fill(mine, 0))
 
 
+@pytest.mark.parametrize("mode", ["concurrent", "many-first", "noalloc"])
+@pytest.mark.parametrize("case", [RU_CASES[i] for i in (0, 1, 2, 4, 7, 9)],
+                         ids=lambda c: f"D{c[0]}-{c[1]}-{c[2]}-{c[4]}")
+def test_update_row_parts_equal_whole(case, mode):
+    """The update in two parts -- rows of at most 64 occurrences
+    (FS_ROWS_FEW) and longer rows (FS_ROWS_MANY) -- gives the one-call
+    result bit for bit: rows, states and reduced sums, for every class
+    filter. "concurrent": the parts on two streams at once with one
+    workspace; "many-first": one stream, long rows first; "noalloc": the
+    allocation-free call, parts concurrent."""
+    dim, dt, optim, hot, n_tok, W, rows = case
+    say("update parts", case, mode)
+    b = _hot_batch(dim + n_tok, rows, n_tok, hot)
+    _, _, obk = _oracle_bucketize(b, [rows], W)
+    ouq = O.unique(obk["shard_keys"], obk["shard_bm"], [rows], W)
+    U = len(ouq["unique"])
+    dq = _csr_to_dev(ouq)
+    touched = cu(np.unique(b["ids"][0]))
+    dcls = cu((np.random.default_rng(2).random(U) < 0.5).astype(np.uint8))
+    grad = cu(synth.gradient_rows(8, 0, 0, np.arange(n_tok), dim))
+    ada = optim == "rw_adagrad"
+    outs = []
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    for split in (False, True):
+        wt = _table(rows, dim, dt, 9)
+        st = torch.full((rows,), 0.25, dtype=torch.float32, device="cuda") if ada else None
+        red = torch.full((U, dim), np.nan, dtype=torch.float32, device="cuda")
+        ws = torch.empty(lib.reduce_workspace_size(n_tok, dim), dtype=torch.uint8,
+                         device="cuda")
+        for which in (lib.FS_COLLISION, lib.FS_EXCLUSIVE, lib.FS_ALL):
+            kw = dict(which=which, cls=dcls if which != lib.FS_ALL else None, reduced_out=[red])
+
+            def call(rows_, stream):
+                if mode == "noalloc":
+                    lib.fs_grad_reduce_update_noalloc([wt], [st], W, [grad], n_tok, dq, optim,
+                                                      0.05, 1e-8, rows=rows_, stream=stream, **kw)
+                else:
+                    lib.fs_grad_reduce_update([wt], [st], W, [grad], n_tok, dq, optim, 0.05,
+                                              1e-8, ws=ws, rows=rows_, stream=stream, **kw)
+            torch.cuda.synchronize()
+            if not split:
+                call(lib.FS_ROWS_ALL, None)
+            elif mode == "many-first":
+                call(lib.FS_ROWS_MANY, None)
+                call(lib.FS_ROWS_FEW, None)
+            else:
+                call(lib.FS_ROWS_MANY, s2)
+                call(lib.FS_ROWS_FEW, s1)
+            torch.cuda.synchronize()
+        w_t = wt.index_select(0, touched)
+        outs.append((host(w_t.view(torch.int16)) if dt == "bf16" else host(w_t).view(np.uint32),
+                     host(st.index_select(0, touched)).view(np.uint32) if ada else None,
+                     host(red).view(np.uint32)))
+    (w0, s0, r0), (w1, s1_, r1) = outs
+    assert np.array_equal(w0, w1)
+    assert np.array_equal(r0, r1)  # bit patterns (rows of other classes hold NaN in both)
+    if ada:
+        assert np.array_equal(s0, s1_)
+
+
 def test_bucketize_repeated_sample_flags_shape():
     # perm holds in-range entries but repeats the longest sample: the
     # lengths under perm overrun n_tok, so the call must write no items
