@@ -279,6 +279,31 @@ int fs_unique_collision_split(const int64_t* shard_keys, const int32_t* shard_bm
 
 size_t fs_unique_workspace_size(int64_t n_cap, int64_t prev_cap, int32_t T, int32_t W);
 
+/* Collision split alone -- Algorithm 2's compute_collision on two dedup      */
+/* results, for a caller that deduplicates an iteration before the previous  */
+/* iteration's rows exist (fs_unique_collision_split with the three prev     */
+/* pointers NULL), so that consecutive dedups need not wait for each other.  */
+/* Together the two calls give exactly the outputs of one                     */
+/* fs_unique_collision_split call with the previous rows.                     */
+/*  unique, unique_offsets  a dedup call's outputs for T tables and W shards  */
+/*                 (rows of (t, d) in unique_offsets[t*W+d] .. [t*W+d+1]).    */
+/*  n_cap          host: capacity of unique and cls (the dedup call's n_cap). */
+/*  prev_unique, prev_unique_offsets, prev_counts, prev_cap: as in            */
+/*                 fs_unique_collision_split (all three NULL: every row       */
+/*                 exclusive).                                               */
+/*  cls            uint8 [U]: FS_COLLISION if the row is in prev_unique.      */
+/*  prev_cls       uint8 [prev U] (NULL when prev_unique is NULL).            */
+/*  counts         [4] int64, in/out: counts[0] = U as the dedup call wrote   */
+/*                 it (read); counts[1..3] = C, U - C, prev U - C (written).  */
+/*  ws, ws_bytes   at least fs_collision_split_workspace_size(n_cap, T, W).   */
+int fs_collision_split(const int64_t* unique, const int64_t* unique_offsets, int64_t n_cap,
+                       int32_t T, int32_t W, const int64_t* prev_unique,
+                       const int64_t* prev_unique_offsets, const int64_t* prev_counts,
+                       int64_t prev_cap, uint8_t* cls, uint8_t* prev_cls, int64_t* counts,
+                       void* ws, size_t ws_bytes, hipStream_t stream);
+
+size_t fs_collision_split_workspace_size(int64_t n_cap, int32_t T, int32_t W);
+
 /* ------------------------------------------------------------------------ */
 /* Jagged lookup -- Algorithm 2's Lookup, the batch-major transform that     */
 /* follows it, and merge: every occurrence of a unique row of class `which`  */

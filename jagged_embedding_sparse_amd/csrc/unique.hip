@@ -602,6 +602,10 @@ k_collide(const int64_t* __restrict__ a, const int64_t* __restrict__ a_off,
   for (int64_t c = s0; c < nchunks; c += S) {
     const int64_t i0 = a_lo + c * kCoChunk, i1 = min(i0 + kCoChunk, a_hi);
     const int na_c = (int)(i1 - i0);
+    if (!b) {  // no previous rows (uniform): every row exclusive
+      for (int x = threadIdx.x; x < na_c; x += kCoThreads) cls[i0 + x] = FS_EXCLUSIVE;
+      continue;
+    }
     // this chunk's previous rows: wave 0 finds where they start, wave 1
     // where they end (the first key of the next chunk)
     if (w < 2) {
@@ -697,6 +701,59 @@ static int64_t seg_tiles(int64_t cap, int32_t W) {
 static int32_t collide_splits(int64_t cap, int32_t T, int32_t W) {
   const int64_t s = cdiv(cap, (int64_t)T * W * kCoChunk * 4);
   return (int32_t)(s < 1 ? 1 : (s > 64 ? 64 : s));
+}
+
+// The collision split of new rows (unique, unique_offsets, counts[0] = U, at
+// most n_cap rows) against the previous call's rows (or none): classes of
+// both sets and counts[1..3]; block_hits holds T * W * collide_splits(...)
+// entries.
+static int launch_collide(const int64_t* unique, const int64_t* unique_offsets, int64_t n_cap,
+                          int32_t T, int32_t W, const int64_t* prev_unique,
+                          const int64_t* prev_unique_offsets, const int64_t* prev_counts,
+                          int64_t prev_cap, uint8_t* cls, uint8_t* prev_cls, int64_t* counts,
+                          uint32_t* block_hits, hipStream_t stream) {
+  const int64_t cap = n_cap > 0 ? n_cap : 1;
+  const int32_t co_split = collide_splits(cap, T, W);
+  const int64_t co_blocks = (int64_t)T * W * co_split;
+  hipLaunchKernelGGL(k_collide, dim3((unsigned)co_blocks), dim3(kCoThreads), 0, stream, unique,
+                     unique_offsets, counts, n_cap, prev_unique, prev_unique_offsets,
+                     prev_counts, prev_cap, co_split, cls, prev_cls, block_hits);
+  FS_LAUNCH_CHECK();
+  hipLaunchKernelGGL(k_collide_counts, dim3(1), dim3(kThreads), 0, stream, block_hits, co_blocks,
+                     prev_counts, prev_cap, counts);
+  FS_LAUNCH_CHECK();
+  return FS_OK;
+}
+
+extern "C" size_t fs_collision_split_workspace_size(int64_t n_cap, int32_t T, int32_t W) {
+  const int64_t cap = n_cap > 0 ? n_cap : 1;
+  const int32_t t = T > 0 ? T : 1, w = W > 0 ? W : 1;
+  Carve c(nullptr);
+  c.take<uint32_t>((size_t)t * w * collide_splits(cap, t, w));
+  return c.used + 256;
+}
+
+extern "C" int fs_collision_split(const int64_t* unique, const int64_t* unique_offsets,
+                                  int64_t n_cap, int32_t T, int32_t W,
+                                  const int64_t* prev_unique, const int64_t* prev_unique_offsets,
+                                  const int64_t* prev_counts, int64_t prev_cap, uint8_t* cls,
+                                  uint8_t* prev_cls, int64_t* counts, void* ws, size_t ws_bytes,
+                                  hipStream_t stream) {
+  if (n_cap < 0 || n_cap >= (int64_t)INT32_MAX || T < 1 || T > FS_MAX_TABLES || W < 1 ||
+      W > FS_MAX_RANKS || !unique_offsets || !counts)
+    return FS_ERR_INVALID_ARG;
+  if (n_cap > 0 && (!unique || !cls)) return FS_ERR_INVALID_ARG;
+  if ((prev_unique == nullptr) != (prev_counts == nullptr) ||
+      (prev_unique == nullptr) != (prev_unique_offsets == nullptr))
+    return FS_ERR_INVALID_ARG;
+  if (prev_unique && (prev_cap < 0 || !prev_cls)) return FS_ERR_INVALID_ARG;
+  if (!prev_unique) prev_cap = 0;
+  if (!ws || ws_bytes < fs_collision_split_workspace_size(n_cap, T, W)) return FS_ERR_WORKSPACE;
+  const int64_t cap = n_cap > 0 ? n_cap : 1;
+  Carve c(ws);
+  uint32_t* block_hits = c.take<uint32_t>((size_t)T * W * collide_splits(cap, T, W));
+  return launch_collide(unique, unique_offsets, n_cap, T, W, prev_unique, prev_unique_offsets,
+                        prev_counts, prev_cap, cls, prev_cls, counts, block_hits, stream);
 }
 
 extern "C" size_t fs_unique_workspace_size(int64_t n_cap, int64_t prev_cap, int32_t T,
@@ -870,12 +927,6 @@ extern "C" int fs_unique_collision_split(const int64_t* shard_keys, const int32_
   hipLaunchKernelGGL(k_compact, dim3(grid), dim3(kThreads), 0, stream, sk, n_valid, g,
                      tile_heads, counts, unique, seg_offsets, occ_uid, unique_offsets);
   FS_LAUNCH_CHECK();
-  hipLaunchKernelGGL(k_collide, dim3((unsigned)co_blocks), dim3(kCoThreads), 0, stream, unique,
-                     unique_offsets, counts, n_cap, prev_unique, prev_unique_offsets,
-                     prev_counts, prev_cap, co_split, cls, prev_cls, block_hits);
-  FS_LAUNCH_CHECK();
-  hipLaunchKernelGGL(k_collide_counts, dim3(1), dim3(kThreads), 0, stream, block_hits, co_blocks,
-                     prev_counts, prev_cap, counts);
-  FS_LAUNCH_CHECK();
-  return FS_OK;
+  return launch_collide(unique, unique_offsets, n_cap, T, W, prev_unique, prev_unique_offsets,
+                        prev_counts, prev_cap, cls, prev_cls, counts, block_hits, stream);
 }

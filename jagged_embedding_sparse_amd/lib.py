@@ -64,6 +64,9 @@ _c_bucketize_ws = _sig("fs_bucketize_workspace_size", _sz, _i64, _i32, _i32, _i3
 _c_unique = _sig("fs_unique_collision_split", C.c_int, _P, _P, _P, _i64, _TP, _i32, _i32, _P, _P,
                  _P, _i64, _P, _P, _P, _P, _P, _P, _P, _P, _P, _sz, _P)
 _c_unique_ws = _sig("fs_unique_workspace_size", _sz, _i64, _i64, _i32, _i32)
+_c_collide = _sig("fs_collision_split", C.c_int, _P, _P, _i64, _i32, _i32, _P, _P, _P, _i64, _P,
+                  _P, _P, _P, _sz, _P)
+_c_collide_ws = _sig("fs_collision_split_workspace_size", _sz, _i64, _i32, _i32)
 _c_lookup = _sig("fs_jagged_lookup", C.c_int, _TP, _i32, _i32, _P, _P, _P, _P, _P, _P, _i32,
                  C.POINTER(_P), _i64, _P)
 _c_combine = _sig("fs_ranged_combine", C.c_int, _P, _i64, _P, _P, _P, _i32, _TP, _i32,
@@ -83,7 +86,8 @@ _c_version = _sig("fs_version", C.c_int)
 EXPORTED = ["fs_balance_fbs", "fs_balance_vbs", "fs_balance_workspace_size",
             "fs_balance_vbs_shares", "fs_rank_cost", "fs_vbs_autotune",
             "fs_bucketize_permute", "fs_bucketize_workspace_size", "fs_unique_collision_split",
-            "fs_unique_workspace_size", "fs_jagged_lookup", "fs_ranged_combine",
+            "fs_unique_workspace_size", "fs_collision_split", "fs_collision_split_workspace_size",
+            "fs_jagged_lookup", "fs_ranged_combine",
             "fs_keyed_transpose", "fs_keyed_transpose_workspace_size",
             "fs_grad_reduce_update", "fs_grad_reduce_update_noalloc",
             "fs_grad_reduce_update_workspace_size", "fs_strerror", "fs_version"]
@@ -326,6 +330,29 @@ def fs_unique_collision_split(shard_keys, shard_bm, shard_offsets, n_cap, rows, 
                 cls=cls, prev_cls=pcls, counts=counts)
 
 
+def collision_workspace_size(n_cap, T, W):
+    return int(_c_collide_ws(n_cap, T, W))
+
+
+def fs_collision_split(uq, n_cap, T, W, prev_unique=None, prev_unique_offsets=None,
+                       prev_counts=None, prev_cap=0, prev_cls=None, ws=None, stream=None):
+    """The collision split alone on a dedup call's outputs `uq` (its cls and
+    counts are rewritten; counts[0] is read). Returns prev_cls (allocated
+    when not given and there are previous rows)."""
+    d = _dev()
+    has = prev_unique is not None
+    if has and prev_cls is None:
+        prev_cls = torch.empty(max(int(prev_cap), 1), dtype=torch.uint8, device=d)
+    ws = _ws(collision_workspace_size(n_cap, T, W), ws)
+    _check("fs_collision_split",
+           _c_collide(_ptr(uq["unique"]), _ptr(uq["unique_offsets"]), int(n_cap), T, W,
+                      _ptr(prev_unique), _ptr(prev_unique_offsets), _ptr(prev_counts),
+                      int(prev_cap) if has else 0, _ptr(uq["cls"]),
+                      _ptr(prev_cls) if has else None, _ptr(uq["counts"]), _ptr(ws), ws.numel(),
+                      _stream(stream)))
+    return prev_cls
+
+
 def _ptr_array(ts):
     arr = (C.c_void_p * len(ts))()
     for i, t in enumerate(ts):
@@ -518,6 +545,18 @@ def prepare_unique(bucket, rows, W, uq, prev_uq, prev_cls, ws):
             _ptr(uq["counts"]), _ptr(ws), ws.numel(), None]
     return Prepared("fs_unique_collision_split", _c_unique, args,
                     dict(n_cap=3, prev_cap=10, stream=21))
+
+
+def prepare_collision(uq, T, W, prev_uq, prev_cls, ws):
+    """fs_collision_split of the dedup result `uq` against `prev_uq` (None:
+    every row exclusive); call with n_cap=, prev_cap=, stream=."""
+    has = prev_uq is not None
+    args = [_ptr(uq["unique"]), _ptr(uq["unique_offsets"]), 0, T, W,
+            _ptr(prev_uq["unique"]) if has else None,
+            _ptr(prev_uq["unique_offsets"]) if has else None,
+            _ptr(prev_uq["counts"]) if has else None, 0, _ptr(uq["cls"]),
+            _ptr(prev_cls) if has else None, _ptr(uq["counts"]), _ptr(ws), ws.numel(), None]
+    return Prepared("fs_collision_split", _c_collide, args, dict(n_cap=2, prev_cap=8, stream=14))
 
 
 def prepare_lookup(weights, W, uq, out, which=FS_ALL, cls=None):

@@ -41,13 +41,13 @@ updated, i+1 looked up, i+2 indexed); the result is again the synchronous
 loop's.
 
 With `lookahead=3` the index stages run three iterations ahead on two index
-streams taken in turn, so that the balance and bucketize of i+3 overlap the
-dedup of i+2: only the dedup (its collision split reads the previous
-iteration's unique rows, and the dedup workspace is shared) waits for the one
-before it. Where the index stages are a chain of latency-bound launches
-longer than the update and the lookup, a step then costs about one dedup
-instead of a whole index chain. Each index stream has its own balance and
-bucketize workspace; four iteration states are alive at once.
+streams taken in turn, each with its own workspaces, so that one iteration's
+index stages overlap the previous iteration's: the dedup runs as a call of
+its own (every row exclusive) and only the collision split after it, which
+reads the previous iteration's unique rows, waits for the previous dedup.
+Where the index stages are a chain of latency-bound launches longer than the
+update and the lookup, a step then costs about one collision split instead
+of a whole index chain. Four iteration states are alive at once.
 
 With the index stages ahead (joined lookup) and a batch of at least 2^17
 IDs, the update runs as two concurrent parts: its rows of at most 64
@@ -179,7 +179,8 @@ class IterState:
     cls_next: torch.Tensor = None  # class of this iteration's rows vs the next one
     out: list = field(default_factory=list)  # lookup output per table
     idx_x: int = 0  # index stream that ran this iteration's index stages
-    ev_done: torch.cuda.Event = None  # index stages done (after the dedup)
+    ev_uq: torch.cuda.Event = None  # dedup done (unique rows and counts[0] ready)
+    ev_done: torch.cuda.Event = None  # index stages done (after the collision split)
     ev_bal: torch.cuda.Event = None  # balance (and AutoTune's share update) done
     graph: object = None  # the step graph whose capture indexed this iteration (graph mode)
 
@@ -238,8 +239,12 @@ class SparseStep:
                        for _ in range(n_idx)]
         self.ws_bkt = [torch.empty(lib.bucketize_workspace_size(cap, N, T, W), dtype=torch.uint8,
                                    device=d) for _ in range(n_idx)]
-        self.ws_uq = torch.empty(lib.unique_workspace_size(ncap, T, W), dtype=torch.uint8,
-                                 device=d)
+        # dedup and collision split per index stream: consecutive dedups run
+        # side by side, only the collision splits wait for the previous dedup
+        self.ws_uq = [torch.empty(lib.unique_workspace_size(ncap, T, W), dtype=torch.uint8,
+                                  device=d) for _ in range(n_idx)]
+        self.ws_co = [torch.empty(lib.collision_workspace_size(ncap, T, W), dtype=torch.uint8,
+                                  device=d) for _ in range(n_idx)]
         rws = lib.reduce_workspace_size(cap, max(self.dims), T)
         self.ws_red = [torch.empty(rws, dtype=torch.uint8, device=d) for _ in range(2)]
         self.lookahead = lookahead
@@ -355,6 +360,7 @@ class SparseStep:
             cls=torch.empty(ncap, dtype=torch.uint8, device=d),
             counts=torch.empty(4, dtype=torch.int64, device=d))
         st.cls_next = torch.empty(ncap, dtype=torch.uint8, device=d)
+        st.ev_uq = torch.cuda.Event()
         st.ev_done = torch.cuda.Event()
         st.ev_bal = torch.cuda.Event()
         st.out = [torch.empty((self.cap, D), dtype=w.dtype, device=d)
@@ -377,11 +383,12 @@ class SparseStep:
         return x, self.s_idx[x]
 
     def _index_stages(self, batch, st, prev, stream, x=0):
-        """balance + bucketize + split of `batch` (device dict) into st, on
-        index stream `x` (`stream`). The split waits for the previous
-        iteration's index stages when another stream ran them (it reads that
-        iteration's unique rows and shares the dedup workspace), and with
-        AutoTune the balance waits for the previous share update."""
+        """balance + bucketize + dedup + collision split of `batch` (device
+        dict) into st, on index stream `x` (`stream`). Each index stream has
+        its own workspaces; only the collision split waits for the previous
+        iteration's dedup when another stream ran it (it reads that
+        iteration's unique rows), and with AutoTune the balance waits for the
+        previous share update."""
         W, T = self.W, self.T
         other = prev is not None and prev.idx_x != x
         st.idx_x = x
@@ -405,11 +412,11 @@ class SparseStep:
                 self.rank_cost, self.shares, at["step"], at["tol"], self.err))
         pk = self._prep(("bkt", st.slot, x), lambda: lib.prepare_bucketize(
             self.rows, st.perm, st.rank_offsets, W, st.bucket, self.err, self.ws_bkt[x]))
-        pu = self._prep(("uq", st.slot, prev.slot if prev is not None else -1),
-                        lambda: lib.prepare_unique(
-                            st.bucket, self.rows, W, st.uq,
-                            prev.uq if prev is not None else None,
-                            prev.cls_next if prev is not None else None, self.ws_uq))
+        pu = self._prep(("uq", st.slot, x), lambda: lib.prepare_unique(
+            st.bucket, self.rows, W, st.uq, None, None, self.ws_uq[x]))
+        pco = None if prev is None else self._prep(
+            ("co", st.slot, prev.slot, x), lambda: lib.prepare_collision(
+                st.uq, T, W, prev.uq, prev.cls_next, self.ws_co[x]))
         if at is not None and other:  # the shares the previous balance left
             self._wait(stream, prev.ev_bal, prev)
         with self._t("balance", stream):
@@ -422,11 +429,15 @@ class SparseStep:
         with self._t("bucketize", stream):
             self._call(pk, ids=lib._ptr(ids), n_tok=n_tok, so=lib._ptr(so), n=so.numel() - 1,
                        stream=sh)
-        if other:
-            self._wait(stream, prev.ev_done, prev)
-        with self._t("unique_split", stream):
-            self._call(pu, n_cap=T * n_tok,
-                       prev_cap=T * prev.n_tok if prev is not None else 0, stream=sh)
+        # the dedup alone (every row exclusive until the split below)
+        with self._t("dedup", stream):
+            self._call(pu, n_cap=T * n_tok, prev_cap=0, stream=sh)
+        self._record(st.ev_uq, stream, st)
+        if pco is not None:
+            if other:
+                self._wait(stream, prev.ev_uq, prev)
+            with self._t("collision", stream):
+                self._call(pco, n_cap=T * n_tok, prev_cap=T * prev.n_tok, stream=sh)
         self._record(st.ev_done, stream, st)
 
     def _lookup(self, st, which, stream):

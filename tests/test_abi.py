@@ -199,6 +199,35 @@ def test_lookup_and_update_reject_unsupported_rows(L):
               L.FS_RW_ADAGRAD, 0.1, 0.0, None, FAKE, 8, None) == L.FS_ERR_WORKSPACE
 
 
+def test_collision_split_rejects(L):
+    """The standalone collision split validates on the host: sizes, the
+    three previous-row pointers together, prev_cls with previous rows, and
+    its workspace."""
+    f = L._c_collide
+    ws_need = L.collision_workspace_size(1000, 2, 8)
+    names = ["unique", "unique_offsets", "n_cap", "T", "W", "prev_unique", "prev_off",
+             "prev_counts", "prev_cap", "cls", "prev_cls", "counts", "ws", "ws_bytes", "stream"]
+    ok = [FAKE, FAKE, 1000, 2, 8, None, None, None, 0, FAKE, None, FAKE, FAKE, ws_need, None]
+
+    def call(**kw):
+        a = list(ok)
+        for k, v in kw.items():
+            a[names.index(k)] = v
+        return f(*a)
+    bad = L.FS_ERR_INVALID_ARG
+    assert call(counts=None) == bad
+    assert call(unique_offsets=None) == bad
+    assert call(cls=None) == bad
+    assert call(n_cap=-1) == bad
+    assert call(T=0) == bad and call(T=L.FS_MAX_TABLES + 1) == bad
+    assert call(W=0) == bad and call(W=L.FS_MAX_RANKS + 1) == bad
+    assert call(prev_unique=FAKE) == bad  # without its offsets and counts
+    assert call(prev_unique=FAKE, prev_off=FAKE, prev_counts=FAKE, prev_cap=10) == bad
+    assert call(ws_bytes=ws_need - 1) == L.FS_ERR_WORKSPACE
+    assert call(ws=None) == L.FS_ERR_WORKSPACE
+    assert L.collision_workspace_size(1 << 20, 2, 8) >= ws_need
+
+
 def test_lookup_and_update_reject_bad_table_layouts(L):
     """Row strides and in-row states: checked on the host before any launch."""
     lk, ru = L._c_lookup, L._c_reduce
@@ -273,6 +302,8 @@ def test_prepared_calls_match_the_c_signatures(L, monkeypatch):
         L.prepare_lookup(weights, 4, uq, [t, t]),
         L.prepare_lookup(weights, 4, uq, [t, t], L.FS_COLLISION, t),
         L.prepare_update(weights, [t, t], 4, uq, "rw_adagrad", 0.1, 1e-8, L.FS_ALL, None, ws),
+        L.prepare_collision(uq, 2, 4, None, None, ws),
+        L.prepare_collision(uq, 2, 4, uq, t, ws),
         L.prepare_balance_shares(4, (3, 2), t, t, t, t, t, ws),
         L.prepare_rank_cost(t, torch.zeros(5), (1, 64, 0), t),
         L.prepare_autotune(t, t, (1, 16), (1, 50), t),

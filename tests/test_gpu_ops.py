@@ -566,6 +566,40 @@ def test_unique_collision_parity(case):
         prev, oprev, prev_cap = uq, ouq, n_cap
 
 
+@pytest.mark.parametrize("case", UQ_CASES, ids=lambda c: f"s{c[0]}")
+def test_dedup_then_collision_split_equals_one_call(case):
+    """A dedup call without previous rows followed by fs_collision_split
+    gives every output of one fs_unique_collision_split call with the
+    previous rows, bit for bit (three consecutive batches, the last
+    identical to the one before)."""
+    seed, N, rows, W, maxlen = case
+    T = len(rows)
+    prev_one, prev_two, prev_cap = None, None, 0
+    for it in range(3):
+        say("dedup + split", case, it)
+        b = _tiny_batch(seed * 10 + (1 if it == 2 else it), N, rows, maxlen,
+                        bad=2 if it >= 1 else 0)
+        _, _, bk, _ = _gpu_bucketize(b, rows, W)
+        n_cap = T * b["n_tok"]
+        one = _gpu_unique(bk, rows, W, n_cap, prev_one, prev_cap)
+        two = _gpu_unique(bk, rows, W, n_cap)  # every row exclusive
+        pcls = lib.fs_collision_split(
+            two, n_cap, T, W, prev_unique=prev_two["unique"] if prev_two else None,
+            prev_unique_offsets=prev_two["unique_offsets"] if prev_two else None,
+            prev_counts=prev_two["counts"] if prev_two else None, prev_cap=prev_cap)
+        torch.cuda.synchronize()
+        U = int(host(one["counts"])[0])
+        n = int(host(bk["shard_offsets"])[-1])
+        assert np.array_equal(host(one["counts"]), host(two["counts"]))
+        for k, m in (("unique", U), ("unique_offsets", T * W + 1), ("seg_offsets", U + 1),
+                     ("occ_bm", n), ("occ_uid", n), ("cls", U)):
+            assert np.array_equal(host(one[k])[:m], host(two[k])[:m]), k
+        if prev_one is not None:
+            pu = int(host(prev_one["counts"])[0])
+            assert np.array_equal(host(one["prev_cls"])[:pu], host(pcls)[:pu])
+        prev_one, prev_two, prev_cap = one, two, n_cap
+
+
 @pytest.mark.parametrize("W,rows", [(1, [2_000_000]), (3, [300_000, 1_000_000])],
                          ids=["W1", "W3-2tables"])
 def test_collision_uneven_batches(W, rows):
