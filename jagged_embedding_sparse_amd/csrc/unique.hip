@@ -452,7 +452,7 @@ k_heads(const uint32_t* __restrict__ sk, const int64_t* __restrict__ nvp, int32_
 }
 
 __global__ void __launch_bounds__(kThreads)
-k_heads_scan(const int64_t* __restrict__ nvp, int32_t W, int32_t n_groups,
+k_heads_scan(const int64_t* __restrict__ nvp, int32_t W, int32_t n_groups, int32_t no_prev,
              uint32_t* __restrict__ tile_heads, int64_t* __restrict__ counts,
              int32_t* __restrict__ seg_offsets, int64_t* __restrict__ unique_offsets) {
   __shared__ int64_t tmp[17];
@@ -483,7 +483,7 @@ k_heads_scan(const int64_t* __restrict__ nvp, int32_t W, int32_t n_groups,
   if (threadIdx.x == 0) {
     counts[0] = carry;  // U
     counts[1] = 0;
-    counts[2] = 0;
+    counts[2] = no_prev ? carry : 0;  // without previous rows every row is exclusive
     counts[3] = 0;
     seg_offsets[carry] = (int32_t)n;
   }
@@ -499,7 +499,8 @@ __global__ void __launch_bounds__(kThreads)
 k_compact(const uint32_t* __restrict__ sk, const int64_t* __restrict__ nvp, Groups g,
           const uint32_t* __restrict__ tile_base, const int64_t* __restrict__ counts,
           int64_t* __restrict__ unique, int32_t* __restrict__ seg_offsets,
-          int32_t* __restrict__ occ_uid, int64_t* __restrict__ unique_offsets) {
+          int32_t* __restrict__ occ_uid, int64_t* __restrict__ unique_offsets,
+          uint8_t* __restrict__ cls_exclusive) {
   __shared__ uint32_t wave_heads[kThreads / kWave];
   const int64_t n = n_valid_of(nvp, g.W);
   const int64_t t0 = (int64_t)blockIdx.x * kTile;
@@ -538,6 +539,7 @@ k_compact(const uint32_t* __restrict__ sk, const int64_t* __restrict__ nvp, Grou
       if ((hm[i] >> l) & 1ull) {
         unique[uid] = (int64_t)k[i];
         seg_offsets[uid] = (int32_t)x;
+        if (cls_exclusive) cls_exclusive[uid] = FS_EXCLUSIVE;  // no previous rows
         // every group in (group(previous unique), group(this)] starts here
         const int32_t gi = group_of(k[i], g);
         const int32_t gp = uid == 0 ? -1 : group_of(prevk[i], g);
@@ -921,12 +923,17 @@ extern "C" int fs_unique_collision_split(const int64_t* shard_keys, const int32_
   hipLaunchKernelGGL(k_heads, dim3(grid), dim3(kThreads), 0, stream, sk, n_valid, W,
                      tile_heads);
   FS_LAUNCH_CHECK();
-  hipLaunchKernelGGL(k_heads_scan, dim3(1), dim3(kThreads), 0, stream, n_valid, W, T * W,
+  // without previous rows the classes and counts come from the compaction
+  // (every row exclusive) and the collision kernels are not launched
+  const int32_t no_prev = prev_unique == nullptr;
+  hipLaunchKernelGGL(k_heads_scan, dim3(1), dim3(kThreads), 0, stream, n_valid, W, T * W, no_prev,
                      tile_heads, counts, seg_offsets, unique_offsets);
   FS_LAUNCH_CHECK();
   hipLaunchKernelGGL(k_compact, dim3(grid), dim3(kThreads), 0, stream, sk, n_valid, g,
-                     tile_heads, counts, unique, seg_offsets, occ_uid, unique_offsets);
+                     tile_heads, counts, unique, seg_offsets, occ_uid, unique_offsets,
+                     no_prev ? cls : (uint8_t*)nullptr);
   FS_LAUNCH_CHECK();
+  if (no_prev) return FS_OK;
   return launch_collide(unique, unique_offsets, n_cap, T, W, prev_unique, prev_unique_offsets,
                         prev_counts, prev_cap, cls, prev_cls, counts, block_hits, stream);
 }

@@ -288,6 +288,9 @@ class SparseStep:
         # most 64 occurrences on the caller's stream, longer rows on stream B)
         self.split_update = split_update
         self._ev_fork, self._ev_join = torch.cuda.Event(), torch.cuda.Event()
+        # one reused fork event per index stream (a new event per wait costs
+        # the host more)
+        self._ev_idx = [torch.cuda.Event() for _ in self.s_idx]
 
     def _t(self, name, stream):
         """Context that brackets one C call with HIP events on its stream."""
@@ -568,13 +571,13 @@ class SparseStep:
         if not self._ahead:  # iteration i+1 was not indexed ahead: index it now
             nxt = self.states_buf[(self.slot + 1) % n]
             x, s_ = self._index_stream()
-            self._fork(s_, cs)
+            self._fork(s_, cs, self._ev_idx[x])
             self._index_stages(batch_next, nxt, cur, s_, x)
         else:
             nxt = self._ahead.popleft()
         if batch_after is not None:
             x, s_ = self._index_stream()
-            self._fork(s_, cs)
+            self._fork(s_, cs, self._ev_idx[x])
             aft_s = (x, s_)
         return nxt, aft_s
 
