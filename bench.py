@@ -66,7 +66,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-per-config", action="store_true",
                     help="only the headline workload (profiling runs)")
-    ap.add_argument("--per-config-steps", type=int, default=20)
+    ap.add_argument("--per-config-steps", type=int, default=30)
     ap.add_argument("--entry", action="store_true",
                     help="print only this workload's per-config entry (one JSON line); the "
                          "headline run starts one such process per other workload")
@@ -521,8 +521,8 @@ def main():
                 continue
             cmd = [sys.executable, os.path.abspath(__file__), "--entry", "--config", str(k),
                    "--balancer", wk.balancer, "--steps", str(args.per_config_steps),
-                   "--warmup", "3", "--schedule", args.schedule, "--lookup", args.lookup,
-                   "--lookahead", str(args.lookahead)]
+                   "--warmup", str(args.warmup), "--schedule", args.schedule,
+                   "--lookup", args.lookup, "--lookahead", str(args.lookahead)]
             r = subprocess.run(cmd, stdout=subprocess.PIPE, text=True, timeout=300)
             if r.returncode != 0:
                 raise RuntimeError(f"per-config run of workload {k} failed ({r.returncode})")
