@@ -72,10 +72,11 @@ def parse():
                          "headline run starts one such process per other workload")
     ap.add_argument("--sync", action="store_true",
                     help="one-stream synchronous schedule (analysis: isolated kernel times)")
-    ap.add_argument("--schedule", choices=["joined", "prioritized"], default="joined",
+    ap.add_argument("--schedule", choices=["joined", "prioritized", "serial"], default="joined",
                     help="with --lookahead 2: every row updated, then every row looked up "
                          "(joined), or collision rows updated and looked up first with the "
-                         "exclusive rows beside them (prioritized)")
+                         "exclusive rows beside them (prioritized); serial: every stage on one "
+                         "stream, one iteration at a time")
     ap.add_argument("--lookup", choices=["auto", "split", "joined"], default="auto",
                     help="with --lookahead 1: exclusive-row lookup ahead of the update (split), "
                          "one lookup after it (joined), or chosen from the first steps' timing "
@@ -180,9 +181,9 @@ def measure(ctx, steps, warmup, args, full):
     from jagged_embedding_sparse_amd.step import SparseStep, StageTimer
     w, NB, n_tok, grads_dev = ctx.w, len(ctx.dev_batches), ctx.n_tok, ctx.grads_dev
     dev_batches = ctx.dev_batches
-    L = 1 if args.sync else args.lookahead
+    L = 1 if (args.sync or args.schedule == "serial") else args.lookahead
     ahead = L >= 2
-    sched = args.schedule if ahead else "joined"
+    sched = args.schedule if (ahead or args.schedule == "serial") else "joined"
     graph = args.graph == "on" and ahead and not args.sync
     step = SparseStep(w, ctx.weights, ctx.states, ctx.cap, lookup=args.lookup,
                       lookahead=L, autotune={} if args.autotune else None, schedule=sched,
@@ -265,6 +266,8 @@ def measure(ctx, steps, warmup, args, full):
         step.set_graph(True)
     if args.sync:
         schedule = "sync"
+    elif sched == "serial":
+        schedule = "serial (every stage on the caller's stream)"
     elif ahead:
         far = {2: "index two ahead", 3: "index three ahead on two index streams"}[L]
         schedule = (f"{far}, prioritized (collision rows first)" if sched == "prioritized"
@@ -303,7 +306,7 @@ def measure(ctx, steps, warmup, args, full):
         # microseconds): with the index stages two ahead the caller's stream,
         # whose lookup waits for the index stream; otherwise stream A, whose
         # last lookup waits for the update (and with --sync runs everything).
-        end_stream = torch.cuda.current_stream() if ahead else step.sA
+        end_stream = torch.cuda.current_stream() if (ahead or sched == "serial") else step.sA
         evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
         for e in evs:  # first records take fresh runtime resources: not in the loop
             e.record(end_stream)

@@ -186,7 +186,7 @@ class IterState:
 
 
 _LOOKUP_MODES = ("split", "joined", "auto")
-_SCHEDULES = ("joined", "prioritized")
+_SCHEDULES = ("joined", "prioritized", "serial")
 # VBS AutoTune: modelled time c2 L^2 + c1 L + c0 per sample (coef), shares
 # moved by max(1, share * step) outside a band of +-tol around the mean time,
 # every share starting at init
@@ -212,6 +212,9 @@ class SparseStep:
             raise ValueError("the prioritized schedule needs the index stages at least two "
                              "ahead (lookahead=2 or 3): the update of i starts from the classes "
                              "of i against i+1")
+        if schedule == "serial" and (lookahead != 1 or graph):
+            raise ValueError("the serial schedule runs every stage on the caller's stream, one "
+                             "iteration at a time (lookahead=1, no graph)")
         if split_update not in ("auto", True, False):
             raise ValueError(f"split_update must be 'auto', True or False, not {split_update!r}")
         if graph and lookahead < 2:
@@ -337,7 +340,7 @@ class SparseStep:
 
     def _record(self, ev, s, st):
         st.graph = self._capture
-        if not self._dry:
+        if not self._dry and self.schedule != "serial":  # serial: no other stream waits
             ev.record(s)
 
     def _alloc_iter(self):
@@ -486,6 +489,8 @@ class SparseStep:
         for s_ in self.s_idx:
             s_.wait_stream(cs)
         x, s0 = self._index_stream()
+        if self.schedule == "serial":
+            s0 = cs
         self._index_stages(batch, st, None, s0, x)
         self._lookup(st, lib.FS_ALL, s0)
         self.cur = st
@@ -521,6 +526,8 @@ class SparseStep:
         with lookahead L >= 2, index `batch_after`, iteration i+L)."""
         if self.graph:
             return self._step_graph(batch_next, grads_cur, batch_after)
+        if self.schedule == "serial":
+            return self._step_serial(batch_next, grads_cur)
         if self.schedule == "prioritized":
             return self._step_prioritized(batch_next, grads_cur, batch_after)
         if self.lookahead >= 2:
@@ -718,6 +725,19 @@ class SparseStep:
                 st.idx_x, st.n_tok, st.graph = x, n, g
         return len(self._graphs)
 
+    def _step_serial(self, batch_next, grads_cur):
+        # every stage on the caller's stream in the loop's order: no events
+        # and no stream waits, whose host cost sets the pace of small batches
+        cur = self.cur
+        nxt = self.states_buf[(self.slot + 1) % self._nslots()]
+        cs = torch.cuda.current_stream()
+        self._index_stages(batch_next, nxt, cur, cs, 0)
+        self._run_update(cur, grads_cur, lib.FS_ALL, self.ws_red[0], cs)
+        self._lookup(nxt, lib.FS_ALL, cs)
+        self.cur = nxt
+        self.slot = (self.slot + 1) % self._nslots()
+        return nxt
+
     def step_sync(self, batch_next, grads_cur):
         """Reference schedule on one stream: update all of i, then look up all of i+1."""
         if self._ahead:
@@ -737,6 +757,10 @@ class SparseStep:
     def epilogue(self, grads_last):
         """Update of the last iteration (no lookahead: every row exclusive)."""
         cur = self.cur
+        if self.schedule == "serial":
+            self._run_update(cur, grads_last, lib.FS_ALL, self.ws_red[0],
+                             torch.cuda.current_stream())
+            return
         self.sA.wait_stream(torch.cuda.current_stream())
         self.sA.wait_stream(self.sB)
         self._run_update(cur, grads_last, lib.FS_ALL, self.ws_red[0], self.sA)

@@ -281,8 +281,9 @@ def test_call_limits_full_step():
 def test_prioritized_equals_synchronous(k):
     """Two-stream schedules (exclusive-row lookup ahead of the update, one
     lookup after it, the timed choice between them, index stages two
-    iterations ahead, and Algorithm 2's split of update and lookup by class)
-    == one-stream synchronous, bit for bit.
+    iterations ahead, Algorithm 2's split of update and lookup by class, and
+    the serial schedule on the caller's stream) == one-stream synchronous,
+    bit for bit.
     The synchronous run comes first and fixes the gradients; the two-stream
     runs then go through all steps without a host synchronisation, copying
     each lookup on the caller's stream, so the streams really overlap."""
@@ -295,14 +296,16 @@ def test_prioritized_equals_synchronous(k):
     runs = []
     grads = []
     for mode in ("sync", "split", "joined", "auto", "ahead", "prioritized", "ahead3",
-                 "prioritized3"):
+                 "prioritized3", "serial"):
         say("schedule", k, mode)
         weights, states = gpu_tables(w, 50 + k)
         L = 3 if mode.endswith("3") else (2 if mode in ("ahead", "prioritized") else 1)
         ahead = L >= 2
         step = SparseStep(w, weights, states, cap,
-                          lookup="split" if (mode == "sync" or ahead) else mode, lookahead=L,
-                          schedule="prioritized" if mode.startswith("prioritized") else "joined")
+                          lookup="split" if (mode in ("sync", "serial") or ahead) else mode,
+                          lookahead=L,
+                          schedule="prioritized" if mode.startswith("prioritized") else
+                          ("serial" if mode == "serial" else "joined"))
         st = step.prologue(dev_b[0], batch_after=dev_b[1:L] if ahead else None)
         step.join()
         looks = [[o[:st.n_tok].clone() for o in st.out]]
