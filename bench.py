@@ -1,14 +1,17 @@
 """Benchmark of the prioritized jagged sparse step on one MI355X.
 
 A step is one pass of the whole hot path over one batch. Default schedule
-(--lookahead 3): on the caller's stream the update of every unique row of
-iteration i (segment-reduce + optimizer), then the lookup of every row of
-iteration i+1; beside them, on two index streams taken in turn, balance (FBS
-or VBS), indexed permute + shard bucketize and dedup + collision split of
-iteration i+3 (its balance and bucketize overlapping the dedup of i+2;
---lookahead 2: one index stream, iteration i+2). --schedule prioritized splits update and lookup by class as the pages'
-Algorithm 2 does (collision rows updated, then looked up, on the caller's
-stream; exclusive rows of both iterations on two more streams).
+(--schedule auto, --lookahead 3): on the caller's stream the update of every
+unique row of iteration i (segment-reduce + optimizer; from 2^17 IDs its rows
+of more than 64 occurrences on a second stream beside the rest), then the
+lookup of every row of iteration i+1; beside them, on two index streams taken
+in turn, balance (FBS or VBS), indexed permute + shard bucketize, dedup and
+collision split of iteration i+3 (only the split waits for the dedup of i+2;
+--lookahead 2: one index stream, iteration i+2). Batches of at most 8192 IDs
+run the serial schedule instead (every stage on the caller's stream, no
+events). --schedule prioritized splits update and lookup by class as the
+pages' Algorithm 2 does (collision rows updated, then looked up, on the
+caller's stream; exclusive rows of both iterations on two more streams).
 --lookahead 1 runs the index stages one iteration ahead instead, with the
 exclusive rows' lookup ahead of the update where that pays (--lookup);
 --sync runs everything on one stream in the order index, update, lookup.
@@ -72,11 +75,13 @@ def parse():
                          "headline run starts one such process per other workload")
     ap.add_argument("--sync", action="store_true",
                     help="one-stream synchronous schedule (analysis: isolated kernel times)")
-    ap.add_argument("--schedule", choices=["joined", "prioritized", "serial"], default="joined",
-                    help="with --lookahead 2: every row updated, then every row looked up "
+    ap.add_argument("--schedule", choices=["auto", "joined", "prioritized", "serial"],
+                    default="auto",
+                    help="with --lookahead 2 or 3: every row updated, then every row looked up "
                          "(joined), or collision rows updated and looked up first with the "
                          "exclusive rows beside them (prioritized); serial: every stage on one "
-                         "stream, one iteration at a time")
+                         "stream, one iteration at a time; auto: serial for batches of at most "
+                         "8192 IDs, else joined")
     ap.add_argument("--lookup", choices=["auto", "split", "joined"], default="auto",
                     help="with --lookahead 1: exclusive-row lookup ahead of the update (split), "
                          "one lookup after it (joined), or chosen from the first steps' timing "
@@ -97,6 +102,14 @@ def parse():
                     help="VBS AutoTune: shares of the weight moved every step by the modelled "
                          "per-rank time (VBS workloads only)")
     return ap.parse_args()
+
+
+# batches of at most this many IDs (token x table) run the serial schedule
+# under --schedule auto: with a few thousand IDs a step is a chain of short
+# launches, and the host's cost of cross-stream events exceeds what overlap
+# gains (workload 1: 0.125 against 0.140 ms/step; workload 2, 25 K IDs, is
+# faster overlapped: 0.14-0.18 against 0.20)
+SERIAL_MAX_IDS = 8192
 
 
 def log(*a):
@@ -181,9 +194,12 @@ def measure(ctx, steps, warmup, args, full):
     from jagged_embedding_sparse_amd.step import SparseStep, StageTimer
     w, NB, n_tok, grads_dev = ctx.w, len(ctx.dev_batches), ctx.n_tok, ctx.grads_dev
     dev_batches = ctx.dev_batches
-    L = 1 if (args.sync or args.schedule == "serial") else args.lookahead
+    asked = args.schedule
+    if asked == "auto":  # batches of a few thousand IDs: the launch count sets the pace
+        asked = "serial" if ctx.cap * len(w.tables) <= SERIAL_MAX_IDS else "joined"
+    L = 1 if (args.sync or asked == "serial") else args.lookahead
     ahead = L >= 2
-    sched = args.schedule if (ahead or args.schedule == "serial") else "joined"
+    sched = asked if (ahead or asked == "serial") else "joined"
     graph = args.graph == "on" and ahead and not args.sync
     step = SparseStep(w, ctx.weights, ctx.states, ctx.cap, lookup=args.lookup,
                       lookahead=L, autotune={} if args.autotune else None, schedule=sched,

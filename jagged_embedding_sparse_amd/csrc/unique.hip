@@ -552,6 +552,173 @@ k_compact(const uint32_t* __restrict__ sk, const int64_t* __restrict__ nvp, Grou
   }
 }
 
+// ---------------------------------------------------------------- small calls
+// A call of at most kSmallMax items runs in one workgroup instead of the
+// ten-odd launches of the radix path. Wave w holds items w * 256 + 64 i +
+// lane (four rounds) in registers; an LSD radix sort by global key with
+// 8-bit digits runs in LDS: per pass, every wave counts its items' digits
+// (LDS atomics), prefixes over the waves and the digits give each wave's
+// first position of each digit, and the waves rank their items round by
+// round (lane masks, a running count per digit) and write each to its
+// sorted place, so equal keys keep their input order (ascending bm). Then
+// head flags, one workgroup scan and the compaction's outputs: unique keys,
+// segment starts, occurrence -> unique index, the (table, shard) group
+// offsets, and the all-exclusive classes and counts (the collision split,
+// when there are previous rows, follows as usual).
+constexpr int kSmallThreads = 1024;
+constexpr int kSmallWaves = kSmallThreads / kWave;
+constexpr int kSmallRounds = 4;
+constexpr int kSmallWaveItems = kWave * kSmallRounds;
+constexpr int kSmallMax = kSmallThreads * kSmallRounds;  // 4096 items
+constexpr int kSmallBits = 8;
+constexpr int kSmallBins = 1 << kSmallBits;
+
+__global__ void __launch_bounds__(kSmallThreads)
+k_dedup_small(const int64_t* __restrict__ keys, const int32_t* __restrict__ bm,
+              const int64_t* __restrict__ so, int32_t W, int64_t n_cap, Groups g, int32_t kbits,
+              int32_t no_prev, int64_t* __restrict__ unique, int64_t* __restrict__ unique_offsets,
+              int32_t* __restrict__ seg_offsets, int32_t* __restrict__ occ_bm,
+              int32_t* __restrict__ occ_uid, uint8_t* __restrict__ cls,
+              int64_t* __restrict__ counts) {
+  __shared__ uint32_t s_key[kSmallMax];
+  __shared__ int32_t s_val[kSmallMax];
+  __shared__ uint64_t peers_tab[kSmallWaves][kSmallBins];  // lane masks of the ranking
+  __shared__ uint32_t base[kSmallWaves][kSmallBins];  // counts, then each wave's next position
+  __shared__ uint32_t tmp[17];
+  __shared__ int32_t s_n;
+  // valid items: the largest shard bound, clamped into [0, n_cap] (the
+  // radix path's running maximum over the bounds ends at the same value)
+  if (threadIdx.x == 0) s_n = 0;
+  __syncthreads();
+  if ((int32_t)threadIdx.x < W) {
+    int64_t x = so[threadIdx.x + 1];
+    x = x < 0 ? 0 : (x > n_cap ? n_cap : x);
+    atomicMax(&s_n, (int32_t)x);
+  }
+  __syncthreads();
+  const int32_t n = s_n;
+  const int32_t n_groups = g.T * g.W;
+  const int w = threadIdx.x / kWave, l = lane();
+  if (n > 0) {  // uniform
+    const int32_t wn = n - w * kSmallWaveItems;  // this wave's items
+    uint32_t key[kSmallRounds];
+    int32_t val[kSmallRounds];
+    // lanes past the end load the last item again: registers written
+    // unconditionally, all loads in flight
+#pragma unroll
+    for (int i = 0; i < kSmallRounds; ++i) {
+      const int32_t x = w * kSmallWaveItems + i * kWave + l;
+      const int32_t xc = x < n ? x : n - 1;
+      key[i] = (uint32_t)keys[xc];
+      val[i] = bm[xc];
+    }
+    for (int b = l; b < kSmallBins; b += kWave) peers_tab[w][b] = 0;
+    const uint64_t lt = lanemask_lt();
+    for (int32_t shift = 0; shift < kbits; shift += kSmallBits) {
+      for (int b = l; b < kSmallBins; b += kWave) base[w][b] = 0;
+      // this wave's digit counts (a wave's LDS operations complete in order)
+#pragma unroll
+      for (int i = 0; i < kSmallRounds; ++i)
+        if (i * kWave + l < wn) atomicAdd(&base[w][(key[i] >> shift) & (kSmallBins - 1)], 1u);
+      __syncthreads();
+      // per digit: prefix over the waves, then over the digits
+      uint32_t tot = 0;
+      if (threadIdx.x < kSmallBins) {
+        const int b = threadIdx.x;
+#pragma unroll
+        for (int x = 0; x < kSmallWaves; ++x) {
+          const uint32_t c = base[x][b];
+          base[x][b] = tot;
+          tot += c;
+        }
+      }
+      uint32_t all;
+      const uint32_t ex =
+          block_excl_scan<uint32_t>(threadIdx.x < kSmallBins ? tot : 0u, tmp, &all);
+      if (threadIdx.x < kSmallBins) {
+#pragma unroll
+        for (int x = 0; x < kSmallWaves; ++x) base[x][threadIdx.x] += ex;
+      }
+      __syncthreads();
+      // stable ranks in order (round by round, lanes in order), each item
+      // written to its place at once; the lowest lane of each digit
+      // advances the wave's next position for it
+#pragma unroll
+      for (int i = 0; i < kSmallRounds; ++i) {
+        if (i * kWave < wn) {  // uniform per wave
+          const bool on = i * kWave + l < wn;
+          const uint32_t dd = on ? (key[i] >> shift) & (kSmallBins - 1) : 0u;
+          const uint64_t peers = lds_peers(peers_tab[w], dd, on);
+          const uint32_t at = base[w][dd];
+          if (on) {
+            const uint32_t p = at + (uint32_t)popc(peers & lt);
+            s_key[p] = key[i];
+            s_val[p] = val[i];
+            if ((peers & lt) == 0) base[w][dd] = at + (uint32_t)popc(peers);
+          }
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < kSmallRounds; ++i) {
+        // every slot is inside the stage; slots past the items are never used
+        const int32_t x = w * kSmallWaveItems + i * kWave + l;
+        key[i] = s_key[x];
+        val[i] = s_val[x];
+      }
+      __syncthreads();  // the stage is rewritten by the next pass
+    }
+    // s_key / s_val hold the sorted items (the last pass wrote them)
+    // thread t owns sorted slots kSmallRounds * t ..: head flags and their scan
+    const int p0 = threadIdx.x * kSmallRounds;
+    bool hd[kSmallRounds];
+    uint32_t heads = 0;
+#pragma unroll
+    for (int k = 0; k < kSmallRounds; ++k) {
+      const int p = p0 + k;
+      hd[k] = p < n && (p == 0 || s_key[p - 1] != s_key[p]);
+      heads += hd[k];
+    }
+    uint32_t U;
+    uint32_t uid = block_excl_scan<uint32_t>(heads, tmp, &U);
+#pragma unroll
+    for (int k = 0; k < kSmallRounds; ++k) {
+      const int p = p0 + k;
+      if (p >= n) break;
+      uid += hd[k];
+      const uint32_t u = uid - 1;  // this item's unique row
+      occ_bm[p] = s_val[p];
+      occ_uid[p] = (int32_t)u;
+      if (hd[k]) {
+        const uint32_t kk = s_key[p];
+        unique[u] = (int64_t)kk;
+        seg_offsets[u] = p;
+        if (no_prev) cls[u] = FS_EXCLUSIVE;
+        // every group in (group of the previous unique key, this key's
+        // group] starts here; after the last unique key the rest end at U
+        const int32_t gi = group_of(kk, g);
+        const int32_t gp = u == 0 ? -1 : group_of(s_key[p - 1], g);
+        for (int32_t q = gp + 1; q <= gi; ++q) unique_offsets[q] = u;
+        if (u == U - 1)
+          for (int32_t q = gi + 1; q <= n_groups; ++q) unique_offsets[q] = U;
+      }
+    }
+    if (threadIdx.x == 0) {
+      seg_offsets[U] = n;
+      counts[0] = U;
+      counts[1] = 0;
+      counts[2] = no_prev ? U : 0;
+      counts[3] = 0;
+    }
+  } else {
+    for (int32_t q = threadIdx.x; q <= n_groups; q += kSmallThreads) unique_offsets[q] = 0;
+    if (threadIdx.x == 0) {
+      seg_offsets[0] = 0;
+      counts[0] = counts[1] = counts[2] = counts[3] = 0;
+    }
+  }
+}
+
 // ---------------------------------------------------------------- collision
 // Both unique lists are ascending and split into the same (table, shard)
 // groups (unique_offsets of this call and of the previous one), and a key of
@@ -818,6 +985,21 @@ extern "C" int fs_unique_collision_split(const int64_t* shard_keys, const int32_
   g.row_base[T] = base;
   if (base > (int64_t)UINT32_MAX) return FS_ERR_UNSUPPORTED;
   if (!ws || ws_bytes < fs_unique_workspace_size(n_cap, prev_cap, T, W)) return FS_ERR_WORKSPACE;
+
+  // small calls: one workgroup sorts and compacts every item
+  if (n_cap <= kSmallMax) {
+    const int32_t no_prev = prev_unique == nullptr;
+    hipLaunchKernelGGL(k_dedup_small, dim3(1), dim3(kSmallThreads), 0, stream, shard_keys,
+                       shard_bm, shard_offsets, W, n_cap, g, key_bits(base), no_prev, unique,
+                       unique_offsets, seg_offsets, occ_bm, occ_uid, cls, counts);
+    FS_LAUNCH_CHECK();
+    if (no_prev) return FS_OK;
+    Carve cs(ws);
+    const int64_t cap1 = n_cap > 0 ? n_cap : 1;
+    uint32_t* block_hits = cs.take<uint32_t>((size_t)T * W * collide_splits(cap1, T, W));
+    return launch_collide(unique, unique_offsets, n_cap, T, W, prev_unique, prev_unique_offsets,
+                          prev_counts, prev_cap, cls, prev_cls, counts, block_hits, stream);
+  }
 
   // Sort inside the W shards (shard-local keys: fewer bits, so often one pass
   // fewer) or over all items as one segment (local key = global key). A pass

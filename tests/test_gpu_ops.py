@@ -540,7 +540,9 @@ UQ_CASES = [(11, 64, [100_000], 4, 60), (12, 512, [300, 5000], 16, 200),
             (13, 2048, [20_000, 20_000, 9000, 500], 256, 40), (14, 37, [50], 8, 30),
             (15, 4096, [200_000_000], 512, 60), (16, 3, [7], 2, 3),
             (17, 2048, [1 << 21], 2, 400), (18, 2048, [1 << 20, 1 << 20], 2, 200),
-            (19, 2048, [1 << 20, 700_000, 300_000], 3, 100)]
+            (19, 2048, [1 << 20, 700_000, 300_000], 3, 100),
+            # at most 4096 items: the one-workgroup path, with 3 and 2 tables
+            (20, 64, [50, 5000, 300], 8, 20), (21, 100, [1 << 20, 1 << 20], 2, 40)]
 
 
 @pytest.mark.parametrize("case", UQ_CASES, ids=lambda c: f"s{c[0]}")
@@ -666,6 +668,11 @@ SS_CASES = [
      ["dup", "edge", "rand", "rand", "rand", "one", "edge", "dup", "rand", "rand", "rand", "rand",
       "edge", "one", "dup", "rand"]),
     ("all-small", 16 << 20, [16384, 9000, 1, 0] * 4, ["edge", "dup", "rand", "rand"] * 4),
+    # the one-workgroup dedup takes calls of up to 4096 items, the radix passes one more
+    ("4096-items", 16 << 20, [1000, 0, 63, 1, 2047, 985] + [0] * 10,
+     ["dup", "rand", "edge", "one", "rand", "edge"] + ["rand"] * 10),
+    ("4097-items", 16 << 20, [1000, 0, 63, 1, 2047, 986] + [0] * 10,
+     ["dup", "rand", "edge", "one", "rand", "edge"] + ["rand"] * 10),
 ]
 
 
@@ -678,7 +685,9 @@ def test_unique_shard_sizes(name, rows, sizes, kinds):
     keys, bm, so = _shard_major(rng, sizes, rows, W, kinds)
     n = len(keys)
     say("unique shard sizes", name, n)
-    for n_cap in (n, n + 5000):
+    # spare capacity, kept on the same side of the one-workgroup path's limit
+    caps = (n, n + 5000) if n > 4097 else ((n, 4096) if n < 4096 else (n,))
+    for n_cap in caps:
         uq = lib.fs_unique_collision_split(cu(keys), cu(bm), cu(so), n_cap, [rows], W)
         ouq = O.unique(keys, bm, [rows], W)
         cls, _, counts = O.collision(ouq["unique"], None)
