@@ -662,6 +662,21 @@ __global__ void __launch_bounds__(kThreads) k_fix(RUArgs a) {
   fix_rows<D, WT>(a, blockIdx.x, part);
 }
 
+// Small calls of one table: long, medium and short rows in one launch (the
+// long rows' workgroups first, as their chunks are the longest work), the
+// fix-up after it -- two launches instead of four, where a call of a few
+// thousand occurrences is a chain of launches more than a stream of bytes.
+constexpr int64_t kFusedMax = 1 << 17;  // occurrences
+
+template <int D, typename WT>
+__global__ void __launch_bounds__(kThreads) k_rows3(RUArgs a, int32_t b_long, int32_t b_medium,
+                                                   int32_t b_short) {
+  const int32_t b = blockIdx.x;
+  if (b < b_long) long_rows<D, WT>(a, b, b_long);
+  else if (b < b_long + b_medium) medium_rows<D, WT>(a, b - b_long, b_medium);
+  else short_rows<D, WT>(a, b - b_long - b_medium, b_short);
+}
+
 // workgroups of each kind for one table with n_cap occurrences
 int64_t blocks_of(int K, int64_t n_cap, int64_t chunk) {
   int64_t b;
@@ -683,6 +698,29 @@ int launch_one(const RUArgs& a, hipStream_t stream) {
   else hipLaunchKernelGGL((k_fix<D, WT>), g, tb, 0, stream, a);
   FS_LAUNCH_CHECK();
   return FS_OK;
+}
+
+template <int D, typename WT>
+int launch_rows3(const RUArgs& a, hipStream_t stream) {
+  const int64_t bl = blocks_of(kLongRows, a.n_cap, a.chunk);
+  const int64_t bm = blocks_of(kMediumRows, a.n_cap, a.chunk);
+  const int64_t bs = blocks_of(kShortRows, a.n_cap, a.chunk);
+  hipLaunchKernelGGL((k_rows3<D, WT>), dim3((unsigned)(bl + bm + bs)), dim3(kThreads), 0, stream,
+                     a, (int32_t)bl, (int32_t)bm, (int32_t)bs);
+  FS_LAUNCH_CHECK();
+  return launch_one<kFixRows, D, WT>(a, stream);
+}
+
+template <typename WT>
+int launch_rows3_dim(int dim, const RUArgs& a, hipStream_t stream) {
+  switch (dim) {
+    case 64: return launch_rows3<64, WT>(a, stream);
+    case 128: return launch_rows3<128, WT>(a, stream);
+    case 256: return launch_rows3<256, WT>(a, stream);
+    case 512: return launch_rows3<512, WT>(a, stream);
+    case 1024: return launch_rows3<1024, WT>(a, stream);
+  }
+  return FS_ERR_UNSUPPORTED;
 }
 
 template <int K, typename WT>
@@ -713,6 +751,9 @@ int shape_of(int dim, bool bf16) {
 // narrow one) and one per wide table
 int launch_tables(const RUArgs* args, const int* dims, const bool* bf16, int T, int32_t rows,
                   hipStream_t stream) {
+  if (T == 1 && rows == FS_ROWS_ALL && args[0].n_cap <= kFusedMax)
+    return bf16[0] ? launch_rows3_dim<uint16_t>(dims[0], args[0], stream)
+                   : launch_rows3_dim<float>(dims[0], args[0], stream);
   int narrow = 0;
   for (int t = 0; t < T; ++t) narrow += dims[t] <= kSetMaxDim;
   for (int K = 0; K < 4; ++K) {
