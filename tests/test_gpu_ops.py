@@ -542,7 +542,9 @@ UQ_CASES = [(11, 64, [100_000], 4, 60), (12, 512, [300, 5000], 16, 200),
             (17, 2048, [1 << 21], 2, 400), (18, 2048, [1 << 20, 1 << 20], 2, 200),
             (19, 2048, [1 << 20, 700_000, 300_000], 3, 100),
             # at most 4096 items: the one-workgroup path, with 3 and 2 tables
-            (20, 64, [50, 5000, 300], 8, 20), (21, 100, [1 << 20, 1 << 20], 2, 40)]
+            (20, 64, [50, 5000, 300], 8, 20), (21, 100, [1 << 20, 1 << 20], 2, 40),
+            # the call limits on the one-workgroup path: 8 tables over 1024 shards
+            (22, 16, [1 << 20] * 7 + [3000], 1024, 20)]
 
 
 @pytest.mark.parametrize("case", UQ_CASES, ids=lambda c: f"s{c[0]}")
