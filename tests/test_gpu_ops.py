@@ -544,7 +544,9 @@ UQ_CASES = [(11, 64, [100_000], 4, 60), (12, 512, [300, 5000], 16, 200),
             # at most 4096 items: the one-workgroup path, with 3 and 2 tables
             (20, 64, [50, 5000, 300], 8, 20), (21, 100, [1 << 20, 1 << 20], 2, 40),
             # the call limits on the one-workgroup path: 8 tables over 1024 shards
-            (22, 16, [1 << 20] * 7 + [3000], 1024, 20)]
+            (22, 16, [1 << 20] * 7 + [3000], 1024, 20),
+            # a few thousand items above the one-workgroup path's limit
+            (23, 256, [5000, 1 << 20], 16, 40), (24, 600, [1 << 22], 64, 50)]
 
 
 @pytest.mark.parametrize("case", UQ_CASES, ids=lambda c: f"s{c[0]}")
@@ -670,10 +672,17 @@ SS_CASES = [
      ["dup", "edge", "rand", "rand", "rand", "one", "edge", "dup", "rand", "rand", "rand", "rand",
       "edge", "one", "dup", "rand"]),
     ("all-small", 16 << 20, [16384, 9000, 1, 0] * 4, ["edge", "dup", "rand", "rand"] * 4),
-    # the one-workgroup dedup takes calls of up to 4096 items, the radix passes one more
+    # the one-workgroup dedup takes calls of up to 4096 items, the radix passes
+    # one more (and the 32768-item pair: a one-workgroup path staged in global
+    # memory up to that size was built and measured slower, so the radix
+    # passes take both)
     ("4096-items", 16 << 20, [1000, 0, 63, 1, 2047, 985] + [0] * 10,
      ["dup", "rand", "edge", "one", "rand", "edge"] + ["rand"] * 10),
     ("4097-items", 16 << 20, [1000, 0, 63, 1, 2047, 986] + [0] * 10,
+     ["dup", "rand", "edge", "one", "rand", "edge"] + ["rand"] * 10),
+    ("32768-items", 16 << 20, [16384, 0, 63, 1, 2047, 14273] + [0] * 10,
+     ["dup", "rand", "edge", "one", "rand", "edge"] + ["rand"] * 10),
+    ("32769-items", 16 << 20, [16384, 0, 63, 1, 2047, 14274] + [0] * 10,
      ["dup", "rand", "edge", "one", "rand", "edge"] + ["rand"] * 10),
 ]
 
