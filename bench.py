@@ -191,6 +191,7 @@ def measure(ctx, steps, warmup, args, full):
     per-stage breakdown and the per-step spread from extra steps."""
     import torch
 
+    from jagged_embedding_sparse_amd.hipevent import HipEvent
     from jagged_embedding_sparse_amd.step import SparseStep, StageTimer
     w, NB, n_tok, grads_dev = ctx.w, len(ctx.dev_batches), ctx.n_tok, ctx.grads_dev
     dev_batches = ctx.dev_batches
@@ -245,7 +246,7 @@ def measure(ctx, steps, warmup, args, full):
     upd_names = ("update_all", "update_co", "update_ex")
     timer = StageTimer(capacity=4 * steps, streams=streams, only=upd_names)
     step.timer = timer
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0, ev1 = HipEvent(enable_timing=True), HipEvent(enable_timing=True)
     pairs = []
     ids_timed = 0
     torch.cuda.synchronize()
@@ -323,7 +324,7 @@ def measure(ctx, steps, warmup, args, full):
         # whose lookup waits for the index stream; otherwise stream A, whose
         # last lookup waits for the update (and with --sync runs everything).
         end_stream = torch.cuda.current_stream() if (ahead or sched == "serial") else step.sA
-        evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        evs = [HipEvent(enable_timing=True) for _ in range(steps + 1)]
         for e in evs:  # first records take fresh runtime resources: not in the loop
             e.record(end_stream)
         torch.cuda.synchronize()

@@ -97,6 +97,7 @@ from dataclasses import dataclass, field
 import torch
 
 from . import lib
+from .hipevent import HipEvent
 
 
 _CLS = {lib.FS_ALL: "all", lib.FS_COLLISION: "co", lib.FS_EXCLUSIVE: "ex"}
@@ -121,7 +122,8 @@ class StageTimer:
     dropped, so a larger pool made and dropped first keeps the timed
     records cheap. Each record also costs the GPU a few microseconds between
     kernels, so `only` limits the timed stages where that would distort the
-    measurement."""
+    measurement; the events skip the system-scope fence (HipEvent), whose
+    cache write-back would otherwise add to every timed span."""
 
     def __init__(self, capacity=0, streams=None, only=None):
         self.pairs = {}
@@ -129,8 +131,8 @@ class StageTimer:
         self.only = set(only) if only is not None else None  # stage names to time
         ss = list(streams) if streams else [torch.cuda.current_stream()]
         for i in range(capacity):
-            a = torch.cuda.Event(enable_timing=True)
-            b = torch.cuda.Event(enable_timing=True)
+            a = HipEvent(enable_timing=True)
+            b = HipEvent(enable_timing=True)
             a.record(ss[i % len(ss)])
             b.record(ss[i % len(ss)])
             self.pool.append((a, b))
@@ -140,7 +142,7 @@ class StageTimer:
     def _pair(self):
         if self.pool:
             return self.pool.pop()
-        return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        return HipEvent(enable_timing=True), HipEvent(enable_timing=True)
 
     def span(self, name, stream):
         if self.only is not None and name not in self.only:
@@ -179,9 +181,9 @@ class IterState:
     cls_next: torch.Tensor = None  # class of this iteration's rows vs the next one
     out: list = field(default_factory=list)  # lookup output per table
     idx_x: int = 0  # index stream that ran this iteration's index stages
-    ev_uq: torch.cuda.Event = None  # dedup done (unique rows and counts[0] ready)
-    ev_done: torch.cuda.Event = None  # index stages done (after the collision split)
-    ev_bal: torch.cuda.Event = None  # balance (and AutoTune's share update) done
+    ev_uq: HipEvent = None  # dedup done (unique rows and counts[0] ready)
+    ev_done: HipEvent = None  # index stages done (after the collision split)
+    ev_bal: HipEvent = None  # balance (and AutoTune's share update) done
     graph: object = None  # the step graph whose capture indexed this iteration (graph mode)
 
 
@@ -260,7 +262,7 @@ class SparseStep:
         self.sB = torch.cuda.Stream(device=d)
         # exclusive-row lookup of the prioritized schedule
         self.sC = torch.cuda.Stream(device=d) if schedule == "prioritized" else None
-        self.ev_b = torch.cuda.Event()
+        self.ev_b = HipEvent()
         self._ahead = deque()  # iterations after i already indexed, oldest first
         self._n_indexed = 0  # iterations whose index stages were issued
         self.cur = None  # IterState of iteration i (already looked up)
@@ -290,10 +292,11 @@ class SparseStep:
         # the joined schedule's update as two concurrent parts (rows of at
         # most 64 occurrences on the caller's stream, longer rows on stream B)
         self.split_update = split_update
-        self._ev_fork, self._ev_join = torch.cuda.Event(), torch.cuda.Event()
+        self._ev_fork, self._ev_join = HipEvent(), HipEvent()
         # one reused fork event per index stream (a new event per wait costs
         # the host more)
-        self._ev_idx = [torch.cuda.Event() for _ in self.s_idx]
+        self._ev_idx = [HipEvent() for _ in self.s_idx]
+        self._cs_ev = None  # the event last recorded on the caller's stream this step
 
     def _t(self, name, stream):
         """Context that brackets one C call with HIP events on its stream."""
@@ -310,9 +313,11 @@ class SparseStep:
         if not self._dry:
             fn(**kw)
 
-    def _fork(self, s, cs, ev=None):
+    def _fork(self, s, cs, ev=None, recorded=False):
         """Stream s waits for everything enqueued on cs so far (through event
-        ev when given: a reused event costs the host less than a new one)."""
+        ev when given: a reused event costs the host less than a new one;
+        `recorded`: ev was recorded on cs with nothing enqueued there since,
+        so s waits for it without a new record)."""
         if self._capture is not None and s not in self._forked:
             self._forked.append(s)
         if self._dry:
@@ -320,7 +325,8 @@ class SparseStep:
         if ev is None:
             s.wait_stream(cs)
         else:
-            ev.record(cs)
+            if not recorded:
+                ev.record(cs)
             s.wait_event(ev)
 
     def _join(self, cs, s, ev=None):
@@ -333,8 +339,12 @@ class SparseStep:
             cs.wait_event(ev)
 
     def _wait(self, s, ev, st):
-        """Stream s waits for event ev of iteration state st."""
+        """Stream s waits for event ev of iteration state st; not when ev has
+        already completed (outside a capture): then there is nothing to order,
+        and the query costs the host less than a wait."""
         if self._dry or (self._capture is not None and st.graph is not self._capture):
+            return
+        if self._capture is None and ev.query():
             return
         s.wait_event(ev)
 
@@ -366,9 +376,9 @@ class SparseStep:
             cls=torch.empty(ncap, dtype=torch.uint8, device=d),
             counts=torch.empty(4, dtype=torch.int64, device=d))
         st.cls_next = torch.empty(ncap, dtype=torch.uint8, device=d)
-        st.ev_uq = torch.cuda.Event()
-        st.ev_done = torch.cuda.Event()
-        st.ev_bal = torch.cuda.Event()
+        st.ev_uq = HipEvent()
+        st.ev_done = HipEvent()
+        st.ev_bal = HipEvent()
         st.out = [torch.empty((self.cap, D), dtype=w.dtype, device=d)
                   for D, w in zip(self.dims, self.weights)]
         return st
@@ -452,13 +462,17 @@ class SparseStep:
         with self._t(f"lookup_{_CLS[which]}", stream):
             self._call(pl, n_tok=st.n_tok, stream=stream.cuda_stream)
 
-    def _run_update(self, st, grads, which, ws, stream, name=None, aux=None):
+    def _run_update(self, st, grads, which, ws, stream, name=None, aux=None, fork_ev=None):
         """The update of st's rows of class `which` on `stream`; with an `aux`
         stream and a batch of at least _SPLIT_MIN IDs (or split_update=True),
         its rows of more than 64 occurrences run on aux beside the rest (the
         two parts touch disjoint rows; only the long rows use the workspace),
         so that each stream has one launch boundary fewer and the parts' ramps
-        and tails overlap."""
+        and tails overlap. `fork_ev`: an event last recorded on `stream` with
+        nothing enqueued there since, which aux may wait for instead of a new
+        record (each record costs the host and the stream a few us). When the
+        update is timed, aux waits for the span's start event instead, so that
+        no part of the update starts before the measured span."""
         pu = self._prep(("upd", st.slot, which, id(ws)), lambda: lib.prepare_update(
             self.weights, self.states, self.W, st.uq, self.w.optim, self.w.lr, self.w.eps, which,
             st.cls_next, ws))
@@ -467,11 +481,15 @@ class SparseStep:
             g[t] = lib._ptr(x)
         split = aux is not None and (self.split_update is True or (
             self.split_update == "auto" and st.n_tok * self.T >= _SPLIT_MIN))
-        with self._t(name or f"update_{_CLS[which]}", stream):
+        with self._t(name or f"update_{_CLS[which]}", stream) as span:
             if not split:
                 self._call(pu, n_tok=st.n_tok, rows=lib.FS_ROWS_ALL, stream=stream.cuda_stream)
                 return
-            self._fork(aux, stream, self._ev_fork)
+            ev = getattr(span, "a", None) or fork_ev
+            if ev is not None:
+                self._fork(aux, stream, ev, recorded=True)
+            else:
+                self._fork(aux, stream, self._ev_fork)
             self._call(pu, n_tok=st.n_tok, rows=lib.FS_ROWS_MANY, stream=aux.cuda_stream)
             self._call(pu, n_tok=st.n_tok, rows=lib.FS_ROWS_FEW, stream=stream.cuda_stream)
             self._join(stream, aux, self._ev_join)
@@ -539,7 +557,7 @@ class SparseStep:
         sA.wait_stream(torch.cuda.current_stream())  # inputs made on the caller's stream
         calib = None
         if self._calib_left > 0:
-            calib = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            calib = [HipEvent(enable_timing=True) for _ in range(3)]
             calib[0].record(sA)
         # B may start once A has finished the previous step (iteration i's
         # index outputs and lookups; the slot A is about to overwrite is free)
@@ -567,9 +585,11 @@ class SparseStep:
     def _next_states(self, batch_next, batch_after, cs):
         """Index stream waits at the start of a step, and iteration i+1's
         state (indexed now if it was not indexed ahead). Returns (nxt, the
-        index stream number and stream for batch_after or None)."""
+        index stream number and stream for batch_after or None); leaves in
+        _cs_ev the event last recorded on cs (None if none was)."""
         cur = self.cur
         n = self._nslots()
+        self._cs_ev = None
         # the index streams about to work wait for everything enqueued so far
         # on the caller's stream: the batches, and the update of i-1 and the
         # lookups whose state slots the new index stages overwrite; enqueued
@@ -579,12 +599,14 @@ class SparseStep:
             nxt = self.states_buf[(self.slot + 1) % n]
             x, s_ = self._index_stream()
             self._fork(s_, cs, self._ev_idx[x])
+            self._cs_ev = self._ev_idx[x]
             self._index_stages(batch_next, nxt, cur, s_, x)
         else:
             nxt = self._ahead.popleft()
         if batch_after is not None:
             x, s_ = self._index_stream()
             self._fork(s_, cs, self._ev_idx[x])
+            self._cs_ev = self._ev_idx[x]
             aft_s = (x, s_)
         return nxt, aft_s
 
@@ -606,7 +628,8 @@ class SparseStep:
         nxt, aft_s = self._next_states(batch_next, batch_after, cs)
         # the update of i needs nothing from the index stages of i+1 (they
         # only read iteration i's unique rows), so only the lookup waits
-        self._run_update(cur, grads_cur, lib.FS_ALL, self.ws_red[1], cs, aux=self.sB)
+        self._run_update(cur, grads_cur, lib.FS_ALL, self.ws_red[1], cs, aux=self.sB,
+                         fork_ev=self._cs_ev)
         self._wait(cs, nxt.ev_done, nxt)
         self._lookup(nxt, lib.FS_ALL, cs)
         self._index_after(batch_after, nxt, aft_s)
