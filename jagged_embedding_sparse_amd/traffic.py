@@ -143,10 +143,12 @@ INDEX_KERNELS = ("k_rank_part", "k_place", "k_vbs_cut", "k_lens", "k_bal", "k_ti
                  "k_compact", "k_collide", "k_collide_counts")
 
 
-def table(res: dict, steps: int, index_algorithmic: float | None) -> str:
+def table(res: dict, steps: int, index_algorithmic: float | None, cmd: str | None = None) -> str:
     """Per-kernel HBM bytes per iteration (`steps` iterations in the run) and
-    the index kernels' total against their algorithmic bytes."""
-    lines = ["kernel                               dispatches   fetch MB/iter  write MB/iter"]
+    the index kernels' total against their algorithmic bytes; `cmd`, the
+    commands that made the counters, heads the table."""
+    lines = [f"Commands: {cmd}", ""] if cmd else []
+    lines.append("kernel                               dispatches   fetch MB/iter  write MB/iter")
     idx = 0.0
     for name, v in sorted(res["kernels"].items(), key=lambda kv: kv[1]["short"]):
         per = v["dispatches"] / steps
@@ -200,6 +202,7 @@ def main() -> None:
                    help="iterations the run made (default: the lookup's launches)")
     s.add_argument("--index-bytes", type=float, default=None,
                    help="algorithmic bytes of the index stages per step")
+    s.add_argument("--cmd", default=None, help="the commands that made the counters (for --txt)")
     a = ap.parse_args()
     if a.cmd == "run":
         run(a.config)
@@ -209,7 +212,7 @@ def main() -> None:
             # one lookup launch per iteration (the prologue's included)
             steps = a.steps or res["stages"]["lookup_all"]["launches"]
             with open(a.txt, "w") as fh:
-                fh.write(table(res, steps, a.index_bytes))
+                fh.write(table(res, steps, a.index_bytes, a.cmd))
 
 
 if __name__ == "__main__":
