@@ -718,6 +718,31 @@ def test_unique_empty_batch():
     assert np.all(host(uq["unique_offsets"]) == 0)
 
 
+def test_lookup_and_update_of_an_empty_batch():
+    """After an empty batch's dedup, the lookup and the update (SGD and
+    row-wise Adagrad, each row part, with a workspace and without) succeed
+    and leave the table and its state as they were."""
+    say("lookup-update-empty")
+    rows = [100]
+    b = dict(uih_len=np.zeros(4, np.int32), sample_offsets=np.zeros(5, np.int64),
+             ids=np.zeros((1, 0), np.int64), n_tok=0)
+    _, _, bk, _ = _gpu_bucketize(b, rows, 4)
+    uq = _gpu_unique(bk, rows, 4, 0)
+    w = _table(100, 64, "f32", 3)
+    st = torch.rand(100, dtype=torch.float32, device="cuda")
+    w0, s0 = w.clone(), st.clone()
+    out = lib.fs_jagged_lookup([w], 4, uq, 0)
+    assert tuple(out[0].shape) == (0, 64)
+    g = torch.empty((0, 64), dtype=torch.float32, device="cuda")
+    for optim in ("sgd", "rw_adagrad"):
+        for part in (lib.FS_ROWS_ALL, lib.FS_ROWS_FEW, lib.FS_ROWS_MANY):
+            lib.fs_grad_reduce_update([w], [st], 4, [g], 0, uq, optim, 0.05, 1e-8, rows=part)
+            lib.fs_grad_reduce_update_noalloc([w], [st], 4, [g], 0, uq, optim, 0.05, 1e-8,
+                                              rows=part)
+    torch.cuda.synchronize()
+    assert torch.equal(w, w0) and torch.equal(st, s0)
+
+
 # ----------------------------------------------------------------------------- lookup + update
 
 
