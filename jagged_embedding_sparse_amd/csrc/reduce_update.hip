@@ -15,7 +15,7 @@
 //     are in flight at once, then the group sums and updates the row.
 //   medium rows (kShort < len < kChunkMin = 65): one lane group per row as
 //     well; the group loads all of the row's occurrence indices with one
-//     load and streams its gradient rows kMedBatch at a time.
+//     load and streams its gradient rows 8 or 16 at a time.
 //   long rows: the table's occurrence range is cut into chunks (128 to 512
 //     occurrences, smaller for smaller batches so that the grid still has
 //     about two chunks per resident wave);
@@ -326,13 +326,13 @@ __device__ __forceinline__ void short_rows(const RUArgs& a, int64_t bid, int64_t
 // ballot, then each lane group takes one of them: the group's lanes load all
 // of the row's occurrence slots with one load (kMedSlots per lane), its
 // weight row and state go out beside them, and its gradient rows stream
-// kMedBatch at a time. A wave thus has GPW rows in progress instead of
-// walking them one after another inside a chunk.
-template <int D, typename WT>
+// MB at a time. A wave thus has GPW rows in progress instead of walking them
+// one after another inside a chunk.
+template <int D, typename WT, int MB = kMedBatch>
 __device__ __forceinline__ void medium_rows(const RUArgs& a, int64_t bid, int64_t nblk) {
   using M = Map<D>;
   constexpr int kMedSlots = (kChunkMin - 1 + M::LPG - 1) / M::LPG;
-  static_assert(M::LPG % kMedBatch == 0, "a batch must not straddle slot registers");
+  static_assert(M::LPG % MB == 0, "a batch must not straddle slot registers");
   const int64_t u_lo = a.unique_offsets[a.g_lo], u_hi = a.unique_offsets[a.g_hi];
   const int l = lane(), grp = l / M::LPG, sub = l % M::LPG;
   const bool ada = a.optim == FS_RW_ADAGRAD;
@@ -378,16 +378,16 @@ __device__ __forceinline__ void medium_rows(const RUArgs& a, int64_t bid, int64_
       double acc[M::CPL];
 #pragma unroll
       for (int c = 0; c < M::CPL; ++c) acc[c] = 0.0;
-      // a batch of kMedBatch (a divisor of LPG) lies inside one slot register
+      // a batch of MB (a divisor of LPG) lies inside one slot register
 #pragma unroll 1
-      for (int m0 = 0; m0 < wlen; m0 += kMedBatch) {
+      for (int m0 = 0; m0 < wlen; m0 += MB) {
         const int q = m0 / M::LPG;
         int32_t slot = mb[0];
 #pragma unroll
         for (int x = 1; x < kMedSlots; ++x) slot = q == x ? mb[x] : slot;
-        float4 gv[kMedBatch][M::NV];
+        float4 gv[MB][M::NV];
 #pragma unroll
-        for (int e = 0; e < kMedBatch; ++e) {
+        for (int e = 0; e < MB; ++e) {
           const int m = m0 + e;
           const int32_t bm = __shfl(slot, grp * M::LPG + (m % M::LPG), kWave);
           if (m < glen) {
@@ -397,7 +397,7 @@ __device__ __forceinline__ void medium_rows(const RUArgs& a, int64_t bid, int64_
           }
         }
 #pragma unroll
-        for (int e = 0; e < kMedBatch; ++e) {
+        for (int e = 0; e < MB; ++e) {
           if (m0 + e < glen) {
 #pragma unroll
             for (int v = 0; v < M::NV; ++v) {
@@ -648,9 +648,24 @@ template <int D, typename WT>
 __global__ void __launch_bounds__(kThreads) k_short(RUArgs a) {
   short_rows<D, WT>(a, blockIdx.x, gridDim.x);
 }
+// A table's own medium-row kernel streams 16 gradient rows at a time when a
+// lane holds one float4 of a row (rows of up to 256 columns): a medium row
+// (about 13 occurrences on average at Zipf IDs) then takes one round of
+// gradient loads instead of two, for 120 instead of 88 VGPRs (four waves per
+// SIMD instead of five). Alone on the GPU the kernel takes the same time
+// (121 us at workload 5); beside the long-row part of the same update the step
+// gains (same box, two runs each): workload 5 1.546/1.545 -> 1.535/1.530 ms,
+// workload 3 0.238/0.248 -> 0.222/0.230. The shared launch of several tables
+// keeps 8 (with 16 it drops to three waves per SIMD and workload 4 gains
+// nothing), as does the one-launch kernel of small calls.
+template <int D>
+struct MedBatch {
+  static constexpr int V = Map<D>::NV == 1 ? 16 : kMedBatch;
+};
+
 template <int D, typename WT>
 __global__ void __launch_bounds__(kThreads) k_medium(RUArgs a) {
-  medium_rows<D, WT>(a, blockIdx.x, gridDim.x);
+  medium_rows<D, WT, MedBatch<D>::V>(a, blockIdx.x, gridDim.x);
 }
 template <int D, typename WT>
 __global__ void __launch_bounds__(kThreads) k_long(RUArgs a) {
