@@ -841,6 +841,13 @@ RU_CASES = [
     (64, "f32", "sgd", [(7, 20_000)], 600_000, 8, 50_000_000),
     # 2.7M tokens: 256-occurrence long-row chunks, one row split over ~1560 of them
     (64, "bf16", "rw_adagrad", [(5, 400_000), (6, 3000)], 2_700_000, 16, 5_000_000),
+    # a row of every medium length (5 .. 64 occurrences) at the widths whose
+    # own medium-row kernel streams 16 gradient rows at a time (calls above
+    # 2^17 occurrences: smaller ones run the one-launch kernel): batches end
+    # ragged
+    (64, "bf16", "rw_adagrad", [(10 + k, 5 + k) for k in range(60)] + [(90, 200)], 150_000, 8,
+     1_000_000),
+    (256, "f32", "sgd", [(10 + k, 5 + k) for k in range(60)], 140_000, 4, 2_000_000),
 ]
 
 
