@@ -13,7 +13,8 @@
 // slices of the comparands, one lane per sample and a quarter slice per
 // wave, and stores the slice's count; a second launch sums the Q counts of
 // each sample and places it. O(n^2 / 64) wave instructions over about 512
-// workgroups, no atomics, stable by construction.
+// workgroups, no atomics, stable by construction. Batches of at most 1024
+// samples take one workgroup for the whole partition (k_balance_small).
 #include "common.hpp"
 
 namespace fs {
@@ -148,12 +149,14 @@ k_place(const int32_t* __restrict__ len, int32_t n, int32_t W, int32_t q,
 constexpr int kCutThreads = 256;
 constexpr int kCutBatch = 16;
 
-__global__ void __launch_bounds__(kCutThreads)
-k_vbs_cut(const int64_t* __restrict__ wsorted, int32_t n, int32_t W,
-          int32_t* __restrict__ rank_offsets, int64_t* __restrict__ rank_weight) {
-  __shared__ int64_t tmp[17];
-  __shared__ int64_t scut[FS_MAX_RANKS + 1];  // S at each rank's first sample
-  const int32_t per = (n + kCutThreads - 1) / kCutThreads;
+// The cuts over the sorted weights wsorted[0 .. n) (global memory or LDS), by
+// a workgroup of NT threads; tmp (17) and scut (W + 1) are LDS scratch.
+template <int NT>
+__device__ __forceinline__ void vbs_cut_body(const int64_t* wsorted, int32_t n, int32_t W,
+                                             int32_t* __restrict__ rank_offsets,
+                                             int64_t* __restrict__ rank_weight, int64_t* tmp,
+                                             int64_t* scut) {
+  const int32_t per = (n + NT - 1) / NT;
   const int32_t k0 = min(n, (int32_t)threadIdx.x * per), k1 = min(n, k0 + per);
   // a thread's weights in batches of kCutBatch independent loads (one
   // memory round trip per batch, not per sample)
@@ -168,7 +171,7 @@ k_vbs_cut(const int64_t* __restrict__ wsorted, int32_t n, int32_t W,
   int64_t T;
   int64_t run = block_excl_scan<int64_t>(local, tmp, &T);
   if (T == 0) {  // no samples: every rank starts at 0, the last ends at n
-    for (int32_t r = threadIdx.x; r <= W; r += kCutThreads) {
+    for (int32_t r = threadIdx.x; r <= W; r += NT) {
       rank_offsets[r] = r == W ? n : 0;
       if (rank_weight && r < W) rank_weight[r] = 0;
     }
@@ -199,7 +202,78 @@ k_vbs_cut(const int64_t* __restrict__ wsorted, int32_t n, int32_t W,
   }
   __syncthreads();
   if (rank_weight)
-    for (int32_t r = threadIdx.x; r < W; r += kCutThreads) rank_weight[r] = scut[r + 1] - scut[r];
+    for (int32_t r = threadIdx.x; r < W; r += NT) rank_weight[r] = scut[r + 1] - scut[r];
+}
+
+__global__ void __launch_bounds__(kCutThreads)
+k_vbs_cut(const int64_t* __restrict__ wsorted, int32_t n, int32_t W,
+          int32_t* __restrict__ rank_offsets, int64_t* __restrict__ rank_weight) {
+  __shared__ int64_t tmp[17];
+  __shared__ int64_t scut[FS_MAX_RANKS + 1];  // S at each rank's first sample
+  vbs_cut_body<kCutThreads>(wsorted, n, W, rank_offsets, rank_weight, tmp, scut);
+}
+
+// Batches of at most kBalSmallMax samples: one workgroup sorts, deals or
+// cuts, in one launch instead of two (FBS) or three (VBS), since for such
+// batches the launches cost more than the work. The keys go to LDS; each
+// thread ranks its kBalSmallPer samples (the keys below each, counted in one
+// pass over the keys), then places them as k_place does; VBS keeps the
+// sorted weights in LDS and cuts them as k_vbs_cut does. 256 threads, like
+// every workgroup of the index path.
+constexpr int kBalSmallMax = 1024;
+constexpr int kBalSmallPer = kBalSmallMax / kCutThreads;
+
+template <bool kFbs>
+__global__ void __launch_bounds__(kCutThreads)
+k_balance_small(const int32_t* __restrict__ len, int32_t n, int32_t W, int anum, int aden,
+                int32_t* __restrict__ perm, int32_t* __restrict__ rank_offsets,
+                int64_t* __restrict__ rank_weight, int32_t* __restrict__ err) {
+  __shared__ uint64_t keys[kBalSmallMax];
+  __shared__ int64_t wsorted[kFbs ? 1 : kBalSmallMax];
+  __shared__ int64_t tmp[17];
+  __shared__ int64_t scut[kFbs ? 1 : FS_MAX_RANKS + 1];
+  for (int32_t b = 0; b < n; b += kCutThreads) {  // uniform trip count: flag_err votes
+    const int32_t s = b + (int32_t)threadIdx.x;
+    const bool valid = s < n;
+    const int32_t L = valid ? len[s] : 0;
+    flag_err(err, valid && (L < 0 || L > FS_MAX_UIH), FS_EF_LEN_RANGE);
+    if (valid) keys[s] = sort_key(L, s);
+  }
+  __syncthreads();
+  uint64_t mine[kBalSmallPer];
+  int32_t pos[kBalSmallPer];
+#pragma unroll
+  for (int i = 0; i < kBalSmallPer; ++i) {
+    const int32_t s = (int32_t)threadIdx.x + i * kCutThreads;
+    mine[i] = s < n ? keys[s] : ~0ull;
+    pos[i] = 0;
+  }
+  for (int32_t c = 0; c < n; ++c) {
+    const uint64_t kc = keys[c];
+#pragma unroll
+    for (int i = 0; i < kBalSmallPer; ++i) pos[i] += kc < mine[i];
+  }
+#pragma unroll
+  for (int i = 0; i < kBalSmallPer; ++i) {
+    const int32_t s = (int32_t)threadIdx.x + i * kCutThreads;
+    if (s >= n) continue;
+    const int32_t p = pos[i];
+    if constexpr (kFbs) {
+      const int32_t round = p / W, off = p % W;
+      const int32_t r = (round % 2 == 0) ? off : (W - 1 - off);
+      perm[fbs_rank_start(r, n, W) + round] = s;
+    } else {
+      perm[p] = s;
+      wsorted[p] = vbs_weight((int64_t)(mine[i] >> 32), anum, aden);  // the clamped length
+    }
+  }
+  if constexpr (kFbs) {
+    for (int32_t r = threadIdx.x; r <= W; r += kCutThreads)
+      rank_offsets[r] = r == W ? n : fbs_rank_start(r, n, W);
+  } else {
+    __syncthreads();
+    vbs_cut_body<kCutThreads>(wsorted, n, W, rank_offsets, rank_weight, tmp, scut);
+  }
 }
 
 // VBS cuts with per-rank shares s_r of the weight (the AutoTune mechanism of
@@ -364,6 +438,12 @@ extern "C" int fs_balance_fbs(const int32_t* uih_len, int32_t n, int32_t W, int3
   int rc = check_common(uih_len, n, W, perm, rank_offsets);
   if (rc) return rc;
   if (!ws || ws_bytes < fs_balance_workspace_size(n, W)) return FS_ERR_WORKSPACE;
+  if (n <= kBalSmallMax) {
+    hipLaunchKernelGGL(k_balance_small<true>, dim3(1), dim3(kCutThreads), 0, stream, uih_len, n,
+                       W, 0, 1, perm, rank_offsets, (int64_t*)nullptr, err);
+    FS_LAUNCH_CHECK();
+    return FS_OK;
+  }
   Carve c(ws);
   c.take<int64_t>((size_t)(n > 0 ? n : 1));
   int32_t* cnt = c.take<int32_t>((size_t)(n > 0 ? n : 1) * (size_t)rank_slices(n));
@@ -380,6 +460,12 @@ extern "C" int fs_balance_vbs(const int32_t* uih_len, int32_t n, int32_t W, int3
             (alpha_den == 2 && alpha_num >= 0 && alpha_num <= 4);
   if (!ok) return FS_ERR_UNSUPPORTED;
   if (ws_bytes < fs_balance_workspace_size(n, W) || !ws) return FS_ERR_WORKSPACE;
+  if (n <= kBalSmallMax) {
+    hipLaunchKernelGGL(k_balance_small<false>, dim3(1), dim3(kCutThreads), 0, stream, uih_len,
+                       n, W, alpha_num, alpha_den, perm, rank_offsets, rank_weight, err);
+    FS_LAUNCH_CHECK();
+    return FS_OK;
+  }
   Carve c(ws);
   int64_t* wsorted = c.take<int64_t>((size_t)(n > 0 ? n : 1));
   int32_t* cnt = c.take<int32_t>((size_t)(n > 0 ? n : 1) * (size_t)rank_slices(n));

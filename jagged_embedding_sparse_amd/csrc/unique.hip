@@ -494,17 +494,16 @@ k_heads_scan(const int64_t* __restrict__ nvp, int32_t W, int32_t n_groups, int32
 // Striped layout: wave w of the tile owns kRounds rounds of 64 consecutive items.
 // Head flags by comparing with the left neighbour (shuffle, or the previous
 // round's last lane), counts by ballot; the wave prefix over the tile's
-// waves comes from LDS, the tile's base from the tile scan.
-__global__ void __launch_bounds__(kThreads)
-k_compact(const uint32_t* __restrict__ sk, const int64_t* __restrict__ nvp, Groups g,
-          const uint32_t* __restrict__ tile_base, const int64_t* __restrict__ counts,
-          int64_t* __restrict__ unique, int32_t* __restrict__ seg_offsets,
-          int32_t* __restrict__ occ_uid, int64_t* __restrict__ unique_offsets,
-          uint8_t* __restrict__ cls_exclusive) {
-  __shared__ uint32_t wave_heads[kThreads / kWave];
-  const int64_t n = n_valid_of(nvp, g.W);
-  const int64_t t0 = (int64_t)blockIdx.x * kTile;
-  if (t0 >= n) return;
+// waves comes from LDS, the tile's base (heads in earlier tiles) and U from
+// the tile scan. Tile blockIdx.x, which starts at t0 < n.
+__device__ __forceinline__ void compact_tile(const uint32_t* __restrict__ sk, int64_t n,
+                                             const Groups& g, int64_t t0, int64_t tile_base,
+                                             int64_t U, int64_t* __restrict__ unique,
+                                             int32_t* __restrict__ seg_offsets,
+                                             int32_t* __restrict__ occ_uid,
+                                             int64_t* __restrict__ unique_offsets,
+                                             uint8_t* __restrict__ cls_exclusive,
+                                             uint32_t* wave_heads) {
   const int w = threadIdx.x / kWave, l = lane();
   const int64_t x0 = t0 + (int64_t)w * kWaveItems;
   uint32_t k[kRounds], prevk[kRounds];
@@ -526,9 +525,8 @@ k_compact(const uint32_t* __restrict__ sk, const int64_t* __restrict__ nvp, Grou
   __syncthreads();
   uint32_t before = 0;
   for (int x = 0; x < w; ++x) before += wave_heads[x];
-  const int64_t U = counts[0];
   const int32_t n_groups = g.T * g.W;
-  int64_t base = (int64_t)tile_base[blockIdx.x] + before;  // heads before this round
+  int64_t base = tile_base + before;  // heads before this round
   const uint64_t le = lanemask_lt() | (1ull << l);
 #pragma unroll
   for (int i = 0; i < kRounds; ++i) {
@@ -550,6 +548,64 @@ k_compact(const uint32_t* __restrict__ sk, const int64_t* __restrict__ nvp, Grou
     }
     base += popc(hm[i]);
   }
+}
+
+__global__ void __launch_bounds__(kThreads)
+k_compact(const uint32_t* __restrict__ sk, const int64_t* __restrict__ nvp, Groups g,
+          const uint32_t* __restrict__ tile_base, const int64_t* __restrict__ counts,
+          int64_t* __restrict__ unique, int32_t* __restrict__ seg_offsets,
+          int32_t* __restrict__ occ_uid, int64_t* __restrict__ unique_offsets,
+          uint8_t* __restrict__ cls_exclusive) {
+  __shared__ uint32_t wave_heads[kThreads / kWave];
+  const int64_t n = n_valid_of(nvp, g.W);
+  const int64_t t0 = (int64_t)blockIdx.x * kTile;
+  if (t0 >= n) return;
+  compact_tile(sk, n, g, t0, tile_base[blockIdx.x], counts[0], unique, seg_offsets, occ_uid,
+               unique_offsets, cls_exclusive, wave_heads);
+}
+
+// Calls of at most kScanTiles tiles: the compaction without k_heads_scan's
+// launch. Every workgroup sums the tiles' head counts itself (at most
+// kScanTiles values: the heads before its tile and U), and workgroup 0 writes
+// what k_heads_scan writes (counts, the end of the last segment, the group
+// offsets of an empty call). One launch fewer on the index path of mid-size
+// batches, where each launch costs the host more than the scan costs the GPU.
+constexpr int64_t kScanTiles = 512;
+
+__global__ void __launch_bounds__(kThreads)
+k_compact_scan(const uint32_t* __restrict__ sk, const int64_t* __restrict__ nvp, Groups g,
+               const uint32_t* __restrict__ tile_heads, int32_t no_prev,
+               int64_t* __restrict__ counts, int64_t* __restrict__ unique,
+               int32_t* __restrict__ seg_offsets, int32_t* __restrict__ occ_uid,
+               int64_t* __restrict__ unique_offsets, uint8_t* __restrict__ cls_exclusive) {
+  __shared__ uint32_t wave_heads[kThreads / kWave];
+  __shared__ int64_t tmp[17];
+  const int64_t n = n_valid_of(nvp, g.W);
+  const int64_t n_tiles = cdiv(n, kTile);
+  int64_t before = 0, all = 0;
+  for (int64_t q = threadIdx.x; q < n_tiles; q += kThreads) {
+    const int64_t c = tile_heads[q];
+    all += c;
+    before += q < (int64_t)blockIdx.x ? c : 0;
+  }
+  int64_t U, base;
+  block_excl_scan<int64_t>(all, tmp, &U);
+  block_excl_scan<int64_t>(before, tmp, &base);
+  if (blockIdx.x == 0) {
+    if (threadIdx.x == 0) {
+      counts[0] = U;
+      counts[1] = 0;
+      counts[2] = no_prev ? U : 0;  // without previous rows every row is exclusive
+      counts[3] = 0;
+      seg_offsets[U] = (int32_t)n;
+    }
+    if (U == 0)
+      for (int32_t q = threadIdx.x; q <= g.T * g.W; q += kThreads) unique_offsets[q] = 0;
+  }
+  const int64_t t0 = (int64_t)blockIdx.x * kTile;
+  if (t0 >= n) return;
+  compact_tile(sk, n, g, t0, base, U, unique, seg_offsets, occ_uid, unique_offsets, cls_exclusive,
+               wave_heads);
 }
 
 // ---------------------------------------------------------------- small calls
@@ -1108,13 +1164,20 @@ extern "C" int fs_unique_collision_split(const int64_t* shard_keys, const int32_
   // without previous rows the classes and counts come from the compaction
   // (every row exclusive) and the collision kernels are not launched
   const int32_t no_prev = prev_unique == nullptr;
-  hipLaunchKernelGGL(k_heads_scan, dim3(1), dim3(kThreads), 0, stream, n_valid, W, T * W, no_prev,
-                     tile_heads, counts, seg_offsets, unique_offsets);
-  FS_LAUNCH_CHECK();
-  hipLaunchKernelGGL(k_compact, dim3(grid), dim3(kThreads), 0, stream, sk, n_valid, g,
-                     tile_heads, counts, unique, seg_offsets, occ_uid, unique_offsets,
-                     no_prev ? cls : (uint8_t*)nullptr);
-  FS_LAUNCH_CHECK();
+  if ((int64_t)grid <= kScanTiles) {
+    hipLaunchKernelGGL(k_compact_scan, dim3(grid), dim3(kThreads), 0, stream, sk, n_valid, g,
+                       tile_heads, no_prev, counts, unique, seg_offsets, occ_uid, unique_offsets,
+                       no_prev ? cls : (uint8_t*)nullptr);
+    FS_LAUNCH_CHECK();
+  } else {
+    hipLaunchKernelGGL(k_heads_scan, dim3(1), dim3(kThreads), 0, stream, n_valid, W, T * W,
+                       no_prev, tile_heads, counts, seg_offsets, unique_offsets);
+    FS_LAUNCH_CHECK();
+    hipLaunchKernelGGL(k_compact, dim3(grid), dim3(kThreads), 0, stream, sk, n_valid, g,
+                       tile_heads, counts, unique, seg_offsets, occ_uid, unique_offsets,
+                       no_prev ? cls : (uint8_t*)nullptr);
+    FS_LAUNCH_CHECK();
+  }
   if (no_prev) return FS_OK;
   return launch_collide(unique, unique_offsets, n_cap, T, W, prev_unique, prev_unique_offsets,
                         prev_counts, prev_cap, cls, prev_cls, counts, block_hits, stream);

@@ -28,8 +28,11 @@ def say(*a):
 
 # ----------------------------------------------------------------------------- balance
 
+# batches of at most 1024 samples take the one-workgroup balance, larger ones
+# the multi-workgroup sort: both sides of the limit, at the largest W too
 BAL_CASES = [(64, 4), (512, 16), (1024, 64), (2048, 256), (4096, 512), (0, 3), (1, 1), (7, 8),
-             (10, 4), (6, 4), (100, 1024), (16384, 1024), (4097, 512)]
+             (10, 4), (6, 4), (100, 1024), (16384, 1024), (4097, 512), (1025, 3),
+             (1024, 1024), (1000, 7)]
 
 
 def _lengths(N, seed, kind):
@@ -68,15 +71,23 @@ def test_vbs_parity(N, W, alpha):
     assert np.array_equal(host(rw), orw)
 
 
-def test_balance_length_range_is_clamped_and_flagged():
-    say("len-range")
-    L = np.array([5, -3, 70000, 12, 0, 65535], np.int32)
+@pytest.mark.parametrize("N", [6, 2000])  # the one-workgroup balance and the larger sort
+def test_balance_length_range_is_clamped_and_flagged(N):
+    say("len-range", N)
+    L = np.random.default_rng(N).integers(0, 3000, N).astype(np.int32)
+    L[:6] = [5, -3, 70000, 12, 0, 65535]
     err = torch.zeros(1, dtype=torch.int32, device="cuda")
     perm, ro, rw = lib.fs_balance_vbs(cu(L), 2, (2, 1), err=err)
     operm, oro, orw = O.balance_vbs(np.clip(L, 0, 65535), 2, (2, 1))
     torch.cuda.synchronize()
     assert int(err.item()) & lib.FS_EF_LEN_RANGE
     assert np.array_equal(host(perm), operm) and np.array_equal(host(rw), orw)
+    err.zero_()
+    perm, ro = lib.fs_balance_fbs(cu(L), 2, err=err)
+    operm, oro = O.balance_fbs(np.clip(L, 0, 65535), 2)
+    torch.cuda.synchronize()
+    assert int(err.item()) & lib.FS_EF_LEN_RANGE
+    assert np.array_equal(host(perm), operm) and np.array_equal(host(ro), oro)
 
 
 @pytest.mark.parametrize("k", [1, 2, 3, 4, 5])
@@ -684,6 +695,10 @@ SS_CASES = [
      ["dup", "rand", "edge", "one", "rand", "edge"] + ["rand"] * 10),
     ("32769-items", 16 << 20, [16384, 0, 63, 1, 2047, 14274] + [0] * 10,
      ["dup", "rand", "edge", "one", "rand", "edge"] + ["rand"] * 10),
+    # calls of up to 2^20 items (512 tiles) compact with the tile scan in the
+    # compaction's own launch, larger ones with a scan launch before it
+    ("1048576-items", 16 << 20, [65536] * 16, ["rand", "dup", "edge", "one"] * 4),
+    ("1048577-items", 16 << 20, [65536] * 15 + [65537], ["rand", "dup", "edge", "one"] * 4),
 ]
 
 
@@ -696,8 +711,10 @@ def test_unique_shard_sizes(name, rows, sizes, kinds):
     keys, bm, so = _shard_major(rng, sizes, rows, W, kinds)
     n = len(keys)
     say("unique shard sizes", name, n)
-    # spare capacity, kept on the same side of the one-workgroup path's limit
-    caps = (n, n + 5000) if n > 4097 else ((n, 4096) if n < 4096 else (n,))
+    # spare capacity, kept on the same side of each path's limit (the
+    # one-workgroup dedup's 4096 items, the compaction's own scan's 2^20)
+    lims = [t for t in (4096, 1 << 20) if n <= t]
+    caps = (n, n + 5000) if not lims else ((n, lims[0]) if n < lims[0] else (n,))
     for n_cap in caps:
         uq = lib.fs_unique_collision_split(cu(keys), cu(bm), cu(so), n_cap, [rows], W)
         ouq = O.unique(keys, bm, [rows], W)
