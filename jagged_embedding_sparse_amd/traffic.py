@@ -137,10 +137,11 @@ def summarize(fetch_csv: str, write_csv: str, config: int, out_path: str | None)
 
 
 # kernels of the index stages (balance, bucketize, dedup + collision split)
-INDEX_KERNELS = ("k_rank_part", "k_place", "k_vbs_cut", "k_lens", "k_bal", "k_tiles", "k_prep1",
-                 "k_hist", "k_colsum", "k_colscan", "k_colscan1", "k_scatter", "k_seg_prep",
-                 "k_seg_hist", "k_seg_groups", "k_seg_scatter", "k_heads", "k_heads_scan",
-                 "k_compact", "k_collide", "k_collide_counts")
+INDEX_KERNELS = ("k_rank_part", "k_place", "k_vbs_cut", "k_balance_small", "k_lens", "k_bal",
+                 "k_tiles", "k_prep1", "k_hist", "k_colsum", "k_colscan", "k_colscan1",
+                 "k_scatter", "k_seg_hist_prep", "k_seg_hist", "k_seg_groups", "k_seg_scatter",
+                 "k_heads", "k_heads_scan", "k_compact", "k_compact_scan", "k_dedup_small",
+                 "k_collide", "k_collide_counts")
 
 
 def table(res: dict, steps: int, index_algorithmic: float | None, cmd: str | None = None) -> str:
