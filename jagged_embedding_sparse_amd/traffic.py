@@ -139,7 +139,7 @@ def summarize(fetch_csv: str, write_csv: str, config: int, out_path: str | None)
 # kernels of the index stages (balance, bucketize, dedup + collision split)
 INDEX_KERNELS = ("k_rank_part", "k_place", "k_vbs_cut", "k_balance_small", "k_lens", "k_bal",
                  "k_tiles", "k_prep1", "k_hist", "k_colsum", "k_colscan", "k_colscan1",
-                 "k_scatter", "k_seg_hist_prep", "k_seg_hist", "k_seg_groups", "k_seg_scatter",
+                 "k_scatter", "k_seg_prep", "k_seg_hist", "k_seg_groups", "k_seg_scatter",
                  "k_heads", "k_heads_scan", "k_compact", "k_compact_scan", "k_dedup_small",
                  "k_collide", "k_collide_counts")
 
