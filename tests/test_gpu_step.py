@@ -205,7 +205,7 @@ def test_workload4_vbs_four_tables_all_iterations():
 
 
 @pytest.mark.timeout(600)
-@pytest.mark.parametrize("align", [16, 256])
+@pytest.mark.parametrize("align", [16, 128, 256])
 def test_workload3_rows_with_their_state(align):
     """Each row's Adagrad state in its own row slot: the step equals the
     oracle's loop."""
